@@ -1,0 +1,227 @@
+"""CPU oracle for the KDA scan -- TEST INFRASTRUCTURE ONLY.
+
+Only `tests/`, `__graft_entry__.smoke()` and the CPU-baseline leg of `bench.py`
+may import this package. The GPU library never loads it and shares no code,
+headers or constants with it.
+
+Contents
+  * `kda_oracle.c`  FP64 token recurrence and its hand-written reverse pass
+                    (C, OpenMP over (sequence, value head)), loaded via ctypes.
+  * `gate_activation`, `gate_cumsum_log2`  FP64 NumPy gate: g = -exp(A_log) *
+                    softplus(x) (omitted A_log = unit scale), then the
+                    chunk-local inclusive cumsum in log2 units.
+  * `forms.py`      independent reformulations (single-chunk dense solve,
+                    chunked UT form) used only to pin the recurrence.
+
+Sources on the pages (the KDA recurrence itself is not printed there; the
+form of record is S_t = (I - b k k^T) Diag(exp g) S_{t-1} + b k v^T,
+o_t = S_t^T q / sqrt(K)):
+  * "[Fix] Use unit KDA gate scale when A_log is omitted" (fla-org
+    flash-linear-attention PR #1294), Summary and Breaking changes: the decay
+    scale is exp(A_log); omitting A_log means unit scale, identical to an
+    explicit zero A_log; an all-ones A_log reproduces exp(1).
+  * "kda in torchtitan (training)" (pytorch/torchtitan PR #4164), quoted
+    attention-gym description of `recurrent_kda`: packed varlen via int32
+    cu_seqlens, repeated offsets are empty slots whose state passes through
+    bitwise, a tail beyond the terminal offset is outside the contract, FP32
+    states one per logical sequence, the gate is a per-token log2 decay
+    (chunk-local cumulative for the chunked op), queries scaled by 1/sqrt(K).
+
+Parity status: every function here is pinned by `tests/test_oracle_*.py`
+(closed forms, invariants, brute force on tiny inputs, finite differences,
+a hand-computed golden case).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+LOG2E = 1.0 / math.log(2.0)
+LN2 = math.log(2.0)
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (FP64, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC",
+                               "-std=c11", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        i64, dbl, p = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        lib.kda_oracle_fwd.argtypes = [i64, p, p, i64, i64, i64, i64, dbl] + [p] * 8
+        lib.kda_oracle_fwd.restype = ctypes.c_int
+        lib.kda_oracle_bwd.argtypes = [i64, p, p, i64, i64, i64, i64, dbl] + [p] * 14
+        lib.kda_oracle_bwd.restype = ctypes.c_int
+        lib.kda_oracle_num_threads.restype = ctypes.c_int
+        lib.kda_oracle_set_threads.argtypes = [ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return _load().kda_oracle_num_threads()
+
+
+def set_threads(n: int) -> None:
+    _load().kda_oracle_set_threads(int(n))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+# --------------------------------------------------------------------------- gate
+
+def softplus(x: np.ndarray) -> np.ndarray:
+    """softplus(x) = log(1 + exp(x)), returning x itself above 20 (PyTorch's
+    default threshold; the pages name softplus without printing a formula)."""
+    x = _f64(x)
+    with np.errstate(over="ignore"):
+        return np.where(x > 20.0, x, np.log1p(np.exp(np.minimum(x, 20.0))))
+
+
+def gate_activation(x: np.ndarray, A_log: Optional[np.ndarray]) -> np.ndarray:
+    """Per-token natural-log decay g = -exp(A_log[hv]) * softplus(x).
+
+    x: [..., HV, K]; A_log: [HV] or None. None means unit scale, which is
+    identical to an explicit zero A_log (PR #1294 Summary)."""
+    x = _f64(x)
+    scale = np.ones(x.shape[-2]) if A_log is None else np.exp(_f64(A_log))
+    return -scale[:, None] * softplus(x)
+
+
+def seq_bounds(B: int, T: int, cu_seqlens: Optional[Sequence[int]]):
+    if cu_seqlens is None:
+        return [(b * T, (b + 1) * T) for b in range(B)]
+    cu = [int(c) for c in cu_seqlens]
+    return [(cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
+
+
+def gate_cumsum_log2(g: np.ndarray, cu_seqlens, chunk_size: int) -> np.ndarray:
+    """Chunk-local inclusive cumsum of the natural-log gate, in log2 units.
+
+    g: [B, T, HV, K] (natural log). Chunks tile each sequence from its own
+    start (dense: each batch row is one sequence); the last chunk of a
+    sequence may be partial. chunk_size=1 gives the per-token log2 decay that
+    the recurrent op consumes. Tokens outside every sequence stay NaN."""
+    g = _f64(g)
+    B, T = g.shape[:2]
+    flat = g.reshape(B * T, *g.shape[2:])
+    out = np.full_like(flat, np.nan)
+    for bos, eos in seq_bounds(B, T, cu_seqlens):
+        for c0 in range(bos, eos, chunk_size):
+            c1 = min(c0 + chunk_size, eos)
+            out[c0:c1] = np.cumsum(flat[c0:c1], axis=0) * LOG2E
+    return out.reshape(g.shape)
+
+
+# --------------------------------------------------------------------------- recurrence
+
+def recurrence(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None):
+    """FP64 token recurrence (C). Shapes: q, k [B,T,H,K]; v [B,T,HV,V];
+    g [B,T,HV,K] natural log; beta [B,T,HV]; h0 [N,HV,K,V] or None.
+    Returns (o [B,T,HV,V] with NaN outside every sequence, ht [N,HV,K,V])."""
+    q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    bounds = seq_bounds(B, T, cu_seqlens)
+    N = len(bounds)
+    bos = np.array([b for b, _ in bounds], dtype=np.int64)
+    eos = np.array([e for _, e in bounds], dtype=np.int64)
+    h0d = None if h0 is None else _f64(h0)
+    if h0d is not None:
+        assert h0d.shape == (N, HV, K, V)
+    o = np.full((B, T, HV, V), np.nan)
+    ht = np.zeros((N, HV, K, V))
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    rc = _load().kda_oracle_fwd(N, _ptr(bos), _ptr(eos), H, HV, K, V, float(scale),
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0d),
+                                _ptr(o), _ptr(ht))
+    if rc != 0:
+        raise ValueError("kda_oracle_fwd rejected its arguments")
+    return o, ht
+
+
+def recurrence_bwd(q, k, v, g, beta, do, h0=None, dht=None, cu_seqlens=None, scale=None):
+    """Reverse pass of `recurrence`. Returns dict dq, dk, dv, dg, dbeta, dh0 (FP64)."""
+    q, k, v, g, beta, do = (_f64(a) for a in (q, k, v, g, beta, do))
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    bounds = seq_bounds(B, T, cu_seqlens)
+    N = len(bounds)
+    bos = np.array([b for b, _ in bounds], dtype=np.int64)
+    eos = np.array([e for _, e in bounds], dtype=np.int64)
+    h0d = None if h0 is None else _f64(h0)
+    dhtd = None if dht is None else _f64(dht)
+    dq = np.zeros((B, T, H, K)); dk = np.zeros((B, T, H, K))
+    dv = np.zeros((B, T, HV, V)); dg = np.zeros((B, T, HV, K))
+    dbeta = np.zeros((B, T, HV)); dh0 = np.zeros((N, HV, K, V))
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    rc = _load().kda_oracle_bwd(N, _ptr(bos), _ptr(eos), H, HV, K, V, float(scale),
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0d),
+                                _ptr(do), _ptr(dhtd), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                _ptr(dbeta), _ptr(dh0))
+    if rc != 0:
+        raise ValueError("kda_oracle_bwd rejected its arguments")
+    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=dh0)
+
+
+# --------------------------------------------------------------------------- workload helpers
+
+def forward(wl, A_log="workload", h0="workload", g_override=None):
+    """Oracle forward of a `workloads.Workload`: gate activation from the raw
+    x (FP64) and the token recurrence. Returns (o, ht)."""
+    a = wl.A_log if (isinstance(A_log, str) and A_log == "workload") else A_log
+    s = wl.h0 if (isinstance(h0, str) and h0 == "workload") else h0
+    g = gate_activation(wl.x, a) if g_override is None else g_override
+    return recurrence(wl.q, wl.k, wl.v, g, wl.beta, s, wl.cu_seqlens)
+
+
+def backward(wl):
+    g = gate_activation(wl.x, wl.A_log)
+    return recurrence_bwd(wl.q, wl.k, wl.v, g, wl.beta, wl.dO, wl.h0, wl.dht, wl.cu_seqlens)
+
+
+def g_from_log2_cumsum(G2: np.ndarray, cu_seqlens, chunk_size: int) -> np.ndarray:
+    """Inverse of gate_cumsum_log2 on exactly given values: per-token natural-log
+    gate g_t = ln2 * (G2_t - G2_{t-1}) within each chunk (G2_{-1} = 0), in FP64.
+    Lets a stage test feed a given fp32 log2 gate to the recurrence."""
+    G2 = _f64(G2)
+    B, T = G2.shape[:2]
+    flat = G2.reshape(B * T, *G2.shape[2:])
+    out = np.full_like(flat, np.nan)
+    for bos, eos in seq_bounds(B, T, cu_seqlens):
+        for c0 in range(bos, eos, chunk_size):
+            c1 = min(c0 + chunk_size, eos)
+            blk = flat[c0:c1]
+            prev = np.concatenate([np.zeros_like(blk[:1]), blk[:-1]], axis=0)
+            out[c0:c1] = (blk - prev) * LN2
+    return out.reshape(G2.shape)
+
+
+from . import forms  # noqa: E402,F401
