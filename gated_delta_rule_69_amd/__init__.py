@@ -1,0 +1,190 @@
+"""MI355X-native Kimi Delta Attention (KDA) scan: thin Python binding of libkda.
+
+Every step of the computation runs in the HIP kernels of `libkda.so`
+(`csrc/`, built for gfx950 by `build.py`). This module only marshals
+arguments: it reads shapes and device pointers from torch tensors, allocates
+outputs and workspace with torch, and passes torch's current HIP stream. If the
+library is missing it raises; there is no fallback path.
+
+Entry points mirror the C ABI in `include/kda.h` (same names and argument
+order as the `recurrent_kda(q, k, v, gate, beta, initial_state=None, *,
+cu_seqlens=None, output_final_state=False)` contract described in "kda in
+torchtitan (training)", quoted attention-gym description):
+  gate_cumsum     step A1  (kda_gate_cumsum)
+  chunk_kda       steps A2..A6 (kda_chunk_fwd)
+  recurrent_kda   step A7  (kda_recurrent_fwd)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_FP32, KDA_BF16 = 0, 1
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
+           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_ALIAS", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_LAUNCH"}
+
+EXPORTED = ("kda_status_string", "kda_gate_cumsum", "kda_chunk_fwd_workspace_bytes",
+            "kda_chunk_fwd", "kda_recurrent_fwd")
+
+
+class KdaDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "T", "N", "H", "HV", "K", "V")]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {_STATUS.get(code, code)} ({_lib().kda_status_string(code).decode()})")
+        self.code = code
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m gated_delta_rule_69_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        p, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        dims = ctypes.POINTER(KdaDims)
+        lib.kda_status_string.argtypes = [ctypes.c_int]
+        lib.kda_status_string.restype = ctypes.c_char_p
+        lib.kda_gate_cumsum.argtypes = [dims, p, i32, p, p, i32, p, p]
+        lib.kda_gate_cumsum.restype = ctypes.c_int
+        lib.kda_chunk_fwd_workspace_bytes.argtypes = [dims, ctypes.c_int, i32]
+        lib.kda_chunk_fwd_workspace_bytes.restype = sz
+        lib.kda_chunk_fwd.argtypes = [dims, ctypes.c_int, p, p, p, p, p, p, p, i32, i32, p, p, p, sz, p]
+        lib.kda_chunk_fwd.restype = ctypes.c_int
+        lib.kda_recurrent_fwd.argtypes = [dims, ctypes.c_int, p, p, p, p, p, p, p, i32, p, p, p]
+        lib.kda_recurrent_fwd.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def load() -> ctypes.CDLL:
+    """Load libkda.so (raises if it is not built)."""
+    return _lib()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dims(q, v, cu_seqlens) -> KdaDims:
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    return KdaDims(B, T, N, H, HV, K, V)
+
+
+def gate_cumsum(gate_in: torch.Tensor, A_log: Optional[torch.Tensor] = None,
+                cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
+                is_raw: bool = True, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Step A1 (kda_gate_cumsum): [B, T, HV, K] FP32 raw gate input x (or the
+    natural-log g if is_raw=False) -> chunk-local inclusive cumsum in log2 units."""
+    for t, n in ((gate_in, "gate_in"), (A_log, "A_log"), (cu_seqlens, "cu_seqlens"), (out, "out")):
+        _check(t, n)
+    B, T, HV, K = gate_in.shape
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    d = KdaDims(B, T, N, 1, HV, K, 1)
+    if out is None:
+        out = torch.empty_like(gate_in)
+    rc = _lib().kda_gate_cumsum(ctypes.byref(d), _ptr(gate_in), int(is_raw), _ptr(A_log),
+                                _ptr(cu_seqlens), int(chunk_size), _ptr(out), _stream())
+    if rc:
+        raise KdaError("kda_gate_cumsum", rc)
+    return out
+
+
+def chunk_workspace_bytes(q: torch.Tensor, v: torch.Tensor, cu_seqlens=None, chunk_size: int = 64) -> int:
+    d = _dims(q, v, cu_seqlens)
+    return int(_lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(d), _dtype_code(q), int(chunk_size)))
+
+
+def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
+              output_final_state: bool = False, chunk_size: int = 64,
+              o: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Steps A2..A6 (kda_chunk_fwd). `gate` is the chunk-local cumulative log2
+    gate (gate_cumsum with the same chunk_size). Returns (o, final_state)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"),
+                 (initial_state, "initial_state"), (cu_seqlens, "cu_seqlens")):
+        _check(t, n)
+    d = _dims(q, v, cu_seqlens)
+    dt = _dtype_code(q)
+    if o is None:
+        o = torch.empty_like(v)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((d.N, d.HV, d.K, d.V), device=q.device, dtype=torch.float32)
+    if not output_final_state:
+        final_state = None
+    need = int(_lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(d), dt, int(chunk_size)))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    rc = _lib().kda_chunk_fwd(ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+                              _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size),
+                              int(bool(output_final_state)), _ptr(o), _ptr(final_state),
+                              _ptr(workspace), workspace.numel(), _stream())
+    if rc:
+        raise KdaError("kda_chunk_fwd", rc)
+    return o, final_state
+
+
+def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
+                  output_final_state: bool = False, o: Optional[torch.Tensor] = None,
+                  final_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Step A7 (kda_recurrent_fwd). `gate` is the per-token log2 decay
+    (gate_cumsum with chunk_size=1). Inference only: inputs that require grad
+    are rejected (use chunk_kda for training). Pass final_state=initial_state
+    to update the states in place."""
+    if any(t is not None and t.requires_grad for t in (q, k, v, gate, beta, initial_state)):
+        raise RuntimeError("recurrent_kda is inference-only; inputs require grad (use chunk_kda)")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"),
+                 (initial_state, "initial_state"), (cu_seqlens, "cu_seqlens")):
+        _check(t, n)
+    d = _dims(q, v, cu_seqlens)
+    dt = _dtype_code(q)
+    if o is None:
+        o = torch.empty_like(v)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((d.N, d.HV, d.K, d.V), device=q.device, dtype=torch.float32)
+    if not output_final_state:
+        final_state = None
+    rc = _lib().kda_recurrent_fwd(ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+                                  _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+                                  int(bool(output_final_state)), _ptr(o), _ptr(final_state), _stream())
+    if rc:
+        raise KdaError("kda_recurrent_fwd", rc)
+    return o, final_state
+
+
+__all__ = ["gate_cumsum", "chunk_kda", "recurrent_kda", "chunk_workspace_bytes", "load",
+           "KdaDims", "KdaError", "LIB_PATH", "EXPORTED", "KDA_FP32", "KDA_BF16"]

@@ -1,0 +1,153 @@
+// C ABI of libkda: argument validation, then kernel launches on the caller's stream.
+#include <stdint.h>
+
+#include "kda_common.h"
+
+namespace {
+
+bool valid_dtype(kda_dtype dt) { return dt == KDA_FP32 || dt == KDA_BF16; }
+size_t esize(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
+
+// [a, a + na) and [b, b + nb) overlap (byte ranges; empty ranges never overlap)
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+kda_status check_dims(const kda_dims* d, const int32_t* cu) {
+  if (!d) return KDA_ERR_NULL;
+  if (d->B < 0 || d->T < 0 || d->N < 0 || d->H <= 0 || d->HV <= 0 || d->K <= 0 || d->V <= 0)
+    return KDA_ERR_SHAPE;
+  if (d->HV % d->H != 0) return KDA_ERR_SHAPE;
+  if (cu) {
+    if (d->B != 1) return KDA_ERR_SHAPE;
+  } else {
+    if (d->N != d->B) return KDA_ERR_SHAPE;
+  }
+  return KDA_OK;
+}
+
+struct Sizes {
+  size_t qk, v, beta, gate, state;
+};
+
+Sizes sizes(const kda_dims* d, kda_dtype dt) {
+  const size_t tok = (size_t)d->B * d->T;
+  Sizes s;
+  s.qk = tok * d->H * d->K * esize(dt);
+  s.v = tok * d->HV * d->V * esize(dt);
+  s.beta = tok * d->HV * esize(dt);
+  s.gate = tok * d->HV * d->K * sizeof(float);
+  s.state = (size_t)d->N * d->HV * d->K * d->V * sizeof(float);
+  return s;
+}
+
+// Shared checks of the two scan entry points.
+kda_status check_scan(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                      const void* v, const float* gate, const void* beta,
+                      const float* h0, const int32_t* cu, int32_t write_final, const void* o,
+                      const float* ht) {
+  kda_status st = check_dims(d, cu);
+  if (st != KDA_OK) return st;
+  if (!valid_dtype(dt)) return KDA_ERR_DTYPE;
+  const bool has_tokens = (size_t)d->B * d->T > 0;
+  if (has_tokens && (!q || !k || !v || !gate || !beta || !o)) return KDA_ERR_NULL;
+  if (write_final && !ht && d->N > 0) return KDA_ERR_NULL;
+  const Sizes s = sizes(d, dt);
+  // final_state may equal initial_state exactly; no other overlap
+  if (h0 && ht && h0 != (const float*)ht && overlaps(h0, s.state, ht, s.state)) return KDA_ERR_ALIAS;
+  const void* ins[] = {q, k, v, gate, beta, h0};
+  const size_t ins_n[] = {s.qk, s.qk, s.v, s.gate, s.beta, s.state};
+  for (int i = 0; i < 6; ++i) {
+    if (overlaps(o, s.v, ins[i], ins_n[i])) return KDA_ERR_ALIAS;
+    if (ht && ins[i] != h0 && overlaps(ht, s.state, ins[i], ins_n[i])) return KDA_ERR_ALIAS;
+  }
+  if (ht && overlaps(o, s.v, ht, s.state)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "required pointer is NULL";
+    case KDA_ERR_SHAPE: return "inconsistent sizes";
+    case KDA_ERR_DTYPE: return "unknown dtype";
+    case KDA_ERR_UNSUPPORTED: return "unsupported size or chunk_size";
+    case KDA_ERR_ALIAS: return "forbidden buffer overlap";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+kda_status kda_gate_cumsum(const kda_dims* d, const float* gate_in, int32_t gate_in_is_raw,
+                           const float* A_log, const int32_t* cu, int32_t chunk_size,
+                           float* gate_out, hipStream_t stream) {
+  kda_status st = check_dims(d, cu);
+  if (st != KDA_OK) return st;
+  if (chunk_size < 1 || chunk_size > 64) return KDA_ERR_UNSUPPORTED;
+  if (!gate_in_is_raw && A_log) return KDA_ERR_SHAPE;
+  const size_t n = (size_t)d->B * d->T * d->HV * d->K;
+  if (n == 0) return KDA_OK;
+  if (!gate_in || !gate_out) return KDA_ERR_NULL;
+  // in place only for per-token output (a chunk may start inside another tile)
+  if (overlaps(gate_in, n * 4, gate_out, n * 4) && !(chunk_size == 1 && gate_in == gate_out))
+    return KDA_ERR_ALIAS;
+  if (A_log && overlaps(A_log, (size_t)d->HV * 4, gate_out, n * 4)) return KDA_ERR_ALIAS;
+  return kda_host::launch_gate(*d, gate_in, gate_in_is_raw ? 1 : 0, A_log, cu, chunk_size,
+                               gate_out, stream) == hipSuccess
+             ? KDA_OK
+             : KDA_ERR_LAUNCH;
+}
+
+size_t kda_chunk_fwd_workspace_bytes(const kda_dims* d, kda_dtype dt, int32_t chunk_size) {
+  if (!d || !valid_dtype(dt) || chunk_size != 64) return 0;
+  if (!((d->K == 64 || d->K == 128) && (d->V == 64 || d->V == 128))) return 0;
+  if (d->N < 0 || d->T < 0 || d->B < 0 || d->HV <= 0) return 0;
+  return kda_host::chunk_workspace_bytes(*d, dt, chunk_size);
+}
+
+kda_status kda_chunk_fwd(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                         const void* v, const float* gate, const void* beta,
+                         const float* h0, const int32_t* cu, int32_t chunk_size,
+                         int32_t write_final, void* o, float* ht, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  kda_status st = check_scan(d, dt, q, k, v, gate, beta, h0, cu, write_final, o, ht);
+  if (st != KDA_OK) return st;
+  if (chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+  if (!((d->K == 64 || d->K == 128) && (d->V == 64 || d->V == 128))) return KDA_ERR_UNSUPPORTED;
+  if (d->N == 0) return KDA_OK;
+  const size_t need = kda_host::chunk_workspace_bytes(*d, dt, chunk_size);
+  if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  const Sizes s = sizes(d, dt);
+  if (overlaps(workspace, need, o, s.v) || overlaps(workspace, need, ht, s.state) ||
+      overlaps(workspace, need, h0, s.state) || overlaps(workspace, need, q, s.qk) ||
+      overlaps(workspace, need, k, s.qk) || overlaps(workspace, need, v, s.v) ||
+      overlaps(workspace, need, gate, s.gate) || overlaps(workspace, need, beta, s.beta))
+    return KDA_ERR_ALIAS;
+  return kda_host::launch_chunk_fwd(*d, dt, q, k, v, gate, beta, h0, cu, write_final ? 1 : 0, o,
+                                    ht, workspace, workspace_bytes, stream) == hipSuccess
+             ? KDA_OK
+             : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_recurrent_fwd(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                             const void* v, const float* gate, const void* beta,
+                             const float* h0, const int32_t* cu, int32_t write_final, void* o,
+                             float* ht, hipStream_t stream) {
+  kda_status st = check_scan(d, dt, q, k, v, gate, beta, h0, cu, write_final, o, ht);
+  if (st != KDA_OK) return st;
+  if (d->K > 256 || d->V > 256) return KDA_ERR_UNSUPPORTED;
+  if (d->N == 0) return KDA_OK;
+  return kda_host::launch_recurrent(*d, dt, q, k, v, gate, beta, h0, cu, write_final ? 1 : 0, o,
+                                    ht, stream) == hipSuccess
+             ? KDA_OK
+             : KDA_ERR_LAUNCH;
+}
+
+}  // extern "C"

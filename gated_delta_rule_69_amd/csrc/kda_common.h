@@ -1,0 +1,106 @@
+// Shared device helpers for the libkda kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Matrix-core tile traits for a 16x16 output tile with FP32 accumulation.
+//
+// Fragment layout (checked on gfx950): for a step of KSTEP contraction
+// indices, lane l (g = l / 16) feeds row (A) or column (B) l % 16 with PER
+// consecutive slots; the accumulator lane l holds rows 4g + i (i = 0..3) of
+// column l % 16.
+//
+// The contraction index carried by slot j of lane group g in step ks is
+// kidx(ks, g, j). It is permuted on purpose: with this order the accumulator
+// of a product X^T (two stacked 16-row tiles for bf16, one tile for FP32) is
+// already the A fragment of X, so results feed the next product without an
+// LDS round trip. Both operands of one product always use the same order.
+template <typename T>
+struct MF;
+
+template <>
+struct MF<bf16> {
+  static constexpr int KSTEP = 32;
+  static constexpr int PER = 8;
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ int kidx(int ks, int g, int j) {
+    return 32 * ks + (j < 4 ? 4 * g + j : 12 + 4 * g + j);
+  }
+  static __device__ __forceinline__ f32x4 mma(const frag& a, const frag& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void set(frag& f, int j, float x) { f[j] = (bf16)x; }
+  static __device__ __forceinline__ float get(const frag& f, int j) { return (float)f[j]; }
+};
+
+struct f32x1 {
+  float v;
+};
+
+template <>
+struct MF<float> {
+  static constexpr int KSTEP = 4;
+  static constexpr int PER = 1;
+  typedef f32x1 frag;
+  static __device__ __forceinline__ int kidx(int ks, int g, int /*j*/) {
+    return 16 * (ks >> 2) + 4 * g + (ks & 3);
+  }
+  static __device__ __forceinline__ f32x4 mma(const frag& a, const frag& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a.v, b.v, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void set(frag& f, int, float x) { f.v = x; }
+  static __device__ __forceinline__ float get(const frag& f, int) { return f.v; }
+};
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Flat offset of the first token of dense/varlen sequence n, and its length.
+__device__ __forceinline__ void seq_range(const int32_t* cu, int n, int T, int64_t* bos, int* len) {
+  if (cu) {
+    int a = cu[n], b = cu[n + 1];
+    *bos = a;
+    *len = b - a;
+  } else {
+    *bos = (int64_t)n * T;
+    *len = T;
+  }
+}
+
+}  // namespace kda
+
+// Host-side launchers (defined in the .hip files, called by the C ABI).
+namespace kda_host {
+hipError_t launch_gate(const kda_dims& d, const float* in, int is_raw, const float* A_log,
+                       const int32_t* cu, int chunk, float* out, hipStream_t s);
+hipError_t launch_recurrent(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
+                            const void* v, const float* gate, const void* beta,
+                            const float* h0, const int32_t* cu, int write_final, void* o,
+                            float* ht, hipStream_t s);
+size_t chunk_workspace_bytes(const kda_dims& d, kda_dtype dt, int chunk);
+hipError_t launch_chunk_fwd(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
+                            const void* v, const float* gate, const void* beta,
+                            const float* h0, const int32_t* cu, int write_final, void* o,
+                            float* ht, void* ws, size_t ws_bytes, hipStream_t s);
+}  // namespace kda_host

@@ -1,0 +1,142 @@
+/*
+ * kda.h -- C ABI of libkda, the MI355X (gfx950) Kimi Delta Attention scan.
+ *
+ * The operation (per value head hv of a sequence, with qk head h = hv / (HV/H)):
+ *   S_t = (I - beta_t k_t k_t^T) Diag(2^{gate_t}) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = S_t^T (q_t / sqrt(K))
+ * with S_t a K x V FP32 state. This is the gated delta rule with a
+ * per-channel decay (KDA). Sources on the pages:
+ *   - "kda in torchtitan (training)", pytorch/torchtitan PR #4164, the quoted
+ *     attention-gym description of `recurrent_kda`: the argument contract
+ *     (q, k, v, gate, beta, initial_state, cu_seqlens, output_final_state),
+ *     device-resident int32 cu_seqlens, repeated offsets as empty slots whose
+ *     state passes through bitwise, a capacity tail outside the contract, FP32
+ *     states with one leading entry per logical sequence, the gate as a
+ *     per-token log2 decay (chunk-local cumulative for the chunked op), the
+ *     internal 1/sqrt(K) query scale, FP32 compute for any input dtype.
+ *   - "[Fix] Use unit KDA gate scale when A_log is omitted", fla-org
+ *     flash-linear-attention PR #1294, Summary and Breaking changes: decay
+ *     scale exp(A_log), omitted A_log = unit scale = explicit zero A_log.
+ *   - same page, squashed commit bodies: the chunked pipeline steps (kkt,
+ *     solve_tril, recompute_w_u, fwd_h, fwd_o) of the sibling gated delta
+ *     rule op, which kda_chunk_fwd follows for a per-channel gate.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major arrays.
+ *     Dense layout: q, k [B, T, H, K]; v, o [B, T, HV, V]; gate [B, T, HV, K]
+ *     FP32; beta [B, T, HV] (same dtype as q); states [N, HV, K, V] FP32.
+ *   - Dense mode: cu_seqlens == NULL and N == B; batch row b is one sequence.
+ *     Varlen mode: cu_seqlens is a device int32 array of N+1 non-decreasing
+ *     offsets with cu_seqlens[0] == 0 and cu_seqlens[N] <= T; B must be 1.
+ *     Sequence n covers tokens [cu_seqlens[n], cu_seqlens[n+1]); an empty
+ *     range is an empty slot. Tokens in [cu_seqlens[N], T) (the capacity
+ *     tail) are neither read nor written. The offsets are NOT validated
+ *     (reading them would force a host sync); violating the preconditions is
+ *     undefined behaviour.
+ *   - Empty slot: no output row; if output_final_state, final_state[n] is a
+ *     bitwise copy of initial_state[n] (or +0.0 when initial_state is NULL).
+ *   - final_state may equal initial_state (in-place update); any other
+ *     overlap between them, or between o and an input, is KDA_ERR_ALIAS.
+ *   - The caller owns every buffer. The library allocates nothing, keeps no
+ *     global state and never synchronises: each call only enqueues work on
+ *     `stream`, and results are valid once that stream has been synchronised.
+ *   - Host-checkable errors return before anything is enqueued. A failed
+ *     kernel launch returns KDA_ERR_LAUNCH.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL */
+  KDA_ERR_SHAPE = 2,       /* inconsistent sizes (HV % H != 0, N != B dense, B != 1 varlen, ...) */
+  KDA_ERR_DTYPE = 3,       /* unknown dtype code */
+  KDA_ERR_UNSUPPORTED = 4, /* valid but not implemented (K, V, chunk_size) */
+  KDA_ERR_ALIAS = 5,       /* forbidden overlap between buffers */
+  KDA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
+  KDA_ERR_LAUNCH = 7       /* the HIP runtime refused a launch */
+} kda_status;
+
+/* Element type of q, k, v, beta and o. States and gates are always FP32. */
+typedef enum { KDA_FP32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Problem sizes. T is the physical token extent per batch row (the capacity
+ * in varlen mode); N is the number of state entries (B dense, len(cu)-1 varlen). */
+typedef struct {
+  int32_t B, T, N, H, HV, K, V;
+} kda_dims;
+
+/* Human-readable name of a status code (static storage). */
+const char* kda_status_string(kda_status s);
+
+/*
+ * kda_gate_cumsum -- step A1: gate activation and chunk-local cumsum.
+ *   gate_in  [B, T, HV, K] FP32. If gate_in_is_raw != 0 it holds the raw
+ *            activation input x and the per-token natural-log decay is
+ *            g = -exp(A_log[hv]) * softplus(x), softplus(x) = ln(1 + e^x)
+ *            (x itself for x > 20); A_log [HV] FP32 or NULL for unit scale,
+ *            bitwise identical to an all-zero A_log. If gate_in_is_raw == 0,
+ *            gate_in already holds the natural-log g and A_log must be NULL.
+ *   gate_out [B, T, HV, K] FP32: log2(e) * inclusive cumsum of g inside each
+ *            chunk, chunks tiling every sequence from its own first token
+ *            (the last chunk may be partial). chunk_size == 1 gives the
+ *            per-token log2 decay consumed by kda_recurrent_fwd; chunk_size
+ *            == 64 gives the input of kda_chunk_fwd. gate_out may equal gate_in.
+ *   Supports chunk_size in [1, 64] (ordinarily 1 or 64), any K, HV.
+ */
+kda_status kda_gate_cumsum(const kda_dims* dims, const float* gate_in, int32_t gate_in_is_raw,
+                           const float* A_log, const int32_t* cu_seqlens, int32_t chunk_size,
+                           float* gate_out, hipStream_t stream);
+
+/* Workspace bytes kda_chunk_fwd needs for these sizes (0 on unsupported input). */
+size_t kda_chunk_fwd_workspace_bytes(const kda_dims* dims, kda_dtype dtype, int32_t chunk_size);
+
+/*
+ * kda_chunk_fwd -- steps A2..A6: the chunked scan (chunk_kda forward).
+ *   gate   [B, T, HV, K] FP32 chunk-local cumulative log2 gate, i.e. the
+ *          output of kda_gate_cumsum with the same chunk_size and cu_seqlens.
+ *   initial_state [N, HV, K, V] FP32 or NULL (zeros).
+ *   o      [B, T, HV, V] in `dtype`; rows outside every sequence untouched.
+ *   final_state [N, HV, K, V] FP32, required iff output_final_state != 0
+ *          (may equal initial_state).
+ *   workspace: device scratch of at least kda_chunk_fwd_workspace_bytes();
+ *          its contents are scratch on entry and on return.
+ *   Supported: K, V in {64, 128}; chunk_size == 64; FP32 or BF16.
+ *   Arithmetic: FP32 accumulation and FP32 state; for BF16 inputs the
+ *   matrix products take bf16 operands on the matrix cores.
+ */
+kda_status kda_chunk_fwd(const kda_dims* dims, kda_dtype dtype, const void* q, const void* k,
+                         const void* v, const float* gate, const void* beta,
+                         const float* initial_state, const int32_t* cu_seqlens,
+                         int32_t chunk_size, int32_t output_final_state, void* o,
+                         float* final_state, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * kda_recurrent_fwd -- step A7: the token-sequential scan (recurrent_kda).
+ *   gate   [B, T, HV, K] FP32 per-token log2 decay (kda_gate_cumsum with
+ *          chunk_size == 1).
+ *   Other arguments as kda_chunk_fwd. Computes in FP32 for any input dtype.
+ *   Supported: 1 <= K, V <= 256 (any value, not only powers of two).
+ *   Decode is the T-per-sequence == 1 case; final_state == initial_state
+ *   updates the states in place.
+ */
+kda_status kda_recurrent_fwd(const kda_dims* dims, kda_dtype dtype, const void* q, const void* k,
+                             const void* v, const float* gate, const void* beta,
+                             const float* initial_state, const int32_t* cu_seqlens,
+                             int32_t output_final_state, void* o, float* final_state,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

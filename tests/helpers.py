@@ -1,0 +1,98 @@
+"""Shared helpers of the GPU parity tests: moving workloads to the device and
+the error measures the tolerances are stated in."""
+import math
+
+import numpy as np
+import torch
+
+import workloads
+
+DEV = "cuda:0"
+
+# Tolerances of the parity bar: FP32 inputs, max error normwise; bf16 inputs
+# with FP32 accumulation, relative RMS on outputs and on final states.
+TOL_FP32 = 2e-5
+TOL_BF16_O = 5e-3
+TOL_BF16_STATE = 1e-2
+
+
+def normwise_max_err(x, ref):
+    """max |x - ref| / max |ref| over the in-contract elements (FP64)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(x - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+def rel_rms(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def tdtype(wl):
+    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+
+def to_dev(a, dtype=torch.float32):
+    if a is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(dtype).contiguous()
+
+
+def device_inputs(wl):
+    """Device tensors of a workload: q, k, v, beta in the workload dtype, x,
+    A_log, h0 FP32, cu_seqlens int32."""
+    dt = tdtype(wl)
+    d = dict(q=to_dev(wl.q, dt), k=to_dev(wl.k, dt), v=to_dev(wl.v, dt), beta=to_dev(wl.beta, dt),
+             x=to_dev(wl.x), A_log=to_dev(wl.A_log), h0=to_dev(wl.h0))
+    d["cu"] = None if wl.cu_seqlens is None else torch.from_numpy(wl.cu_seqlens.astype(np.int32)).to(DEV)
+    return d
+
+
+def in_contract_rows(wl):
+    """Boolean mask [B, T] of token rows inside some sequence."""
+    m = np.zeros((wl.B, wl.T), dtype=bool)
+    if wl.cu_seqlens is None:
+        m[:] = True
+    else:
+        m[0, : int(wl.cu_seqlens[-1])] = True
+    return m
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def run_gpu(wl, d, path, in_place=False, o_fill=None):
+    """Whole GPU path from the raw gate: kda_gate_cumsum then the scan.
+    path: "chunk" (chunk_size 64) or "recurrent" (chunk_size 1)."""
+    import gated_delta_rule_69_amd as kda
+    chunk = 64 if path == "chunk" else 1
+    G = kda.gate_cumsum(d["x"], d["A_log"], d["cu"], chunk)
+    o = None
+    if o_fill is not None:
+        o = torch.full_like(d["v"], o_fill)
+    h0 = d["h0"]
+    if path == "chunk":
+        out, ht = kda.chunk_kda(d["q"], d["k"], d["v"], G, d["beta"], h0, cu_seqlens=d["cu"],
+                                output_final_state=True, o=o)
+    else:
+        fs = h0 if (in_place and h0 is not None) else None
+        out, ht = kda.recurrent_kda(d["q"], d["k"], d["v"], G, d["beta"], h0, cu_seqlens=d["cu"],
+                                    output_final_state=True, o=o, final_state=fs)
+    torch.cuda.synchronize()
+    return out, ht
+
+
+def check_parity(wl, o, ht, o_ref, ht_ref, label=""):
+    """Assert the parity bar; returns the measured errors."""
+    mask = in_contract_rows(wl)
+    og, orf = to_np(o)[mask], o_ref[mask]
+    hg = to_np(ht)
+    if wl.dtype == "fp32":
+        eo, eh = normwise_max_err(og, orf), normwise_max_err(hg, ht_ref)
+        assert eo <= TOL_FP32 and eh <= TOL_FP32, (label, eo, eh)
+    else:
+        eo, eh = rel_rms(og, orf), rel_rms(hg, ht_ref)
+        assert eo <= TOL_BF16_O and eh <= TOL_BF16_STATE, (label, eo, eh)
+    return eo, eh

@@ -1,0 +1,96 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+that include/kda.h declares, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_69_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    assert set(_declared()) == set(kda.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kda.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = kda.load()
+    for code in range(8):
+        assert lib.kda_status_string(code)
+
+
+FAKE = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(16)]  # never dereferenced
+
+
+def _dims(**kw):
+    d = dict(B=1, T=64, N=1, H=1, HV=1, K=64, V=64)
+    d.update(kw)
+    return kda.KdaDims(**d)
+
+
+def _chunk(lib, d, dt=1, chunk=64, ws=None, ws_bytes=1 << 40, h0=None, ht=None, o=None, cu=None, fin=1):
+    return lib.kda_chunk_fwd(ctypes.byref(d), dt, FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4],
+                             h0, cu, chunk, fin, o if o is not None else FAKE[5],
+                             ht if ht is not None else FAKE[6],
+                             ws if ws is not None else FAKE[7], ws_bytes, None)
+
+
+def test_chunk_rejects_bad_arguments():
+    lib = kda.load()
+    assert lib.kda_chunk_fwd(None, 1, *[None] * 7, 64, 0, None, None, None, 0, None) == 1  # NULL dims
+    assert _chunk(lib, _dims(H=2, HV=3)) == 2  # HV % H != 0
+    assert _chunk(lib, _dims(N=2)) == 2  # dense needs N == B
+    assert _chunk(lib, _dims(B=2, N=2), cu=FAKE[8]) == 2  # varlen needs B == 1
+    assert _chunk(lib, _dims(), dt=7) == 3  # dtype
+    assert _chunk(lib, _dims(), chunk=32) == 4  # chunk size
+    assert _chunk(lib, _dims(K=96)) == 4  # head dim
+    assert _chunk(lib, _dims(), ws_bytes=16) == 6  # workspace too small
+    assert _chunk(lib, _dims(), o=FAKE[0]) == 5  # o aliases q
+    assert _chunk(lib, _dims(), h0=ctypes.c_void_p(0x10000 * 7 + 64)) == 5  # partial state overlap
+    d = _dims()
+    assert lib.kda_chunk_fwd(ctypes.byref(d), 1, FAKE[0], None, FAKE[2], FAKE[3], FAKE[4], None, None,
+                             64, 0, FAKE[5], None, FAKE[7], 1 << 40, None) == 1  # k NULL
+    assert lib.kda_chunk_fwd(ctypes.byref(d), 1, FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, None,
+                             64, 1, FAKE[5], None, FAKE[7], 1 << 40, None) == 1  # final_state NULL
+
+
+def test_recurrent_rejects_bad_arguments():
+    lib = kda.load()
+    d = _dims(K=300)
+    assert lib.kda_recurrent_fwd(ctypes.byref(d), 0, FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4],
+                                 None, None, 0, FAKE[5], None, None) == 4
+    d = _dims(H=3, HV=4)
+    assert lib.kda_recurrent_fwd(ctypes.byref(d), 0, FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4],
+                                 None, None, 0, FAKE[5], None, None) == 2
+
+
+def test_gate_rejects_bad_arguments():
+    lib = kda.load()
+    d = _dims()
+    assert lib.kda_gate_cumsum(ctypes.byref(d), FAKE[0], 1, None, None, 0, FAKE[1], None) == 4
+    assert lib.kda_gate_cumsum(ctypes.byref(d), FAKE[0], 1, None, None, 65, FAKE[1], None) == 4
+    assert lib.kda_gate_cumsum(ctypes.byref(d), FAKE[0], 0, FAKE[2], None, 64, FAKE[1], None) == 2
+    assert lib.kda_gate_cumsum(ctypes.byref(d), FAKE[0], 1, None, None, 64, FAKE[0], None) == 5
+
+
+def test_workspace_bytes():
+    lib = kda.load()
+    d = _dims(B=4, T=4096, N=4, H=16, HV=16, K=128, V=128)
+    b = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d), 1, 64)
+    assert b > 4 * 64 * 16 * 64 * 128 * 2
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d), 1, 32) == 0

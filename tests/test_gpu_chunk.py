@@ -1,0 +1,125 @@
+"""GPU parity of steps A1..A6 (kda_gate_cumsum + kda_chunk_fwd) against the FP64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_69_amd as kda
+import oracle
+import workloads
+from helpers import (DEV, check_parity, device_inputs, in_contract_rows, rel_rms, run_gpu, to_np,
+                     normwise_max_err, TOL_FP32)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dense", [False, True])
+def test_tiny_fp32_chunk(dense):
+    wl = workloads.workload1(dense=dense)
+    d = device_inputs(wl)
+    o, ht = run_gpu(wl, d, "chunk")
+    o_ref, ht_ref = oracle.forward(wl)
+    check_parity(wl, o, ht, o_ref, ht_ref, "tiny")
+
+
+@pytest.mark.parametrize("K,V", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_ragged_multi_chunk(K, V, dtype):
+    # 3 full chunks + a ragged tail of 9 tokens, two batch rows, GVA
+    wl = workloads.tiny_case(300 + K + V, B=2, T=201, H=1, HV=2, K=K, V=V, dtype=dtype)
+    d = device_inputs(wl)
+    o, ht = run_gpu(wl, d, "chunk")
+    o_ref, ht_ref = oracle.forward(wl)
+    check_parity(wl, o, ht, o_ref, ht_ref, f"{dtype} K{K} V{V}")
+
+
+@pytest.mark.parametrize("gate_scale,A_log", [(1.0, 2.772588722239781), (4.0, 2.772588722239781),
+                                              (0.05, 0.0)])
+def test_strong_and_weak_decay(gate_scale, A_log):
+    """A_log = ln 16 with amplified gate input drives chunk-local log2 cumsums
+    far below -126 (2^G would underflow); near-zero gates barely decay."""
+    wl = workloads.tiny_case(310, B=1, T=130, H=1, HV=2, K=128, V=128, dtype="fp32",
+                             A_log=A_log, gate_scale=gate_scale)
+    d = device_inputs(wl)
+    G = kda.gate_cumsum(d["x"], d["A_log"], None, 64)
+    assert to_np(G).min() < -126 or gate_scale < 1
+    o, ht = run_gpu(wl, d, "chunk")
+    o_ref, ht_ref = oracle.forward(wl)
+    check_parity(wl, o, ht, o_ref, ht_ref, f"scale{gate_scale}")
+    assert np.isfinite(to_np(o)).all() and np.isfinite(to_np(ht)).all()
+
+
+def test_varlen_empty_slots_and_tail():
+    cu = [0, 0, 1, 64, 64, 129, 300, 300]
+    wl = workloads.tiny_case(320, T=330, H=2, HV=4, K=128, V=128, dtype="bf16", cu_seqlens=cu)
+    wl.q[:, 300:] = np.nan
+    wl.k[:, 300:] = np.nan
+    wl.v[:, 300:] = np.nan
+    wl.x[:, 300:] = np.nan
+    wl.beta[:, 300:] = np.nan
+    d = device_inputs(wl)
+    h0_before = d["h0"].clone()
+    o, ht = run_gpu(wl, d, "chunk", o_fill=-3.0)
+    assert (to_np(o)[:, 300:] == -3.0).all()
+    o_ref, ht_ref = oracle.forward(wl)
+    check_parity(wl, o, ht, o_ref, ht_ref, "varlen")
+    for s in (0, 3, 6):
+        assert torch.equal(ht[s].view(torch.int32), h0_before[s].view(torch.int32))
+
+
+def test_zero_initial_state_and_no_final_state():
+    wl = workloads.tiny_case(330, B=2, T=70, H=1, HV=1, K=64, V=64, dtype="bf16", h0=False)
+    d = device_inputs(wl)
+    G = kda.gate_cumsum(d["x"], d["A_log"], None, 64)
+    o, ht = kda.chunk_kda(d["q"], d["k"], d["v"], G, d["beta"], None, output_final_state=False)
+    torch.cuda.synchronize()
+    assert ht is None
+    o_ref, _ = oracle.forward(wl)
+    assert rel_rms(to_np(o), o_ref) < 5e-3
+
+
+def test_in_place_final_state():
+    wl = workloads.tiny_case(331, B=1, T=100, H=1, HV=2, K=64, V=128, dtype="bf16")
+    d = device_inputs(wl)
+    G = kda.gate_cumsum(d["x"], d["A_log"], None, 64)
+    h = d["h0"].clone()
+    o, ht = kda.chunk_kda(d["q"], d["k"], d["v"], G, d["beta"], h, output_final_state=True, final_state=h)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle.forward(wl)
+    check_parity(wl, o, h, o_ref, ht_ref, "inplace")
+
+
+def test_chunk_matches_recurrent_path():
+    """Chunk size 64 and per-token (chunk size 1) forms of the same problem agree."""
+    wl = workloads.tiny_case(340, B=1, T=150, H=1, HV=2, K=64, V=64, dtype="fp32")
+    d = device_inputs(wl)
+    oc, hc = run_gpu(wl, d, "chunk")
+    orr, hr = run_gpu(wl, d, "recurrent")
+    assert normwise_max_err(to_np(oc), to_np(orr)) < 2 * TOL_FP32
+    assert normwise_max_err(to_np(hc), to_np(hr)) < 2 * TOL_FP32
+
+
+def test_packed_equals_separate_bitwise():
+    cu = [0, 70, 70, 200]
+    wl = workloads.tiny_case(350, T=210, H=1, HV=2, K=128, V=128, dtype="bf16", cu_seqlens=cu)
+    d = device_inputs(wl)
+    o, ht = run_gpu(wl, d, "chunk")
+    for n, (a, b) in enumerate([(0, 70), (70, 70), (70, 200)]):
+        if a == b:
+            continue
+        sl = slice(a, b)
+        G = kda.gate_cumsum(d["x"][:, sl].contiguous(), d["A_log"], None, 64)
+        o1, h1 = kda.chunk_kda(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
+                               d["v"][:, sl].contiguous(), G, d["beta"][:, sl].contiguous(),
+                               d["h0"][n:n + 1].contiguous(), output_final_state=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o[:, sl].view(torch.int16))
+        assert torch.equal(h1.view(torch.int32), ht[n:n + 1].view(torch.int32))
+
+
+def test_deterministic_rerun():
+    wl = workloads.tiny_case(360, B=2, T=300, H=2, HV=2, K=128, V=128, dtype="bf16")
+    d = device_inputs(wl)
+    o1, h1 = run_gpu(wl, d, "chunk")
+    o2, h2 = run_gpu(wl, d, "chunk")
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(h1.view(torch.int32), h2.view(torch.int32))
