@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+Step = one pass of the forward hot path over one batch of synthetic input:
+  kda_gate_cumsum (raw gate -> chunk-local log2 cumsum) + kda_chunk_fwd
+on the dense workload B=4, T=4096, H=HV=16, K=V=128, bf16 inputs, FP32 state,
+zero initial state, final state returned. value = in-contract tokens / s.
+
+Also measured (same JSON line): recurrent decode on 256 slots (26 empty),
+HV=32, K=V=128, FP32 state updated in place: kda_gate_cumsum(chunk 1) +
+kda_recurrent_fwd, in us/step.
+
+Timing: HIP events on torch's current stream, which is the stream every libkda
+call in this process is enqueued on. Warmup W steps, then exactly K timed
+steps between two device synchronisations.
+
+`roofline` reports the dominant entry point of the step against MI355X's
+8 TB/s HBM peak with algorithmic bytes (inputs read once, outputs written
+once). `cpu_baseline` times the FP64 oracle on the host cores over a bounded
+sample of the same workload (one batch row, all 16 heads).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--decode-steps", type=int, default=200)
+    return p.parse_args()
+
+
+def chunk_fwd_bytes(B, T, H, HV, K, V, esize=2, h0=False, final=True):
+    tok = B * T
+    b = tok * H * K * esize * 2          # q, k
+    b += tok * HV * V * esize * 2        # v in, o out
+    b += tok * HV * esize                # beta
+    b += tok * HV * K * 4                # chunk-local log2 gate (fp32)
+    st = B * HV * K * V * 4
+    b += st if h0 else 0
+    b += st if final else 0
+    return b
+
+
+def gate_bytes(B, T, HV, K):
+    return B * T * HV * K * 4 * 2 + HV * 4
+
+
+def decode_bytes(tokens, H, HV, K, V, esize=2):
+    b = tokens * HV * K * V * 4 * 2                      # state read + write (active slots)
+    b += tokens * (2 * H * K + HV * V * 2 + HV) * esize  # q, k, v, o, beta
+    b += tokens * HV * K * 4                             # per-token log2 gate
+    return b
+
+
+def chunk_fwd_flops(B, T, HV, K, V, C=64):
+    """Useful flops of the chunked forward per token-head (masks counted as
+    half products): A and P (each C/2 x K per token), the solve (C^2/3),
+    W and U (C/2 x (K + V)), then W S, (Q Gamma) S, P Delta (C/2) and the
+    state update Khat^T Delta."""
+    per_tok = (2 * (C / 2) * K * 2          # A, P
+               + (C * C) / 3                # solve (per token share)
+               + 2 * (C / 2) * (K + V)      # W, U
+               + 2 * K * V * 3              # W S, (Q Gamma) S, Khat^T Delta
+               + 2 * (C / 2) * V)           # P Delta
+    return B * T * HV * per_tok
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the KDA scan has no "
+              "multi-GPU path in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_69_amd as kda
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf = torch.bfloat16
+
+    def T_(x, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt)
+
+    # ---------------- chunked forward workload
+    wl = workloads.workload2()
+    B, T, H, HV, K, V = wl.B, wl.T, wl.H, wl.HV, wl.K, wl.V
+    q, k, v, beta = T_(wl.q, bf), T_(wl.k, bf), T_(wl.v, bf), T_(wl.beta, bf)
+    x, A_log = T_(wl.x), T_(wl.A_log)
+    G = torch.empty_like(x)
+    o = torch.empty_like(v)
+    ht = torch.empty((B, HV, K, V), device=dev, dtype=torch.float32)
+    ws = torch.empty(kda.chunk_workspace_bytes(q, v), device=dev, dtype=torch.uint8)
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    gate_ms, chunk_ms = [], []
+
+    def step(record):
+        if record:
+            ev[0].record()
+        kda.gate_cumsum(x, A_log, None, 64, out=G)
+        if record:
+            ev[1].record()
+        kda.chunk_kda(q, k, v, G, beta, None, output_final_state=True, o=o, final_state=ht,
+                      workspace=ws)
+        if record:
+            ev[2].record()
+
+    for _ in range(a.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step(False)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / a.steps
+    # per-entry-point durations with events (separate pass, same work)
+    for _ in range(a.steps):
+        step(True)
+        torch.cuda.synchronize()
+        gate_ms.append(ev[0].elapsed_time(ev[1]))
+        chunk_ms.append(ev[1].elapsed_time(ev[2]))
+    tokens = B * T
+    value = tokens / (ms_per_step / 1e3)
+    g_ms, c_ms = float(np.median(gate_ms)), float(np.median(chunk_ms))
+
+    cb = chunk_fwd_bytes(B, T, H, HV, K, V)
+    gb = gate_bytes(B, T, HV, K)
+    chunk_gbs = cb / (c_ms * 1e-3) / 1e9
+    gate_gbs = gb / (g_ms * 1e-3) / 1e9
+    flops = chunk_fwd_flops(B, T, HV, K, V)
+    dominant = "kda_chunk_fwd" if c_ms >= g_ms else "kda_gate_cumsum"
+    if dominant == "kda_chunk_fwd":
+        roof = dict(bound="hbm", achieved=round(chunk_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(chunk_gbs / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="kda_chunk_fwd (chunk_intra_kernel + chunk_scan_kernel)",
+                    algorithmic_bytes=cb, avg_ms=round(c_ms, 4),
+                    mfma_tflops=round(flops / (c_ms * 1e-3) / 1e12, 2))
+    else:
+        roof = dict(bound="hbm", achieved=round(gate_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(gate_gbs / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="kda_gate_cumsum (gate_cumsum_kernel)", algorithmic_bytes=gb,
+                    avg_ms=round(g_ms, 4))
+
+    # ---------------- recurrent decode workload
+    wd = workloads.workload4()
+    dq, dk, dv, db = T_(wd.q, bf), T_(wd.k, bf), T_(wd.v, bf), T_(wd.beta, bf)
+    dx, dh = T_(wd.x), T_(wd.h0)
+    dcu = torch.from_numpy(wd.cu_seqlens).to(dev)
+    dG = torch.empty_like(dx)
+    do = torch.empty_like(dv)
+    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def dstep(record):
+        if record:
+            dev_ev[0].record()
+        kda.gate_cumsum(dx, None, dcu, 1, out=dG)
+        if record:
+            dev_ev[1].record()
+        kda.recurrent_kda(dq, dk, dv, dG, db, dh, cu_seqlens=dcu, output_final_state=True, o=do,
+                          final_state=dh)
+        if record:
+            dev_ev[2].record()
+
+    for _ in range(20):
+        dstep(False)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(a.decode_steps):
+        dstep(False)
+    torch.cuda.synchronize()
+    dec_us = (time.perf_counter() - t1) * 1e6 / a.decode_steps
+    rec_ms = []
+    for _ in range(min(a.decode_steps, 100)):
+        dstep(True)
+        torch.cuda.synchronize()
+        rec_ms.append(dev_ev[1].elapsed_time(dev_ev[2]))
+    rec_us = float(np.median(rec_ms)) * 1e3
+    ntok = int(wd.cu_seqlens[-1])
+    dbytes = decode_bytes(ntok, wd.H, wd.HV, wd.K, wd.V)
+    rec_gbs = dbytes / (rec_us * 1e-6) / 1e9
+
+    # ---------------- CPU baseline: the FP64 oracle on one batch row, all heads
+    cpu = None
+    if not a.no_cpu_baseline:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
+        oracle.set_threads(threads)
+        Ts = T
+        sl = dict(q=wl.q[:1, :Ts], k=wl.k[:1, :Ts], v=wl.v[:1, :Ts], beta=wl.beta[:1, :Ts],
+                  x=wl.x[:1, :Ts])
+        c0 = time.perf_counter()
+        g = oracle.gate_activation(sl["x"], wl.A_log)
+        oracle.recurrence(sl["q"], sl["k"], sl["v"], g, sl["beta"], None)
+        c_s = time.perf_counter() - c0
+        used = min(oracle.num_threads(), HV)
+        cpu = dict(value=round(Ts / c_s, 1), unit="tokens/s", cores=used, kind="oracle",
+                   sample=f"FP64 oracle (gate + token recurrence) on batch row 0: T={Ts}, all "
+                          f"{HV} heads, K=V={K}; {c_s:.2f} s wall")
+
+    out = {
+        "metric": "chunk_kda fwd tokens/s (B4 T4096 H16 K=V=128 bf16) + recurrent decode us/step",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dense chunk_kda forward: gate cumsum + chunked scan, B=4 T=4096 "
+                               "H=HV=16 K=V=128 bf16, chunk 64, zero h0, final state out",
+                   "B": B, "T": T, "H": H, "HV": HV, "K": K, "V": V, "chunk_size": 64,
+                   "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
+        "step_breakdown_ms": {"kda_gate_cumsum": round(g_ms, 4), "kda_chunk_fwd": round(c_ms, 4),
+                              "gate_GBps": round(gate_gbs, 1), "chunk_fwd_GBps": round(chunk_gbs, 1)},
+        "roofline": roof,
+        "decode": {"workload": "recurrent_kda decode: 256 slots (26 empty), 1 token each, H=16 "
+                               "HV=32 K=V=128 bf16, FP32 state in place",
+                   "us_per_step": round(dec_us, 2), "kda_recurrent_fwd_us": round(rec_us, 2),
+                   "recurrent_GBps": round(rec_gbs, 1),
+                   "recurrent_hbm_frac": round(rec_gbs / HBM_PEAK_GBS, 4),
+                   "algorithmic_bytes": dbytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

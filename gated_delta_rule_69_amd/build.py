@@ -11,6 +11,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["kda_api.hip", "kda_gate.hip", "kda_recurrent.hip", "kda_chunk.hip"]
 ARCH = "gfx950"
@@ -29,6 +30,7 @@ def flags():
         # packed FP32 VALU ops stay off (plain float code only)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-result", "-Wno-unused-variable",
+        f"-I{INCLUDE}",
     ]
 
 

@@ -122,6 +122,10 @@ kda_status kda_chunk_fwd(const kda_dims* d, kda_dtype dt, const void* q, const v
   if (chunk_size != 64) return KDA_ERR_UNSUPPORTED;
   if (!((d->K == 64 || d->K == 128) && (d->V == 64 || d->V == 128))) return KDA_ERR_UNSUPPORTED;
   if (d->N == 0) return KDA_OK;
+  // 16-byte vector loads of q, k, v and the gate; 256-byte aligned workspace
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)gate) & 15) ||
+      ((uintptr_t)workspace & 255))
+    return KDA_ERR_UNSUPPORTED;
   const size_t need = kda_host::chunk_workspace_bytes(*d, dt, chunk_size);
   if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
   const Sizes s = sizes(d, dt);

@@ -33,6 +33,7 @@
 // with its own reference), plus the exact diagonal i == j. This keeps
 // unbounded gates (chunk-local cumsums far below -126 in log2 units) exact.
 #include <algorithm>
+#include <type_traits>
 
 #include "kda_common.h"
 
@@ -137,13 +138,67 @@ struct IntraLds {
   static constexpr int GS = K + 4;                // G2 row stride (floats)
   static constexpr int KSTR = K + TP;             // k / q row stride
   static constexpr int AS = kC + 4;               // A / T row stride (floats)
-  static constexpr int BTS = kC + TP;             // B^T and (bV)^T row stride
+  static constexpr int VSTR = V + TP;             // b v row stride
   static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
-  static constexpr size_t R1 = cmax((size_t)kC * GS * 4, (size_t)V * BTS * sizeof(T));
-  static constexpr size_t R2 = cmax((size_t)kC * KSTR * sizeof(T), (size_t)K * BTS * sizeof(T));
+  static constexpr size_t R1 = cmax((size_t)kC * GS * 4, (size_t)kC * VSTR * sizeof(T));
+  static constexpr size_t R2 = (size_t)kC * KSTR * sizeof(T);
   static constexpr size_t R3 = cmax((size_t)kC * KSTR * sizeof(T), (size_t)kC * AS * 4);
   static constexpr size_t total = R1 + R2 + R3 + kC * 4;
 };
+
+// 2^x on the transcendental unit (v_exp_f32). Results below 2^-126 flush to
+// zero, which only drops decay products that are below FP32 range anyway.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Four consecutive LDS elements as floats (one 16- or 8-byte LDS read).
+__device__ __forceinline__ void lds4(const float* p, float o[4]) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+}
+__device__ __forceinline__ void lds4(const bf16* p, float o[4]) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+  o[0] = (float)x[0]; o[1] = (float)x[1]; o[2] = (float)x[2]; o[3] = (float)x[3];
+}
+
+// Element e of a 16-byte unit holding T values, as float.
+template <typename T>
+__device__ __forceinline__ float unit_elem(const uint4& u, int e) {
+  const uint32_t w = (e >> (sizeof(T) == 2 ? 1 : 0)) == 0 ? u.x
+                   : (e >> (sizeof(T) == 2 ? 1 : 0)) == 1 ? u.y
+                   : (e >> (sizeof(T) == 2 ? 1 : 0)) == 2 ? u.z : u.w;
+  if constexpr (sizeof(T) == 2) return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  else return __uint_as_float(w);
+}
+
+// Quad p of a contraction dimension holds indices 16p + 4g + e (e = 0..3) for
+// lane group g. With the kidx() order of MF<>, quad p is slots 4(p&1)..+3 of
+// bf16 fragment p/2, or FP32 fragments 4p..4p+3.
+template <typename M>
+__device__ __forceinline__ void put_quad(typename M::frag* fr, int p, const float v[4]) {
+  if constexpr (M::KSTEP == 32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) M::set(fr[p >> 1], 4 * (p & 1) + e, v[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) M::set(fr[4 * p + e], 0, v[e]);
+  }
+}
+
+// Fragment of contraction step ks built from accumulator tiles of the
+// transposed product (see MF<>): element jj comes from tile tile_of(ks, jj).
+template <typename M>
+__device__ __forceinline__ int acc_tile(int ks, int jj) {
+  return (M::KSTEP == 32) ? (2 * ks + (jj >> 2)) : (ks >> 2);
+}
+template <typename M>
+__device__ __forceinline__ int acc_elem(int ks, int jj) {
+  return (M::KSTEP == 32) ? (jj & 3) : (ks & 3);
+}
+
+// Max exponent range (log2 units) that a single reference token may span in a
+// diagonal tile: factors up to 2^112 and sums of 128 such products stay
+// finite in FP32 and bf16.
+constexpr float kFastRange = 112.f;
 
 template <typename T, int K, int V>
 __global__ void __launch_bounds__(kThreads, 2)
@@ -157,13 +212,18 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   using WsL = Ws<T, K, V>;
   constexpr int KS_K = K / M::KSTEP;
   constexpr int KS_C = kC / M::KSTEP;
-  constexpr int GS = Lds::GS, KSTR = Lds::KSTR, AS = Lds::AS, BTS = Lds::BTS;
+  constexpr int QK = K / 16;   // quads over channels
+  constexpr int QC = kC / 16;  // quads over tokens
+  constexpr int GS = Lds::GS, KSTR = Lds::KSTR, AS = Lds::AS;
+  constexpr int EPU = 16 / (int)sizeof(T);      // elements of T per 16-byte unit
+  constexpr int GU = kC * K / 4 / kThreads;     // float4 units of G2 per thread
+  constexpr int KU = kC * K / EPU / kThreads;   // 16-byte units of k (and of q) per thread
+  constexpr int VU = kC * V / EPU / kThreads;   // 16-byte units of v per thread
+  static_assert(GU >= 1 && KU >= 1 && VU >= 1, "tile shape");
 
   extern __shared__ __align__(16) char smem[];
-  float* sG = reinterpret_cast<float*>(smem);                       // R1: G2 [C][GS]
-  T* sVT = reinterpret_cast<T*>(smem);                              // R1 later: (b v)^T [V][BTS]
+  float* sG = reinterpret_cast<float*>(smem);                       // R1: G2 [C][GS], later b v
   T* sK = reinterpret_cast<T*>(smem + Lds::R1);                     // R2: k [C][KSTR]
-  T* sBT = reinterpret_cast<T*>(smem + Lds::R1);                    // R2 later: B^T [K][BTS]
   T* sQ = reinterpret_cast<T*>(smem + Lds::R1 + Lds::R2);           // R3: q [C][KSTR]
   float* sA = reinterpret_cast<float*>(smem + Lds::R1 + Lds::R2);   // R3 later: A, then T [C][AS]
   float* sBeta = reinterpret_cast<float*>(smem + Lds::R1 + Lds::R2 + Lds::R3);
@@ -177,94 +237,179 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   const int64_t t0 = geo.t0;
   const size_t ch = (size_t)blockIdx.x * HV + hv;
 
-  // ---- 1. stage G2, k, q, beta; prefetch v into registers
-  for (int e = tid; e < kC * K; e += kThreads) {
-    const int i = e / K, c = e - i * K;
-    const int ii = i < L ? i : L - 1;  // pad rows repeat the last gate row
-    sG[i * GS + c] = gate[((t0 + ii) * HV + hv) * K + c];
-    T kv = from_f32<T>(0.f), qv = from_f32<T>(0.f);
-    if (i < L) {
-      kv = k[((t0 + i) * H + h) * K + c];
-      qv = q[((t0 + i) * H + h) * K + c];
+  // ---- 1. global loads first (16-byte units), then LDS stores
+  float4 gr[GU];
+  uint4 kr[KU], qr[KU], vr[VU];
+#pragma unroll
+  for (int u = 0; u < GU; ++u) {
+    const int f = tid + u * kThreads, row = f / (K / 4), c4 = f % (K / 4);
+    const int rr = row < L ? row : L - 1;  // pad rows repeat the last gate row
+    gr[u] = *reinterpret_cast<const float4*>(gate + ((t0 + rr) * HV + hv) * K + 4 * c4);
+  }
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int f = tid + u * kThreads, row = f / (K / EPU), cu_ = f % (K / EPU);
+    kr[u] = qr[u] = make_uint4(0, 0, 0, 0);
+    if (row < L) {
+      kr[u] = *reinterpret_cast<const uint4*>(k + ((t0 + row) * H + h) * K + EPU * cu_);
+      qr[u] = *reinterpret_cast<const uint4*>(q + ((t0 + row) * H + h) * K + EPU * cu_);
     }
-    sK[i * KSTR + c] = kv;
-    sQ[i * KSTR + c] = qv;
+  }
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int f = tid + u * kThreads, row = f / (V / EPU), cu_ = f % (V / EPU);
+    vr[u] = make_uint4(0, 0, 0, 0);
+    if (row < L) vr[u] = *reinterpret_cast<const uint4*>(v + ((t0 + row) * HV + hv) * V + EPU * cu_);
   }
   if (tid < kC) sBeta[tid] = tid < L ? to_f32(beta[(t0 + tid) * HV + hv]) : 0.f;
-  constexpr int VPT = kC * V / kThreads;  // v elements per thread
-  float vreg[VPT];
 #pragma unroll
-  for (int u = 0; u < VPT; ++u) {
-    const int e = tid + u * kThreads;
-    const int i = e / V, c = e - i * V;
-    vreg[u] = i < L ? to_f32(v[((t0 + i) * HV + hv) * V + c]) : 0.f;
+  for (int u = 0; u < GU; ++u) {
+    const int f = tid + u * kThreads, row = f / (K / 4), c4 = f % (K / 4);
+    *reinterpret_cast<float4*>(sG + row * GS + 4 * c4) = gr[u];
+  }
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int f = tid + u * kThreads, row = f / (K / EPU), cu_ = f % (K / EPU);
+    *reinterpret_cast<uint4*>(sK + row * KSTR + EPU * cu_) = kr[u];
+    *reinterpret_cast<uint4*>(sQ + row * KSTR + EPU * cu_) = qr[u];
   }
   __syncthreads();
 
-  // ---- 2. A^T and P^T tiles (column tile I = wave; row tiles J <= I)
+  // ---- 2. A^T and P^T tiles: column tile I = wave (tokens i), row tiles J <= I (tokens j)
   const int I = wave;
-  f32x4 accA[4], accP[4];  // tiles J < I (off-diagonal)
+  const int icol = 16 * I + l16;
+  const int r = 16 * I;  // reference token of every tile in column I
+  F lkf[KS_K], lqf[KS_K];  // column factors k_i 2^(G2_i - G2_r), q~_i 2^(G2_i - G2_r) (<= 1)
+#pragma unroll
+  for (int p = 0; p < QK; ++p) {
+    const int c0 = 16 * p + 4 * g;
+    float gi[4], g0[4], ki[4], qi[4], vk[4], vq[4];
+    lds4(sG + icol * GS + c0, gi);
+    lds4(sG + r * GS + c0, g0);
+    lds4(sK + icol * KSTR + c0, ki);
+    lds4(sQ + icol * KSTR + c0, qi);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = ex2(gi[e] - g0[e]);
+      vk[e] = ki[e] * x;
+      vq[e] = qi[e] * scale * x;
+    }
+    put_quad<M>(lkf, p, vk);
+    put_quad<M>(lqf, p, vq);
+  }
+  f32x4 accA[3], accP[3];            // tiles J < I
   f32x4 dA = zero4(), dP = zero4();  // tile J == I
 #pragma unroll
-  for (int J = 0; J < 4; ++J) accA[J] = accP[J] = zero4();
-  {
-    const int icol = 16 * I + l16;  // B operand column (token i)
-    // off-diagonal tiles: reference token r = 16 I
-    const int r = 16 * I;
+  for (int J = 0; J < 3; ++J) {
+    accA[J] = accP[J] = zero4();
+    if (J < I) {
+      const int jrow = 16 * J + l16;
+      F rf[KS_K];  // row factors k_j 2^(G2_r - G2_j) (<= 1: j < r)
 #pragma unroll
-    for (int J = 0; J < 3; ++J) {
-      if (J >= I) break;
-      const int jrow = 16 * J + l16;  // A operand row (token j)
+      for (int p = 0; p < QK; ++p) {
+        const int c0 = 16 * p + 4 * g;
+        float gj[4], g0[4], kj[4], vv[4];
+        lds4(sG + jrow * GS + c0, gj);
+        lds4(sG + r * GS + c0, g0);
+        lds4(sK + jrow * KSTR + c0, kj);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vv[e] = kj[e] * ex2(g0[e] - gj[e]);
+        put_quad<M>(rf, p, vv);
+      }
 #pragma unroll
       for (int ks = 0; ks < KS_K; ++ks) {
-        F ra, lk, lq;
-#pragma unroll
-        for (int jj = 0; jj < M::PER; ++jj) {
-          const int c = M::kidx(ks, g, jj);
-          const float gr = sG[r * GS + c];
-          M::set(ra, jj, to_f32(sK[jrow * KSTR + c]) * exp2f(gr - sG[jrow * GS + c]));
-          const float e = exp2f(sG[icol * GS + c] - gr);
-          M::set(lk, jj, to_f32(sK[icol * KSTR + c]) * e);
-          M::set(lq, jj, to_f32(sQ[icol * KSTR + c]) * scale * e);
-        }
-        accA[J] = M::mma(ra, lk, accA[J]);
-        accP[J] = M::mma(ra, lq, accP[J]);
+        accA[J] = M::mma(rf[ks], lkf[ks], accA[J]);
+        accP[J] = M::mma(rf[ks], lqf[ks], accP[J]);
       }
     }
-    // diagonal tile (I, I): levels 3..0 then the exact diagonal
-    const int jl = l16, il = l16;
-    const int jrow = 16 * I + jl;
+  }
+  // diagonal tile: one pass with reference r when the tile's gate range allows it
+  float rng = 0.f;
+#pragma unroll
+  for (int p = 0; p < QK; ++p) {
+    const int c0 = 16 * p + 4 * g;
+    float a0[4], a1[4];
+    lds4(sG + r * GS + c0, a0);
+    lds4(sG + (r + 15) * GS + c0, a1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rng = fmaxf(rng, a0[e] - a1[e]);
+  }
+  rng = fmaxf(rng, __shfl_xor(rng, 16));
+  rng = fmaxf(rng, __shfl_xor(rng, 32));
+  const int jl = l16, il = l16;
+  const int jrow = 16 * I + jl;
+  if (rng <= kFastRange) {
+    F rf[KS_K];  // k_j 2^(G2_r - G2_j) with r <= j: >= 1 but at most 2^112
+#pragma unroll
+    for (int p = 0; p < QK; ++p) {
+      const int c0 = 16 * p + 4 * g;
+      float gj[4], g0[4], kj[4], vv[4];
+      lds4(sG + jrow * GS + c0, gj);
+      lds4(sG + r * GS + c0, g0);
+      lds4(sK + jrow * KSTR + c0, kj);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[e] = kj[e] * ex2(g0[e] - gj[e]);
+      put_quad<M>(rf, p, vv);
+    }
+    f32x4 xa = zero4(), xp = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS_K; ++ks) {
+      xa = M::mma(rf[ks], lkf[ks], xa);
+      xp = M::mma(rf[ks], lqf[ks], xp);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int jr = 4 * g + e;
+      dA[e] = (il > jr) ? xa[e] : 0.f;
+      dP[e] = (il >= jr) ? xp[e] : 0.f;
+    }
+  } else {
+    // exact split by the highest differing bit of the local indices (levels
+    // 3..0, each with its own reference token), then the diagonal i == j
 #pragma unroll
     for (int lev = 3; lev >= -1; --lev) {
-      f32x4 xa = zero4(), xp = zero4();
       const bool rowOn = lev < 0 || ((jl >> lev) & 1) == 0;
       const bool colOn = lev < 0 || ((il >> lev) & 1) == 1;
-      const int rr = lev < 0 ? 0 : 16 * I + ((((jl >> lev) | 1)) << lev);  // ref for row j
-      const int rc = lev < 0 ? 0 : 16 * I + ((il >> lev) << lev);          // ref for col i
+      const int rr = lev < 0 ? 0 : 16 * I + ((((jl >> lev) | 1)) << lev);  // reference of row j
+      const int rc = lev < 0 ? 0 : 16 * I + ((il >> lev) << lev);          // reference of col i
+      F ra[KS_K], lk[KS_K], lq[KS_K];
+#pragma unroll
+      for (int p = 0; p < QK; ++p) {
+        const int c0 = 16 * p + 4 * g;
+        float kj[4], ki[4], qi[4], va[4], vk[4], vq[4];
+        lds4(sK + jrow * KSTR + c0, kj);
+        lds4(sQ + icol * KSTR + c0, qi);
+        if (lev < 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            va[e] = kj[e];
+            vk[e] = 0.f;
+            vq[e] = qi[e] * scale;
+          }
+        } else {
+          float gj[4], grr[4], gi[4], grc[4];
+          lds4(sK + icol * KSTR + c0, ki);
+          lds4(sG + jrow * GS + c0, gj);
+          lds4(sG + rr * GS + c0, grr);
+          lds4(sG + icol * GS + c0, gi);
+          lds4(sG + rc * GS + c0, grc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            va[e] = rowOn ? kj[e] * ex2(grr[e] - gj[e]) : 0.f;
+            const float x = colOn ? ex2(gi[e] - grc[e]) : 0.f;
+            vk[e] = ki[e] * x;
+            vq[e] = qi[e] * scale * x;
+          }
+        }
+        put_quad<M>(ra, p, va);
+        put_quad<M>(lk, p, vk);
+        put_quad<M>(lq, p, vq);
+      }
+      f32x4 xa = zero4(), xp = zero4();
 #pragma unroll
       for (int ks = 0; ks < KS_K; ++ks) {
-        F ra, lk, lq;
-#pragma unroll
-        for (int jj = 0; jj < M::PER; ++jj) {
-          const int c = M::kidx(ks, g, jj);
-          float a = 0.f, bk = 0.f, bq = 0.f;
-          if (lev < 0) {
-            a = to_f32(sK[jrow * KSTR + c]);
-            bq = to_f32(sQ[icol * KSTR + c]) * scale;
-          } else {
-            if (rowOn) a = to_f32(sK[jrow * KSTR + c]) * exp2f(sG[rr * GS + c] - sG[jrow * GS + c]);
-            if (colOn) {
-              const float e = exp2f(sG[icol * GS + c] - sG[rc * GS + c]);
-              bk = to_f32(sK[icol * KSTR + c]) * e;
-              bq = to_f32(sQ[icol * KSTR + c]) * scale * e;
-            }
-          }
-          M::set(ra, jj, a);
-          M::set(lk, jj, bk);
-          M::set(lq, jj, bq);
-        }
-        if (lev >= 0) xa = M::mma(ra, lk, xa);
-        xp = M::mma(ra, lq, xp);
+        if (lev >= 0) xa = M::mma(ra[ks], lk[ks], xa);
+        xp = M::mma(ra[ks], lq[ks], xp);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -293,82 +438,70 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     F f;
 #pragma unroll
     for (int jj = 0; jj < M::PER; ++jj) {
-      const int tile = (M::KSTEP == 32) ? (2 * ks + (jj >> 2)) : (ks >> 2);
-      const int el = (M::KSTEP == 32) ? (jj & 3) : (ks & 3);
+      const int tile = acc_tile<M>(ks, jj), el = acc_elem<M>(ks, jj);
       float x = 0.f;
 #pragma unroll
       for (int J = 0; J < 4; ++J)
-        if (J == tile) x = (J < I) ? accP[J][el] : (J == I ? dP[el] : 0.f);
+        if (J == tile) x = (J < I) ? accP[J < 3 ? J : 0][el] : (J == I ? dP[el] : 0.f);
       M::set(f, jj, x);
     }
     reinterpret_cast<F*>(wsP)[((size_t)I * KS_C + ks) * 64 + lane] = f;
   }
   // ---- 4. Q~ * Gamma fragments (rows i of tile I, contraction over channels)
   {
-    const int i = 16 * I + l16;
+    F f[KS_K];
 #pragma unroll
-    for (int ks = 0; ks < KS_K; ++ks) {
-      F f;
+    for (int p = 0; p < QK; ++p) {
+      const int c0 = 16 * p + 4 * g;
+      float qi[4], gi[4], vv[4];
+      lds4(sQ + icol * KSTR + c0, qi);
+      lds4(sG + icol * GS + c0, gi);
 #pragma unroll
-      for (int jj = 0; jj < M::PER; ++jj) {
-        const int c = M::kidx(ks, g, jj);
-        M::set(f, jj, to_f32(sQ[i * KSTR + c]) * scale * exp2f(sG[i * GS + c]));
-      }
-      reinterpret_cast<F*>(wsQG)[((size_t)I * KS_K + ks) * 64 + lane] = f;
+      for (int e = 0; e < 4; ++e) vv[e] = qi[e] * scale * ex2(gi[e]);
+      put_quad<M>(f, p, vv);
     }
+#pragma unroll
+    for (int ks = 0; ks < KS_K; ++ks) reinterpret_cast<F*>(wsQG)[((size_t)I * KS_K + ks) * 64 + lane] = f[ks];
   }
   // ---- 5. Khat^T fragments (rows = channels, contraction over tokens j)
-  for (int rt = wave; rt < K / 16; rt += 4) {
+#pragma unroll
+  for (int rt0 = 0; rt0 < K / 16; rt0 += 4) {
+    const int rt = rt0 + wave;
     const int c = 16 * rt + l16;
     const float gl = sG[(L - 1) * GS + c];
+    F f[KS_C];
 #pragma unroll
-    for (int ks = 0; ks < KS_C; ++ks) {
-      F f;
+    for (int p = 0; p < QC; ++p) {
+      float vv[4];
 #pragma unroll
-      for (int jj = 0; jj < M::PER; ++jj) {
-        const int j = M::kidx(ks, g, jj);
-        M::set(f, jj, to_f32(sK[j * KSTR + c]) * exp2f(gl - sG[j * GS + c]));
+      for (int e = 0; e < 4; ++e) {
+        const int j = 16 * p + 4 * g + e;
+        vv[e] = to_f32(sK[j * KSTR + c]) * ex2(gl - sG[j * GS + c]);
       }
-      reinterpret_cast<F*>(wsKH)[((size_t)rt * KS_C + ks) * 64 + lane] = f;
+      put_quad<M>(f, p, vv);
     }
+#pragma unroll
+    for (int ks = 0; ks < KS_C; ++ks) reinterpret_cast<F*>(wsKH)[((size_t)rt * KS_C + ks) * 64 + lane] = f[ks];
   }
-  if (tid < K) wsGL[tid] = exp2f(sG[(L - 1) * GS + tid]);
-  __syncthreads();  // q is dead: R3 becomes A
+  if (tid < K) wsGL[tid] = ex2(sG[(L - 1) * GS + tid]);
+  __syncthreads();  // q is dead: R3 <- A
 
-  // ---- 6. A = beta_i * (A^T accumulators)^T into LDS, zero elsewhere
+  // ---- 6. A = b_i (A^T accumulators)^T into LDS (zero above the diagonal tiles)
   {
-    const int i = 16 * I + l16;
-    const float b = sBeta[i];
+    const float b = sBeta[icol];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (J < I) x = make_float4(b * accA[J][0], b * accA[J][1], b * accA[J][2], b * accA[J][3]);
-      else if (J == I) x = make_float4(b * dA[0], b * dA[1], b * dA[2], b * dA[3]);
-      *reinterpret_cast<float4*>(&sA[i * AS + 16 * J + 4 * g]) = x;
+      if (J < I) {
+        const f32x4 a = accA[J < 3 ? J : 0];
+        x = make_float4(b * a[0], b * a[1], b * a[2], b * a[3]);
+      } else if (J == I) {
+        x = make_float4(b * dA[0], b * dA[1], b * dA[2], b * dA[3]);
+      }
+      *reinterpret_cast<float4*>(&sA[icol * AS + 16 * J + 4 * g]) = x;
     }
   }
-  // B^T = (b_m k_mc 2^G2_mc)^T and (b v)^T values into registers (G2 and k still live)
-  constexpr int BPT = kC * K / kThreads;
-  float breg[BPT];
-#pragma unroll
-  for (int u = 0; u < BPT; ++u) {
-    const int e = tid + u * kThreads;
-    const int m = e / K, c = e - m * K;
-    breg[u] = sBeta[m] * to_f32(sK[m * KSTR + c]) * exp2f(sG[m * GS + c]);
-  }
-  __syncthreads();  // G2 and k are dead: R1 becomes (b v)^T, R2 becomes B^T
-#pragma unroll
-  for (int u = 0; u < BPT; ++u) {
-    const int e = tid + u * kThreads;
-    const int m = e / K, c = e - m * K;
-    sBT[c * BTS + m] = from_f32<T>(breg[u]);
-  }
-#pragma unroll
-  for (int u = 0; u < VPT; ++u) {
-    const int e = tid + u * kThreads;
-    const int m = e / V, c = e - m * V;
-    sVT[c * BTS + m] = from_f32<T>(sBeta[m] * vreg[u]);
-  }
+  __syncthreads();
 
   // ---- 7. T = (I + A)^-1 in FP32, in place
   // 7a. diagonal 16x16 blocks by forward substitution (wave d, lane = column)
@@ -377,114 +510,194 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      float arow[16];
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) lds4(sA + (16 * d + i) * AS + 16 * d + 4 * m4, arow + 4 * m4);
       float s = (i == jj) ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < i; ++m) s -= sA[(16 * d + i) * AS + 16 * d + m] * x[m];
+      for (int m = 0; m < i; ++m) s -= arow[m] * x[m];
       x[i] = s;
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) sA[(16 * d + i) * AS + 16 * d + jj] = x[i];
   }
   __syncthreads();
-  // 7b. block rows: T_IJ = -T_II * sum_{M=J}^{I-1} A_IM T_MJ, scratch in the upper block (J, I)
+  // 7b. block rows: T_IJ = -T_II * sum_{M=J}^{I-1} A_IM T_MJ (scratch: upper block (J, I))
   for (int Ib = 1; Ib < 4; ++Ib) {
     const int Jb = wave;
     const int a = l16, b0 = 4 * g;  // lane owns row a, columns b0..b0+3 of the block
     if (Jb < Ib) {
       float xs[4] = {0.f, 0.f, 0.f, 0.f};
       for (int Mb = Jb; Mb < Ib; ++Mb) {
+        float arow[16];
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) lds4(sA + (16 * Ib + a) * AS + 16 * Mb + 4 * m4, arow + 4 * m4);
 #pragma unroll
         for (int p = 0; p < 16; ++p) {
-          const float aim = sA[(16 * Ib + a) * AS + 16 * Mb + p];
+          float t4[4];
+          lds4(sA + (16 * Mb + p) * AS + 16 * Jb + b0, t4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) xs[e] += aim * sA[(16 * Mb + p) * AS + 16 * Jb + b0 + e];
+          for (int e = 0; e < 4; ++e) xs[e] += arow[p] * t4[e];
         }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sA[(16 * Jb + a) * AS + 16 * Ib + b0 + e] = xs[e];
+      *reinterpret_cast<float4*>(sA + (16 * Jb + a) * AS + 16 * Ib + b0) = make_float4(xs[0], xs[1], xs[2], xs[3]);
     }
     __syncthreads();
     if (Jb < Ib) {
       float ts[4] = {0.f, 0.f, 0.f, 0.f};
+      float trow[16];
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) lds4(sA + (16 * Ib + a) * AS + 16 * Ib + 4 * m4, trow + 4 * m4);
 #pragma unroll
       for (int p = 0; p < 16; ++p) {
-        const float tii = sA[(16 * Ib + a) * AS + 16 * Ib + p];
+        float x4[4];
+        lds4(sA + (16 * Jb + p) * AS + 16 * Ib + b0, x4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ts[e] -= tii * sA[(16 * Jb + p) * AS + 16 * Ib + b0 + e];
+        for (int e = 0; e < 4; ++e) ts[e] -= trow[p] * x4[e];
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sA[(16 * Ib + a) * AS + 16 * Jb + b0 + e] = ts[e];
+      *reinterpret_cast<float4*>(sA + (16 * Ib + a) * AS + 16 * Jb + b0) = make_float4(ts[0], ts[1], ts[2], ts[3]);
     }
     __syncthreads();
-    if (Jb < Ib) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sA[(16 * Jb + a) * AS + 16 * Ib + b0 + e] = 0.f;
-    }
+    if (Jb < Ib)
+      *reinterpret_cast<float4*>(sA + (16 * Jb + a) * AS + 16 * Ib + b0) = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
   }
 
-  // ---- 8. W^T = B^T T^T (rows channels, cols tokens of tile I) -> W fragments of row tile I
+  // ---- 8. W^T = B^T T^T with B_mc = b_m k_mc 2^G2_mc built on the fly.
+  // Wave split: a pair of 16-row tiles of the output dimension (= one bf16
+  // contraction step of the consumer) times NI token tiles, so every wave
+  // writes whole fragments.
   {
-    const int i = 16 * I + l16;
-    f32x4 accW[K / 16];
+    constexpr int NP = K / 32;  // tile pairs over channels
+    const int pw = wave % NP, I0 = (wave / NP) * NP;
+    F tfr[NP][KS_C];  // T rows i of token tiles I0..I0+NP-1, over m
 #pragma unroll
-    for (int ct = 0; ct < K / 16; ++ct) accW[ct] = zero4();
+    for (int ii = 0; ii < NP; ++ii)
 #pragma unroll
-    for (int ks = 0; ks < KS_C; ++ks) {
-      F tb;
+      for (int p = 0; p < QC; ++p) {
+        float t4[4];
+        lds4(sA + (16 * (I0 + ii) + l16) * AS + 16 * p + 4 * g, t4);
+        put_quad<M>(tfr[ii], p, t4);
+      }
+    f32x4 accW[2][NP];
 #pragma unroll
-      for (int jj = 0; jj < M::PER; ++jj) M::set(tb, jj, sA[i * AS + M::kidx(ks, g, jj)]);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int c = 16 * (2 * pw + h2) + l16;
+      F ba[KS_C];
 #pragma unroll
-      for (int ct = 0; ct < K / 16; ++ct) {
-        const int c = 16 * ct + l16;
-        F ba;
+      for (int p = 0; p < QC; ++p) {
+        float b4[4];
 #pragma unroll
-        for (int jj = 0; jj < M::PER; ++jj) M::set(ba, jj, to_f32(sBT[c * BTS + M::kidx(ks, g, jj)]));
-        accW[ct] = M::mma(ba, tb, accW[ct]);
+        for (int e = 0; e < 4; ++e) {
+          const int m = 16 * p + 4 * g + e;
+          b4[e] = sBeta[m] * to_f32(sK[m * KSTR + c]) * ex2(sG[m * GS + c]);
+        }
+        put_quad<M>(ba, p, b4);
+      }
+#pragma unroll
+      for (int ii = 0; ii < NP; ++ii) {
+        accW[h2][ii] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) accW[h2][ii] = M::mma(ba[ks], tfr[ii][ks], accW[h2][ii]);
       }
     }
+    // channel tiles 2pw, 2pw+1 are contraction steps {pw} (bf16) or {8pw..8pw+7} (FP32)
 #pragma unroll
-    for (int ks = 0; ks < KS_K; ++ks) {
-      F f;
+    for (int ii = 0; ii < NP; ++ii) {
+      if constexpr (M::KSTEP == 32) {
+        F f;
 #pragma unroll
-      for (int jj = 0; jj < M::PER; ++jj) {
-        const int tile = (M::KSTEP == 32) ? (2 * ks + (jj >> 2)) : (ks >> 2);
-        const int el = (M::KSTEP == 32) ? (jj & 3) : (ks & 3);
-        M::set(f, jj, accW[tile][el]);
+        for (int jj = 0; jj < 8; ++jj) M::set(f, jj, accW[jj >> 2][ii][jj & 3]);
+        reinterpret_cast<F*>(wsW)[((size_t)(I0 + ii) * KS_K + pw) * 64 + lane] = f;
+      } else {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            F f;
+            M::set(f, 0, accW[h2][ii][e]);
+            reinterpret_cast<F*>(wsW)[((size_t)(I0 + ii) * KS_K + 4 * (2 * pw + h2) + e) * 64 + lane] = f;
+          }
       }
-      reinterpret_cast<F*>(wsW)[((size_t)I * KS_K + ks) * 64 + lane] = f;
     }
   }
-  // ---- 9. U = T (b V) (rows tokens of tile I), stored in accumulator order
+  __syncthreads();  // G2 and k are dead: R1 <- b V (row-major)
+  constexpr int VSTR = Lds::VSTR;
+  T* sV = reinterpret_cast<T*>(smem);  // R1: b v [C][VSTR]
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int f = tid + u * kThreads, m = f / (V / EPU), cu_ = f % (V / EPU);
+    const float b = sBeta[m];
+    T tmp[EPU];
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) tmp[e] = from_f32<T>(b * unit_elem<T>(vr[u], e));
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) sV[m * VSTR + EPU * cu_ + e] = tmp[e];
+  }
+  __syncthreads();
+
+  // ---- 9. U = T (b V), same wave split over value tiles; accumulator order
   {
-    const int i = 16 * I + l16;
-    f32x4 accU[V / 16];
+    constexpr int NP = V / 32;
+    const int pw = wave % NP, I0 = (wave / NP) * NP;
 #pragma unroll
-    for (int vt = 0; vt < V / 16; ++vt) accU[vt] = zero4();
+    for (int ii = 0; ii < NP; ++ii) {
+      F ta[KS_C];
 #pragma unroll
-    for (int ks = 0; ks < KS_C; ++ks) {
-      F ta;
-#pragma unroll
-      for (int jj = 0; jj < M::PER; ++jj) M::set(ta, jj, sA[i * AS + M::kidx(ks, g, jj)]);
-#pragma unroll
-      for (int vt = 0; vt < V / 16; ++vt) {
-        const int c = 16 * vt + l16;
-        F vb;
-#pragma unroll
-        for (int jj = 0; jj < M::PER; ++jj) M::set(vb, jj, to_f32(sVT[c * BTS + M::kidx(ks, g, jj)]));
-        accU[vt] = M::mma(ta, vb, accU[vt]);
+      for (int p = 0; p < QC; ++p) {
+        float t4[4];
+        lds4(sA + (16 * (I0 + ii) + l16) * AS + 16 * p + 4 * g, t4);
+        put_quad<M>(ta, p, t4);
       }
-    }
 #pragma unroll
-    for (int vt = 0; vt < V / 16; ++vt) {
-      T* dst = wsU + (((size_t)I * (V / 16) + vt) * 64 + lane) * 4;
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int vt = 2 * pw + h2;
+        const int c = 16 * vt + l16;
+        F vb[KS_C];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(accU[vt][e]);
+        for (int p = 0; p < QC; ++p) {
+          float v4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = to_f32(sV[(16 * p + 4 * g + e) * VSTR + c]);
+          put_quad<M>(vb, p, v4);
+        }
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(ta[ks], vb[ks], acc);
+        T* dst = wsU + (((size_t)(I0 + ii) * (V / 16) + vt) * 64 + lane) * 4;
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = (bf16)acc[e];
+          *reinterpret_cast<bf16x4*>(dst) = x;
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------ inter-chunk scan + output
+// Raw 4-element vector of T (U in accumulator order).
+template <typename T>
+struct Raw4;
+template <>
+struct Raw4<bf16> {
+  typedef uint2 type;
+  static __device__ __forceinline__ float get(const uint2& r, int e) {
+    const uint32_t w = e < 2 ? r.x : r.y;
+    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+};
+template <>
+struct Raw4<float> {
+  typedef float4 type;
+  static __device__ __forceinline__ float get(const float4& r, int e) {
+    return e == 0 ? r.x : e == 1 ? r.y : e == 2 ? r.z : r.w;
+  }
+};
+
 template <typename T, int K, int V, int BV>
 __global__ void __launch_bounds__(kThreads)
 chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
@@ -494,6 +707,8 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
   using M = MF<T>;
   using F = typename M::frag;
   using WsL = Ws<T, K, V>;
+  using R4 = Raw4<T>;
+  typedef typename R4::type raw4;
   constexpr int KS_K = K / M::KSTEP;
   constexpr int KS_C = kC / M::KSTEP;
   constexpr int RTW = K / 64;   // state row tiles per wave
@@ -531,6 +746,41 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     return;
   }
 
+  // per-chunk operands of this wave, loaded one chunk ahead
+  struct Ops {
+    F w[KS_K], qg[KS_K], p[KS_C], kh[RTW][KS_C];
+    raw4 u[CTB];
+    float4 gl[RTW];
+  };
+  auto load_ops = [&](int cj, Ops& op) {
+    const size_t ch = (size_t)cj * HV + hv;
+    const T* wsW = ws_T + ch * WsL::elems;
+    const F* fW = reinterpret_cast<const F*>(wsW);
+    const F* fQG = reinterpret_cast<const F*>(wsW + WsL::W);
+    const F* fKH = reinterpret_cast<const F*>(wsW + WsL::W + WsL::QG);
+    const F* fP = reinterpret_cast<const F*>(wsW + WsL::W + WsL::QG + WsL::KH);
+    const T* wsU = wsW + WsL::W + WsL::QG + WsL::KH + WsL::P;
+#pragma unroll
+    for (int ks = 0; ks < KS_K; ++ks) {
+      op.w[ks] = fW[((size_t)wave * KS_K + ks) * 64 + lane];
+      op.qg[ks] = fQG[((size_t)wave * KS_K + ks) * 64 + lane];
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS_C; ++ks) op.p[ks] = fP[((size_t)wave * KS_C + ks) * 64 + lane];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+#pragma unroll
+      for (int ks = 0; ks < KS_C; ++ks)
+        op.kh[rt][ks] = fKH[((size_t)(RTW * wave + rt) * KS_C + ks) * 64 + lane];
+      op.gl[rt] = *reinterpret_cast<const float4*>(ws_GL + ch * K + 16 * (RTW * wave + rt) + 4 * g);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CTB; ++ct) {
+      const int vt = (col_base >> 4) + ct;
+      op.u[ct] = *reinterpret_cast<const raw4*>(wsU + (((size_t)wave * (V / 16) + vt) * 64 + lane) * 4);
+    }
+  };
+
   // S accumulators: wave owns channel tiles RTW*wave .. RTW*wave+RTW-1
   f32x4 S[RTW][CTB];
 #pragma unroll
@@ -545,18 +795,11 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
       }
     }
 
-  int buf = 0;
-  for (int cj = cbeg; cj < cend; ++cj) {
+  // one chunk of the recurrence with operands `cur`, LDS buffer `buf`
+  auto step = [&](const Ops& cur, const int cj, const int buf) __attribute__((always_inline)) {
     const int cidx = cj - cbeg;
     const int64_t t0 = bos + (int64_t)cidx * kC;
     const int L = min(kC, len - cidx * kC);
-    const size_t ch = (size_t)cj * HV + hv;
-    const T* wsW = ws_T + ch * WsL::elems;
-    const T* wsQG = wsW + WsL::W;
-    const T* wsKH = wsQG + WsL::QG;
-    const T* wsP = wsKH + WsL::KH;
-    const T* wsU = wsP + WsL::P;
-    const float* wsGL = ws_GL + ch * K;
 
     // (1) publish S as B fragments: k-step ks is owned by the wave holding its channels
 #pragma unroll
@@ -567,9 +810,10 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
         if constexpr (M::KSTEP == 32) {
           // channel tile pair (2ks, 2ks+1) -> k-step ks; this tile fills half a fragment
           const int ks = tileK >> 1, half = tileK & 1;
-          bf16* dst = reinterpret_cast<bf16*>(&sS[buf][ks][ct][lane]) + 4 * half;
+          bf16x4 x;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = (bf16)S[rt][ct][e];
+          for (int e = 0; e < 4; ++e) x[e] = (bf16)S[rt][ct][e];
+          *(reinterpret_cast<bf16x4*>(&sS[buf][ks][ct][lane]) + half) = x;
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -590,26 +834,23 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
       for (int ct = 0; ct < CTB; ++ct) ws_[ct] = zero4();
 #pragma unroll
       for (int ks = 0; ks < KS_K; ++ks) {
-        const F a = reinterpret_cast<const F*>(wsW)[((size_t)wave * KS_K + ks) * 64 + lane];
 #pragma unroll
-        for (int ct = 0; ct < CTB; ++ct) ws_[ct] = M::mma(a, sS[buf][ks][ct][lane], ws_[ct]);
+        for (int ct = 0; ct < CTB; ++ct) ws_[ct] = M::mma(cur.w[ks], sS[buf][ks][ct][lane], ws_[ct]);
       }
 #pragma unroll
-      for (int ct = 0; ct < CTB; ++ct) {
-        const int vt = (col_base >> 4) + ct;
-        const T* u = wsU + (((size_t)wave * (V / 16) + vt) * 64 + lane) * 4;
+      for (int ct = 0; ct < CTB; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) D[ct][e] = to_f32(u[e]) - ws_[ct][e];
-      }
+        for (int e = 0; e < 4; ++e) D[ct][e] = R4::get(cur.u[ct], e) - ws_[ct][e];
     }
     // publish Delta as B fragments (contraction over tokens)
 #pragma unroll
     for (int ct = 0; ct < CTB; ++ct) {
       if constexpr (M::KSTEP == 32) {
         const int ks = wave >> 1, half = wave & 1;
-        bf16* dst = reinterpret_cast<bf16*>(&sD[ks][ct][lane]) + 4 * half;
+        bf16x4 x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = (bf16)D[ct][e];
+        for (int e = 0; e < 4; ++e) x[e] = (bf16)D[ct][e];
+        *(reinterpret_cast<bf16x4*>(&sD[ks][ct][lane]) + half) = x;
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -621,23 +862,32 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     }
     __syncthreads();
 
-    // (3) output rows of token tile `wave`: O = (Q~ Gamma) S0 + P Delta
+    // (3) S = Diag(Gamma_last) S + Khat^T Delta for the wave's channel tiles
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const float gl[4] = {cur.gl[rt].x, cur.gl[rt].y, cur.gl[rt].z, cur.gl[rt].w};
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[rt][ct][e] *= gl[e];
+#pragma unroll
+      for (int ks = 0; ks < KS_C; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < CTB; ++ct) S[rt][ct] = M::mma(cur.kh[rt][ks], sD[ks][ct][lane], S[rt][ct]);
+    }
+    // (4) output rows of token tile `wave`: O = (Q~ Gamma) S0 + P Delta
     {
       f32x4 O[CTB];
 #pragma unroll
       for (int ct = 0; ct < CTB; ++ct) O[ct] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < KS_K; ++ks) {
-        const F a = reinterpret_cast<const F*>(wsQG)[((size_t)wave * KS_K + ks) * 64 + lane];
+      for (int ks = 0; ks < KS_K; ++ks)
 #pragma unroll
-        for (int ct = 0; ct < CTB; ++ct) O[ct] = M::mma(a, sS[buf][ks][ct][lane], O[ct]);
-      }
+        for (int ct = 0; ct < CTB; ++ct) O[ct] = M::mma(cur.qg[ks], sS[buf][ks][ct][lane], O[ct]);
 #pragma unroll
-      for (int ks = 0; ks < KS_C; ++ks) {
-        const F a = reinterpret_cast<const F*>(wsP)[((size_t)wave * KS_C + ks) * 64 + lane];
+      for (int ks = 0; ks < KS_C; ++ks)
 #pragma unroll
-        for (int ct = 0; ct < CTB; ++ct) O[ct] = M::mma(a, sD[ks][ct][lane], O[ct]);
-      }
+        for (int ct = 0; ct < CTB; ++ct) O[ct] = M::mma(cur.p[ks], sD[ks][ct][lane], O[ct]);
 #pragma unroll
       for (int ct = 0; ct < CTB; ++ct) {
         const int col = col_base + 16 * ct + l16;
@@ -648,25 +898,20 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
         }
       }
     }
-    // (4) S = Diag(Gamma_last) S + Khat^T Delta for the wave's channel tiles
-#pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-      const int tileK = RTW * wave + rt;
-      float gl[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) gl[e] = wsGL[16 * tileK + 4 * g + e];
-#pragma unroll
-      for (int ct = 0; ct < CTB; ++ct)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S[rt][ct][e] *= gl[e];
-#pragma unroll
-      for (int ks = 0; ks < KS_C; ++ks) {
-        const F a = reinterpret_cast<const F*>(wsKH)[((size_t)tileK * KS_C + ks) * 64 + lane];
-#pragma unroll
-        for (int ct = 0; ct < CTB; ++ct) S[rt][ct] = M::mma(a, sD[ks][ct][lane], S[rt][ct]);
-      }
-    }
-    buf ^= 1;
+  };
+
+  // two operand sets, unrolled by two so the next chunk's loads stay in flight
+  Ops opA, opB;
+  load_ops(cbeg, opA);
+  // (loads are unconditional -- the last chunk is simply fetched again -- so
+  // the number of loads in flight is the same on every path)
+  for (int cj = cbeg;; cj += 2) {
+    load_ops(min(cj + 1, cend - 1), opB);
+    step(opA, cj, 0);
+    if (cj + 1 >= cend) break;
+    load_ops(min(cj + 2, cend - 1), opA);
+    step(opB, cj + 1, 1);
+    if (cj + 2 >= cend) break;
   }
 
   if (write_final) {
@@ -690,6 +935,13 @@ inline int64_t max_chunks(const kda_dims& d, bool varlen) {
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline int scan_block_v(int64_t chains, int V) {
+  constexpr int64_t kCUs = 256;
+  int bv = 64;
+  while (bv > 16 && chains * (V / bv) < kCUs) bv >>= 1;
+  return bv > V ? V : bv;
+}
 
 template <typename T, int K, int V>
 size_t ws_bytes_t(const kda_dims& d, bool varlen) {
@@ -726,10 +978,20 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  constexpr int BV = (V >= 128) ? 32 : 16;
-  hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BV>), dim3((unsigned)(d.N * d.HV), V / BV),
-                     dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL,
-                     (const int*)ws_int, cu, h0, d.N, d.T, d.HV, write_final, (T*)o, ht);
+  // V-block width of the scan: every V block of a chain re-reads the chain's
+  // W, Q~Gamma, Khat and P from L2, so blocks are as wide as possible while
+  // the grid still has a workgroup for every compute unit.
+  const int64_t chains = (int64_t)d.N * d.HV;
+  const int bv = scan_block_v(chains, V);
+  auto launch_scan = [&](auto bvc) {
+    constexpr int BVC = decltype(bvc)::value;
+    hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC>), dim3((unsigned)chains, V / BVC),
+                       dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL,
+                       (const int*)ws_int, cu, h0, d.N, d.T, d.HV, write_final, (T*)o, ht);
+  };
+  if (bv >= 64) launch_scan(std::integral_constant<int, 64>());
+  else if (bv == 32) launch_scan(std::integral_constant<int, 32>());
+  else launch_scan(std::integral_constant<int, 16>());
   return hipGetLastError();
 }
 

@@ -18,8 +18,18 @@ namespace kda {
 constexpr int kGateTile = 64;
 constexpr int kGateThreads = 256;
 
+constexpr float kLn2 = 0.6931471805599453f;
+
+// softplus(x) = ln(1 + e^x) = max(x, 0) + ln(1 + z), z = e^{-|x|} in (0, 1],
+// on the transcendental unit. ln(1 + z) uses the classic correction
+// ln(u) * z / (u - 1) with u = 1 + z (u - 1 is exact), which keeps full
+// relative accuracy for small z. Above 20 the result is x itself.
 __device__ __forceinline__ float softplus_f32(float x) {
-  return x > 20.f ? x : log1pf(expf(x));
+  if (x > 20.f) return x;
+  const float z = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+  const float u = 1.f + z;
+  const float l = (u == 1.f) ? z : __builtin_amdgcn_logf(u) * kLn2 * (z / (u - 1.f));
+  return fmaxf(x, 0.f) + l;
 }
 
 template <int VEC>
@@ -89,29 +99,38 @@ gate_cumsum_kernel(const float* __restrict__ in, int is_raw, const float* __rest
       }
     }
   }
-  for (int i = 0; i < kGateTile; ++i) {
-    const int64_t t = t_a + i;
-    const int64_t cs = s_cstart[i];
-    if (cs < 0) continue;  // outside the tensor or in the capacity tail
-    if (cs == t) {
+  // main pass: BATCH tokens of loads in flight, then the scan and the stores
+  // (a thread only ever touches its own elements, so in-place per-token use is safe)
+  constexpr int BATCH = 16;
+  for (int i0 = 0; i0 < kGateTile; i0 += BATCH) {
+    float g[BATCH][VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    for (int b = 0; b < BATCH; ++b) {
+      if (s_cstart[i0 + b] >= 0) gate_of(t_a + i0 + b, g[b]);
     }
-    float g[VEC];
-    gate_of(t, g);
-    float r[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      acc[e] += g[e];
-      r[e] = acc[e] * kLog2e;
-    }
-    float* p = out + t * row + f0;
-    if constexpr (VEC == 4) {
-      *reinterpret_cast<float4*>(p) = make_float4(r[0], r[1], r[2], r[3]);
-    } else if constexpr (VEC == 2) {
-      *reinterpret_cast<float2*>(p) = make_float2(r[0], r[1]);
-    } else {
-      *p = r[0];
+    for (int b = 0; b < BATCH; ++b) {
+      const int64_t t = t_a + i0 + b;
+      const int64_t cs = s_cstart[i0 + b];
+      if (cs < 0) continue;  // outside the tensor or in the capacity tail
+      if (cs == t) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+      }
+      float r[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        acc[e] += g[b][e];
+        r[e] = acc[e] * kLog2e;
+      }
+      float* p = out + t * row + f0;
+      if constexpr (VEC == 4) {
+        *reinterpret_cast<float4*>(p) = make_float4(r[0], r[1], r[2], r[3]);
+      } else if constexpr (VEC == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(r[0], r[1]);
+      } else {
+        *p = r[0];
+      }
     }
   }
 }

@@ -89,7 +89,8 @@ const char* kda_status_string(kda_status s);
  *            chunk, chunks tiling every sequence from its own first token
  *            (the last chunk may be partial). chunk_size == 1 gives the
  *            per-token log2 decay consumed by kda_recurrent_fwd; chunk_size
- *            == 64 gives the input of kda_chunk_fwd. gate_out may equal gate_in.
+ *            == 64 gives the input of kda_chunk_fwd. gate_out may equal gate_in
+ *            only when chunk_size == 1 (else KDA_ERR_ALIAS).
  *   Supports chunk_size in [1, 64] (ordinarily 1 or 64), any K, HV.
  */
 kda_status kda_gate_cumsum(const kda_dims* dims, const float* gate_in, int32_t gate_in_is_raw,
@@ -109,7 +110,9 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_dims* dims, kda_dtype dtype, int3
  *          (may equal initial_state).
  *   workspace: device scratch of at least kda_chunk_fwd_workspace_bytes();
  *          its contents are scratch on entry and on return.
- *   Supported: K, V in {64, 128}; chunk_size == 64; FP32 or BF16.
+ *   Supported: K, V in {64, 128}; chunk_size == 64; FP32 or BF16; q, k, v
+ *   and gate 16-byte aligned, workspace 256-byte aligned (else
+ *   KDA_ERR_UNSUPPORTED).
  *   Arithmetic: FP32 accumulation and FP32 state; for BF16 inputs the
  *   matrix products take bf16 operands on the matrix cores.
  */
