@@ -30,7 +30,7 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE
            4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_ALIAS", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_LAUNCH"}
 
 EXPORTED = ("kda_status_string", "kda_gate_cumsum", "kda_chunk_fwd_workspace_bytes",
-            "kda_chunk_fwd", "kda_recurrent_fwd")
+            "kda_chunk_fwd", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_recurrent_fwd")
 
 
 class KdaDims(ctypes.Structure):
@@ -62,6 +62,10 @@ def _lib():
         lib.kda_chunk_fwd_workspace_bytes.restype = sz
         lib.kda_chunk_fwd.argtypes = [dims, ctypes.c_int, p, p, p, p, p, p, p, i32, i32, p, p, p, sz, p]
         lib.kda_chunk_fwd.restype = ctypes.c_int
+        lib.kda_chunk_bwd_workspace_bytes.argtypes = [dims, ctypes.c_int, i32]
+        lib.kda_chunk_bwd_workspace_bytes.restype = sz
+        lib.kda_chunk_bwd.argtypes = [dims, ctypes.c_int] + [p] * 7 + [i32] + [p] * 8 + [p, sz, p]
+        lib.kda_chunk_bwd.restype = ctypes.c_int
         lib.kda_recurrent_fwd.argtypes = [dims, ctypes.c_int, p, p, p, p, p, p, p, i32, p, p, p]
         lib.kda_recurrent_fwd.restype = ctypes.c_int
         _LIB = lib
@@ -158,6 +162,32 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     return o, final_state
 
 
+def chunk_kda_bwd(q, k, v, gate, beta, initial_state, do, dht=None, *, cu_seqlens=None,
+                  chunk_size: int = 64, workspace: Optional[torch.Tensor] = None):
+    """Steps B1..B3 (kda_chunk_bwd). Returns a dict with dq, dk (shape of q),
+    dv (shape of v), dg (FP32, w.r.t. the per-token natural-log gate), dbeta
+    and dh0 (FP32 [N, HV, K, V])."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (do, "do"),
+                 (initial_state, "initial_state"), (dht, "dht"), (cu_seqlens, "cu_seqlens")):
+        _check(t, n)
+    d = _dims(q, v, cu_seqlens)
+    dt = _dtype_code(q)
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    dg = torch.zeros_like(gate)
+    dbeta = torch.zeros_like(beta)
+    dh0 = torch.empty((d.N, d.HV, d.K, d.V), device=q.device, dtype=torch.float32)
+    need = int(_lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(d), dt, int(chunk_size)))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    rc = _lib().kda_chunk_bwd(ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+                              _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), _ptr(do),
+                              _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta),
+                              _ptr(dh0), _ptr(workspace), workspace.numel(), _stream())
+    if rc:
+        raise KdaError("kda_chunk_bwd", rc)
+    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=dh0)
+
+
 def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
                   output_final_state: bool = False, o: Optional[torch.Tensor] = None,
                   final_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
@@ -186,5 +216,5 @@ def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     return o, final_state
 
 
-__all__ = ["gate_cumsum", "chunk_kda", "recurrent_kda", "chunk_workspace_bytes", "load",
+__all__ = ["gate_cumsum", "chunk_kda", "chunk_kda_bwd", "recurrent_kda", "chunk_workspace_bytes", "load",
            "KdaDims", "KdaError", "LIB_PATH", "EXPORTED", "KDA_FP32", "KDA_BF16"]

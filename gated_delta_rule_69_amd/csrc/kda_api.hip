@@ -140,6 +140,56 @@ kda_status kda_chunk_fwd(const kda_dims* d, kda_dtype dt, const void* q, const v
              : KDA_ERR_LAUNCH;
 }
 
+size_t kda_chunk_bwd_workspace_bytes(const kda_dims* d, kda_dtype dt, int32_t chunk_size) {
+  if (!d || !valid_dtype(dt) || chunk_size != 64) return 0;
+  if (!((d->K == 64 || d->K == 128) && (d->V == 64 || d->V == 128))) return 0;
+  if (dt == KDA_FP32 && d->K != 64) return 0;
+  if (d->N < 0 || d->T < 0 || d->B < 0 || d->HV <= 0 || d->H <= 0) return 0;
+  return kda_host::chunk_bwd_workspace_bytes(*d, dt, chunk_size);
+}
+
+kda_status kda_chunk_bwd(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                         const void* v, const float* gate, const void* beta, const float* h0,
+                         const int32_t* cu, int32_t chunk_size, const void* do_,
+                         const float* dht, void* dq, void* dk, void* dv, float* dg, void* dbeta,
+                         float* dh0, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  kda_status st = check_dims(d, cu);
+  if (st != KDA_OK) return st;
+  if (!valid_dtype(dt)) return KDA_ERR_DTYPE;
+  const bool has_tokens = (size_t)d->B * d->T > 0;
+  if (has_tokens && (!q || !k || !v || !gate || !beta || !do_ || !dq || !dk || !dv || !dg || !dbeta))
+    return KDA_ERR_NULL;
+  if (d->N > 0 && !dh0) return KDA_ERR_NULL;
+  if (chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+  if (!((d->K == 64 || d->K == 128) && (d->V == 64 || d->V == 128))) return KDA_ERR_UNSUPPORTED;
+  if (dt == KDA_FP32 && d->K != 64) return KDA_ERR_UNSUPPORTED;  // FP32 staging exceeds LDS
+  const Sizes s = sizes(d, dt);
+  const void* ins[] = {q, k, v, gate, beta, h0, do_, dht};
+  const size_t ins_n[] = {s.qk, s.qk, s.v, s.gate, s.beta, s.state, s.v, s.state};
+  const void* outs[] = {dq, dk, dv, dg, dbeta, dh0};
+  const size_t outs_n[] = {s.qk, s.qk, s.v, s.gate, s.beta, s.state};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 8; ++j)
+      if (overlaps(outs[i], outs_n[i], ins[j], ins_n[j])) return KDA_ERR_ALIAS;
+    for (int j = i + 1; j < 6; ++j)
+      if (overlaps(outs[i], outs_n[i], outs[j], outs_n[j])) return KDA_ERR_ALIAS;
+  }
+  if (d->N == 0) return KDA_OK;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)gate | (uintptr_t)do_) & 15) ||
+      ((uintptr_t)workspace & 255))
+    return KDA_ERR_UNSUPPORTED;
+  const size_t need = kda_host::chunk_bwd_workspace_bytes(*d, dt, chunk_size);
+  if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  for (int i = 0; i < 6; ++i)
+    if (overlaps(workspace, need, outs[i], outs_n[i])) return KDA_ERR_ALIAS;
+  for (int j = 0; j < 8; ++j)
+    if (overlaps(workspace, need, ins[j], ins_n[j])) return KDA_ERR_ALIAS;
+  return kda_host::launch_chunk_bwd(*d, dt, q, k, v, gate, beta, h0, cu, do_, dht, dq, dk, dv, dg,
+                                    dbeta, dh0, workspace, stream) == hipSuccess
+             ? KDA_OK
+             : KDA_ERR_LAUNCH;
+}
+
 kda_status kda_recurrent_fwd(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
                              const void* v, const float* gate, const void* beta,
                              const float* h0, const int32_t* cu, int32_t write_final, void* o,

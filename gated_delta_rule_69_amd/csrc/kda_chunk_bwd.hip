@@ -1,0 +1,1085 @@
+// Steps B1..B3: backward of the chunked KDA scan (chunk_kda backward).
+//
+// Per chunk, with the forward chunk form of kda_chunk_kernels.h, start state
+// S0, upstream dO and dS1 (gradient of the chunk's end state):
+//   dDelta = P^T dO + Khat dS1
+//   dS0    = (Q~ Gamma)^T dO + Diag(gamma) dS1 - W^T dDelta          [reverse scan]
+//   dP = tril(dO Delta^T), d(Q~Gamma) = dO S0^T, dKhat = Delta dS1^T,
+//   dgamma = rowsum(dS1 * S0), dW = -dDelta S0^T,
+//   dT = dDelta (bV)^T + dW (b Kg)^T, dv = b * T^T dDelta, dKg = b * T^T dW,
+//   dA = tril(-T^T dT T^T, -1), dAbar = b * dA,
+//   then the decay-weighted products
+//     X1_ic = sum_j dAbar_ij k_jc 2^(G2_ic - G2_jc),  X2_jc = sum_i dAbar_ij k_ic 2^(G2_ic - G2_jc)
+//     Y1_ic = sum_j dP_ij    k_jc 2^(G2_ic - G2_jc),  Y2_jc = sum_i dP_ij    q~_ic 2^(G2_ic - G2_jc)
+//   give dk = X1 + X2 + Y2 + dKhat * e_L + dKg * Gamma, dq~ = Y1 + d(Q~Gamma) * Gamma and the
+//   gradient of the natural-log cumulative gate, dG = k (X1 - X2) + q~ Y1 - k Y2 + d(Q~Gamma) Q~Gamma
+//   - dKhat Khat + dKg Kg (+ the last row's colsum(dKhat Khat) + dgamma gamma); dg is its reverse
+//   cumsum inside the chunk. This is the reverse of the gated-delta-rule chunk
+//   pipeline the "[Fix] Use unit KDA gate scale when A_log is omitted" page
+//   lists (chunk_gated_delta_rule_bwd_dhu, chunk_bwd_dv_local, chunk_bwd_dqkwg,
+//   prepare_wy_repr_bwd), written out here for the per-channel gate.
+//
+// Kernels (one stream, no host synchronisation):
+//   chunk_intra_kernel<..., BWD=true>  forward intra-chunk terms + P^T, Khat,
+//                                      (Q~Gamma)^T, W^T fragments, Abar, T.
+//   chunk_scan_kernel (ws_B != null)   forward recurrence keeping S0, Delta.
+//   chunk_rev_scan_kernel              reverse recurrence of dS per chain;
+//                                      keeps dS1 and dDelta per chunk; dh0.
+//   chunk_bwd_local_kernel             one workgroup per (chunk, value head):
+//                                      every local gradient above.
+//   gva_reduce_kernel                  dq, dk summed over the value heads
+//                                      sharing a qk head (fixed order).
+#include "kda_chunk_kernels.h"
+
+namespace kda {
+
+// ------------------------------------------------------------------ reverse scan
+template <typename T, int K, int V, int BV>
+__global__ void __launch_bounds__(kThreads)
+chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
+                      T* __restrict__ ws_B, const int* __restrict__ ws_int,
+                      const int32_t* __restrict__ cu, const T* __restrict__ dO,
+                      const float* __restrict__ dht, int N, int T_, int HV,
+                      float* __restrict__ dh0) {
+  using M = MF<T>;
+  using F = typename M::frag;
+  using WB = WsB<T, K, V>;
+  constexpr int KS_K = K / M::KSTEP;
+  constexpr int KS_C = kC / M::KSTEP;
+  constexpr int QC = kC / 16;
+  constexpr int RTW = K / 64;
+  constexpr int CTB = BV / 16;
+  constexpr int TP = 16 / (int)sizeof(T);
+  constexpr int DS = BV + TP;  // dO staging row stride
+
+  __shared__ F sS[2][KS_K][CTB][64];  // dS1 as B fragments (contraction over channels)
+  __shared__ F sD[KS_C][CTB][64];     // dDelta as B fragments (contraction over tokens)
+  __shared__ __align__(16) T sdO[kC * DS];  // dO block of the chunk, row-major
+
+  const int n = blockIdx.x / HV, hv = blockIdx.x % HV, vb = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  int64_t bos;
+  int len;
+  seq_range(cu, n, T_, &bos, &len);
+  int cbeg, cend;
+  if (cu == nullptr) {
+    const int nc = (T_ + kC - 1) / kC;
+    cbeg = n * nc;
+    cend = cbeg + nc;
+  } else {
+    cbeg = ws_int[1 + n];
+    cend = ws_int[2 + n];
+  }
+  const size_t st_base = ((size_t)n * HV + hv) * (size_t)K * V;
+  const int col_base = vb * BV;
+
+  if (len == 0) {  // empty slot: dh0 = dht
+    for (int e = tid; e < K * BV; e += kThreads) {
+      const int r = e / BV, c = col_base + e % BV;
+      const size_t off = st_base + (size_t)r * V + c;
+      uint32_t bits = dht ? reinterpret_cast<const uint32_t*>(dht)[off] : 0u;
+      reinterpret_cast<uint32_t*>(dh0)[off] = bits;
+    }
+    return;
+  }
+
+  f32x4 S[RTW][CTB];  // dS: wave owns channel tiles RTW*wave ..
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CTB; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 16 * (RTW * wave + rt) + 4 * g + e;
+        const int col = col_base + 16 * ct + l16;
+        S[rt][ct][e] = dht ? dht[st_base + (size_t)c * V + col] : 0.f;
+      }
+
+  int buf = 0;
+  for (int cj = cend - 1; cj >= cbeg; --cj) {
+    const int cidx = cj - cbeg;
+    const int64_t t0 = bos + (int64_t)cidx * kC;
+    const int L = min(kC, len - cidx * kC);
+    const size_t ch = (size_t)cj * HV + hv;
+    T* wb = ws_B + ch * WB::elems;
+    const F* fPT = reinterpret_cast<const F*>(wb + WB::oPT);
+    const F* fKHn = reinterpret_cast<const F*>(wb + WB::oKHn);
+    const F* fQGT = reinterpret_cast<const F*>(wb + WB::oQGT);
+    const F* fWT = reinterpret_cast<const F*>(wb + WB::oWT);
+    const float* gl = ws_GL + ch * K;
+
+    // stage the dO block (rows >= L are zero)
+    constexpr int UPR = BV * (int)sizeof(T) / 16;  // 16-byte units per row
+    for (int u = tid; u < kC * UPR; u += kThreads) {
+      const int row = u / UPR, cu_ = u % UPR;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (row < L)
+        x = *reinterpret_cast<const uint4*>(dO + ((t0 + row) * HV + hv) * V + col_base + cu_ * (16 / sizeof(T)));
+      *reinterpret_cast<uint4*>(sdO + row * DS + cu_ * (16 / sizeof(T))) = x;
+    }
+    // keep dS1 of this chunk for the local kernel; publish it as B fragments
+    T* dsl = wb + WB::oDS;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int tileK = RTW * wave + rt;
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dsl[(size_t)(16 * tileK + 4 * g + e) * V + col_base + 16 * ct + l16] = from_f32<T>(S[rt][ct][e]);
+        if constexpr (M::KSTEP == 32) {
+          bf16x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = (bf16)S[rt][ct][e];
+          *(reinterpret_cast<bf16x4*>(&sS[buf][tileK >> 1][ct][lane]) + (tileK & 1)) = x;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            F f;
+            M::set(f, 0, S[rt][ct][e]);
+            sS[buf][4 * tileK + e][ct][lane] = f;
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // dO as B fragments (contraction over tokens), built by every wave
+    F bdo[CTB][KS_C];
+#pragma unroll
+    for (int ct = 0; ct < CTB; ++ct)
+#pragma unroll
+      for (int p = 0; p < QC; ++p) {
+        float x4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x4[e] = to_f32(sdO[(16 * p + 4 * g + e) * DS + 16 * ct + l16]);
+        put_quad<M>(bdo[ct], p, x4);
+      }
+
+    // dDelta for token tile `wave`: Khat dS1 + P^T dO
+    f32x4 D[CTB];
+#pragma unroll
+    for (int ct = 0; ct < CTB; ++ct) D[ct] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS_K; ++ks) {
+      const F a = fKHn[((size_t)wave * KS_K + ks) * 64 + lane];
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct) D[ct] = M::mma(a, sS[buf][ks][ct][lane], D[ct]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS_C; ++ks) {
+      const F a = fPT[((size_t)wave * KS_C + ks) * 64 + lane];
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct) D[ct] = M::mma(a, bdo[ct][ks], D[ct]);
+    }
+    T* ddl = wb + WB::oDDL;
+#pragma unroll
+    for (int ct = 0; ct < CTB; ++ct) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ddl[(size_t)(16 * wave + 4 * g + e) * V + col_base + 16 * ct + l16] = from_f32<T>(D[ct][e]);
+      if constexpr (M::KSTEP == 32) {
+        bf16x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (bf16)D[ct][e];
+        *(reinterpret_cast<bf16x4*>(&sD[wave >> 1][ct][lane]) + (wave & 1)) = x;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          F f;
+          M::set(f, 0, D[ct][e]);
+          sD[4 * wave + e][ct][lane] = f;
+        }
+      }
+    }
+    __syncthreads();
+
+    // dS0 = Diag(gamma) dS1 + (Q~Gamma)^T dO - W^T dDelta
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int tileK = RTW * wave + rt;
+      const float4 gv = *reinterpret_cast<const float4*>(gl + 16 * tileK + 4 * g);
+      const float ga[4] = {gv.x, gv.y, gv.z, gv.w};
+      f32x4 neg[CTB];
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct) {
+        neg[ct] = zero4();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[rt][ct][e] *= ga[e];
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS_C; ++ks) {
+        const F aq = fQGT[((size_t)tileK * KS_C + ks) * 64 + lane];
+        const F aw = fWT[((size_t)tileK * KS_C + ks) * 64 + lane];
+#pragma unroll
+        for (int ct = 0; ct < CTB; ++ct) {
+          S[rt][ct] = M::mma(aq, bdo[ct][ks], S[rt][ct]);
+          neg[ct] = M::mma(aw, sD[ks][ct][lane], neg[ct]);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[rt][ct][e] -= neg[ct][e];
+    }
+    buf ^= 1;
+    __syncthreads();  // sdO is restaged next chunk
+  }
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CTB; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 16 * (RTW * wave + rt) + 4 * g + e;
+        const int col = col_base + 16 * ct + l16;
+        dh0[st_base + (size_t)c * V + col] = S[rt][ct][e];
+      }
+}
+
+// ------------------------------------------------------------------ local gradients
+template <typename T, int K, int V>
+struct BwdLds {
+  static constexpr int TP = 16 / (int)sizeof(T);
+  static constexpr int VB = 32;             // V columns per phase-1 block
+  static constexpr int GS = K + 4;          // G2 (floats)
+  static constexpr int KSTR = K + TP;       // k, q, dW, b*Kg (elements of T)
+  static constexpr int TS = kC + 4;         // T (floats)
+  static constexpr int CS = kC + TP;        // C x C matrices and transposed C x K (elements of T)
+  static constexpr int BS = VB + TP;        // phase-1 blocks
+  static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+  static constexpr size_t szG = (size_t)kC * GS * 4;
+  static constexpr size_t szK = (size_t)kC * KSTR * sizeof(T);
+  static constexpr size_t szT = (size_t)kC * TS * 4;
+  static constexpr size_t szQ = (size_t)kC * KSTR * sizeof(T);
+  // phase 1: dO, Delta, dDelta, v blocks [C][BS]; S0, dS1 blocks [K][BS]
+  static constexpr size_t p1 = (4 * (size_t)kC + 2 * (size_t)K) * BS * sizeof(T);
+  // phase 1.5: dP, dP^T [C][CS]
+  static constexpr size_t p15 = 2 * (size_t)kC * CS * sizeof(T);
+  // phase 2: dW^T [K][CS] + b*Kg [C][KSTR]; later dT^T, Xm, dAbar, dAbar^T [C][CS]
+  static constexpr size_t p2a = (size_t)K * CS * sizeof(T) + (size_t)kC * KSTR * sizeof(T);
+  static constexpr size_t p2b = 4 * (size_t)kC * CS * sizeof(T);
+  static constexpr size_t szX = cmax(cmax(p1, p15), cmax(p2a, p2b));
+  // small arrays: per-wave column sums [4][K], dgamma [K], row sums [C] x 3
+  static constexpr size_t szSmall = (4 * (size_t)K + K + 3 * (size_t)kC) * 4;
+  static constexpr size_t oG = 0, oK = oG + szG, oT = oK + szK, oQ = oT + szT, oX = oQ + szQ,
+                          oSm = oX + szX, total = oSm + szSmall;
+};
+
+// A fragments of a row-major LDS matrix: rows `row`, contraction along the row.
+template <typename M, typename E, int NQ>
+__device__ __forceinline__ void frag_rows(typename M::frag* f, const E* base, int row, int stride,
+                                          int g) {
+#pragma unroll
+  for (int p = 0; p < NQ; ++p) {
+    float v[4];
+    lds4(base + row * stride + 16 * p + 4 * g, v);
+    put_quad<M>(f, p, v);
+  }
+}
+// Fragments whose contraction runs down a column of a row-major LDS matrix.
+template <typename M, typename E, int NQ>
+__device__ __forceinline__ void frag_cols(typename M::frag* f, const E* base, int col, int stride,
+                                          int g) {
+#pragma unroll
+  for (int p = 0; p < NQ; ++p) {
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = to_f32(base[(16 * p + 4 * g + e) * stride + col]);
+    put_quad<M>(f, p, v);
+  }
+}
+
+// Quad p of a hi/lo operand pair: hi = bf16(v), lo = bf16(v - hi), so that
+// hi*a + lo*a carries about 16 mantissa bits of v (FP32 fragments: lo = 0).
+template <typename M>
+__device__ __forceinline__ void put_quad_split(typename M::frag* hi, typename M::frag* lo, int p,
+                                               const float v[4]) {
+  float h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (M::KSTEP == 32) {
+      h[e] = (float)(bf16)v[e];
+      l[e] = v[e] - h[e];
+    } else {
+      h[e] = v[e];
+      l[e] = 0.f;
+    }
+  }
+  put_quad<M>(hi, p, h);
+  put_quad<M>(lo, p, l);
+}
+
+template <typename T, int K, int V>
+__global__ void __launch_bounds__(kThreads, 1)
+chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                       const float* __restrict__ gate, const T* __restrict__ beta,
+                       const T* __restrict__ dO, const int32_t* __restrict__ cu,
+                       const int* __restrict__ ws_int, const T* __restrict__ ws_B,
+                       const float* __restrict__ ws_Bf, int N, int T_, int H, int HV, float scale,
+                       T* __restrict__ dq_out, T* __restrict__ dk_out, float* __restrict__ dq_part,
+                       float* __restrict__ dk_part, T* __restrict__ dv, float* __restrict__ dg,
+                       T* __restrict__ dbeta) {
+  using M = MF<T>;
+  using F = typename M::frag;
+  using Lds = BwdLds<T, K, V>;
+  using WB = WsB<T, K, V>;
+  constexpr int KS_C = kC / M::KSTEP;
+  constexpr int QK = K / 16, QC = kC / 16, NCT = K / 16;
+  constexpr int GS = Lds::GS, KSTR = Lds::KSTR, TS = Lds::TS, CS = Lds::CS, BS = Lds::BS;
+  constexpr int VB = Lds::VB;
+  constexpr int EPU = 16 / (int)sizeof(T);
+
+  extern __shared__ __align__(16) char smem[];
+  float* sG = reinterpret_cast<float*>(smem + Lds::oG);
+  T* sK = reinterpret_cast<T*>(smem + Lds::oK);
+  float* sT = reinterpret_cast<float*>(smem + Lds::oT);
+  T* sQ = reinterpret_cast<T*>(smem + Lds::oQ);
+  char* X = smem + Lds::oX;
+  float* sColP = reinterpret_cast<float*>(smem + Lds::oSm);  // [4][K] per-wave column sums
+  float* sDgam = sColP + 4 * K;                               // [K]
+  float* sRow = sDgam + K;                                    // [3][C] row sums (dbeta parts)
+
+  const ChunkGeo geo = chunk_geo(blockIdx.x, cu, ws_int, N, T_);
+  if (!geo.ok) return;
+  const int hv = blockIdx.y;
+  const int h = hv / (HV / H);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int L = geo.L;
+  const int64_t t0 = geo.t0;
+  const size_t ch = (size_t)blockIdx.x * HV + hv;
+  const T* wb = ws_B + ch * WB::elems;
+  const float* wTm = ws_Bf + ch * WB::elems_f;
+  const float* wAb = wTm + WB::TM;
+
+  // ---- stage G2, k, q, T; zero the small arrays
+  for (int f = tid; f < kC * K / 4; f += kThreads) {
+    const int row = f / (K / 4), c4 = f % (K / 4);
+    const int rr = row < L ? row : L - 1;
+    *reinterpret_cast<float4*>(sG + row * GS + 4 * c4) =
+        *reinterpret_cast<const float4*>(gate + ((t0 + rr) * HV + hv) * K + 4 * c4);
+  }
+  for (int f = tid; f < kC * K / EPU; f += kThreads) {
+    const int row = f / (K / EPU), cu_ = f % (K / EPU);
+    uint4 kx = make_uint4(0, 0, 0, 0), qx = kx;
+    if (row < L) {
+      kx = *reinterpret_cast<const uint4*>(k + ((t0 + row) * H + h) * K + EPU * cu_);
+      qx = *reinterpret_cast<const uint4*>(q + ((t0 + row) * H + h) * K + EPU * cu_);
+    }
+    *reinterpret_cast<uint4*>(sK + row * KSTR + EPU * cu_) = kx;
+    *reinterpret_cast<uint4*>(sQ + row * KSTR + EPU * cu_) = qx;
+  }
+  for (int f = tid; f < kC * kC / 4; f += kThreads) {
+    const int row = f / (kC / 4), c4 = f % (kC / 4);
+    *reinterpret_cast<float4*>(sT + row * TS + 4 * c4) = *reinterpret_cast<const float4*>(wTm + row * kC + 4 * c4);
+  }
+  for (int f = tid; f < 4 * K + K + 3 * kC; f += kThreads) sColP[f] = 0.f;
+  float bet[4];  // beta of the rows 16w + 4g + e this lane's accumulators cover
+  float betc;    // beta of row 16w + l16
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 16 * w + 4 * g + e;
+    bet[e] = i < L ? to_f32(beta[(t0 + i) * HV + hv]) : 0.f;
+  }
+  {
+    const int i = 16 * w + l16;
+    betc = i < L ? to_f32(beta[(t0 + i) * HV + hv]) : 0.f;
+  }
+  __syncthreads();
+
+  // persistent accumulators for token tile w: dq~, dk, dG (natural-log cumulative gate)
+  f32x4 aq[NCT], ak[NCT], aG[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) aq[ct] = ak[ct] = aG[ct] = zero4();
+
+  // ---- phase 1: contractions over V, in blocks of VB columns
+  f32x4 dP[4], dQG[NCT], dW[NCT], dKH[NCT], dT1[4];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) dP[J] = dT1[J] = zero4();
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) dQG[ct] = dW[ct] = dKH[ct] = zero4();
+  float dbU[4] = {0.f, 0.f, 0.f, 0.f};
+  float dgam_acc = 0.f;  // thread-partial of rowsum(dS1 * S0) for channel tid % K
+  {
+    T* bdO = reinterpret_cast<T*>(X);
+    T* bDl = bdO + kC * BS;
+    T* bdDl = bDl + kC * BS;
+    T* bV = bdDl + kC * BS;
+    T* bS0 = bV + kC * BS;
+    T* bdS = bS0 + K * BS;
+    constexpr int UPR = VB / EPU;  // 16-byte units per block row
+    for (int vb = 0; vb < V / VB; ++vb) {
+      const int c0 = vb * VB;
+      for (int u = tid; u < kC * UPR; u += kThreads) {
+        const int row = u / UPR, cu_ = u % UPR;
+        uint4 a = make_uint4(0, 0, 0, 0), b = a, c = a, d = a;
+        if (row < L) {
+          a = *reinterpret_cast<const uint4*>(dO + ((t0 + row) * HV + hv) * V + c0 + EPU * cu_);
+          d = *reinterpret_cast<const uint4*>(v + ((t0 + row) * HV + hv) * V + c0 + EPU * cu_);
+        }
+        b = *reinterpret_cast<const uint4*>(wb + WB::oDL + (size_t)row * V + c0 + EPU * cu_);
+        c = *reinterpret_cast<const uint4*>(wb + WB::oDDL + (size_t)row * V + c0 + EPU * cu_);
+        *reinterpret_cast<uint4*>(bdO + row * BS + EPU * cu_) = a;
+        *reinterpret_cast<uint4*>(bDl + row * BS + EPU * cu_) = b;
+        *reinterpret_cast<uint4*>(bdDl + row * BS + EPU * cu_) = c;
+        *reinterpret_cast<uint4*>(bV + row * BS + EPU * cu_) = d;
+      }
+      for (int u = tid; u < K * UPR; u += kThreads) {
+        const int row = u / UPR, cu_ = u % UPR;
+        *reinterpret_cast<uint4*>(bS0 + row * BS + EPU * cu_) =
+            *reinterpret_cast<const uint4*>(wb + WB::oS0 + (size_t)row * V + c0 + EPU * cu_);
+        *reinterpret_cast<uint4*>(bdS + row * BS + EPU * cu_) =
+            *reinterpret_cast<const uint4*>(wb + WB::oDS + (size_t)row * V + c0 + EPU * cu_);
+      }
+      __syncthreads();
+      constexpr int QV = VB / 16;
+      F aO[VB / M::KSTEP > 0 ? VB / M::KSTEP : 1], aDl[VB / M::KSTEP > 0 ? VB / M::KSTEP : 1],
+          adDl[VB / M::KSTEP > 0 ? VB / M::KSTEP : 1];
+      frag_rows<M, T, QV>(aO, bdO, 16 * w + l16, BS, g);
+      frag_rows<M, T, QV>(aDl, bDl, 16 * w + l16, BS, g);
+      frag_rows<M, T, QV>(adDl, bdDl, 16 * w + l16, BS, g);
+      constexpr int KSV = VB / M::KSTEP;
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        F bD[KSV], bVv[KSV];
+        frag_rows<M, T, QV>(bD, bDl, 16 * J + l16, BS, g);   // Delta^T: column j, contraction over v
+        frag_rows<M, T, QV>(bVv, bV, 16 * J + l16, BS, g);   // v^T
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks) {
+          dP[J] = M::mma(aO[ks], bD[ks], dP[J]);
+          dT1[J] = M::mma(adDl[ks], bVv[ks], dT1[J]);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        F bS[KSV], bdS_[KSV];
+        frag_rows<M, T, QV>(bS, bS0, 16 * ct + l16, BS, g);
+        frag_rows<M, T, QV>(bdS_, bdS, 16 * ct + l16, BS, g);
+#pragma unroll
+        for (int ks = 0; ks < KSV; ++ks) {
+          dQG[ct] = M::mma(aO[ks], bS[ks], dQG[ct]);
+          dW[ct] = M::mma(adDl[ks], bS[ks], dW[ct]);
+          dKH[ct] = M::mma(aDl[ks], bdS_[ks], dKH[ct]);
+        }
+      }
+      // T^T dDelta for token tile w (rows j) -> dv, and the v part of dbeta
+      {
+        F aTt[KS_C];
+        frag_cols<M, float, QC>(aTt, sT, 16 * w + l16, TS, g);  // T^T rows j: T[i][j] down i
+#pragma unroll
+        for (int vt = 0; vt < VB / 16; ++vt) {
+          F bdd[KS_C];
+          frag_cols<M, T, QC>(bdd, bdDl, 16 * vt + l16, BS, g);  // dDelta down i
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(aTt[ks], bdd[ks], acc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 16 * w + 4 * g + e;
+            const int col = c0 + 16 * vt + l16;
+            if (j < L) dv[((t0 + j) * HV + hv) * V + col] = from_f32<T>(bet[e] * acc[e]);
+            dbU[e] += to_f32(bV[j * BS + 16 * vt + l16]) * acc[e];
+          }
+        }
+      }
+      // dgamma partial: rowsum(dS1 * S0) over this block
+      {
+        const int c = tid % K;
+        const int parts = kThreads / K;  // threads per channel
+        const int pidx = tid / K;
+        float s = 0.f;
+        for (int x = pidx; x < VB; x += parts) s += to_f32(bdS[c * BS + x]) * to_f32(bS0[c * BS + x]);
+        dgam_acc += s;
+      }
+      __syncthreads();
+    }
+  }
+  // dgamma: reduce the thread partials per channel (fixed order)
+  {
+    float* sRed = reinterpret_cast<float*>(X);
+    sRed[tid] = dgam_acc;
+    __syncthreads();
+    if (tid < K) {
+      float s = 0.f;
+      for (int p = tid; p < kThreads; p += K) s += sRed[p];
+      sDgam[tid] = s;
+    }
+    __syncthreads();
+  }
+  // dbeta (v part): rowsum over the 16 lanes of each lane group
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float x = dbU[e];
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    dbU[e] = x;
+  }
+  if (l16 == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sRow[16 * w + 4 * g + e] = dbU[e];
+  }
+
+  // consume d(Q~Gamma) and dKhat; keep per-wave column sums of dKhat * Khat
+  float colp[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int c = 16 * ct + l16;
+    const float glast = sG[(L - 1) * GS + c];
+    float cs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * w + 4 * g + e;
+      const float gi = sG[i * GS + c];
+      const float Gam = ex2(gi);
+      const float qs = to_f32(sQ[i * KSTR + c]) * scale;
+      const float kk = to_f32(sK[i * KSTR + c]);
+      const float eL = ex2(glast - gi);
+      aq[ct][e] += dQG[ct][e] * Gam;
+      aG[ct][e] += dQG[ct][e] * qs * Gam;
+      ak[ct][e] += dKH[ct][e] * eL;
+      const float tt = dKH[ct][e] * kk * eL;
+      aG[ct][e] -= tt;
+      cs += tt;
+    }
+    cs += __shfl_xor(cs, 16);
+    cs += __shfl_xor(cs, 32);
+    colp[ct] = cs;
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) sColP[w * K + 16 * ct + l16] = colp[ct];
+  }
+  // dT1 = dDelta (b v)^T: scale column j by beta_j
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    const int j = 16 * J + l16;
+    const float bj = j < L ? to_f32(beta[(t0 + j) * HV + hv]) : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dT1[J][e] *= bj;
+  }
+  // dP (lower, inclusive) into LDS, both orientations
+  {
+    T* sdP = reinterpret_cast<T*>(X);
+    T* sdPT = sdP + kC * CS;
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g + e, j = 16 * J + l16;
+        const T x = from_f32<T>((j <= i) ? dP[J][e] : 0.f);
+        sdP[i * CS + j] = x;
+        sdPT[j * CS + i] = x;
+      }
+  }
+  __syncthreads();
+
+  // ---- decay-weighted products
+  // fast single-reference path for the diagonal tile when its gate range fits
+  float rng = 0.f;
+#pragma unroll
+  for (int p = 0; p < QK; ++p) {
+    float a0[4], a1[4];
+    lds4(sG + (16 * w) * GS + 16 * p + 4 * g, a0);
+    lds4(sG + (16 * w + 15) * GS + 16 * p + 4 * g, a1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rng = fmaxf(rng, a0[e] - a1[e]);
+  }
+  rng = fmaxf(rng, __shfl_xor(rng, 16));
+  rng = fmaxf(rng, __shfl_xor(rng, 32));
+  const bool fast = rng <= kFastRange;
+
+  // Z pattern: out(i, c) = sum_j Mm[i][j] Xs[j][c] 2^(G2_i - G2_j), rows i of tile w.
+  // Reference r = 16w: operands Xs_j 2^(G2_r - G2_j) (<= 1 for j < r; <= 2^112 on
+  // the diagonal tile in the fast path), output times 2^(G2_i - G2_r) (<= 1).
+  auto zprod = [&](f32x4* out, const T* Mm, const T* Xs, float xscale) {
+    const int r = 16 * w;
+    F am[KS_C];
+    frag_rows<M, T, QC>(am, Mm, 16 * w + l16, CS, g);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = 16 * ct + l16;
+      const float gr = sG[r * GS + c];
+      F bx[KS_C], bl[KS_C];
+#pragma unroll
+      for (int p = 0; p < QC; ++p) {
+        float x4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * p + 4 * g + e;
+          const bool on = (j < r) || (fast && j < r + 16);
+          x4[e] = on ? to_f32(Xs[j * KSTR + c]) * xscale * ex2(gr - sG[j * GS + c]) : 0.f;
+        }
+        put_quad_split<M>(bx, bl, p, x4);
+      }
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS_C; ++ks) {
+        acc = M::mma(am[ks], bx[ks], acc);
+        if constexpr (M::KSTEP == 32) acc = M::mma(am[ks], bl[ks], acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = r + 4 * g + e;
+        float z = acc[e] * ex2(sG[i * GS + c] - gr);
+        if (!fast) {  // diagonal tile, exact elementwise
+          for (int j = r; j <= i; ++j)
+            z += to_f32(Mm[i * CS + j]) * to_f32(Xs[j * KSTR + c]) * xscale * ex2(sG[i * GS + c] - sG[j * GS + c]);
+        }
+        out[ct][e] = z;
+      }
+    }
+  };
+  // Z' pattern: out(j, c) = sum_i MmT[j][i] Xs[i][c] 2^(G2_i - G2_j), rows j of tile w.
+  // Reference r = 16w + 15: operands Xs_i 2^(G2_i - G2_r) (<= 1 for i > r),
+  // output times 2^(G2_r - G2_j) (<= 1).
+  auto zprodT = [&](f32x4* out, const T* MmT, const T* Xs, float xscale) {
+    const int r = 16 * w + 15;
+    F am[KS_C];
+    frag_rows<M, T, QC>(am, MmT, 16 * w + l16, CS, g);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = 16 * ct + l16;
+      const float gr = sG[r * GS + c];
+      F bx[KS_C], bl[KS_C];
+#pragma unroll
+      for (int p = 0; p < QC; ++p) {
+        float x4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * p + 4 * g + e;
+          const bool on = (i > r) || (fast && i > r - 16);
+          x4[e] = on ? to_f32(Xs[i * KSTR + c]) * xscale * ex2(sG[i * GS + c] - gr) : 0.f;
+        }
+        put_quad_split<M>(bx, bl, p, x4);
+      }
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS_C; ++ks) {
+        acc = M::mma(am[ks], bx[ks], acc);
+        if constexpr (M::KSTEP == 32) acc = M::mma(am[ks], bl[ks], acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 16 * w + 4 * g + e;
+        float z = acc[e] * ex2(gr - sG[j * GS + c]);
+        if (!fast) {
+          for (int i = j; i <= r; ++i)
+            z += to_f32(MmT[j * CS + i]) * to_f32(Xs[i * KSTR + c]) * xscale * ex2(sG[i * GS + c] - sG[j * GS + c]);
+        }
+        out[ct][e] = z;
+      }
+    }
+  };
+
+  {
+    const T* sdP = reinterpret_cast<const T*>(X);
+    const T* sdPT = sdP + kC * CS;
+    f32x4 z[NCT];
+    zprod(z, sdP, sK, 1.f);  // Y1
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g + e, c = 16 * ct + l16;
+        aq[ct][e] += z[ct][e];
+        aG[ct][e] += to_f32(sQ[i * KSTR + c]) * scale * z[ct][e];
+      }
+    zprodT(z, sdPT, sQ, scale);  // Y2
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 16 * w + 4 * g + e, c = 16 * ct + l16;
+        ak[ct][e] += z[ct][e];
+        aG[ct][e] -= to_f32(sK[j * KSTR + c]) * z[ct][e];
+      }
+  }
+  __syncthreads();  // q, dP, dP^T dead
+
+  // ---- phase 2: dT, T^T dW, dA
+  {
+    T* sdW = sQ;                                  // [C][KSTR] row-major dW
+    T* sdWT = reinterpret_cast<T*>(X);            // [K][CS]
+    T* sBKg = sdWT + K * CS;                      // [C][KSTR] b * k * Gamma
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g + e, c = 16 * ct + l16;
+        const T x = from_f32<T>(-dW[ct][e]);
+        sdW[i * KSTR + c] = x;
+        sdWT[c * CS + i] = x;
+      }
+    for (int f = tid; f < kC * K / 4; f += kThreads) {
+      const int m = f / (K / 4), c4 = f % (K / 4);
+      float km[4], gm[4];
+      lds4(sK + m * KSTR + 4 * c4, km);
+      lds4(sG + m * GS + 4 * c4, gm);
+      const float bm = m < L ? to_f32(beta[(t0 + m) * HV + hv]) : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sBKg[m * KSTR + 4 * c4 + e] = from_f32<T>(bm * km[e] * ex2(gm[e]));
+    }
+    __syncthreads();
+    // dT = dT1 + dW (b Kg)^T, rows i of tile w
+    f32x4 dT[4];
+    {
+      F adw[K / M::KSTEP];
+      frag_rows<M, T, QK>(adw, sdW, 16 * w + l16, KSTR, g);
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        F bk[K / M::KSTEP];
+        frag_rows<M, T, QK>(bk, sBKg, 16 * J + l16, KSTR, g);
+        dT[J] = dT1[J];
+#pragma unroll
+        for (int ks = 0; ks < K / M::KSTEP; ++ks) dT[J] = M::mma(adw[ks], bk[ks], dT[J]);
+      }
+    }
+    // T^T dW, rows j of tile w -> dKg = b_j (T^T dW)
+    {
+      F aTt[KS_C];
+      frag_cols<M, float, QC>(aTt, sT, 16 * w + l16, TS, g);
+      float dbw[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        F bw[KS_C];
+        frag_rows<M, T, QC>(bw, sdWT, 16 * ct + l16, CS, g);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(aTt[ks], bw[ks], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * w + 4 * g + e, c = 16 * ct + l16;
+          const float Gam = ex2(sG[j * GS + c]);
+          const float kg = to_f32(sK[j * KSTR + c]) * Gam;
+          const float dkg = bet[e] * acc[e];
+          ak[ct][e] += dkg * Gam;
+          aG[ct][e] += dkg * kg;
+          dbw[e] += kg * acc[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = dbw[e];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        dbw[e] = x;
+      }
+      if (l16 == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sRow[kC + 16 * w + 4 * g + e] = dbw[e];
+      }
+    }
+    __syncthreads();  // dW, dW^T, b Kg dead
+    T* sdTT = reinterpret_cast<T*>(X);  // dT transposed [j][i]
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sdTT[(16 * J + l16) * CS + 16 * w + 4 * g + e] = from_f32<T>(dT[J][e]);
+    __syncthreads();
+    // Xm = T^T dT, rows a of tile w
+    T* sXm = sdTT + kC * CS;
+    {
+      F aTt[KS_C];
+      frag_cols<M, float, QC>(aTt, sT, 16 * w + l16, TS, g);
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        F bt[KS_C];
+        frag_rows<M, T, QC>(bt, sdTT, 16 * J + l16, CS, g);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(aTt[ks], bt[ks], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sXm[(16 * w + 4 * g + e) * CS + 16 * J + l16] = from_f32<T>(acc[e]);
+      }
+    }
+    __syncthreads();
+    // dA = -Xm T^T (strictly lower), dAbar = b dA; Abar part of dbeta
+    T* sdAb = sXm + kC * CS;
+    T* sdAbT = sdAb + kC * CS;
+    {
+      F ax[KS_C];
+      frag_rows<M, T, QC>(ax, sXm, 16 * w + l16, CS, g);
+      float dba[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        F bt[KS_C];
+        frag_rows<M, float, QC>(bt, sT, 16 * J + l16, TS, g);  // T^T column c = T row c
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(ax[ks], bt[ks], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int a = 16 * w + 4 * g + e, c = 16 * J + l16;
+          const float da = (c < a) ? -acc[e] : 0.f;
+          dba[e] += wAb[a * kC + c] * da;
+          const T x = from_f32<T>(bet[e] * da);
+          sdAb[a * CS + c] = x;
+          sdAbT[c * CS + a] = x;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = dba[e];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        dba[e] = x;
+      }
+      if (l16 == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sRow[2 * kC + 16 * w + 4 * g + e] = dba[e];
+      }
+    }
+    __syncthreads();
+    f32x4 z[NCT];
+    zprod(z, sdAb, sK, 1.f);  // X1
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g + e, c = 16 * ct + l16;
+        ak[ct][e] += z[ct][e];
+        aG[ct][e] += to_f32(sK[i * KSTR + c]) * z[ct][e];
+      }
+    zprodT(z, sdAbT, sK, 1.f);  // X2
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 16 * w + 4 * g + e, c = 16 * ct + l16;
+        ak[ct][e] += z[ct][e];
+        aG[ct][e] -= to_f32(sK[j * KSTR + c]) * z[ct][e];
+      }
+  }
+
+  // ---- last row: colsum(dKhat * Khat) + dgamma * gamma; reverse cumsum; outputs
+  __syncthreads();
+  {
+    float* sTile = reinterpret_cast<float*>(X);  // per-wave column totals [4][K]
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = 16 * ct + l16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g + e;
+        if (i == L - 1) {
+          const float cs = sColP[c] + sColP[K + c] + sColP[2 * K + c] + sColP[3 * K + c];
+          aG[ct][e] += cs + sDgam[c] * ex2(sG[(L - 1) * GS + c]);
+        }
+      }
+      float tot = aG[ct][0] + aG[ct][1] + aG[ct][2] + aG[ct][3];
+      tot += __shfl_xor(tot, 16);
+      tot += __shfl_xor(tot, 32);
+      if (g == 0) sTile[w * K + c] = tot;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = 16 * ct + l16;
+      float later = 0.f;  // rows of the later tiles
+      for (int w2 = w + 1; w2 < 4; ++w2) later += sTile[w2 * K + c];
+      // suffix sums inside the tile: rows 4g..4g+3 in lanes of group g
+      float s3 = aG[ct][3], s2 = s3 + aG[ct][2], s1 = s2 + aG[ct][1], s0 = s1 + aG[ct][0];
+      float grp = s0;  // total of this lane group's 4 rows
+      float after = 0.f;
+      const float g1 = __shfl_xor(grp, 16), g2 = __shfl_xor(grp, 32), g3 = __shfl_xor(grp, 48);
+      // lane group g receives the totals of groups g^1, g^2, g^3; add those with a larger index
+      if ((g ^ 1) > g) after += g1;
+      if ((g ^ 2) > g) after += g2;
+      if ((g ^ 3) > g) after += g3;
+      const float base = later + after;
+      const float sfx[4] = {s0 + base, s1 + base, s2 + base, s3 + base};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * w + 4 * g + e;
+        if (i < L) dg[((t0 + i) * HV + hv) * K + c] = sfx[e];
+      }
+    }
+  }
+  // dq, dk (per value head; summed over the GVA group later when HV > H), dbeta
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int c = 16 * ct + l16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * w + 4 * g + e;
+      if (i >= L) continue;
+      const float dqv = aq[ct][e] * scale;
+      const float dkv = ak[ct][e];
+      if (dq_part) {
+        dq_part[((t0 + i) * HV + hv) * K + c] = dqv;
+        dk_part[((t0 + i) * HV + hv) * K + c] = dkv;
+      } else {
+        dq_out[((t0 + i) * H + h) * K + c] = from_f32<T>(dqv);
+        dk_out[((t0 + i) * H + h) * K + c] = from_f32<T>(dkv);
+      }
+    }
+  }
+  if (tid < kC && tid < L) {
+    const float db = sRow[tid] + sRow[kC + tid] + sRow[2 * kC + tid];
+    dbeta[(t0 + tid) * HV + hv] = from_f32<T>(db);
+  }
+  (void)betc;
+}
+
+// dq, dk of a qk head = sum over its HV/H value heads, in head order.
+template <typename T>
+__global__ void gva_reduce_kernel(const float* __restrict__ dq_part, const float* __restrict__ dk_part,
+                                  const int32_t* __restrict__ cu, int N, int64_t n_tok, int H, int HV,
+                                  int K, T* __restrict__ dq, T* __restrict__ dk) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_tok = (int64_t)H * K;
+  if (idx >= n_tok * per_tok) return;
+  const int64_t t = idx / per_tok;
+  if (cu && t >= cu[N]) return;
+  const int h = (int)((idx % per_tok) / K), c = (int)(idx % K);
+  const int G = HV / H;
+  float a = 0.f, b = 0.f;
+  for (int j = 0; j < G; ++j) {
+    const int64_t o = (t * HV + h * G + j) * K + c;
+    a += dq_part[o];
+    b += dk_part[o];
+  }
+  dq[idx] = from_f32<T>(a);
+  dk[idx] = from_f32<T>(b);
+}
+
+// ------------------------------------------------------------------ host side
+template <typename T, int K, int V>
+size_t bwd_ws_bytes_t(const kda_dims& d, bool varlen) {
+  const int64_t mc = max_chunks(d, varlen);
+  size_t b = align256(sizeof(int) * (size_t)(2 + d.N + mc));
+  b += align256((size_t)mc * d.HV * Ws<T, K, V>::bytes_T);
+  b += align256((size_t)mc * d.HV * Ws<T, K, V>::bytes_GL);
+  b += align256((size_t)mc * d.HV * WsB<T, K, V>::elems * sizeof(T));
+  b += align256((size_t)mc * d.HV * WsB<T, K, V>::elems_f * sizeof(float));
+  if (d.HV != d.H) b += 2 * align256((size_t)d.B * d.T * d.HV * K * sizeof(float));
+  return b;
+}
+
+template <typename T, int K, int V>
+hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const void* v,
+                       const float* gate, const void* beta, const float* h0, const int32_t* cu,
+                       const void* dO, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                       void* dbeta, float* dh0, void* ws, hipStream_t s) {
+  const bool varlen = cu != nullptr;
+  const int64_t mc = max_chunks(d, varlen);
+  char* p = reinterpret_cast<char*>(ws);
+  int* ws_int = reinterpret_cast<int*>(p);
+  p += align256(sizeof(int) * (size_t)(2 + d.N + mc));
+  T* ws_T = reinterpret_cast<T*>(p);
+  p += align256((size_t)mc * d.HV * Ws<T, K, V>::bytes_T);
+  float* ws_GL = reinterpret_cast<float*>(p);
+  p += align256((size_t)mc * d.HV * Ws<T, K, V>::bytes_GL);
+  T* ws_B = reinterpret_cast<T*>(p);
+  p += align256((size_t)mc * d.HV * WsB<T, K, V>::elems * sizeof(T));
+  float* ws_Bf = reinterpret_cast<float*>(p);
+  p += align256((size_t)mc * d.HV * WsB<T, K, V>::elems_f * sizeof(float));
+  float* dq_part = nullptr;
+  float* dk_part = nullptr;
+  if (d.HV != d.H) {
+    dq_part = reinterpret_cast<float*>(p);
+    p += align256((size_t)d.B * d.T * d.HV * K * sizeof(float));
+    dk_part = reinterpret_cast<float*>(p);
+  }
+  hipError_t e;
+  if (varlen) {
+    e = launch_chunk_table(cu, d.N, ws_int, (int)mc, s);
+    if (e != hipSuccess) return e;
+  }
+  const float scale = 1.0f / sqrtf((float)K);
+  if (mc > 0) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_intra_kernel<T, K, V, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)IntraLds<T, K, V>::total);
+    if (e != hipSuccess) return e;
+    const size_t lds_intra = IntraLds<T, K, V>::total;
+    hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, true>), dim3((unsigned)mc, (unsigned)d.HV),
+                       dim3(kThreads), lds_intra, s, (const T*)q, (const T*)k,
+                       (const T*)v, gate, (const T*)beta, cu, ws_int, d.N, d.T, d.H, d.HV, scale,
+                       ws_T, ws_GL, ws_B, ws_Bf);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t chains = (int64_t)d.N * d.HV;
+  // forward recurrence keeping S0 and Delta (no outputs)
+  hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, 32>), dim3((unsigned)chains, V / 32), dim3(kThreads),
+                     0, s, (const T*)ws_T, (const float*)ws_GL, (const int*)ws_int, cu, h0, d.N, d.T,
+                     d.HV, 0, (T*)nullptr, (float*)nullptr, ws_B);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((chunk_rev_scan_kernel<T, K, V, 32>), dim3((unsigned)chains, V / 32),
+                     dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL, ws_B,
+                     (const int*)ws_int, cu, (const T*)dO, dht, d.N, d.T, d.HV, dh0);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (mc > 0) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_bwd_local_kernel<T, K, V>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)BwdLds<T, K, V>::total);
+    if (e != hipSuccess) return e;
+    const size_t lds_local = BwdLds<T, K, V>::total;
+    hipLaunchKernelGGL((chunk_bwd_local_kernel<T, K, V>), dim3((unsigned)mc, (unsigned)d.HV),
+                       dim3(kThreads), lds_local, s, (const T*)q, (const T*)k,
+                       (const T*)v, gate, (const T*)beta, (const T*)dO, cu, (const int*)ws_int,
+                       (const T*)ws_B, (const float*)ws_Bf, d.N, d.T, d.H, d.HV, scale, (T*)dq,
+                       (T*)dk, dq_part, dk_part, (T*)dv, dg, (T*)dbeta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (d.HV != d.H) {
+    const int64_t n_tok = (int64_t)d.B * d.T;
+    const int64_t total = n_tok * d.H * K;
+    hipLaunchKernelGGL(gva_reduce_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       dq_part, dk_part, cu, d.N, n_tok, d.H, d.HV, K, (T*)dq, (T*)dk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace kda
+
+namespace kda_host {
+
+template <typename T>
+static size_t bwd_ws_dispatch(const kda_dims& d) {
+  auto both = [](size_t a, size_t b) { return std::max(a, b); };
+  if (d.K == 64 && d.V == 64) return both(kda::bwd_ws_bytes_t<T, 64, 64>(d, false), kda::bwd_ws_bytes_t<T, 64, 64>(d, true));
+  if (d.K == 64 && d.V == 128) return both(kda::bwd_ws_bytes_t<T, 64, 128>(d, false), kda::bwd_ws_bytes_t<T, 64, 128>(d, true));
+  if (d.K == 128 && d.V == 64) return both(kda::bwd_ws_bytes_t<T, 128, 64>(d, false), kda::bwd_ws_bytes_t<T, 128, 64>(d, true));
+  if (d.K == 128 && d.V == 128) return both(kda::bwd_ws_bytes_t<T, 128, 128>(d, false), kda::bwd_ws_bytes_t<T, 128, 128>(d, true));
+  return 0;
+}
+
+size_t chunk_bwd_workspace_bytes(const kda_dims& d, kda_dtype dt, int chunk) {
+  if (chunk != kda::kC) return 0;
+  return dt == KDA_BF16 ? bwd_ws_dispatch<kda::bf16>(d) : bwd_ws_dispatch<float>(d);
+}
+
+template <typename T>
+static hipError_t bwd_t(const kda_dims& d, const void* q, const void* k, const void* v,
+                        const float* gate, const void* beta, const float* h0, const int32_t* cu,
+                        const void* dO, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                        void* dbeta, float* dh0, void* ws, hipStream_t s) {
+#define KDA_BWD_CASE(KK, VV)                                                                    \
+  if (d.K == KK && d.V == VV)                                                                   \
+    return kda::chunk_bwd_t<T, KK, VV>(d, q, k, v, gate, beta, h0, cu, dO, dht, dq, dk, dv, dg, \
+                                       dbeta, dh0, ws, s);
+  KDA_BWD_CASE(64, 64)
+  KDA_BWD_CASE(64, 128)
+  KDA_BWD_CASE(128, 64)
+  KDA_BWD_CASE(128, 128)
+#undef KDA_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_bwd(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
+                            const void* v, const float* gate, const void* beta, const float* h0,
+                            const int32_t* cu, const void* dO, const float* dht, void* dq,
+                            void* dk, void* dv, float* dg, void* dbeta, float* dh0, void* ws,
+                            hipStream_t s) {
+  if (dt == KDA_BF16)
+    return bwd_t<kda::bf16>(d, q, k, v, gate, beta, h0, cu, dO, dht, dq, dk, dv, dg, dbeta, dh0, ws, s);
+  return bwd_t<float>(d, q, k, v, gate, beta, h0, cu, dO, dht, dq, dk, dv, dg, dbeta, dh0, ws, s);
+}
+
+}  // namespace kda_host

@@ -1,0 +1,1060 @@
+#pragma once
+// Steps A2..A6: the chunked KDA scan (chunk_kda forward) on gfx950.
+//
+// Per chunk of C = 64 tokens with start state S0, natural-log cumulative gate
+// G (here log2 units, G2) and Gamma = 2^G2, the chunk form of the per-channel
+// gated delta rule is
+//   A_ij  = b_i sum_c k_ic k_jc 2^(G2_ic - G2_jc)   (i > j)         [kkt]
+//   T     = (I + A)^-1                                              [solve_tril]
+//   W     = T diag(b) (K * Gamma),  U = T diag(b) V                 [recompute_w_u]
+//   Delta = U - W S0;  S_end = Diag(Gamma_last) S0 + Khat^T Delta   [fwd_h]
+//   O     = (Q~ * Gamma) S0 + (P o M) Delta                         [fwd_o]
+// with Khat = K * 2^(G2_last - G2), P_ij = sum_c q~_ic k_jc 2^(G2_ic - G2_jc)
+// (j <= i) and q~ = q / sqrt(K). The step names in brackets are those the
+// "[Fix] Use unit KDA gate scale when A_log is omitted" page lists for the
+// sibling gated-delta-rule op (squashed commit bodies); the per-channel
+// factors are written out for KDA here.
+//
+// Kernels (all on the caller's stream, no host synchronisation):
+//   chunk_table_kernel  varlen only: chunks per sequence -> chunk table.
+//   chunk_intra_kernel  one workgroup per (chunk, value head), fully parallel:
+//                       A and P on the matrix cores, the FP32 solve, then W,
+//                       U, Q~*Gamma, Khat^T, P and Gamma_last written to the
+//                       workspace already in matrix-core fragment order.
+//   chunk_scan_kernel   one workgroup per (sequence, value head, V block):
+//                       the sequential inter-chunk recurrence with S held in
+//                       FP32 matrix-core accumulators, fused with the output.
+//
+// Overflow-free decay products. 2^(G2_i - G2_j) for j < i is factored as
+// 2^(G2_i - G2_r) * 2^(G2_r - G2_j) with a reference token j < r <= i, so
+// both factors are <= 1 and a product of them can only underflow (harmless:
+// the true value is then below FP32 range too). Off-diagonal 16x16 tiles use
+// r = first token of the row tile. Inside a diagonal tile the pairs are split
+// by the highest bit in which the local indices differ (levels 3..0, each
+// with its own reference), plus the exact diagonal i == j. This keeps
+// unbounded gates (chunk-local cumsums far below -126 in log2 units) exact.
+#include <algorithm>
+#include <type_traits>
+
+#include "kda_common.h"
+
+namespace kda {
+
+
+constexpr int kC = 64;          // chunk size
+constexpr int kThreads = 256;   // 4 waves
+
+// ------------------------------------------------------------------ workspace layout
+template <typename T, int K, int V>
+struct Ws {
+  // per (chunk, value head), in elements of T unless noted
+  static constexpr size_t W = (size_t)kC * K;    // W fragments   [4][K/KSTEP][64][PER]
+  static constexpr size_t QG = (size_t)kC * K;   // Q~*Gamma      [4][K/KSTEP][64][PER]
+  static constexpr size_t KH = (size_t)K * kC;   // Khat^T        [K/16][C/KSTEP][64][PER]
+  static constexpr size_t P = (size_t)kC * kC;   // P             [4][C/KSTEP][64][PER]
+  static constexpr size_t U = (size_t)kC * V;    // U accum order [4][V/16][64][4]
+  static constexpr size_t elems = W + QG + KH + P + U;
+  static constexpr size_t bytes_T = elems * sizeof(T);
+  static constexpr size_t bytes_GL = (size_t)K * sizeof(float);  // Gamma_last (FP32)
+};
+
+// Extra per-(chunk, value head) workspace of the backward pass.
+template <typename T, int K, int V>
+struct WsB {
+  // elements of T
+  static constexpr size_t PT = (size_t)kC * kC;   // P^T fragments     [4][C/KSTEP][64][PER]
+  static constexpr size_t KHn = (size_t)kC * K;   // Khat fragments    [4][K/KSTEP][64][PER]
+  static constexpr size_t QGT = (size_t)K * kC;   // (Q~ Gamma)^T frags [K/16][C/KSTEP][64][PER]
+  static constexpr size_t WT = (size_t)K * kC;    // W^T fragments     [K/16][C/KSTEP][64][PER]
+  static constexpr size_t S0 = (size_t)K * V;     // chunk start state, row-major [K][V]
+  static constexpr size_t DL = (size_t)kC * V;    // Delta, row-major [C][V]
+  static constexpr size_t DS = (size_t)K * V;     // dS at the chunk end, row-major [K][V]
+  static constexpr size_t DDL = (size_t)kC * V;   // dDelta, row-major [C][V]
+  static constexpr size_t elems = PT + KHn + QGT + WT + S0 + DL + DS + DDL;
+  // FP32
+  static constexpr size_t TM = (size_t)kC * kC;   // T = (I + A)^-1, row-major [C][C]
+  static constexpr size_t AB = (size_t)kC * kC;   // Abar (A without beta), row-major [C][C]
+  static constexpr size_t elems_f = TM + AB;
+  // offsets inside one chunk-head block
+  static constexpr size_t oPT = 0, oKHn = PT, oQGT = oKHn + KHn, oWT = oQGT + QGT,
+                          oS0 = oWT + WT, oDL = oS0 + S0, oDS = oDL + DL, oDDL = oDS + DS;
+};
+
+struct ChunkGeo {
+  int ok;        // 0: no such chunk (grid over-provisioned)
+  int n;         // sequence
+  int64_t t0;    // flat index of the chunk's first token
+  int L;         // tokens in the chunk (1..64)
+};
+
+__device__ __forceinline__ ChunkGeo chunk_geo(int j, const int32_t* cu, const int* ws_int, int N,
+                                              int T) {
+  ChunkGeo r{0, 0, 0, 0};
+  if (cu == nullptr) {
+    const int nc = (T + kC - 1) / kC;
+    const int n = j / nc, c = j % nc;
+    if (n >= N) return r;
+    r.ok = 1;
+    r.n = n;
+    r.t0 = (int64_t)n * T + (int64_t)c * kC;
+    r.L = min(kC, T - c * kC);
+  } else {
+    if (j >= ws_int[0]) return r;
+    const int n = ws_int[2 + N + j];
+    const int c = j - ws_int[1 + n];
+    const int bos = cu[n], len = cu[n + 1] - bos;
+    r.ok = 1;
+    r.n = n;
+    r.t0 = bos + (int64_t)c * kC;
+    r.L = min(kC, len - c * kC);
+  }
+  return r;
+}
+
+// ------------------------------------------------------------------ intra-chunk kernel
+template <typename T, int K, int V>
+struct IntraLds {
+  static constexpr int TP = 16 / (int)sizeof(T);  // 16-byte row pad, in elements
+  static constexpr int GS = K + 4;                // G2 row stride (floats)
+  static constexpr int KSTR = K + TP;             // k / q row stride
+  static constexpr int AS = kC + 4;               // A / T row stride (floats)
+  static constexpr int VSTR = V + TP;             // b v row stride
+  static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+  static constexpr size_t R1 = cmax((size_t)kC * GS * 4, (size_t)kC * VSTR * sizeof(T));
+  static constexpr size_t R2 = (size_t)kC * KSTR * sizeof(T);
+  static constexpr size_t R3 = cmax((size_t)kC * KSTR * sizeof(T), (size_t)kC * AS * 4);
+  static constexpr size_t total = R1 + R2 + R3 + kC * 4;
+};
+
+// 2^x on the transcendental unit (v_exp_f32). Results below 2^-126 flush to
+// zero, which only drops decay products that are below FP32 range anyway.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Four consecutive LDS elements as floats (one 16- or 8-byte LDS read).
+__device__ __forceinline__ void lds4(const float* p, float o[4]) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  o[0] = x.x; o[1] = x.y; o[2] = x.z; o[3] = x.w;
+}
+__device__ __forceinline__ void lds4(const bf16* p, float o[4]) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+  o[0] = (float)x[0]; o[1] = (float)x[1]; o[2] = (float)x[2]; o[3] = (float)x[3];
+}
+
+// Element e of a 16-byte unit holding T values, as float.
+template <typename T>
+__device__ __forceinline__ float unit_elem(const uint4& u, int e) {
+  const uint32_t w = (e >> (sizeof(T) == 2 ? 1 : 0)) == 0 ? u.x
+                   : (e >> (sizeof(T) == 2 ? 1 : 0)) == 1 ? u.y
+                   : (e >> (sizeof(T) == 2 ? 1 : 0)) == 2 ? u.z : u.w;
+  if constexpr (sizeof(T) == 2) return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  else return __uint_as_float(w);
+}
+
+// Quad p of a contraction dimension holds indices 16p + 4g + e (e = 0..3) for
+// lane group g. With the kidx() order of MF<>, quad p is slots 4(p&1)..+3 of
+// bf16 fragment p/2, or FP32 fragments 4p..4p+3.
+template <typename M>
+__device__ __forceinline__ void put_quad(typename M::frag* fr, int p, const float v[4]) {
+  if constexpr (M::KSTEP == 32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) M::set(fr[p >> 1], 4 * (p & 1) + e, v[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) M::set(fr[4 * p + e], 0, v[e]);
+  }
+}
+
+// Fragment of contraction step ks built from accumulator tiles of the
+// transposed product (see MF<>): element jj comes from tile tile_of(ks, jj).
+template <typename M>
+__device__ __forceinline__ int acc_tile(int ks, int jj) {
+  return (M::KSTEP == 32) ? (2 * ks + (jj >> 2)) : (ks >> 2);
+}
+template <typename M>
+__device__ __forceinline__ int acc_elem(int ks, int jj) {
+  return (M::KSTEP == 32) ? (jj & 3) : (ks & 3);
+}
+
+// Max exponent range (log2 units) that a single reference token may span in a
+// diagonal tile: factors up to 2^112 and sums of 128 such products stay
+// finite in FP32 and bf16.
+constexpr float kFastRange = 112.f;
+
+// BWD: also write what the backward pass needs (P^T, Khat, (Q~ Gamma)^T and
+// W^T fragments, Abar and T) into ws_B / ws_Bf.
+template <typename T, int K, int V, bool BWD>
+__global__ void __launch_bounds__(kThreads, 2)
+chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                   const float* __restrict__ gate, const T* __restrict__ beta,
+                   const int32_t* __restrict__ cu, const int* __restrict__ ws_int, int N, int T_,
+                   int H, int HV, float scale, T* __restrict__ ws_T, float* __restrict__ ws_GL,
+                   T* __restrict__ ws_B, float* __restrict__ ws_Bf) {
+  using M = MF<T>;
+  using F = typename M::frag;
+  using Lds = IntraLds<T, K, V>;
+  using WsL = Ws<T, K, V>;
+  constexpr int KS_K = K / M::KSTEP;
+  constexpr int KS_C = kC / M::KSTEP;
+  constexpr int QK = K / 16;   // quads over channels
+  constexpr int QC = kC / 16;  // quads over tokens
+  constexpr int GS = Lds::GS, KSTR = Lds::KSTR, AS = Lds::AS;
+  constexpr int EPU = 16 / (int)sizeof(T);      // elements of T per 16-byte unit
+  constexpr int GU = kC * K / 4 / kThreads;     // float4 units of G2 per thread
+  constexpr int KU = kC * K / EPU / kThreads;   // 16-byte units of k (and of q) per thread
+  constexpr int VU = kC * V / EPU / kThreads;   // 16-byte units of v per thread
+  static_assert(GU >= 1 && KU >= 1 && VU >= 1, "tile shape");
+
+  extern __shared__ __align__(16) char smem[];
+  float* sG = reinterpret_cast<float*>(smem);                       // R1: G2 [C][GS], later b v
+  T* sK = reinterpret_cast<T*>(smem + Lds::R1);                     // R2: k [C][KSTR]
+  T* sQ = reinterpret_cast<T*>(smem + Lds::R1 + Lds::R2);           // R3: q [C][KSTR]
+  float* sA = reinterpret_cast<float*>(smem + Lds::R1 + Lds::R2);   // R3 later: A, then T [C][AS]
+  float* sBeta = reinterpret_cast<float*>(smem + Lds::R1 + Lds::R2 + Lds::R3);
+
+  const ChunkGeo geo = chunk_geo(blockIdx.x, cu, ws_int, N, T_);
+  if (!geo.ok) return;
+  const int hv = blockIdx.y;
+  const int h = hv / (HV / H);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int L = geo.L;
+  const int64_t t0 = geo.t0;
+  const size_t ch = (size_t)blockIdx.x * HV + hv;
+
+  // ---- 1. global loads first (16-byte units), then LDS stores
+  float4 gr[GU];
+  uint4 kr[KU], qr[KU], vr[VU];
+#pragma unroll
+  for (int u = 0; u < GU; ++u) {
+    const int f = tid + u * kThreads, row = f / (K / 4), c4 = f % (K / 4);
+    const int rr = row < L ? row : L - 1;  // pad rows repeat the last gate row
+    gr[u] = *reinterpret_cast<const float4*>(gate + ((t0 + rr) * HV + hv) * K + 4 * c4);
+  }
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int f = tid + u * kThreads, row = f / (K / EPU), cu_ = f % (K / EPU);
+    kr[u] = qr[u] = make_uint4(0, 0, 0, 0);
+    if (row < L) {
+      kr[u] = *reinterpret_cast<const uint4*>(k + ((t0 + row) * H + h) * K + EPU * cu_);
+      qr[u] = *reinterpret_cast<const uint4*>(q + ((t0 + row) * H + h) * K + EPU * cu_);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int f = tid + u * kThreads, row = f / (V / EPU), cu_ = f % (V / EPU);
+    vr[u] = make_uint4(0, 0, 0, 0);
+    if (row < L) vr[u] = *reinterpret_cast<const uint4*>(v + ((t0 + row) * HV + hv) * V + EPU * cu_);
+  }
+  if (tid < kC) sBeta[tid] = tid < L ? to_f32(beta[(t0 + tid) * HV + hv]) : 0.f;
+#pragma unroll
+  for (int u = 0; u < GU; ++u) {
+    const int f = tid + u * kThreads, row = f / (K / 4), c4 = f % (K / 4);
+    *reinterpret_cast<float4*>(sG + row * GS + 4 * c4) = gr[u];
+  }
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int f = tid + u * kThreads, row = f / (K / EPU), cu_ = f % (K / EPU);
+    *reinterpret_cast<uint4*>(sK + row * KSTR + EPU * cu_) = kr[u];
+    *reinterpret_cast<uint4*>(sQ + row * KSTR + EPU * cu_) = qr[u];
+  }
+  __syncthreads();
+
+  // ---- 2. A^T and P^T tiles: column tile I = wave (tokens i), row tiles J <= I (tokens j)
+  const int I = wave;
+  const int icol = 16 * I + l16;
+  const int r = 16 * I;  // reference token of every tile in column I
+  F lkf[KS_K], lqf[KS_K];  // column factors k_i 2^(G2_i - G2_r), q~_i 2^(G2_i - G2_r) (<= 1)
+#pragma unroll
+  for (int p = 0; p < QK; ++p) {
+    const int c0 = 16 * p + 4 * g;
+    float gi[4], g0[4], ki[4], qi[4], vk[4], vq[4];
+    lds4(sG + icol * GS + c0, gi);
+    lds4(sG + r * GS + c0, g0);
+    lds4(sK + icol * KSTR + c0, ki);
+    lds4(sQ + icol * KSTR + c0, qi);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = ex2(gi[e] - g0[e]);
+      vk[e] = ki[e] * x;
+      vq[e] = qi[e] * scale * x;
+    }
+    put_quad<M>(lkf, p, vk);
+    put_quad<M>(lqf, p, vq);
+  }
+  f32x4 accA[3], accP[3];            // tiles J < I
+  f32x4 dA = zero4(), dP = zero4();  // tile J == I
+  f32x4 pT[3], dPT = zero4();        // BWD: P tiles (rows i, cols j), J < I and J == I
+#pragma unroll
+  for (int J = 0; J < 3; ++J) {
+    accA[J] = accP[J] = pT[J] = zero4();
+    if (J < I) {
+      const int jrow = 16 * J + l16;
+      F rf[KS_K];  // row factors k_j 2^(G2_r - G2_j) (<= 1: j < r)
+#pragma unroll
+      for (int p = 0; p < QK; ++p) {
+        const int c0 = 16 * p + 4 * g;
+        float gj[4], g0[4], kj[4], vv[4];
+        lds4(sG + jrow * GS + c0, gj);
+        lds4(sG + r * GS + c0, g0);
+        lds4(sK + jrow * KSTR + c0, kj);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vv[e] = kj[e] * ex2(g0[e] - gj[e]);
+        put_quad<M>(rf, p, vv);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS_K; ++ks) {
+        accA[J] = M::mma(rf[ks], lkf[ks], accA[J]);
+        accP[J] = M::mma(rf[ks], lqf[ks], accP[J]);
+        if constexpr (BWD) pT[J] = M::mma(lqf[ks], rf[ks], pT[J]);
+      }
+    }
+  }
+  // diagonal tile: one pass with reference r when the tile's gate range allows it
+  float rng = 0.f;
+#pragma unroll
+  for (int p = 0; p < QK; ++p) {
+    const int c0 = 16 * p + 4 * g;
+    float a0[4], a1[4];
+    lds4(sG + r * GS + c0, a0);
+    lds4(sG + (r + 15) * GS + c0, a1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rng = fmaxf(rng, a0[e] - a1[e]);
+  }
+  rng = fmaxf(rng, __shfl_xor(rng, 16));
+  rng = fmaxf(rng, __shfl_xor(rng, 32));
+  const int jl = l16, il = l16;
+  const int jrow = 16 * I + jl;
+  if (rng <= kFastRange) {
+    F rf[KS_K];  // k_j 2^(G2_r - G2_j) with r <= j: >= 1 but at most 2^112
+#pragma unroll
+    for (int p = 0; p < QK; ++p) {
+      const int c0 = 16 * p + 4 * g;
+      float gj[4], g0[4], kj[4], vv[4];
+      lds4(sG + jrow * GS + c0, gj);
+      lds4(sG + r * GS + c0, g0);
+      lds4(sK + jrow * KSTR + c0, kj);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[e] = kj[e] * ex2(g0[e] - gj[e]);
+      put_quad<M>(rf, p, vv);
+    }
+    f32x4 xa = zero4(), xp = zero4(), xt = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS_K; ++ks) {
+      xa = M::mma(rf[ks], lkf[ks], xa);
+      xp = M::mma(rf[ks], lqf[ks], xp);
+      if constexpr (BWD) xt = M::mma(lqf[ks], rf[ks], xt);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int jr = 4 * g + e;
+      dA[e] = (il > jr) ? xa[e] : 0.f;
+      dP[e] = (il >= jr) ? xp[e] : 0.f;
+      dPT[e] = (jr >= l16) ? xt[e] : 0.f;  // P tile: row i = 4g + e, column j = l16
+    }
+  } else {
+    // exact split by the highest differing bit of the local indices (levels
+    // 3..0, each with its own reference token), then the diagonal i == j
+#pragma unroll
+    for (int lev = 3; lev >= -1; --lev) {
+      const bool rowOn = lev < 0 || ((jl >> lev) & 1) == 0;
+      const bool colOn = lev < 0 || ((il >> lev) & 1) == 1;
+      const int rr = lev < 0 ? 0 : 16 * I + ((((jl >> lev) | 1)) << lev);  // reference of row j
+      const int rc = lev < 0 ? 0 : 16 * I + ((il >> lev) << lev);          // reference of col i
+      F ra[KS_K], lk[KS_K], lq[KS_K];
+#pragma unroll
+      for (int p = 0; p < QK; ++p) {
+        const int c0 = 16 * p + 4 * g;
+        float kj[4], ki[4], qi[4], va[4], vk[4], vq[4];
+        lds4(sK + jrow * KSTR + c0, kj);
+        lds4(sQ + icol * KSTR + c0, qi);
+        if (lev < 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            va[e] = kj[e];
+            vk[e] = 0.f;
+            vq[e] = qi[e] * scale;
+          }
+        } else {
+          float gj[4], grr[4], gi[4], grc[4];
+          lds4(sK + icol * KSTR + c0, ki);
+          lds4(sG + jrow * GS + c0, gj);
+          lds4(sG + rr * GS + c0, grr);
+          lds4(sG + icol * GS + c0, gi);
+          lds4(sG + rc * GS + c0, grc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            va[e] = rowOn ? kj[e] * ex2(grr[e] - gj[e]) : 0.f;
+            const float x = colOn ? ex2(gi[e] - grc[e]) : 0.f;
+            vk[e] = ki[e] * x;
+            vq[e] = qi[e] * scale * x;
+          }
+        }
+        put_quad<M>(ra, p, va);
+        put_quad<M>(lk, p, vk);
+        put_quad<M>(lq, p, vq);
+      }
+      f32x4 xa = zero4(), xp = zero4(), xt = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS_K; ++ks) {
+        if (lev >= 0) xa = M::mma(ra[ks], lk[ks], xa);
+        xp = M::mma(ra[ks], lq[ks], xp);
+        if constexpr (BWD) xt = M::mma(lq[ks], ra[ks], xt);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jr = 4 * g + e;  // local row j of this accumulator element
+        bool valid;
+        if (lev < 0) valid = (jr == il);
+        else valid = ((il >> (lev + 1)) == (jr >> (lev + 1))) && ((il >> lev) & 1) && !((jr >> lev) & 1);
+        if (valid) {
+          dA[e] += xa[e];
+          dP[e] += xp[e];
+        }
+        if constexpr (BWD) {
+          // transposed tile: row i = 4g + e (= jr), column j = l16
+          const int ir = jr, jc = l16;
+          bool vt;
+          if (lev < 0) vt = (ir == jc);
+          else vt = ((ir >> (lev + 1)) == (jc >> (lev + 1))) && ((ir >> lev) & 1) && !((jc >> lev) & 1);
+          if (vt) dPT[e] += xt[e];
+        }
+      }
+    }
+  }
+
+  T* wsW = ws_T + ch * WsL::elems;
+  T* wsQG = wsW + WsL::W;
+  T* wsKH = wsQG + WsL::QG;
+  T* wsP = wsKH + WsL::KH;
+  T* wsU = wsP + WsL::P;
+  float* wsGL = ws_GL + ch * K;
+
+  // ---- 3. P fragments (rows i of tile I, contraction over j): accumulators of P^T
+#pragma unroll
+  for (int ks = 0; ks < KS_C; ++ks) {
+    F f;
+#pragma unroll
+    for (int jj = 0; jj < M::PER; ++jj) {
+      const int tile = acc_tile<M>(ks, jj), el = acc_elem<M>(ks, jj);
+      float x = 0.f;
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+        if (J == tile) x = (J < I) ? accP[J < 3 ? J : 0][el] : (J == I ? dP[el] : 0.f);
+      M::set(f, jj, x);
+    }
+    reinterpret_cast<F*>(wsP)[((size_t)I * KS_C + ks) * 64 + lane] = f;
+  }
+  if constexpr (BWD) {
+    // P^T fragments (rows j, contraction over i): the P tile (I, J) accumulators
+    // are half of fragment (J, I/2) (bf16) or fragments (J, 4I..4I+3) (FP32).
+    T* wsPT = ws_B + ch * WsB<T, K, V>::elems + WsB<T, K, V>::oPT;
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      f32x4 x = zero4();
+#pragma unroll
+      for (int jj = 0; jj < 3; ++jj)
+        if (jj == J && J < I) x = pT[jj];
+      if (J == I) x = dPT;
+      if constexpr (M::KSTEP == 32) {
+        bf16x4 hx;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hx[e] = (bf16)x[e];
+        *reinterpret_cast<bf16x4*>(wsPT + (((size_t)J * KS_C + (I >> 1)) * 64 + lane) * 8 + 4 * (I & 1)) = hx;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wsPT[((size_t)J * KS_C + 4 * I + e) * 64 + lane] = from_f32<T>(x[e]);
+      }
+    }
+    // Khat fragments (rows tokens i of tile I, contraction over channels)
+    T* wsKHn = ws_B + ch * WsB<T, K, V>::elems + WsB<T, K, V>::oKHn;
+    {
+      F f[KS_K];
+#pragma unroll
+      for (int p = 0; p < QK; ++p) {
+        const int c0 = 16 * p + 4 * g;
+        float ki[4], gi[4], gl[4], vv[4];
+        lds4(sK + icol * KSTR + c0, ki);
+        lds4(sG + icol * GS + c0, gi);
+        lds4(sG + (L - 1) * GS + c0, gl);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vv[e] = ki[e] * ex2(gl[e] - gi[e]);
+        put_quad<M>(f, p, vv);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS_K; ++ks) reinterpret_cast<F*>(wsKHn)[((size_t)I * KS_K + ks) * 64 + lane] = f[ks];
+    }
+    // (Q~ Gamma)^T fragments (rows channels, contraction over tokens)
+    T* wsQGT = ws_B + ch * WsB<T, K, V>::elems + WsB<T, K, V>::oQGT;
+#pragma unroll
+    for (int rt0 = 0; rt0 < K / 16; rt0 += 4) {
+      const int rt = rt0 + wave;
+      const int c = 16 * rt + l16;
+      F f[KS_C];
+#pragma unroll
+      for (int p = 0; p < QC; ++p) {
+        float vv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * p + 4 * g + e;
+          vv[e] = to_f32(sQ[j * KSTR + c]) * scale * ex2(sG[j * GS + c]);
+        }
+        put_quad<M>(f, p, vv);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS_C; ++ks) reinterpret_cast<F*>(wsQGT)[((size_t)rt * KS_C + ks) * 64 + lane] = f[ks];
+    }
+  }
+  // ---- 4. Q~ * Gamma fragments (rows i of tile I, contraction over channels)
+  {
+    F f[KS_K];
+#pragma unroll
+    for (int p = 0; p < QK; ++p) {
+      const int c0 = 16 * p + 4 * g;
+      float qi[4], gi[4], vv[4];
+      lds4(sQ + icol * KSTR + c0, qi);
+      lds4(sG + icol * GS + c0, gi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[e] = qi[e] * scale * ex2(gi[e]);
+      put_quad<M>(f, p, vv);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS_K; ++ks) reinterpret_cast<F*>(wsQG)[((size_t)I * KS_K + ks) * 64 + lane] = f[ks];
+  }
+  // ---- 5. Khat^T fragments (rows = channels, contraction over tokens j)
+#pragma unroll
+  for (int rt0 = 0; rt0 < K / 16; rt0 += 4) {
+    const int rt = rt0 + wave;
+    const int c = 16 * rt + l16;
+    const float gl = sG[(L - 1) * GS + c];
+    F f[KS_C];
+#pragma unroll
+    for (int p = 0; p < QC; ++p) {
+      float vv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 16 * p + 4 * g + e;
+        vv[e] = to_f32(sK[j * KSTR + c]) * ex2(gl - sG[j * GS + c]);
+      }
+      put_quad<M>(f, p, vv);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS_C; ++ks) reinterpret_cast<F*>(wsKH)[((size_t)rt * KS_C + ks) * 64 + lane] = f[ks];
+  }
+  if (tid < K) wsGL[tid] = ex2(sG[(L - 1) * GS + tid]);
+  __syncthreads();  // q is dead: R3 <- A
+
+  // ---- 6. A = b_i (A^T accumulators)^T into LDS (zero above the diagonal tiles)
+  {
+    const float b = sBeta[icol];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (J < I) {
+        const f32x4 a = accA[J < 3 ? J : 0];
+        x = make_float4(b * a[0], b * a[1], b * a[2], b * a[3]);
+      } else if (J == I) {
+        x = make_float4(b * dA[0], b * dA[1], b * dA[2], b * dA[3]);
+      }
+      *reinterpret_cast<float4*>(&sA[icol * AS + 16 * J + 4 * g]) = x;
+      if constexpr (BWD) {
+        float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (J < I) {
+          const f32x4 a = accA[J < 3 ? J : 0];
+          y = make_float4(a[0], a[1], a[2], a[3]);
+        } else if (J == I) {
+          y = make_float4(dA[0], dA[1], dA[2], dA[3]);
+        }
+        float* wsAB = ws_Bf + ch * WsB<T, K, V>::elems_f + WsB<T, K, V>::TM;
+        *reinterpret_cast<float4*>(wsAB + icol * kC + 16 * J + 4 * g) = y;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 7. T = (I + A)^-1 in FP32, in place
+  // 7a. diagonal 16x16 blocks by forward substitution (wave d, lane = column)
+  if (lane < 16) {
+    const int d = wave, jj = lane;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float arow[16];
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) lds4(sA + (16 * d + i) * AS + 16 * d + 4 * m4, arow + 4 * m4);
+      float s = (i == jj) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) s -= arow[m] * x[m];
+      x[i] = s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sA[(16 * d + i) * AS + 16 * d + jj] = x[i];
+  }
+  __syncthreads();
+  // 7b. block rows: T_IJ = -T_II * sum_{M=J}^{I-1} A_IM T_MJ (scratch: upper block (J, I))
+  for (int Ib = 1; Ib < 4; ++Ib) {
+    const int Jb = wave;
+    const int a = l16, b0 = 4 * g;  // lane owns row a, columns b0..b0+3 of the block
+    if (Jb < Ib) {
+      float xs[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int Mb = Jb; Mb < Ib; ++Mb) {
+        float arow[16];
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) lds4(sA + (16 * Ib + a) * AS + 16 * Mb + 4 * m4, arow + 4 * m4);
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+          float t4[4];
+          lds4(sA + (16 * Mb + p) * AS + 16 * Jb + b0, t4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xs[e] += arow[p] * t4[e];
+        }
+      }
+      *reinterpret_cast<float4*>(sA + (16 * Jb + a) * AS + 16 * Ib + b0) = make_float4(xs[0], xs[1], xs[2], xs[3]);
+    }
+    __syncthreads();
+    if (Jb < Ib) {
+      float ts[4] = {0.f, 0.f, 0.f, 0.f};
+      float trow[16];
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) lds4(sA + (16 * Ib + a) * AS + 16 * Ib + 4 * m4, trow + 4 * m4);
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        float x4[4];
+        lds4(sA + (16 * Jb + p) * AS + 16 * Ib + b0, x4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ts[e] -= trow[p] * x4[e];
+      }
+      *reinterpret_cast<float4*>(sA + (16 * Ib + a) * AS + 16 * Jb + b0) = make_float4(ts[0], ts[1], ts[2], ts[3]);
+    }
+    __syncthreads();
+    if (Jb < Ib)
+      *reinterpret_cast<float4*>(sA + (16 * Jb + a) * AS + 16 * Ib + b0) = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+  }
+
+  if constexpr (BWD) {
+    float* wsTM = ws_Bf + ch * WsB<T, K, V>::elems_f;
+#pragma unroll
+    for (int u = 0; u < kC * kC / 4 / kThreads; ++u) {
+      const int f = tid + u * kThreads, i = f / (kC / 4), c4 = f % (kC / 4);
+      *reinterpret_cast<float4*>(wsTM + i * kC + 4 * c4) = *reinterpret_cast<const float4*>(sA + i * AS + 4 * c4);
+    }
+  }
+  // ---- 8. W^T = B^T T^T with B_mc = b_m k_mc 2^G2_mc built on the fly.
+  // Wave split: a pair of 16-row tiles of the output dimension (= one bf16
+  // contraction step of the consumer) times NI token tiles, so every wave
+  // writes whole fragments.
+  {
+    constexpr int NP = K / 32;  // tile pairs over channels
+    const int pw = wave % NP, I0 = (wave / NP) * NP;
+    F tfr[NP][KS_C];  // T rows i of token tiles I0..I0+NP-1, over m
+#pragma unroll
+    for (int ii = 0; ii < NP; ++ii)
+#pragma unroll
+      for (int p = 0; p < QC; ++p) {
+        float t4[4];
+        lds4(sA + (16 * (I0 + ii) + l16) * AS + 16 * p + 4 * g, t4);
+        put_quad<M>(tfr[ii], p, t4);
+      }
+    f32x4 accW[2][NP];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int c = 16 * (2 * pw + h2) + l16;
+      F ba[KS_C];
+#pragma unroll
+      for (int p = 0; p < QC; ++p) {
+        float b4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 16 * p + 4 * g + e;
+          b4[e] = sBeta[m] * to_f32(sK[m * KSTR + c]) * ex2(sG[m * GS + c]);
+        }
+        put_quad<M>(ba, p, b4);
+      }
+#pragma unroll
+      for (int ii = 0; ii < NP; ++ii) {
+        accW[h2][ii] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) accW[h2][ii] = M::mma(ba[ks], tfr[ii][ks], accW[h2][ii]);
+        if constexpr (BWD) {
+          // W tile (rows i of token tile I0+ii, columns c of channel tile 2pw+h2):
+          // half of the W^T fragment (channel tile, (I0+ii)/2)
+          f32x4 wt = zero4();
+#pragma unroll
+          for (int ks = 0; ks < KS_C; ++ks) wt = M::mma(tfr[ii][ks], ba[ks], wt);
+          T* wsWT = ws_B + ch * WsB<T, K, V>::elems + WsB<T, K, V>::oWT;
+          const int ctile = 2 * pw + h2, It = I0 + ii;
+          if constexpr (M::KSTEP == 32) {
+            bf16x4 hx;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hx[e] = (bf16)wt[e];
+            *reinterpret_cast<bf16x4*>(wsWT + (((size_t)ctile * KS_C + (It >> 1)) * 64 + lane) * 8 + 4 * (It & 1)) = hx;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wsWT[((size_t)ctile * KS_C + 4 * It + e) * 64 + lane] = from_f32<T>(wt[e]);
+          }
+        }
+      }
+    }
+    // channel tiles 2pw, 2pw+1 are contraction steps {pw} (bf16) or {8pw..8pw+7} (FP32)
+#pragma unroll
+    for (int ii = 0; ii < NP; ++ii) {
+      if constexpr (M::KSTEP == 32) {
+        F f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) M::set(f, jj, accW[jj >> 2][ii][jj & 3]);
+        reinterpret_cast<F*>(wsW)[((size_t)(I0 + ii) * KS_K + pw) * 64 + lane] = f;
+      } else {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            F f;
+            M::set(f, 0, accW[h2][ii][e]);
+            reinterpret_cast<F*>(wsW)[((size_t)(I0 + ii) * KS_K + 4 * (2 * pw + h2) + e) * 64 + lane] = f;
+          }
+      }
+    }
+  }
+  __syncthreads();  // G2 and k are dead: R1 <- b V (row-major)
+  constexpr int VSTR = Lds::VSTR;
+  T* sV = reinterpret_cast<T*>(smem);  // R1: b v [C][VSTR]
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int f = tid + u * kThreads, m = f / (V / EPU), cu_ = f % (V / EPU);
+    const float b = sBeta[m];
+    T tmp[EPU];
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) tmp[e] = from_f32<T>(b * unit_elem<T>(vr[u], e));
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) sV[m * VSTR + EPU * cu_ + e] = tmp[e];
+  }
+  __syncthreads();
+
+  // ---- 9. U = T (b V), same wave split over value tiles; accumulator order
+  {
+    constexpr int NP = V / 32;
+    const int pw = wave % NP, I0 = (wave / NP) * NP;
+#pragma unroll
+    for (int ii = 0; ii < NP; ++ii) {
+      F ta[KS_C];
+#pragma unroll
+      for (int p = 0; p < QC; ++p) {
+        float t4[4];
+        lds4(sA + (16 * (I0 + ii) + l16) * AS + 16 * p + 4 * g, t4);
+        put_quad<M>(ta, p, t4);
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int vt = 2 * pw + h2;
+        const int c = 16 * vt + l16;
+        F vb[KS_C];
+#pragma unroll
+        for (int p = 0; p < QC; ++p) {
+          float v4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = to_f32(sV[(16 * p + 4 * g + e) * VSTR + c]);
+          put_quad<M>(vb, p, v4);
+        }
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(ta[ks], vb[ks], acc);
+        T* dst = wsU + (((size_t)(I0 + ii) * (V / 16) + vt) * 64 + lane) * 4;
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = (bf16)acc[e];
+          *reinterpret_cast<bf16x4*>(dst) = x;
+        } else {
+          *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ inter-chunk scan + output
+// Raw 4-element vector of T (U in accumulator order).
+template <typename T>
+struct Raw4;
+template <>
+struct Raw4<bf16> {
+  typedef uint2 type;
+  static __device__ __forceinline__ float get(const uint2& r, int e) {
+    const uint32_t w = e < 2 ? r.x : r.y;
+    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+};
+template <>
+struct Raw4<float> {
+  typedef float4 type;
+  static __device__ __forceinline__ float get(const float4& r, int e) {
+    return e == 0 ? r.x : e == 1 ? r.y : e == 2 ? r.z : r.w;
+  }
+};
+
+template <typename T, int K, int V, int BV>
+__global__ void __launch_bounds__(kThreads)
+chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
+                  const int* __restrict__ ws_int, const int32_t* __restrict__ cu,
+                  const float* h0, int N, int T_, int HV, int write_final, T* __restrict__ o,
+                  float* ht, T* __restrict__ ws_B) {
+  using M = MF<T>;
+  using F = typename M::frag;
+  using WsL = Ws<T, K, V>;
+  using R4 = Raw4<T>;
+  typedef typename R4::type raw4;
+  constexpr int KS_K = K / M::KSTEP;
+  constexpr int KS_C = kC / M::KSTEP;
+  constexpr int RTW = K / 64;   // state row tiles per wave
+  constexpr int CTB = BV / 16;  // column tiles per block
+  static_assert(RTW >= 1 && CTB >= 1, "tile shape");
+
+  __shared__ F sS[2][KS_K][CTB][64];  // S as B fragments (contraction over channels), 2 buffers
+  __shared__ F sD[KS_C][CTB][64];     // Delta as B fragments (contraction over tokens)
+
+  const int n = blockIdx.x / HV, hv = blockIdx.x % HV, vb = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  int64_t bos;
+  int len;
+  seq_range(cu, n, T_, &bos, &len);
+  int cbeg, cend;
+  if (cu == nullptr) {
+    const int nc = (T_ + kC - 1) / kC;
+    cbeg = n * nc;
+    cend = cbeg + nc;
+  } else {
+    cbeg = ws_int[1 + n];
+    cend = ws_int[2 + n];
+  }
+  const size_t st_base = ((size_t)n * HV + hv) * (size_t)K * V;
+  const int col_base = vb * BV;
+
+  if (len == 0) {
+    if (!write_final || (h0 == ht && h0 != nullptr)) return;
+    for (int e = tid; e < K * BV; e += kThreads) {
+      const int r = e / BV, c = col_base + e % BV;
+      const size_t off = st_base + (size_t)r * V + c;
+      uint32_t bits = h0 ? reinterpret_cast<const uint32_t*>(h0)[off] : 0u;
+      reinterpret_cast<uint32_t*>(ht)[off] = bits;
+    }
+    return;
+  }
+
+  // per-chunk operands of this wave, loaded one chunk ahead
+  struct Ops {
+    F w[KS_K], qg[KS_K], p[KS_C], kh[RTW][KS_C];
+    raw4 u[CTB];
+    float4 gl[RTW];
+  };
+  auto load_ops = [&](int cj, Ops& op) {
+    const size_t ch = (size_t)cj * HV + hv;
+    const T* wsW = ws_T + ch * WsL::elems;
+    const F* fW = reinterpret_cast<const F*>(wsW);
+    const F* fQG = reinterpret_cast<const F*>(wsW + WsL::W);
+    const F* fKH = reinterpret_cast<const F*>(wsW + WsL::W + WsL::QG);
+    const F* fP = reinterpret_cast<const F*>(wsW + WsL::W + WsL::QG + WsL::KH);
+    const T* wsU = wsW + WsL::W + WsL::QG + WsL::KH + WsL::P;
+#pragma unroll
+    for (int ks = 0; ks < KS_K; ++ks) {
+      op.w[ks] = fW[((size_t)wave * KS_K + ks) * 64 + lane];
+      op.qg[ks] = fQG[((size_t)wave * KS_K + ks) * 64 + lane];
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS_C; ++ks) op.p[ks] = fP[((size_t)wave * KS_C + ks) * 64 + lane];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+#pragma unroll
+      for (int ks = 0; ks < KS_C; ++ks)
+        op.kh[rt][ks] = fKH[((size_t)(RTW * wave + rt) * KS_C + ks) * 64 + lane];
+      op.gl[rt] = *reinterpret_cast<const float4*>(ws_GL + ch * K + 16 * (RTW * wave + rt) + 4 * g);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CTB; ++ct) {
+      const int vt = (col_base >> 4) + ct;
+      op.u[ct] = *reinterpret_cast<const raw4*>(wsU + (((size_t)wave * (V / 16) + vt) * 64 + lane) * 4);
+    }
+  };
+
+  // S accumulators: wave owns channel tiles RTW*wave .. RTW*wave+RTW-1
+  f32x4 S[RTW][CTB];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CTB; ++ct) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 16 * (RTW * wave + rt) + 4 * g + e;
+        const int col = col_base + 16 * ct + l16;
+        S[rt][ct][e] = h0 ? h0[st_base + (size_t)c * V + col] : 0.f;
+      }
+    }
+
+  // one chunk of the recurrence with operands `cur`, LDS buffer `buf`
+  auto step = [&](const Ops& cur, const int cj, const int buf) __attribute__((always_inline)) {
+    const int cidx = cj - cbeg;
+    const int64_t t0 = bos + (int64_t)cidx * kC;
+    const int L = min(kC, len - cidx * kC);
+
+    if (ws_B) {  // backward support: keep the chunk's start state
+      T* st = ws_B + ((size_t)cj * HV + hv) * WsB<T, K, V>::elems + WsB<T, K, V>::oS0;
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CTB; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            st[(size_t)(16 * (RTW * wave + rt) + 4 * g + e) * V + col_base + 16 * ct + l16] = from_f32<T>(S[rt][ct][e]);
+    }
+    // (1) publish S as B fragments: k-step ks is owned by the wave holding its channels
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int tileK = RTW * wave + rt;  // channel tile
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct) {
+        if constexpr (M::KSTEP == 32) {
+          // channel tile pair (2ks, 2ks+1) -> k-step ks; this tile fills half a fragment
+          const int ks = tileK >> 1, half = tileK & 1;
+          bf16x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = (bf16)S[rt][ct][e];
+          *(reinterpret_cast<bf16x4*>(&sS[buf][ks][ct][lane]) + half) = x;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            F f;
+            M::set(f, 0, S[rt][ct][e]);
+            sS[buf][4 * tileK + e][ct][lane] = f;
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // (2) Delta = U - W S for token tile `wave`
+    f32x4 D[CTB];
+    {
+      f32x4 ws_[CTB];
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct) ws_[ct] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS_K; ++ks) {
+#pragma unroll
+        for (int ct = 0; ct < CTB; ++ct) ws_[ct] = M::mma(cur.w[ks], sS[buf][ks][ct][lane], ws_[ct]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) D[ct][e] = R4::get(cur.u[ct], e) - ws_[ct][e];
+    }
+    if (ws_B) {  // backward support: keep Delta
+      T* dl = ws_B + ((size_t)cj * HV + hv) * WsB<T, K, V>::elems + WsB<T, K, V>::oDL;
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dl[(size_t)(16 * wave + 4 * g + e) * V + col_base + 16 * ct + l16] = from_f32<T>(D[ct][e]);
+    }
+    // publish Delta as B fragments (contraction over tokens)
+#pragma unroll
+    for (int ct = 0; ct < CTB; ++ct) {
+      if constexpr (M::KSTEP == 32) {
+        const int ks = wave >> 1, half = wave & 1;
+        bf16x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (bf16)D[ct][e];
+        *(reinterpret_cast<bf16x4*>(&sD[ks][ct][lane]) + half) = x;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          F f;
+          M::set(f, 0, D[ct][e]);
+          sD[4 * wave + e][ct][lane] = f;
+        }
+      }
+    }
+    __syncthreads();
+
+    // (3) S = Diag(Gamma_last) S + Khat^T Delta for the wave's channel tiles
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const float gl[4] = {cur.gl[rt].x, cur.gl[rt].y, cur.gl[rt].z, cur.gl[rt].w};
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[rt][ct][e] *= gl[e];
+#pragma unroll
+      for (int ks = 0; ks < KS_C; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < CTB; ++ct) S[rt][ct] = M::mma(cur.kh[rt][ks], sD[ks][ct][lane], S[rt][ct]);
+    }
+    // (4) output rows of token tile `wave`: O = (Q~ Gamma) S0 + P Delta
+    {
+      f32x4 O[CTB];
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct) O[ct] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS_K; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < CTB; ++ct) O[ct] = M::mma(cur.qg[ks], sS[buf][ks][ct][lane], O[ct]);
+#pragma unroll
+      for (int ks = 0; ks < KS_C; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < CTB; ++ct) O[ct] = M::mma(cur.p[ks], sD[ks][ct][lane], O[ct]);
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct) {
+        const int col = col_base + 16 * ct + l16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * wave + 4 * g + e;
+          if (i < L && o) o[((t0 + i) * HV + hv) * V + col] = from_f32<T>(O[ct][e]);
+        }
+      }
+    }
+  };
+
+  // two operand sets, unrolled by two so the next chunk's loads stay in flight
+  Ops opA, opB;
+  load_ops(cbeg, opA);
+  // (loads are unconditional -- the last chunk is simply fetched again -- so
+  // the number of loads in flight is the same on every path)
+  for (int cj = cbeg;; cj += 2) {
+    load_ops(min(cj + 1, cend - 1), opB);
+    step(opA, cj, 0);
+    if (cj + 1 >= cend) break;
+    load_ops(min(cj + 2, cend - 1), opA);
+    step(opB, cj + 1, 1);
+    if (cj + 2 >= cend) break;
+  }
+
+  if (write_final) {
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = 16 * (RTW * wave + rt) + 4 * g + e;
+          const int col = col_base + 16 * ct + l16;
+          ht[st_base + (size_t)c * V + col] = S[rt][ct][e];
+        }
+  }
+}
+
+// ------------------------------------------------------------------ host side
+inline int64_t max_chunks(const kda_dims& d, bool varlen) {
+  const int64_t per = (d.T + kC - 1) / kC;
+  return varlen ? per + d.N : per * d.B;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline int scan_block_v(int64_t chains, int V) {
+  constexpr int64_t kCUs = 256;
+  int bv = 64;
+  while (bv > 16 && chains * (V / bv) < kCUs) bv >>= 1;
+  return bv > V ? V : bv;
+}
+
+// Chunk table of a varlen batch (chunk_table_kernel), enqueued on `s`.
+hipError_t launch_chunk_table(const int32_t* cu, int N, int* ws_int, int max_chunks, hipStream_t s);
+
+}  // namespace kda

@@ -123,6 +123,33 @@ kda_status kda_chunk_fwd(const kda_dims* dims, kda_dtype dtype, const void* q, c
                          float* final_state, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/* Workspace bytes kda_chunk_bwd needs for these sizes (0 on unsupported input). */
+size_t kda_chunk_bwd_workspace_bytes(const kda_dims* dims, kda_dtype dtype, int32_t chunk_size);
+
+/*
+ * kda_chunk_bwd -- steps B1..B3: gradients of kda_chunk_fwd.
+ *   Forward arguments as kda_chunk_fwd (gate = chunk-local log2 cumsum).
+ *   do_    [B, T, HV, V] in `dtype`: gradient of o.
+ *   dht    [N, HV, K, V] FP32 gradient of the final state, or NULL (zero).
+ *   dq, dk [B, T, H, K] in `dtype` (summed over the HV/H value heads of each
+ *          qk head); dv [B, T, HV, V] and dbeta [B, T, HV] in `dtype`;
+ *   dg     [B, T, HV, K] FP32, gradient w.r.t. the per-token natural-log gate
+ *          g (dg_t = sum over t' >= t in the chunk of dL/dG_t', G the
+ *          natural-log cumulative gate);
+ *   dh0    [N, HV, K, V] FP32 gradient of the initial state (for an empty
+ *          slot a bitwise copy of dht, or +0.0).
+ *   Rows outside every sequence are left untouched. The forward intra-chunk
+ *   terms and chunk start states are recomputed, not taken from a forward
+ *   call. Supported sizes and alignment as kda_chunk_fwd, except that FP32
+ *   inputs need K == 64 (KDA_ERR_UNSUPPORTED otherwise).
+ */
+kda_status kda_chunk_bwd(const kda_dims* dims, kda_dtype dtype, const void* q, const void* k,
+                         const void* v, const float* gate, const void* beta,
+                         const float* initial_state, const int32_t* cu_seqlens,
+                         int32_t chunk_size, const void* do_, const float* dht, void* dq,
+                         void* dk, void* dv, float* dg, void* dbeta, float* dh0,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /*
  * kda_recurrent_fwd -- step A7: the token-sequential scan (recurrent_kda).
  *   gate   [B, T, HV, K] FP32 per-token log2 decay (kda_gate_cumsum with

@@ -1,0 +1,119 @@
+"""GPU parity of steps B1..B3 (kda_chunk_bwd) against the FP64 oracle's reverse pass."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_69_amd as kda
+import oracle
+import workloads
+from helpers import DEV, device_inputs, in_contract_rows, normwise_max_err, rel_rms, to_dev, to_np, tdtype
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def _run(wl):
+    d = device_inputs(wl)
+    dt = tdtype(wl)
+    dO = to_dev(np.nan_to_num(wl.dO), dt)
+    dht = to_dev(wl.dht)
+    G = kda.gate_cumsum(d["x"], d["A_log"], d["cu"], 64)
+    got = kda.chunk_kda_bwd(d["q"], d["k"], d["v"], G, d["beta"], d["h0"], dO, dht, cu_seqlens=d["cu"])
+    torch.cuda.synchronize()
+    return {n: to_np(t) for n, t in got.items()}
+
+
+def _ref(wl):
+    g = oracle.gate_activation(wl.x, wl.A_log)
+    dO = np.nan_to_num(wl.dO.astype(np.float64))
+    if wl.cu_seqlens is not None:
+        dO[:, int(wl.cu_seqlens[-1]):] = 0.0
+    return oracle.recurrence_bwd(wl.q, wl.k, wl.v, g, wl.beta, dO, wl.h0, wl.dht, wl.cu_seqlens)
+
+
+def _check(wl, got, ref, tol_fp32=2e-5, tol_bf16=1e-2):
+    mask = in_contract_rows(wl)
+    errs = {}
+    for n in NAMES:
+        a, b = got[n], ref[n]
+        if n != "dh0":
+            a, b = a[mask], b[mask]
+        e = normwise_max_err(a, b) if wl.dtype == "fp32" else rel_rms(a, b)
+        errs[n] = e
+    tol = tol_fp32 if wl.dtype == "fp32" else tol_bf16
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, (errs, tol)
+    return errs
+
+
+@pytest.mark.parametrize("K,V,dtype", [(64, 64, "fp32"), (64, 128, "fp32"), (64, 64, "bf16"),
+                                       (64, 128, "bf16"), (128, 64, "bf16"), (128, 128, "bf16")])
+def test_bwd_ragged(K, V, dtype):
+    wl = workloads.tiny_case(400 + K + V, B=2, T=150, H=1, HV=1, K=K, V=V, dtype=dtype, grads=True)
+    _check(wl, _run(wl), _ref(wl))
+
+
+def test_bwd_fp32_k128_is_rejected():
+    wl = workloads.tiny_case(405, B=1, T=8, H=1, HV=1, K=128, V=64, grads=True)
+    with pytest.raises(kda.KdaError, match="UNSUPPORTED"):
+        _run(wl)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_bwd_varlen_gva_empty_slots(dtype):
+    cu = [0, 0, 37, 37, 170, 200]
+    K = 64 if dtype == "fp32" else 128
+    wl = workloads.tiny_case(410, T=210, H=2, HV=4, K=K, V=128, dtype=dtype, cu_seqlens=cu, grads=True)
+    got = _run(wl)
+    _check(wl, got, _ref(wl))
+    # empty slots: dh0 is dht bitwise
+    for s in (0, 2):
+        assert np.array_equal(got["dh0"][s].astype(np.float32).view(np.int32),
+                              wl.dht[s].astype(np.float32).view(np.int32))
+
+
+@pytest.mark.parametrize("gate_scale,A_log", [(1.0, 2.772588722239781), (3.0, 2.772588722239781)])
+def test_bwd_strong_decay(gate_scale, A_log):
+    """Chunk-local log2 cumsums far below -126 (exact split paths). Stage test
+    of kda_chunk_bwd alone: both sides take the same FP32 log2 gate, computed by
+    the oracle (FP64 cumsum rounded to FP32); the oracle's per-token gate is
+    its exact difference. At these magnitudes an FP32 log2 cumsum carries
+    ~1e-4 absolute exponent error, which an end-to-end comparison from the raw
+    gate would measure instead of the kernel."""
+    wl = workloads.tiny_case(420, B=1, T=130, H=1, HV=2, K=64, V=64, dtype="fp32", grads=True,
+                             A_log=A_log, gate_scale=gate_scale)
+    G2 = oracle.gate_cumsum_log2(oracle.gate_activation(wl.x, wl.A_log), None, 64).astype(np.float32)
+    assert G2.min() < -126
+    d = device_inputs(wl)
+    got = kda.chunk_kda_bwd(d["q"], d["k"], d["v"], to_dev(G2), d["beta"], d["h0"], to_dev(wl.dO),
+                            to_dev(wl.dht))
+    torch.cuda.synchronize()
+    got = {n: to_np(t) for n, t in got.items()}
+    for n in NAMES:
+        assert np.isfinite(got[n]).all(), n
+    g = oracle.g_from_log2_cumsum(G2, None, 64)
+    ref = oracle.recurrence_bwd(wl.q, wl.k, wl.v, g, wl.beta, wl.dO, wl.h0, wl.dht)
+    _check(wl, got, ref)
+
+
+def test_bwd_long_context_slice():
+    """A T=256 slice of the long-context workload (B=1, H=HV=32, K=V=128, bf16)."""
+    full = workloads.workload5(T=256)
+    got = _run(full)
+    errs = _check(full, got, _ref(full))
+    print("long-context slice rel-RMS:", {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+def test_bwd_no_dht_no_h0():
+    wl = workloads.tiny_case(430, B=1, T=100, H=1, HV=1, K=64, V=64, dtype="bf16", grads=True, h0=False)
+    wl.dht = np.zeros_like(wl.dht)
+    d = device_inputs(wl)
+    G = kda.gate_cumsum(d["x"], d["A_log"], None, 64)
+    dO = to_dev(wl.dO, torch.bfloat16)
+    got = kda.chunk_kda_bwd(d["q"], d["k"], d["v"], G, d["beta"], None, dO, None)
+    torch.cuda.synchronize()
+    g = oracle.gate_activation(wl.x, wl.A_log)
+    ref = oracle.recurrence_bwd(wl.q, wl.k, wl.v, g, wl.beta, wl.dO, None, None, None)
+    for n in NAMES:
+        assert rel_rms(to_np(got[n]), ref[n]) < 1e-2, n
