@@ -41,7 +41,57 @@ def _args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--decode-steps", type=int, default=200)
+    p.add_argument("--skip-extra", action="store_true", help="skip the context workloads")
+    p.add_argument("--profile", choices=["dense", "decode", "long", "copy"], default=None,
+                   help="run only one workload a few times (for rocprofv3), print no JSON")
+    p.add_argument("--profile-reps", type=int, default=3)
     return p.parse_args()
+
+
+def profile_only(a):
+    """A few launches of one workload, nothing else, for counter collection.
+    `copy` is the calibration kernel: a plain device copy of 1 GiB."""
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_69_amd as kda
+    import workloads
+
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    T_ = lambda x, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt)
+    if a.profile == "copy":
+        src = torch.empty(1 << 28, device=dev, dtype=torch.float32).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(a.profile_reps):
+            dst.copy_(src)
+    elif a.profile == "dense":
+        wl = workloads.workload2()
+        q, k, v, b = T_(wl.q, bf), T_(wl.k, bf), T_(wl.v, bf), T_(wl.beta, bf)
+        x, A = T_(wl.x), T_(wl.A_log)
+        G = torch.empty_like(x)
+        for _ in range(a.profile_reps):
+            kda.gate_cumsum(x, A, None, 64, out=G)
+            kda.chunk_kda(q, k, v, G, b, None, output_final_state=True)
+    elif a.profile == "decode":
+        wd = workloads.workload4()
+        q, k, v, b = T_(wd.q, bf), T_(wd.k, bf), T_(wd.v, bf), T_(wd.beta, bf)
+        x, h = T_(wd.x), T_(wd.h0)
+        cu = torch.from_numpy(wd.cu_seqlens).to(dev)
+        for _ in range(a.profile_reps):
+            G = kda.gate_cumsum(x, None, cu, 1)
+            kda.recurrent_kda(q, k, v, G, b, h, cu_seqlens=cu, output_final_state=True, final_state=h)
+    elif a.profile == "long":
+        w5 = workloads.workload5()
+        t = [T_(w5.q, bf), T_(w5.k, bf), T_(w5.v, bf), T_(w5.beta, bf)]
+        x, h0, dO, dht = T_(w5.x), T_(w5.h0), T_(w5.dO, bf), T_(w5.dht)
+        del w5
+        for _ in range(a.profile_reps):
+            G = kda.gate_cumsum(x, None, None, 64)
+            kda.chunk_kda(*t[:3], G, t[3], h0, output_final_state=True)
+            kda.chunk_kda_bwd(*t[:3], G, t[3], h0, dO, dht)
+    torch.cuda.synchronize()
+    print(f"profile {a.profile}: {a.profile_reps} reps done", flush=True)
 
 
 def chunk_fwd_bytes(B, T, H, HV, K, V, esize=2, h0=False, final=True):
@@ -82,6 +132,9 @@ def chunk_fwd_flops(B, T, HV, K, V, C=64):
 
 def main():
     a = _args()
+    if a.profile:
+        profile_only(a)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the KDA scan has no "
               "multi-GPU path in this build", file=sys.stderr)
@@ -100,7 +153,11 @@ def main():
     def T_(x, dt=torch.float32):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt)
 
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     # ---------------- chunked forward workload
+    progress("dense chunked forward")
     wl = workloads.workload2()
     B, T, H, HV, K, V = wl.B, wl.T, wl.H, wl.HV, wl.K, wl.V
     q, k, v, beta = T_(wl.q, bf), T_(wl.k, bf), T_(wl.v, bf), T_(wl.beta, bf)
@@ -162,6 +219,7 @@ def main():
                     avg_ms=round(g_ms, 4))
 
     # ---------------- recurrent decode workload
+    progress("recurrent decode")
     wd = workloads.workload4()
     dq, dk, dv, db = T_(wd.q, bf), T_(wd.k, bf), T_(wd.v, bf), T_(wd.beta, bf)
     dx, dh = T_(wd.x), T_(wd.h0)
@@ -199,9 +257,85 @@ def main():
     dbytes = decode_bytes(ntok, wd.H, wd.HV, wd.K, wd.V)
     rec_gbs = dbytes / (rec_us * 1e-6) / 1e9
 
+    # ---------------- other workloads (context lines; not part of `value`)
+    def time_it(fn, reps, warm=3):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    extra = {}
+    if not a.skip_extra:
+        # tiny FP32 problem of the pages' latency table (B=1, T=73, HV=2, K=V=64, varlen [0,3,73])
+        w1 = workloads.workload1()
+        t1 = dict(q=T_(w1.q), k=T_(w1.k), v=T_(w1.v), b=T_(w1.beta), x=T_(w1.x), A=T_(w1.A_log),
+                  h0=T_(w1.h0), cu=torch.from_numpy(w1.cu_seqlens).to(dev))
+
+        def tiny_chunk():
+            g = kda.gate_cumsum(t1["x"], t1["A"], t1["cu"], 64)
+            kda.chunk_kda(t1["q"], t1["k"], t1["v"], g, t1["b"], t1["h0"], cu_seqlens=t1["cu"],
+                          output_final_state=True)
+
+        def tiny_rec():
+            g = kda.gate_cumsum(t1["x"], t1["A"], t1["cu"], 1)
+            kda.recurrent_kda(t1["q"], t1["k"], t1["v"], g, t1["b"], t1["h0"], cu_seqlens=t1["cu"],
+                              output_final_state=True)
+        extra["tiny_fp32_varlen_T73"] = {
+            "chunk_us": round(time_it(tiny_chunk, 200) * 1e3, 2),
+            "recurrent_us": round(time_it(tiny_rec, 200) * 1e3, 2),
+            "note": "gate + scan per call, launch-latency bound"}
+        # packed varlen + GVA forward
+        progress("varlen + GVA forward")
+        w3 = workloads.workload3()
+        t3 = dict(q=T_(w3.q, bf), k=T_(w3.k, bf), v=T_(w3.v, bf), b=T_(w3.beta, bf), x=T_(w3.x),
+                  A=T_(w3.A_log), h0=T_(w3.h0), cu=torch.from_numpy(w3.cu_seqlens).to(dev))
+        G3 = torch.empty_like(t3["x"])
+        ws3 = torch.empty(kda.chunk_workspace_bytes(t3["q"], t3["v"], t3["cu"]), device=dev,
+                          dtype=torch.uint8)
+
+        def varlen_step():
+            kda.gate_cumsum(t3["x"], t3["A"], t3["cu"], 64, out=G3)
+            kda.chunk_kda(t3["q"], t3["k"], t3["v"], G3, t3["b"], t3["h0"], cu_seqlens=t3["cu"],
+                          output_final_state=True, workspace=ws3)
+        ms3 = time_it(varlen_step, 20)
+        extra["varlen_gva_32768tok_HV32"] = {"ms_per_step": round(ms3, 4),
+                                             "tokens_per_s": round(int(w3.cu_seqlens[-1]) / (ms3 * 1e-3), 1)}
+        del t3, G3, ws3
+        # long-context training step: forward + backward, B=1 T=65536 H=HV=32
+        progress("long-context forward + backward")
+        w5 = workloads.workload5()
+        t5 = dict(q=T_(w5.q, bf), k=T_(w5.k, bf), v=T_(w5.v, bf), b=T_(w5.beta, bf), x=T_(w5.x),
+                  A=T_(w5.A_log), h0=T_(w5.h0), dO=T_(w5.dO, bf), dht=T_(w5.dht))
+        del w5
+        G5 = torch.empty_like(t5["x"])
+        o5 = torch.empty_like(t5["v"])
+        ws5f = torch.empty(kda.chunk_workspace_bytes(t5["q"], t5["v"]), device=dev, dtype=torch.uint8)
+
+        def fwd5():
+            kda.gate_cumsum(t5["x"], t5["A"], None, 64, out=G5)
+            kda.chunk_kda(t5["q"], t5["k"], t5["v"], G5, t5["b"], t5["h0"], output_final_state=True,
+                          o=o5, workspace=ws5f)
+
+        def bwd5():
+            kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], G5, t5["b"], t5["h0"], t5["dO"], t5["dht"])
+        fwd_ms = time_it(fwd5, 5, warm=2)
+        bwd_ms = time_it(bwd5, 3, warm=1)
+        extra["long_context_T65536_H32_train"] = {
+            "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+            "fwd_bwd_tokens_per_s": round(65536 / ((fwd_ms + bwd_ms) * 1e-3), 1)}
+        del t5, G5, o5, ws5f
+        torch.cuda.empty_cache()
+
     # ---------------- CPU baseline: the FP64 oracle on one batch row, all heads
     cpu = None
     if not a.no_cpu_baseline:
+        progress("CPU baseline (FP64 oracle)")
         import oracle
         threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
         oracle.set_threads(threads)
@@ -243,6 +377,7 @@ def main():
                    "recurrent_GBps": round(rec_gbs, 1),
                    "recurrent_hbm_frac": round(rec_gbs / HBM_PEAK_GBS, 4),
                    "algorithmic_bytes": dbytes},
+        "other_workloads": extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
