@@ -2,21 +2,25 @@
 """Benchmark of the KDA hot path on one MI355X.
 
 Step = one pass of the forward hot path over one batch of synthetic input:
-  kda_gate_cumsum (raw gate -> chunk-local log2 cumsum) + kda_chunk_fwd
-on the dense workload B=4, T=4096, H=HV=16, K=V=128, bf16 inputs, FP32 state,
-zero initial state, final state returned. value = in-contract tokens / s.
+gate activation + chunk-local log2 cumsum, intra-chunk products, UT
+transform, inter-chunk scan and output, in one call of
+kda_chunk_fwd_fused_gate (the fused-gate chunk_kda path), on the dense
+workload B=4, T=4096, H=HV=16, K=V=128, bf16 inputs, FP32 state, zero initial
+state, final state returned. value = in-contract tokens / s. The two-call
+path (kda_gate_cumsum, then kda_chunk_fwd) is timed beside it.
 
 Also measured (same JSON line): recurrent decode on 256 slots (26 empty),
-HV=32, K=V=128, FP32 state updated in place: kda_gate_cumsum(chunk 1) +
-kda_recurrent_fwd, in us/step.
+HV=32, K=V=128, FP32 state updated in place: kda_recurrent_fwd_fused_gate
+(per-token gate activation inside the scan kernel), in us/step, with the
+two-call path (kda_gate_cumsum(chunk 1) + kda_recurrent_fwd) beside it.
 
 Timing: HIP events on torch's current stream, which is the stream every libkda
 call in this process is enqueued on. Warmup W steps, then exactly K timed
 steps between two device synchronisations.
 
-`roofline` reports the dominant entry point of the step against MI355X's
-8 TB/s HBM peak with algorithmic bytes (inputs read once, outputs written
-once). `cpu_baseline` times the FP64 oracle on the host cores over a bounded
+`roofline` reports the step's entry point (its two kernels, intra-chunk and
+scan) against MI355X's 8 TB/s HBM peak with algorithmic bytes (inputs read
+once, outputs written once). `cpu_baseline` times the FP64 oracle on the host cores over a bounded
 sample of the same workload (one batch row, all 16 heads).
 """
 from __future__ import annotations
@@ -42,7 +46,8 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--skip-extra", action="store_true", help="skip the context workloads")
-    p.add_argument("--profile", choices=["dense", "decode", "long", "copy"], default=None,
+    p.add_argument("--profile", choices=["dense", "dense2", "decode", "decode2", "long", "copy"],
+                   default=None,
                    help="run only one workload a few times (for rocprofv3), print no JSON")
     p.add_argument("--profile-reps", type=int, default=3)
     return p.parse_args()
@@ -50,7 +55,9 @@ def _args():
 
 def profile_only(a):
     """A few launches of one workload, nothing else, for counter collection.
-    `copy` is the calibration kernel: a plain device copy of 1 GiB."""
+    `copy` is the calibration kernel: a plain device copy of 1 GiB. `dense`
+    and `decode` run the fused-gate entry points, `dense2` and `decode2` the
+    two-call paths."""
     import numpy as np
     import torch
 
@@ -65,22 +72,31 @@ def profile_only(a):
         dst = torch.empty_like(src)
         for _ in range(a.profile_reps):
             dst.copy_(src)
-    elif a.profile == "dense":
+    elif a.profile in ("dense", "dense2"):
         wl = workloads.workload2()
         q, k, v, b = T_(wl.q, bf), T_(wl.k, bf), T_(wl.v, bf), T_(wl.beta, bf)
         x, A = T_(wl.x), T_(wl.A_log)
         G = torch.empty_like(x)
         for _ in range(a.profile_reps):
-            kda.gate_cumsum(x, A, None, 64, out=G)
-            kda.chunk_kda(q, k, v, G, b, None, output_final_state=True)
-    elif a.profile == "decode":
+            if a.profile == "dense":
+                kda.chunk_kda(q, k, v, x, b, None, output_final_state=True, use_gate_in_kernel=True,
+                              A_log=A)
+            else:
+                kda.gate_cumsum(x, A, None, 64, out=G)
+                kda.chunk_kda(q, k, v, G, b, None, output_final_state=True)
+    elif a.profile in ("decode", "decode2"):
         wd = workloads.workload4()
         q, k, v, b = T_(wd.q, bf), T_(wd.k, bf), T_(wd.v, bf), T_(wd.beta, bf)
         x, h = T_(wd.x), T_(wd.h0)
         cu = torch.from_numpy(wd.cu_seqlens).to(dev)
         for _ in range(a.profile_reps):
-            G = kda.gate_cumsum(x, None, cu, 1)
-            kda.recurrent_kda(q, k, v, G, b, h, cu_seqlens=cu, output_final_state=True, final_state=h)
+            if a.profile == "decode":
+                kda.recurrent_kda(q, k, v, x, b, h, cu_seqlens=cu, output_final_state=True,
+                                  final_state=h, use_gate_in_kernel=True)
+            else:
+                G = kda.gate_cumsum(x, None, cu, 1)
+                kda.recurrent_kda(q, k, v, G, b, h, cu_seqlens=cu, output_final_state=True,
+                                  final_state=h)
     elif a.profile == "long":
         w5 = workloads.workload5()
         t = [T_(w5.q, bf), T_(w5.k, bf), T_(w5.v, bf), T_(w5.beta, bf)]
@@ -99,7 +115,7 @@ def chunk_fwd_bytes(B, T, H, HV, K, V, esize=2, h0=False, final=True):
     b = tok * H * K * esize * 2          # q, k
     b += tok * HV * V * esize * 2        # v in, o out
     b += tok * HV * esize                # beta
-    b += tok * HV * K * 4                # chunk-local log2 gate (fp32)
+    b += tok * HV * K * 4                # gate input (fp32: raw x, or G2 for kda_chunk_fwd)
     st = B * HV * K * V * 4
     b += st if h0 else 0
     b += st if final else 0
@@ -113,7 +129,7 @@ def gate_bytes(B, T, HV, K):
 def decode_bytes(tokens, H, HV, K, V, esize=2):
     b = tokens * HV * K * V * 4 * 2                      # state read + write (active slots)
     b += tokens * (2 * H * K + HV * V * 2 + HV) * esize  # q, k, v, o, beta
-    b += tokens * HV * K * 4                             # per-token log2 gate
+    b += tokens * HV * K * 4                             # per-token gate input (fp32)
     return b
 
 
@@ -156,6 +172,23 @@ def main():
     def progress(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
+    def timed_region(fn, reps, warm):
+        """(wall ms per call, HIP-event ms per call) over `reps` back-to-back
+        calls on torch's current stream (the stream libkda launches on),
+        bracketed by device synchronisations."""
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / reps
+        return wall, e0.elapsed_time(e1) / reps
+
     # ---------------- chunked forward workload
     progress("dense chunked forward")
     wl = workloads.workload2()
@@ -167,56 +200,38 @@ def main():
     ht = torch.empty((B, HV, K, V), device=dev, dtype=torch.float32)
     ws = torch.empty(kda.chunk_workspace_bytes(q, v), device=dev, dtype=torch.uint8)
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    gate_ms, chunk_ms = [], []
+    def step():
+        kda.chunk_kda(q, k, v, x, beta, None, output_final_state=True, o=o, final_state=ht,
+                      workspace=ws, use_gate_in_kernel=True, A_log=A_log)
 
-    def step(record):
-        if record:
-            ev[0].record()
+    def gate_call():
         kda.gate_cumsum(x, A_log, None, 64, out=G)
-        if record:
-            ev[1].record()
+
+    def chunk_call():
         kda.chunk_kda(q, k, v, G, beta, None, output_final_state=True, o=o, final_state=ht,
                       workspace=ws)
-        if record:
-            ev[2].record()
 
-    for _ in range(a.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(a.steps):
-        step(False)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / a.steps
-    # per-entry-point durations with events (separate pass, same work)
-    for _ in range(a.steps):
-        step(True)
-        torch.cuda.synchronize()
-        gate_ms.append(ev[0].elapsed_time(ev[1]))
-        chunk_ms.append(ev[1].elapsed_time(ev[2]))
+    # timed region: K back-to-back steps between two synchronisations, with
+    # HIP events on the launch stream at both ends (average launch duration)
+    ms_per_step, f_ms = timed_region(step, a.steps, a.warmup)
     tokens = B * T
     value = tokens / (ms_per_step / 1e3)
-    g_ms, c_ms = float(np.median(gate_ms)), float(np.median(chunk_ms))
+    # the two-call path, each entry point on its own back-to-back loop
+    _, g_ms = timed_region(gate_call, a.steps, a.warmup)
+    _, c_ms = timed_region(chunk_call, a.steps, a.warmup)
 
     cb = chunk_fwd_bytes(B, T, H, HV, K, V)
     gb = gate_bytes(B, T, HV, K)
+    fused_gbs = cb / (f_ms * 1e-3) / 1e9
     chunk_gbs = cb / (c_ms * 1e-3) / 1e9
     gate_gbs = gb / (g_ms * 1e-3) / 1e9
     flops = chunk_fwd_flops(B, T, HV, K, V)
-    dominant = "kda_chunk_fwd" if c_ms >= g_ms else "kda_gate_cumsum"
-    if dominant == "kda_chunk_fwd":
-        roof = dict(bound="hbm", achieved=round(chunk_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(chunk_gbs / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel="kda_chunk_fwd (chunk_intra_kernel + chunk_scan_kernel)",
-                    algorithmic_bytes=cb, avg_ms=round(c_ms, 4),
-                    mfma_tflops=round(flops / (c_ms * 1e-3) / 1e12, 2))
-    else:
-        roof = dict(bound="hbm", achieved=round(gate_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(gate_gbs / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel="kda_gate_cumsum (gate_cumsum_kernel)", algorithmic_bytes=gb,
-                    avg_ms=round(g_ms, 4))
+    roof = dict(bound="hbm", achieved=round(fused_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(fused_gbs / HBM_PEAK_GBS, 4), traffic=None,
+                kernel="kda_chunk_fwd_fused_gate (chunk_intra_kernel + chunk_scan_kernel)",
+                algorithmic_bytes=cb, avg_ms=round(f_ms, 4),
+                mfma_tflops=round(flops / (f_ms * 1e-3) / 1e12, 2),
+                mfma_frac=round(flops / (f_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4))
 
     # ---------------- recurrent decode workload
     progress("recurrent decode")
@@ -226,36 +241,29 @@ def main():
     dcu = torch.from_numpy(wd.cu_seqlens).to(dev)
     dG = torch.empty_like(dx)
     do = torch.empty_like(dv)
-    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    def dstep():
+        kda.recurrent_kda(dq, dk, dv, dx, db, dh, cu_seqlens=dcu, output_final_state=True, o=do,
+                          final_state=dh, use_gate_in_kernel=True)
 
-    def dstep(record):
-        if record:
-            dev_ev[0].record()
+    def dgate():
         kda.gate_cumsum(dx, None, dcu, 1, out=dG)
-        if record:
-            dev_ev[1].record()
+
+    def drec():
         kda.recurrent_kda(dq, dk, dv, dG, db, dh, cu_seqlens=dcu, output_final_state=True, o=do,
                           final_state=dh)
-        if record:
-            dev_ev[2].record()
 
-    for _ in range(20):
-        dstep(False)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(a.decode_steps):
-        dstep(False)
-    torch.cuda.synchronize()
-    dec_us = (time.perf_counter() - t1) * 1e6 / a.decode_steps
-    rec_ms = []
-    for _ in range(min(a.decode_steps, 100)):
-        dstep(True)
-        torch.cuda.synchronize()
-        rec_ms.append(dev_ev[1].elapsed_time(dev_ev[2]))
-    rec_us = float(np.median(rec_ms)) * 1e3
+    def dstep2():
+        dgate()
+        drec()
+
+    dec_ms, fused_ms = timed_region(dstep, a.decode_steps, 20)
+    dec_us, fused_us = dec_ms * 1e3, fused_ms * 1e3
+    dec2_us = timed_region(dstep2, a.decode_steps, 20)[0] * 1e3
+    g1_us = timed_region(dgate, a.decode_steps, 20)[1] * 1e3
+    rec_us = timed_region(drec, a.decode_steps, 20)[1] * 1e3
     ntok = int(wd.cu_seqlens[-1])
     dbytes = decode_bytes(ntok, wd.H, wd.HV, wd.K, wd.V)
-    rec_gbs = dbytes / (rec_us * 1e-6) / 1e9
+    fused_dec_gbs = dbytes / (fused_us * 1e-6) / 1e9
 
     # ---------------- other workloads (context lines; not part of `value`)
     def time_it(fn, reps, warm=3):
@@ -278,18 +286,30 @@ def main():
                   h0=T_(w1.h0), cu=torch.from_numpy(w1.cu_seqlens).to(dev))
 
         def tiny_chunk():
+            kda.chunk_kda(t1["q"], t1["k"], t1["v"], t1["x"], t1["b"], t1["h0"], cu_seqlens=t1["cu"],
+                          output_final_state=True, use_gate_in_kernel=True, A_log=t1["A"])
+
+        def tiny_rec():
+            kda.recurrent_kda(t1["q"], t1["k"], t1["v"], t1["x"], t1["b"], t1["h0"],
+                              cu_seqlens=t1["cu"], output_final_state=True,
+                              use_gate_in_kernel=True, A_log=t1["A"])
+
+        def tiny_chunk2():
             g = kda.gate_cumsum(t1["x"], t1["A"], t1["cu"], 64)
             kda.chunk_kda(t1["q"], t1["k"], t1["v"], g, t1["b"], t1["h0"], cu_seqlens=t1["cu"],
                           output_final_state=True)
 
-        def tiny_rec():
+        def tiny_rec2():
             g = kda.gate_cumsum(t1["x"], t1["A"], t1["cu"], 1)
             kda.recurrent_kda(t1["q"], t1["k"], t1["v"], g, t1["b"], t1["h0"], cu_seqlens=t1["cu"],
                               output_final_state=True)
         extra["tiny_fp32_varlen_T73"] = {
             "chunk_us": round(time_it(tiny_chunk, 200) * 1e3, 2),
             "recurrent_us": round(time_it(tiny_rec, 200) * 1e3, 2),
-            "note": "gate + scan per call, launch-latency bound"}
+            "two_call_chunk_us": round(time_it(tiny_chunk2, 200) * 1e3, 2),
+            "two_call_recurrent_us": round(time_it(tiny_rec2, 200) * 1e3, 2),
+            "note": "fused-gate call (and gate + scan calls) incl. output allocation by the "
+                    "binding; launch-latency bound"}
         # packed varlen + GVA forward
         progress("varlen + GVA forward")
         w3 = workloads.workload3()
@@ -300,9 +320,9 @@ def main():
                           dtype=torch.uint8)
 
         def varlen_step():
-            kda.gate_cumsum(t3["x"], t3["A"], t3["cu"], 64, out=G3)
-            kda.chunk_kda(t3["q"], t3["k"], t3["v"], G3, t3["b"], t3["h0"], cu_seqlens=t3["cu"],
-                          output_final_state=True, workspace=ws3)
+            kda.chunk_kda(t3["q"], t3["k"], t3["v"], t3["x"], t3["b"], t3["h0"], cu_seqlens=t3["cu"],
+                          output_final_state=True, workspace=ws3, use_gate_in_kernel=True,
+                          A_log=t3["A"])
         ms3 = time_it(varlen_step, 20)
         extra["varlen_gva_32768tok_HV32"] = {"ms_per_step": round(ms3, 4),
                                              "tokens_per_s": round(int(w3.cu_seqlens[-1]) / (ms3 * 1e-3), 1)}
@@ -318,11 +338,13 @@ def main():
         ws5f = torch.empty(kda.chunk_workspace_bytes(t5["q"], t5["v"]), device=dev, dtype=torch.uint8)
 
         def fwd5():
-            kda.gate_cumsum(t5["x"], t5["A"], None, 64, out=G5)
-            kda.chunk_kda(t5["q"], t5["k"], t5["v"], G5, t5["b"], t5["h0"], output_final_state=True,
-                          o=o5, workspace=ws5f)
+            kda.chunk_kda(t5["q"], t5["k"], t5["v"], t5["x"], t5["b"], t5["h0"],
+                          output_final_state=True, o=o5, workspace=ws5f, use_gate_in_kernel=True,
+                          A_log=t5["A"])
 
         def bwd5():
+            # the backward takes the chunk-local log2 gate (kda_gate_cumsum) as input
+            kda.gate_cumsum(t5["x"], t5["A"], None, 64, out=G5)
             kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], G5, t5["b"], t5["h0"], t5["dO"], t5["dht"])
         fwd_ms = time_it(fwd5, 5, warm=2)
         bwd_ms = time_it(bwd5, 3, warm=1)
@@ -364,19 +386,27 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "dense chunk_kda forward: gate cumsum + chunked scan, B=4 T=4096 "
-                               "H=HV=16 K=V=128 bf16, chunk 64, zero h0, final state out",
+        "config": {"workload": "dense chunk_kda forward with the gate in the kernel (raw gate "
+                               "x, A_log ~ U(0, ln 16)), B=4 T=4096 H=HV=16 K=V=128 bf16, chunk "
+                               "64, zero h0, final state out",
                    "B": B, "T": T, "H": H, "HV": HV, "K": K, "V": V, "chunk_size": 64,
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
-        "step_breakdown_ms": {"kda_gate_cumsum": round(g_ms, 4), "kda_chunk_fwd": round(c_ms, 4),
-                              "gate_GBps": round(gate_gbs, 1), "chunk_fwd_GBps": round(chunk_gbs, 1)},
+        "step_breakdown_ms": {"kda_chunk_fwd_fused_gate": round(f_ms, 4)},
+        "two_call_path_ms": {"kda_gate_cumsum": round(g_ms, 4), "kda_chunk_fwd": round(c_ms, 4),
+                             "sum": round(g_ms + c_ms, 4), "gate_GBps": round(gate_gbs, 1),
+                             "chunk_fwd_GBps": round(chunk_gbs, 1)},
         "roofline": roof,
         "decode": {"workload": "recurrent_kda decode: 256 slots (26 empty), 1 token each, H=16 "
-                               "HV=32 K=V=128 bf16, FP32 state in place",
-                   "us_per_step": round(dec_us, 2), "kda_recurrent_fwd_us": round(rec_us, 2),
-                   "recurrent_GBps": round(rec_gbs, 1),
-                   "recurrent_hbm_frac": round(rec_gbs / HBM_PEAK_GBS, 4),
-                   "algorithmic_bytes": dbytes},
+                               "HV=32 K=V=128 bf16, FP32 state in place, raw gate activated in "
+                               "the scan kernel",
+                   "us_per_step": round(dec_us, 2),
+                   "kda_recurrent_fwd_fused_gate_us": round(fused_us, 2),
+                   "GBps": round(fused_dec_gbs, 1),
+                   "hbm_frac": round(fused_dec_gbs / HBM_PEAK_GBS, 4),
+                   "algorithmic_bytes": dbytes,
+                   "two_call_us_per_step": round(dec2_us, 2),
+                   "two_call_kda_gate_cumsum_us": round(g1_us, 2),
+                   "two_call_kda_recurrent_fwd_us": round(rec_us, 2)},
         "other_workloads": extra,
         "cpu_baseline": cpu,
     }

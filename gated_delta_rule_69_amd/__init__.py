@@ -11,8 +11,11 @@ order as the `recurrent_kda(q, k, v, gate, beta, initial_state=None, *,
 cu_seqlens=None, output_final_state=False)` contract described in "kda in
 torchtitan (training)", quoted attention-gym description):
   gate_cumsum     step A1  (kda_gate_cumsum)
-  chunk_kda       steps A2..A6 (kda_chunk_fwd)
-  recurrent_kda   step A7  (kda_recurrent_fwd)
+  chunk_kda       steps A2..A6 (kda_chunk_fwd); with use_gate_in_kernel=True
+                  steps A1..A6 (kda_chunk_fwd_fused_gate)
+  chunk_kda_bwd   steps B1..B3 (kda_chunk_bwd)
+  recurrent_kda   step A7  (kda_recurrent_fwd); with use_gate_in_kernel=True
+                  steps A1 + A7 (kda_recurrent_fwd_fused_gate)
 """
 from __future__ import annotations
 
@@ -30,7 +33,8 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE
            4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_ALIAS", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_LAUNCH"}
 
 EXPORTED = ("kda_status_string", "kda_gate_cumsum", "kda_chunk_fwd_workspace_bytes",
-            "kda_chunk_fwd", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd", "kda_recurrent_fwd")
+            "kda_chunk_fwd", "kda_chunk_fwd_fused_gate", "kda_chunk_bwd_workspace_bytes",
+            "kda_chunk_bwd", "kda_recurrent_fwd", "kda_recurrent_fwd_fused_gate")
 
 
 class KdaDims(ctypes.Structure):
@@ -62,12 +66,18 @@ def _lib():
         lib.kda_chunk_fwd_workspace_bytes.restype = sz
         lib.kda_chunk_fwd.argtypes = [dims, ctypes.c_int, p, p, p, p, p, p, p, i32, i32, p, p, p, sz, p]
         lib.kda_chunk_fwd.restype = ctypes.c_int
+        lib.kda_chunk_fwd_fused_gate.argtypes = [dims, ctypes.c_int, p, p, p, p, i32, p, p, p, p,
+                                                 i32, i32, p, p, p, sz, p]
+        lib.kda_chunk_fwd_fused_gate.restype = ctypes.c_int
         lib.kda_chunk_bwd_workspace_bytes.argtypes = [dims, ctypes.c_int, i32]
         lib.kda_chunk_bwd_workspace_bytes.restype = sz
         lib.kda_chunk_bwd.argtypes = [dims, ctypes.c_int] + [p] * 7 + [i32] + [p] * 8 + [p, sz, p]
         lib.kda_chunk_bwd.restype = ctypes.c_int
         lib.kda_recurrent_fwd.argtypes = [dims, ctypes.c_int, p, p, p, p, p, p, p, i32, p, p, p]
         lib.kda_recurrent_fwd.restype = ctypes.c_int
+        lib.kda_recurrent_fwd_fused_gate.argtypes = [dims, ctypes.c_int, p, p, p, p, i32, p, p, p, p,
+                                                     i32, p, p, p]
+        lib.kda_recurrent_fwd_fused_gate.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -136,12 +146,19 @@ def chunk_workspace_bytes(q: torch.Tensor, v: torch.Tensor, cu_seqlens=None, chu
 def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
               output_final_state: bool = False, chunk_size: int = 64,
               o: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              workspace: Optional[torch.Tensor] = None, use_gate_in_kernel: bool = False,
+              A_log: Optional[torch.Tensor] = None,
+              gate_is_raw: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Steps A2..A6 (kda_chunk_fwd). `gate` is the chunk-local cumulative log2
-    gate (gate_cumsum with the same chunk_size). Returns (o, final_state)."""
+    gate (gate_cumsum with the same chunk_size). With use_gate_in_kernel=True,
+    `gate` is gate_cumsum's input instead (raw x with optional A_log, or the
+    natural-log g if gate_is_raw=False) and the gate step runs inside the
+    chunk kernel (kda_chunk_fwd_fused_gate). Returns (o, final_state)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"),
-                 (initial_state, "initial_state"), (cu_seqlens, "cu_seqlens")):
+                 (initial_state, "initial_state"), (cu_seqlens, "cu_seqlens"), (A_log, "A_log")):
         _check(t, n)
+    if A_log is not None and not use_gate_in_kernel:
+        raise ValueError("A_log needs use_gate_in_kernel=True (else pass it to gate_cumsum)")
     d = _dims(q, v, cu_seqlens)
     dt = _dtype_code(q)
     if o is None:
@@ -153,6 +170,15 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     need = int(_lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(d), dt, int(chunk_size)))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    if use_gate_in_kernel:
+        rc = _lib().kda_chunk_fwd_fused_gate(
+            ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), int(bool(gate_is_raw)),
+            _ptr(A_log), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size),
+            int(bool(output_final_state)), _ptr(o), _ptr(final_state), _ptr(workspace),
+            workspace.numel(), _stream())
+        if rc:
+            raise KdaError("kda_chunk_fwd_fused_gate", rc)
+        return o, final_state
     rc = _lib().kda_chunk_fwd(ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
                               _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size),
                               int(bool(output_final_state)), _ptr(o), _ptr(final_state),
@@ -190,16 +216,23 @@ def chunk_kda_bwd(q, k, v, gate, beta, initial_state, do, dht=None, *, cu_seqlen
 
 def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
                   output_final_state: bool = False, o: Optional[torch.Tensor] = None,
-                  final_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  final_state: Optional[torch.Tensor] = None, use_gate_in_kernel: bool = False,
+                  A_log: Optional[torch.Tensor] = None,
+                  gate_is_raw: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Step A7 (kda_recurrent_fwd). `gate` is the per-token log2 decay
-    (gate_cumsum with chunk_size=1). Inference only: inputs that require grad
+    (gate_cumsum with chunk_size=1). With use_gate_in_kernel=True, `gate` is
+    gate_cumsum's input instead (raw x with optional A_log, or the natural-log
+    g if gate_is_raw=False), activated inside the scan kernel
+    (kda_recurrent_fwd_fused_gate). Inference only: inputs that require grad
     are rejected (use chunk_kda for training). Pass final_state=initial_state
     to update the states in place."""
     if any(t is not None and t.requires_grad for t in (q, k, v, gate, beta, initial_state)):
         raise RuntimeError("recurrent_kda is inference-only; inputs require grad (use chunk_kda)")
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"),
-                 (initial_state, "initial_state"), (cu_seqlens, "cu_seqlens")):
+                 (initial_state, "initial_state"), (cu_seqlens, "cu_seqlens"), (A_log, "A_log")):
         _check(t, n)
+    if A_log is not None and not use_gate_in_kernel:
+        raise ValueError("A_log needs use_gate_in_kernel=True (else pass it to gate_cumsum)")
     d = _dims(q, v, cu_seqlens)
     dt = _dtype_code(q)
     if o is None:
@@ -208,6 +241,14 @@ def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
         final_state = torch.empty((d.N, d.HV, d.K, d.V), device=q.device, dtype=torch.float32)
     if not output_final_state:
         final_state = None
+    if use_gate_in_kernel:
+        rc = _lib().kda_recurrent_fwd_fused_gate(
+            ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), int(bool(gate_is_raw)),
+            _ptr(A_log), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+            int(bool(output_final_state)), _ptr(o), _ptr(final_state), _stream())
+        if rc:
+            raise KdaError("kda_recurrent_fwd_fused_gate", rc)
+        return o, final_state
     rc = _lib().kda_recurrent_fwd(ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
                                   _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
                                   int(bool(output_final_state)), _ptr(o), _ptr(final_state), _stream())

@@ -67,6 +67,57 @@ kda_status check_scan(const kda_dims* d, kda_dtype dt, const void* q, const void
   return KDA_OK;
 }
 
+kda_status chunk_fwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                          const void* v, const float* gate, int gate_mode, const float* A_log,
+                          const void* beta, const float* h0, const int32_t* cu,
+                          int32_t chunk_size, int32_t write_final, void* o, float* ht,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  kda_status st = check_scan(d, dt, q, k, v, gate, beta, h0, cu, write_final, o, ht);
+  if (st != KDA_OK) return st;
+  if (chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+  if (!((d->K == 64 || d->K == 128) && (d->V == 64 || d->V == 128))) return KDA_ERR_UNSUPPORTED;
+  const Sizes s = sizes(d, dt);
+  if (A_log && (overlaps(A_log, (size_t)d->HV * 4, o, s.v) ||
+                overlaps(A_log, (size_t)d->HV * 4, ht, s.state)))
+    return KDA_ERR_ALIAS;
+  if (d->N == 0) return KDA_OK;
+  // 16-byte vector loads of q, k, v and the gate; 256-byte aligned workspace
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)gate) & 15) ||
+      ((uintptr_t)workspace & 255))
+    return KDA_ERR_UNSUPPORTED;
+  const size_t need = kda_host::chunk_workspace_bytes(*d, dt, chunk_size);
+  if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  if (overlaps(workspace, need, o, s.v) || overlaps(workspace, need, ht, s.state) ||
+      overlaps(workspace, need, h0, s.state) || overlaps(workspace, need, q, s.qk) ||
+      overlaps(workspace, need, k, s.qk) || overlaps(workspace, need, v, s.v) ||
+      overlaps(workspace, need, gate, s.gate) || overlaps(workspace, need, beta, s.beta) ||
+      overlaps(workspace, need, A_log, A_log ? (size_t)d->HV * 4 : 0))
+    return KDA_ERR_ALIAS;
+  return kda_host::launch_chunk_fwd(*d, dt, q, k, v, gate, gate_mode, A_log, beta, h0, cu,
+                                    write_final ? 1 : 0, o, ht, workspace, workspace_bytes,
+                                    stream) == hipSuccess
+             ? KDA_OK
+             : KDA_ERR_LAUNCH;
+}
+
+kda_status recurrent_impl(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                          const void* v, const float* gate, int gate_mode, const float* A_log,
+                          const void* beta, const float* h0, const int32_t* cu,
+                          int32_t write_final, void* o, float* ht, hipStream_t stream) {
+  kda_status st = check_scan(d, dt, q, k, v, gate, beta, h0, cu, write_final, o, ht);
+  if (st != KDA_OK) return st;
+  if (d->K > 256 || d->V > 256) return KDA_ERR_UNSUPPORTED;
+  const Sizes s = sizes(d, dt);
+  if (A_log && (overlaps(A_log, (size_t)d->HV * 4, o, s.v) ||
+                overlaps(A_log, (size_t)d->HV * 4, ht, s.state)))
+    return KDA_ERR_ALIAS;
+  if (d->N == 0) return KDA_OK;
+  return kda_host::launch_recurrent(*d, dt, q, k, v, gate, gate_mode, A_log, beta, h0, cu,
+                                    write_final ? 1 : 0, o, ht, stream) == hipSuccess
+             ? KDA_OK
+             : KDA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,27 +168,20 @@ kda_status kda_chunk_fwd(const kda_dims* d, kda_dtype dt, const void* q, const v
                          const float* h0, const int32_t* cu, int32_t chunk_size,
                          int32_t write_final, void* o, float* ht, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
-  kda_status st = check_scan(d, dt, q, k, v, gate, beta, h0, cu, write_final, o, ht);
-  if (st != KDA_OK) return st;
-  if (chunk_size != 64) return KDA_ERR_UNSUPPORTED;
-  if (!((d->K == 64 || d->K == 128) && (d->V == 64 || d->V == 128))) return KDA_ERR_UNSUPPORTED;
-  if (d->N == 0) return KDA_OK;
-  // 16-byte vector loads of q, k, v and the gate; 256-byte aligned workspace
-  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)gate) & 15) ||
-      ((uintptr_t)workspace & 255))
-    return KDA_ERR_UNSUPPORTED;
-  const size_t need = kda_host::chunk_workspace_bytes(*d, dt, chunk_size);
-  if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
-  const Sizes s = sizes(d, dt);
-  if (overlaps(workspace, need, o, s.v) || overlaps(workspace, need, ht, s.state) ||
-      overlaps(workspace, need, h0, s.state) || overlaps(workspace, need, q, s.qk) ||
-      overlaps(workspace, need, k, s.qk) || overlaps(workspace, need, v, s.v) ||
-      overlaps(workspace, need, gate, s.gate) || overlaps(workspace, need, beta, s.beta))
-    return KDA_ERR_ALIAS;
-  return kda_host::launch_chunk_fwd(*d, dt, q, k, v, gate, beta, h0, cu, write_final ? 1 : 0, o,
-                                    ht, workspace, workspace_bytes, stream) == hipSuccess
-             ? KDA_OK
-             : KDA_ERR_LAUNCH;
+  return chunk_fwd_impl(d, dt, q, k, v, gate, kda::kGateLog2, nullptr, beta, h0, cu, chunk_size,
+                        write_final, o, ht, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_fused_gate(const kda_dims* d, kda_dtype dt, const void* q,
+                                    const void* k, const void* v, const float* gate_in,
+                                    int32_t gate_in_is_raw, const float* A_log, const void* beta,
+                                    const float* h0, const int32_t* cu, int32_t chunk_size,
+                                    int32_t write_final, void* o, float* ht, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  if (!gate_in_is_raw && A_log) return KDA_ERR_SHAPE;
+  return chunk_fwd_impl(d, dt, q, k, v, gate_in, gate_in_is_raw ? kda::kGateRaw : kda::kGateLog,
+                        A_log, beta, h0, cu, chunk_size, write_final, o, ht, workspace,
+                        workspace_bytes, stream);
 }
 
 size_t kda_chunk_bwd_workspace_bytes(const kda_dims* d, kda_dtype dt, int32_t chunk_size) {
@@ -194,14 +238,19 @@ kda_status kda_recurrent_fwd(const kda_dims* d, kda_dtype dt, const void* q, con
                              const void* v, const float* gate, const void* beta,
                              const float* h0, const int32_t* cu, int32_t write_final, void* o,
                              float* ht, hipStream_t stream) {
-  kda_status st = check_scan(d, dt, q, k, v, gate, beta, h0, cu, write_final, o, ht);
-  if (st != KDA_OK) return st;
-  if (d->K > 256 || d->V > 256) return KDA_ERR_UNSUPPORTED;
-  if (d->N == 0) return KDA_OK;
-  return kda_host::launch_recurrent(*d, dt, q, k, v, gate, beta, h0, cu, write_final ? 1 : 0, o,
-                                    ht, stream) == hipSuccess
-             ? KDA_OK
-             : KDA_ERR_LAUNCH;
+  return recurrent_impl(d, dt, q, k, v, gate, kda::kGateLog2, nullptr, beta, h0, cu, write_final,
+                        o, ht, stream);
+}
+
+kda_status kda_recurrent_fwd_fused_gate(const kda_dims* d, kda_dtype dt, const void* q,
+                                        const void* k, const void* v, const float* gate_in,
+                                        int32_t gate_in_is_raw, const float* A_log,
+                                        const void* beta, const float* h0, const int32_t* cu,
+                                        int32_t write_final, void* o, float* ht,
+                                        hipStream_t stream) {
+  if (!gate_in_is_raw && A_log) return KDA_ERR_SHAPE;
+  return recurrent_impl(d, dt, q, k, v, gate_in, gate_in_is_raw ? kda::kGateRaw : kda::kGateLog,
+                        A_log, beta, h0, cu, write_final, o, ht, stream);
 }
 
 }  // extern "C"

@@ -185,7 +185,8 @@ constexpr float kFastRange = 112.f;
 template <typename T, int K, int V, bool BWD>
 __global__ void __launch_bounds__(kThreads, 2)
 chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                   const float* __restrict__ gate, const T* __restrict__ beta,
+                   const float* __restrict__ gate, int gate_mode,
+                   const float* __restrict__ A_log, const T* __restrict__ beta,
                    const int32_t* __restrict__ cu, const int* __restrict__ ws_int, int N, int T_,
                    int H, int HV, float scale, T* __restrict__ ws_T, float* __restrict__ ws_GL,
                    T* __restrict__ ws_B, float* __restrict__ ws_Bf) {
@@ -245,6 +246,17 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     if (row < L) vr[u] = *reinterpret_cast<const uint4*>(v + ((t0 + row) * HV + hv) * V + EPU * cu_);
   }
   if (tid < kC) sBeta[tid] = tid < L ? to_f32(beta[(t0 + tid) * HV + hv]) : 0.f;
+  if (gate_mode != kGateLog2) {
+    // fused gate step: per-token natural-log gate first (cumsum below)
+    const float sc = gate_head_scale(gate_mode, A_log, hv);
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      gr[u].x = gate_nat(gr[u].x, gate_mode, sc);
+      gr[u].y = gate_nat(gr[u].y, gate_mode, sc);
+      gr[u].z = gate_nat(gr[u].z, gate_mode, sc);
+      gr[u].w = gate_nat(gr[u].w, gate_mode, sc);
+    }
+  }
 #pragma unroll
   for (int u = 0; u < GU; ++u) {
     const int f = tid + u * kThreads, row = f / (K / 4), c4 = f % (K / 4);
@@ -257,6 +269,20 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     *reinterpret_cast<uint4*>(sQ + row * KSTR + EPU * cu_) = qr[u];
   }
   __syncthreads();
+  if (gate_mode != kGateLog2) {
+    // chunk-local inclusive cumsum in token order, times log2(e): the same
+    // float operations as the gate kernel, so G2 is bit-identical to its
+    // output. Pad rows keep the last token's value.
+    if (tid < K) {
+      float acc = 0.f;
+#pragma unroll 16
+      for (int r = 0; r < kC; ++r) {
+        if (r < L) acc = acc + sG[r * GS + tid];
+        sG[r * GS + tid] = acc * kLog2e;
+      }
+    }
+    __syncthreads();
+  }
 
   // ---- 2. A^T and P^T tiles: column tile I = wave (tokens i), row tiles J <= I (tokens j)
   const int I = wave;

@@ -12,6 +12,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -76,6 +77,49 @@ struct MF<float> {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+constexpr float kLn2 = 0.6931471805599453f;
+
+// softplus(x) = ln(1 + e^x) = max(x, 0) + ln(1 + z), z = e^{-|x|} in (0, 1],
+// on the transcendental unit. ln(1 + z) uses the classic correction
+// ln(u) * z / (u - 1) with u = 1 + z (u - 1 is exact), which keeps full
+// relative accuracy for small z; the quotient (a factor within an ulp of 1)
+// takes the hardware reciprocal. Above 20 the result is x itself.
+// Branch-free (selects), so loads around it can stay batched. No FMA
+// contraction, so every kernel that inlines it rounds the same way.
+__device__ __forceinline__ float softplus_f32(float x) {
+#pragma clang fp contract(off)
+  const float z = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+  const float u = 1.f + z;
+  const float corr = __builtin_amdgcn_logf(u) * kLn2 * (z * __builtin_amdgcn_rcpf(u - 1.f));
+  const float l = (u == 1.f) ? z : corr;
+  const float r = fmaxf(x, 0.f) + l;
+  return x > 20.f ? x : r;
+}
+
+// What a scan kernel's gate operand holds:
+//   kGateLog2: the log2 gate already prepared (per token for the recurrent
+//              scan, chunk-local inclusive cumsum G2 for the chunked scan);
+//   kGateLog:  the per-token natural-log gate g;
+//   kGateRaw:  the pre-activation x, with g = -exp(A_log[hv]) softplus(x)
+//              (unit scale without A_log).
+// The two last modes fuse the gate step into the scan; the arithmetic is the
+// one of the gate kernel, so fused and two-step results agree bit for bit.
+enum GateMode : int { kGateLog2 = 0, kGateLog = 1, kGateRaw = 2 };
+
+__device__ __forceinline__ float gate_head_scale(int mode, const float* A_log, int hv) {
+  return (mode == kGateRaw && A_log) ? expf(A_log[hv]) : 1.f;
+}
+// natural-log gate g of one element (modes kGateLog and kGateRaw)
+__device__ __forceinline__ float gate_nat(float x, int mode, float scale) {
+#pragma clang fp contract(off)
+  return mode == kGateRaw ? -scale * softplus_f32(x) : x;
+}
+// per-token log2 gate of one element, as the gate kernel writes it with chunk 1
+__device__ __forceinline__ float gate_log2_token(float x, int mode, float scale) {
+#pragma clang fp contract(off)
+  return mode == kGateLog2 ? x : (0.f + gate_nat(x, mode, scale)) * kLog2e;
+}
+
 // Flat offset of the first token of dense/varlen sequence n, and its length.
 __device__ __forceinline__ void seq_range(const int32_t* cu, int n, int T, int64_t* bos, int* len) {
   if (cu) {
@@ -95,14 +139,15 @@ namespace kda_host {
 hipError_t launch_gate(const kda_dims& d, const float* in, int is_raw, const float* A_log,
                        const int32_t* cu, int chunk, float* out, hipStream_t s);
 hipError_t launch_recurrent(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
-                            const void* v, const float* gate, const void* beta,
-                            const float* h0, const int32_t* cu, int write_final, void* o,
-                            float* ht, hipStream_t s);
+                            const void* v, const float* gate, int gate_mode, const float* A_log,
+                            const void* beta, const float* h0, const int32_t* cu,
+                            int write_final, void* o, float* ht, hipStream_t s);
 size_t chunk_workspace_bytes(const kda_dims& d, kda_dtype dt, int chunk);
 hipError_t launch_chunk_fwd(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
-                            const void* v, const float* gate, const void* beta,
-                            const float* h0, const int32_t* cu, int write_final, void* o,
-                            float* ht, void* ws, size_t ws_bytes, hipStream_t s);
+                            const void* v, const float* gate, int gate_mode, const float* A_log,
+                            const void* beta, const float* h0, const int32_t* cu,
+                            int write_final, void* o, float* ht, void* ws, size_t ws_bytes,
+                            hipStream_t s);
 size_t chunk_bwd_workspace_bytes(const kda_dims& d, kda_dtype dt, int chunk);
 hipError_t launch_chunk_bwd(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
                             const void* v, const float* gate, const void* beta, const float* h0,

@@ -15,36 +15,25 @@
 
 namespace kda {
 
-constexpr int kGateTile = 64;
 constexpr int kGateThreads = 256;
-
-constexpr float kLn2 = 0.6931471805599453f;
-
-// softplus(x) = ln(1 + e^x) = max(x, 0) + ln(1 + z), z = e^{-|x|} in (0, 1],
-// on the transcendental unit. ln(1 + z) uses the classic correction
-// ln(u) * z / (u - 1) with u = 1 + z (u - 1 is exact), which keeps full
-// relative accuracy for small z. Above 20 the result is x itself.
-__device__ __forceinline__ float softplus_f32(float x) {
-  if (x > 20.f) return x;
-  const float z = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
-  const float u = 1.f + z;
-  const float l = (u == 1.f) ? z : __builtin_amdgcn_logf(u) * kLn2 * (z / (u - 1.f));
-  return fmaxf(x, 0.f) + l;
-}
-
-template <int VEC>
+// TILE tokens per workgroup (64 for chunked output so any chunk start is
+// reachable within one carry-in pass; 16 for per-token output).
+template <int VEC, int TILE>
 __global__ void __launch_bounds__(kGateThreads)
 gate_cumsum_kernel(const float* __restrict__ in, int is_raw, const float* __restrict__ A_log,
                    const int32_t* __restrict__ cu, int N, int T, int64_t n_tok, int HV, int K,
                    int chunk, float* out) {
-  __shared__ int64_t s_cstart[kGateTile];  // chunk start of each tile token (-1: outside)
-  const int64_t t_a = (int64_t)blockIdx.x * kGateTile;
+  __shared__ int64_t s_cstart[TILE];  // chunk start of each tile token (-1: outside)
+  const int64_t t_a = (int64_t)blockIdx.x * TILE;
   const int row = HV * K;
   // per-token chunk start (sequence lookup: dense rows or binary search of cu)
-  if (threadIdx.x < kGateTile) {
-    int64_t t = t_a + threadIdx.x;
+  if (threadIdx.x < TILE) {
+    const int64_t t = t_a + threadIdx.x;
     int64_t cs = -1;
-    if (t < n_tok) {
+    if (chunk == 1) {
+      const int64_t lim = cu ? (int64_t)cu[N] : n_tok;
+      cs = t < lim ? t : -1;
+    } else if (t < n_tok) {
       int64_t bos = -1;
       if (cu == nullptr) {
         bos = (t / T) * (int64_t)T;
@@ -69,9 +58,8 @@ gate_cumsum_kernel(const float* __restrict__ in, int is_raw, const float* __rest
     int hv = (f0 + e) / K;
     scale[e] = (is_raw && A_log) ? expf(A_log[hv]) : 1.f;
   }
-  auto gate_of = [&](int64_t t, float* g) {
+  auto load = [&](int64_t t, float* x) {
     const float* p = in + t * row + f0;
-    float x[VEC];
     if constexpr (VEC == 4) {
       float4 v = *reinterpret_cast<const float4*>(p);
       x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
@@ -81,55 +69,59 @@ gate_cumsum_kernel(const float* __restrict__ in, int is_raw, const float* __rest
     } else {
       x[0] = *p;
     }
+  };
+  auto act = [&](float* x) {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) g[e] = is_raw ? -scale[e] * softplus_f32(x[e]) : x[e];
+    for (int e = 0; e < VEC; ++e) x[e] = gate_nat(x[e], is_raw ? kGateRaw : kGateLog, scale[e]);
   };
   float acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
   // carry-in: the tile starts inside a chunk that began earlier
-  {
-    int64_t cs = s_cstart[0];
+  if (chunk > 1) {
+    const int64_t cs = s_cstart[0];
     if (cs >= 0 && cs < t_a) {
       for (int64_t t = cs; t < t_a; ++t) {
         float g[VEC];
-        gate_of(t, g);
+        load(t, g);
+        act(g);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[e] += g[e];
       }
     }
   }
-  // main pass: BATCH tokens of loads in flight, then the scan and the stores
-  // (a thread only ever touches its own elements, so in-place per-token use is safe)
-  constexpr int BATCH = 16;
-  for (int i0 = 0; i0 < kGateTile; i0 += BATCH) {
+  // main pass: BATCH loads in flight (tokens outside the contract load token 0
+  // and are discarded), then the scan and the stores. A thread only touches its
+  // own elements, so in-place per-token use is safe.
+  constexpr int BATCH = TILE < 16 ? TILE : 16;
+  for (int i0 = 0; i0 < TILE; i0 += BATCH) {
     float g[BATCH][VEC];
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
-      if (s_cstart[i0 + b] >= 0) gate_of(t_a + i0 + b, g[b]);
+      const int64_t t = t_a + i0 + b;
+      load(s_cstart[i0 + b] >= 0 ? t : 0, g[b]);
     }
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
+      act(g[b]);
       const int64_t t = t_a + i0 + b;
       const int64_t cs = s_cstart[i0 + b];
-      if (cs < 0) continue;  // outside the tensor or in the capacity tail
-      if (cs == t) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
-      }
+      const bool fresh = cs == t;
       float r[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        acc[e] += g[b][e];
+        acc[e] = (fresh ? 0.f : acc[e]) + g[b][e];
         r[e] = acc[e] * kLog2e;
       }
-      float* p = out + t * row + f0;
-      if constexpr (VEC == 4) {
-        *reinterpret_cast<float4*>(p) = make_float4(r[0], r[1], r[2], r[3]);
-      } else if constexpr (VEC == 2) {
-        *reinterpret_cast<float2*>(p) = make_float2(r[0], r[1]);
-      } else {
-        *p = r[0];
+      if (cs >= 0) {
+        float* p = out + t * row + f0;
+        if constexpr (VEC == 4) {
+          *reinterpret_cast<float4*>(p) = make_float4(r[0], r[1], r[2], r[3]);
+        } else if constexpr (VEC == 2) {
+          *reinterpret_cast<float2*>(p) = make_float2(r[0], r[1]);
+        } else {
+          *p = r[0];
+        }
       }
     }
   }
@@ -147,18 +139,23 @@ hipError_t launch_gate(const kda_dims& d, const float* in, int is_raw, const flo
   int vec = 1;
   if (row % 4 == 0 && ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0)) vec = 4;
   else if (row % 2 == 0 && ((uintptr_t)in % 8 == 0) && ((uintptr_t)out % 8 == 0)) vec = 2;
-  dim3 grid((unsigned)((n_tok + kda::kGateTile - 1) / kda::kGateTile),
+  const int tile = chunk == 1 ? 16 : 64;
+  dim3 grid((unsigned)((n_tok + tile - 1) / tile),
             (unsigned)((row / vec + kda::kGateThreads - 1) / kda::kGateThreads));
   dim3 block(kda::kGateThreads);
-  if (vec == 4)
-    hipLaunchKernelGGL(kda::gate_cumsum_kernel<4>, grid, block, 0, s, in, is_raw, A_log, cu, d.N,
-                       d.T, n_tok, d.HV, d.K, chunk, out);
-  else if (vec == 2)
-    hipLaunchKernelGGL(kda::gate_cumsum_kernel<2>, grid, block, 0, s, in, is_raw, A_log, cu, d.N,
-                       d.T, n_tok, d.HV, d.K, chunk, out);
-  else
-    hipLaunchKernelGGL(kda::gate_cumsum_kernel<1>, grid, block, 0, s, in, is_raw, A_log, cu, d.N,
-                       d.T, n_tok, d.HV, d.K, chunk, out);
+#define KDA_GATE_LAUNCH(V_, TL_)                                                              \
+  hipLaunchKernelGGL((kda::gate_cumsum_kernel<V_, TL_>), grid, block, 0, s, in, is_raw, A_log, \
+                     cu, d.N, d.T, n_tok, d.HV, d.K, chunk, out)
+  if (tile == 16) {
+    if (vec == 4) KDA_GATE_LAUNCH(4, 16);
+    else if (vec == 2) KDA_GATE_LAUNCH(2, 16);
+    else KDA_GATE_LAUNCH(1, 16);
+  } else {
+    if (vec == 4) KDA_GATE_LAUNCH(4, 64);
+    else if (vec == 2) KDA_GATE_LAUNCH(2, 64);
+    else KDA_GATE_LAUNCH(1, 64);
+  }
+#undef KDA_GATE_LAUNCH
   return hipGetLastError();
 }
 

@@ -51,7 +51,8 @@ struct VecF<1> {
 template <typename T, int VEC, int ROWS>
 __global__ void __launch_bounds__(kRecThreads)
 recurrent_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                 const float* __restrict__ gate, const T* __restrict__ beta,
+                 const float* __restrict__ gate, int gate_mode, const float* __restrict__ A_log,
+                 const T* __restrict__ beta,
                  const float* h0, const int32_t* __restrict__ cu, int Tlen, int H, int HV, int K,
                  int V, int BV, float scale, int write_final, T* __restrict__ o, float* ht) {
   extern __shared__ float smem[];
@@ -95,6 +96,7 @@ recurrent_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
     return;
   }
 
+  const float gscale = gate_head_scale(gate_mode, A_log, hv);
   float s[ROWS][VEC];
 #pragma unroll
   for (int i = 0; i < ROWS; ++i) {
@@ -110,7 +112,7 @@ recurrent_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
     for (int c = tid; c < K; c += kRecThreads) {
       s_k[c] = to_f32(k[(t * H + h) * K + c]);
       s_q[c] = to_f32(q[(t * H + h) * K + c]) * scale;
-      s_d[c] = exp2f(gate[(t * HV + hv) * K + c]);
+      s_d[c] = exp2f(gate_log2_token(gate[(t * HV + hv) * K + c], gate_mode, gscale));
     }
     __syncthreads();
     float pu[VEC], pw[VEC], pkq = 0.f;
@@ -187,23 +189,264 @@ recurrent_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   }
 }
 
+// Wave-per-column-block form for K in {64, 128, 256}, V % 4 == 0 and 16-byte
+// aligned operands (the common case, and the decode hot path).
+//
+// Each 64-lane wave owns all K rows of a CW-column block of one (sequence,
+// value head) state: lane = rl * CL + cl holds rows [16 rl, 16 rl + 16) of the
+// 4 columns starting at 4 cl. The reductions over K are 16-term partial sums
+// followed by a butterfly over the RL row lanes (lane xor CL, 2 CL, ..., 32), so
+// every lane ends with u, w and k . q~ of its columns and computes delta
+// redundantly: no LDS and no barrier. Waves are independent. The decays of a
+// row group are split over its CL lanes (NPL rows each, activation included
+// for a fused gate) and gathered with lane shuffles. The next token's inputs
+// are loaded while the current one is processed (two register sets).
+template <int K>
+struct WaveGeo {
+  static constexpr int RPL = 16;       // state rows per lane
+  static constexpr int RL = K / RPL;   // row lanes
+  static constexpr int CL = 64 / RL;   // column lanes (4 columns each)
+  static constexpr int CW = 4 * CL;    // columns per wave
+  static constexpr int NPL = RPL / CL; // decays computed per lane
+};
+
+template <int NPL>
+struct GVec;  // the NPL gate values of one lane
+template <>
+struct GVec<1> { float x[1]; };
+template <>
+struct GVec<2> { float2 v; };
+template <>
+struct GVec<4> { float4 v; };
+
+template <typename T, int NPL>
+struct WTok;  // one token's inputs for one lane (16 rows of k and q, NPL gates, 4 of v)
+template <int NPL>
+struct WTok<bf16, NPL> {
+  uint4 k[2], q[2];
+  GVec<NPL> g;
+  uint2 v;
+  bf16 b;
+};
+template <int NPL>
+struct WTok<float, NPL> {
+  float4 k[4], q[4];
+  GVec<NPL> g;
+  float4 v;
+  float b;
+};
+
+template <int NPL>
+__device__ __forceinline__ void unpack16(const WTok<bf16, NPL>& x, float* kf, float* qf) {
+  const bf16* kk = reinterpret_cast<const bf16*>(x.k);
+  const bf16* qq = reinterpret_cast<const bf16*>(x.q);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    kf[i] = (float)kk[i];
+    qf[i] = (float)qq[i];
+  }
+}
+template <int NPL>
+__device__ __forceinline__ void unpack16(const WTok<float, NPL>& x, float* kf, float* qf) {
+  const float* kk = reinterpret_cast<const float*>(x.k);
+  const float* qq = reinterpret_cast<const float*>(x.q);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    kf[i] = kk[i];
+    qf[i] = qq[i];
+  }
+}
+template <int NPL>
+__device__ __forceinline__ void unpack_v(const WTok<bf16, NPL>& x, float* vf) {
+  const bf16* vv = reinterpret_cast<const bf16*>(&x.v);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vf[e] = (float)vv[e];
+}
+template <int NPL>
+__device__ __forceinline__ void unpack_v(const WTok<float, NPL>& x, float* vf) {
+  vf[0] = x.v.x; vf[1] = x.v.y; vf[2] = x.v.z; vf[3] = x.v.w;
+}
+__device__ __forceinline__ void store_o4(bf16* p, const float* r) {
+  bf16x4 t = {(bf16)r[0], (bf16)r[1], (bf16)r[2], (bf16)r[3]};
+  *reinterpret_cast<bf16x4*>(p) = t;
+}
+__device__ __forceinline__ void store_o4(float* p, const float* r) {
+  *reinterpret_cast<float4*>(p) = make_float4(r[0], r[1], r[2], r[3]);
+}
+
+template <typename T, int K>
+__global__ void __launch_bounds__(kRecThreads)
+recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                      const float* __restrict__ gate, int gate_mode,
+                      const float* __restrict__ A_log, const T* __restrict__ beta,
+                      const float* h0, const int32_t* __restrict__ cu, int Tlen, int H, int HV,
+                      int V, int n_cb, int64_t n_tasks, float scale, int write_final,
+                      T* __restrict__ o, float* ht) {
+  using G = WaveGeo<K>;
+  constexpr int RPL = G::RPL, CL = G::CL, CW = G::CW, NPL = G::NPL;
+  using Tok = WTok<T, NPL>;
+  const int64_t task = (int64_t)blockIdx.x * (kRecThreads / 64) + (threadIdx.x >> 6);
+  if (task >= n_tasks) return;  // whole wave
+  const int lane = threadIdx.x & 63;
+  const int cb = (int)(task % n_cb);
+  const int64_t nh = task / n_cb;
+  const int n = (int)(nh / HV), hv = (int)(nh % HV);
+  const int h = hv / (HV / H);
+  const int rl = lane / CL, cl = lane % CL;
+  const int r0 = rl * RPL;
+  const int col = cb * CW + cl * 4;
+  const bool col_ok = col < V;
+
+  int64_t bos;
+  int len;
+  seq_range(cu, n, Tlen, &bos, &len);
+  const size_t st_base = (size_t)nh * K * V + (size_t)r0 * V + col;
+
+  if (len == 0) {
+    // empty slot: bitwise passthrough of the state (or +0.0 without one)
+    if (!write_final || (h0 == ht && h0 != nullptr) || !col_ok) return;
+    u32x4 bits[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+      bits[i] = h0 ? __builtin_nontemporal_load(
+                         reinterpret_cast<const u32x4*>(h0 + st_base + (size_t)i * V))
+                   : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+      __builtin_nontemporal_store(bits[i], reinterpret_cast<u32x4*>(ht + st_base + (size_t)i * V));
+    return;
+  }
+
+  // The state streams through once: non-temporal loads and stores keep it
+  // from evicting the small per-token inputs from the caches.
+  float s[RPL][4];
+  if (h0 && col_ok) {
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const f32x4 x =
+          __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(h0 + st_base + (size_t)i * V));
+      s[i][0] = x[0]; s[i][1] = x[1]; s[i][2] = x[2]; s[i][3] = x[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) s[i][0] = s[i][1] = s[i][2] = s[i][3] = 0.f;
+  }
+
+  const float gscale = gate_head_scale(gate_mode, A_log, hv);
+  const int colc = col_ok ? col : 0;  // lanes past V read column 0 and discard it
+  auto load_tok = [&](int64_t t, Tok& x) {
+    const T* kp = k + (t * H + h) * K + r0;
+    const T* qp = q + (t * H + h) * K + r0;
+    constexpr int NV = 16 * sizeof(T) / 16;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      reinterpret_cast<uint4*>(x.k)[j] = reinterpret_cast<const uint4*>(kp)[j];
+      reinterpret_cast<uint4*>(x.q)[j] = reinterpret_cast<const uint4*>(qp)[j];
+    }
+    x.g = *reinterpret_cast<const GVec<NPL>*>(gate + (t * HV + hv) * K + r0 + cl * NPL);
+    x.v = *reinterpret_cast<const decltype(x.v)*>(v + (t * HV + hv) * V + colc);
+    x.b = beta[t * HV + hv];
+  };
+  auto step = [&](const Tok& x, int64_t t) {
+    float kf[RPL], qf[RPL], vf[4];
+    unpack16(x, kf, qf);
+    unpack_v(x, vf);
+    // this lane's NPL decays (rows r0 + cl * NPL + m), then the row group's 16
+    const float* gf = reinterpret_cast<const float*>(&x.g);
+    float dloc[NPL];
+#pragma unroll
+    for (int m = 0; m < NPL; ++m) dloc[m] = exp2f(gate_log2_token(gf[m], gate_mode, gscale));
+    float u[4] = {0.f, 0.f, 0.f, 0.f}, w[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const float d = __shfl(dloc[i % NPL], rl * CL + i / NPL);
+      qf[i] *= scale;
+      kq += kf[i] * qf[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[i][e] *= d;
+        u[e] += s[i][e] * kf[i];
+        w[e] += s[i][e] * qf[i];
+      }
+    }
+#pragma unroll
+    for (int m = CL; m < 64; m <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u[e] += __shfl_xor(u[e], m);
+        w[e] += __shfl_xor(w[e], m);
+      }
+      kq += __shfl_xor(kq, m);
+    }
+    const float b = to_f32(x.b);
+    float dl[4], r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dl[e] = b * (vf[e] - u[e]);
+      r[e] = w[e] + dl[e] * kq;
+    }
+    if (rl == 0 && col_ok) store_o4(o + (t * HV + hv) * V + col, r);
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[i][e] += kf[i] * dl[e];
+    }
+  };
+
+  Tok A, B;
+  load_tok(bos, A);
+  for (int it = 0; it < len; it += 2) {
+    load_tok(bos + min(it + 1, len - 1), B);
+    step(A, bos + it);
+    if (it + 1 >= len) break;
+    load_tok(bos + min(it + 2, len - 1), A);
+    step(B, bos + it + 1);
+  }
+
+  if (write_final && col_ok) {
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+      __builtin_nontemporal_store(f32x4{s[i][0], s[i][1], s[i][2], s[i][3]},
+                                  reinterpret_cast<f32x4*>(ht + st_base + (size_t)i * V));
+  }
+}
+
+template <typename T, int K>
+static hipError_t launch_rec_wave(const kda_dims& d, const void* q, const void* k, const void* v,
+                                  const float* gate, int gm, const float* A_log, const void* beta,
+                                  const float* h0, const int32_t* cu, int write_final, void* o,
+                                  float* ht, hipStream_t s) {
+  const int n_cb = (d.V + WaveGeo<K>::CW - 1) / WaveGeo<K>::CW;
+  const int64_t n_tasks = (int64_t)d.N * d.HV * n_cb;
+  const int wpb = kRecThreads / 64;
+  dim3 grid((unsigned)((n_tasks + wpb - 1) / wpb));
+  hipLaunchKernelGGL((recurrent_wave_kernel<T, K>), grid, dim3(kRecThreads), 0, s, (const T*)q,
+                     (const T*)k, (const T*)v, gate, gm, A_log, (const T*)beta, h0, cu, d.T, d.H,
+                     d.HV, d.V,
+                     n_cb, n_tasks, 1.0f / sqrtf((float)d.K), write_final, (T*)o, ht);
+  return hipGetLastError();
+}
+
 template <typename T, int VEC, int ROWS>
 static hipError_t launch_rec_t(const kda_dims& d, const void* q, const void* k, const void* v,
-                               const float* gate, const void* beta, const float* h0,
+                               const float* gate, int gm, const float* A_log, const void* beta,
+                               const float* h0,
                                const int32_t* cu, int write_final, void* o, float* ht, int BV,
                                hipStream_t s) {
   const int TPR = BV / VEC, RG = kRecThreads / TPR;
   size_t lds = sizeof(float) * (3 * (size_t)d.K + (size_t)RG * TPR * (2 * VEC + 1) + BV);
   dim3 grid((unsigned)(d.N * d.HV), (unsigned)((d.V + BV - 1) / BV));
   hipLaunchKernelGGL((recurrent_kernel<T, VEC, ROWS>), grid, dim3(kRecThreads), lds, s,
-                     (const T*)q, (const T*)k, (const T*)v, gate, (const T*)beta, h0, cu, d.T,
+                     (const T*)q, (const T*)k, (const T*)v, gate, gm, A_log, (const T*)beta, h0, cu,
+                     d.T,
                      d.H, d.HV, d.K, d.V, BV, 1.0f / sqrtf((float)d.K), write_final, (T*)o, ht);
   return hipGetLastError();
 }
 
 template <typename T, int VEC>
 static hipError_t launch_rec_v(const kda_dims& d, const void* q, const void* k, const void* v,
-                               const float* gate, const void* beta, const float* h0,
+                               const float* gate, int gm, const float* A_log, const void* beta,
+                               const float* h0,
                                const int32_t* cu, int write_final, void* o, float* ht,
                                hipStream_t s) {
   // columns per workgroup: 32 threads per row segment, at most 128 columns
@@ -211,10 +454,10 @@ static hipError_t launch_rec_v(const kda_dims& d, const void* q, const void* k, 
   if (BV > d.V) BV = ((d.V + VEC - 1) / VEC) * VEC;
   const int TPR = BV / VEC, RG = kRecThreads / TPR;
   const int rows = (d.K + RG - 1) / RG;
-  if (rows <= 4) return launch_rec_t<T, VEC, 4>(d, q, k, v, gate, beta, h0, cu, write_final, o, ht, BV, s);
-  if (rows <= 8) return launch_rec_t<T, VEC, 8>(d, q, k, v, gate, beta, h0, cu, write_final, o, ht, BV, s);
-  if (rows <= 16) return launch_rec_t<T, VEC, 16>(d, q, k, v, gate, beta, h0, cu, write_final, o, ht, BV, s);
-  return launch_rec_t<T, VEC, 32>(d, q, k, v, gate, beta, h0, cu, write_final, o, ht, BV, s);
+  if (rows <= 4) return launch_rec_t<T, VEC, 4>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, BV, s);
+  if (rows <= 8) return launch_rec_t<T, VEC, 8>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, BV, s);
+  if (rows <= 16) return launch_rec_t<T, VEC, 16>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, BV, s);
+  return launch_rec_t<T, VEC, 32>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, BV, s);
 }
 
 }  // namespace kda
@@ -222,20 +465,39 @@ static hipError_t launch_rec_v(const kda_dims& d, const void* q, const void* k, 
 namespace kda_host {
 
 hipError_t launch_recurrent(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
-                            const void* v, const float* gate, const void* beta,
-                            const float* h0, const int32_t* cu, int write_final, void* o,
-                            float* ht, hipStream_t s) {
+                            const void* v, const float* gate, int gm, const float* A_log,
+                            const void* beta, const float* h0, const int32_t* cu,
+                            int write_final, void* o, float* ht, hipStream_t s) {
   if (d.N == 0) return hipSuccess;
+  auto al = [](const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; };
+  const size_t esz = dt == KDA_BF16 ? 2 : 4;
+  const bool wave_ok = (d.K == 64 || d.K == 128 || d.K == 256) && d.V % 4 == 0 && al(q, 16) &&
+                       al(k, 16) && al(gate, 16) && al(v, 4 * esz) && al(o, 4 * esz) &&
+                       al(h0, 16) && al(ht, 16);
+  if (wave_ok) {
+#define KDA_REC_WAVE(T_)                                                                     \
+  switch (d.K) {                                                                             \
+    case 64: return kda::launch_rec_wave<T_, 64>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);   \
+    case 128: return kda::launch_rec_wave<T_, 128>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s); \
+    default: return kda::launch_rec_wave<T_, 256>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);  \
+  }
+    if (dt == KDA_BF16) {
+      KDA_REC_WAVE(kda::bf16)
+    } else {
+      KDA_REC_WAVE(float)
+    }
+#undef KDA_REC_WAVE
+  }
   const bool st_al16 = ((uintptr_t)h0 % 16 == 0) && ((uintptr_t)ht % 16 == 0);
   const int vec = (d.V % 4 == 0 && st_al16) ? 4 : (d.V % 2 == 0 ? 2 : 1);
   if (dt == KDA_BF16) {
-    if (vec == 4) return kda::launch_rec_v<kda::bf16, 4>(d, q, k, v, gate, beta, h0, cu, write_final, o, ht, s);
-    if (vec == 2) return kda::launch_rec_v<kda::bf16, 2>(d, q, k, v, gate, beta, h0, cu, write_final, o, ht, s);
-    return kda::launch_rec_v<kda::bf16, 1>(d, q, k, v, gate, beta, h0, cu, write_final, o, ht, s);
+    if (vec == 4) return kda::launch_rec_v<kda::bf16, 4>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);
+    if (vec == 2) return kda::launch_rec_v<kda::bf16, 2>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);
+    return kda::launch_rec_v<kda::bf16, 1>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);
   }
-  if (vec == 4) return kda::launch_rec_v<float, 4>(d, q, k, v, gate, beta, h0, cu, write_final, o, ht, s);
-  if (vec == 2) return kda::launch_rec_v<float, 2>(d, q, k, v, gate, beta, h0, cu, write_final, o, ht, s);
-  return kda::launch_rec_v<float, 1>(d, q, k, v, gate, beta, h0, cu, write_final, o, ht, s);
+  if (vec == 4) return kda::launch_rec_v<float, 4>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);
+  if (vec == 2) return kda::launch_rec_v<float, 2>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);
+  return kda::launch_rec_v<float, 1>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);
 }
 
 }  // namespace kda_host

@@ -123,6 +123,28 @@ kda_status kda_chunk_fwd(const kda_dims* dims, kda_dtype dtype, const void* q, c
                          float* final_state, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/*
+ * kda_chunk_fwd_fused_gate -- steps A1..A6 in one call: kda_chunk_fwd with
+ * the gate step done inside the intra-chunk kernel (the fused-gate chunk KDA
+ * path, `use_gate_in_kernel`, of "[Fix] Use unit KDA gate scale when A_log is
+ * omitted", Summary).
+ *   gate_in, gate_in_is_raw, A_log: as kda_gate_cumsum (raw x with
+ *          g = -exp(A_log[hv]) softplus(x), A_log NULL = unit scale; or the
+ *          natural-log g itself, A_log NULL). The chunk-local log2 cumsum is
+ *          formed in the kernel with the gate kernel's float operations, so o
+ *          and final_state are bit-identical to kda_gate_cumsum(chunk_size)
+ *          followed by kda_chunk_fwd, without materialising the log2 gate.
+ *   Other arguments, workspace size, support and alignment as kda_chunk_fwd
+ *   (gate_in in place of gate).
+ */
+kda_status kda_chunk_fwd_fused_gate(const kda_dims* dims, kda_dtype dtype, const void* q,
+                                    const void* k, const void* v, const float* gate_in,
+                                    int32_t gate_in_is_raw, const float* A_log, const void* beta,
+                                    const float* initial_state, const int32_t* cu_seqlens,
+                                    int32_t chunk_size, int32_t output_final_state, void* o,
+                                    float* final_state, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
 /* Workspace bytes kda_chunk_bwd needs for these sizes (0 on unsupported input). */
 size_t kda_chunk_bwd_workspace_bytes(const kda_dims* dims, kda_dtype dtype, int32_t chunk_size);
 
@@ -164,6 +186,21 @@ kda_status kda_recurrent_fwd(const kda_dims* dims, kda_dtype dtype, const void* 
                              const float* initial_state, const int32_t* cu_seqlens,
                              int32_t output_final_state, void* o, float* final_state,
                              hipStream_t stream);
+
+/*
+ * kda_recurrent_fwd_fused_gate -- steps A1 + A7 in one call: kda_recurrent_fwd
+ * with the per-token gate activation done in the scan kernel (the fused-gate
+ * recurrent path of the same page).
+ *   gate_in, gate_in_is_raw, A_log: as kda_gate_cumsum. Results are
+ *   bit-identical to kda_gate_cumsum(chunk_size = 1) followed by
+ *   kda_recurrent_fwd. Other arguments and support as kda_recurrent_fwd.
+ */
+kda_status kda_recurrent_fwd_fused_gate(const kda_dims* dims, kda_dtype dtype, const void* q,
+                                        const void* k, const void* v, const float* gate_in,
+                                        int32_t gate_in_is_raw, const float* A_log,
+                                        const void* beta, const float* initial_state,
+                                        const int32_t* cu_seqlens, int32_t output_final_state,
+                                        void* o, float* final_state, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -86,8 +86,9 @@ def run_gpu(wl, d, path, in_place=False, o_fill=None):
 
 def check_parity(wl, o, ht, o_ref, ht_ref, label=""):
     """Assert the parity bar; returns the measured errors."""
-    mask = in_contract_rows(wl)
-    og, orf = to_np(o)[mask], o_ref[mask]
+    n = wl.T if wl.cu_seqlens is None else int(wl.cu_seqlens[-1])
+    mask = in_contract_rows(wl)[:, :n]
+    og, orf = to_np(o[:, :n])[mask], o_ref[:, :n][mask]
     hg = to_np(ht)
     if wl.dtype == "fp32":
         eo, eh = normwise_max_err(og, orf), normwise_max_err(hg, ht_ref)

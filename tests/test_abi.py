@@ -94,3 +94,26 @@ def test_workspace_bytes():
     b = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d), 1, 64)
     assert b > 4 * 64 * 16 * 64 * 128 * 2
     assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d), 1, 32) == 0
+
+
+def test_fused_gate_entries_reject_bad_arguments():
+    lib = kda.load()
+    d = _dims()
+
+    def chunk(is_raw, A_log, o=FAKE[5], chunk=64):
+        return lib.kda_chunk_fwd_fused_gate(ctypes.byref(d), 1, FAKE[0], FAKE[1], FAKE[2], FAKE[3],
+                                            is_raw, A_log, FAKE[4], None, None, chunk, 1, o,
+                                            FAKE[6], FAKE[7], 1 << 40, None)
+
+    def rec(is_raw, A_log, o=FAKE[5], dd=d):
+        return lib.kda_recurrent_fwd_fused_gate(ctypes.byref(dd), 1, FAKE[0], FAKE[1], FAKE[2],
+                                                FAKE[3], is_raw, A_log, FAKE[4], None, None, 1, o,
+                                                FAKE[6], None)
+
+    assert chunk(0, FAKE[9]) == 2  # A_log only with a raw gate input
+    assert rec(0, FAKE[9]) == 2
+    assert chunk(1, FAKE[9], chunk=32) == 4
+    assert chunk(1, FAKE[5]) == 5  # A_log overlaps o
+    assert rec(1, FAKE[5]) == 5
+    assert chunk(1, FAKE[9], o=FAKE[3]) == 5  # o overlaps the gate input
+    assert rec(1, None, dd=_dims(V=300)) == 4

@@ -51,8 +51,10 @@ def test_decode_in_place_and_empty_slots_bitwise():
         assert torch.equal(ht[s].view(torch.int32), h0_before[s].view(torch.int32)), s
 
 
-def test_empty_slot_copy_not_in_place_bitwise():
-    wl = workloads.tiny_case(220, T=10, HV=2, K=16, V=16, cu_seqlens=[0, 0, 10, 10])
+@pytest.mark.parametrize("K,V", [(16, 16), (64, 72), (128, 128)])
+def test_empty_slot_copy_not_in_place_bitwise(K, V):
+    """K=16 runs the general kernel; K in {64, 128} with V % 4 == 0 the per-wave one."""
+    wl = workloads.tiny_case(220, T=10, HV=2, K=K, V=V, cu_seqlens=[0, 0, 10, 10])
     d = device_inputs(wl)
     h0 = d["h0"]
     h0[0, 0, 0, 0] = -0.0
@@ -60,10 +62,14 @@ def test_empty_slot_copy_not_in_place_bitwise():
     o, ht = run_gpu(wl, d, "recurrent")
     for s in (0, 2):
         assert torch.equal(ht[s].view(torch.int32), h0[s].view(torch.int32))
+    # the planted -0.0 and NaN live in the empty slots only; slot 1 is computed
+    o_ref, ht_ref = oracle.forward(wl)
+    check_parity(wl, o, ht[1:2], o_ref, ht_ref[1:2], f"empty K{K}")
 
 
-def test_empty_slot_without_initial_state_is_zero():
-    wl = workloads.tiny_case(221, T=10, HV=2, K=16, V=16, cu_seqlens=[0, 0, 10, 10], h0=False)
+@pytest.mark.parametrize("K,V", [(16, 16), (128, 128)])
+def test_empty_slot_without_initial_state_is_zero(K, V):
+    wl = workloads.tiny_case(221, T=10, HV=2, K=K, V=V, cu_seqlens=[0, 0, 10, 10], h0=False)
     d = device_inputs(wl)
     o, ht = run_gpu(wl, d, "recurrent")
     z = ht[[0, 2]]
@@ -90,9 +96,10 @@ def test_packed_equals_separate_bitwise():
         assert torch.equal(h1.view(torch.int32), ht[n:n + 1].view(torch.int32))
 
 
-def test_capacity_tail_untouched():
+@pytest.mark.parametrize("K", [32, 64])
+def test_capacity_tail_untouched(K):
     cu = [0, 12, 30]
-    wl = workloads.tiny_case(240, T=40, HV=2, K=32, V=32, cu_seqlens=cu)
+    wl = workloads.tiny_case(240, T=40, HV=2, K=K, V=32, cu_seqlens=cu)
     wl.q[:, 30:] = np.nan
     wl.v[:, 30:] = np.nan
     wl.x[:, 30:] = np.nan
@@ -101,6 +108,25 @@ def test_capacity_tail_untouched():
     assert (to_np(o)[:, 30:] == -9.0).all()
     o_ref, ht_ref = oracle.forward(wl)
     check_parity(wl, o, ht, o_ref, ht_ref, "tail")
+
+
+def test_misaligned_operands_take_the_general_kernel():
+    """q, k offset by one element (not 16-byte aligned): same results as aligned."""
+    wl = workloads.tiny_case(260, T=33, H=1, HV=2, K=64, V=64, dtype="bf16")
+    d = device_inputs(wl)
+    o, ht = run_gpu(wl, d, "recurrent")
+    G = kda.gate_cumsum(d["x"], d["A_log"], d["cu"], 1)
+    qb = torch.empty(d["q"].numel() + 1, dtype=d["q"].dtype, device=DEV)
+    kb = torch.empty(d["k"].numel() + 1, dtype=d["k"].dtype, device=DEV)
+    q2 = qb[1:].view(d["q"].shape)
+    k2 = kb[1:].view(d["k"].shape)
+    q2.copy_(d["q"])
+    k2.copy_(d["k"])
+    o2, h2 = kda.recurrent_kda(q2, k2, d["v"], G, d["beta"], d["h0"], output_final_state=True)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle.forward(wl)
+    check_parity(wl, o2, h2, o_ref, ht_ref, "misaligned")
+    check_parity(wl, o, ht, o_ref, ht_ref, "aligned")
 
 
 def test_rejects_inputs_that_require_grad():
