@@ -29,9 +29,10 @@
 // 2^(G2_i - G2_r) * 2^(G2_r - G2_j) with a reference token j < r <= i, so
 // both factors are <= 1 and a product of them can only underflow (harmless:
 // the true value is then below FP32 range too). Off-diagonal 16x16 tiles use
-// r = first token of the row tile. Inside a diagonal tile the pairs are split
-// by the highest bit in which the local indices differ (levels 3..0, each
-// with its own reference), plus the exact diagonal i == j. This keeps
+// r = first token of the row tile. Inside a diagonal tile the reference is
+// the middle token of a segment, halving segments until every factor is
+// within 2^-+112 (pairs straddling a middle are exact at any range), plus
+// the exact diagonal i == j when single tokens decay further. This keeps
 // unbounded gates (chunk-local cumsums far below -126 in log2 units) exact.
 #include <algorithm>
 #include <type_traits>
@@ -334,115 +335,126 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
       }
     }
   }
-  // diagonal tile: one pass with reference r when the tile's gate range allows it
-  float rng = 0.f;
-#pragma unroll
-  for (int p = 0; p < QK; ++p) {
-    const int c0 = 16 * p + 4 * g;
-    float a0[4], a1[4];
-    lds4(sG + r * GS + c0, a0);
-    lds4(sG + (r + 15) * GS + c0, a1);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) rng = fmaxf(rng, a0[e] - a1[e]);
-  }
-  rng = fmaxf(rng, __shfl_xor(rng, 16));
-  rng = fmaxf(rng, __shfl_xor(rng, 32));
+  // Diagonal tile, recursive mid-point references. Pass `lev` (0..3) splits
+  // the tile into segments of S = 16 >> lev tokens and uses each segment's
+  // middle token m as the reference of its rows and columns:
+  // 2^(G2_i - G2_j) = 2^(G2_i - G2_m) 2^(G2_m - G2_j). Pairs that straddle the
+  // middle (j < m <= i) get two factors <= 1 and are exact at any gate range;
+  // the remaining same-segment pairs are exact when every factor stays within
+  // 2^-+kFastRange, i.e. when the segment's gate range on each side of m is
+  // at most kFastRange. The passes stop at the first level where that holds
+  // for all segments (one pass for moderate gates); if even single tokens
+  // exceed it, a last pass adds the diagonal i == j (decay factor 1).
   const int jl = l16, il = l16;
   const int jrow = 16 * I + jl;
-  if (rng <= kFastRange) {
-    F rf[KS_K];  // k_j 2^(G2_r - G2_j) with r <= j: >= 1 but at most 2^112
+  int lstar = 3;
+  bool need_diag = false;
+  {
+    // 15 (level, segment) items on lanes l16 < 15; channels split over g
+    const int lv = l16 < 1 ? 0 : l16 < 3 ? 1 : l16 < 7 ? 2 : 3;
+    const int S = 16 >> lv, seg = l16 - ((1 << lv) - 1);
+    const int ta = r + seg * S, tm = ta + S / 2, tb = ta + S - 1;
+    float rng = 0.f;
+    if (l16 < 15) {
+#pragma unroll
+      for (int p = 0; p < QK; ++p) {
+        const int c0 = 16 * p + 4 * g;
+        float ga[4], gm[4], gb[4];
+        lds4(sG + ta * GS + c0, ga);
+        lds4(sG + tm * GS + c0, gm);
+        lds4(sG + tb * GS + c0, gb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rng = fmaxf(rng, fmaxf(ga[e] - gm[e], gm[e] - gb[e]));
+      }
+    }
+    rng = fmaxf(rng, __shfl_xor(rng, 16));
+    rng = fmaxf(rng, __shfl_xor(rng, 32));
+    const uint64_t okb = __ballot(rng <= kFastRange);  // bit l16 (lanes 0..15)
+    if ((okb & 0x1ull) == 0x1ull) lstar = 0;
+    else if ((okb & 0x6ull) == 0x6ull) lstar = 1;
+    else if ((okb & 0x78ull) == 0x78ull) lstar = 2;
+    else if ((okb & 0x7F80ull) == 0x7F80ull) lstar = 3;
+    else need_diag = true;
+  }
+  for (int lev = 0; lev <= lstar; ++lev) {
+    const int S = 16 >> lev;
+    const bool final_pass = (lev == lstar) && !need_diag;
+    const int mj = 16 * I + (jl / S) * S + S / 2;  // reference of row j
+    const int mi = 16 * I + (il / S) * S + S / 2;  // reference of column i
+    F ra[KS_K], lk[KS_K], lq[KS_K];
 #pragma unroll
     for (int p = 0; p < QK; ++p) {
       const int c0 = 16 * p + 4 * g;
-      float gj[4], g0[4], kj[4], vv[4];
-      lds4(sG + jrow * GS + c0, gj);
-      lds4(sG + r * GS + c0, g0);
+      float kj[4], ki[4], qi[4], gj[4], gmj[4], gi[4], gmi[4], va[4], vk[4], vq[4];
       lds4(sK + jrow * KSTR + c0, kj);
+      lds4(sK + icol * KSTR + c0, ki);
+      lds4(sQ + icol * KSTR + c0, qi);
+      lds4(sG + jrow * GS + c0, gj);
+      lds4(sG + mj * GS + c0, gmj);
+      lds4(sG + icol * GS + c0, gi);
+      lds4(sG + mi * GS + c0, gmi);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vv[e] = kj[e] * ex2(g0[e] - gj[e]);
-      put_quad<M>(rf, p, vv);
+      for (int e = 0; e < 4; ++e) {
+        va[e] = kj[e] * ex2(gmj[e] - gj[e]);
+        const float x = ex2(gi[e] - gmi[e]);
+        vk[e] = ki[e] * x;
+        vq[e] = qi[e] * scale * x;
+      }
+      put_quad<M>(ra, p, va);
+      put_quad<M>(lk, p, vk);
+      put_quad<M>(lq, p, vq);
     }
     f32x4 xa = zero4(), xp = zero4(), xt = zero4();
 #pragma unroll
     for (int ks = 0; ks < KS_K; ++ks) {
-      xa = M::mma(rf[ks], lkf[ks], xa);
-      xp = M::mma(rf[ks], lqf[ks], xp);
-      if constexpr (BWD) xt = M::mma(lqf[ks], rf[ks], xt);
+      xa = M::mma(ra[ks], lk[ks], xa);
+      xp = M::mma(ra[ks], lq[ks], xp);
+      if constexpr (BWD) xt = M::mma(lq[ks], ra[ks], xt);
+    }
+    // pair (row a, column b) belongs to this pass: same segment, and either
+    // the last pass or straddling the segment's middle
+    auto take = [&](int a, int b) {
+      return (a / S == b / S) && (final_pass || ((a / (S / 2)) != (b / (S / 2))));
+    };
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int jr = 4 * g + e;  // local row j of this accumulator element, column i = il
+      if (take(jr, il)) {
+        if (il > jr) dA[e] += xa[e];
+        if (il >= jr) dP[e] += xp[e];
+      }
+      if constexpr (BWD) {
+        // transposed tile: row i = 4g + e, column j = l16
+        if (take(l16, jr) && jr >= l16) dPT[e] += xt[e];
+      }
+    }
+  }
+  if (need_diag) {
+    // i == j: P_ii = q~_i . k_i (no decay)
+    F ra[KS_K], lq[KS_K];
+#pragma unroll
+    for (int p = 0; p < QK; ++p) {
+      const int c0 = 16 * p + 4 * g;
+      float kj[4], qi[4], vq[4];
+      lds4(sK + jrow * KSTR + c0, kj);
+      lds4(sQ + icol * KSTR + c0, qi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vq[e] = qi[e] * scale;
+      put_quad<M>(ra, p, kj);
+      put_quad<M>(lq, p, vq);
+    }
+    f32x4 xp = zero4(), xt = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS_K; ++ks) {
+      xp = M::mma(ra[ks], lq[ks], xp);
+      if constexpr (BWD) xt = M::mma(lq[ks], ra[ks], xt);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int jr = 4 * g + e;
-      dA[e] = (il > jr) ? xa[e] : 0.f;
-      dP[e] = (il >= jr) ? xp[e] : 0.f;
-      dPT[e] = (jr >= l16) ? xt[e] : 0.f;  // P tile: row i = 4g + e, column j = l16
-    }
-  } else {
-    // exact split by the highest differing bit of the local indices (levels
-    // 3..0, each with its own reference token), then the diagonal i == j
-#pragma unroll
-    for (int lev = 3; lev >= -1; --lev) {
-      const bool rowOn = lev < 0 || ((jl >> lev) & 1) == 0;
-      const bool colOn = lev < 0 || ((il >> lev) & 1) == 1;
-      const int rr = lev < 0 ? 0 : 16 * I + ((((jl >> lev) | 1)) << lev);  // reference of row j
-      const int rc = lev < 0 ? 0 : 16 * I + ((il >> lev) << lev);          // reference of col i
-      F ra[KS_K], lk[KS_K], lq[KS_K];
-#pragma unroll
-      for (int p = 0; p < QK; ++p) {
-        const int c0 = 16 * p + 4 * g;
-        float kj[4], ki[4], qi[4], va[4], vk[4], vq[4];
-        lds4(sK + jrow * KSTR + c0, kj);
-        lds4(sQ + icol * KSTR + c0, qi);
-        if (lev < 0) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            va[e] = kj[e];
-            vk[e] = 0.f;
-            vq[e] = qi[e] * scale;
-          }
-        } else {
-          float gj[4], grr[4], gi[4], grc[4];
-          lds4(sK + icol * KSTR + c0, ki);
-          lds4(sG + jrow * GS + c0, gj);
-          lds4(sG + rr * GS + c0, grr);
-          lds4(sG + icol * GS + c0, gi);
-          lds4(sG + rc * GS + c0, grc);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            va[e] = rowOn ? kj[e] * ex2(grr[e] - gj[e]) : 0.f;
-            const float x = colOn ? ex2(gi[e] - grc[e]) : 0.f;
-            vk[e] = ki[e] * x;
-            vq[e] = qi[e] * scale * x;
-          }
-        }
-        put_quad<M>(ra, p, va);
-        put_quad<M>(lk, p, vk);
-        put_quad<M>(lq, p, vq);
-      }
-      f32x4 xa = zero4(), xp = zero4(), xt = zero4();
-#pragma unroll
-      for (int ks = 0; ks < KS_K; ++ks) {
-        if (lev >= 0) xa = M::mma(ra[ks], lk[ks], xa);
-        xp = M::mma(ra[ks], lq[ks], xp);
-        if constexpr (BWD) xt = M::mma(lq[ks], ra[ks], xt);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int jr = 4 * g + e;  // local row j of this accumulator element
-        bool valid;
-        if (lev < 0) valid = (jr == il);
-        else valid = ((il >> (lev + 1)) == (jr >> (lev + 1))) && ((il >> lev) & 1) && !((jr >> lev) & 1);
-        if (valid) {
-          dA[e] += xa[e];
-          dP[e] += xp[e];
-        }
-        if constexpr (BWD) {
-          // transposed tile: row i = 4g + e (= jr), column j = l16
-          const int ir = jr, jc = l16;
-          bool vt;
-          if (lev < 0) vt = (ir == jc);
-          else vt = ((ir >> (lev + 1)) == (jc >> (lev + 1))) && ((ir >> lev) & 1) && !((jc >> lev) & 1);
-          if (vt) dPT[e] += xt[e];
-        }
+      if (jr == il) dP[e] += xp[e];
+      if constexpr (BWD) {
+        if (jr == l16) dPT[e] += xt[e];
       }
     }
   }
@@ -615,44 +627,50 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     for (int i = 0; i < 16; ++i) sA[(16 * d + i) * AS + 16 * d + jj] = x[i];
   }
   __syncthreads();
-  // 7b. block rows: T_IJ = -T_II * sum_{M=J}^{I-1} A_IM T_MJ (scratch: upper block (J, I))
-  for (int Ib = 1; Ib < 4; ++Ib) {
-    const int Jb = wave;
-    const int a = l16, b0 = 4 * g;  // lane owns row a, columns b0..b0+3 of the block
-    if (Jb < Ib) {
-      float xs[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int Mb = Jb; Mb < Ib; ++Mb) {
-        float arow[16];
+  // 7b. block rows T_IJ = -T_II sum_{M=J}^{I-1} A_IM T_MJ on the FP32 matrix
+  // cores. Wave J owns block column J: its T_MJ stay in registers, since an
+  // FP32 16x16 accumulator (lane: column l16, rows 4g..4g+3) is exactly the B
+  // operand of the next product over those rows. A_IM and T_II are A operands
+  // read as rows from LDS. The blocks are stored after every wave has read A.
+  {
+    f32x4 tcol[4];  // T_MJ of this wave's block column J, in B-operand layout
 #pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4) lds4(sA + (16 * Ib + a) * AS + 16 * Mb + 4 * m4, arow + 4 * m4);
+    for (int m = 0; m < 4; ++m) tcol[m] = zero4();
 #pragma unroll
-        for (int p = 0; p < 16; ++p) {
-          float t4[4];
-          lds4(sA + (16 * Mb + p) * AS + 16 * Jb + b0, t4);
+    for (int J = 0; J < 3; ++J) {  // compile-time J: register indices stay static
+      if (J != wave) continue;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) xs[e] += arow[p] * t4[e];
+      for (int i = 0; i < 4; ++i) tcol[J][i] = sA[(16 * J + 4 * g + i) * AS + 16 * J + l16];
+#pragma unroll
+      for (int Ib = J + 1; Ib < 4; ++Ib) {
+        f32x4 x = zero4();
+#pragma unroll
+        for (int Mb = J; Mb < Ib; ++Mb) {
+          float a4[4];
+          lds4(sA + (16 * Ib + l16) * AS + 16 * Mb + 4 * g, a4);
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[ks], tcol[Mb][ks], x, 0, 0, 0);
         }
+        float t4[4];
+        lds4(sA + (16 * Ib + l16) * AS + 16 * Ib + 4 * g, t4);
+        f32x4 y = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          y = __builtin_amdgcn_mfma_f32_16x16x4f32(t4[ks], x[ks], y, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tcol[Ib][i] = -y[i];
       }
-      *reinterpret_cast<float4*>(sA + (16 * Jb + a) * AS + 16 * Ib + b0) = make_float4(xs[0], xs[1], xs[2], xs[3]);
     }
-    __syncthreads();
-    if (Jb < Ib) {
-      float ts[4] = {0.f, 0.f, 0.f, 0.f};
-      float trow[16];
+    __syncthreads();  // every read of A is done
 #pragma unroll
-      for (int m4 = 0; m4 < 4; ++m4) lds4(sA + (16 * Ib + a) * AS + 16 * Ib + 4 * m4, trow + 4 * m4);
+    for (int J = 0; J < 3; ++J) {
+      if (J != wave) continue;
 #pragma unroll
-      for (int p = 0; p < 16; ++p) {
-        float x4[4];
-        lds4(sA + (16 * Jb + p) * AS + 16 * Ib + b0, x4);
+      for (int Ib = J + 1; Ib < 4; ++Ib)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ts[e] -= trow[p] * x4[e];
-      }
-      *reinterpret_cast<float4*>(sA + (16 * Ib + a) * AS + 16 * Jb + b0) = make_float4(ts[0], ts[1], ts[2], ts[3]);
+        for (int i = 0; i < 4; ++i) sA[(16 * Ib + 4 * g + i) * AS + 16 * J + l16] = tcol[Ib][i];
     }
-    __syncthreads();
-    if (Jb < Ib)
-      *reinterpret_cast<float4*>(sA + (16 * Jb + a) * AS + 16 * Ib + b0) = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
   }
 
@@ -747,11 +765,13 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   for (int u = 0; u < VU; ++u) {
     const int f = tid + u * kThreads, m = f / (V / EPU), cu_ = f % (V / EPU);
     const float b = sBeta[m];
-    T tmp[EPU];
+    union {
+      T t[EPU];
+      uint4 u;
+    } tmp;
 #pragma unroll
-    for (int e = 0; e < EPU; ++e) tmp[e] = from_f32<T>(b * unit_elem<T>(vr[u], e));
-#pragma unroll
-    for (int e = 0; e < EPU; ++e) sV[m * VSTR + EPU * cu_ + e] = tmp[e];
+    for (int e = 0; e < EPU; ++e) tmp.t[e] = from_f32<T>(b * unit_elem<T>(vr[u], e));
+    *reinterpret_cast<uint4*>(sV + m * VSTR + EPU * cu_) = tmp.u;
   }
   __syncthreads();
 
