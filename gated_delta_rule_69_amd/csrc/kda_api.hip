@@ -81,8 +81,9 @@ kda_status chunk_fwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const 
                 overlaps(A_log, (size_t)d->HV * 4, ht, s.state)))
     return KDA_ERR_ALIAS;
   if (d->N == 0) return KDA_OK;
-  // 16-byte vector loads of q, k, v and the gate; 256-byte aligned workspace
-  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)gate) & 15) ||
+  // 16-byte vector loads of q, k, v and the gate, vector stores of o;
+  // 256-byte aligned workspace
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)gate | (uintptr_t)o) & 15) ||
       ((uintptr_t)workspace & 255))
     return KDA_ERR_UNSUPPORTED;
   const size_t need = kda_host::chunk_workspace_bytes(*d, dt, chunk_size);

@@ -96,7 +96,7 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
   const int bv = scan_block_v(chains, V);
   auto launch_scan = [&](auto bvc) {
     constexpr int BVC = decltype(bvc)::value;
-    hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC>), dim3((unsigned)chains, V / BVC),
+    hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, false>), dim3((unsigned)chains, V / BVC),
                        dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL,
                        (const int*)ws_int, cu, h0, d.N, d.T, d.HV, write_final, (T*)o, ht,
                        (T*)nullptr);

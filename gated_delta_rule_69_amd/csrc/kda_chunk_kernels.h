@@ -837,7 +837,9 @@ struct Raw4<float> {
   }
 };
 
-template <typename T, int K, int V, int BV>
+// KEEP: also store every chunk's start state S0 and Delta into ws_B (the
+// backward pass reuses them); the forward instantiation has none of it.
+template <typename T, int K, int V, int BV, bool KEEP>
 __global__ void __launch_bounds__(kThreads)
 chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
                   const int* __restrict__ ws_int, const int32_t* __restrict__ cu,
@@ -855,7 +857,7 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
   static_assert(RTW >= 1 && CTB >= 1, "tile shape");
 
   __shared__ F sS[2][KS_K][CTB][64];  // S as B fragments (contraction over channels), 2 buffers
-  __shared__ F sD[KS_C][CTB][64];     // Delta as B fragments (contraction over tokens)
+  __shared__ F sD[2][KS_C][CTB][64];  // Delta as B fragments (contraction over tokens), 2 buffers
 
   const int n = blockIdx.x / HV, hv = blockIdx.x % HV, vb = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
@@ -934,13 +936,57 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
       }
     }
 
-  // one chunk of the recurrence with operands `cur`, LDS buffer `buf`
+  // Output rows of token tile `wave` of a chunk whose S0 and Delta sit in LDS
+  // buffer `buf`: O = (Q~ Gamma) S0 + P Delta, formed transposed
+  // (O^T = S0^T (Q~ Gamma)^T + Delta^T P^T): the B fragments of S0 and Delta are
+  // the A fragments of their transposes and vice versa, and the O^T
+  // accumulator gives each lane 4 consecutive value columns of one token,
+  // written as one 8- or 16-byte store. It runs one chunk late, next to the
+  // following chunk's W S products, so it stays off the recurrence's path.
+  struct OutOps {
+    F qg[KS_K], p[KS_C];
+  };
+  auto output = [&](const OutOps& op, const int cj, const int buf) __attribute__((always_inline)) {
+    const int cidx = cj - cbeg;
+    const int64_t t0 = bos + (int64_t)cidx * kC;
+    const int L = min(kC, len - cidx * kC);
+    f32x4 OT[CTB];
+#pragma unroll
+    for (int ct = 0; ct < CTB; ++ct) OT[ct] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS_K; ++ks)
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct) OT[ct] = M::mma(sS[buf][ks][ct][lane], op.qg[ks], OT[ct]);
+#pragma unroll
+    for (int ks = 0; ks < KS_C; ++ks)
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct) OT[ct] = M::mma(sD[buf][ks][ct][lane], op.p[ks], OT[ct]);
+    const int i = 16 * wave + l16;
+    if (i < L && o) {
+      T* orow = o + ((t0 + i) * HV + hv) * V + col_base + 4 * g;
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct) {
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = (bf16)OT[ct][e];
+          *reinterpret_cast<bf16x4*>(orow + 16 * ct) = x;
+        } else {
+          *reinterpret_cast<float4*>(orow + 16 * ct) = make_float4(OT[ct][0], OT[ct][1], OT[ct][2], OT[ct][3]);
+        }
+      }
+    }
+  };
+  OutOps prev;  // Q~ Gamma and P of the previous chunk
+
+  // one chunk of the recurrence with operands `cur`, LDS buffer `buf`; the
+  // previous chunk's output is formed after the first barrier
   auto step = [&](const Ops& cur, const int cj, const int buf) __attribute__((always_inline)) {
     const int cidx = cj - cbeg;
     const int64_t t0 = bos + (int64_t)cidx * kC;
     const int L = min(kC, len - cidx * kC);
 
-    if (ws_B) {  // backward support: keep the chunk's start state
+    if constexpr (KEEP) {  // backward support: keep the chunk's start state
       T* st = ws_B + ((size_t)cj * HV + hv) * WsB<T, K, V>::elems + WsB<T, K, V>::oS0;
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt)
@@ -975,6 +1021,7 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     }
     __syncthreads();
 
+    if (cj > cbeg) output(prev, cj - 1, buf ^ 1);
     // (2) Delta = U - W S for token tile `wave`
     f32x4 D[CTB];
     {
@@ -991,7 +1038,7 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
 #pragma unroll
         for (int e = 0; e < 4; ++e) D[ct][e] = R4::get(cur.u[ct], e) - ws_[ct][e];
     }
-    if (ws_B) {  // backward support: keep Delta
+    if constexpr (KEEP) {  // backward support: keep Delta
       T* dl = ws_B + ((size_t)cj * HV + hv) * WsB<T, K, V>::elems + WsB<T, K, V>::oDL;
 #pragma unroll
       for (int ct = 0; ct < CTB; ++ct)
@@ -1007,13 +1054,13 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
         bf16x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = (bf16)D[ct][e];
-        *(reinterpret_cast<bf16x4*>(&sD[ks][ct][lane]) + half) = x;
+        *(reinterpret_cast<bf16x4*>(&sD[buf][ks][ct][lane]) + half) = x;
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           F f;
           M::set(f, 0, D[ct][e]);
-          sD[4 * wave + e][ct][lane] = f;
+          sD[buf][4 * wave + e][ct][lane] = f;
         }
       }
     }
@@ -1030,31 +1077,12 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
 #pragma unroll
       for (int ks = 0; ks < KS_C; ++ks)
 #pragma unroll
-        for (int ct = 0; ct < CTB; ++ct) S[rt][ct] = M::mma(cur.kh[rt][ks], sD[ks][ct][lane], S[rt][ct]);
+        for (int ct = 0; ct < CTB; ++ct) S[rt][ct] = M::mma(cur.kh[rt][ks], sD[buf][ks][ct][lane], S[rt][ct]);
     }
-    // (4) output rows of token tile `wave`: O = (Q~ Gamma) S0 + P Delta
-    {
-      f32x4 O[CTB];
 #pragma unroll
-      for (int ct = 0; ct < CTB; ++ct) O[ct] = zero4();
+    for (int ks = 0; ks < KS_K; ++ks) prev.qg[ks] = cur.qg[ks];
 #pragma unroll
-      for (int ks = 0; ks < KS_K; ++ks)
-#pragma unroll
-        for (int ct = 0; ct < CTB; ++ct) O[ct] = M::mma(cur.qg[ks], sS[buf][ks][ct][lane], O[ct]);
-#pragma unroll
-      for (int ks = 0; ks < KS_C; ++ks)
-#pragma unroll
-        for (int ct = 0; ct < CTB; ++ct) O[ct] = M::mma(cur.p[ks], sD[ks][ct][lane], O[ct]);
-#pragma unroll
-      for (int ct = 0; ct < CTB; ++ct) {
-        const int col = col_base + 16 * ct + l16;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * wave + 4 * g + e;
-          if (i < L && o) o[((t0 + i) * HV + hv) * V + col] = from_f32<T>(O[ct][e]);
-        }
-      }
-    }
+    for (int ks = 0; ks < KS_C; ++ks) prev.p[ks] = cur.p[ks];
   };
 
   // two operand sets, unrolled by two so the next chunk's loads stay in flight
@@ -1070,6 +1098,9 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     step(opB, cj + 1, 1);
     if (cj + 2 >= cend) break;
   }
+  // the last chunk's output (its S0 and Delta buffers are intact: no barrier
+  // has been passed since they were published, and nothing writes them again)
+  output(prev, cend - 1, (cend - 1 - cbeg) & 1);
 
   if (write_final) {
 #pragma unroll

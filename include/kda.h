@@ -110,8 +110,8 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_dims* dims, kda_dtype dtype, int3
  *          (may equal initial_state).
  *   workspace: device scratch of at least kda_chunk_fwd_workspace_bytes();
  *          its contents are scratch on entry and on return.
- *   Supported: K, V in {64, 128}; chunk_size == 64; FP32 or BF16; q, k, v
- *   and gate 16-byte aligned, workspace 256-byte aligned (else
+ *   Supported: K, V in {64, 128}; chunk_size == 64; FP32 or BF16; q, k, v,
+ *   gate and o 16-byte aligned, workspace 256-byte aligned (else
  *   KDA_ERR_UNSUPPORTED).
  *   Arithmetic: FP32 accumulation and FP32 state; for BF16 inputs the
  *   matrix products take bf16 operands on the matrix cores.
