@@ -124,7 +124,9 @@ struct IntraLds {
   static constexpr size_t R1 = cmax((size_t)kC * GS * 4, (size_t)kC * VSTR * sizeof(T));
   static constexpr size_t R2 = (size_t)kC * KSTR * sizeof(T);
   static constexpr size_t R3 = cmax((size_t)kC * KSTR * sizeof(T), (size_t)kC * AS * 4);
-  static constexpr size_t total = R1 + R2 + R3 + kC * 4;
+  static constexpr size_t RB = (size_t)kC * 4;                    // beta
+  static constexpr size_t RT = (size_t)(kC / kGateBlock) * K * 4;  // gate block totals
+  static constexpr size_t total = R1 + R2 + R3 + RB + RT;
 };
 
 // 2^x on the transcendental unit (v_exp_f32). Results below 2^-126 flush to
@@ -212,6 +214,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   T* sQ = reinterpret_cast<T*>(smem + Lds::R1 + Lds::R2);           // R3: q [C][KSTR]
   float* sA = reinterpret_cast<float*>(smem + Lds::R1 + Lds::R2);   // R3 later: A, then T [C][AS]
   float* sBeta = reinterpret_cast<float*>(smem + Lds::R1 + Lds::R2 + Lds::R3);
+  float* sTot = reinterpret_cast<float*>(smem + Lds::R1 + Lds::R2 + Lds::R3 + Lds::RB);
 
   const ChunkGeo geo = chunk_geo(blockIdx.x, cu, ws_int, N, T_);
   if (!geo.ok) return;
@@ -271,15 +274,42 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   }
   __syncthreads();
   if (gate_mode != kGateLog2) {
-    // chunk-local inclusive cumsum in token order, times log2(e): the same
-    // float operations as the gate kernel, so G2 is bit-identical to its
-    // output. Pad rows keep the last token's value.
-    if (tid < K) {
-      float acc = 0.f;
-#pragma unroll 16
-      for (int r = 0; r < kC; ++r) {
-        if (r < L) acc = acc + sG[r * GS + tid];
-        sG[r * GS + tid] = acc * kLog2e;
+    // chunk-local inclusive cumsum times log2(e) in the blocked order of
+    // kGateBlock (the gate kernel's order, so G2 is bit-identical to its
+    // output). Thread (cg, rb) owns channels 4cg..4cg+3 of token block rb.
+    // Pad rows keep the last token's value.
+    constexpr int NCG = K / 4, NB = kC / kGateBlock;
+    const int cg = tid % NCG, rb = tid / NCG;
+    float pm[kGateBlock][4];
+    if (rb < NB) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < kGateBlock; ++m) {
+        const int rr = rb * kGateBlock + m;
+        lds4(sG + rr * GS + 4 * cg, pm[m]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (rr < L) acc[e] = acc[e] + pm[m][e];
+          pm[m][e] = acc[e];
+        }
+      }
+      *reinterpret_cast<float4*>(sTot + rb * K + 4 * cg) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    __syncthreads();
+    if (rb < NB) {
+      float c[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < rb; ++b) {
+        float t4[4];
+        lds4(sTot + b * K + 4 * cg, t4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[e] = c[e] + t4[e];
+      }
+#pragma unroll
+      for (int m = 0; m < kGateBlock; ++m) {
+        const int rr = rb * kGateBlock + m;
+        *reinterpret_cast<float4*>(sG + rr * GS + 4 * cg) =
+            make_float4((c[0] + pm[m][0]) * kLog2e, (c[1] + pm[m][1]) * kLog2e,
+                        (c[2] + pm[m][2]) * kLog2e, (c[3] + pm[m][3]) * kLog2e);
       }
     }
     __syncthreads();
@@ -288,8 +318,47 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   // ---- 2. A^T and P^T tiles: column tile I = wave (tokens i), row tiles J <= I (tokens j)
   const int I = wave;
   const int icol = 16 * I + l16;
-  const int r = 16 * I;  // reference token of every tile in column I
-  F lkf[KS_K], lqf[KS_K];  // column factors k_i 2^(G2_i - G2_r), q~_i 2^(G2_i - G2_r) (<= 1)
+  const int jl = l16, il = l16;
+  const int jrow = 16 * I + jl;
+  int lstar = 3;
+  bool need_diag = false;
+  {
+    // 15 (level, segment) items on lanes l16 < 15; channels split over g
+    const int lv = l16 < 1 ? 0 : l16 < 3 ? 1 : l16 < 7 ? 2 : 3;
+    const int S = 16 >> lv, seg = l16 - ((1 << lv) - 1);
+    const int ta = 16 * I + seg * S, tm = ta + S / 2, tb = ta + S - 1;
+    float rng = 0.f;
+    if (l16 < 15) {
+#pragma unroll
+      for (int p = 0; p < QK; ++p) {
+        const int c0 = 16 * p + 4 * g;
+        float ga[4], gm[4], gb[4];
+        lds4(sG + ta * GS + c0, ga);
+        lds4(sG + tm * GS + c0, gm);
+        lds4(sG + tb * GS + c0, gb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rng = fmaxf(rng, fmaxf(ga[e] - gm[e], gm[e] - gb[e]));
+      }
+    }
+    rng = fmaxf(rng, __shfl_xor(rng, 16));
+    rng = fmaxf(rng, __shfl_xor(rng, 32));
+    const uint64_t okb = __ballot(rng <= kFastRange);  // bit l16 (lanes 0..15)
+    if ((okb & 0x1ull) == 0x1ull) lstar = 0;
+    else if ((okb & 0x6ull) == 0x6ull) lstar = 1;
+    else if ((okb & 0x78ull) == 0x78ull) lstar = 2;
+    else if ((okb & 0x7F80ull) == 0x7F80ull) lstar = 3;
+    else need_diag = true;
+  }
+  // Reference token of column tile I. When the diagonal tile passes the
+  // one-pass test (every factor of its middle token within 2^-+kFastRange),
+  // the middle token r = 16I + 8 serves the whole column: left factors
+  // 2^(G2_i - G2_r) stay below 2^kFastRange, right factors of earlier tiles
+  // are <= 1, and the diagonal tile needs only its row factors. Otherwise
+  // r = 16I keeps every off-diagonal factor <= 1 and the diagonal tile takes
+  // the recursive passes below.
+  const bool mid = (lstar == 0) && !need_diag;
+  const int r = 16 * I + (mid ? 8 : 0);
+  F lkf[KS_K], lqf[KS_K];  // column factors k_i 2^(G2_i - G2_r), q~_i 2^(G2_i - G2_r)
 #pragma unroll
   for (int p = 0; p < QK; ++p) {
     const int c0 = 16 * p + 4 * g;
@@ -315,7 +384,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     accA[J] = accP[J] = pT[J] = zero4();
     if (J < I) {
       const int jrow = 16 * J + l16;
-      F rf[KS_K];  // row factors k_j 2^(G2_r - G2_j) (<= 1: j < r)
+      F rf[KS_K];  // row factors k_j 2^(G2_r - G2_j) (<= 1: j < 16I <= r)
 #pragma unroll
       for (int p = 0; p < QK; ++p) {
         const int c0 = 16 * p + 4 * g;
@@ -345,38 +414,35 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   // at most kFastRange. The passes stop at the first level where that holds
   // for all segments (one pass for moderate gates); if even single tokens
   // exceed it, a last pass adds the diagonal i == j (decay factor 1).
-  const int jl = l16, il = l16;
-  const int jrow = 16 * I + jl;
-  int lstar = 3;
-  bool need_diag = false;
-  {
-    // 15 (level, segment) items on lanes l16 < 15; channels split over g
-    const int lv = l16 < 1 ? 0 : l16 < 3 ? 1 : l16 < 7 ? 2 : 3;
-    const int S = 16 >> lv, seg = l16 - ((1 << lv) - 1);
-    const int ta = r + seg * S, tm = ta + S / 2, tb = ta + S - 1;
-    float rng = 0.f;
-    if (l16 < 15) {
+  if (mid) {
+    F ra[KS_K];  // k_j 2^(G2_r - G2_j), within 2^-+kFastRange
 #pragma unroll
-      for (int p = 0; p < QK; ++p) {
-        const int c0 = 16 * p + 4 * g;
-        float ga[4], gm[4], gb[4];
-        lds4(sG + ta * GS + c0, ga);
-        lds4(sG + tm * GS + c0, gm);
-        lds4(sG + tb * GS + c0, gb);
+    for (int p = 0; p < QK; ++p) {
+      const int c0 = 16 * p + 4 * g;
+      float gj[4], g0[4], kj[4], vv[4];
+      lds4(sG + jrow * GS + c0, gj);
+      lds4(sG + r * GS + c0, g0);
+      lds4(sK + jrow * KSTR + c0, kj);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rng = fmaxf(rng, fmaxf(ga[e] - gm[e], gm[e] - gb[e]));
-      }
+      for (int e = 0; e < 4; ++e) vv[e] = kj[e] * ex2(g0[e] - gj[e]);
+      put_quad<M>(ra, p, vv);
     }
-    rng = fmaxf(rng, __shfl_xor(rng, 16));
-    rng = fmaxf(rng, __shfl_xor(rng, 32));
-    const uint64_t okb = __ballot(rng <= kFastRange);  // bit l16 (lanes 0..15)
-    if ((okb & 0x1ull) == 0x1ull) lstar = 0;
-    else if ((okb & 0x6ull) == 0x6ull) lstar = 1;
-    else if ((okb & 0x78ull) == 0x78ull) lstar = 2;
-    else if ((okb & 0x7F80ull) == 0x7F80ull) lstar = 3;
-    else need_diag = true;
+    f32x4 xa = zero4(), xp = zero4(), xt = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS_K; ++ks) {
+      xa = M::mma(ra[ks], lkf[ks], xa);
+      xp = M::mma(ra[ks], lqf[ks], xp);
+      if constexpr (BWD) xt = M::mma(lqf[ks], ra[ks], xt);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int jr = 4 * g + e;
+      dA[e] = (il > jr) ? xa[e] : 0.f;
+      dP[e] = (il >= jr) ? xp[e] : 0.f;
+      dPT[e] = (jr >= l16) ? xt[e] : 0.f;  // P tile: row i = 4g + e, column j = l16
+    }
   }
-  for (int lev = 0; lev <= lstar; ++lev) {
+  for (int lev = 0; !mid && lev <= lstar; ++lev) {
     const int S = 16 >> lev;
     const bool final_pass = (lev == lstar) && !need_diag;
     const int mj = 16 * I + (jl / S) * S + S / 2;  // reference of row j
@@ -429,7 +495,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
       }
     }
   }
-  if (need_diag) {
+  if (!mid && need_diag) {
     // i == j: P_ii = q~_i . k_i (no decay)
     F ra[KS_K], lq[KS_K];
 #pragma unroll

@@ -106,6 +106,13 @@ __device__ __forceinline__ float softplus_f32(float x) {
 // one of the gate kernel, so fused and two-step results agree bit for bit.
 enum GateMode : int { kGateLog2 = 0, kGateLog = 1, kGateRaw = 2 };
 
+// Summation order of the chunk-local cumsum (shared by the gate kernel and the
+// fused-gate chunk kernel, so both round identically): inside a chunk, tokens
+// form blocks of kGateBlock from the chunk's first token; token t at position
+// m of block b gets (C_b + P_m) * log2(e), where P_m sums the block's tokens
+// 0..m in order and C_b sums the totals of blocks 0..b-1 in order (C_0 = 0).
+constexpr int kGateBlock = 8;
+
 __device__ __forceinline__ float gate_head_scale(int mode, const float* A_log, int hv) {
   return (mode == kGateRaw && A_log) ? expf(A_log[hv]) : 1.f;
 }

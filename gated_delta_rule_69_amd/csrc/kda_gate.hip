@@ -10,7 +10,8 @@
 // floats of a token row (HV*K floats) and walks TILE tokens in order, so a
 // wave reads 64*VEC*4 contiguous bytes per token. Chunks tile each sequence
 // from its own first token, so a tile may start inside a chunk: the thread
-// then first sums the chunk's earlier tokens (at most chunk-1 of them).
+// then first sums the chunk's earlier tokens (at most chunk-1 of them). The
+// sums follow the blocked order of kGateBlock.
 #include "kda_common.h"
 
 namespace kda {
@@ -74,9 +75,19 @@ gate_cumsum_kernel(const float* __restrict__ in, int is_raw, const float* __rest
 #pragma unroll
     for (int e = 0; e < VEC; ++e) x[e] = gate_nat(x[e], is_raw ? kGateRaw : kGateLog, scale[e]);
   };
-  float acc[VEC];
+  // blocked running sum (see kGateBlock): carry C of finished blocks, P of
+  // the current block
+  float C[VEC], P[VEC];
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  for (int e = 0; e < VEC; ++e) C[e] = P[e] = 0.f;
+  auto accumulate = [&](int64_t pos, const float* g) {
+    const bool fresh = pos == 0, bstart = (pos % kGateBlock) == 0;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      C[e] = fresh ? 0.f : (bstart ? C[e] + P[e] : C[e]);
+      P[e] = (bstart ? 0.f : P[e]) + g[e];
+    }
+  };
   // carry-in: the tile starts inside a chunk that began earlier
   if (chunk > 1) {
     const int64_t cs = s_cstart[0];
@@ -85,8 +96,7 @@ gate_cumsum_kernel(const float* __restrict__ in, int is_raw, const float* __rest
         float g[VEC];
         load(t, g);
         act(g);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += g[e];
+        accumulate(t - cs, g);
       }
     }
   }
@@ -106,13 +116,10 @@ gate_cumsum_kernel(const float* __restrict__ in, int is_raw, const float* __rest
       act(g[b]);
       const int64_t t = t_a + i0 + b;
       const int64_t cs = s_cstart[i0 + b];
-      const bool fresh = cs == t;
+      accumulate(cs >= 0 ? t - cs : 0, g[b]);
       float r[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        acc[e] = (fresh ? 0.f : acc[e]) + g[b][e];
-        r[e] = acc[e] * kLog2e;
-      }
+      for (int e = 0; e < VEC; ++e) r[e] = (C[e] + P[e]) * kLog2e;
       if (cs >= 0) {
         float* p = out + t * row + f0;
         if constexpr (VEC == 4) {

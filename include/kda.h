@@ -91,6 +91,10 @@ const char* kda_status_string(kda_status s);
  *            per-token log2 decay consumed by kda_recurrent_fwd; chunk_size
  *            == 64 gives the input of kda_chunk_fwd. gate_out may equal gate_in
  *            only when chunk_size == 1 (else KDA_ERR_ALIAS).
+ *            Summation order (FP32): within a chunk, blocks of 8 tokens from
+ *            the chunk's first token; a token's sum is (C + P) where P adds
+ *            its block's tokens up to it in order and C adds the earlier
+ *            blocks' totals in order.
  *   Supports chunk_size in [1, 64] (ordinarily 1 or 64), any K, HV.
  */
 kda_status kda_gate_cumsum(const kda_dims* dims, const float* gate_in, int32_t gate_in_is_raw,
