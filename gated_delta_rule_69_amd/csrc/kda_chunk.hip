@@ -94,16 +94,26 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
   // the grid still has a workgroup for every compute unit.
   const int64_t chains = (int64_t)d.N * d.HV;
   const int bv = scan_block_v(chains, V);
+  // 4 waves per workgroup (8, with half the tiles per wave, measured slower:
+  // more LDS traffic and wider barriers for the same chain latency)
   auto launch_scan = [&](auto bvc) {
     constexpr int BVC = decltype(bvc)::value;
-    hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, false>), dim3((unsigned)chains, V / BVC),
+    hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, false, 4>), dim3((unsigned)chains, V / BVC),
                        dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL,
                        (const int*)ws_int, cu, h0, d.N, d.T, d.HV, write_final, (T*)o, ht,
                        (T*)nullptr);
   };
-  if (bv >= 64) launch_scan(std::integral_constant<int, 64>());
-  else if (bv == 32) launch_scan(std::integral_constant<int, 32>());
-  else launch_scan(std::integral_constant<int, 16>());
+  // FP32 with K = 128 stays at 32 columns: the 64-column tile set does not
+  // fit the register file
+  constexpr bool kWide = !(sizeof(T) == 4 && K == 128);
+  if (bv >= 64) {
+    if constexpr (kWide) launch_scan(std::integral_constant<int, 64>());
+    else launch_scan(std::integral_constant<int, 32>());
+  } else if (bv == 32) {
+    launch_scan(std::integral_constant<int, 32>());
+  } else {
+    launch_scan(std::integral_constant<int, 16>());
+  }
   return hipGetLastError();
 }
 

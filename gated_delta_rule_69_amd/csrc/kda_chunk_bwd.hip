@@ -1007,7 +1007,7 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
   }
   const int64_t chains = (int64_t)d.N * d.HV;
   // forward recurrence keeping S0 and Delta (no outputs)
-  hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, 32, true>), dim3((unsigned)chains, V / 32), dim3(kThreads),
+  hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, 32, true, 4>), dim3((unsigned)chains, V / 32), dim3(kThreads),
                      0, s, (const T*)ws_T, (const float*)ws_GL, (const int*)ws_int, cu, h0, d.N, d.T,
                      d.HV, 0, (T*)nullptr, (float*)nullptr, ws_B);
   if ((e = hipGetLastError()) != hipSuccess) return e;

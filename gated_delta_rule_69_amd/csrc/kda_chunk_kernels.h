@@ -905,8 +905,13 @@ struct Raw4<float> {
 
 // KEEP: also store every chunk's start state S0 and Delta into ws_B (the
 // backward pass reuses them); the forward instantiation has none of it.
-template <typename T, int K, int V, int BV, bool KEEP>
-__global__ void __launch_bounds__(kThreads)
+// NW waves per workgroup (4 or 8). Work of one chunk: the Delta and output
+// tiles (token tile x value tile) are split over the waves, NW / 4 waves per
+// token tile; the state tiles (channel tile x value tile) by channel tile.
+// With 8 waves every SIMD holds two waves of the chain, which hides part of
+// the LDS, matrix-core and barrier latency of the sequential recurrence.
+template <typename T, int K, int V, int BV, bool KEEP, int NW>
+__global__ void __launch_bounds__(NW * 64)
 chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
                   const int* __restrict__ ws_int, const int32_t* __restrict__ cu,
                   const float* h0, int N, int T_, int HV, int write_final, T* __restrict__ o,
@@ -918,15 +923,21 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
   typedef typename R4::type raw4;
   constexpr int KS_K = K / M::KSTEP;
   constexpr int KS_C = kC / M::KSTEP;
-  constexpr int RTW = K / 64;   // state row tiles per wave
-  constexpr int CTB = BV / 16;  // column tiles per block
-  static_assert(RTW >= 1 && CTB >= 1, "tile shape");
+  constexpr int NTH = NW * 64;
+  constexpr int NTT = kC / 16;       // token tiles
+  constexpr int WPT = NW / NTT;      // waves per token tile
+  constexpr int RTW = K / 16 / NW;   // state row (channel) tiles per wave
+  constexpr int CTB = BV / 16;       // column tiles per block
+  constexpr int CPW = CTB / WPT;     // column tiles per wave for Delta and the output
+  static_assert(RTW >= 1 && CTB >= 1 && CPW >= 1 && CTB % WPT == 0 && NW % NTT == 0, "tile shape");
 
   __shared__ F sS[2][KS_K][CTB][64];  // S as B fragments (contraction over channels), 2 buffers
   __shared__ F sD[2][KS_C][CTB][64];  // Delta as B fragments (contraction over tokens), 2 buffers
 
   const int n = blockIdx.x / HV, hv = blockIdx.x % HV, vb = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  // token tile and first value tile of this wave's Delta / output tiles
+  const int tt = wave % NTT, ct0 = WPT == 1 ? 0 : (wave / NTT) * CPW;
   int64_t bos;
   int len;
   seq_range(cu, n, T_, &bos, &len);
@@ -944,7 +955,7 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
 
   if (len == 0) {
     if (!write_final || (h0 == ht && h0 != nullptr)) return;
-    for (int e = tid; e < K * BV; e += kThreads) {
+    for (int e = tid; e < K * BV; e += NTH) {
       const int r = e / BV, c = col_base + e % BV;
       const size_t off = st_base + (size_t)r * V + c;
       uint32_t bits = h0 ? reinterpret_cast<const uint32_t*>(h0)[off] : 0u;
@@ -956,7 +967,7 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
   // per-chunk operands of this wave, loaded one chunk ahead
   struct Ops {
     F w[KS_K], qg[KS_K], p[KS_C], kh[RTW][KS_C];
-    raw4 u[CTB];
+    raw4 u[CPW];
     float4 gl[RTW];
   };
   auto load_ops = [&](int cj, Ops& op) {
@@ -969,11 +980,11 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     const T* wsU = wsW + WsL::W + WsL::QG + WsL::KH + WsL::P;
 #pragma unroll
     for (int ks = 0; ks < KS_K; ++ks) {
-      op.w[ks] = fW[((size_t)wave * KS_K + ks) * 64 + lane];
-      op.qg[ks] = fQG[((size_t)wave * KS_K + ks) * 64 + lane];
+      op.w[ks] = fW[((size_t)tt * KS_K + ks) * 64 + lane];
+      op.qg[ks] = fQG[((size_t)tt * KS_K + ks) * 64 + lane];
     }
 #pragma unroll
-    for (int ks = 0; ks < KS_C; ++ks) op.p[ks] = fP[((size_t)wave * KS_C + ks) * 64 + lane];
+    for (int ks = 0; ks < KS_C; ++ks) op.p[ks] = fP[((size_t)tt * KS_C + ks) * 64 + lane];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
 #pragma unroll
@@ -982,9 +993,9 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
       op.gl[rt] = *reinterpret_cast<const float4*>(ws_GL + ch * K + 16 * (RTW * wave + rt) + 4 * g);
     }
 #pragma unroll
-    for (int ct = 0; ct < CTB; ++ct) {
-      const int vt = (col_base >> 4) + ct;
-      op.u[ct] = *reinterpret_cast<const raw4*>(wsU + (((size_t)wave * (V / 16) + vt) * 64 + lane) * 4);
+    for (int cc = 0; cc < CPW; ++cc) {
+      const int vt = (col_base >> 4) + ct0 + cc;
+      op.u[cc] = *reinterpret_cast<const raw4*>(wsU + (((size_t)tt * (V / 16) + vt) * 64 + lane) * 4);
     }
   };
 
@@ -1002,52 +1013,66 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
       }
     }
 
-  // Output rows of token tile `wave` of a chunk whose S0 and Delta sit in LDS
+  // Output rows of token tile tt of a chunk whose S0 and Delta sit in LDS
   // buffer `buf`: O = (Q~ Gamma) S0 + P Delta, formed transposed
   // (O^T = S0^T (Q~ Gamma)^T + Delta^T P^T): the B fragments of S0 and Delta are
   // the A fragments of their transposes and vice versa, and the O^T
   // accumulator gives each lane 4 consecutive value columns of one token,
   // written as one 8- or 16-byte store. It runs one chunk late, next to the
   // following chunk's W S products, so it stays off the recurrence's path.
+  // What the deferred output needs is kept in registers: Q~ Gamma and P of
+  // the chunk and, for bf16 with up to 32 value columns (CACHE), the S0 /
+  // Delta fragments its step already read from LDS; otherwise they would not
+  // fit the register file and are read again from the chunk's LDS buffers
+  // (intact until the step after next).
+  constexpr bool CACHE = sizeof(T) == 2 && CTB <= 2;
   struct OutOps {
     F qg[KS_K], p[KS_C];
+    F sf[CACHE ? KS_K : 1][CACHE ? CPW : 1];  // S0 fragments (value tiles ct0..)
+    F df[CACHE ? KS_C : 1][CACHE ? CPW : 1];  // Delta fragments (value tiles ct0..)
   };
   auto output = [&](const OutOps& op, const int cj, const int buf) __attribute__((always_inline)) {
     const int cidx = cj - cbeg;
     const int64_t t0 = bos + (int64_t)cidx * kC;
     const int L = min(kC, len - cidx * kC);
-    f32x4 OT[CTB];
+    f32x4 OT[CPW];
 #pragma unroll
-    for (int ct = 0; ct < CTB; ++ct) OT[ct] = zero4();
+    for (int cc = 0; cc < CPW; ++cc) OT[cc] = zero4();
 #pragma unroll
     for (int ks = 0; ks < KS_K; ++ks)
 #pragma unroll
-      for (int ct = 0; ct < CTB; ++ct) OT[ct] = M::mma(sS[buf][ks][ct][lane], op.qg[ks], OT[ct]);
+      for (int cc = 0; cc < CPW; ++cc) {
+        if constexpr (CACHE) OT[cc] = M::mma(op.sf[ks][cc], op.qg[ks], OT[cc]);
+        else OT[cc] = M::mma(sS[buf][ks][ct0 + cc][lane], op.qg[ks], OT[cc]);
+      }
 #pragma unroll
     for (int ks = 0; ks < KS_C; ++ks)
 #pragma unroll
-      for (int ct = 0; ct < CTB; ++ct) OT[ct] = M::mma(sD[buf][ks][ct][lane], op.p[ks], OT[ct]);
-    const int i = 16 * wave + l16;
+      for (int cc = 0; cc < CPW; ++cc) {
+        if constexpr (CACHE) OT[cc] = M::mma(op.df[ks][cc], op.p[ks], OT[cc]);
+        else OT[cc] = M::mma(sD[buf][ks][ct0 + cc][lane], op.p[ks], OT[cc]);
+      }
+    const int i = 16 * tt + l16;
     if (i < L && o) {
-      T* orow = o + ((t0 + i) * HV + hv) * V + col_base + 4 * g;
+      T* orow = o + ((t0 + i) * HV + hv) * V + col_base + 16 * ct0 + 4 * g;
 #pragma unroll
-      for (int ct = 0; ct < CTB; ++ct) {
+      for (int cc = 0; cc < CPW; ++cc) {
         if constexpr (sizeof(T) == 2) {
           bf16x4 x;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = (bf16)OT[ct][e];
-          *reinterpret_cast<bf16x4*>(orow + 16 * ct) = x;
+          for (int e = 0; e < 4; ++e) x[e] = (bf16)OT[cc][e];
+          *reinterpret_cast<bf16x4*>(orow + 16 * cc) = x;
         } else {
-          *reinterpret_cast<float4*>(orow + 16 * ct) = make_float4(OT[ct][0], OT[ct][1], OT[ct][2], OT[ct][3]);
+          *reinterpret_cast<float4*>(orow + 16 * cc) = make_float4(OT[cc][0], OT[cc][1], OT[cc][2], OT[cc][3]);
         }
       }
     }
   };
-  OutOps prev;  // Q~ Gamma and P of the previous chunk
-
   // one chunk of the recurrence with operands `cur`, LDS buffer `buf`; the
-  // previous chunk's output is formed after the first barrier
-  auto step = [&](const Ops& cur, const int cj, const int buf) __attribute__((always_inline)) {
+  // previous chunk's output (registers `prv`) is formed after the first
+  // barrier, and this chunk's output registers are collected in `mine`
+  auto step = [&](const Ops& cur, const int cj, const int buf, OutOps& mine,
+                  const OutOps& prv) __attribute__((always_inline)) {
     const int cidx = cj - cbeg;
     const int64_t t0 = bos + (int64_t)cidx * kC;
     const int L = min(kC, len - cidx * kC);
@@ -1087,50 +1112,74 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     }
     __syncthreads();
 
-    if (cj > cbeg) output(prev, cj - 1, buf ^ 1);
-    // (2) Delta = U - W S for token tile `wave`
-    f32x4 D[CTB];
+    if (cj > cbeg) output(prv, cj - 1, buf ^ 1);
+    // (2) Delta = U - W S for token tile tt, value tiles ct0..ct0+CPW-1
+    f32x4 D[CPW];
     {
-      f32x4 ws_[CTB];
+      f32x4 ws_[CPW];
 #pragma unroll
-      for (int ct = 0; ct < CTB; ++ct) ws_[ct] = zero4();
+      for (int cc = 0; cc < CPW; ++cc) ws_[cc] = zero4();
 #pragma unroll
       for (int ks = 0; ks < KS_K; ++ks) {
 #pragma unroll
-        for (int ct = 0; ct < CTB; ++ct) ws_[ct] = M::mma(cur.w[ks], sS[buf][ks][ct][lane], ws_[ct]);
+        for (int cc = 0; cc < CPW; ++cc) {
+          const F sfr = sS[buf][ks][ct0 + cc][lane];
+          if constexpr (CACHE) mine.sf[ks][cc] = sfr;
+          ws_[cc] = M::mma(cur.w[ks], sfr, ws_[cc]);
+        }
       }
 #pragma unroll
-      for (int ct = 0; ct < CTB; ++ct)
+      for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) D[ct][e] = R4::get(cur.u[ct], e) - ws_[ct][e];
+        for (int e = 0; e < 4; ++e) D[cc][e] = R4::get(cur.u[cc], e) - ws_[cc][e];
     }
     if constexpr (KEEP) {  // backward support: keep Delta
       T* dl = ws_B + ((size_t)cj * HV + hv) * WsB<T, K, V>::elems + WsB<T, K, V>::oDL;
 #pragma unroll
-      for (int ct = 0; ct < CTB; ++ct)
+      for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          dl[(size_t)(16 * wave + 4 * g + e) * V + col_base + 16 * ct + l16] = from_f32<T>(D[ct][e]);
+          dl[(size_t)(16 * tt + 4 * g + e) * V + col_base + 16 * (ct0 + cc) + l16] = from_f32<T>(D[cc][e]);
     }
     // publish Delta as B fragments (contraction over tokens)
 #pragma unroll
-    for (int ct = 0; ct < CTB; ++ct) {
+    for (int cc = 0; cc < CPW; ++cc) {
+      const int ct = ct0 + cc;
       if constexpr (M::KSTEP == 32) {
-        const int ks = wave >> 1, half = wave & 1;
+        const int ks = tt >> 1, half = tt & 1;
         bf16x4 x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = (bf16)D[ct][e];
+        for (int e = 0; e < 4; ++e) x[e] = (bf16)D[cc][e];
         *(reinterpret_cast<bf16x4*>(&sD[buf][ks][ct][lane]) + half) = x;
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           F f;
-          M::set(f, 0, D[ct][e]);
-          sD[buf][4 * wave + e][ct][lane] = f;
+          M::set(f, 0, D[cc][e]);
+          sD[buf][4 * tt + e][ct][lane] = f;
         }
       }
     }
     __syncthreads();
+    F dall[KS_C][CTB];
+#pragma unroll
+    for (int ks = 0; ks < KS_C; ++ks) {
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct) dall[ks][ct] = sD[buf][ks][ct][lane];
+#pragma unroll
+      for (int cc = 0; cc < CPW; ++cc) {
+        if constexpr (!CACHE) {
+        } else if constexpr (WPT == 1) {
+          mine.df[ks][cc] = dall[ks][cc];
+        } else {  // select (no register-array indexing by a run-time value)
+          F x = dall[ks][0];
+#pragma unroll
+          for (int ct = 1; ct < CTB; ++ct)
+            if (ct == ct0 + cc) x = dall[ks][ct];
+          mine.df[ks][cc] = x;
+        }
+      }
+    }
 
     // (3) S = Diag(Gamma_last) S + Khat^T Delta for the wave's channel tiles
 #pragma unroll
@@ -1143,30 +1192,35 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
 #pragma unroll
       for (int ks = 0; ks < KS_C; ++ks)
 #pragma unroll
-        for (int ct = 0; ct < CTB; ++ct) S[rt][ct] = M::mma(cur.kh[rt][ks], sD[buf][ks][ct][lane], S[rt][ct]);
+        for (int ct = 0; ct < CTB; ++ct) S[rt][ct] = M::mma(cur.kh[rt][ks], dall[ks][ct], S[rt][ct]);
     }
 #pragma unroll
-    for (int ks = 0; ks < KS_K; ++ks) prev.qg[ks] = cur.qg[ks];
+    for (int ks = 0; ks < KS_K; ++ks) mine.qg[ks] = cur.qg[ks];
 #pragma unroll
-    for (int ks = 0; ks < KS_C; ++ks) prev.p[ks] = cur.p[ks];
+    for (int ks = 0; ks < KS_C; ++ks) mine.p[ks] = cur.p[ks];
   };
 
   // two operand sets, unrolled by two so the next chunk's loads stay in flight
-  Ops opA, opB;
-  load_ops(cbeg, opA);
   // (loads are unconditional -- the last chunk is simply fetched again -- so
-  // the number of loads in flight is the same on every path)
+  // the number of loads in flight is the same on every path); two output
+  // register sets alternate the same way
+  Ops opA, opB;
+  OutOps oA, oB;
+  load_ops(cbeg, opA);
   for (int cj = cbeg;; cj += 2) {
     load_ops(min(cj + 1, cend - 1), opB);
-    step(opA, cj, 0);
-    if (cj + 1 >= cend) break;
+    step(opA, cj, 0, oA, oB);
+    if (cj + 1 >= cend) {
+      output(oA, cj, 0);
+      break;
+    }
     load_ops(min(cj + 2, cend - 1), opA);
-    step(opB, cj + 1, 1);
-    if (cj + 2 >= cend) break;
+    step(opB, cj + 1, 1, oB, oA);
+    if (cj + 2 >= cend) {
+      output(oB, cj + 1, 1);
+      break;
+    }
   }
-  // the last chunk's output (its S0 and Delta buffers are intact: no barrier
-  // has been passed since they were published, and nothing writes them again)
-  output(prev, cend - 1, (cend - 1 - cbeg) & 1);
 
   if (write_final) {
 #pragma unroll
