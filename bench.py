@@ -37,6 +37,25 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
+# HBM bytes one kda_chunk_fwd_fused_gate call moves on the dense workload,
+# from rocprofv3 FETCH_SIZE / WRITE_SIZE (calibrated on a plain copy; see
+# profiles/hbm_traffic_dense_B4_T4096_and_decode.txt), valid for the chunk
+# kernel sources with this hash; any other source state reports null.
+TRAFFIC_SOURCES = ("gated_delta_rule_69_amd/csrc/kda_common.h",
+                   "gated_delta_rule_69_amd/csrc/kda_chunk_kernels.h",
+                   "gated_delta_rule_69_amd/csrc/kda_chunk.hip")
+TRAFFIC_SHA16 = "7a90f470f666c1b2"
+TRAFFIC_BYTES = 1020.7e6
+
+
+def measured_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return TRAFFIC_BYTES if h.hexdigest()[:16] == TRAFFIC_SHA16 else None
+
 
 def _args():
     p = argparse.ArgumentParser()
@@ -227,7 +246,7 @@ def main():
     gate_gbs = gb / (g_ms * 1e-3) / 1e9
     flops = chunk_fwd_flops(B, T, HV, K, V)
     roof = dict(bound="hbm", achieved=round(fused_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(fused_gbs / HBM_PEAK_GBS, 4), traffic=None,
+                frac=round(fused_gbs / HBM_PEAK_GBS, 4), traffic=measured_traffic(),
                 kernel="kda_chunk_fwd_fused_gate (chunk_intra_kernel + chunk_scan_kernel)",
                 algorithmic_bytes=cb, avg_ms=round(f_ms, 4),
                 mfma_tflops=round(flops / (f_ms * 1e-3) / 1e12, 2),
