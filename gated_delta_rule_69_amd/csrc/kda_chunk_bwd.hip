@@ -95,27 +95,66 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
         S[rt][ct][e] = dht ? dht[st_base + (size_t)c * V + col] : 0.f;
       }
 
-  int buf = 0;
-  for (int cj = cend - 1; cj >= cbeg; --cj) {
+  // per-chunk operands of this wave (and one 16-byte unit of the chunk's dO
+  // block per thread), loaded one chunk ahead
+  constexpr int UPR = BV * (int)sizeof(T) / 16;               // 16-byte units per dO row
+  constexpr int DOU = (kC * UPR + kThreads - 1) / kThreads;  // units per thread
+  struct ROps {
+    F khn[KS_K], pt[KS_C], qgt[RTW][KS_C], wt[RTW][KS_C];
+    float4 gl[RTW];
+    uint4 dob[DOU];
+  };
+  auto load_ops = [&](int cj, ROps& op) {
     const int cidx = cj - cbeg;
     const int64_t t0 = bos + (int64_t)cidx * kC;
     const int L = min(kC, len - cidx * kC);
     const size_t ch = (size_t)cj * HV + hv;
-    T* wb = ws_B + ch * WB::elems;
+    const T* wb = ws_B + ch * WB::elems;
     const F* fPT = reinterpret_cast<const F*>(wb + WB::oPT);
     const F* fKHn = reinterpret_cast<const F*>(wb + WB::oKHn);
     const F* fQGT = reinterpret_cast<const F*>(wb + WB::oQGT);
     const F* fWT = reinterpret_cast<const F*>(wb + WB::oWT);
-    const float* gl = ws_GL + ch * K;
+#pragma unroll
+    for (int ks = 0; ks < KS_K; ++ks) op.khn[ks] = fKHn[((size_t)wave * KS_K + ks) * 64 + lane];
+#pragma unroll
+    for (int ks = 0; ks < KS_C; ++ks) op.pt[ks] = fPT[((size_t)wave * KS_C + ks) * 64 + lane];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int tileK = RTW * wave + rt;
+#pragma unroll
+      for (int ks = 0; ks < KS_C; ++ks) {
+        op.qgt[rt][ks] = fQGT[((size_t)tileK * KS_C + ks) * 64 + lane];
+        op.wt[rt][ks] = fWT[((size_t)tileK * KS_C + ks) * 64 + lane];
+      }
+      op.gl[rt] = *reinterpret_cast<const float4*>(ws_GL + ch * K + 16 * tileK + 4 * g);
+    }
+    // dO rows >= L read row 0 of the chunk and are zeroed when staged
+#pragma unroll
+    for (int d = 0; d < DOU; ++d) {
+      const int u = tid + d * kThreads;
+      const int row = (u / UPR) < L ? (u / UPR) : 0, cu_ = u % UPR;
+      op.dob[d] = u < kC * UPR
+                      ? *reinterpret_cast<const uint4*>(dO + ((t0 + row) * HV + hv) * V + col_base + cu_ * (16 / sizeof(T)))
+                      : make_uint4(0, 0, 0, 0);
+    }
+  };
 
-    // stage the dO block (rows >= L are zero)
-    constexpr int UPR = BV * (int)sizeof(T) / 16;  // 16-byte units per row
-    for (int u = tid; u < kC * UPR; u += kThreads) {
-      const int row = u / UPR, cu_ = u % UPR;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (row < L)
-        x = *reinterpret_cast<const uint4*>(dO + ((t0 + row) * HV + hv) * V + col_base + cu_ * (16 / sizeof(T)));
-      *reinterpret_cast<uint4*>(sdO + row * DS + cu_ * (16 / sizeof(T))) = x;
+  auto step = [&](const ROps& op, const int cj, const int buf) __attribute__((always_inline)) {
+    const int cidx = cj - cbeg;
+    const int L = min(kC, len - cidx * kC);
+    const size_t ch = (size_t)cj * HV + hv;
+    T* wb = ws_B + ch * WB::elems;
+
+    // stage the dO block (rows >= L are zero); the previous chunk's reads of
+    // sdO finished before its last barrier
+#pragma unroll
+    for (int d = 0; d < DOU; ++d) {
+      const int u = tid + d * kThreads;
+      if (u < kC * UPR) {
+        const int row = u / UPR, cu_ = u % UPR;
+        *reinterpret_cast<uint4*>(sdO + row * DS + cu_ * (16 / sizeof(T))) =
+            row < L ? op.dob[d] : make_uint4(0, 0, 0, 0);
+      }
     }
     // keep dS1 of this chunk for the local kernel; publish it as B fragments
     T* dsl = wb + WB::oDS;
@@ -162,15 +201,13 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
     for (int ct = 0; ct < CTB; ++ct) D[ct] = zero4();
 #pragma unroll
     for (int ks = 0; ks < KS_K; ++ks) {
-      const F a = fKHn[((size_t)wave * KS_K + ks) * 64 + lane];
 #pragma unroll
-      for (int ct = 0; ct < CTB; ++ct) D[ct] = M::mma(a, sS[buf][ks][ct][lane], D[ct]);
+      for (int ct = 0; ct < CTB; ++ct) D[ct] = M::mma(op.khn[ks], sS[buf][ks][ct][lane], D[ct]);
     }
 #pragma unroll
     for (int ks = 0; ks < KS_C; ++ks) {
-      const F a = fPT[((size_t)wave * KS_C + ks) * 64 + lane];
 #pragma unroll
-      for (int ct = 0; ct < CTB; ++ct) D[ct] = M::mma(a, bdo[ct][ks], D[ct]);
+      for (int ct = 0; ct < CTB; ++ct) D[ct] = M::mma(op.pt[ks], bdo[ct][ks], D[ct]);
     }
     T* ddl = wb + WB::oDDL;
 #pragma unroll
@@ -197,9 +234,7 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
     // dS0 = Diag(gamma) dS1 + (Q~Gamma)^T dO - W^T dDelta
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-      const int tileK = RTW * wave + rt;
-      const float4 gv = *reinterpret_cast<const float4*>(gl + 16 * tileK + 4 * g);
-      const float ga[4] = {gv.x, gv.y, gv.z, gv.w};
+      const float ga[4] = {op.gl[rt].x, op.gl[rt].y, op.gl[rt].z, op.gl[rt].w};
       f32x4 neg[CTB];
 #pragma unroll
       for (int ct = 0; ct < CTB; ++ct) {
@@ -209,12 +244,10 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
       }
 #pragma unroll
       for (int ks = 0; ks < KS_C; ++ks) {
-        const F aq = fQGT[((size_t)tileK * KS_C + ks) * 64 + lane];
-        const F aw = fWT[((size_t)tileK * KS_C + ks) * 64 + lane];
 #pragma unroll
         for (int ct = 0; ct < CTB; ++ct) {
-          S[rt][ct] = M::mma(aq, bdo[ct][ks], S[rt][ct]);
-          neg[ct] = M::mma(aw, sD[ks][ct][lane], neg[ct]);
+          S[rt][ct] = M::mma(op.qgt[rt][ks], bdo[ct][ks], S[rt][ct]);
+          neg[ct] = M::mma(op.wt[rt][ks], sD[ks][ct][lane], neg[ct]);
         }
       }
 #pragma unroll
@@ -222,8 +255,20 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[rt][ct][e] -= neg[ct][e];
     }
-    buf ^= 1;
-    __syncthreads();  // sdO is restaged next chunk
+    __syncthreads();  // sdO and sD are written again next chunk
+  };
+
+  // chunks in reverse; two operand sets, unrolled by two (the first chunk is
+  // fetched again near the end so every path has the same loads in flight)
+  ROps opA, opB;
+  load_ops(cend - 1, opA);
+  for (int cj = cend - 1;; cj -= 2) {
+    load_ops(max(cj - 1, cbeg), opB);
+    step(opA, cj, 0);
+    if (cj - 1 < cbeg) break;
+    load_ops(max(cj - 2, cbeg), opA);
+    step(opB, cj - 1, 1);
+    if (cj - 2 < cbeg) break;
   }
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt)
@@ -1006,15 +1051,25 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t chains = (int64_t)d.N * d.HV;
-  // forward recurrence keeping S0 and Delta (no outputs)
-  hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, 32, true, 4>), dim3((unsigned)chains, V / 32), dim3(kThreads),
-                     0, s, (const T*)ws_T, (const float*)ws_GL, (const int*)ws_int, cu, h0, d.N, d.T,
-                     d.HV, 0, (T*)nullptr, (float*)nullptr, ws_B);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((chunk_rev_scan_kernel<T, K, V, 32>), dim3((unsigned)chains, V / 32),
-                     dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL, ws_B,
-                     (const int*)ws_int, cu, (const T*)dO, dht, d.N, d.T, d.HV, dh0);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // both recurrences are latency chains: 16-column V blocks when 32-column
+  // blocks would leave compute units without a workgroup
+  auto launch_scans = [&](auto bvc) -> hipError_t {
+    constexpr int BVC = decltype(bvc)::value;
+    // forward recurrence keeping S0 and Delta (no outputs)
+    hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, true, 4>), dim3((unsigned)chains, V / BVC),
+                       dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL, (const int*)ws_int,
+                       cu, h0, d.N, d.T, d.HV, 0, (T*)nullptr, (float*)nullptr, ws_B);
+    hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+    hipLaunchKernelGGL((chunk_rev_scan_kernel<T, K, V, BVC>), dim3((unsigned)chains, V / BVC),
+                       dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL, ws_B,
+                       (const int*)ws_int, cu, (const T*)dO, dht, d.N, d.T, d.HV, dh0);
+    return hipGetLastError();
+  };
+  constexpr int64_t kCUs = 256;
+  e = chains * (V / 32) < kCUs ? launch_scans(std::integral_constant<int, 16>())
+                                : launch_scans(std::integral_constant<int, 32>());
+  if (e != hipSuccess) return e;
   if (mc > 0) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_bwd_local_kernel<T, K, V>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)BwdLds<T, K, V>::total);
