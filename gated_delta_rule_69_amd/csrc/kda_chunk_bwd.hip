@@ -305,8 +305,8 @@ struct BwdLds {
   static constexpr size_t p2a = (size_t)K * CS * sizeof(T) + (size_t)kC * KSTR * sizeof(T);
   static constexpr size_t p2b = 4 * (size_t)kC * CS * sizeof(T);
   static constexpr size_t szX = cmax(cmax(p1, p15), cmax(p2a, p2b));
-  // small arrays: per-wave column sums [4][K], dgamma [K], row sums [C] x 3
-  static constexpr size_t szSmall = (4 * (size_t)K + K + 3 * (size_t)kC) * 4;
+  // small arrays: per-token-tile column sums [4][K], dgamma [K], row sums [C] x 3 parts x 2 halves
+  static constexpr size_t szSmall = (4 * (size_t)K + K + 6 * (size_t)kC) * 4;
   static constexpr size_t oG = 0, oK = oG + szG, oT = oK + szK, oQ = oT + szT, oX = oQ + szQ,
                           oSm = oX + szX, total = oSm + szSmall;
 };
@@ -355,8 +355,14 @@ __device__ __forceinline__ void put_quad_split(typename M::frag* hi, typename M:
   put_quad<M>(lo, p, l);
 }
 
+// One workgroup per (chunk, value head), 8 waves: wave w takes token tile
+// tt = w % 4 (16 rows of the chunk) and half hh = w / 4 of the column tiles
+// (channel tiles hh*NCT/2 .. of the C x K products, column tiles 2hh, 2hh+1 of
+// the C x C products), so every SIMD holds two waves of the workgroup.
+constexpr int kBwdThreads = 512;
+
 template <typename T, int K, int V>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kBwdThreads, 1)
 chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                        const float* __restrict__ gate, const T* __restrict__ beta,
                        const T* __restrict__ dO, const int32_t* __restrict__ cu,
@@ -369,11 +375,15 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   using F = typename M::frag;
   using Lds = BwdLds<T, K, V>;
   using WB = WsB<T, K, V>;
+  constexpr int NT = kBwdThreads;
   constexpr int KS_C = kC / M::KSTEP;
   constexpr int QK = K / 16, QC = kC / 16, NCT = K / 16;
+  constexpr int NCH = NCT / 2;  // channel tiles per wave
+  constexpr int JH = QC / 2;    // C x C column tiles per wave
   constexpr int GS = Lds::GS, KSTR = Lds::KSTR, TS = Lds::TS, CS = Lds::CS, BS = Lds::BS;
   constexpr int VB = Lds::VB;
   constexpr int EPU = 16 / (int)sizeof(T);
+  static_assert(VB / 16 == 2, "one value tile of a V block per half");
 
   extern __shared__ __align__(16) char smem[];
   float* sG = reinterpret_cast<float*>(smem + Lds::oG);
@@ -381,15 +391,17 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   float* sT = reinterpret_cast<float*>(smem + Lds::oT);
   T* sQ = reinterpret_cast<T*>(smem + Lds::oQ);
   char* X = smem + Lds::oX;
-  float* sColP = reinterpret_cast<float*>(smem + Lds::oSm);  // [4][K] per-wave column sums
+  float* sColP = reinterpret_cast<float*>(smem + Lds::oSm);  // [4][K] per-token-tile column sums
   float* sDgam = sColP + 4 * K;                               // [K]
-  float* sRow = sDgam + K;                                    // [3][C] row sums (dbeta parts)
+  float* sRow = sDgam + K;                                    // [3 parts][2 halves][C] dbeta parts
 
   const ChunkGeo geo = chunk_geo(blockIdx.x, cu, ws_int, N, T_);
   if (!geo.ok) return;
   const int hv = blockIdx.y;
   const int h = hv / (HV / H);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int tt = w & 3, hh = w >> 2;
+  const int cb = NCH * hh;  // first channel tile of the wave
   const int L = geo.L;
   const int64_t t0 = geo.t0;
   const size_t ch = (size_t)blockIdx.x * HV + hv;
@@ -397,52 +409,73 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   const float* wTm = ws_Bf + ch * WB::elems_f;
   const float* wAb = wTm + WB::TM;
 
-  // ---- stage G2, k, q, T; zero the small arrays
-  for (int f = tid; f < kC * K / 4; f += kThreads) {
-    const int row = f / (K / 4), c4 = f % (K / 4);
-    const int rr = row < L ? row : L - 1;
-    *reinterpret_cast<float4*>(sG + row * GS + 4 * c4) =
-        *reinterpret_cast<const float4*>(gate + ((t0 + rr) * HV + hv) * K + 4 * c4);
-  }
-  for (int f = tid; f < kC * K / EPU; f += kThreads) {
-    const int row = f / (K / EPU), cu_ = f % (K / EPU);
-    uint4 kx = make_uint4(0, 0, 0, 0), qx = kx;
-    if (row < L) {
-      kx = *reinterpret_cast<const uint4*>(k + ((t0 + row) * H + h) * K + EPU * cu_);
-      qx = *reinterpret_cast<const uint4*>(q + ((t0 + row) * H + h) * K + EPU * cu_);
+  // ---- stage G2, k, q, T (all loads of a thread issued before its stores); zero the small arrays
+  {
+    constexpr int NG = kC * K / 4 / NT, NKQ = kC * K / EPU / NT, NTm = kC * kC / 4 / NT;
+    static_assert(NG * NT == kC * K / 4 && NKQ * NT == kC * K / EPU && NTm * NT == kC * kC / 4, "stage");
+    float4 gx[NG], tx[NTm];
+    uint4 kx[NKQ], qx[NKQ];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int f = tid + i * NT, row = f / (K / 4), c4 = f % (K / 4);
+      const int rr = row < L ? row : L - 1;
+      gx[i] = *reinterpret_cast<const float4*>(gate + ((t0 + rr) * HV + hv) * K + 4 * c4);
     }
-    *reinterpret_cast<uint4*>(sK + row * KSTR + EPU * cu_) = kx;
-    *reinterpret_cast<uint4*>(sQ + row * KSTR + EPU * cu_) = qx;
+#pragma unroll
+    for (int i = 0; i < NKQ; ++i) {
+      const int f = tid + i * NT, row = f / (K / EPU), cu_ = f % (K / EPU);
+      const int rr = row < L ? row : 0;
+      kx[i] = *reinterpret_cast<const uint4*>(k + ((t0 + rr) * H + h) * K + EPU * cu_);
+      qx[i] = *reinterpret_cast<const uint4*>(q + ((t0 + rr) * H + h) * K + EPU * cu_);
+    }
+#pragma unroll
+    for (int i = 0; i < NTm; ++i) {
+      const int f = tid + i * NT, row = f / (kC / 4), c4 = f % (kC / 4);
+      tx[i] = *reinterpret_cast<const float4*>(wTm + row * kC + 4 * c4);
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int f = tid + i * NT, row = f / (K / 4), c4 = f % (K / 4);
+      *reinterpret_cast<float4*>(sG + row * GS + 4 * c4) = gx[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NKQ; ++i) {
+      const int f = tid + i * NT, row = f / (K / EPU), cu_ = f % (K / EPU);
+      uint4 kv = kx[i], qv = qx[i];
+      if (row >= L) kv = qv = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(sK + row * KSTR + EPU * cu_) = kv;
+      *reinterpret_cast<uint4*>(sQ + row * KSTR + EPU * cu_) = qv;
+    }
+#pragma unroll
+    for (int i = 0; i < NTm; ++i) {
+      const int f = tid + i * NT, row = f / (kC / 4), c4 = f % (kC / 4);
+      *reinterpret_cast<float4*>(sT + row * TS + 4 * c4) = tx[i];
+    }
   }
-  for (int f = tid; f < kC * kC / 4; f += kThreads) {
-    const int row = f / (kC / 4), c4 = f % (kC / 4);
-    *reinterpret_cast<float4*>(sT + row * TS + 4 * c4) = *reinterpret_cast<const float4*>(wTm + row * kC + 4 * c4);
-  }
-  for (int f = tid; f < 4 * K + K + 3 * kC; f += kThreads) sColP[f] = 0.f;
-  float bet[4];  // beta of the rows 16w + 4g + e this lane's accumulators cover
-  float betc;    // beta of row 16w + l16
+  for (int f = tid; f < 4 * K + K + 6 * kC; f += NT) sColP[f] = 0.f;
+  float bet[4];  // beta of the rows 16tt + 4g + e this lane's accumulators cover
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int i = 16 * w + 4 * g + e;
+    const int i = 16 * tt + 4 * g + e;
     bet[e] = i < L ? to_f32(beta[(t0 + i) * HV + hv]) : 0.f;
-  }
-  {
-    const int i = 16 * w + l16;
-    betc = i < L ? to_f32(beta[(t0 + i) * HV + hv]) : 0.f;
   }
   __syncthreads();
 
-  // persistent accumulators for token tile w: dq~, dk, dG (natural-log cumulative gate)
-  f32x4 aq[NCT], ak[NCT], aG[NCT];
+  // T^T fragments for rows j of token tile tt (T[i][j] down i), used three times
+  F aTt[KS_C];
+  frag_cols<M, float, QC>(aTt, sT, 16 * tt + l16, TS, g);
+
+  // persistent accumulators for token tile tt, channel tiles cb..: dq~, dk, dG
+  f32x4 aq[NCH], ak[NCH], aG[NCH];
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) aq[ct] = ak[ct] = aG[ct] = zero4();
+  for (int cc = 0; cc < NCH; ++cc) aq[cc] = ak[cc] = aG[cc] = zero4();
 
   // ---- phase 1: contractions over V, in blocks of VB columns
-  f32x4 dP[4], dQG[NCT], dW[NCT], dKH[NCT], dT1[4];
+  f32x4 dP[JH], dQG[NCH], dW[NCH], dKH[NCH], dT1[JH];
 #pragma unroll
-  for (int J = 0; J < 4; ++J) dP[J] = dT1[J] = zero4();
+  for (int jj = 0; jj < JH; ++jj) dP[jj] = dT1[jj] = zero4();
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) dQG[ct] = dW[ct] = dKH[ct] = zero4();
+  for (int cc = 0; cc < NCH; ++cc) dQG[cc] = dW[cc] = dKH[cc] = zero4();
   float dbU[4] = {0.f, 0.f, 0.f, 0.f};
   float dgam_acc = 0.f;  // thread-partial of rowsum(dS1 * S0) for channel tid % K
   {
@@ -453,87 +486,108 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     T* bS0 = bV + kC * BS;
     T* bdS = bS0 + K * BS;
     constexpr int UPR = VB / EPU;  // 16-byte units per block row
+    constexpr int NUC = (kC * UPR + NT - 1) / NT, NUK = (K * UPR + NT - 1) / NT;
     for (int vb = 0; vb < V / VB; ++vb) {
       const int c0 = vb * VB;
-      for (int u = tid; u < kC * UPR; u += kThreads) {
-        const int row = u / UPR, cu_ = u % UPR;
-        uint4 a = make_uint4(0, 0, 0, 0), b = a, c = a, d = a;
-        if (row < L) {
-          a = *reinterpret_cast<const uint4*>(dO + ((t0 + row) * HV + hv) * V + c0 + EPU * cu_);
-          d = *reinterpret_cast<const uint4*>(v + ((t0 + row) * HV + hv) * V + c0 + EPU * cu_);
+      {
+        uint4 a[NUC], b[NUC], c[NUC], d[NUC], s0[NUK], ds[NUK];
+#pragma unroll
+        for (int i = 0; i < NUC; ++i) {
+          const int u = tid + i * NT;
+          const int row = u / UPR < kC ? u / UPR : 0, cu_ = u % UPR;
+          const int rr = row < L ? row : 0;
+          a[i] = *reinterpret_cast<const uint4*>(dO + ((t0 + rr) * HV + hv) * V + c0 + EPU * cu_);
+          d[i] = *reinterpret_cast<const uint4*>(v + ((t0 + rr) * HV + hv) * V + c0 + EPU * cu_);
+          b[i] = *reinterpret_cast<const uint4*>(wb + WB::oDL + (size_t)row * V + c0 + EPU * cu_);
+          c[i] = *reinterpret_cast<const uint4*>(wb + WB::oDDL + (size_t)row * V + c0 + EPU * cu_);
         }
-        b = *reinterpret_cast<const uint4*>(wb + WB::oDL + (size_t)row * V + c0 + EPU * cu_);
-        c = *reinterpret_cast<const uint4*>(wb + WB::oDDL + (size_t)row * V + c0 + EPU * cu_);
-        *reinterpret_cast<uint4*>(bdO + row * BS + EPU * cu_) = a;
-        *reinterpret_cast<uint4*>(bDl + row * BS + EPU * cu_) = b;
-        *reinterpret_cast<uint4*>(bdDl + row * BS + EPU * cu_) = c;
-        *reinterpret_cast<uint4*>(bV + row * BS + EPU * cu_) = d;
-      }
-      for (int u = tid; u < K * UPR; u += kThreads) {
-        const int row = u / UPR, cu_ = u % UPR;
-        *reinterpret_cast<uint4*>(bS0 + row * BS + EPU * cu_) =
-            *reinterpret_cast<const uint4*>(wb + WB::oS0 + (size_t)row * V + c0 + EPU * cu_);
-        *reinterpret_cast<uint4*>(bdS + row * BS + EPU * cu_) =
-            *reinterpret_cast<const uint4*>(wb + WB::oDS + (size_t)row * V + c0 + EPU * cu_);
+#pragma unroll
+        for (int i = 0; i < NUK; ++i) {
+          const int u = tid + i * NT;
+          const int row = u / UPR < K ? u / UPR : 0, cu_ = u % UPR;
+          s0[i] = *reinterpret_cast<const uint4*>(wb + WB::oS0 + (size_t)row * V + c0 + EPU * cu_);
+          ds[i] = *reinterpret_cast<const uint4*>(wb + WB::oDS + (size_t)row * V + c0 + EPU * cu_);
+        }
+#pragma unroll
+        for (int i = 0; i < NUC; ++i) {
+          const int u = tid + i * NT;
+          if (u < kC * UPR) {
+            const int row = u / UPR, cu_ = u % UPR;
+            uint4 av = a[i], dv_ = d[i];
+            if (row >= L) av = dv_ = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(bdO + row * BS + EPU * cu_) = av;
+            *reinterpret_cast<uint4*>(bDl + row * BS + EPU * cu_) = b[i];
+            *reinterpret_cast<uint4*>(bdDl + row * BS + EPU * cu_) = c[i];
+            *reinterpret_cast<uint4*>(bV + row * BS + EPU * cu_) = dv_;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NUK; ++i) {
+          const int u = tid + i * NT;
+          if (u < K * UPR) {
+            const int row = u / UPR, cu_ = u % UPR;
+            *reinterpret_cast<uint4*>(bS0 + row * BS + EPU * cu_) = s0[i];
+            *reinterpret_cast<uint4*>(bdS + row * BS + EPU * cu_) = ds[i];
+          }
+        }
       }
       __syncthreads();
       constexpr int QV = VB / 16;
-      F aO[VB / M::KSTEP > 0 ? VB / M::KSTEP : 1], aDl[VB / M::KSTEP > 0 ? VB / M::KSTEP : 1],
-          adDl[VB / M::KSTEP > 0 ? VB / M::KSTEP : 1];
-      frag_rows<M, T, QV>(aO, bdO, 16 * w + l16, BS, g);
-      frag_rows<M, T, QV>(aDl, bDl, 16 * w + l16, BS, g);
-      frag_rows<M, T, QV>(adDl, bdDl, 16 * w + l16, BS, g);
       constexpr int KSV = VB / M::KSTEP;
+      F aO[KSV], aDl[KSV], adDl[KSV];
+      frag_rows<M, T, QV>(aO, bdO, 16 * tt + l16, BS, g);
+      frag_rows<M, T, QV>(aDl, bDl, 16 * tt + l16, BS, g);
+      frag_rows<M, T, QV>(adDl, bdDl, 16 * tt + l16, BS, g);
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
+      for (int jj = 0; jj < JH; ++jj) {
+        const int J = JH * hh + jj;
         F bD[KSV], bVv[KSV];
         frag_rows<M, T, QV>(bD, bDl, 16 * J + l16, BS, g);   // Delta^T: column j, contraction over v
         frag_rows<M, T, QV>(bVv, bV, 16 * J + l16, BS, g);   // v^T
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks) {
-          dP[J] = M::mma(aO[ks], bD[ks], dP[J]);
-          dT1[J] = M::mma(adDl[ks], bVv[ks], dT1[J]);
+          dP[jj] = M::mma(aO[ks], bD[ks], dP[jj]);
+          dT1[jj] = M::mma(adDl[ks], bVv[ks], dT1[jj]);
         }
       }
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
+      for (int cc = 0; cc < NCH; ++cc) {
+        const int ct = cb + cc;
         F bS[KSV], bdS_[KSV];
         frag_rows<M, T, QV>(bS, bS0, 16 * ct + l16, BS, g);
         frag_rows<M, T, QV>(bdS_, bdS, 16 * ct + l16, BS, g);
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks) {
-          dQG[ct] = M::mma(aO[ks], bS[ks], dQG[ct]);
-          dW[ct] = M::mma(adDl[ks], bS[ks], dW[ct]);
-          dKH[ct] = M::mma(aDl[ks], bdS_[ks], dKH[ct]);
+          dQG[cc] = M::mma(aO[ks], bS[ks], dQG[cc]);
+          dW[cc] = M::mma(adDl[ks], bS[ks], dW[cc]);
+          dKH[cc] = M::mma(aDl[ks], bdS_[ks], dKH[cc]);
         }
       }
-      // T^T dDelta for token tile w (rows j) -> dv, and the v part of dbeta
+      // T^T dDelta for token tile tt (rows j), value tile hh of the block -> dv, v part of dbeta
       {
-        F aTt[KS_C];
-        frag_cols<M, float, QC>(aTt, sT, 16 * w + l16, TS, g);  // T^T rows j: T[i][j] down i
+        const int vt = hh;
+        F bdd[KS_C];
+        frag_cols<M, T, QC>(bdd, bdDl, 16 * vt + l16, BS, g);  // dDelta down i
+        f32x4 acc = zero4();
 #pragma unroll
-        for (int vt = 0; vt < VB / 16; ++vt) {
-          F bdd[KS_C];
-          frag_cols<M, T, QC>(bdd, bdDl, 16 * vt + l16, BS, g);  // dDelta down i
-          f32x4 acc = zero4();
+        for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(aTt[ks], bdd[ks], acc);
 #pragma unroll
-          for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(aTt[ks], bdd[ks], acc);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = 16 * w + 4 * g + e;
-            const int col = c0 + 16 * vt + l16;
-            if (j < L) dv[((t0 + j) * HV + hv) * V + col] = from_f32<T>(bet[e] * acc[e]);
-            dbU[e] += to_f32(bV[j * BS + 16 * vt + l16]) * acc[e];
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * tt + 4 * g + e;
+          const int col = c0 + 16 * vt + l16;
+          if (j < L) dv[((t0 + j) * HV + hv) * V + col] = from_f32<T>(bet[e] * acc[e]);
+          dbU[e] += to_f32(bV[j * BS + 16 * vt + l16]) * acc[e];
         }
       }
       // dgamma partial: rowsum(dS1 * S0) over this block
       {
         const int c = tid % K;
-        const int parts = kThreads / K;  // threads per channel
+        constexpr int parts = NT / K;  // threads per channel
         const int pidx = tid / K;
         float s = 0.f;
-        for (int x = pidx; x < VB; x += parts) s += to_f32(bdS[c * BS + x]) * to_f32(bS0[c * BS + x]);
+#pragma unroll
+        for (int x = 0; x < VB / parts; ++x)
+          s += to_f32(bdS[c * BS + pidx + parts * x]) * to_f32(bS0[c * BS + pidx + parts * x]);
         dgam_acc += s;
       }
       __syncthreads();
@@ -546,74 +600,74 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     __syncthreads();
     if (tid < K) {
       float s = 0.f;
-      for (int p = tid; p < kThreads; p += K) s += sRed[p];
+#pragma unroll
+      for (int p = 0; p < NT / K; ++p) s += sRed[tid + p * K];
       sDgam[tid] = s;
     }
     __syncthreads();
   }
-  // dbeta (v part): rowsum over the 16 lanes of each lane group
+  // row sums over the 16 lanes of each lane group, into dbeta part `part`
+  auto row_part = [&](float x4[4], int part) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float x = dbU[e];
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
-    dbU[e] = x;
-  }
-  if (l16 == 0) {
+    for (int e = 0; e < 4; ++e) {
+      float x = x4[e];
+      x += __shfl_xor(x, 1);
+      x += __shfl_xor(x, 2);
+      x += __shfl_xor(x, 4);
+      x += __shfl_xor(x, 8);
+      x4[e] = x;
+    }
+    if (l16 == 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sRow[16 * w + 4 * g + e] = dbU[e];
-  }
+      for (int e = 0; e < 4; ++e) sRow[(2 * part + hh) * kC + 16 * tt + 4 * g + e] = x4[e];
+    }
+  };
+  row_part(dbU, 0);
 
-  // consume d(Q~Gamma) and dKhat; keep per-wave column sums of dKhat * Khat
-  float colp[NCT];
+  // consume d(Q~Gamma) and dKhat; keep per-token-tile column sums of dKhat * Khat
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int c = 16 * ct + l16;
+  for (int cc = 0; cc < NCH; ++cc) {
+    const int c = 16 * (cb + cc) + l16;
     const float glast = sG[(L - 1) * GS + c];
     float cs = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * g + e;
+      const int i = 16 * tt + 4 * g + e;
       const float gi = sG[i * GS + c];
       const float Gam = ex2(gi);
       const float qs = to_f32(sQ[i * KSTR + c]) * scale;
       const float kk = to_f32(sK[i * KSTR + c]);
       const float eL = ex2(glast - gi);
-      aq[ct][e] += dQG[ct][e] * Gam;
-      aG[ct][e] += dQG[ct][e] * qs * Gam;
-      ak[ct][e] += dKH[ct][e] * eL;
-      const float tt = dKH[ct][e] * kk * eL;
-      aG[ct][e] -= tt;
-      cs += tt;
+      aq[cc][e] += dQG[cc][e] * Gam;
+      aG[cc][e] += dQG[cc][e] * qs * Gam;
+      ak[cc][e] += dKH[cc][e] * eL;
+      const float t = dKH[cc][e] * kk * eL;
+      aG[cc][e] -= t;
+      cs += t;
     }
     cs += __shfl_xor(cs, 16);
     cs += __shfl_xor(cs, 32);
-    colp[ct] = cs;
-  }
-  if (g == 0) {
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) sColP[w * K + 16 * ct + l16] = colp[ct];
+    if (g == 0) sColP[tt * K + c] = cs;
+    __builtin_amdgcn_sched_barrier(0);
   }
   // dT1 = dDelta (b v)^T: scale column j by beta_j
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    const int j = 16 * J + l16;
+  for (int jj = 0; jj < JH; ++jj) {
+    const int j = 16 * (JH * hh + jj) + l16;
     const float bj = j < L ? to_f32(beta[(t0 + j) * HV + hv]) : 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dT1[J][e] *= bj;
+    for (int e = 0; e < 4; ++e) dT1[jj][e] *= bj;
   }
   // dP (lower, inclusive) into LDS, both orientations
   {
     T* sdP = reinterpret_cast<T*>(X);
     T* sdPT = sdP + kC * CS;
 #pragma unroll
-    for (int J = 0; J < 4; ++J)
+    for (int jj = 0; jj < JH; ++jj)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * w + 4 * g + e, j = 16 * J + l16;
-        const T x = from_f32<T>((j <= i) ? dP[J][e] : 0.f);
+        const int i = 16 * tt + 4 * g + e, j = 16 * (JH * hh + jj) + l16;
+        const T x = from_f32<T>((j <= i) ? dP[jj][e] : 0.f);
         sdP[i * CS + j] = x;
         sdPT[j * CS + i] = x;
       }
@@ -626,8 +680,8 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
 #pragma unroll
   for (int p = 0; p < QK; ++p) {
     float a0[4], a1[4];
-    lds4(sG + (16 * w) * GS + 16 * p + 4 * g, a0);
-    lds4(sG + (16 * w + 15) * GS + 16 * p + 4 * g, a1);
+    lds4(sG + (16 * tt) * GS + 16 * p + 4 * g, a0);
+    lds4(sG + (16 * tt + 15) * GS + 16 * p + 4 * g, a1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) rng = fmaxf(rng, a0[e] - a1[e]);
   }
@@ -635,16 +689,16 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   rng = fmaxf(rng, __shfl_xor(rng, 32));
   const bool fast = rng <= kFastRange;
 
-  // Z pattern: out(i, c) = sum_j Mm[i][j] Xs[j][c] 2^(G2_i - G2_j), rows i of tile w.
-  // Reference r = 16w: operands Xs_j 2^(G2_r - G2_j) (<= 1 for j < r; <= 2^112 on
+  // Z pattern: out(i, c) = sum_j Mm[i][j] Xs[j][c] 2^(G2_i - G2_j), rows i of tile tt.
+  // Reference r = 16tt: operands Xs_j 2^(G2_r - G2_j) (<= 1 for j < r; <= 2^112 on
   // the diagonal tile in the fast path), output times 2^(G2_i - G2_r) (<= 1).
-  auto zprod = [&](f32x4* out, const T* Mm, const T* Xs, float xscale) {
-    const int r = 16 * w;
+  auto zprod = [&](const T* Mm, const T* Xs, float xscale, auto&& consume) {
+    const int r = 16 * tt;
     F am[KS_C];
-    frag_rows<M, T, QC>(am, Mm, 16 * w + l16, CS, g);
+    frag_rows<M, T, QC>(am, Mm, 16 * tt + l16, CS, g);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int c = 16 * ct + l16;
+    for (int cc = 0; cc < NCH; ++cc) {
+      const int c = 16 * (cb + cc) + l16;
       const float gr = sG[r * GS + c];
       F bx[KS_C], bl[KS_C];
 #pragma unroll
@@ -664,28 +718,31 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
         acc = M::mma(am[ks], bx[ks], acc);
         if constexpr (M::KSTEP == 32) acc = M::mma(am[ks], bl[ks], acc);
       }
+      f32x4 z;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = r + 4 * g + e;
-        float z = acc[e] * ex2(sG[i * GS + c] - gr);
+        z[e] = acc[e] * ex2(sG[i * GS + c] - gr);
         if (!fast) {  // diagonal tile, exact elementwise
           for (int j = r; j <= i; ++j)
-            z += to_f32(Mm[i * CS + j]) * to_f32(Xs[j * KSTR + c]) * xscale * ex2(sG[i * GS + c] - sG[j * GS + c]);
+            z[e] += to_f32(Mm[i * CS + j]) * to_f32(Xs[j * KSTR + c]) * xscale * ex2(sG[i * GS + c] - sG[j * GS + c]);
         }
-        out[ct][e] = z;
       }
+      consume(cc, z);
+      // one channel tile at a time: hoisting the next tile's LDS reads evicts the accumulators
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Z' pattern: out(j, c) = sum_i MmT[j][i] Xs[i][c] 2^(G2_i - G2_j), rows j of tile w.
-  // Reference r = 16w + 15: operands Xs_i 2^(G2_i - G2_r) (<= 1 for i > r),
+  // Z' pattern: out(j, c) = sum_i MmT[j][i] Xs[i][c] 2^(G2_i - G2_j), rows j of tile tt.
+  // Reference r = 16tt + 15: operands Xs_i 2^(G2_i - G2_r) (<= 1 for i > r),
   // output times 2^(G2_r - G2_j) (<= 1).
-  auto zprodT = [&](f32x4* out, const T* MmT, const T* Xs, float xscale) {
-    const int r = 16 * w + 15;
+  auto zprodT = [&](const T* MmT, const T* Xs, float xscale, auto&& consume) {
+    const int r = 16 * tt + 15;
     F am[KS_C];
-    frag_rows<M, T, QC>(am, MmT, 16 * w + l16, CS, g);
+    frag_rows<M, T, QC>(am, MmT, 16 * tt + l16, CS, g);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int c = 16 * ct + l16;
+    for (int cc = 0; cc < NCH; ++cc) {
+      const int c = 16 * (cb + cc) + l16;
       const float gr = sG[r * GS + c];
       F bx[KS_C], bl[KS_C];
 #pragma unroll
@@ -705,41 +762,44 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
         acc = M::mma(am[ks], bx[ks], acc);
         if constexpr (M::KSTEP == 32) acc = M::mma(am[ks], bl[ks], acc);
       }
+      f32x4 z;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int j = 16 * w + 4 * g + e;
-        float z = acc[e] * ex2(gr - sG[j * GS + c]);
+        const int j = 16 * tt + 4 * g + e;
+        z[e] = acc[e] * ex2(gr - sG[j * GS + c]);
         if (!fast) {
           for (int i = j; i <= r; ++i)
-            z += to_f32(MmT[j * CS + i]) * to_f32(Xs[i * KSTR + c]) * xscale * ex2(sG[i * GS + c] - sG[j * GS + c]);
+            z[e] += to_f32(MmT[j * CS + i]) * to_f32(Xs[i * KSTR + c]) * xscale * ex2(sG[i * GS + c] - sG[j * GS + c]);
         }
-        out[ct][e] = z;
       }
+      consume(cc, z);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   {
     const T* sdP = reinterpret_cast<const T*>(X);
     const T* sdPT = sdP + kC * CS;
-    f32x4 z[NCT];
-    zprod(z, sdP, sK, 1.f);  // Y1
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    zprod(sdP, sK, 1.f, [&](int cc, const f32x4& z) {  // Y1; dq~ is then complete
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * w + 4 * g + e, c = 16 * ct + l16;
-        aq[ct][e] += z[ct][e];
-        aG[ct][e] += to_f32(sQ[i * KSTR + c]) * scale * z[ct][e];
+        const int i = 16 * tt + 4 * g + e, c = 16 * (cb + cc) + l16;
+        aG[cc][e] += to_f32(sQ[i * KSTR + c]) * scale * z[e];
+        if (i < L) {  // dq (per value head; summed over the GVA group later when HV > H)
+          const float dqv = (aq[cc][e] + z[e]) * scale;
+          if (dq_part) dq_part[((t0 + i) * HV + hv) * K + c] = dqv;
+          else dq_out[((t0 + i) * H + h) * K + c] = from_f32<T>(dqv);
+        }
       }
-    zprodT(z, sdPT, sQ, scale);  // Y2
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    });
+    zprodT(sdPT, sQ, scale, [&](int cc, const f32x4& z) {  // Y2
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int j = 16 * w + 4 * g + e, c = 16 * ct + l16;
-        ak[ct][e] += z[ct][e];
-        aG[ct][e] -= to_f32(sK[j * KSTR + c]) * z[ct][e];
+        const int j = 16 * tt + 4 * g + e, c = 16 * (cb + cc) + l16;
+        ak[cc][e] += z[e];
+        aG[cc][e] -= to_f32(sK[j * KSTR + c]) * z[e];
       }
+    });
   }
   __syncthreads();  // q, dP, dP^T dead
 
@@ -749,15 +809,17 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     T* sdWT = reinterpret_cast<T*>(X);            // [K][CS]
     T* sBKg = sdWT + K * CS;                      // [C][KSTR] b * k * Gamma
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int cc = 0; cc < NCH; ++cc)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * w + 4 * g + e, c = 16 * ct + l16;
-        const T x = from_f32<T>(-dW[ct][e]);
+        const int i = 16 * tt + 4 * g + e, c = 16 * (cb + cc) + l16;
+        const T x = from_f32<T>(-dW[cc][e]);
         sdW[i * KSTR + c] = x;
         sdWT[c * CS + i] = x;
       }
-    for (int f = tid; f < kC * K / 4; f += kThreads) {
+#pragma unroll
+    for (int it = 0; it < kC * K / 4 / NT; ++it) {
+      const int f = tid + it * NT;
       const int m = f / (K / 4), c4 = f % (K / 4);
       float km[4], gm[4];
       lds4(sK + m * KSTR + 4 * c4, km);
@@ -767,27 +829,26 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       for (int e = 0; e < 4; ++e) sBKg[m * KSTR + 4 * c4 + e] = from_f32<T>(bm * km[e] * ex2(gm[e]));
     }
     __syncthreads();
-    // dT = dT1 + dW (b Kg)^T, rows i of tile w
-    f32x4 dT[4];
+    // dT = dT1 + dW (b Kg)^T, rows i of tile tt, column tiles of the half
+    f32x4 dT[JH];
     {
       F adw[K / M::KSTEP];
-      frag_rows<M, T, QK>(adw, sdW, 16 * w + l16, KSTR, g);
+      frag_rows<M, T, QK>(adw, sdW, 16 * tt + l16, KSTR, g);
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
+      for (int jj = 0; jj < JH; ++jj) {
         F bk[K / M::KSTEP];
-        frag_rows<M, T, QK>(bk, sBKg, 16 * J + l16, KSTR, g);
-        dT[J] = dT1[J];
+        frag_rows<M, T, QK>(bk, sBKg, 16 * (JH * hh + jj) + l16, KSTR, g);
+        dT[jj] = dT1[jj];
 #pragma unroll
-        for (int ks = 0; ks < K / M::KSTEP; ++ks) dT[J] = M::mma(adw[ks], bk[ks], dT[J]);
+        for (int ks = 0; ks < K / M::KSTEP; ++ks) dT[jj] = M::mma(adw[ks], bk[ks], dT[jj]);
       }
     }
-    // T^T dW, rows j of tile w -> dKg = b_j (T^T dW)
+    // T^T dW, rows j of tile tt -> dKg = b_j (T^T dW)
     {
-      F aTt[KS_C];
-      frag_cols<M, float, QC>(aTt, sT, 16 * w + l16, TS, g);
       float dbw[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
+      for (int cc = 0; cc < NCH; ++cc) {
+        const int ct = cb + cc;
         F bw[KS_C];
         frag_rows<M, T, QC>(bw, sdWT, 16 * ct + l16, CS, g);
         f32x4 acc = zero4();
@@ -795,51 +856,38 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
         for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(aTt[ks], bw[ks], acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int j = 16 * w + 4 * g + e, c = 16 * ct + l16;
+          const int j = 16 * tt + 4 * g + e, c = 16 * ct + l16;
           const float Gam = ex2(sG[j * GS + c]);
           const float kg = to_f32(sK[j * KSTR + c]) * Gam;
           const float dkg = bet[e] * acc[e];
-          ak[ct][e] += dkg * Gam;
-          aG[ct][e] += dkg * kg;
+          ak[cc][e] += dkg * Gam;
+          aG[cc][e] += dkg * kg;
           dbw[e] += kg * acc[e];
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = dbw[e];
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
-        x += __shfl_xor(x, 4);
-        x += __shfl_xor(x, 8);
-        dbw[e] = x;
-      }
-      if (l16 == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sRow[kC + 16 * w + 4 * g + e] = dbw[e];
-      }
+      row_part(dbw, 1);
     }
     __syncthreads();  // dW, dW^T, b Kg dead
     T* sdTT = reinterpret_cast<T*>(X);  // dT transposed [j][i]
 #pragma unroll
-    for (int J = 0; J < 4; ++J)
+    for (int jj = 0; jj < JH; ++jj)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sdTT[(16 * J + l16) * CS + 16 * w + 4 * g + e] = from_f32<T>(dT[J][e]);
+      for (int e = 0; e < 4; ++e)
+        sdTT[(16 * (JH * hh + jj) + l16) * CS + 16 * tt + 4 * g + e] = from_f32<T>(dT[jj][e]);
     __syncthreads();
-    // Xm = T^T dT, rows a of tile w
+    // Xm = T^T dT, rows a of tile tt
     T* sXm = sdTT + kC * CS;
-    {
-      F aTt[KS_C];
-      frag_cols<M, float, QC>(aTt, sT, 16 * w + l16, TS, g);
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        F bt[KS_C];
-        frag_rows<M, T, QC>(bt, sdTT, 16 * J + l16, CS, g);
-        f32x4 acc = zero4();
+    for (int jj = 0; jj < JH; ++jj) {
+      const int J = JH * hh + jj;
+      F bt[KS_C];
+      frag_rows<M, T, QC>(bt, sdTT, 16 * J + l16, CS, g);
+      f32x4 acc = zero4();
 #pragma unroll
-        for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(aTt[ks], bt[ks], acc);
+      for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(aTt[ks], bt[ks], acc);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sXm[(16 * w + 4 * g + e) * CS + 16 * J + l16] = from_f32<T>(acc[e]);
-      }
+      for (int e = 0; e < 4; ++e) sXm[(16 * tt + 4 * g + e) * CS + 16 * J + l16] = from_f32<T>(acc[e]);
     }
     __syncthreads();
     // dA = -Xm T^T (strictly lower), dAbar = b dA; Abar part of dbeta
@@ -847,10 +895,11 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     T* sdAbT = sdAb + kC * CS;
     {
       F ax[KS_C];
-      frag_rows<M, T, QC>(ax, sXm, 16 * w + l16, CS, g);
+      frag_rows<M, T, QC>(ax, sXm, 16 * tt + l16, CS, g);
       float dba[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
+      for (int jj = 0; jj < JH; ++jj) {
+        const int J = JH * hh + jj;
         F bt[KS_C];
         frag_rows<M, float, QC>(bt, sT, 16 * J + l16, TS, g);  // T^T column c = T row c
         f32x4 acc = zero4();
@@ -858,7 +907,7 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
         for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(ax[ks], bt[ks], acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int a = 16 * w + 4 * g + e, c = 16 * J + l16;
+          const int a = 16 * tt + 4 * g + e, c = 16 * J + l16;
           const float da = (c < a) ? -acc[e] : 0.f;
           dba[e] += wAb[a * kC + c] * da;
           const T x = from_f32<T>(bet[e] * da);
@@ -866,73 +915,57 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
           sdAbT[c * CS + a] = x;
         }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = dba[e];
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
-        x += __shfl_xor(x, 4);
-        x += __shfl_xor(x, 8);
-        dba[e] = x;
-      }
-      if (l16 == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sRow[2 * kC + 16 * w + 4 * g + e] = dba[e];
-      }
+      row_part(dba, 2);
     }
     __syncthreads();
-    f32x4 z[NCT];
-    zprod(z, sdAb, sK, 1.f);  // X1
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    zprod(sdAb, sK, 1.f, [&](int cc, const f32x4& z) {  // X1
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * w + 4 * g + e, c = 16 * ct + l16;
-        ak[ct][e] += z[ct][e];
-        aG[ct][e] += to_f32(sK[i * KSTR + c]) * z[ct][e];
+        const int i = 16 * tt + 4 * g + e, c = 16 * (cb + cc) + l16;
+        ak[cc][e] += z[e];
+        aG[cc][e] += to_f32(sK[i * KSTR + c]) * z[e];
       }
-    zprodT(z, sdAbT, sK, 1.f);  // X2
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    });
+    zprodT(sdAbT, sK, 1.f, [&](int cc, const f32x4& z) {  // X2
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int j = 16 * w + 4 * g + e, c = 16 * ct + l16;
-        ak[ct][e] += z[ct][e];
-        aG[ct][e] -= to_f32(sK[j * KSTR + c]) * z[ct][e];
+        const int j = 16 * tt + 4 * g + e, c = 16 * (cb + cc) + l16;
+        ak[cc][e] += z[e];
+        aG[cc][e] -= to_f32(sK[j * KSTR + c]) * z[e];
       }
+    });
   }
 
   // ---- last row: colsum(dKhat * Khat) + dgamma * gamma; reverse cumsum; outputs
   __syncthreads();
   {
-    float* sTile = reinterpret_cast<float*>(X);  // per-wave column totals [4][K]
+    float* sTile = reinterpret_cast<float*>(X);  // per-token-tile column totals [4][K]
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int c = 16 * ct + l16;
+    for (int cc = 0; cc < NCH; ++cc) {
+      const int c = 16 * (cb + cc) + l16;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * w + 4 * g + e;
+        const int i = 16 * tt + 4 * g + e;
         if (i == L - 1) {
           const float cs = sColP[c] + sColP[K + c] + sColP[2 * K + c] + sColP[3 * K + c];
-          aG[ct][e] += cs + sDgam[c] * ex2(sG[(L - 1) * GS + c]);
+          aG[cc][e] += cs + sDgam[c] * ex2(sG[(L - 1) * GS + c]);
         }
       }
-      float tot = aG[ct][0] + aG[ct][1] + aG[ct][2] + aG[ct][3];
+      float tot = aG[cc][0] + aG[cc][1] + aG[cc][2] + aG[cc][3];
       tot += __shfl_xor(tot, 16);
       tot += __shfl_xor(tot, 32);
-      if (g == 0) sTile[w * K + c] = tot;
+      if (g == 0) sTile[tt * K + c] = tot;
     }
     __syncthreads();
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int c = 16 * ct + l16;
+    for (int cc = 0; cc < NCH; ++cc) {
+      const int c = 16 * (cb + cc) + l16;
       float later = 0.f;  // rows of the later tiles
-      for (int w2 = w + 1; w2 < 4; ++w2) later += sTile[w2 * K + c];
+      for (int t2 = tt + 1; t2 < 4; ++t2) later += sTile[t2 * K + c];
       // suffix sums inside the tile: rows 4g..4g+3 in lanes of group g
-      float s3 = aG[ct][3], s2 = s3 + aG[ct][2], s1 = s2 + aG[ct][1], s0 = s1 + aG[ct][0];
-      float grp = s0;  // total of this lane group's 4 rows
+      float s3 = aG[cc][3], s2 = s3 + aG[cc][2], s1 = s2 + aG[cc][1], s0 = s1 + aG[cc][0];
       float after = 0.f;
-      const float g1 = __shfl_xor(grp, 16), g2 = __shfl_xor(grp, 32), g3 = __shfl_xor(grp, 48);
+      const float g1 = __shfl_xor(s0, 16), g2 = __shfl_xor(s0, 32), g3 = __shfl_xor(s0, 48);
       // lane group g receives the totals of groups g^1, g^2, g^3; add those with a larger index
       if ((g ^ 1) > g) after += g1;
       if ((g ^ 2) > g) after += g2;
@@ -941,35 +974,29 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       const float sfx[4] = {s0 + base, s1 + base, s2 + base, s3 + base};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * w + 4 * g + e;
+        const int i = 16 * tt + 4 * g + e;
         if (i < L) dg[((t0 + i) * HV + hv) * K + c] = sfx[e];
       }
     }
   }
-  // dq, dk (per value head; summed over the GVA group later when HV > H), dbeta
+  // dk (per value head; summed over the GVA group later when HV > H), dbeta
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int c = 16 * ct + l16;
+  for (int cc = 0; cc < NCH; ++cc) {
+    const int c = 16 * (cb + cc) + l16;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * g + e;
+      const int i = 16 * tt + 4 * g + e;
       if (i >= L) continue;
-      const float dqv = aq[ct][e] * scale;
-      const float dkv = ak[ct][e];
-      if (dq_part) {
-        dq_part[((t0 + i) * HV + hv) * K + c] = dqv;
-        dk_part[((t0 + i) * HV + hv) * K + c] = dkv;
-      } else {
-        dq_out[((t0 + i) * H + h) * K + c] = from_f32<T>(dqv);
-        dk_out[((t0 + i) * H + h) * K + c] = from_f32<T>(dkv);
-      }
+      if (dq_part) dk_part[((t0 + i) * HV + hv) * K + c] = ak[cc][e];
+      else dk_out[((t0 + i) * H + h) * K + c] = from_f32<T>(ak[cc][e]);
     }
   }
   if (tid < kC && tid < L) {
-    const float db = sRow[tid] + sRow[kC + tid] + sRow[2 * kC + tid];
+    float db = 0.f;
+#pragma unroll
+    for (int p = 0; p < 6; ++p) db += sRow[p * kC + tid];
     dbeta[(t0 + tid) * HV + hv] = from_f32<T>(db);
   }
-  (void)betc;
 }
 
 // dq, dk of a qk head = sum over its HV/H value heads, in head order.
@@ -1076,7 +1103,7 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
     if (e != hipSuccess) return e;
     const size_t lds_local = BwdLds<T, K, V>::total;
     hipLaunchKernelGGL((chunk_bwd_local_kernel<T, K, V>), dim3((unsigned)mc, (unsigned)d.HV),
-                       dim3(kThreads), lds_local, s, (const T*)q, (const T*)k,
+                       dim3(kBwdThreads), lds_local, s, (const T*)q, (const T*)k,
                        (const T*)v, gate, (const T*)beta, (const T*)dO, cu, (const int*)ws_int,
                        (const T*)ws_B, (const float*)ws_Bf, d.N, d.T, d.H, d.HV, scale, (T*)dq,
                        (T*)dk, dq_part, dk_part, (T*)dv, dg, (T*)dbeta);
