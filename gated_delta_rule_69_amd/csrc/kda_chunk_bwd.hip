@@ -299,12 +299,13 @@ struct BwdLds {
   static constexpr size_t szQ = (size_t)kC * KSTR * sizeof(T);
   // phase 1: dO, Delta, dDelta, v blocks [C][BS]; S0, dS1 blocks [K][BS]
   static constexpr size_t p1 = (4 * (size_t)kC + 2 * (size_t)K) * BS * sizeof(T);
-  // phase 1.5: dP, dP^T [C][CS]
-  static constexpr size_t p15 = 2 * (size_t)kC * CS * sizeof(T);
-  // phase 2: dW^T [K][CS] + b*Kg [C][KSTR]; later dT^T, Xm, dAbar, dAbar^T [C][CS]
-  static constexpr size_t p2a = (size_t)K * CS * sizeof(T) + (size_t)kC * KSTR * sizeof(T);
-  static constexpr size_t p2b = 4 * (size_t)kC * CS * sizeof(T);
-  static constexpr size_t szX = cmax(cmax(p1, p15), cmax(p2a, p2b));
+  // from the end of phase 1 to the end: dP, dP^T [C][CS]; behind them the phase-2 area
+  static constexpr size_t pP = 2 * (size_t)kC * CS * sizeof(T);
+  // phase 2: dW^T [K][CS] + b*Kg [C][KSTR] + dW [C][KSTR]; later three [C][CS] slots:
+  // dT^T then dAbar, Xm, dAbar^T
+  static constexpr size_t p2a = (size_t)K * CS * sizeof(T) + 2 * (size_t)kC * KSTR * sizeof(T);
+  static constexpr size_t p2b = 3 * (size_t)kC * CS * sizeof(T);
+  static constexpr size_t szX = cmax(p1, pP + cmax(p2a, p2b));
   // small arrays: per-token-tile column sums [4][K], dgamma [K], row sums [C] x 3 parts x 2 halves
   static constexpr size_t szSmall = (4 * (size_t)K + K + 6 * (size_t)kC) * 4;
   static constexpr size_t oG = 0, oK = oG + szG, oT = oK + szK, oQ = oT + szT, oX = oQ + szQ,
@@ -355,6 +356,10 @@ __device__ __forceinline__ void put_quad_split(typename M::frag* hi, typename M:
   put_quad<M>(lo, p, l);
 }
 
+// Materialise a running sum where it stands: keeps the compiler from sinking
+// an accumulation chain towards its last use with every addend kept alive.
+__device__ __forceinline__ void pin(f32x4& x) { asm volatile("" : "+v"(x)); }
+
 // One workgroup per (chunk, value head), 8 waves: wave w takes token tile
 // tt = w % 4 (16 rows of the chunk) and half hh = w / 4 of the column tiles
 // (channel tiles hh*NCT/2 .. of the C x K products, column tiles 2hh, 2hh+1 of
@@ -391,6 +396,8 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   float* sT = reinterpret_cast<float*>(smem + Lds::oT);
   T* sQ = reinterpret_cast<T*>(smem + Lds::oQ);
   char* X = smem + Lds::oX;
+  T* XT = reinterpret_cast<T*>(X);  // dP, dP^T from the end of phase 1 on
+  T* XP = XT + 2 * kC * CS;         // phase-2 area behind them
   float* sColP = reinterpret_cast<float*>(smem + Lds::oSm);  // [4][K] per-token-tile column sums
   float* sDgam = sColP + 4 * K;                               // [K]
   float* sRow = sDgam + K;                                    // [3 parts][2 halves][C] dbeta parts
@@ -464,11 +471,6 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   // T^T fragments for rows j of token tile tt (T[i][j] down i), used three times
   F aTt[KS_C];
   frag_cols<M, float, QC>(aTt, sT, 16 * tt + l16, TS, g);
-
-  // persistent accumulators for token tile tt, channel tiles cb..: dq~, dk, dG
-  f32x4 aq[NCH], ak[NCH], aG[NCH];
-#pragma unroll
-  for (int cc = 0; cc < NCH; ++cc) aq[cc] = ak[cc] = aG[cc] = zero4();
 
   // ---- phase 1: contractions over V, in blocks of VB columns
   f32x4 dP[JH], dQG[NCH], dW[NCH], dKH[NCH], dT1[JH];
@@ -593,11 +595,25 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       __syncthreads();
     }
   }
+  // Reference token of the one-reference decay products, and whether every
+  // gate value of the chunk is within 2^-+kFastRange of it (pad rows repeat row L-1)
+  const int mref = (L - 1) >> 1;
+  int bad = 0;
+  {
+    const int c = tid % K;
+    const float gm = sG[mref * GS + c];
+#pragma unroll
+    for (int x = 0; x < kC * K / NT; ++x) {
+      const int j = tid / K + (NT / K) * x;
+      bad |= !(fabsf(sG[j * GS + c] - gm) <= kFastRange);
+    }
+  }
+  bool fastC;
   // dgamma: reduce the thread partials per channel (fixed order)
   {
     float* sRed = reinterpret_cast<float*>(X);
     sRed[tid] = dgam_acc;
-    __syncthreads();
+    fastC = __syncthreads_or(bad) == 0;
     if (tid < K) {
       float s = 0.f;
 #pragma unroll
@@ -624,7 +640,10 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   };
   row_part(dbU, 0);
 
-  // consume d(Q~Gamma) and dKhat; keep per-token-tile column sums of dKhat * Khat
+  // accumulators for token tile tt, channel tiles cb..: dq~, dk, dG (natural-log
+  // cumulative gate), started from d(Q~Gamma) and dKhat; keep per-token-tile
+  // column sums of dKhat * Khat
+  f32x4 aq[NCH], ak[NCH], aG[NCH];
 #pragma unroll
   for (int cc = 0; cc < NCH; ++cc) {
     const int c = 16 * (cb + cc) + l16;
@@ -638,16 +657,18 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       const float qs = to_f32(sQ[i * KSTR + c]) * scale;
       const float kk = to_f32(sK[i * KSTR + c]);
       const float eL = ex2(glast - gi);
-      aq[cc][e] += dQG[cc][e] * Gam;
-      aG[cc][e] += dQG[cc][e] * qs * Gam;
-      ak[cc][e] += dKH[cc][e] * eL;
+      aq[cc][e] = dQG[cc][e] * Gam;
+      ak[cc][e] = dKH[cc][e] * eL;
       const float t = dKH[cc][e] * kk * eL;
-      aG[cc][e] -= t;
+      aG[cc][e] = dQG[cc][e] * qs * Gam - t;
       cs += t;
     }
     cs += __shfl_xor(cs, 16);
     cs += __shfl_xor(cs, 32);
     if (g == 0) sColP[tt * K + c] = cs;
+    pin(aq[cc]);
+    pin(ak[cc]);
+    pin(aG[cc]);
     __builtin_amdgcn_sched_barrier(0);
   }
   // dT1 = dDelta (b v)^T: scale column j by beta_j
@@ -674,140 +695,11 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   }
   __syncthreads();
 
-  // ---- decay-weighted products
-  // fast single-reference path for the diagonal tile when its gate range fits
-  float rng = 0.f;
-#pragma unroll
-  for (int p = 0; p < QK; ++p) {
-    float a0[4], a1[4];
-    lds4(sG + (16 * tt) * GS + 16 * p + 4 * g, a0);
-    lds4(sG + (16 * tt + 15) * GS + 16 * p + 4 * g, a1);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) rng = fmaxf(rng, a0[e] - a1[e]);
-  }
-  rng = fmaxf(rng, __shfl_xor(rng, 16));
-  rng = fmaxf(rng, __shfl_xor(rng, 32));
-  const bool fast = rng <= kFastRange;
-
-  // Z pattern: out(i, c) = sum_j Mm[i][j] Xs[j][c] 2^(G2_i - G2_j), rows i of tile tt.
-  // Reference r = 16tt: operands Xs_j 2^(G2_r - G2_j) (<= 1 for j < r; <= 2^112 on
-  // the diagonal tile in the fast path), output times 2^(G2_i - G2_r) (<= 1).
-  auto zprod = [&](const T* Mm, const T* Xs, float xscale, auto&& consume) {
-    const int r = 16 * tt;
-    F am[KS_C];
-    frag_rows<M, T, QC>(am, Mm, 16 * tt + l16, CS, g);
-#pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-      const int c = 16 * (cb + cc) + l16;
-      const float gr = sG[r * GS + c];
-      F bx[KS_C], bl[KS_C];
-#pragma unroll
-      for (int p = 0; p < QC; ++p) {
-        float x4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 16 * p + 4 * g + e;
-          const bool on = (j < r) || (fast && j < r + 16);
-          x4[e] = on ? to_f32(Xs[j * KSTR + c]) * xscale * ex2(gr - sG[j * GS + c]) : 0.f;
-        }
-        put_quad_split<M>(bx, bl, p, x4);
-      }
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int ks = 0; ks < KS_C; ++ks) {
-        acc = M::mma(am[ks], bx[ks], acc);
-        if constexpr (M::KSTEP == 32) acc = M::mma(am[ks], bl[ks], acc);
-      }
-      f32x4 z;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = r + 4 * g + e;
-        z[e] = acc[e] * ex2(sG[i * GS + c] - gr);
-        if (!fast) {  // diagonal tile, exact elementwise
-          for (int j = r; j <= i; ++j)
-            z[e] += to_f32(Mm[i * CS + j]) * to_f32(Xs[j * KSTR + c]) * xscale * ex2(sG[i * GS + c] - sG[j * GS + c]);
-        }
-      }
-      consume(cc, z);
-      // one channel tile at a time: hoisting the next tile's LDS reads evicts the accumulators
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // Z' pattern: out(j, c) = sum_i MmT[j][i] Xs[i][c] 2^(G2_i - G2_j), rows j of tile tt.
-  // Reference r = 16tt + 15: operands Xs_i 2^(G2_i - G2_r) (<= 1 for i > r),
-  // output times 2^(G2_r - G2_j) (<= 1).
-  auto zprodT = [&](const T* MmT, const T* Xs, float xscale, auto&& consume) {
-    const int r = 16 * tt + 15;
-    F am[KS_C];
-    frag_rows<M, T, QC>(am, MmT, 16 * tt + l16, CS, g);
-#pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-      const int c = 16 * (cb + cc) + l16;
-      const float gr = sG[r * GS + c];
-      F bx[KS_C], bl[KS_C];
-#pragma unroll
-      for (int p = 0; p < QC; ++p) {
-        float x4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * p + 4 * g + e;
-          const bool on = (i > r) || (fast && i > r - 16);
-          x4[e] = on ? to_f32(Xs[i * KSTR + c]) * xscale * ex2(sG[i * GS + c] - gr) : 0.f;
-        }
-        put_quad_split<M>(bx, bl, p, x4);
-      }
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int ks = 0; ks < KS_C; ++ks) {
-        acc = M::mma(am[ks], bx[ks], acc);
-        if constexpr (M::KSTEP == 32) acc = M::mma(am[ks], bl[ks], acc);
-      }
-      f32x4 z;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 16 * tt + 4 * g + e;
-        z[e] = acc[e] * ex2(gr - sG[j * GS + c]);
-        if (!fast) {
-          for (int i = j; i <= r; ++i)
-            z[e] += to_f32(MmT[j * CS + i]) * to_f32(Xs[i * KSTR + c]) * xscale * ex2(sG[i * GS + c] - sG[j * GS + c]);
-        }
-      }
-      consume(cc, z);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  {
-    const T* sdP = reinterpret_cast<const T*>(X);
-    const T* sdPT = sdP + kC * CS;
-    zprod(sdP, sK, 1.f, [&](int cc, const f32x4& z) {  // Y1; dq~ is then complete
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * tt + 4 * g + e, c = 16 * (cb + cc) + l16;
-        aG[cc][e] += to_f32(sQ[i * KSTR + c]) * scale * z[e];
-        if (i < L) {  // dq (per value head; summed over the GVA group later when HV > H)
-          const float dqv = (aq[cc][e] + z[e]) * scale;
-          if (dq_part) dq_part[((t0 + i) * HV + hv) * K + c] = dqv;
-          else dq_out[((t0 + i) * H + h) * K + c] = from_f32<T>(dqv);
-        }
-      }
-    });
-    zprodT(sdPT, sQ, scale, [&](int cc, const f32x4& z) {  // Y2
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 16 * tt + 4 * g + e, c = 16 * (cb + cc) + l16;
-        ak[cc][e] += z[e];
-        aG[cc][e] -= to_f32(sK[j * KSTR + c]) * z[e];
-      }
-    });
-  }
-  __syncthreads();  // q, dP, dP^T dead
-
   // ---- phase 2: dT, T^T dW, dA
   {
-    T* sdW = sQ;                                  // [C][KSTR] row-major dW
-    T* sdWT = reinterpret_cast<T*>(X);            // [K][CS]
+    T* sdWT = XP;                                 // [K][CS]
     T* sBKg = sdWT + K * CS;                      // [C][KSTR] b * k * Gamma
+    T* sdW = sBKg + kC * KSTR;                    // [C][KSTR] row-major dW
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc)
 #pragma unroll
@@ -864,12 +756,14 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
           aG[cc][e] += dkg * kg;
           dbw[e] += kg * acc[e];
         }
+        pin(ak[cc]);
+        pin(aG[cc]);
         __builtin_amdgcn_sched_barrier(0);
       }
       row_part(dbw, 1);
     }
     __syncthreads();  // dW, dW^T, b Kg dead
-    T* sdTT = reinterpret_cast<T*>(X);  // dT transposed [j][i]
+    T* sdTT = XP;  // dT transposed [j][i]
 #pragma unroll
     for (int jj = 0; jj < JH; ++jj)
 #pragma unroll
@@ -891,8 +785,8 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     }
     __syncthreads();
     // dA = -Xm T^T (strictly lower), dAbar = b dA; Abar part of dbeta
-    T* sdAb = sXm + kC * CS;
-    T* sdAbT = sdAb + kC * CS;
+    T* sdAb = sdTT;  // dT^T is dead once Xm is in
+    T* sdAbT = sXm + kC * CS;
     {
       F ax[KS_C];
       frag_rows<M, T, QC>(ax, sXm, 16 * tt + l16, CS, g);
@@ -918,22 +812,129 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       row_part(dba, 2);
     }
     __syncthreads();
-    zprod(sdAb, sK, 1.f, [&](int cc, const f32x4& z) {  // X1
+  }
+
+  // ---- decay-weighted products Y1, Y2 (with dP) and X1, X2 (with dAbar)
+  //   Y1_ic = sum_j dP_ij    k_jc 2^(G2_ic - G2_jc) = 2^(G2_ic - G2_rc)  sum_j dP_ij    [k_jc 2^(G2_rc - G2_jc)]
+  //   X1_ic = sum_j dAbar_ij k_jc 2^(G2_ic - G2_jc) = 2^(G2_ic - G2_rc)  sum_j dAbar_ij [k_jc 2^(G2_rc - G2_jc)]
+  //   Y2_jc = sum_i dP_ij    q~_ic 2^(G2_ic - G2_jc) = 2^(G2_r'c - G2_jc) sum_i dP_ij  [q~_ic 2^(G2_ic - G2_r'c)]
+  //   X2_jc = sum_i dAbar_ij k_ic 2^(G2_ic - G2_jc) = 2^(G2_r'c - G2_jc) sum_i dAbar_ij [k_ic 2^(G2_ic - G2_r'c)]
+  // for rows i (resp. j) of token tile tt. Each lane builds the three bracketed
+  // operands of its channel column over all 64 tokens and feeds four products.
+  // References: the chunk's middle token m for r and r' when every gate value
+  // of the chunk is within 2^-+kFastRange of it (all factors bounded; the row
+  // factors of the tile are then the operand exponentials of its own rows);
+  // otherwise r = 16tt and r' = 16tt + 15, which keep every factor of an
+  // earlier (later) tile <= 1, and the diagonal tile enters the products only
+  // when its own gate range is within kFastRange, else it is summed exactly
+  // element by element.
+  {
+    const T* sdP = XT;
+    const T* sdPT = sdP + kC * CS;
+    const T* sdAb = XP;
+    const T* sdAbT = XP + 2 * kC * CS;
+    bool tfast = true;  // gate range of tile tt within kFastRange (per-tile mode)
+    if (!fastC) {
+      float rng = 0.f;
+#pragma unroll
+      for (int p = 0; p < QK; ++p) {
+        float a0[4], a1[4];
+        lds4(sG + (16 * tt) * GS + 16 * p + 4 * g, a0);
+        lds4(sG + (16 * tt + 15) * GS + 16 * p + 4 * g, a1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rng = fmaxf(rng, a0[e] - a1[e]);
+      }
+      rng = fmaxf(rng, __shfl_xor(rng, 16));
+      rng = fmaxf(rng, __shfl_xor(rng, 32));
+      tfast = rng <= kFastRange;
+    }
+    const int rz = fastC ? mref : 16 * tt;        // reference of the Y1 / X1 operands
+    const int rzt = fastC ? mref : 16 * tt + 15;  // reference of the Y2 / X2 operands
+    // operand rows that enter the products: Z pattern j <= jmax, Z' pattern i >= imin
+    const int jmax = fastC ? kC - 1 : (tfast ? 16 * tt + 15 : 16 * tt - 1);
+    const int imin = fastC ? 0 : (tfast ? 16 * tt : 16 * tt + 16);
+    F aP[KS_C], aPT[KS_C], aAb[KS_C], aAbT[KS_C];
+    frag_rows<M, T, QC>(aP, sdP, 16 * tt + l16, CS, g);
+    frag_rows<M, T, QC>(aPT, sdPT, 16 * tt + l16, CS, g);
+    frag_rows<M, T, QC>(aAb, sdAb, 16 * tt + l16, CS, g);
+    frag_rows<M, T, QC>(aAbT, sdAbT, 16 * tt + l16, CS, g);
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+      const int c = 16 * (cb + cc) + l16;
+      const float gz = sG[rz * GS + c], gzt = sG[rzt * GS + c];
+      F kdh[KS_C], kdl[KS_C], keh[KS_C], kel[KS_C], qdh[KS_C], qdl[KS_C];
+      float ed_t[4], eu_t[4], q_t[4], k_t[4], g_t[4];  // rows 16tt + 4g + e
+#pragma unroll
+      for (int p = 0; p < QC; ++p) {
+        float kd[4], ke[4], qd[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * p + 4 * g + e;
+          const float gj = sG[j * GS + c];
+          const float kj = to_f32(sK[j * KSTR + c]), qj = to_f32(sQ[j * KSTR + c]);
+          const float ed = ex2(gz - gj), eu = ex2(gj - gzt);
+          kd[e] = j <= jmax ? kj * ed : 0.f;
+          ke[e] = j >= imin ? kj * eu : 0.f;
+          qd[e] = j >= imin ? qj * scale * eu : 0.f;
+          if (p == tt) {
+            ed_t[e] = ed;
+            eu_t[e] = eu;
+            q_t[e] = qj;
+            k_t[e] = kj;
+            g_t[e] = gj;
+          }
+        }
+        put_quad_split<M>(kdh, kdl, p, kd);
+        put_quad_split<M>(keh, kel, p, ke);
+        put_quad_split<M>(qdh, qdl, p, qd);
+      }
+      f32x4 y1 = zero4(), x1 = zero4(), y2 = zero4(), x2 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS_C; ++ks) {
+        y1 = M::mma(aP[ks], kdh[ks], y1);
+        x1 = M::mma(aAb[ks], kdh[ks], x1);
+        y2 = M::mma(aPT[ks], qdh[ks], y2);
+        x2 = M::mma(aAbT[ks], keh[ks], x2);
+        if constexpr (M::KSTEP == 32) {
+          y1 = M::mma(aP[ks], kdl[ks], y1);
+          x1 = M::mma(aAb[ks], kdl[ks], x1);
+          y2 = M::mma(aPT[ks], qdl[ks], y2);
+          x2 = M::mma(aAbT[ks], kel[ks], x2);
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * tt + 4 * g + e, c = 16 * (cb + cc) + l16;
-        ak[cc][e] += z[e];
-        aG[cc][e] += to_f32(sK[i * KSTR + c]) * z[e];
+        const int i = 16 * tt + 4 * g + e;
+        // row factors 2^(G2_i - G2_r) and 2^(G2_r' - G2_i); with one reference
+        // they are the operand exponentials of row i
+        const float fz = fastC ? eu_t[e] : ex2(g_t[e] - gz);
+        const float fzt = fastC ? ed_t[e] : ex2(gzt - g_t[e]);
+        float Y1 = y1[e] * fz, X1 = x1[e] * fz, Y2 = y2[e] * fzt, X2 = x2[e] * fzt;
+        if (!tfast) {  // diagonal tile, exact elementwise (per-tile mode only)
+          for (int j = 16 * tt; j <= i; ++j) {
+            const float f = to_f32(sK[j * KSTR + c]) * ex2(g_t[e] - sG[j * GS + c]);
+            Y1 += to_f32(sdP[i * CS + j]) * f;
+            X1 += to_f32(sdAb[i * CS + j]) * f;
+          }
+          for (int j = i; j <= 16 * tt + 15; ++j) {
+            const float f = ex2(sG[j * GS + c] - g_t[e]);
+            Y2 += to_f32(sdPT[i * CS + j]) * to_f32(sQ[j * KSTR + c]) * scale * f;
+            X2 += to_f32(sdAbT[i * CS + j]) * to_f32(sK[j * KSTR + c]) * f;
+          }
+        }
+        if (i < L) {  // dq complete (per value head; summed over the GVA group later when HV > H)
+          const float dqv = (aq[cc][e] + Y1) * scale;
+          if (dq_part) dq_part[((t0 + i) * HV + hv) * K + c] = dqv;
+          else dq_out[((t0 + i) * H + h) * K + c] = from_f32<T>(dqv);
+        }
+        aG[cc][e] += q_t[e] * scale * Y1 + k_t[e] * X1 - k_t[e] * Y2 - k_t[e] * X2;
+        ak[cc][e] += X1 + Y2 + X2;
       }
-    });
-    zprodT(sdAbT, sK, 1.f, [&](int cc, const f32x4& z) {  // X2
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 16 * tt + 4 * g + e, c = 16 * (cb + cc) + l16;
-        ak[cc][e] += z[e];
-        aG[cc][e] -= to_f32(sK[j * KSTR + c]) * z[e];
-      }
-    });
+      pin(ak[cc]);
+      pin(aG[cc]);
+      // one channel tile at a time: hoisting the next tile's LDS reads evicts the accumulators
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // ---- last row: colsum(dKhat * Khat) + dgamma * gamma; reverse cumsum; outputs
@@ -1097,6 +1098,8 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
   e = chains * (V / 32) < kCUs ? launch_scans(std::integral_constant<int, 16>())
                                 : launch_scans(std::integral_constant<int, 32>());
   if (e != hipSuccess) return e;
+  // the instantiations the entry point accepts (bf16; FP32 with K = 64) fit one CU's LDS
+  static_assert(!(sizeof(T) == 2 || K == 64) || BwdLds<T, K, V>::total <= 160 * 1024, "LDS budget");
   if (mc > 0) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_bwd_local_kernel<T, K, V>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)BwdLds<T, K, V>::total);
