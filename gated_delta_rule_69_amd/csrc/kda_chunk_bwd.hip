@@ -313,14 +313,20 @@ struct BwdLds {
 };
 
 // A fragments of a row-major LDS matrix: rows `row`, contraction along the row.
+// bf16 sources feed bf16 fragments bit for bit (quad p is half p & 1 of fragment p / 2).
 template <typename M, typename E, int NQ>
 __device__ __forceinline__ void frag_rows(typename M::frag* f, const E* base, int row, int stride,
                                           int g) {
 #pragma unroll
   for (int p = 0; p < NQ; ++p) {
-    float v[4];
-    lds4(base + row * stride + 16 * p + 4 * g, v);
-    put_quad<M>(f, p, v);
+    if constexpr (M::KSTEP == 32 && sizeof(E) == 2) {
+      *(reinterpret_cast<bf16x4*>(&f[p >> 1]) + (p & 1)) =
+          *reinterpret_cast<const bf16x4*>(base + row * stride + 16 * p + 4 * g);
+    } else {
+      float v[4];
+      lds4(base + row * stride + 16 * p + 4 * g, v);
+      put_quad<M>(f, p, v);
+    }
   }
 }
 // Fragments whose contraction runs down a column of a row-major LDS matrix.
@@ -329,10 +335,15 @@ __device__ __forceinline__ void frag_cols(typename M::frag* f, const E* base, in
                                           int g) {
 #pragma unroll
   for (int p = 0; p < NQ; ++p) {
-    float v[4];
+    if constexpr (M::KSTEP == 32 && sizeof(E) == 2) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = to_f32(base[(16 * p + 4 * g + e) * stride + col]);
-    put_quad<M>(f, p, v);
+      for (int e = 0; e < 4; ++e) f[p >> 1][4 * (p & 1) + e] = base[(16 * p + 4 * g + e) * stride + col];
+    } else {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = to_f32(base[(16 * p + 4 * g + e) * stride + col]);
+      put_quad<M>(f, p, v);
+    }
   }
 }
 
@@ -416,7 +427,67 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   const float* wTm = ws_Bf + ch * WB::elems_f;
   const float* wAb = wTm + WB::TM;
 
-  // ---- stage G2, k, q, T (all loads of a thread issued before its stores); zero the small arrays
+  // phase-1 blocks of VB value columns: dO, Delta, dDelta, v [C][BS]; S0, dS1 [K][BS],
+  // staged through registers one block ahead
+  T* bdO = XT;
+  T* bDl = bdO + kC * BS;
+  T* bdDl = bDl + kC * BS;
+  T* bV = bdDl + kC * BS;
+  T* bS0 = bV + kC * BS;
+  T* bdS = bS0 + K * BS;
+  constexpr int UPR = VB / EPU;  // 16-byte units per block row
+  constexpr int NUC = (kC * UPR + NT - 1) / NT, NUK = (K * UPR + NT - 1) / NT;
+  struct Blk {
+    uint4 a[NUC], b[NUC], c[NUC], d[NUC], s0[NUK], ds[NUK];
+  };
+  auto load_blk = [&](int vb, Blk& x) {
+    const int c0 = vb * VB;
+#pragma unroll
+    for (int i = 0; i < NUC; ++i) {
+      const int u = tid + i * NT;
+      const int row = u / UPR < kC ? u / UPR : 0, cu_ = u % UPR;
+      const int rr = row < L ? row : 0;
+      x.a[i] = *reinterpret_cast<const uint4*>(dO + ((t0 + rr) * HV + hv) * V + c0 + EPU * cu_);
+      x.d[i] = *reinterpret_cast<const uint4*>(v + ((t0 + rr) * HV + hv) * V + c0 + EPU * cu_);
+      x.b[i] = *reinterpret_cast<const uint4*>(wb + WB::oDL + (size_t)row * V + c0 + EPU * cu_);
+      x.c[i] = *reinterpret_cast<const uint4*>(wb + WB::oDDL + (size_t)row * V + c0 + EPU * cu_);
+    }
+#pragma unroll
+    for (int i = 0; i < NUK; ++i) {
+      const int u = tid + i * NT;
+      const int row = u / UPR < K ? u / UPR : 0, cu_ = u % UPR;
+      x.s0[i] = *reinterpret_cast<const uint4*>(wb + WB::oS0 + (size_t)row * V + c0 + EPU * cu_);
+      x.ds[i] = *reinterpret_cast<const uint4*>(wb + WB::oDS + (size_t)row * V + c0 + EPU * cu_);
+    }
+  };
+  auto store_blk = [&](const Blk& x) {
+#pragma unroll
+    for (int i = 0; i < NUC; ++i) {
+      const int u = tid + i * NT;
+      if (u < kC * UPR) {
+        const int row = u / UPR, cu_ = u % UPR;
+        uint4 av = x.a[i], dv_ = x.d[i];
+        if (row >= L) av = dv_ = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(bdO + row * BS + EPU * cu_) = av;
+        *reinterpret_cast<uint4*>(bDl + row * BS + EPU * cu_) = x.b[i];
+        *reinterpret_cast<uint4*>(bdDl + row * BS + EPU * cu_) = x.c[i];
+        *reinterpret_cast<uint4*>(bV + row * BS + EPU * cu_) = dv_;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NUK; ++i) {
+      const int u = tid + i * NT;
+      if (u < K * UPR) {
+        const int row = u / UPR, cu_ = u % UPR;
+        *reinterpret_cast<uint4*>(bS0 + row * BS + EPU * cu_) = x.s0[i];
+        *reinterpret_cast<uint4*>(bdS + row * BS + EPU * cu_) = x.ds[i];
+      }
+    }
+  };
+  Blk pf;
+
+  // ---- stage G2, k, q, T and the first phase-1 block (all loads of a thread
+  // issued before its stores); zero the small arrays
   {
     constexpr int NG = kC * K / 4 / NT, NKQ = kC * K / EPU / NT, NTm = kC * kC / 4 / NT;
     static_assert(NG * NT == kC * K / 4 && NKQ * NT == kC * K / EPU && NTm * NT == kC * kC / 4, "stage");
@@ -440,6 +511,7 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       const int f = tid + i * NT, row = f / (kC / 4), c4 = f % (kC / 4);
       tx[i] = *reinterpret_cast<const float4*>(wTm + row * kC + 4 * c4);
     }
+    load_blk(0, pf);
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       const int f = tid + i * NT, row = f / (K / 4), c4 = f % (K / 4);
@@ -458,8 +530,17 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       const int f = tid + i * NT, row = f / (kC / 4), c4 = f % (kC / 4);
       *reinterpret_cast<float4*>(sT + row * TS + 4 * c4) = tx[i];
     }
+    store_blk(pf);
+    if (V / VB > 1) load_blk(1, pf);
   }
   for (int f = tid; f < 4 * K + K + 6 * kC; f += NT) sColP[f] = 0.f;
+  // outputs of this chunk: uniform base pointers, 32-bit element offsets per lane
+  T* const dvb = dv + (t0 * HV + hv) * (int64_t)V;
+  float* const dgb = dg + (t0 * HV + hv) * (int64_t)K;
+  float* const dqpb = dq_part ? dq_part + (t0 * HV + hv) * (int64_t)K : nullptr;
+  float* const dkpb = dk_part ? dk_part + (t0 * HV + hv) * (int64_t)K : nullptr;
+  T* const dqb = dq_out + (t0 * H + h) * (int64_t)K;
+  T* const dkb = dk_out + (t0 * H + h) * (int64_t)K;
   float bet[4];  // beta of the rows 16tt + 4g + e this lane's accumulators cover
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -481,59 +562,10 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   float dbU[4] = {0.f, 0.f, 0.f, 0.f};
   float dgam_acc = 0.f;  // thread-partial of rowsum(dS1 * S0) for channel tid % K
   {
-    T* bdO = reinterpret_cast<T*>(X);
-    T* bDl = bdO + kC * BS;
-    T* bdDl = bDl + kC * BS;
-    T* bV = bdDl + kC * BS;
-    T* bS0 = bV + kC * BS;
-    T* bdS = bS0 + K * BS;
-    constexpr int UPR = VB / EPU;  // 16-byte units per block row
-    constexpr int NUC = (kC * UPR + NT - 1) / NT, NUK = (K * UPR + NT - 1) / NT;
-    for (int vb = 0; vb < V / VB; ++vb) {
+    constexpr int NVB = V / VB;
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
       const int c0 = vb * VB;
-      {
-        uint4 a[NUC], b[NUC], c[NUC], d[NUC], s0[NUK], ds[NUK];
-#pragma unroll
-        for (int i = 0; i < NUC; ++i) {
-          const int u = tid + i * NT;
-          const int row = u / UPR < kC ? u / UPR : 0, cu_ = u % UPR;
-          const int rr = row < L ? row : 0;
-          a[i] = *reinterpret_cast<const uint4*>(dO + ((t0 + rr) * HV + hv) * V + c0 + EPU * cu_);
-          d[i] = *reinterpret_cast<const uint4*>(v + ((t0 + rr) * HV + hv) * V + c0 + EPU * cu_);
-          b[i] = *reinterpret_cast<const uint4*>(wb + WB::oDL + (size_t)row * V + c0 + EPU * cu_);
-          c[i] = *reinterpret_cast<const uint4*>(wb + WB::oDDL + (size_t)row * V + c0 + EPU * cu_);
-        }
-#pragma unroll
-        for (int i = 0; i < NUK; ++i) {
-          const int u = tid + i * NT;
-          const int row = u / UPR < K ? u / UPR : 0, cu_ = u % UPR;
-          s0[i] = *reinterpret_cast<const uint4*>(wb + WB::oS0 + (size_t)row * V + c0 + EPU * cu_);
-          ds[i] = *reinterpret_cast<const uint4*>(wb + WB::oDS + (size_t)row * V + c0 + EPU * cu_);
-        }
-#pragma unroll
-        for (int i = 0; i < NUC; ++i) {
-          const int u = tid + i * NT;
-          if (u < kC * UPR) {
-            const int row = u / UPR, cu_ = u % UPR;
-            uint4 av = a[i], dv_ = d[i];
-            if (row >= L) av = dv_ = make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4*>(bdO + row * BS + EPU * cu_) = av;
-            *reinterpret_cast<uint4*>(bDl + row * BS + EPU * cu_) = b[i];
-            *reinterpret_cast<uint4*>(bdDl + row * BS + EPU * cu_) = c[i];
-            *reinterpret_cast<uint4*>(bV + row * BS + EPU * cu_) = dv_;
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < NUK; ++i) {
-          const int u = tid + i * NT;
-          if (u < K * UPR) {
-            const int row = u / UPR, cu_ = u % UPR;
-            *reinterpret_cast<uint4*>(bS0 + row * BS + EPU * cu_) = s0[i];
-            *reinterpret_cast<uint4*>(bdS + row * BS + EPU * cu_) = ds[i];
-          }
-        }
-      }
-      __syncthreads();
       constexpr int QV = VB / 16;
       constexpr int KSV = VB / M::KSTEP;
       F aO[KSV], aDl[KSV], adDl[KSV];
@@ -577,7 +609,7 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
         for (int e = 0; e < 4; ++e) {
           const int j = 16 * tt + 4 * g + e;
           const int col = c0 + 16 * vt + l16;
-          if (j < L) dv[((t0 + j) * HV + hv) * V + col] = from_f32<T>(bet[e] * acc[e]);
+          if (j < L) dvb[j * HV * V + col] = from_f32<T>(bet[e] * acc[e]);
           dbU[e] += to_f32(bV[j * BS + 16 * vt + l16]) * acc[e];
         }
       }
@@ -592,7 +624,12 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
           s += to_f32(bdS[c * BS + pidx + parts * x]) * to_f32(bS0[c * BS + pidx + parts * x]);
         dgam_acc += s;
       }
-      __syncthreads();
+      __syncthreads();  // every read of block vb done
+      if (vb + 1 < NVB) {
+        store_blk(pf);
+        if (vb + 2 < NVB) load_blk(vb + 2, pf);
+        __syncthreads();
+      }
     }
   }
   // Reference token of the one-reference decay products, and whether every
@@ -924,8 +961,8 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
         }
         if (i < L) {  // dq complete (per value head; summed over the GVA group later when HV > H)
           const float dqv = (aq[cc][e] + Y1) * scale;
-          if (dq_part) dq_part[((t0 + i) * HV + hv) * K + c] = dqv;
-          else dq_out[((t0 + i) * H + h) * K + c] = from_f32<T>(dqv);
+          if (dqpb) dqpb[i * HV * K + c] = dqv;
+          else dqb[i * H * K + c] = from_f32<T>(dqv);
         }
         aG[cc][e] += q_t[e] * scale * Y1 + k_t[e] * X1 - k_t[e] * Y2 - k_t[e] * X2;
         ak[cc][e] += X1 + Y2 + X2;
@@ -976,7 +1013,7 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * tt + 4 * g + e;
-        if (i < L) dg[((t0 + i) * HV + hv) * K + c] = sfx[e];
+        if (i < L) dgb[i * HV * K + c] = sfx[e];
       }
     }
   }
@@ -988,8 +1025,8 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * tt + 4 * g + e;
       if (i >= L) continue;
-      if (dq_part) dk_part[((t0 + i) * HV + hv) * K + c] = ak[cc][e];
-      else dk_out[((t0 + i) * H + h) * K + c] = from_f32<T>(ak[cc][e]);
+      if (dkpb) dkpb[i * HV * K + c] = ak[cc][e];
+      else dkb[i * H * K + c] = from_f32<T>(ak[cc][e]);
     }
   }
   if (tid < kC && tid < L) {
