@@ -533,19 +533,23 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   float* wsGL = ws_GL + ch * K;
 
   // ---- 3. P fragments (rows i of tile I, contraction over j): accumulators of P^T
+  // (P and Q~ Gamma in ws_T feed only the forward output; the backward's
+  // recurrence forms no output and reads neither)
+  if constexpr (!BWD) {
 #pragma unroll
-  for (int ks = 0; ks < KS_C; ++ks) {
-    F f;
+    for (int ks = 0; ks < KS_C; ++ks) {
+      F f;
 #pragma unroll
-    for (int jj = 0; jj < M::PER; ++jj) {
-      const int tile = acc_tile<M>(ks, jj), el = acc_elem<M>(ks, jj);
-      float x = 0.f;
+      for (int jj = 0; jj < M::PER; ++jj) {
+        const int tile = acc_tile<M>(ks, jj), el = acc_elem<M>(ks, jj);
+        float x = 0.f;
 #pragma unroll
-      for (int J = 0; J < 4; ++J)
-        if (J == tile) x = (J < I) ? accP[J < 3 ? J : 0][el] : (J == I ? dP[el] : 0.f);
-      M::set(f, jj, x);
+        for (int J = 0; J < 4; ++J)
+          if (J == tile) x = (J < I) ? accP[J < 3 ? J : 0][el] : (J == I ? dP[el] : 0.f);
+        M::set(f, jj, x);
+      }
+      reinterpret_cast<F*>(wsP)[((size_t)I * KS_C + ks) * 64 + lane] = f;
     }
-    reinterpret_cast<F*>(wsP)[((size_t)I * KS_C + ks) * 64 + lane] = f;
   }
   if constexpr (BWD) {
     // P^T fragments (rows j, contraction over i): the P tile (I, J) accumulators
@@ -608,7 +612,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     }
   }
   // ---- 4. Q~ * Gamma fragments (rows i of tile I, contraction over channels)
-  {
+  if constexpr (!BWD) {
     F f[KS_K];
 #pragma unroll
     for (int p = 0; p < QK; ++p) {
@@ -903,8 +907,9 @@ struct Raw4<float> {
   }
 };
 
-// KEEP: also store every chunk's start state S0 and Delta into ws_B (the
-// backward pass reuses them); the forward instantiation has none of it.
+// KEEP: store every chunk's start state S0 and Delta into ws_B for the
+// backward pass instead of forming outputs (Q~ Gamma and P are not read);
+// the forward instantiation has none of it.
 // NW waves per workgroup (4 or 8). Work of one chunk: the Delta and output
 // tiles (token tile x value tile) are split over the waves, NW / 4 waves per
 // token tile; the state tiles (channel tile x value tile) by channel tile.
@@ -981,10 +986,12 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
 #pragma unroll
     for (int ks = 0; ks < KS_K; ++ks) {
       op.w[ks] = fW[((size_t)tt * KS_K + ks) * 64 + lane];
-      op.qg[ks] = fQG[((size_t)tt * KS_K + ks) * 64 + lane];
+      if constexpr (!KEEP) op.qg[ks] = fQG[((size_t)tt * KS_K + ks) * 64 + lane];
     }
+    if constexpr (!KEEP) {
 #pragma unroll
-    for (int ks = 0; ks < KS_C; ++ks) op.p[ks] = fP[((size_t)tt * KS_C + ks) * 64 + lane];
+      for (int ks = 0; ks < KS_C; ++ks) op.p[ks] = fP[((size_t)tt * KS_C + ks) * 64 + lane];
+    }
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
 #pragma unroll
@@ -1025,13 +1032,14 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
   // Delta fragments its step already read from LDS; otherwise they would not
   // fit the register file and are read again from the chunk's LDS buffers
   // (intact until the step after next).
-  constexpr bool CACHE = sizeof(T) == 2 && CTB <= 2;
+  constexpr bool CACHE = !KEEP && sizeof(T) == 2 && CTB <= 2;
   struct OutOps {
     F qg[KS_K], p[KS_C];
     F sf[CACHE ? KS_K : 1][CACHE ? CPW : 1];  // S0 fragments (value tiles ct0..)
     F df[CACHE ? KS_C : 1][CACHE ? CPW : 1];  // Delta fragments (value tiles ct0..)
   };
   auto output = [&](const OutOps& op, const int cj, const int buf) __attribute__((always_inline)) {
+    if constexpr (KEEP) return;  // the backward's recurrence forms no output
     const int cidx = cj - cbeg;
     const int64_t t0 = bos + (int64_t)cidx * kC;
     const int L = min(kC, len - cidx * kC);
@@ -1194,10 +1202,12 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
 #pragma unroll
         for (int ct = 0; ct < CTB; ++ct) S[rt][ct] = M::mma(cur.kh[rt][ks], dall[ks][ct], S[rt][ct]);
     }
+    if constexpr (!KEEP) {
 #pragma unroll
-    for (int ks = 0; ks < KS_K; ++ks) mine.qg[ks] = cur.qg[ks];
+      for (int ks = 0; ks < KS_K; ++ks) mine.qg[ks] = cur.qg[ks];
 #pragma unroll
-    for (int ks = 0; ks < KS_C; ++ks) mine.p[ks] = cur.p[ks];
+      for (int ks = 0; ks < KS_C; ++ks) mine.p[ks] = cur.p[ks];
+    }
   };
 
   // two operand sets, unrolled by two so the next chunk's loads stay in flight
