@@ -286,12 +286,13 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
 template <typename T, int K, int V>
 struct BwdLds {
   static constexpr int TP = 16 / (int)sizeof(T);
-  static constexpr int VB = 32;             // V columns per phase-1 block
+  // V columns per phase-1 block: 64 for bf16 (128-byte row pieces), 32 for FP32
+  static constexpr int VB = sizeof(T) == 2 ? 64 : 32;
   static constexpr int GS = K + 4;          // G2 (floats)
   static constexpr int KSTR = K + TP;       // k, q, dW, b*Kg (elements of T)
   static constexpr int TS = kC + 4;         // T (floats)
   static constexpr int CS = kC + TP;        // C x C matrices and transposed C x K (elements of T)
-  static constexpr int BS = VB + TP;        // phase-1 blocks
+  static constexpr int BS = VB + 4;         // phase-1 blocks (8-byte aligned rows)
   static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr size_t szG = (size_t)kC * GS * 4;
   static constexpr size_t szK = (size_t)kC * KSTR * sizeof(T);
@@ -399,7 +400,8 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   constexpr int GS = Lds::GS, KSTR = Lds::KSTR, TS = Lds::TS, CS = Lds::CS, BS = Lds::BS;
   constexpr int VB = Lds::VB;
   constexpr int EPU = 16 / (int)sizeof(T);
-  static_assert(VB / 16 == 2, "one value tile of a V block per half");
+  constexpr int VTH = VB / 32;  // value tiles of a block per half
+  static_assert(VTH * 32 == VB && V % VB == 0, "V blocks");
 
   extern __shared__ __align__(16) char smem[];
   float* sG = reinterpret_cast<float*>(smem + Lds::oG);
@@ -460,6 +462,10 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       x.ds[i] = *reinterpret_cast<const uint4*>(wb + WB::oDS + (size_t)row * V + c0 + EPU * cu_);
     }
   };
+  auto put16 = [](T* dst, const uint4& x) {  // block rows are 8-byte aligned
+    reinterpret_cast<uint2*>(dst)[0] = make_uint2(x.x, x.y);
+    reinterpret_cast<uint2*>(dst)[1] = make_uint2(x.z, x.w);
+  };
   auto store_blk = [&](const Blk& x) {
 #pragma unroll
     for (int i = 0; i < NUC; ++i) {
@@ -468,10 +474,10 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
         const int row = u / UPR, cu_ = u % UPR;
         uint4 av = x.a[i], dv_ = x.d[i];
         if (row >= L) av = dv_ = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(bdO + row * BS + EPU * cu_) = av;
-        *reinterpret_cast<uint4*>(bDl + row * BS + EPU * cu_) = x.b[i];
-        *reinterpret_cast<uint4*>(bdDl + row * BS + EPU * cu_) = x.c[i];
-        *reinterpret_cast<uint4*>(bV + row * BS + EPU * cu_) = dv_;
+        put16(bdO + row * BS + EPU * cu_, av);
+        put16(bDl + row * BS + EPU * cu_, x.b[i]);
+        put16(bdDl + row * BS + EPU * cu_, x.c[i]);
+        put16(bV + row * BS + EPU * cu_, dv_);
       }
     }
 #pragma unroll
@@ -479,8 +485,8 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       const int u = tid + i * NT;
       if (u < K * UPR) {
         const int row = u / UPR, cu_ = u % UPR;
-        *reinterpret_cast<uint4*>(bS0 + row * BS + EPU * cu_) = x.s0[i];
-        *reinterpret_cast<uint4*>(bdS + row * BS + EPU * cu_) = x.ds[i];
+        put16(bS0 + row * BS + EPU * cu_, x.s0[i]);
+        put16(bdS + row * BS + EPU * cu_, x.ds[i]);
       }
     }
   };
@@ -597,9 +603,10 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
           dKH[cc] = M::mma(aDl[ks], bdS_[ks], dKH[cc]);
         }
       }
-      // T^T dDelta for token tile tt (rows j), value tile hh of the block -> dv, v part of dbeta
-      {
-        const int vt = hh;
+      // T^T dDelta for token tile tt (rows j), value tiles of half hh of the block -> dv, v part of dbeta
+#pragma unroll
+      for (int vv = 0; vv < VTH; ++vv) {
+        const int vt = VTH * hh + vv;
         F bdd[KS_C];
         frag_cols<M, T, QC>(bdd, bdDl, 16 * vt + l16, BS, g);  // dDelta down i
         f32x4 acc = zero4();
@@ -1135,8 +1142,9 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
   e = chains * (V / 32) < kCUs ? launch_scans(std::integral_constant<int, 16>())
                                 : launch_scans(std::integral_constant<int, 32>());
   if (e != hipSuccess) return e;
-  // the instantiations the entry point accepts (bf16; FP32 with K = 64) fit one CU's LDS
-  static_assert(!(sizeof(T) == 2 || K == 64) || BwdLds<T, K, V>::total <= 160 * 1024, "LDS budget");
+  // the instantiations the entry point accepts (bf16; FP32 with K = 64) stay within 158 KiB of
+  // LDS (a workgroup asking for the full 160 KiB of the CU does not launch)
+  static_assert(!(sizeof(T) == 2 || K == 64) || BwdLds<T, K, V>::total <= 158 * 1024, "LDS budget");
   if (mc > 0) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_bwd_local_kernel<T, K, V>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)BwdLds<T, K, V>::total);
