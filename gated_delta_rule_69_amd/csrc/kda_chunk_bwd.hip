@@ -52,9 +52,10 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
   constexpr int TP = 16 / (int)sizeof(T);
   constexpr int DS = BV + TP;  // dO staging row stride
 
+  // double buffered by chunk parity: two barriers per chunk suffice
   __shared__ F sS[2][KS_K][CTB][64];  // dS1 as B fragments (contraction over channels)
-  __shared__ F sD[KS_C][CTB][64];     // dDelta as B fragments (contraction over tokens)
-  __shared__ __align__(16) T sdO[kC * DS];  // dO block of the chunk, row-major
+  __shared__ F sD[2][KS_C][CTB][64];  // dDelta as B fragments (contraction over tokens)
+  __shared__ __align__(16) T sdO[2][kC * DS];  // dO block of the chunk, row-major, staged a chunk ahead
 
   const int n = blockIdx.x / HV, hv = blockIdx.x % HV, vb = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
@@ -95,19 +96,43 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
         S[rt][ct][e] = dht ? dht[st_base + (size_t)c * V + col] : 0.f;
       }
 
-  // per-chunk operands of this wave (and one 16-byte unit of the chunk's dO
-  // block per thread), loaded one chunk ahead
+  // Per-chunk operands of this wave, loaded one chunk ahead, and one 16-byte
+  // unit per thread of the dO block of the chunk after it in the reverse order
+  // (staged into LDS during this chunk's step, read in the next one).
   constexpr int UPR = BV * (int)sizeof(T) / 16;               // 16-byte units per dO row
   constexpr int DOU = (kC * UPR + kThreads - 1) / kThreads;  // units per thread
   struct ROps {
     F khn[KS_K], pt[KS_C], qgt[RTW][KS_C], wt[RTW][KS_C];
     float4 gl[RTW];
-    uint4 dob[DOU];
+    uint4 dob[DOU];  // dO of chunk cj - 1 (clamped to cbeg)
   };
-  auto load_ops = [&](int cj, ROps& op) {
+  // dO block of chunk cj: rows >= L read row 0 of the chunk and are zeroed when staged
+  auto load_dob = [&](int cj, uint4* dob) {
     const int cidx = cj - cbeg;
     const int64_t t0 = bos + (int64_t)cidx * kC;
     const int L = min(kC, len - cidx * kC);
+#pragma unroll
+    for (int d = 0; d < DOU; ++d) {
+      const int u = tid + d * kThreads;
+      const int row = (u / UPR) < L ? (u / UPR) : 0, cu_ = u % UPR;
+      dob[d] = u < kC * UPR
+                   ? *reinterpret_cast<const uint4*>(dO + ((t0 + row) * HV + hv) * V + col_base + cu_ * (16 / sizeof(T)))
+                   : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stage_dob = [&](int cj, const uint4* dob, T* dst) {
+    const int L = min(kC, len - (cj - cbeg) * kC);
+#pragma unroll
+    for (int d = 0; d < DOU; ++d) {
+      const int u = tid + d * kThreads;
+      if (u < kC * UPR) {
+        const int row = u / UPR, cu_ = u % UPR;
+        *reinterpret_cast<uint4*>(dst + row * DS + cu_ * (16 / sizeof(T))) =
+            row < L ? dob[d] : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto load_ops = [&](int cj, ROps& op) {
     const size_t ch = (size_t)cj * HV + hv;
     const T* wb = ws_B + ch * WB::elems;
     const F* fPT = reinterpret_cast<const F*>(wb + WB::oPT);
@@ -128,34 +153,47 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
       }
       op.gl[rt] = *reinterpret_cast<const float4*>(ws_GL + ch * K + 16 * tileK + 4 * g);
     }
-    // dO rows >= L read row 0 of the chunk and are zeroed when staged
-#pragma unroll
-    for (int d = 0; d < DOU; ++d) {
-      const int u = tid + d * kThreads;
-      const int row = (u / UPR) < L ? (u / UPR) : 0, cu_ = u % UPR;
-      op.dob[d] = u < kC * UPR
-                      ? *reinterpret_cast<const uint4*>(dO + ((t0 + row) * HV + hv) * V + col_base + cu_ * (16 / sizeof(T)))
-                      : make_uint4(0, 0, 0, 0);
-    }
+    load_dob(max(cj - 1, cbeg), op.dob);
   };
 
+  // One chunk with LDS buffer set `buf`. Its dO block is already in sdO[buf]
+  // (staged during the previous step, visible since that step's second
+  // barrier), so P^T dO and (Q~Gamma)^T dO, which do not depend on dS, are
+  // formed before the first barrier. Buffer reuse: every read of a buffer set
+  // happens before the first barrier of the following step, and the set is
+  // written again only after that barrier, two steps later.
   auto step = [&](const ROps& op, const int cj, const int buf) __attribute__((always_inline)) {
-    const int cidx = cj - cbeg;
-    const int L = min(kC, len - cidx * kC);
     const size_t ch = (size_t)cj * HV + hv;
     T* wb = ws_B + ch * WB::elems;
 
-    // stage the dO block (rows >= L are zero); the previous chunk's reads of
-    // sdO finished before its last barrier
+    // dO as B fragments (contraction over tokens)
+    F bdo[CTB][KS_C];
 #pragma unroll
-    for (int d = 0; d < DOU; ++d) {
-      const int u = tid + d * kThreads;
-      if (u < kC * UPR) {
-        const int row = u / UPR, cu_ = u % UPR;
-        *reinterpret_cast<uint4*>(sdO + row * DS + cu_ * (16 / sizeof(T))) =
-            row < L ? op.dob[d] : make_uint4(0, 0, 0, 0);
+    for (int ct = 0; ct < CTB; ++ct)
+#pragma unroll
+      for (int p = 0; p < QC; ++p) {
+        float x4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x4[e] = to_f32(sdO[buf][(16 * p + 4 * g + e) * DS + 16 * ct + l16]);
+        put_quad<M>(bdo[ct], p, x4);
       }
+    // input terms: P^T dO (token tile `wave`) and (Q~Gamma)^T dO (the wave's channel tiles)
+    f32x4 D[CTB], Sin[RTW][CTB];
+#pragma unroll
+    for (int ct = 0; ct < CTB; ++ct) {
+      D[ct] = zero4();
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) Sin[rt][ct] = zero4();
     }
+#pragma unroll
+    for (int ks = 0; ks < KS_C; ++ks)
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct) {
+        D[ct] = M::mma(op.pt[ks], bdo[ct][ks], D[ct]);
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) Sin[rt][ct] = M::mma(op.qgt[rt][ks], bdo[ct][ks], Sin[rt][ct]);
+      }
+
     // keep dS1 of this chunk for the local kernel; publish it as B fragments
     T* dsl = wb + WB::oDS;
 #pragma unroll
@@ -183,31 +221,11 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
     }
     __syncthreads();
 
-    // dO as B fragments (contraction over tokens), built by every wave
-    F bdo[CTB][KS_C];
-#pragma unroll
-    for (int ct = 0; ct < CTB; ++ct)
-#pragma unroll
-      for (int p = 0; p < QC; ++p) {
-        float x4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x4[e] = to_f32(sdO[(16 * p + 4 * g + e) * DS + 16 * ct + l16]);
-        put_quad<M>(bdo[ct], p, x4);
-      }
-
-    // dDelta for token tile `wave`: Khat dS1 + P^T dO
-    f32x4 D[CTB];
-#pragma unroll
-    for (int ct = 0; ct < CTB; ++ct) D[ct] = zero4();
+    // dDelta for token tile `wave`: P^T dO + Khat dS1
 #pragma unroll
     for (int ks = 0; ks < KS_K; ++ks) {
 #pragma unroll
       for (int ct = 0; ct < CTB; ++ct) D[ct] = M::mma(op.khn[ks], sS[buf][ks][ct][lane], D[ct]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS_C; ++ks) {
-#pragma unroll
-      for (int ct = 0; ct < CTB; ++ct) D[ct] = M::mma(op.pt[ks], bdo[ct][ks], D[ct]);
     }
     T* ddl = wb + WB::oDDL;
 #pragma unroll
@@ -219,16 +237,18 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
         bf16x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = (bf16)D[ct][e];
-        *(reinterpret_cast<bf16x4*>(&sD[wave >> 1][ct][lane]) + (wave & 1)) = x;
+        *(reinterpret_cast<bf16x4*>(&sD[buf][wave >> 1][ct][lane]) + (wave & 1)) = x;
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           F f;
           M::set(f, 0, D[ct][e]);
-          sD[4 * wave + e][ct][lane] = f;
+          sD[buf][4 * wave + e][ct][lane] = f;
         }
       }
     }
+    // the dO block of the next chunk in the reverse order
+    stage_dob(max(cj - 1, cbeg), op.dob, sdO[buf ^ 1]);
     __syncthreads();
 
     // dS0 = Diag(gamma) dS1 + (Q~Gamma)^T dO - W^T dDelta
@@ -237,31 +257,29 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
       const float ga[4] = {op.gl[rt].x, op.gl[rt].y, op.gl[rt].z, op.gl[rt].w};
       f32x4 neg[CTB];
 #pragma unroll
-      for (int ct = 0; ct < CTB; ++ct) {
-        neg[ct] = zero4();
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S[rt][ct][e] *= ga[e];
-      }
+      for (int ct = 0; ct < CTB; ++ct) neg[ct] = zero4();
 #pragma unroll
       for (int ks = 0; ks < KS_C; ++ks) {
 #pragma unroll
-        for (int ct = 0; ct < CTB; ++ct) {
-          S[rt][ct] = M::mma(op.qgt[rt][ks], bdo[ct][ks], S[rt][ct]);
-          neg[ct] = M::mma(op.wt[rt][ks], sD[ks][ct][lane], neg[ct]);
-        }
+        for (int ct = 0; ct < CTB; ++ct) neg[ct] = M::mma(op.wt[rt][ks], sD[buf][ks][ct][lane], neg[ct]);
       }
 #pragma unroll
       for (int ct = 0; ct < CTB; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) S[rt][ct][e] -= neg[ct][e];
+        for (int e = 0; e < 4; ++e) S[rt][ct][e] = S[rt][ct][e] * ga[e] + Sin[rt][ct][e] - neg[ct][e];
     }
-    __syncthreads();  // sdO and sD are written again next chunk
   };
 
   // chunks in reverse; two operand sets, unrolled by two (the first chunk is
   // fetched again near the end so every path has the same loads in flight)
   ROps opA, opB;
-  load_ops(cend - 1, opA);
+  {
+    uint4 d0[DOU];
+    load_dob(cend - 1, d0);
+    load_ops(cend - 1, opA);
+    stage_dob(cend - 1, d0, sdO[0]);
+  }
+  __syncthreads();
   for (int cj = cend - 1;; cj -= 2) {
     load_ops(max(cj - 1, cbeg), opB);
     step(opA, cj, 0);
