@@ -8,8 +8,10 @@ Contents
   * `kda_oracle.c`  FP64 token recurrence and its hand-written reverse pass
                     (C, OpenMP over (sequence, value head)), loaded via ctypes.
   * `gate_activation`, `gate_cumsum_log2`  FP64 NumPy gate: g = -exp(A_log) *
-                    softplus(x) (omitted A_log = unit scale), then the
-                    chunk-local inclusive cumsum in log2 units.
+                    softplus(x + dt_bias) (omitted A_log = unit scale, omitted
+                    dt_bias = no bias), then the chunk-local inclusive cumsum
+                    in log2 units; `gate_activation_bwd` its reverse (dx,
+                    dA_log, d_dt_bias).
   * `forms.py`      independent reformulations (single-chunk dense solve,
                     chunked UT form) used only to pin the recurrence.
 
@@ -103,14 +105,57 @@ def softplus(x: np.ndarray) -> np.ndarray:
         return np.where(x > 20.0, x, np.log1p(np.exp(np.minimum(x, 20.0))))
 
 
-def gate_activation(x: np.ndarray, A_log: Optional[np.ndarray]) -> np.ndarray:
-    """Per-token natural-log decay g = -exp(A_log[hv]) * softplus(x).
+def gate_activation(x: np.ndarray, A_log: Optional[np.ndarray],
+                    dt_bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """Per-token natural-log decay g = -exp(A_log[hv]) * softplus(x + dt_bias[hv, c]).
 
     x: [..., HV, K]; A_log: [HV] or None. None means unit scale, which is
-    identical to an explicit zero A_log (PR #1294 Summary)."""
+    identical to an explicit zero A_log (PR #1294 Summary). dt_bias: [HV, K]
+    (or flat HV*K) or None (no bias); the pages name a gate bias and its
+    gradient (PR #1294 commit list, "Reduce GDN/KDA gate bias gradients
+    before downcasting") without printing where it enters: here it is added
+    to the raw input before the softplus."""
     x = _f64(x)
-    scale = np.ones(x.shape[-2]) if A_log is None else np.exp(_f64(A_log))
-    return -scale[:, None] * softplus(x)
+    HV, K = x.shape[-2], x.shape[-1]
+    scale = np.ones(HV) if A_log is None else np.exp(_f64(A_log))
+    u = x if dt_bias is None else x + _f64(dt_bias).reshape(HV, K)
+    return -scale[:, None] * softplus(u)
+
+
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    """Derivative of `softplus` above: 1 / (1 + exp(-x)), exactly 1 above 20
+    where softplus returns its argument."""
+    x = _f64(x)
+    with np.errstate(over="ignore"):
+        return np.where(x > 20.0, 1.0, 1.0 / (1.0 + np.exp(-x)))
+
+
+def gate_activation_bwd(x: np.ndarray, A_log: Optional[np.ndarray],
+                        dt_bias: Optional[np.ndarray], dg: np.ndarray,
+                        cu_seqlens=None):
+    """Reverse of `gate_activation` for the gradient dg of the per-token gate g.
+
+    x, dg: [B, T, HV, K]. Returns (dx, dA_log, d_dt_bias):
+      dx[t, h, c]    = dg * dg/dx = -exp(A_log[h]) * sigmoid(x + dt_bias[h, c]) * dg
+      dA_log[h]      = sum over tokens and channels of dg * g   (dg/dA_log = g)
+      d_dt_bias[h, c] = sum over tokens of dx                  (dg/ddt_bias = dg/dx)
+    dA_log is None when A_log is None and d_dt_bias is None when dt_bias is
+    None (no parameter). Only tokens inside a sequence (dense: every token;
+    varlen: [cu[n], cu[n+1])) enter the sums; dx of other tokens is NaN."""
+    x, dg = _f64(x), _f64(dg)
+    B, T, HV, K = x.shape
+    scale = np.ones(HV) if A_log is None else np.exp(_f64(A_log))
+    u = x if dt_bias is None else x + _f64(dt_bias).reshape(HV, K)
+    g = -scale[:, None] * softplus(u)
+    dx_all = -scale[:, None] * sigmoid(u) * dg
+    inside = np.zeros(B * T, dtype=bool)
+    for bos, eos in seq_bounds(B, T, cu_seqlens):
+        inside[bos:eos] = True
+    inside = inside.reshape(B, T)
+    dx = np.where(inside[:, :, None, None], dx_all, np.nan)
+    dA = None if A_log is None else (dg * g)[inside].sum(axis=(0, 2))
+    db = None if dt_bias is None else dx_all[inside].sum(axis=0)
+    return dx, dA, db
 
 
 def seq_bounds(B: int, T: int, cu_seqlens: Optional[Sequence[int]]):

@@ -75,3 +75,135 @@ def test_log2_cumsum_roundtrip(oracle):
     cu = [0, 7, 30]
     G2 = oracle.gate_cumsum_log2(g, cu, 8)
     np.testing.assert_allclose(oracle.g_from_log2_cumsum(G2, cu, 8), g, rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------- gate backward (dx, dA_log, d_dt_bias)
+
+def _gate_bwd_case(seed, B=1, T=9, HV=2, K=3, cu=(0, 3, 3, 8)):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, T, HV, K))
+    x[0, 1, 0, 0] = 24.0   # above the softplus threshold (derivative exactly 1 there)
+    x[0, 2, 1, 2] = -27.0  # deep in the exponential tail
+    A_log = 0.7 * rng.standard_normal(HV)
+    dt_bias = rng.standard_normal((HV, K))
+    dg = rng.standard_normal((B, T, HV, K))
+    return x, A_log, dt_bias, dg, (None if cu is None else list(cu))
+
+
+def _inside(B, T, cu):
+    m = np.zeros((B, T), dtype=bool)
+    if cu is None:
+        m[:] = True
+    else:
+        for a, b in zip(cu[:-1], cu[1:]):
+            m[0, a:b] = True
+    return m
+
+
+@pytest.mark.parametrize("cu", [None, (0, 3, 3, 8)])
+def test_gate_bwd_matches_finite_differences(oracle, cu):
+    """dx, dA_log and d_dt_bias against central differences of the scalar
+    L = sum over tokens inside a sequence of dg * g(x, A_log, dt_bias)."""
+    x, A_log, dt_bias, dg, cu = _gate_bwd_case(5, cu=cu)
+    B, T = x.shape[:2]
+    inside = _inside(B, T, cu)[:, :, None, None]
+
+    def loss(x_, a_, b_):
+        return float(np.sum(np.where(inside, dg * oracle.gate_activation(x_, a_, b_), 0.0)))
+
+    dx, dA, db = oracle.gate_activation_bwd(x, A_log, dt_bias, dg, cu)
+    eps = 1e-6
+    for idx in np.ndindex(x.shape):
+        p, m = x.copy(), x.copy()
+        p[idx] += eps
+        m[idx] -= eps
+        fd = (loss(p, A_log, dt_bias) - loss(m, A_log, dt_bias)) / (2 * eps)
+        if inside[idx[0], idx[1], 0, 0]:
+            assert abs(fd - dx[idx]) <= 1e-7 * max(1.0, abs(fd)), (idx, fd, dx[idx])
+        else:
+            assert fd == 0.0 and np.isnan(dx[idx])
+    for h in range(A_log.size):
+        p, m = A_log.copy(), A_log.copy()
+        p[h] += eps
+        m[h] -= eps
+        fd = (loss(x, p, dt_bias) - loss(x, m, dt_bias)) / (2 * eps)
+        assert abs(fd - dA[h]) <= 1e-7 * max(1.0, abs(fd)), (h, fd, dA[h])
+    for idx in np.ndindex(dt_bias.shape):
+        p, m = dt_bias.copy(), dt_bias.copy()
+        p[idx] += eps
+        m[idx] -= eps
+        fd = (loss(x, A_log, p) - loss(x, A_log, m)) / (2 * eps)
+        assert abs(fd - db[idx]) <= 1e-7 * max(1.0, abs(fd)), (idx, fd, db[idx])
+
+
+def test_gate_bias_zero_is_no_bias_bitwise(oracle):
+    x, A_log, _, dg, _ = _gate_bwd_case(6, cu=None)
+    g0 = oracle.gate_activation(x, A_log)
+    gz = oracle.gate_activation(x, A_log, np.zeros((x.shape[2], x.shape[3])))
+    assert g0.tobytes() == gz.tobytes()
+    dx0, dA0, db0 = oracle.gate_activation_bwd(x, A_log, None, dg)
+    dxz, dAz, dbz = oracle.gate_activation_bwd(x, A_log, np.zeros((x.shape[2], x.shape[3])), dg)
+    assert db0 is None and dbz is not None
+    assert dx0.tobytes() == dxz.tobytes() and dA0.tobytes() == dAz.tobytes()
+    _, dAn, _ = oracle.gate_activation_bwd(x, None, None, dg)
+    assert dAn is None
+
+
+def test_gate_bwd_closed_form_at_zero_argument(oracle):
+    """x + dt_bias = 0: softplus' = sigmoid(0) = 1/2 and softplus(0) = ln 2, so
+    dx = -exp(A_log) dg / 2 and dA_log = -exp(A_log) ln 2 * sum(dg)."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((1, 4, 2, 3))
+    dt_bias = -x[0, 0]                      # zero argument on token 0
+    x[0, 1:] = x[0, 0]
+    dg = rng.standard_normal((1, 4, 2, 3))
+    A_log = np.array([0.0, math.log(3.0)])
+    dx, dA, db = oracle.gate_activation_bwd(x, A_log, dt_bias, dg)
+    s = np.exp(A_log)[None, None, :, None]
+    np.testing.assert_allclose(dx, -s * dg / 2, rtol=1e-15, atol=0)
+    np.testing.assert_allclose(dA, -np.exp(A_log) * math.log(2.0) * dg.sum(axis=(0, 1, 3)), rtol=1e-14)
+    np.testing.assert_allclose(db, (-s * dg / 2).sum(axis=(0, 1)), rtol=1e-14)
+
+
+def test_gate_bwd_through_the_scan_matches_finite_differences(oracle):
+    """End to end: x -> g -> recurrence -> L = <o, W_o> + <h_T, W_h>. The
+    recurrence's dg fed to gate_activation_bwd gives dL/dx, dL/dA_log and
+    dL/d_dt_bias (checked on sampled entries)."""
+    import workloads
+    wl = workloads.tiny_case(72, T=11, H=1, HV=2, K=4, V=3, cu_seqlens=[0, 4, 4, 10], grads=True)
+    A_log = np.array([0.3, -0.4])
+    dt_bias = np.random.default_rng(8).standard_normal((2, 4))
+    x = wl.x.astype(np.float64)
+    W_o = np.nan_to_num(wl.dO.astype(np.float64))
+    W_o[:, 10:] = 0.0
+    W_h = wl.dht.astype(np.float64)
+
+    def loss(x_, a_, b_):
+        o, ht = oracle.recurrence(wl.q, wl.k, wl.v, oracle.gate_activation(x_, a_, b_), wl.beta, wl.h0,
+                                  wl.cu_seqlens)
+        return float(np.sum(np.nan_to_num(o) * W_o) + np.sum(ht * W_h))
+
+    g = oracle.gate_activation(x, A_log, dt_bias)
+    grads = oracle.recurrence_bwd(wl.q, wl.k, wl.v, g, wl.beta, W_o, wl.h0, W_h, wl.cu_seqlens)
+    dx, dA, db = oracle.gate_activation_bwd(x, A_log, dt_bias, grads["dg"], wl.cu_seqlens)
+    eps = 1e-6
+    rng = np.random.default_rng(9)
+    for fi in rng.choice(10 * 2 * 4, size=10, replace=False):
+        idx = (0,) + np.unravel_index(fi, (10, 2, 4))
+        p, m = x.copy(), x.copy()
+        p[idx] += eps
+        m[idx] -= eps
+        fd = (loss(p, A_log, dt_bias) - loss(m, A_log, dt_bias)) / (2 * eps)
+        assert abs(fd - dx[idx]) <= 1e-6 * max(1.0, abs(fd)), (idx, fd, dx[idx])
+    for h in range(2):
+        p, m = A_log.copy(), A_log.copy()
+        p[h] += eps
+        m[h] -= eps
+        fd = (loss(x, p, dt_bias) - loss(x, m, dt_bias)) / (2 * eps)
+        assert abs(fd - dA[h]) <= 1e-6 * max(1.0, abs(fd)), (h, fd, dA[h])
+    for idx in [(0, 0), (1, 3)]:
+        p, m = dt_bias.copy(), dt_bias.copy()
+        p[idx] += eps
+        m[idx] -= eps
+        fd = (loss(x, A_log, p) - loss(x, A_log, m)) / (2 * eps)
+        assert abs(fd - db[idx]) <= 1e-6 * max(1.0, abs(fd)), (idx, fd, db[idx])
