@@ -32,7 +32,8 @@ KDA_FP32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
            4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_ALIAS", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_LAUNCH"}
 
-EXPORTED = ("kda_status_string", "kda_gate_cumsum", "kda_chunk_fwd_workspace_bytes",
+EXPORTED = ("kda_status_string", "kda_gate_cumsum", "kda_gate_cumsum_biased",
+            "kda_gate_bwd_workspace_bytes", "kda_gate_bwd", "kda_chunk_fwd_workspace_bytes",
             "kda_chunk_fwd", "kda_chunk_fwd_fused_gate", "kda_chunk_bwd_workspace_bytes",
             "kda_chunk_bwd", "kda_recurrent_fwd", "kda_recurrent_fwd_fused_gate")
 
@@ -62,6 +63,12 @@ def _lib():
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_gate_cumsum.argtypes = [dims, p, i32, p, p, i32, p, p]
         lib.kda_gate_cumsum.restype = ctypes.c_int
+        lib.kda_gate_cumsum_biased.argtypes = [dims, p, p, p, p, i32, p, p]
+        lib.kda_gate_cumsum_biased.restype = ctypes.c_int
+        lib.kda_gate_bwd_workspace_bytes.argtypes = [dims]
+        lib.kda_gate_bwd_workspace_bytes.restype = sz
+        lib.kda_gate_bwd.argtypes = [dims, p, p, p, p, p, p, p, p, p, sz, p]
+        lib.kda_gate_bwd.restype = ctypes.c_int
         lib.kda_chunk_fwd_workspace_bytes.argtypes = [dims, ctypes.c_int, i32]
         lib.kda_chunk_fwd_workspace_bytes.restype = sz
         lib.kda_chunk_fwd.argtypes = [dims, ctypes.c_int, p, p, p, p, p, p, p, i32, i32, p, p, p, sz, p]
@@ -121,21 +128,61 @@ def _dims(q, v, cu_seqlens) -> KdaDims:
 
 def gate_cumsum(gate_in: torch.Tensor, A_log: Optional[torch.Tensor] = None,
                 cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
-                is_raw: bool = True, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                is_raw: bool = True, out: Optional[torch.Tensor] = None,
+                dt_bias: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Step A1 (kda_gate_cumsum): [B, T, HV, K] FP32 raw gate input x (or the
-    natural-log g if is_raw=False) -> chunk-local inclusive cumsum in log2 units."""
-    for t, n in ((gate_in, "gate_in"), (A_log, "A_log"), (cu_seqlens, "cu_seqlens"), (out, "out")):
+    natural-log g if is_raw=False) -> chunk-local inclusive cumsum in log2 units.
+    With dt_bias ([HV, K] FP32, raw input only) it is kda_gate_cumsum_biased."""
+    for t, n in ((gate_in, "gate_in"), (A_log, "A_log"), (cu_seqlens, "cu_seqlens"), (out, "out"),
+                 (dt_bias, "dt_bias")):
         _check(t, n)
     B, T, HV, K = gate_in.shape
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     d = KdaDims(B, T, N, 1, HV, K, 1)
     if out is None:
         out = torch.empty_like(gate_in)
+    if dt_bias is not None:
+        if not is_raw:
+            raise ValueError("dt_bias applies to a raw gate input")
+        rc = _lib().kda_gate_cumsum_biased(ctypes.byref(d), _ptr(gate_in), _ptr(A_log), _ptr(dt_bias),
+                                           _ptr(cu_seqlens), int(chunk_size), _ptr(out), _stream())
+        if rc:
+            raise KdaError("kda_gate_cumsum_biased", rc)
+        return out
     rc = _lib().kda_gate_cumsum(ctypes.byref(d), _ptr(gate_in), int(is_raw), _ptr(A_log),
                                 _ptr(cu_seqlens), int(chunk_size), _ptr(out), _stream())
     if rc:
         raise KdaError("kda_gate_cumsum", rc)
     return out
+
+
+def gate_bwd(x: torch.Tensor, dg: torch.Tensor, A_log: Optional[torch.Tensor] = None,
+             dt_bias: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+             dx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Reverse of the raw gate activation (kda_gate_bwd): x, dg [B, T, HV, K] FP32
+    (dg = gradient of the per-token natural-log gate, e.g. chunk_kda_bwd's dg) ->
+    (dx, dA_log or None, d_dt_bias or None); the parameter gradients are
+    produced exactly for the parameters given."""
+    for t, n in ((x, "x"), (dg, "dg"), (A_log, "A_log"), (dt_bias, "dt_bias"),
+                 (cu_seqlens, "cu_seqlens"), (dx, "dx"), (workspace, "workspace")):
+        _check(t, n)
+    B, T, HV, K = x.shape
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    d = KdaDims(B, T, N, 1, HV, K, 1)
+    if dx is None:
+        dx = torch.empty_like(x)
+    dA = None if A_log is None else torch.empty(HV, device=x.device, dtype=torch.float32)
+    db = None if dt_bias is None else torch.empty(HV, K, device=x.device, dtype=torch.float32)
+    need = int(_lib().kda_gate_bwd_workspace_bytes(ctypes.byref(d)))
+    if (dA is not None or db is not None) and workspace is None:
+        workspace = torch.empty(max(need, 1), device=x.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib().kda_gate_bwd(ctypes.byref(d), _ptr(x), _ptr(A_log), _ptr(dt_bias), _ptr(dg),
+                             _ptr(cu_seqlens), _ptr(dx), _ptr(dA), _ptr(db), _ptr(workspace),
+                             ws_bytes, _stream())
+    if rc:
+        raise KdaError("kda_gate_bwd", rc)
+    return dx, dA, db
 
 
 def chunk_workspace_bytes(q: torch.Tensor, v: torch.Tensor, cu_seqlens=None, chunk_size: int = 64) -> int:

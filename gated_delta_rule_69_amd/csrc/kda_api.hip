@@ -151,8 +151,67 @@ kda_status kda_gate_cumsum(const kda_dims* d, const float* gate_in, int32_t gate
   if (overlaps(gate_in, n * 4, gate_out, n * 4) && !(chunk_size == 1 && gate_in == gate_out))
     return KDA_ERR_ALIAS;
   if (A_log && overlaps(A_log, (size_t)d->HV * 4, gate_out, n * 4)) return KDA_ERR_ALIAS;
-  return kda_host::launch_gate(*d, gate_in, gate_in_is_raw ? 1 : 0, A_log, cu, chunk_size,
-                               gate_out, stream) == hipSuccess
+  return kda_host::launch_gate(*d, gate_in, gate_in_is_raw ? 1 : 0, A_log, nullptr, cu,
+                               chunk_size, gate_out, stream) == hipSuccess
+             ? KDA_OK
+             : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_gate_cumsum_biased(const kda_dims* d, const float* x, const float* A_log,
+                                  const float* dt_bias, const int32_t* cu, int32_t chunk_size,
+                                  float* gate_out, hipStream_t stream) {
+  kda_status st = check_dims(d, cu);
+  if (st != KDA_OK) return st;
+  if (chunk_size < 1 || chunk_size > 64) return KDA_ERR_UNSUPPORTED;
+  const size_t n = (size_t)d->B * d->T * d->HV * d->K;
+  if (n == 0) return KDA_OK;
+  if (!x || !gate_out) return KDA_ERR_NULL;
+  const size_t nb = (size_t)d->HV * d->K * 4;
+  if (overlaps(x, n * 4, gate_out, n * 4) && !(chunk_size == 1 && x == gate_out)) return KDA_ERR_ALIAS;
+  if (overlaps(A_log, (size_t)d->HV * 4, gate_out, n * 4) || overlaps(dt_bias, nb, gate_out, n * 4))
+    return KDA_ERR_ALIAS;
+  return kda_host::launch_gate(*d, x, 1, A_log, dt_bias, cu, chunk_size, gate_out, stream) ==
+                 hipSuccess
+             ? KDA_OK
+             : KDA_ERR_LAUNCH;
+}
+
+size_t kda_gate_bwd_workspace_bytes(const kda_dims* d) {
+  if (!d || d->B < 0 || d->T < 0 || d->HV <= 0 || d->K <= 0) return 0;
+  return kda_host::gate_bwd_ws_bytes(*d);
+}
+
+kda_status kda_gate_bwd(const kda_dims* d, const float* x, const float* A_log,
+                        const float* dt_bias, const float* dg, const int32_t* cu, float* dx,
+                        float* dA_log, float* d_dt_bias, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  kda_status st = check_dims(d, cu);
+  if (st != KDA_OK) return st;
+  if (d->K > 4096) return KDA_ERR_UNSUPPORTED;
+  // a parameter's gradient is produced exactly when the parameter is given
+  if ((A_log == nullptr) != (dA_log == nullptr) || (dt_bias == nullptr) != (d_dt_bias == nullptr))
+    return KDA_ERR_SHAPE;
+  const size_t n = (size_t)d->B * d->T * d->HV * d->K * 4;
+  const size_t na = (size_t)d->HV * 4, nb = (size_t)d->HV * d->K * 4;
+  if (n > 0 && (!x || !dg || !dx)) return KDA_ERR_NULL;
+  const bool reduce = dA_log || d_dt_bias;
+  const size_t need = kda_host::gate_bwd_ws_bytes(*d);
+  if (reduce && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+  if (reduce && ((uintptr_t)workspace & 15)) return KDA_ERR_UNSUPPORTED;
+  // dx may be dg itself (in place); no other overlap between outputs and anything else
+  if (overlaps(dx, n, dg, n) && dx != dg) return KDA_ERR_ALIAS;
+  const void* outs[] = {dx, dA_log, d_dt_bias, reduce ? workspace : nullptr};
+  const size_t outs_n[] = {n, na, nb, reduce ? need : 0};
+  const void* ins[] = {x, A_log, dt_bias, dg, cu};
+  const size_t ins_n[] = {n, na, nb, n, cu ? (size_t)(d->N + 1) * 4 : 0};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (!(i == 0 && j == 3) && overlaps(outs[i], outs_n[i], ins[j], ins_n[j])) return KDA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs_n[i], outs[j], outs_n[j])) return KDA_ERR_ALIAS;
+  }
+  return kda_host::launch_gate_bwd(*d, x, A_log, dt_bias, dg, cu, dx, dA_log, d_dt_bias,
+                                   workspace, stream) == hipSuccess
              ? KDA_OK
              : KDA_ERR_LAUNCH;
 }

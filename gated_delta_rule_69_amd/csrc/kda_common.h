@@ -96,6 +96,14 @@ __device__ __forceinline__ float softplus_f32(float x) {
   return x > 20.f ? x : r;
 }
 
+// d softplus_f32 / dx = 1 / (1 + e^-x), exactly 1 above softplus_f32's threshold
+__device__ __forceinline__ float sigmoid_f32(float x) {
+#pragma clang fp contract(off)
+  const float z = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+  const float r = (x >= 0.f ? 1.f : z) / (1.f + z);
+  return x > 20.f ? 1.f : r;
+}
+
 // What a scan kernel's gate operand holds:
 //   kGateLog2: the log2 gate already prepared (per token for the recurrent
 //              scan, chunk-local inclusive cumsum G2 for the chunked scan);
@@ -144,7 +152,14 @@ __device__ __forceinline__ void seq_range(const int32_t* cu, int n, int T, int64
 // Host-side launchers (defined in the .hip files, called by the C ABI).
 namespace kda_host {
 hipError_t launch_gate(const kda_dims& d, const float* in, int is_raw, const float* A_log,
-                       const int32_t* cu, int chunk, float* out, hipStream_t s);
+                       const float* dt_bias, const int32_t* cu, int chunk, float* out,
+                       hipStream_t s);
+// Gate backward: dx and, when dA_log / d_dt_bias are requested, FP32 partials
+// per token block in `ws` reduced in a fixed order.
+size_t gate_bwd_ws_bytes(const kda_dims& d);
+hipError_t launch_gate_bwd(const kda_dims& d, const float* x, const float* A_log,
+                           const float* dt_bias, const float* dg, const int32_t* cu, float* dx,
+                           float* dA_log, float* d_dt_bias, void* ws, hipStream_t s);
 hipError_t launch_recurrent(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
                             const void* v, const float* gate, int gate_mode, const float* A_log,
                             const void* beta, const float* h0, const int32_t* cu,

@@ -101,6 +101,54 @@ kda_status kda_gate_cumsum(const kda_dims* dims, const float* gate_in, int32_t g
                            const float* A_log, const int32_t* cu_seqlens, int32_t chunk_size,
                            float* gate_out, hipStream_t stream);
 
+/*
+ * kda_gate_cumsum_biased -- step A1 with a gate bias: as kda_gate_cumsum with a
+ * raw input, g = -exp(A_log[hv]) * softplus(x + dt_bias[hv * K + c]). The
+ * pages ("[Fix] Use unit KDA gate scale when A_log is omitted", commit list:
+ * gate bias gradients reduced in FP32 before downcasting) name a gate bias
+ * without printing where it enters; it is added to the raw input here.
+ *   x        [B, T, HV, K] FP32 raw gate input.
+ *   A_log    [HV] FP32 or NULL (unit scale).
+ *   dt_bias  [HV, K] FP32 or NULL (no bias; bitwise identical to kda_gate_cumsum).
+ *   gate_out as kda_gate_cumsum (same summation order, same in-place rule).
+ * Errors as kda_gate_cumsum; dt_bias or A_log overlapping gate_out -> KDA_ERR_ALIAS.
+ */
+kda_status kda_gate_cumsum_biased(const kda_dims* dims, const float* x, const float* A_log,
+                                  const float* dt_bias, const int32_t* cu_seqlens,
+                                  int32_t chunk_size, float* gate_out, hipStream_t stream);
+
+/* Workspace bytes kda_gate_bwd needs when it reduces dA_log or d_dt_bias. */
+size_t kda_gate_bwd_workspace_bytes(const kda_dims* dims);
+
+/*
+ * kda_gate_bwd -- reverse of the raw gate activation of kda_gate_cumsum_biased
+ * (and of kda_gate_cumsum with a raw input, dt_bias = NULL), for the gradient dg
+ * of the per-token natural-log gate g (what kda_chunk_bwd returns as dg):
+ *   dx[t, hv, c]   = -exp(A_log[hv]) * sigmoid(x + dt_bias[hv, c]) * dg[t, hv, c]
+ *                    (sigmoid = 1 above 20, where softplus returns its argument)
+ *   dA_log[hv]     = sum over tokens inside a sequence and channels of dg * g
+ *   d_dt_bias[hv, c] = sum over tokens inside a sequence of dx[t, hv, c]
+ *   x, dg    [B, T, HV, K] FP32; dx [B, T, HV, K] FP32 (may be dg itself; rows
+ *            of tokens outside every sequence are untouched).
+ *   A_log, dt_bias as in kda_gate_cumsum_biased; dA_log [HV] and d_dt_bias
+ *            [HV, K] FP32 are written exactly when A_log, resp. dt_bias, is
+ *            given (else KDA_ERR_SHAPE).
+ *   Reductions: each block of 256 tokens sums its tokens in order into an FP32
+ *            partial per element (in `workspace`); the partials are summed over
+ *            blocks in order, and for dA_log then over channels in order, so
+ *            results are run-to-run deterministic.
+ *   workspace: at least kda_gate_bwd_workspace_bytes(), 16-byte aligned,
+ *            required only when dA_log or d_dt_bias is requested (else may be
+ *            NULL); scratch on entry and return.
+ *   Supports any B, T, HV and K <= 4096. Errors: NULL inputs/outputs with
+ *   tokens present -> KDA_ERR_NULL; missing or small workspace ->
+ *   KDA_ERR_WORKSPACE; overlaps other than dx == dg -> KDA_ERR_ALIAS.
+ */
+kda_status kda_gate_bwd(const kda_dims* dims, const float* x, const float* A_log,
+                        const float* dt_bias, const float* dg, const int32_t* cu_seqlens,
+                        float* dx, float* dA_log, float* d_dt_bias, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes kda_chunk_fwd needs for these sizes (0 on unsupported input). */
 size_t kda_chunk_fwd_workspace_bytes(const kda_dims* dims, kda_dtype dtype, int32_t chunk_size);
 

@@ -117,3 +117,31 @@ def test_fused_gate_entries_reject_bad_arguments():
     assert rec(1, FAKE[5]) == 5
     assert chunk(1, FAKE[9], o=FAKE[3]) == 5  # o overlaps the gate input
     assert rec(1, None, dd=_dims(V=300)) == 4
+
+
+def test_gate_bias_and_gate_bwd_reject_bad_arguments():
+    lib = kda.load()
+    d = _dims()
+    # kda_gate_cumsum_biased(dims, x, A_log, dt_bias, cu, chunk, out, stream)
+    assert lib.kda_gate_cumsum_biased(ctypes.byref(d), FAKE[0], None, FAKE[2], None, 0, FAKE[1], None) == 4
+    assert lib.kda_gate_cumsum_biased(ctypes.byref(d), FAKE[0], None, FAKE[2], None, 64, FAKE[0], None) == 5
+    assert lib.kda_gate_cumsum_biased(ctypes.byref(d), FAKE[0], None, FAKE[1], None, 64, FAKE[1], None) == 5
+    need = lib.kda_gate_bwd_workspace_bytes(ctypes.byref(d))
+    assert need >= 2 * 64 * 4
+
+    # kda_gate_bwd(dims, x, A_log, dt_bias, dg, cu, dx, dA_log, d_dt_bias, ws, ws_bytes, stream)
+    def bwd(A_log=None, bias=None, dx=FAKE[4], dA=None, db=None, ws=FAKE[7], ws_bytes=1 << 30, dd=d):
+        return lib.kda_gate_bwd(ctypes.byref(dd), FAKE[0], A_log, bias, FAKE[3], None, dx, dA, db,
+                                ws, ws_bytes, None)
+
+    assert bwd(A_log=FAKE[1]) == 2                   # A_log given, dA_log missing
+    assert bwd(dA=FAKE[5]) == 2                      # dA_log without A_log
+    assert bwd(bias=FAKE[2]) == 2                    # dt_bias given, d_dt_bias missing
+    assert bwd(A_log=FAKE[1], dA=FAKE[5], ws=None) == 6
+    assert bwd(A_log=FAKE[1], dA=FAKE[5], ws_bytes=need - 1) == 6
+    assert bwd(dx=FAKE[0]) == 5                      # dx overlaps x
+    assert bwd(bias=FAKE[2], db=FAKE[4]) == 5        # d_dt_bias overlaps dx
+    assert bwd(A_log=FAKE[1], dA=FAKE[5], ws=FAKE[4]) == 5  # workspace overlaps dx
+    assert bwd(dd=_dims(K=5000)) == 4
+    assert lib.kda_gate_bwd(ctypes.byref(d), None, None, None, FAKE[3], None, FAKE[4], None, None,
+                            None, 0, None) == 1
