@@ -65,7 +65,8 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--skip-extra", action="store_true", help="skip the context workloads")
-    p.add_argument("--profile", choices=["dense", "dense2", "decode", "decode2", "long", "copy"],
+    p.add_argument("--profile", choices=["dense", "dense2", "decode", "decode2", "long", "gatebwd",
+                                         "copy"],
                    default=None,
                    help="run only one workload a few times (for rocprofv3), print no JSON")
     p.add_argument("--profile-reps", type=int, default=3)
@@ -125,6 +126,16 @@ def profile_only(a):
             G = kda.gate_cumsum(x, None, None, 64)
             kda.chunk_kda(*t[:3], G, t[3], h0, output_final_state=True)
             kda.chunk_kda_bwd(*t[:3], G, t[3], h0, dO, dht)
+    elif a.profile == "gatebwd":
+        # gate backward on the long-context shape: B=1 T=65536 HV=32 K=128, A_log and dt_bias
+        gen = torch.Generator(device=dev).manual_seed(5)
+        x = torch.randn((1, 65536, 32, 128), device=dev, generator=gen)
+        dg = torch.randn(x.shape, device=dev, generator=gen)
+        A = torch.rand(32, device=dev, generator=gen) * 2.772588722239781
+        db = 0.5 * torch.randn((32, 128), device=dev, generator=gen)
+        dx = torch.empty_like(x)
+        for _ in range(a.profile_reps):
+            kda.gate_bwd(x, dg, A, db, dx=dx)
     torch.cuda.synchronize()
     print(f"profile {a.profile}: {a.profile_reps} reps done", flush=True)
 
@@ -352,6 +363,7 @@ def main():
         t5 = dict(q=T_(w5.q, bf), k=T_(w5.k, bf), v=T_(w5.v, bf), b=T_(w5.beta, bf), x=T_(w5.x),
                   A=T_(w5.A_log), h0=T_(w5.h0), dO=T_(w5.dO, bf), dht=T_(w5.dht))
         del w5
+        HV5, K5 = t5["x"].shape[2], t5["x"].shape[3]
         G5 = torch.empty_like(t5["x"])
         o5 = torch.empty_like(t5["v"])
         ws5f = torch.empty(kda.chunk_workspace_bytes(t5["q"], t5["v"]), device=dev, dtype=torch.uint8)
@@ -361,16 +373,31 @@ def main():
                           output_final_state=True, o=o5, workspace=ws5f, use_gate_in_kernel=True,
                           A_log=t5["A"])
 
+        wsg = torch.empty(max(1, kda.gate_bwd_workspace_bytes(t5["x"])), device=dev, dtype=torch.uint8)
+
         def bwd5():
-            # the backward takes the chunk-local log2 gate (kda_gate_cumsum) as input
+            # the backward takes the chunk-local log2 gate (kda_gate_cumsum) as input; the gate
+            # backward turns its dg into dx and dA_log (in place over dg)
             kda.gate_cumsum(t5["x"], t5["A"], None, 64, out=G5)
-            kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], G5, t5["b"], t5["h0"], t5["dO"], t5["dht"])
+            r = kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], G5, t5["b"], t5["h0"], t5["dO"], t5["dht"])
+            kda.gate_bwd(t5["x"], r["dg"], t5["A"], dx=r["dg"], workspace=wsg)
         fwd_ms = time_it(fwd5, 5, warm=2)
         bwd_ms = time_it(bwd5, 3, warm=1)
+        # gate backward alone, with a bias: x, dg in, dx out (FP32), dA_log and d_dt_bias
+        gen = torch.Generator(device=dev).manual_seed(5)
+        dg5 = torch.randn(t5["x"].shape, device=dev, generator=gen)
+        db5 = 0.5 * torch.randn((HV5, K5), device=dev, generator=gen)
+        dx5 = torch.empty_like(dg5)
+        gb_ms = time_it(lambda: kda.gate_bwd(t5["x"], dg5, t5["A"], db5, dx=dx5, workspace=wsg), 10,
+                        warm=2)
+        gb_bytes = 3 * t5["x"].numel() * 4
         extra["long_context_T65536_H32_train"] = {
             "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
-            "fwd_bwd_tokens_per_s": round(65536 / ((fwd_ms + bwd_ms) * 1e-3), 1)}
-        del t5, G5, o5, ws5f
+            "fwd_bwd_tokens_per_s": round(65536 / ((fwd_ms + bwd_ms) * 1e-3), 1),
+            "note": "bwd = kda_gate_cumsum + kda_chunk_bwd + kda_gate_bwd (dx, dA_log)",
+            "gate_bwd_ms": round(gb_ms, 4), "gate_bwd_GBps": round(gb_bytes / (gb_ms * 1e-3) / 1e9, 1),
+            "gate_bwd_hbm_frac": round(gb_bytes / (gb_ms * 1e-3) / 8e12, 4)}
+        del t5, G5, o5, ws5f, wsg, dg5, db5, dx5
         torch.cuda.empty_cache()
 
     # ---------------- CPU baseline: the FP64 oracle on one batch row, all heads

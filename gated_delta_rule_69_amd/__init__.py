@@ -156,6 +156,14 @@ def gate_cumsum(gate_in: torch.Tensor, A_log: Optional[torch.Tensor] = None,
     return out
 
 
+def gate_bwd_workspace_bytes(x: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None) -> int:
+    """Workspace bytes kda_gate_bwd needs for x [B, T, HV, K] when it reduces dA_log or d_dt_bias."""
+    B, T, HV, K = x.shape
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    d = KdaDims(B, T, N, 1, HV, K, 1)
+    return int(_lib().kda_gate_bwd_workspace_bytes(ctypes.byref(d)))
+
+
 def gate_bwd(x: torch.Tensor, dg: torch.Tensor, A_log: Optional[torch.Tensor] = None,
              dt_bias: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
              dx: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):

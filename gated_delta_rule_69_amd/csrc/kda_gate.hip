@@ -230,12 +230,25 @@ gate_bwd_reduce_kernel(const float* __restrict__ part_db, const float* __restric
                        float* __restrict__ dA) {
   extern __shared__ float s_ch[];
   const int hv = blockIdx.x, row = HV * K;
+  constexpr int R = 16;  // partials in flight per thread; the sums still run in block order
   for (int c = threadIdx.x; c < K; c += blockDim.x) {
     float sb = 0.f, sa = 0.f;
-    for (int b = 0; b < nblk; ++b) {
-      const int64_t o = (int64_t)b * row + hv * K + c;
-      if (d_bias) sb += part_db[o];
-      if (dA) sa += part_da[o];
+    const int64_t base = (int64_t)hv * K + c;
+    for (int b0 = 0; b0 < nblk; b0 += R) {
+      float vb[R], va[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int64_t o = (int64_t)(b0 + r < nblk ? b0 + r : 0) * row + base;
+        vb[r] = d_bias ? part_db[o] : 0.f;
+        va[r] = dA ? part_da[o] : 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (b0 + r < nblk) {
+          sb += vb[r];
+          sa += va[r];
+        }
+      }
     }
     if (d_bias) d_bias[hv * K + c] = sb;
     s_ch[c] = sa;
