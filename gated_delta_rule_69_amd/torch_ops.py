@@ -1,0 +1,83 @@
+"""torch.library registration of the KDA entry points (argument marshalling
+only; every step runs in libkda's kernels).
+
+  torch.ops.kda.chunk_kda_train(q, k, v, x, beta, A_log, dt_bias,
+                                initial_state, cu_seqlens) -> (o, final_state)
+      The chunked forward from the raw gate input x (kda_gate_cumsum_biased,
+      then kda_chunk_fwd), differentiable in q, k, v, x, beta, A_log, dt_bias
+      and initial_state: the backward recomputes the chunk-local log2 gate
+      and runs kda_chunk_bwd, then kda_gate_bwd on its dg.
+  torch.ops.kda.recurrent_kda(q, k, v, x, beta, A_log, initial_state,
+                              cu_seqlens) -> (o, final_state)
+      Token-sequential forward with the gate activated in the scan kernel
+      (kda_recurrent_fwd_fused_gate); inference only (no autograd formula).
+
+Both have fake (meta) implementations, so they trace under torch.compile and
+FakeTensor. Shapes: q, k [B, T, H, K]; v [B, T, HV, V]; x [B, T, HV, K] FP32;
+beta [B, T, HV]; A_log [HV] FP32; dt_bias [HV, K] FP32; initial_state
+[N, HV, K, V] FP32; cu_seqlens [N + 1] int32 (varlen, B == 1).
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+from torch import Tensor
+
+from . import chunk_kda, chunk_kda_bwd, gate_bwd, gate_cumsum, recurrent_kda
+
+_CHUNK = 64
+
+
+def _n_states(q: Tensor, cu_seqlens: Optional[Tensor]) -> int:
+    return q.shape[0] if cu_seqlens is None else cu_seqlens.shape[0] - 1
+
+
+@torch.library.custom_op("kda::chunk_kda_train", mutates_args=(), device_types="cuda")
+def chunk_kda_train(q: Tensor, k: Tensor, v: Tensor, x: Tensor, beta: Tensor,
+                    A_log: Optional[Tensor], dt_bias: Optional[Tensor],
+                    initial_state: Optional[Tensor],
+                    cu_seqlens: Optional[Tensor]) -> Tuple[Tensor, Tensor]:
+    G = gate_cumsum(x, A_log, cu_seqlens, _CHUNK, dt_bias=dt_bias)
+    o, ht = chunk_kda(q, k, v, G, beta, initial_state, cu_seqlens=cu_seqlens,
+                      output_final_state=True, chunk_size=_CHUNK)
+    return o, ht
+
+
+@chunk_kda_train.register_fake
+def _chunk_kda_train_fake(q, k, v, x, beta, A_log, dt_bias, initial_state, cu_seqlens):
+    N = _n_states(q, cu_seqlens)
+    return torch.empty_like(v), q.new_empty((N, v.shape[2], q.shape[3], v.shape[3]),
+                                            dtype=torch.float32)
+
+
+def _chunk_setup(ctx, inputs, output):
+    ctx.save_for_backward(*inputs)
+
+
+def _chunk_backward(ctx, do, dht):
+    q, k, v, x, beta, A_log, dt_bias, h0, cu = ctx.saved_tensors
+    G = gate_cumsum(x, A_log, cu, _CHUNK, dt_bias=dt_bias)
+    r = chunk_kda_bwd(q, k, v, G, beta, h0, do.contiguous(), dht.contiguous(), cu_seqlens=cu,
+                      chunk_size=_CHUNK)
+    dx, dA, db = gate_bwd(x, r["dg"], A_log, dt_bias, cu, dx=r["dg"])
+    return (r["dq"], r["dk"], r["dv"], dx, r["dbeta"], dA, db,
+            r["dh0"] if h0 is not None else None, None)
+
+
+chunk_kda_train.register_autograd(_chunk_backward, setup_context=_chunk_setup)
+
+
+@torch.library.custom_op("kda::recurrent_kda", mutates_args=(), device_types="cuda")
+def recurrent_kda_op(q: Tensor, k: Tensor, v: Tensor, x: Tensor, beta: Tensor,
+                     A_log: Optional[Tensor], initial_state: Optional[Tensor],
+                     cu_seqlens: Optional[Tensor]) -> Tuple[Tensor, Tensor]:
+    return recurrent_kda(q, k, v, x, beta, initial_state, cu_seqlens=cu_seqlens,
+                         output_final_state=True, use_gate_in_kernel=True, A_log=A_log)
+
+
+@recurrent_kda_op.register_fake
+def _recurrent_kda_fake(q, k, v, x, beta, A_log, initial_state, cu_seqlens):
+    N = _n_states(q, cu_seqlens)
+    return torch.empty_like(v), q.new_empty((N, v.shape[2], q.shape[3], v.shape[3]),
+                                            dtype=torch.float32)

@@ -145,3 +145,23 @@ def test_gate_bias_and_gate_bwd_reject_bad_arguments():
     assert bwd(dd=_dims(K=5000)) == 4
     assert lib.kda_gate_bwd(ctypes.byref(d), None, None, None, FAKE[3], None, FAKE[4], None, None,
                             None, 0, None) == 1
+
+
+def test_torch_ops_fake_shapes_on_meta_tensors():
+    """The torch.library registrations import without a GPU and their fake
+    implementations give the output shapes (dense and varlen, GVA)."""
+    import torch
+
+    import gated_delta_rule_69_amd.torch_ops  # noqa: F401
+
+    m = dict(device="meta")
+    q = torch.empty(1, 50, 2, 64, dtype=torch.bfloat16, **m)
+    v = torch.empty(1, 50, 4, 32, dtype=torch.bfloat16, **m)
+    x = torch.empty(1, 50, 4, 64, **m)
+    beta = torch.empty(1, 50, 4, dtype=torch.bfloat16, **m)
+    cu = torch.empty(4, dtype=torch.int32, **m)
+    o, ht = torch.ops.kda.chunk_kda_train(q, q, v, x, beta, None, None, None, cu)
+    assert o.shape == v.shape and o.dtype == v.dtype
+    assert ht.shape == (3, 4, 64, 32) and ht.dtype == torch.float32
+    o, ht = torch.ops.kda.recurrent_kda(q, q, v, x, beta, None, None, None)
+    assert o.shape == v.shape and ht.shape == (1, 4, 64, 32)
