@@ -11,7 +11,8 @@ Contents
                     softplus(x + dt_bias) (omitted A_log = unit scale, omitted
                     dt_bias = no bias), then the chunk-local inclusive cumsum
                     in log2 units; `gate_activation_bwd` its reverse (dx,
-                    dA_log, d_dt_bias).
+                    dA_log, d_dt_bias); `l2norm` the optional q/k
+                    normalisation of the fused forward.
   * `forms.py`      independent reformulations (single-chunk dense solve,
                     chunked UT form) used only to pin the recurrence.
 
@@ -156,6 +157,20 @@ def gate_activation_bwd(x: np.ndarray, A_log: Optional[np.ndarray],
     dA = None if A_log is None else (dg * g)[inside].sum(axis=(0, 2))
     db = None if dt_bias is None else dx_all[inside].sum(axis=0)
     return dx, dA, db
+
+
+# Stabiliser of the q/k normalisation. The pages name an l2norm step applied to
+# q and k before the scan ("kda in torchtitan (training)": the attention-gym
+# imports next to recurrent_kda) without printing it; the plainest reading is
+# x / sqrt(sum x^2 + eps) over the K channels of each (token, head), with eps
+# chosen here as 1e-6.
+L2NORM_EPS = 1e-6
+
+
+def l2norm(x: np.ndarray, eps: float = L2NORM_EPS) -> np.ndarray:
+    """x / sqrt(sum over the last axis of x^2 + eps), in FP64."""
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
 
 
 def seq_bounds(B: int, T: int, cu_seqlens: Optional[Sequence[int]]):

@@ -207,3 +207,38 @@ def test_gate_bwd_through_the_scan_matches_finite_differences(oracle):
         m[idx] -= eps
         fd = (loss(x, A_log, p) - loss(x, A_log, m)) / (2 * eps)
         assert abs(fd - db[idx]) <= 1e-6 * max(1.0, abs(fd)), (idx, fd, db[idx])
+
+
+# ---------------------------------------------------------------- q/k L2 normalisation
+
+def test_l2norm_hand_computed(oracle):
+    """(3, 4) has squared norm 25: y = (3, 4) / sqrt(25 + 1e-6)."""
+    y = oracle.l2norm(np.array([[3.0, 4.0]]))
+    s = 1.0 / math.sqrt(25.000001)
+    np.testing.assert_allclose(y, [[3.0 * s, 4.0 * s]], rtol=1e-15, atol=0)
+    assert abs(s - 0.2 * (1.0 - 2e-8)) < 1e-15
+
+
+def test_l2norm_properties(oracle):
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((5, 7, 3, 16)) * rng.uniform(0.01, 100.0, (5, 7, 3, 1))
+    y = oracle.l2norm(x)
+    n2 = np.sum(x * x, axis=-1)
+    # parallel to x, squared norm n2 / (n2 + eps), zero stays zero
+    np.testing.assert_allclose(np.sum(y * y, axis=-1), n2 / (n2 + oracle.L2NORM_EPS), rtol=1e-13)
+    cos = np.sum(y * x, axis=-1) / np.sqrt(np.sum(y * y, axis=-1) * n2)
+    np.testing.assert_allclose(cos, 1.0, rtol=1e-13)
+    assert (oracle.l2norm(np.zeros((2, 8))) == 0.0).all()
+
+
+def test_l2norm_of_unit_rows_changes_the_scan_by_eps_only(oracle):
+    """Inputs already of unit norm: normalising q and k moves the outputs by
+    O(eps); normalising v instead (a plausible slip) moves them by O(1)."""
+    import workloads
+    wl = workloads.tiny_case(12, B=1, T=40, H=1, HV=2, K=16, V=8)
+    g = oracle.gate_activation(wl.x, wl.A_log)
+    o1, h1 = oracle.recurrence(wl.q, wl.k, wl.v, g, wl.beta, wl.h0)
+    o2, h2 = oracle.recurrence(oracle.l2norm(wl.q), oracle.l2norm(wl.k), wl.v, g, wl.beta, wl.h0)
+    assert np.abs(o2 - o1).max() <= 1e-5 * np.abs(o1).max()
+    o3, _ = oracle.recurrence(wl.q, wl.k, oracle.l2norm(wl.v), g, wl.beta, wl.h0)
+    assert np.abs(o3 - o1).max() > 1e-2 * np.abs(o1).max()
