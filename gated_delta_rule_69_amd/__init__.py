@@ -35,7 +35,9 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE
 EXPORTED = ("kda_status_string", "kda_gate_cumsum", "kda_gate_cumsum_biased",
             "kda_gate_bwd_workspace_bytes", "kda_gate_bwd", "kda_chunk_fwd_workspace_bytes",
             "kda_chunk_fwd", "kda_chunk_fwd_fused_gate", "kda_chunk_bwd_workspace_bytes",
-            "kda_chunk_bwd", "kda_recurrent_fwd", "kda_recurrent_fwd_fused_gate")
+            "kda_chunk_bwd", "kda_recurrent_fwd", "kda_recurrent_fwd_fused_gate",
+            "kda_chunk_fwd_ex", "kda_recurrent_fwd_ex")
+KDA_GATE_LOG2, KDA_GATE_NAT, KDA_GATE_RAW = 0, 1, 2
 
 
 class KdaDims(ctypes.Structure):
@@ -85,6 +87,12 @@ def _lib():
         lib.kda_recurrent_fwd_fused_gate.argtypes = [dims, ctypes.c_int, p, p, p, p, i32, p, p, p, p,
                                                      i32, p, p, p]
         lib.kda_recurrent_fwd_fused_gate.restype = ctypes.c_int
+        lib.kda_chunk_fwd_ex.argtypes = [dims, ctypes.c_int, p, p, p, p, i32, p, i32, p, p, p, i32, i32,
+                                         p, p, p, sz, p]
+        lib.kda_chunk_fwd_ex.restype = ctypes.c_int
+        lib.kda_recurrent_fwd_ex.argtypes = [dims, ctypes.c_int, p, p, p, p, i32, p, i32, p, p, p, i32,
+                                             p, p, p]
+        lib.kda_recurrent_fwd_ex.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -202,13 +210,14 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
               output_final_state: bool = False, chunk_size: int = 64,
               o: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, use_gate_in_kernel: bool = False,
-              A_log: Optional[torch.Tensor] = None,
-              gate_is_raw: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              A_log: Optional[torch.Tensor] = None, gate_is_raw: bool = True,
+              qk_l2norm: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Steps A2..A6 (kda_chunk_fwd). `gate` is the chunk-local cumulative log2
     gate (gate_cumsum with the same chunk_size). With use_gate_in_kernel=True,
     `gate` is gate_cumsum's input instead (raw x with optional A_log, or the
     natural-log g if gate_is_raw=False) and the gate step runs inside the
-    chunk kernel (kda_chunk_fwd_fused_gate). Returns (o, final_state)."""
+    chunk kernel (kda_chunk_fwd_fused_gate). qk_l2norm=True normalises q and k
+    in the kernel (kda_chunk_fwd_ex). Returns (o, final_state)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"),
                  (initial_state, "initial_state"), (cu_seqlens, "cu_seqlens"), (A_log, "A_log")):
         _check(t, n)
@@ -225,6 +234,16 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     need = int(_lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(d), dt, int(chunk_size)))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    if qk_l2norm:
+        kind = (KDA_GATE_RAW if gate_is_raw else KDA_GATE_NAT) if use_gate_in_kernel else KDA_GATE_LOG2
+        rc = _lib().kda_chunk_fwd_ex(
+            ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), kind, _ptr(A_log), 1,
+            _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size),
+            int(bool(output_final_state)), _ptr(o), _ptr(final_state), _ptr(workspace),
+            workspace.numel(), _stream())
+        if rc:
+            raise KdaError("kda_chunk_fwd_ex", rc)
+        return o, final_state
     if use_gate_in_kernel:
         rc = _lib().kda_chunk_fwd_fused_gate(
             ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), int(bool(gate_is_raw)),
@@ -272,13 +291,14 @@ def chunk_kda_bwd(q, k, v, gate, beta, initial_state, do, dht=None, *, cu_seqlen
 def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
                   output_final_state: bool = False, o: Optional[torch.Tensor] = None,
                   final_state: Optional[torch.Tensor] = None, use_gate_in_kernel: bool = False,
-                  A_log: Optional[torch.Tensor] = None,
-                  gate_is_raw: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  A_log: Optional[torch.Tensor] = None, gate_is_raw: bool = True,
+                  qk_l2norm: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Step A7 (kda_recurrent_fwd). `gate` is the per-token log2 decay
     (gate_cumsum with chunk_size=1). With use_gate_in_kernel=True, `gate` is
     gate_cumsum's input instead (raw x with optional A_log, or the natural-log
     g if gate_is_raw=False), activated inside the scan kernel
-    (kda_recurrent_fwd_fused_gate). Inference only: inputs that require grad
+    (kda_recurrent_fwd_fused_gate). qk_l2norm=True normalises q and k in the
+    kernel (kda_recurrent_fwd_ex). Inference only: inputs that require grad
     are rejected (use chunk_kda for training). Pass final_state=initial_state
     to update the states in place."""
     if any(t is not None and t.requires_grad for t in (q, k, v, gate, beta, initial_state)):
@@ -296,6 +316,15 @@ def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
         final_state = torch.empty((d.N, d.HV, d.K, d.V), device=q.device, dtype=torch.float32)
     if not output_final_state:
         final_state = None
+    if qk_l2norm:
+        kind = (KDA_GATE_RAW if gate_is_raw else KDA_GATE_NAT) if use_gate_in_kernel else KDA_GATE_LOG2
+        rc = _lib().kda_recurrent_fwd_ex(
+            ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), kind, _ptr(A_log), 1,
+            _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), int(bool(output_final_state)), _ptr(o),
+            _ptr(final_state), _stream())
+        if rc:
+            raise KdaError("kda_recurrent_fwd_ex", rc)
+        return o, final_state
     if use_gate_in_kernel:
         rc = _lib().kda_recurrent_fwd_fused_gate(
             ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), int(bool(gate_is_raw)),

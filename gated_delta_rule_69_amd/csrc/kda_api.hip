@@ -69,7 +69,7 @@ kda_status check_scan(const kda_dims* d, kda_dtype dt, const void* q, const void
 
 kda_status chunk_fwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
                           const void* v, const float* gate, int gate_mode, const float* A_log,
-                          const void* beta, const float* h0, const int32_t* cu,
+                          int qk_norm, const void* beta, const float* h0, const int32_t* cu,
                           int32_t chunk_size, int32_t write_final, void* o, float* ht,
                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   kda_status st = check_scan(d, dt, q, k, v, gate, beta, h0, cu, write_final, o, ht);
@@ -94,7 +94,8 @@ kda_status chunk_fwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const 
       overlaps(workspace, need, gate, s.gate) || overlaps(workspace, need, beta, s.beta) ||
       overlaps(workspace, need, A_log, A_log ? (size_t)d->HV * 4 : 0))
     return KDA_ERR_ALIAS;
-  return kda_host::launch_chunk_fwd(*d, dt, q, k, v, gate, gate_mode, A_log, beta, h0, cu,
+  return kda_host::launch_chunk_fwd(*d, dt, q, k, v, gate, gate_mode, A_log, qk_norm ? 1 : 0,
+                                    beta, h0, cu,
                                     write_final ? 1 : 0, o, ht, workspace, workspace_bytes,
                                     stream) == hipSuccess
              ? KDA_OK
@@ -103,7 +104,7 @@ kda_status chunk_fwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const 
 
 kda_status recurrent_impl(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
                           const void* v, const float* gate, int gate_mode, const float* A_log,
-                          const void* beta, const float* h0, const int32_t* cu,
+                          int qk_norm, const void* beta, const float* h0, const int32_t* cu,
                           int32_t write_final, void* o, float* ht, hipStream_t stream) {
   kda_status st = check_scan(d, dt, q, k, v, gate, beta, h0, cu, write_final, o, ht);
   if (st != KDA_OK) return st;
@@ -113,7 +114,8 @@ kda_status recurrent_impl(const kda_dims* d, kda_dtype dt, const void* q, const 
                 overlaps(A_log, (size_t)d->HV * 4, ht, s.state)))
     return KDA_ERR_ALIAS;
   if (d->N == 0) return KDA_OK;
-  return kda_host::launch_recurrent(*d, dt, q, k, v, gate, gate_mode, A_log, beta, h0, cu,
+  return kda_host::launch_recurrent(*d, dt, q, k, v, gate, gate_mode, A_log, qk_norm ? 1 : 0,
+                                    beta, h0, cu,
                                     write_final ? 1 : 0, o, ht, stream) == hipSuccess
              ? KDA_OK
              : KDA_ERR_LAUNCH;
@@ -228,8 +230,8 @@ kda_status kda_chunk_fwd(const kda_dims* d, kda_dtype dt, const void* q, const v
                          const float* h0, const int32_t* cu, int32_t chunk_size,
                          int32_t write_final, void* o, float* ht, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
-  return chunk_fwd_impl(d, dt, q, k, v, gate, kda::kGateLog2, nullptr, beta, h0, cu, chunk_size,
-                        write_final, o, ht, workspace, workspace_bytes, stream);
+  return chunk_fwd_impl(d, dt, q, k, v, gate, kda::kGateLog2, nullptr, 0, beta, h0, cu,
+                        chunk_size, write_final, o, ht, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_chunk_fwd_fused_gate(const kda_dims* d, kda_dtype dt, const void* q,
@@ -240,8 +242,20 @@ kda_status kda_chunk_fwd_fused_gate(const kda_dims* d, kda_dtype dt, const void*
                                     size_t workspace_bytes, hipStream_t stream) {
   if (!gate_in_is_raw && A_log) return KDA_ERR_SHAPE;
   return chunk_fwd_impl(d, dt, q, k, v, gate_in, gate_in_is_raw ? kda::kGateRaw : kda::kGateLog,
-                        A_log, beta, h0, cu, chunk_size, write_final, o, ht, workspace,
+                        A_log, 0, beta, h0, cu, chunk_size, write_final, o, ht, workspace,
                         workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_ex(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                            const void* v, const float* gate, int32_t gate_kind,
+                            const float* A_log, int32_t qk_l2norm, const void* beta,
+                            const float* h0, const int32_t* cu, int32_t chunk_size,
+                            int32_t write_final, void* o, float* ht, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (gate_kind < KDA_GATE_LOG2 || gate_kind > KDA_GATE_RAW) return KDA_ERR_SHAPE;
+  if (gate_kind != KDA_GATE_RAW && A_log) return KDA_ERR_SHAPE;
+  return chunk_fwd_impl(d, dt, q, k, v, gate, (int)gate_kind, A_log, qk_l2norm != 0, beta, h0, cu,
+                        chunk_size, write_final, o, ht, workspace, workspace_bytes, stream);
 }
 
 size_t kda_chunk_bwd_workspace_bytes(const kda_dims* d, kda_dtype dt, int32_t chunk_size) {
@@ -298,8 +312,8 @@ kda_status kda_recurrent_fwd(const kda_dims* d, kda_dtype dt, const void* q, con
                              const void* v, const float* gate, const void* beta,
                              const float* h0, const int32_t* cu, int32_t write_final, void* o,
                              float* ht, hipStream_t stream) {
-  return recurrent_impl(d, dt, q, k, v, gate, kda::kGateLog2, nullptr, beta, h0, cu, write_final,
-                        o, ht, stream);
+  return recurrent_impl(d, dt, q, k, v, gate, kda::kGateLog2, nullptr, 0, beta, h0, cu,
+                        write_final, o, ht, stream);
 }
 
 kda_status kda_recurrent_fwd_fused_gate(const kda_dims* d, kda_dtype dt, const void* q,
@@ -310,7 +324,18 @@ kda_status kda_recurrent_fwd_fused_gate(const kda_dims* d, kda_dtype dt, const v
                                         hipStream_t stream) {
   if (!gate_in_is_raw && A_log) return KDA_ERR_SHAPE;
   return recurrent_impl(d, dt, q, k, v, gate_in, gate_in_is_raw ? kda::kGateRaw : kda::kGateLog,
-                        A_log, beta, h0, cu, write_final, o, ht, stream);
+                        A_log, 0, beta, h0, cu, write_final, o, ht, stream);
+}
+
+kda_status kda_recurrent_fwd_ex(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                                const void* v, const float* gate, int32_t gate_kind,
+                                const float* A_log, int32_t qk_l2norm, const void* beta,
+                                const float* h0, const int32_t* cu, int32_t write_final, void* o,
+                                float* ht, hipStream_t stream) {
+  if (gate_kind < KDA_GATE_LOG2 || gate_kind > KDA_GATE_RAW) return KDA_ERR_SHAPE;
+  if (gate_kind != KDA_GATE_RAW && A_log) return KDA_ERR_SHAPE;
+  return recurrent_impl(d, dt, q, k, v, gate, (int)gate_kind, A_log, qk_l2norm != 0, beta, h0, cu,
+                        write_final, o, ht, stream);
 }
 
 }  // extern "C"

@@ -65,7 +65,7 @@ size_t ws_bytes_t(const kda_dims& d, bool varlen) {
 
 template <typename T, int K, int V>
 hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const void* v,
-                       const float* gate, int gate_mode, const float* A_log, const void* beta,
+                       const float* gate, int gate_mode, const float* A_log, int qn, const void* beta,
                        const float* h0, const int32_t* cu, int write_final, void* o, float* ht,
                        void* ws, hipStream_t s) {
   const bool varlen = cu != nullptr;
@@ -84,7 +84,7 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
     const size_t lds = IntraLds<T, K, V>::total;
     hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, false>), dim3((unsigned)mc, (unsigned)d.HV),
                        dim3(kThreads), lds, s, (const T*)q, (const T*)k, (const T*)v, gate,
-                       gate_mode, A_log, (const T*)beta, cu, ws_int, d.N, d.T, d.H, d.HV,
+                       gate_mode, A_log, qn, (const T*)beta, cu, ws_int, d.N, d.T, d.H, d.HV,
                        1.0f / sqrtf((float)K), ws_T, ws_GL, (T*)nullptr, (float*)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -138,36 +138,36 @@ size_t chunk_workspace_bytes(const kda_dims& d, kda_dtype dt, int chunk) {
 
 template <typename T, int K, int V>
 static hipError_t run_kv(const kda_dims& d, const void* q, const void* k, const void* v,
-                         const float* gate, int gm, const float* A_log, const void* beta,
+                         const float* gate, int gm, const float* A_log, int qn, const void* beta,
                          const float* h0, const int32_t* cu, int write_final, void* o,
                          float* ht, void* ws, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)kda::IntraLds<T, K, V>::total);
   if (e != hipSuccess) return e;
-  return kda::chunk_fwd_t<T, K, V>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht,
+  return kda::chunk_fwd_t<T, K, V>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht,
                                    ws, s);
 }
 
 template <typename T>
 static hipError_t run_t(const kda_dims& d, const void* q, const void* k, const void* v,
-                        const float* gate, int gm, const float* A_log, const void* beta,
+                        const float* gate, int gm, const float* A_log, int qn, const void* beta,
                         const float* h0, const int32_t* cu, int write_final, void* o, float* ht,
                         void* ws, hipStream_t s) {
-  if (d.K == 64 && d.V == 64) return run_kv<T, 64, 64>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, ws, s);
-  if (d.K == 64 && d.V == 128) return run_kv<T, 64, 128>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, ws, s);
-  if (d.K == 128 && d.V == 64) return run_kv<T, 128, 64>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, ws, s);
-  if (d.K == 128 && d.V == 128) return run_kv<T, 128, 128>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, ws, s);
+  if (d.K == 64 && d.V == 64) return run_kv<T, 64, 64>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, ws, s);
+  if (d.K == 64 && d.V == 128) return run_kv<T, 64, 128>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, ws, s);
+  if (d.K == 128 && d.V == 64) return run_kv<T, 128, 64>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, ws, s);
+  if (d.K == 128 && d.V == 128) return run_kv<T, 128, 128>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, ws, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_fwd(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
                             const void* v, const float* gate, int gm, const float* A_log,
-                            const void* beta, const float* h0, const int32_t* cu,
+                            int qn, const void* beta, const float* h0, const int32_t* cu,
                             int write_final, void* o, float* ht, void* ws, size_t /*ws_bytes*/,
                             hipStream_t s) {
-  if (dt == KDA_BF16) return run_t<kda::bf16>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, ws, s);
-  return run_t<float>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, ws, s);
+  if (dt == KDA_BF16) return run_t<kda::bf16>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, ws, s);
+  return run_t<float>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, ws, s);
 }
 
 }  // namespace kda_host

@@ -153,6 +153,22 @@ __device__ __forceinline__ float unit_elem(const uint4& u, int e) {
   else return __uint_as_float(w);
 }
 
+// A 16-byte unit of T values, each multiplied by s (rounded back to T).
+template <typename T>
+__device__ __forceinline__ uint4 unit_scaled(const uint4& u, float s) {
+  uint4 r = u;
+  if constexpr (sizeof(T) == 2) {
+    bf16* x = reinterpret_cast<bf16*>(&r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * s);
+  } else {
+    float* x = reinterpret_cast<float*>(&r);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] *= s;
+  }
+  return r;
+}
+
 // Quad p of a contraction dimension holds indices 16p + 4g + e (e = 0..3) for
 // lane group g. With the kidx() order of MF<>, quad p is slots 4(p&1)..+3 of
 // bf16 fragment p/2, or FP32 fragments 4p..4p+3.
@@ -189,7 +205,7 @@ template <typename T, int K, int V, bool BWD>
 __global__ void __launch_bounds__(kThreads, 2)
 chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                    const float* __restrict__ gate, int gate_mode,
-                   const float* __restrict__ A_log, const T* __restrict__ beta,
+                   const float* __restrict__ A_log, int qk_norm, const T* __restrict__ beta,
                    const int32_t* __restrict__ cu, const int* __restrict__ ws_int, int N, int T_,
                    int H, int HV, float scale, T* __restrict__ ws_T, float* __restrict__ ws_GL,
                    T* __restrict__ ws_B, float* __restrict__ ws_Bf) {
@@ -250,6 +266,27 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     if (row < L) vr[u] = *reinterpret_cast<const uint4*>(v + ((t0 + row) * HV + hv) * V + EPU * cu_);
   }
   if (tid < kC) sBeta[tid] = tid < L ? to_f32(beta[(t0 + tid) * HV + hv]) : 0.f;
+  if (qk_norm) {
+    // the K / EPU threads holding a row of q and k are consecutive lanes
+    constexpr int TPR = K / EPU;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) {
+        const float a = unit_elem<T>(kr[u], e), b = unit_elem<T>(qr[u], e);
+        sk += a * a;
+        sq += b * b;
+      }
+#pragma unroll
+      for (int m = 1; m < TPR; m <<= 1) {
+        sk += __shfl_xor(sk, m);
+        sq += __shfl_xor(sq, m);
+      }
+      kr[u] = unit_scaled<T>(kr[u], l2norm_inv(sk));
+      qr[u] = unit_scaled<T>(qr[u], l2norm_inv(sq));
+    }
+  }
   if (gate_mode != kGateLog2) {
     // fused gate step: per-token natural-log gate first (cumsum below)
     const float sc = gate_head_scale(gate_mode, A_log, hv);

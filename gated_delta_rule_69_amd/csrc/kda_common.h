@@ -104,6 +104,14 @@ __device__ __forceinline__ float sigmoid_f32(float x) {
   return x > 20.f ? 1.f : r;
 }
 
+// Optional q/k normalisation: x / sqrt(sum over K of x^2 + kL2NormEps) per
+// (token, qk head), before any use of q and k.
+constexpr float kL2NormEps = 1e-6f;
+__device__ __forceinline__ float l2norm_inv(float sum_sq) {
+#pragma clang fp contract(off)
+  return 1.f / sqrtf(sum_sq + kL2NormEps);
+}
+
 // What a scan kernel's gate operand holds:
 //   kGateLog2: the log2 gate already prepared (per token for the recurrent
 //              scan, chunk-local inclusive cumsum G2 for the chunked scan);
@@ -162,12 +170,12 @@ hipError_t launch_gate_bwd(const kda_dims& d, const float* x, const float* A_log
                            float* dA_log, float* d_dt_bias, void* ws, hipStream_t s);
 hipError_t launch_recurrent(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
                             const void* v, const float* gate, int gate_mode, const float* A_log,
-                            const void* beta, const float* h0, const int32_t* cu,
+                            int qk_norm, const void* beta, const float* h0, const int32_t* cu,
                             int write_final, void* o, float* ht, hipStream_t s);
 size_t chunk_workspace_bytes(const kda_dims& d, kda_dtype dt, int chunk);
 hipError_t launch_chunk_fwd(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
                             const void* v, const float* gate, int gate_mode, const float* A_log,
-                            const void* beta, const float* h0, const int32_t* cu,
+                            int qk_norm, const void* beta, const float* h0, const int32_t* cu,
                             int write_final, void* o, float* ht, void* ws, size_t ws_bytes,
                             hipStream_t s);
 size_t chunk_bwd_workspace_bytes(const kda_dims& d, kda_dtype dt, int chunk);

@@ -52,11 +52,12 @@ template <typename T, int VEC, int ROWS>
 __global__ void __launch_bounds__(kRecThreads)
 recurrent_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                  const float* __restrict__ gate, int gate_mode, const float* __restrict__ A_log,
-                 const T* __restrict__ beta,
+                 int qk_norm, const T* __restrict__ beta,
                  const float* h0, const int32_t* __restrict__ cu, int Tlen, int H, int HV, int K,
                  int V, int BV, float scale, int write_final, T* __restrict__ o, float* ht) {
   extern __shared__ float smem[];
-  // LDS: k[K], q~[K], decay[K], then partials [RG][TPR][2*VEC+1], then delta/final [BV]
+  // LDS: k[K], q~[K], decay[K], then partials [RG][TPR][PW], then delta/final [BV]
+  constexpr int PW = 2 * VEC + 3;  // u, w, k.q~, |k|^2, |q~|^2
   float* s_k = smem;
   float* s_q = s_k + K;
   float* s_d = s_q + K;
@@ -73,7 +74,7 @@ recurrent_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   const int h = hv / (HV / H);
   const int col0 = blockIdx.y * BV + cg * VEC;
   const bool col_ok = active && col0 < V;  // V % VEC == 0, so the whole vector is in range
-  float* s_fin = s_part + (size_t)RG * TPR * (2 * VEC + 1);
+  float* s_fin = s_part + (size_t)RG * TPR * PW;
 
   int64_t bos;
   int len;
@@ -115,7 +116,7 @@ recurrent_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
       s_d[c] = exp2f(gate_log2_token(gate[(t * HV + hv) * K + c], gate_mode, gscale));
     }
     __syncthreads();
-    float pu[VEC], pw[VEC], pkq = 0.f;
+    float pu[VEC], pw[VEC], pkq = 0.f, pkk = 0.f, pqq = 0.f;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) pu[e] = pw[e] = 0.f;
 #pragma unroll
@@ -124,6 +125,8 @@ recurrent_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
       if (r < K) {
         const float d = s_d[r], kr = s_k[r], qr = s_q[r];
         pkq += kr * qr;
+        pkk += kr * kr;  // row norms: one thread per row group counts them (cg == 0)
+        pqq += qr * qr;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           s[i][e] *= d;
@@ -133,34 +136,51 @@ recurrent_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
       }
     }
     if (active) {
-      float* p = s_part + ((size_t)rg * TPR + cg) * (2 * VEC + 1);
+      float* p = s_part + ((size_t)rg * TPR + cg) * PW;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         p[e] = pu[e];
         p[VEC + e] = pw[e];
       }
       p[2 * VEC] = pkq;
+      p[2 * VEC + 1] = pkk;
+      p[2 * VEC + 2] = pqq;
     }
     __syncthreads();
     if (tid < TPR && col0 < V) {
-      float u[VEC], w[VEC], kq = 0.f;
+      float u[VEC], w[VEC], kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) u[e] = w[e] = 0.f;
       for (int g = 0; g < RG; ++g) {
-        const float* p = s_part + ((size_t)g * TPR + cg) * (2 * VEC + 1);
+        const float* p = s_part + ((size_t)g * TPR + cg) * PW;
+        const float* p0 = s_part + ((size_t)g * TPR) * PW;  // column group 0 of the row group
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           u[e] += p[e];
           w[e] += p[VEC + e];
         }
         kq += p[2 * VEC];
+        kk += p0[2 * VEC + 1];
+        qq += p0[2 * VEC + 2];
+      }
+      // optional q/k normalisation (q~ = q * scale, so |q|^2 = |q~|^2 / scale^2)
+      float rk = 1.f;
+      if (qk_norm) {
+        rk = l2norm_inv(kk);
+        const float rq = l2norm_inv(qq / (scale * scale));
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          u[e] *= rk;
+          w[e] *= rq;
+        }
+        kq *= rk * rq;
       }
       const float b = to_f32(beta[t * HV + hv]);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float vv = to_f32(v[(t * HV + hv) * V + col0 + e]);
         const float dl = b * (vv - u[e]);
-        s_fin[cg * VEC + e] = dl;
+        s_fin[cg * VEC + e] = dl * rk;  // the update takes the normalised k
         o[(t * HV + hv) * V + col0 + e] = from_f32<T>(w[e] + dl * kq);
       }
     }
@@ -278,7 +298,7 @@ template <typename T, int K>
 __global__ void __launch_bounds__(kRecThreads)
 recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                       const float* __restrict__ gate, int gate_mode,
-                      const float* __restrict__ A_log, const T* __restrict__ beta,
+                      const float* __restrict__ A_log, int qk_norm, const T* __restrict__ beta,
                       const float* h0, const int32_t* __restrict__ cu, int Tlen, int H, int HV,
                       int V, int n_cb, int64_t n_tasks, float scale, int write_final,
                       T* __restrict__ o, float* ht) {
@@ -356,10 +376,12 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     float dloc[NPL];
 #pragma unroll
     for (int m = 0; m < NPL; ++m) dloc[m] = exp2f(gate_log2_token(gf[m], gate_mode, gscale));
-    float u[4] = {0.f, 0.f, 0.f, 0.f}, w[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f;
+    float u[4] = {0.f, 0.f, 0.f, 0.f}, w[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
       const float d = __shfl(dloc[i % NPL], rl * CL + i / NPL);
+      kk += kf[i] * kf[i];
+      qq += qf[i] * qf[i];
       qf[i] *= scale;
       kq += kf[i] * qf[i];
 #pragma unroll
@@ -377,6 +399,23 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
         w[e] += __shfl_xor(w[e], m);
       }
       kq += __shfl_xor(kq, m);
+      if (qk_norm) {
+        kk += __shfl_xor(kk, m);
+        qq += __shfl_xor(qq, m);
+      }
+    }
+    // optional q/k normalisation, applied to the reduced terms (u and the update
+    // are linear in k, w in q, k.q~ in both)
+    float rk = 1.f;
+    if (qk_norm) {
+      rk = l2norm_inv(kk);
+      const float rq = l2norm_inv(qq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u[e] *= rk;
+        w[e] *= rq;
+      }
+      kq *= rk * rq;
     }
     const float b = to_f32(x.b);
     float dl[4], r[4];
@@ -384,6 +423,7 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     for (int e = 0; e < 4; ++e) {
       dl[e] = b * (vf[e] - u[e]);
       r[e] = w[e] + dl[e] * kq;
+      dl[e] *= rk;
     }
     if (rl == 0 && col_ok) store_o4(o + (t * HV + hv) * V + col, r);
 #pragma unroll
@@ -413,7 +453,7 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
 
 template <typename T, int K>
 static hipError_t launch_rec_wave(const kda_dims& d, const void* q, const void* k, const void* v,
-                                  const float* gate, int gm, const float* A_log, const void* beta,
+                                  const float* gate, int gm, const float* A_log, int qn, const void* beta,
                                   const float* h0, const int32_t* cu, int write_final, void* o,
                                   float* ht, hipStream_t s) {
   const int n_cb = (d.V + WaveGeo<K>::CW - 1) / WaveGeo<K>::CW;
@@ -421,7 +461,7 @@ static hipError_t launch_rec_wave(const kda_dims& d, const void* q, const void* 
   const int wpb = kRecThreads / 64;
   dim3 grid((unsigned)((n_tasks + wpb - 1) / wpb));
   hipLaunchKernelGGL((recurrent_wave_kernel<T, K>), grid, dim3(kRecThreads), 0, s, (const T*)q,
-                     (const T*)k, (const T*)v, gate, gm, A_log, (const T*)beta, h0, cu, d.T, d.H,
+                     (const T*)k, (const T*)v, gate, gm, A_log, qn, (const T*)beta, h0, cu, d.T, d.H,
                      d.HV, d.V,
                      n_cb, n_tasks, 1.0f / sqrtf((float)d.K), write_final, (T*)o, ht);
   return hipGetLastError();
@@ -429,15 +469,15 @@ static hipError_t launch_rec_wave(const kda_dims& d, const void* q, const void* 
 
 template <typename T, int VEC, int ROWS>
 static hipError_t launch_rec_t(const kda_dims& d, const void* q, const void* k, const void* v,
-                               const float* gate, int gm, const float* A_log, const void* beta,
+                               const float* gate, int gm, const float* A_log, int qn, const void* beta,
                                const float* h0,
                                const int32_t* cu, int write_final, void* o, float* ht, int BV,
                                hipStream_t s) {
   const int TPR = BV / VEC, RG = kRecThreads / TPR;
-  size_t lds = sizeof(float) * (3 * (size_t)d.K + (size_t)RG * TPR * (2 * VEC + 1) + BV);
+  size_t lds = sizeof(float) * (3 * (size_t)d.K + (size_t)RG * TPR * (2 * VEC + 3) + BV);
   dim3 grid((unsigned)(d.N * d.HV), (unsigned)((d.V + BV - 1) / BV));
   hipLaunchKernelGGL((recurrent_kernel<T, VEC, ROWS>), grid, dim3(kRecThreads), lds, s,
-                     (const T*)q, (const T*)k, (const T*)v, gate, gm, A_log, (const T*)beta, h0, cu,
+                     (const T*)q, (const T*)k, (const T*)v, gate, gm, A_log, qn, (const T*)beta, h0, cu,
                      d.T,
                      d.H, d.HV, d.K, d.V, BV, 1.0f / sqrtf((float)d.K), write_final, (T*)o, ht);
   return hipGetLastError();
@@ -445,7 +485,7 @@ static hipError_t launch_rec_t(const kda_dims& d, const void* q, const void* k, 
 
 template <typename T, int VEC>
 static hipError_t launch_rec_v(const kda_dims& d, const void* q, const void* k, const void* v,
-                               const float* gate, int gm, const float* A_log, const void* beta,
+                               const float* gate, int gm, const float* A_log, int qn, const void* beta,
                                const float* h0,
                                const int32_t* cu, int write_final, void* o, float* ht,
                                hipStream_t s) {
@@ -454,10 +494,10 @@ static hipError_t launch_rec_v(const kda_dims& d, const void* q, const void* k, 
   if (BV > d.V) BV = ((d.V + VEC - 1) / VEC) * VEC;
   const int TPR = BV / VEC, RG = kRecThreads / TPR;
   const int rows = (d.K + RG - 1) / RG;
-  if (rows <= 4) return launch_rec_t<T, VEC, 4>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, BV, s);
-  if (rows <= 8) return launch_rec_t<T, VEC, 8>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, BV, s);
-  if (rows <= 16) return launch_rec_t<T, VEC, 16>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, BV, s);
-  return launch_rec_t<T, VEC, 32>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, BV, s);
+  if (rows <= 4) return launch_rec_t<T, VEC, 4>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, BV, s);
+  if (rows <= 8) return launch_rec_t<T, VEC, 8>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, BV, s);
+  if (rows <= 16) return launch_rec_t<T, VEC, 16>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, BV, s);
+  return launch_rec_t<T, VEC, 32>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, BV, s);
 }
 
 }  // namespace kda
@@ -466,7 +506,7 @@ namespace kda_host {
 
 hipError_t launch_recurrent(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
                             const void* v, const float* gate, int gm, const float* A_log,
-                            const void* beta, const float* h0, const int32_t* cu,
+                            int qn, const void* beta, const float* h0, const int32_t* cu,
                             int write_final, void* o, float* ht, hipStream_t s) {
   if (d.N == 0) return hipSuccess;
   auto al = [](const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; };
@@ -477,9 +517,9 @@ hipError_t launch_recurrent(const kda_dims& d, kda_dtype dt, const void* q, cons
   if (wave_ok) {
 #define KDA_REC_WAVE(T_)                                                                     \
   switch (d.K) {                                                                             \
-    case 64: return kda::launch_rec_wave<T_, 64>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);   \
-    case 128: return kda::launch_rec_wave<T_, 128>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s); \
-    default: return kda::launch_rec_wave<T_, 256>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);  \
+    case 64: return kda::launch_rec_wave<T_, 64>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, s);   \
+    case 128: return kda::launch_rec_wave<T_, 128>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, s); \
+    default: return kda::launch_rec_wave<T_, 256>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, s);  \
   }
     if (dt == KDA_BF16) {
       KDA_REC_WAVE(kda::bf16)
@@ -491,13 +531,13 @@ hipError_t launch_recurrent(const kda_dims& d, kda_dtype dt, const void* q, cons
   const bool st_al16 = ((uintptr_t)h0 % 16 == 0) && ((uintptr_t)ht % 16 == 0);
   const int vec = (d.V % 4 == 0 && st_al16) ? 4 : (d.V % 2 == 0 ? 2 : 1);
   if (dt == KDA_BF16) {
-    if (vec == 4) return kda::launch_rec_v<kda::bf16, 4>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);
-    if (vec == 2) return kda::launch_rec_v<kda::bf16, 2>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);
-    return kda::launch_rec_v<kda::bf16, 1>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);
+    if (vec == 4) return kda::launch_rec_v<kda::bf16, 4>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, s);
+    if (vec == 2) return kda::launch_rec_v<kda::bf16, 2>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, s);
+    return kda::launch_rec_v<kda::bf16, 1>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, s);
   }
-  if (vec == 4) return kda::launch_rec_v<float, 4>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);
-  if (vec == 2) return kda::launch_rec_v<float, 2>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);
-  return kda::launch_rec_v<float, 1>(d, q, k, v, gate, gm, A_log, beta, h0, cu, write_final, o, ht, s);
+  if (vec == 4) return kda::launch_rec_v<float, 4>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, s);
+  if (vec == 2) return kda::launch_rec_v<float, 2>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, s);
+  return kda::launch_rec_v<float, 1>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, s);
 }
 
 }  // namespace kda_host

@@ -68,6 +68,13 @@ typedef enum {
 /* Element type of q, k, v, beta and o. States and gates are always FP32. */
 typedef enum { KDA_FP32 = 0, KDA_BF16 = 1 } kda_dtype;
 
+/* What the gate operand of kda_chunk_fwd_ex / kda_recurrent_fwd_ex holds:
+ *   KDA_GATE_LOG2  the prepared log2 gate (kda_gate_cumsum output: chunk-local
+ *                  cumsum for the chunked op, chunk_size 1 for the recurrent one);
+ *   KDA_GATE_NAT   the per-token natural-log gate g (cumsum formed in the kernel);
+ *   KDA_GATE_RAW   the raw activation input x, g = -exp(A_log) * softplus(x). */
+typedef enum { KDA_GATE_LOG2 = 0, KDA_GATE_NAT = 1, KDA_GATE_RAW = 2 } kda_gate_kind;
+
 /* Problem sizes. T is the physical token extent per batch row (the capacity
  * in varlen mode); N is the number of state entries (B dense, len(cu)-1 varlen). */
 typedef struct {
@@ -197,6 +204,27 @@ kda_status kda_chunk_fwd_fused_gate(const kda_dims* dims, kda_dtype dtype, const
                                     float* final_state, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/*
+ * kda_chunk_fwd_ex -- kda_chunk_fwd / kda_chunk_fwd_fused_gate with the gate
+ * kind as an argument and optional q/k L2 normalisation (the pages' l2norm
+ * pre-processing step, "kda in torchtitan (training)", fused into the loads):
+ *   gate_kind  kda_gate_kind; A_log only with KDA_GATE_RAW (else KDA_ERR_SHAPE).
+ *   qk_l2norm  nonzero: q and k are used as x / sqrt(sum over K of x^2 + 1e-6)
+ *              per (token, qk head), computed in FP32 from the input (bf16
+ *              inputs: the normalised rows are rounded to bf16 before the
+ *              matrix products, as a separate normalisation pass would store them).
+ * With qk_l2norm == 0 the results are bit-identical to kda_chunk_fwd
+ * (KDA_GATE_LOG2) and kda_chunk_fwd_fused_gate (the other kinds). No backward
+ * counterpart: kda_chunk_bwd expects normalised inputs.
+ */
+kda_status kda_chunk_fwd_ex(const kda_dims* dims, kda_dtype dtype, const void* q, const void* k,
+                            const void* v, const float* gate, int32_t gate_kind,
+                            const float* A_log, int32_t qk_l2norm, const void* beta,
+                            const float* initial_state, const int32_t* cu_seqlens,
+                            int32_t chunk_size, int32_t output_final_state, void* o,
+                            float* final_state, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* Workspace bytes kda_chunk_bwd needs for these sizes (0 on unsupported input). */
 size_t kda_chunk_bwd_workspace_bytes(const kda_dims* dims, kda_dtype dtype, int32_t chunk_size);
 
@@ -253,6 +281,19 @@ kda_status kda_recurrent_fwd_fused_gate(const kda_dims* dims, kda_dtype dtype, c
                                         const void* beta, const float* initial_state,
                                         const int32_t* cu_seqlens, int32_t output_final_state,
                                         void* o, float* final_state, hipStream_t stream);
+
+/*
+ * kda_recurrent_fwd_ex -- kda_recurrent_fwd / kda_recurrent_fwd_fused_gate with
+ * the gate kind as an argument and optional q/k L2 normalisation, as
+ * kda_chunk_fwd_ex (normalisation in FP32, reduced with the scan's own
+ * reductions). With qk_l2norm == 0 bit-identical to those entry points.
+ */
+kda_status kda_recurrent_fwd_ex(const kda_dims* dims, kda_dtype dtype, const void* q,
+                                const void* k, const void* v, const float* gate,
+                                int32_t gate_kind, const float* A_log, int32_t qk_l2norm,
+                                const void* beta, const float* initial_state,
+                                const int32_t* cu_seqlens, int32_t output_final_state, void* o,
+                                float* final_state, hipStream_t stream);
 
 #ifdef __cplusplus
 }

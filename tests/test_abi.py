@@ -165,3 +165,21 @@ def test_torch_ops_fake_shapes_on_meta_tensors():
     assert ht.shape == (3, 4, 64, 32) and ht.dtype == torch.float32
     o, ht = torch.ops.kda.recurrent_kda(q, q, v, x, beta, None, None, None)
     assert o.shape == v.shape and ht.shape == (1, 4, 64, 32)
+
+
+def test_ex_entries_reject_bad_arguments():
+    lib = kda.load()
+    d = _dims()
+
+    def chunk(kind, A_log):
+        return lib.kda_chunk_fwd_ex(ctypes.byref(d), 1, FAKE[0], FAKE[1], FAKE[2], FAKE[3], kind,
+                                    A_log, 1, FAKE[4], None, None, 64, 1, FAKE[5], FAKE[6], FAKE[7],
+                                    1 << 40, None)
+
+    def rec(kind, A_log):
+        return lib.kda_recurrent_fwd_ex(ctypes.byref(d), 1, FAKE[0], FAKE[1], FAKE[2], FAKE[3], kind,
+                                        A_log, 1, FAKE[4], None, None, 1, FAKE[5], FAKE[6], None)
+
+    assert chunk(3, None) == 2 and rec(-1, None) == 2          # unknown gate kind
+    assert chunk(0, FAKE[9]) == 2 and rec(1, FAKE[9]) == 2     # A_log only with a raw gate
+    assert chunk(2, FAKE[5]) == 5                              # A_log overlaps o
