@@ -250,6 +250,16 @@ def main():
     _, g_ms = timed_region(gate_call, a.steps, a.warmup)
     _, c_ms = timed_region(chunk_call, a.steps, a.warmup)
 
+    # the same call from raw q, k normalised in the kernel (kda_chunk_fwd_ex); a
+    # separate normalisation pass would read and write q and k once more
+    qr, kr = q * 3.0, k * 0.5
+
+    def step_norm():
+        kda.chunk_kda(qr, kr, v, x, beta, None, output_final_state=True, o=o, final_state=ht,
+                      workspace=ws, use_gate_in_kernel=True, A_log=A_log, qk_l2norm=True)
+    _, n_ms = timed_region(step_norm, a.steps, a.warmup)
+    del qr, kr
+
     cb = chunk_fwd_bytes(B, T, H, HV, K, V)
     gb = gate_bytes(B, T, HV, K)
     fused_gbs = cb / (f_ms * 1e-3) / 1e9
@@ -441,6 +451,9 @@ def main():
         "two_call_path_ms": {"kda_gate_cumsum": round(g_ms, 4), "kda_chunk_fwd": round(c_ms, 4),
                              "sum": round(g_ms + c_ms, 4), "gate_GBps": round(gate_gbs, 1),
                              "chunk_fwd_GBps": round(chunk_gbs, 1)},
+        "fused_qk_l2norm": {"entry": "kda_chunk_fwd_ex (raw q, k normalised in the kernel)",
+                            "ms": round(n_ms, 4), "plain_ms": round(f_ms, 4),
+                            "separate_pass_bytes": 2 * 2 * B * T * H * K * 2},
         "roofline": roof,
         "decode": {"workload": "recurrent_kda decode: 256 slots (26 empty), 1 token each, H=16 "
                                "HV=32 K=V=128 bf16, FP32 state in place, raw gate activated in "

@@ -82,10 +82,15 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
   }
   if (mc > 0) {
     const size_t lds = IntraLds<T, K, V>::total;
-    hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, false>), dim3((unsigned)mc, (unsigned)d.HV),
-                       dim3(kThreads), lds, s, (const T*)q, (const T*)k, (const T*)v, gate,
-                       gate_mode, A_log, qn, (const T*)beta, cu, ws_int, d.N, d.T, d.H, d.HV,
-                       1.0f / sqrtf((float)K), ws_T, ws_GL, (T*)nullptr, (float*)nullptr);
+    auto launch_intra = [&](auto qnc) {
+      constexpr bool QN = decltype(qnc)::value;
+      hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, false, QN>), dim3((unsigned)mc, (unsigned)d.HV),
+                         dim3(kThreads), lds, s, (const T*)q, (const T*)k, (const T*)v, gate,
+                         gate_mode, A_log, (const T*)beta, cu, ws_int, d.N, d.T, d.H, d.HV,
+                         1.0f / sqrtf((float)K), ws_T, ws_GL, (T*)nullptr, (float*)nullptr);
+    };
+    if (qn) launch_intra(std::true_type());
+    else launch_intra(std::false_type());
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -141,9 +146,12 @@ static hipError_t run_kv(const kda_dims& d, const void* q, const void* k, const 
                          const float* gate, int gm, const float* A_log, int qn, const void* beta,
                          const float* h0, const int32_t* cu, int write_final, void* o,
                          float* ht, void* ws, hipStream_t s) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)kda::IntraLds<T, K, V>::total);
+  const int lds = (int)kda::IntraLds<T, K, V>::total;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, false>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   return kda::chunk_fwd_t<T, K, V>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht,
                                    ws, s);

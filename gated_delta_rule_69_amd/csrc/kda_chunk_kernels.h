@@ -200,12 +200,14 @@ __device__ __forceinline__ int acc_elem(int ks, int jj) {
 constexpr float kFastRange = 112.f;
 
 // BWD: also write what the backward pass needs (P^T, Khat, (Q~ Gamma)^T and
-// W^T fragments, Abar and T) into ws_B / ws_Bf.
-template <typename T, int K, int V, bool BWD>
+// W^T fragments, Abar and T) into ws_B / ws_Bf.  QN: L2-normalise the q and k
+// rows as they are loaded (a template flag: the runtime branch alone cost the
+// plain path a few percent in registers and scheduling).
+template <typename T, int K, int V, bool BWD, bool QN>
 __global__ void __launch_bounds__(kThreads, 2)
 chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                    const float* __restrict__ gate, int gate_mode,
-                   const float* __restrict__ A_log, int qk_norm, const T* __restrict__ beta,
+                   const float* __restrict__ A_log, const T* __restrict__ beta,
                    const int32_t* __restrict__ cu, const int* __restrict__ ws_int, int N, int T_,
                    int H, int HV, float scale, T* __restrict__ ws_T, float* __restrict__ ws_GL,
                    T* __restrict__ ws_B, float* __restrict__ ws_Bf) {
@@ -266,7 +268,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     if (row < L) vr[u] = *reinterpret_cast<const uint4*>(v + ((t0 + row) * HV + hv) * V + EPU * cu_);
   }
   if (tid < kC) sBeta[tid] = tid < L ? to_f32(beta[(t0 + tid) * HV + hv]) : 0.f;
-  if (qk_norm) {
+  if constexpr (QN) {
     // the K / EPU threads holding a row of q and k are consecutive lanes
     constexpr int TPR = K / EPU;
 #pragma unroll
