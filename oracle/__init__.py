@@ -12,7 +12,9 @@ Contents
                     dt_bias = no bias), then the chunk-local inclusive cumsum
                     in log2 units; `gate_activation_bwd` its reverse (dx,
                     dA_log, d_dt_bias); `l2norm` the optional q/k
-                    normalisation of the fused forward.
+                    normalisation of the fused forward; `short_conv_silu`
+                    the short causal convolution + SiLU of q, k and v, and
+                    `preprocess` the two in the layer's order.
   * `forms.py`      independent reformulations (single-chunk dense solve,
                     chunked UT form) used only to pin the recurrence.
 
@@ -171,6 +173,69 @@ def l2norm(x: np.ndarray, eps: float = L2NORM_EPS) -> np.ndarray:
     """x / sqrt(sum over the last axis of x^2 + eps), in FP64."""
     x = _f64(x)
     return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU z * logistic(z) = z / (1 + exp(-z)), in FP64 (no threshold)."""
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+# Widths of the short convolution the fused forward accepts. The pages name a
+# short causal depthwise convolution followed by SiLU on q, k and v
+# (ShortConvolution and causal_conv1d_silu imports on the Paddle compatibility
+# page and the torchtitan training page) without printing it.
+CONV_MAX_WIDTH = 4
+
+
+def short_conv_silu(x: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray],
+                    cu_seqlens=None) -> np.ndarray:
+    """Causal depthwise convolution along the tokens of each sequence, then SiLU.
+
+    x: [B, T, D] (any trailing shape is flattened to D channels); weight
+    [D, W]; bias [D] or None. Reading of the pages' ShortConvolution: a
+    PyTorch Conv1d cross-correlation per channel with W - 1 zeros of history in
+    front of every sequence, so weight[c, W - 1] multiplies the current token:
+        z[t, c] = bias[c] + sum_{j<W} weight[c, j] * x[t - (W - 1) + j, c]
+        y[t, c] = silu(z[t, c]),
+    with x taken as zero before the sequence's first token. Sequences are the
+    batch rows (dense) or [cu[n], cu[n+1]) of the packed rows (varlen); tokens
+    outside every sequence are NaN."""
+    x = _f64(x)
+    B, T = x.shape[:2]
+    D = int(np.prod(x.shape[2:]))
+    w = _f64(weight).reshape(D, -1)
+    W = w.shape[1]
+    b = np.zeros(D) if bias is None else _f64(bias).reshape(D)
+    flat = x.reshape(B * T, D)
+    out = np.full_like(flat, np.nan)
+    for bos, eos in seq_bounds(B, T, cu_seqlens):
+        for t in range(bos, eos):
+            z = b.copy()
+            for j in range(W):
+                src = t - (W - 1) + j
+                if src >= bos:
+                    z = z + w[:, j] * flat[src]
+            out[t] = silu(z)
+    return out.reshape(x.shape)
+
+
+def preprocess(q: np.ndarray, k: np.ndarray, v: np.ndarray, conv=None, qk_l2norm: bool = False,
+               cu_seqlens=None):
+    """The pre-processing the fused forward applies before the scan: the short
+    convolution + SiLU of q, k and v (conv = ((wq, bq), (wk, bk), (wv, bv)) or
+    None), then the optional q/k L2 normalisation (after the convolution, as
+    the layer applies them). Returns (q, k, v) in FP64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if conv is not None:
+        (wq, bq), (wk, bk), (wv, bv) = conv
+        q = short_conv_silu(q, wq, bq, cu_seqlens)
+        k = short_conv_silu(k, wk, bk, cu_seqlens)
+        v = short_conv_silu(v, wv, bv, cu_seqlens)
+    if qk_l2norm:
+        q, k = l2norm(q), l2norm(k)
+    return q, k, v
 
 
 def seq_bounds(B: int, T: int, cu_seqlens: Optional[Sequence[int]]):
