@@ -65,8 +65,8 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--skip-extra", action="store_true", help="skip the context workloads")
-    p.add_argument("--profile", choices=["dense", "dense2", "decode", "decode2", "long", "gatebwd",
-                                         "copy"],
+    p.add_argument("--profile", choices=["dense", "dense2", "dense_conv", "decode", "decode2", "long",
+                                         "gatebwd", "copy"],
                    default=None,
                    help="run only one workload a few times (for rocprofv3), print no JSON")
     p.add_argument("--profile-reps", type=int, default=3)
@@ -104,6 +104,16 @@ def profile_only(a):
             else:
                 kda.gate_cumsum(x, A, None, 64, out=G)
                 kda.chunk_kda(q, k, v, G, b, None, output_final_state=True)
+    elif a.profile == "dense_conv":
+        # raw projections through the fused short convolution (width 4, biases)
+        # and q/k normalisation, gate in the kernel
+        wl, taps = workloads.with_raw_projections(workloads.workload2(), 850, 4, True)
+        q, k, v, b = T_(wl.q, bf), T_(wl.k, bf), T_(wl.v, bf), T_(wl.beta, bf)
+        x, A = T_(wl.x), T_(wl.A_log)
+        tp = tuple((T_(w), T_(bb)) for w, bb in taps)
+        for _ in range(a.profile_reps):
+            kda.chunk_kda(q, k, v, x, b, None, output_final_state=True, use_gate_in_kernel=True,
+                          A_log=A, qk_l2norm=True, short_conv=tp)
     elif a.profile in ("decode", "decode2"):
         wd = workloads.workload4()
         q, k, v, b = T_(wd.q, bf), T_(wd.k, bf), T_(wd.v, bf), T_(wd.beta, bf)
@@ -258,7 +268,20 @@ def main():
         kda.chunk_kda(qr, kr, v, x, beta, None, output_final_state=True, o=o, final_state=ht,
                       workspace=ws, use_gate_in_kernel=True, A_log=A_log, qk_l2norm=True)
     _, n_ms = timed_region(step_norm, a.steps, a.warmup)
-    del qr, kr
+
+    # raw q, k, v through the short convolution (width 4, biases) + SiLU and
+    # the q/k normalisation in the kernel (kda_chunk_fwd_conv); a separate
+    # pre-processing pass would read and write q, k and v once more
+    cgen = torch.Generator(device=dev).manual_seed(850)
+    taps = tuple(((torch.rand(D, 4, device=dev, generator=cgen) - 0.5),
+                  (torch.rand(D, device=dev, generator=cgen) - 0.5)) for D in (H * K, H * K, HV * V))
+
+    def step_conv():
+        kda.chunk_kda(qr, kr, v, x, beta, None, output_final_state=True, o=o, final_state=ht,
+                      workspace=ws, use_gate_in_kernel=True, A_log=A_log, qk_l2norm=True,
+                      short_conv=taps)
+    _, cv_ms = timed_region(step_conv, a.steps, a.warmup)
+    del qr, kr, taps
 
     cb = chunk_fwd_bytes(B, T, H, HV, K, V)
     gb = gate_bytes(B, T, HV, K)
@@ -454,6 +477,10 @@ def main():
         "fused_qk_l2norm": {"entry": "kda_chunk_fwd_ex (raw q, k normalised in the kernel)",
                             "ms": round(n_ms, 4), "plain_ms": round(f_ms, 4),
                             "separate_pass_bytes": 2 * 2 * B * T * H * K * 2},
+        "fused_short_conv": {"entry": "kda_chunk_fwd_conv (raw q, k, v: width-4 causal convolution "
+                                      "+ bias + SiLU, then q/k L2 norm, in the kernel)",
+                             "ms": round(cv_ms, 4), "plain_ms": round(f_ms, 4),
+                             "separate_pass_bytes": 2 * (2 * B * T * H * K + B * T * HV * V) * 2},
         "roofline": roof,
         "decode": {"workload": "recurrent_kda decode: 256 slots (26 empty), 1 token each, H=16 "
                                "HV=32 K=V=128 bf16, FP32 state in place, raw gate activated in "

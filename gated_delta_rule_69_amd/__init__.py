@@ -36,12 +36,20 @@ EXPORTED = ("kda_status_string", "kda_gate_cumsum", "kda_gate_cumsum_biased",
             "kda_gate_bwd_workspace_bytes", "kda_gate_bwd", "kda_chunk_fwd_workspace_bytes",
             "kda_chunk_fwd", "kda_chunk_fwd_fused_gate", "kda_chunk_bwd_workspace_bytes",
             "kda_chunk_bwd", "kda_recurrent_fwd", "kda_recurrent_fwd_fused_gate",
-            "kda_chunk_fwd_ex", "kda_recurrent_fwd_ex")
+            "kda_chunk_fwd_ex", "kda_recurrent_fwd_ex", "kda_chunk_fwd_conv")
 KDA_GATE_LOG2, KDA_GATE_NAT, KDA_GATE_RAW = 0, 1, 2
 
 
 class KdaDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("B", "T", "N", "H", "HV", "K", "V")]
+
+
+class KdaShortConv(ctypes.Structure):
+    """kda_short_conv: FP32 taps [channels, width] and optional biases of the
+    short convolution applied to q, k and v."""
+    _fields_ = [("q_weight", ctypes.c_void_p), ("k_weight", ctypes.c_void_p),
+                ("v_weight", ctypes.c_void_p), ("q_bias", ctypes.c_void_p),
+                ("k_bias", ctypes.c_void_p), ("v_bias", ctypes.c_void_p), ("width", ctypes.c_int32)]
 
 
 class KdaError(RuntimeError):
@@ -93,6 +101,9 @@ def _lib():
         lib.kda_recurrent_fwd_ex.argtypes = [dims, ctypes.c_int, p, p, p, p, i32, p, i32, p, p, p, i32,
                                              p, p, p]
         lib.kda_recurrent_fwd_ex.restype = ctypes.c_int
+        lib.kda_chunk_fwd_conv.argtypes = [dims, ctypes.c_int, p, p, p, ctypes.POINTER(KdaShortConv), p,
+                                           i32, p, i32, p, p, p, i32, i32, p, p, p, sz, p]
+        lib.kda_chunk_fwd_conv.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -211,13 +222,17 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
               o: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, use_gate_in_kernel: bool = False,
               A_log: Optional[torch.Tensor] = None, gate_is_raw: bool = True,
-              qk_l2norm: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              qk_l2norm: bool = False, short_conv=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Steps A2..A6 (kda_chunk_fwd). `gate` is the chunk-local cumulative log2
     gate (gate_cumsum with the same chunk_size). With use_gate_in_kernel=True,
     `gate` is gate_cumsum's input instead (raw x with optional A_log, or the
     natural-log g if gate_is_raw=False) and the gate step runs inside the
     chunk kernel (kda_chunk_fwd_fused_gate). qk_l2norm=True normalises q and k
-    in the kernel (kda_chunk_fwd_ex). Returns (o, final_state)."""
+    in the kernel (kda_chunk_fwd_ex). short_conv=((wq, bq), (wk, bk), (wv, bv))
+    treats q, k, v as raw projections and applies the short causal convolution
+    + SiLU to them in the kernel (kda_chunk_fwd_conv): FP32 taps [H*K, W] /
+    [HV*V, W] (a [D, 1, W] Conv1d weight is accepted too), biases or None.
+    Returns (o, final_state)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"),
                  (initial_state, "initial_state"), (cu_seqlens, "cu_seqlens"), (A_log, "A_log")):
         _check(t, n)
@@ -234,8 +249,18 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     need = int(_lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(d), dt, int(chunk_size)))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    kind = (KDA_GATE_RAW if gate_is_raw else KDA_GATE_NAT) if use_gate_in_kernel else KDA_GATE_LOG2
+    if short_conv is not None:
+        sc = _short_conv(short_conv, d)
+        rc = _lib().kda_chunk_fwd_conv(
+            ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), ctypes.byref(sc), _ptr(gate), kind,
+            _ptr(A_log), int(bool(qk_l2norm)), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+            int(chunk_size), int(bool(output_final_state)), _ptr(o), _ptr(final_state),
+            _ptr(workspace), workspace.numel(), _stream())
+        if rc:
+            raise KdaError("kda_chunk_fwd_conv", rc)
+        return o, final_state
     if qk_l2norm:
-        kind = (KDA_GATE_RAW if gate_is_raw else KDA_GATE_NAT) if use_gate_in_kernel else KDA_GATE_LOG2
         rc = _lib().kda_chunk_fwd_ex(
             ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), kind, _ptr(A_log), 1,
             _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size),
@@ -260,6 +285,30 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     if rc:
         raise KdaError("kda_chunk_fwd", rc)
     return o, final_state
+
+
+def _short_conv(short_conv, d: KdaDims) -> KdaShortConv:
+    """Marshal ((wq, bq), (wk, bk), (wv, bv)) into a kda_short_conv (the
+    tensors must stay alive until the call returns; the caller holds them)."""
+    (wq, bq), (wk, bk), (wv, bv) = short_conv
+    widths = set()
+    for t, n in ((wq, "wq"), (wk, "wk"), (wv, "wv"), (bq, "bq"), (bk, "bk"), (bv, "bv")):
+        _check(t, n)
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"short_conv {n} must be float32")
+    for w in (wq, wk, wv):
+        if w.dim() not in (2, 3) or (w.dim() == 3 and w.shape[1] != 1):
+            raise ValueError("short_conv weights are [D, W] or [D, 1, W]")
+        widths.add(int(w.shape[-1]))
+    if len(widths) != 1:
+        raise ValueError("q, k and v convolutions must have one width")
+    W = next(iter(widths))
+    for w, b, n, D in ((wq, bq, "q", d.H * d.K), (wk, bk, "k", d.H * d.K), (wv, bv, "v", d.HV * d.V)):
+        if w.numel() != D * W or (b is not None and b.numel() != D):
+            raise ValueError(f"short_conv {n}: weight must be [{D}, {W}] and bias [{D}]")
+    return KdaShortConv(wq.data_ptr(), wk.data_ptr(), wv.data_ptr(),
+                        None if bq is None else bq.data_ptr(), None if bk is None else bk.data_ptr(),
+                        None if bv is None else bv.data_ptr(), W)
 
 
 def chunk_kda_bwd(q, k, v, gate, beta, initial_state, do, dht=None, *, cu_seqlens=None,
@@ -342,4 +391,4 @@ def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
 
 
 __all__ = ["gate_cumsum", "chunk_kda", "chunk_kda_bwd", "recurrent_kda", "chunk_workspace_bytes", "load",
-           "KdaDims", "KdaError", "LIB_PATH", "EXPORTED", "KDA_FP32", "KDA_BF16"]
+           "KdaDims", "KdaShortConv", "KdaError", "LIB_PATH", "EXPORTED", "KDA_FP32", "KDA_BF16"]

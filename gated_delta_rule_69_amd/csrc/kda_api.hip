@@ -69,9 +69,10 @@ kda_status check_scan(const kda_dims* d, kda_dtype dt, const void* q, const void
 
 kda_status chunk_fwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
                           const void* v, const float* gate, int gate_mode, const float* A_log,
-                          int qk_norm, const void* beta, const float* h0, const int32_t* cu,
-                          int32_t chunk_size, int32_t write_final, void* o, float* ht,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                          int qk_norm, const kda_short_conv* conv, const void* beta,
+                          const float* h0, const int32_t* cu, int32_t chunk_size,
+                          int32_t write_final, void* o, float* ht, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
   kda_status st = check_scan(d, dt, q, k, v, gate, beta, h0, cu, write_final, o, ht);
   if (st != KDA_OK) return st;
   if (chunk_size != 64) return KDA_ERR_UNSUPPORTED;
@@ -94,8 +95,18 @@ kda_status chunk_fwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const 
       overlaps(workspace, need, gate, s.gate) || overlaps(workspace, need, beta, s.beta) ||
       overlaps(workspace, need, A_log, A_log ? (size_t)d->HV * 4 : 0))
     return KDA_ERR_ALIAS;
+  if (conv) {
+    const size_t nqk = (size_t)d->H * d->K, nv = (size_t)d->HV * d->V, W = (size_t)conv->width;
+    const void* bufs[] = {conv->q_weight, conv->k_weight, conv->v_weight,
+                          conv->q_bias, conv->k_bias, conv->v_bias};
+    const size_t lens[] = {nqk * W * 4, nqk * W * 4, nv * W * 4, nqk * 4, nqk * 4, nv * 4};
+    for (int i = 0; i < 6; ++i)
+      if (overlaps(bufs[i], lens[i], o, s.v) || overlaps(bufs[i], lens[i], ht, s.state) ||
+          overlaps(bufs[i], lens[i], workspace, need))
+        return KDA_ERR_ALIAS;
+  }
   return kda_host::launch_chunk_fwd(*d, dt, q, k, v, gate, gate_mode, A_log, qk_norm ? 1 : 0,
-                                    beta, h0, cu,
+                                    conv, beta, h0, cu,
                                     write_final ? 1 : 0, o, ht, workspace, workspace_bytes,
                                     stream) == hipSuccess
              ? KDA_OK
@@ -230,7 +241,7 @@ kda_status kda_chunk_fwd(const kda_dims* d, kda_dtype dt, const void* q, const v
                          const float* h0, const int32_t* cu, int32_t chunk_size,
                          int32_t write_final, void* o, float* ht, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
-  return chunk_fwd_impl(d, dt, q, k, v, gate, kda::kGateLog2, nullptr, 0, beta, h0, cu,
+  return chunk_fwd_impl(d, dt, q, k, v, gate, kda::kGateLog2, nullptr, 0, nullptr, beta, h0, cu,
                         chunk_size, write_final, o, ht, workspace, workspace_bytes, stream);
 }
 
@@ -242,8 +253,8 @@ kda_status kda_chunk_fwd_fused_gate(const kda_dims* d, kda_dtype dt, const void*
                                     size_t workspace_bytes, hipStream_t stream) {
   if (!gate_in_is_raw && A_log) return KDA_ERR_SHAPE;
   return chunk_fwd_impl(d, dt, q, k, v, gate_in, gate_in_is_raw ? kda::kGateRaw : kda::kGateLog,
-                        A_log, 0, beta, h0, cu, chunk_size, write_final, o, ht, workspace,
-                        workspace_bytes, stream);
+                        A_log, 0, nullptr, beta, h0, cu, chunk_size, write_final, o, ht,
+                        workspace, workspace_bytes, stream);
 }
 
 kda_status kda_chunk_fwd_ex(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
@@ -254,8 +265,22 @@ kda_status kda_chunk_fwd_ex(const kda_dims* d, kda_dtype dt, const void* q, cons
                             size_t workspace_bytes, hipStream_t stream) {
   if (gate_kind < KDA_GATE_LOG2 || gate_kind > KDA_GATE_RAW) return KDA_ERR_SHAPE;
   if (gate_kind != KDA_GATE_RAW && A_log) return KDA_ERR_SHAPE;
-  return chunk_fwd_impl(d, dt, q, k, v, gate, (int)gate_kind, A_log, qk_l2norm != 0, beta, h0, cu,
-                        chunk_size, write_final, o, ht, workspace, workspace_bytes, stream);
+  return chunk_fwd_impl(d, dt, q, k, v, gate, (int)gate_kind, A_log, qk_l2norm != 0, nullptr, beta,
+                        h0, cu, chunk_size, write_final, o, ht, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_conv(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                              const void* v, const kda_short_conv* conv, const float* gate,
+                              int32_t gate_kind, const float* A_log, int32_t qk_l2norm,
+                              const void* beta, const float* h0, const int32_t* cu,
+                              int32_t chunk_size, int32_t write_final, void* o, float* ht,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (gate_kind < KDA_GATE_LOG2 || gate_kind > KDA_GATE_RAW) return KDA_ERR_SHAPE;
+  if (gate_kind != KDA_GATE_RAW && A_log) return KDA_ERR_SHAPE;
+  if (!conv || !conv->q_weight || !conv->k_weight || !conv->v_weight) return KDA_ERR_NULL;
+  if (conv->width < 1 || conv->width > kda::kConvMaxWidth) return KDA_ERR_UNSUPPORTED;
+  return chunk_fwd_impl(d, dt, q, k, v, gate, (int)gate_kind, A_log, qk_l2norm != 0, conv, beta,
+                        h0, cu, chunk_size, write_final, o, ht, workspace, workspace_bytes, stream);
 }
 
 size_t kda_chunk_bwd_workspace_bytes(const kda_dims* d, kda_dtype dt, int32_t chunk_size) {

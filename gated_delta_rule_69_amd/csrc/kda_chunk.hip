@@ -65,9 +65,10 @@ size_t ws_bytes_t(const kda_dims& d, bool varlen) {
 
 template <typename T, int K, int V>
 hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const void* v,
-                       const float* gate, int gate_mode, const float* A_log, int qn, const void* beta,
-                       const float* h0, const int32_t* cu, int write_final, void* o, float* ht,
-                       void* ws, hipStream_t s) {
+                       const float* gate, int gate_mode, const float* A_log, int qn,
+                       const kda_short_conv* conv, const void* beta, const float* h0,
+                       const int32_t* cu, int write_final, void* o, float* ht, void* ws,
+                       hipStream_t s) {
   const bool varlen = cu != nullptr;
   const int64_t mc = max_chunks(d, varlen);
   char* p = reinterpret_cast<char*>(ws);
@@ -82,15 +83,21 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
   }
   if (mc > 0) {
     const size_t lds = IntraLds<T, K, V>::total;
-    auto launch_intra = [&](auto qnc) {
-      constexpr bool QN = decltype(qnc)::value;
-      hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, false, QN>), dim3((unsigned)mc, (unsigned)d.HV),
+    const kda_short_conv taps = conv ? *conv : kda_short_conv{};
+    auto launch_intra = [&](auto qnc, auto cvc) {
+      constexpr bool QN = decltype(qnc)::value, CV = decltype(cvc)::value;
+      hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, false, QN, CV>), dim3((unsigned)mc, (unsigned)d.HV),
                          dim3(kThreads), lds, s, (const T*)q, (const T*)k, (const T*)v, gate,
                          gate_mode, A_log, (const T*)beta, cu, ws_int, d.N, d.T, d.H, d.HV,
-                         1.0f / sqrtf((float)K), ws_T, ws_GL, (T*)nullptr, (float*)nullptr);
+                         1.0f / sqrtf((float)K), ws_T, ws_GL, (T*)nullptr, (float*)nullptr, taps);
     };
-    if (qn) launch_intra(std::true_type());
-    else launch_intra(std::false_type());
+    if (conv) {
+      if (qn) launch_intra(std::true_type(), std::true_type());
+      else launch_intra(std::false_type(), std::true_type());
+    } else {
+      if (qn) launch_intra(std::true_type(), std::false_type());
+      else launch_intra(std::false_type(), std::false_type());
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -143,39 +150,43 @@ size_t chunk_workspace_bytes(const kda_dims& d, kda_dtype dt, int chunk) {
 
 template <typename T, int K, int V>
 static hipError_t run_kv(const kda_dims& d, const void* q, const void* k, const void* v,
-                         const float* gate, int gm, const float* A_log, int qn, const void* beta,
-                         const float* h0, const int32_t* cu, int write_final, void* o,
-                         float* ht, void* ws, hipStream_t s) {
+                         const float* gate, int gm, const float* A_log, int qn,
+                         const kda_short_conv* conv, const void* beta, const float* h0,
+                         const int32_t* cu, int write_final, void* o, float* ht, void* ws,
+                         hipStream_t s) {
   const int lds = (int)kda::IntraLds<T, K, V>::total;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, false>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, true>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (e != hipSuccess) return e;
-  return kda::chunk_fwd_t<T, K, V>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht,
-                                   ws, s);
+  const void* fns[] = {reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, false, false>),
+                       reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, true, false>),
+                       reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, false, true>),
+                       reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, true, true>)};
+  for (const void* f : fns) {
+    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
+  return kda::chunk_fwd_t<T, K, V>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final,
+                                   o, ht, ws, s);
 }
 
 template <typename T>
 static hipError_t run_t(const kda_dims& d, const void* q, const void* k, const void* v,
-                        const float* gate, int gm, const float* A_log, int qn, const void* beta,
+                        const float* gate, int gm, const float* A_log, int qn,
+                        const kda_short_conv* conv, const void* beta,
                         const float* h0, const int32_t* cu, int write_final, void* o, float* ht,
                         void* ws, hipStream_t s) {
-  if (d.K == 64 && d.V == 64) return run_kv<T, 64, 64>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, ws, s);
-  if (d.K == 64 && d.V == 128) return run_kv<T, 64, 128>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, ws, s);
-  if (d.K == 128 && d.V == 64) return run_kv<T, 128, 64>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, ws, s);
-  if (d.K == 128 && d.V == 128) return run_kv<T, 128, 128>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, ws, s);
+  if (d.K == 64 && d.V == 64) return run_kv<T, 64, 64>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, s);
+  if (d.K == 64 && d.V == 128) return run_kv<T, 64, 128>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, s);
+  if (d.K == 128 && d.V == 64) return run_kv<T, 128, 64>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, s);
+  if (d.K == 128 && d.V == 128) return run_kv<T, 128, 128>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_fwd(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
                             const void* v, const float* gate, int gm, const float* A_log,
-                            int qn, const void* beta, const float* h0, const int32_t* cu,
-                            int write_final, void* o, float* ht, void* ws, size_t /*ws_bytes*/,
-                            hipStream_t s) {
-  if (dt == KDA_BF16) return run_t<kda::bf16>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, ws, s);
-  return run_t<float>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, ws, s);
+                            int qn, const kda_short_conv* conv, const void* beta,
+                            const float* h0, const int32_t* cu, int write_final, void* o,
+                            float* ht, void* ws, size_t /*ws_bytes*/, hipStream_t s) {
+  if (dt == KDA_BF16) return run_t<kda::bf16>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, s);
+  return run_t<float>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, s);
 }
 
 }  // namespace kda_host

@@ -1129,15 +1129,15 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
   }
   const float scale = 1.0f / sqrtf((float)K);
   if (mc > 0) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_intra_kernel<T, K, V, true, false>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_intra_kernel<T, K, V, true, false, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)IntraLds<T, K, V>::total);
     if (e != hipSuccess) return e;
     const size_t lds_intra = IntraLds<T, K, V>::total;
-    hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, true, false>), dim3((unsigned)mc, (unsigned)d.HV),
+    hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, true, false, false>), dim3((unsigned)mc, (unsigned)d.HV),
                        dim3(kThreads), lds_intra, s, (const T*)q, (const T*)k,
                        (const T*)v, gate, (int)kGateLog2, (const float*)nullptr, (const T*)beta,
                        cu, ws_int, d.N, d.T, d.H, d.HV, scale,
-                       ws_T, ws_GL, ws_B, ws_Bf);
+                       ws_T, ws_GL, ws_B, ws_Bf, kda_short_conv{});
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t chains = (int64_t)d.N * d.HV;

@@ -86,11 +86,12 @@ struct ChunkGeo {
   int n;         // sequence
   int64_t t0;    // flat index of the chunk's first token
   int L;         // tokens in the chunk (1..64)
+  int c;         // chunk index inside its sequence (0: the sequence's first)
 };
 
 __device__ __forceinline__ ChunkGeo chunk_geo(int j, const int32_t* cu, const int* ws_int, int N,
                                               int T) {
-  ChunkGeo r{0, 0, 0, 0};
+  ChunkGeo r{0, 0, 0, 0, 0};
   if (cu == nullptr) {
     const int nc = (T + kC - 1) / kC;
     const int n = j / nc, c = j % nc;
@@ -99,6 +100,7 @@ __device__ __forceinline__ ChunkGeo chunk_geo(int j, const int32_t* cu, const in
     r.n = n;
     r.t0 = (int64_t)n * T + (int64_t)c * kC;
     r.L = min(kC, T - c * kC);
+    r.c = c;
   } else {
     if (j >= ws_int[0]) return r;
     const int n = ws_int[2 + N + j];
@@ -108,6 +110,7 @@ __device__ __forceinline__ ChunkGeo chunk_geo(int j, const int32_t* cu, const in
     r.n = n;
     r.t0 = bos + (int64_t)c * kC;
     r.L = min(kC, len - c * kC);
+    r.c = c;
   }
   return r;
 }
@@ -169,6 +172,64 @@ __device__ __forceinline__ uint4 unit_scaled(const uint4& u, float s) {
   return r;
 }
 
+// Short causal convolution + SiLU (depthwise, taps on tokens t - W + 1 .. t,
+// the last tap on t) of NU consecutive rows r0 .. r0 + NU - 1 of one head's
+// [C][D] tile, channels ch .. ch + EPU - 1. x holds the raw rows (zero past
+// the chunk's L tokens) and receives SiLU(z) rounded to T; rows past L stay
+// zero. The W - 1 rows above r0 are read from src (the sequence's earlier
+// tokens) when they exist: always inside the chunk, before it only when the
+// chunk is not the sequence's first (hist); otherwise they are zero.
+//   src   row pointer of token 0 at channel ch; token t at src + t * tok_stride
+//   w     taps of channel ch, [EPU][W] row-major; bias of channel ch or null
+// z is summed in FP32 from the bias, oldest tap first.
+template <typename T, int NU>
+__device__ __forceinline__ void conv_silu_rows(uint4 (&x)[NU], const T* __restrict__ src,
+                                               int64_t t0, int r0, int L, bool hist,
+                                               int64_t tok_stride, const float* __restrict__ w,
+                                               const float* __restrict__ bias, int W) {
+  constexpr int EPU = 16 / (int)sizeof(T);
+  constexpr int MW = kConvMaxWidth;
+  if (r0 >= L) return;
+  uint4 hx[MW - 1];  // hx[s - 1]: row r0 - s
+#pragma unroll
+  for (int s = 1; s < MW; ++s) {
+    hx[s - 1] = make_uint4(0, 0, 0, 0);
+    if (s < W && (r0 - s >= 0 || hist))
+      hx[s - 1] = *reinterpret_cast<const uint4*>(src + (t0 + r0 - s) * tok_stride);
+  }
+  float ws[EPU][MW];  // ws[e][s]: tap on token t - s
+  float bb[EPU];
+#pragma unroll
+  for (int e = 0; e < EPU; ++e) {
+    bb[e] = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int s = 0; s < MW; ++s) ws[e][s] = s < W ? w[e * W + (W - 1 - s)] : 0.f;
+  }
+#pragma unroll
+  for (int u = NU - 1; u >= 0; --u) {  // descending: row u's raw value is read last by row u
+    if (r0 + u < L) {
+      union {
+        T t[EPU];
+        uint4 v;
+      } out;
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) {
+        float z = bb[e];
+#pragma unroll
+        for (int s = MW - 1; s >= 0; --s) {
+          if (s < W) {
+            const float xv = s <= u ? unit_elem<T>(x[s <= u ? u - s : 0], e)
+                                    : unit_elem<T>(hx[s > u ? s - u - 1 : 0], e);
+            z = fmaf(ws[e][s], xv, z);
+          }
+        }
+        out.t[e] = from_f32<T>(z * sigmoid_f32(z));
+      }
+      x[u] = out.v;
+    }
+  }
+}
+
 // Quad p of a contraction dimension holds indices 16p + 4g + e (e = 0..3) for
 // lane group g. With the kidx() order of MF<>, quad p is slots 4(p&1)..+3 of
 // bf16 fragment p/2, or FP32 fragments 4p..4p+3.
@@ -202,15 +263,18 @@ constexpr float kFastRange = 112.f;
 // BWD: also write what the backward pass needs (P^T, Khat, (Q~ Gamma)^T and
 // W^T fragments, Abar and T) into ws_B / ws_Bf.  QN: L2-normalise the q and k
 // rows as they are loaded (a template flag: the runtime branch alone cost the
-// plain path a few percent in registers and scheduling).
-template <typename T, int K, int V, bool BWD, bool QN>
+// plain path a few percent in registers and scheduling).  CONV: q, k and v
+// are raw projections; the short convolution + SiLU (taps in `conv`) runs on
+// them first, and each thread then holds consecutive rows so that a row's
+// window above it is its own rows plus W - 1 rows read again from L2.
+template <typename T, int K, int V, bool BWD, bool QN, bool CONV>
 __global__ void __launch_bounds__(kThreads, 2)
 chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                    const float* __restrict__ gate, int gate_mode,
                    const float* __restrict__ A_log, const T* __restrict__ beta,
                    const int32_t* __restrict__ cu, const int* __restrict__ ws_int, int N, int T_,
                    int H, int HV, float scale, T* __restrict__ ws_T, float* __restrict__ ws_GL,
-                   T* __restrict__ ws_B, float* __restrict__ ws_Bf) {
+                   T* __restrict__ ws_B, float* __restrict__ ws_Bf, kda_short_conv conv) {
   using M = MF<T>;
   using F = typename M::frag;
   using Lds = IntraLds<T, K, V>;
@@ -225,6 +289,11 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   constexpr int KU = kC * K / EPU / kThreads;   // 16-byte units of k (and of q) per thread
   constexpr int VU = kC * V / EPU / kThreads;   // 16-byte units of v per thread
   static_assert(GU >= 1 && KU >= 1 && VU >= 1, "tile shape");
+  constexpr int TK = K / EPU, TV = V / EPU;    // threads per row of k (q) and of v
+  static_assert(kThreads % TK == 0 && kThreads % TV == 0, "row split");
+  // row of a thread's 16-byte unit u (its column unit is tid % TK, resp. tid % TV)
+  auto krow = [](int t, int u) { return CONV ? (t / TK) * KU + u : (t + u * kThreads) / TK; };
+  auto vrow = [](int t, int u) { return CONV ? (t / TV) * VU + u : (t + u * kThreads) / TV; };
 
   extern __shared__ __align__(16) char smem[];
   float* sG = reinterpret_cast<float*>(smem);                       // R1: G2 [C][GS], later b v
@@ -254,7 +323,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   }
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
-    const int f = tid + u * kThreads, row = f / (K / EPU), cu_ = f % (K / EPU);
+    const int row = krow(tid, u), cu_ = tid % TK;
     kr[u] = qr[u] = make_uint4(0, 0, 0, 0);
     if (row < L) {
       kr[u] = *reinterpret_cast<const uint4*>(k + ((t0 + row) * H + h) * K + EPU * cu_);
@@ -263,11 +332,22 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   }
 #pragma unroll
   for (int u = 0; u < VU; ++u) {
-    const int f = tid + u * kThreads, row = f / (V / EPU), cu_ = f % (V / EPU);
+    const int row = vrow(tid, u), cu_ = tid % TV;
     vr[u] = make_uint4(0, 0, 0, 0);
     if (row < L) vr[u] = *reinterpret_cast<const uint4*>(v + ((t0 + row) * HV + hv) * V + EPU * cu_);
   }
   if (tid < kC) sBeta[tid] = tid < L ? to_f32(beta[(t0 + tid) * HV + hv]) : 0.f;
+  if constexpr (CONV) {
+    const bool hist = geo.c > 0;
+    const int W = conv.width;
+    const int chk = h * K + EPU * (tid % TK), chv = hv * V + EPU * (tid % TV);
+    conv_silu_rows<T, KU>(kr, k + chk, t0, krow(tid, 0), L, hist, (int64_t)H * K,
+                          conv.k_weight + (size_t)chk * W, conv.k_bias ? conv.k_bias + chk : nullptr, W);
+    conv_silu_rows<T, KU>(qr, q + chk, t0, krow(tid, 0), L, hist, (int64_t)H * K,
+                          conv.q_weight + (size_t)chk * W, conv.q_bias ? conv.q_bias + chk : nullptr, W);
+    conv_silu_rows<T, VU>(vr, v + chv, t0, vrow(tid, 0), L, hist, (int64_t)HV * V,
+                          conv.v_weight + (size_t)chv * W, conv.v_bias ? conv.v_bias + chv : nullptr, W);
+  }
   if constexpr (QN) {
     // the K / EPU threads holding a row of q and k are consecutive lanes
     constexpr int TPR = K / EPU;
@@ -307,7 +387,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   }
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
-    const int f = tid + u * kThreads, row = f / (K / EPU), cu_ = f % (K / EPU);
+    const int row = krow(tid, u), cu_ = tid % TK;
     *reinterpret_cast<uint4*>(sK + row * KSTR + EPU * cu_) = kr[u];
     *reinterpret_cast<uint4*>(sQ + row * KSTR + EPU * cu_) = qr[u];
   }
@@ -872,7 +952,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   T* sV = reinterpret_cast<T*>(smem);  // R1: b v [C][VSTR]
 #pragma unroll
   for (int u = 0; u < VU; ++u) {
-    const int f = tid + u * kThreads, m = f / (V / EPU), cu_ = f % (V / EPU);
+    const int m = vrow(tid, u), cu_ = tid % TV;
     const float b = sBeta[m];
     union {
       T t[EPU];

@@ -104,6 +104,9 @@ __device__ __forceinline__ float sigmoid_f32(float x) {
   return x > 20.f ? 1.f : r;
 }
 
+// Widest short convolution the fused pre-processing accepts (taps per channel).
+constexpr int kConvMaxWidth = 4;
+
 // Optional q/k normalisation: x / sqrt(sum over K of x^2 + kL2NormEps) per
 // (token, qk head), before any use of q and k.
 constexpr float kL2NormEps = 1e-6f;
@@ -175,9 +178,9 @@ hipError_t launch_recurrent(const kda_dims& d, kda_dtype dt, const void* q, cons
 size_t chunk_workspace_bytes(const kda_dims& d, kda_dtype dt, int chunk);
 hipError_t launch_chunk_fwd(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
                             const void* v, const float* gate, int gate_mode, const float* A_log,
-                            int qk_norm, const void* beta, const float* h0, const int32_t* cu,
-                            int write_final, void* o, float* ht, void* ws, size_t ws_bytes,
-                            hipStream_t s);
+                            int qk_norm, const kda_short_conv* conv, const void* beta,
+                            const float* h0, const int32_t* cu, int write_final, void* o,
+                            float* ht, void* ws, size_t ws_bytes, hipStream_t s);
 size_t chunk_bwd_workspace_bytes(const kda_dims& d, kda_dtype dt, int chunk);
 hipError_t launch_chunk_bwd(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
                             const void* v, const float* gate, const void* beta, const float* h0,

@@ -75,6 +75,29 @@ typedef enum { KDA_FP32 = 0, KDA_BF16 = 1 } kda_dtype;
  *   KDA_GATE_RAW   the raw activation input x, g = -exp(A_log) * softplus(x). */
 typedef enum { KDA_GATE_LOG2 = 0, KDA_GATE_NAT = 1, KDA_GATE_RAW = 2 } kda_gate_kind;
 
+/* Short causal convolution + SiLU applied to q, k and v before the scan (the
+ * ShortConvolution / causal_conv1d_silu pre-processing step the pages import
+ * next to the KDA op, "kda in torchtitan (training)" and the Paddle
+ * compatibility page; no formula is printed there). Per channel c of a
+ * sequence, with x taken as zero before the sequence's first token:
+ *   z[t, c] = bias[c] + sum_{j < width} weight[c, j] * x[t - width + 1 + j, c]
+ *   y[t, c] = z * sigmoid(z)                          (SiLU)
+ * i.e. a depthwise Conv1d cross-correlation with width - 1 zeros of history
+ * per sequence; weight[c, width - 1] multiplies the current token.
+ * Caller-owned device buffers, FP32, contiguous:
+ *   q_weight, k_weight [H*K, width], v_weight [HV*V, width] (channel = head * K
+ *   + k, the flattening of [H, K]); q_bias, k_bias [H*K], v_bias [HV*V] or NULL
+ *   (no bias). width in [1, 4]. */
+typedef struct {
+  const float* q_weight;
+  const float* k_weight;
+  const float* v_weight;
+  const float* q_bias;
+  const float* k_bias;
+  const float* v_bias;
+  int32_t width;
+} kda_short_conv;
+
 /* Problem sizes. T is the physical token extent per batch row (the capacity
  * in varlen mode); N is the number of state entries (B dense, len(cu)-1 varlen). */
 typedef struct {
@@ -224,6 +247,29 @@ kda_status kda_chunk_fwd_ex(const kda_dims* dims, kda_dtype dtype, const void* q
                             int32_t chunk_size, int32_t output_final_state, void* o,
                             float* final_state, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/*
+ * kda_chunk_fwd_conv -- kda_chunk_fwd_ex with the short convolution + SiLU of
+ * q, k and v fused into the loads (pre-processing step of the KDA layer; the
+ * torchtitan training page and the Paddle compatibility page import it):
+ *   q, k, v  the raw projections ([B, T, H, K] / [B, T, HV, V] in `dtype`);
+ *            the scan sees y = SiLU(conv(x)) of each (kda_short_conv), rounded
+ *            to `dtype` as a separate convolution pass would store it.
+ *   conv     taps and biases (kda_short_conv); NULL, a NULL weight or a width
+ *            outside [1, 4] is an error (KDA_ERR_NULL / KDA_ERR_UNSUPPORTED).
+ *   qk_l2norm  as kda_chunk_fwd_ex, applied to the convolution's output.
+ * Every sequence starts from zero convolution history (no carried-over
+ * convolution state). Other arguments, sizes, workspace and errors as
+ * kda_chunk_fwd_ex; the conv buffers must not overlap o, final_state or the
+ * workspace (KDA_ERR_ALIAS). No backward counterpart.
+ */
+kda_status kda_chunk_fwd_conv(const kda_dims* dims, kda_dtype dtype, const void* q, const void* k,
+                              const void* v, const kda_short_conv* conv, const float* gate,
+                              int32_t gate_kind, const float* A_log, int32_t qk_l2norm,
+                              const void* beta, const float* initial_state,
+                              const int32_t* cu_seqlens, int32_t chunk_size,
+                              int32_t output_final_state, void* o, float* final_state,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes kda_chunk_bwd needs for these sizes (0 on unsupported input). */
 size_t kda_chunk_bwd_workspace_bytes(const kda_dims* dims, kda_dtype dtype, int32_t chunk_size);

@@ -183,3 +183,31 @@ def test_ex_entries_reject_bad_arguments():
     assert chunk(3, None) == 2 and rec(-1, None) == 2          # unknown gate kind
     assert chunk(0, FAKE[9]) == 2 and rec(1, FAKE[9]) == 2     # A_log only with a raw gate
     assert chunk(2, FAKE[5]) == 5                              # A_log overlaps o
+
+
+def test_conv_entry_rejects_bad_arguments():
+    lib = kda.load()
+    d = _dims()
+
+    def call(conv):
+        return lib.kda_chunk_fwd_conv(ctypes.byref(d), 1, FAKE[0], FAKE[1], FAKE[2],
+                                      None if conv is None else ctypes.byref(conv), FAKE[3], 2,
+                                      None, 1, FAKE[4], None, None, 64, 1, FAKE[5], FAKE[6],
+                                      FAKE[7], 1 << 40, None)
+
+    def taps(width=4, **kw):
+        f = dict(q_weight=FAKE[10].value, k_weight=FAKE[11].value, v_weight=FAKE[12].value,
+                 q_bias=None, k_bias=None, v_bias=None, width=width)
+        f.update(kw)
+        return kda.KdaShortConv(**f)
+
+    assert call(None) == 1                          # no taps
+    assert call(taps(k_weight=None)) == 1           # a missing weight
+    assert call(taps(width=0)) == 4                 # widths 1..4
+    assert call(taps(width=5)) == 4
+    assert call(taps(v_weight=FAKE[5].value)) == 5  # taps overlap o
+    assert call(taps(q_bias=FAKE[6].value)) == 5    # bias overlaps the final state
+    conv = taps()
+    assert lib.kda_chunk_fwd_conv(ctypes.byref(d), 1, FAKE[0], FAKE[1], FAKE[2], ctypes.byref(conv),
+                                  FAKE[3], 0, FAKE[9], 0, FAKE[4], None, None, 64, 1, FAKE[5],
+                                  FAKE[6], FAKE[7], 1 << 40, None) == 2  # A_log with a log2 gate

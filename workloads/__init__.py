@@ -237,3 +237,26 @@ WORKLOADS = {
 
 def make(n: int, **kw) -> Workload:
     return WORKLOADS[n](**kw)
+
+
+def with_raw_projections(wl: Workload, seed: int, width: int = 4, bias: bool = True,
+                         tap_scale: float = 1.0):
+    """Inputs of the fused short-convolution forward: replaces q, k, v of `wl`
+    by raw projections ~ N(0, 1) (rounded to the workload dtype) and draws the
+    FP32 taps [channels, width] and biases [channels] of the q, k and v
+    convolutions from U(-b, b), b = tap_scale / sqrt(width) (PyTorch's default
+    Conv1d initialisation for a depthwise filter: fan-in = width). Returns
+    (wl, taps) with taps = ((wq, bq), (wk, bk), (wv, bv)), biases None when
+    bias is False."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, T, H, HV, K, V = wl.B, wl.T, wl.H, wl.HV, wl.K, wl.V
+    wl.q = _rnd(wl.dtype, rng.standard_normal((B, T, H, K), dtype=np.float32))
+    wl.k = _rnd(wl.dtype, rng.standard_normal((B, T, H, K), dtype=np.float32))
+    wl.v = _rnd(wl.dtype, rng.standard_normal((B, T, HV, V), dtype=np.float32))
+    lim = tap_scale / math.sqrt(width)
+    taps = []
+    for D in (H * K, H * K, HV * V):
+        w = rng.uniform(-lim, lim, (D, width)).astype(np.float32)
+        b = rng.uniform(-lim, lim, D).astype(np.float32) if bias else None
+        taps.append((w, b))
+    return wl, tuple(taps)
