@@ -82,7 +82,7 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
     if (e != hipSuccess) return e;
   }
   if (mc > 0) {
-    const size_t lds = IntraLds<T, K, V>::total;
+    const size_t lds = conv ? IntraLds<T, K, V>::total_conv : IntraLds<T, K, V>::total;
     const kda_short_conv taps = conv ? *conv : kda_short_conv{};
     auto launch_intra = [&](auto qnc, auto cvc) {
       constexpr bool QN = decltype(qnc)::value, CV = decltype(cvc)::value;
@@ -154,13 +154,16 @@ static hipError_t run_kv(const kda_dims& d, const void* q, const void* k, const 
                          const kda_short_conv* conv, const void* beta, const float* h0,
                          const int32_t* cu, int write_final, void* o, float* ht, void* ws,
                          hipStream_t s) {
-  const int lds = (int)kda::IntraLds<T, K, V>::total;
+  using Lds = kda::IntraLds<T, K, V>;
+  static_assert(sizeof(T) == 4 && K == 128 ? true : 2 * Lds::total_conv <= 158 * 1024,
+                "two workgroups per compute unit, also with the convolution taps");
   const void* fns[] = {reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, false, false>),
                        reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, true, false>),
                        reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, false, true>),
                        reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, true, true>)};
-  for (const void* f : fns) {
-    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  for (int i = 0; i < 4; ++i) {
+    const int lds = (int)(i < 2 ? Lds::total : Lds::total_conv);
+    hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
   }
   return kda::chunk_fwd_t<T, K, V>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final,

@@ -130,6 +130,10 @@ struct IntraLds {
   static constexpr size_t RB = (size_t)kC * 4;                    // beta
   static constexpr size_t RT = (size_t)(kC / kGateBlock) * K * 4;  // gate block totals
   static constexpr size_t total = R1 + R2 + R3 + RB + RT;
+  // short convolution: taps by distance [kConvMaxWidth][D] then the bias [D],
+  // for k, q (D = K) and v (D = V) of the workgroup's heads
+  static constexpr size_t RC = (size_t)(kConvMaxWidth + 1) * (2 * K + V) * 4;
+  static constexpr size_t total_conv = total + RC;
 };
 
 // 2^x on the transcendental unit (v_exp_f32). Results below 2^-126 flush to
@@ -174,57 +178,79 @@ __device__ __forceinline__ uint4 unit_scaled(const uint4& u, float s) {
 
 // Short causal convolution + SiLU (depthwise, taps on tokens t - W + 1 .. t,
 // the last tap on t) of NU consecutive rows r0 .. r0 + NU - 1 of one head's
-// [C][D] tile, channels ch .. ch + EPU - 1. x holds the raw rows (zero past
-// the chunk's L tokens) and receives SiLU(z) rounded to T; rows past L stay
-// zero. The W - 1 rows above r0 are read from src (the sequence's earlier
-// tokens) when they exist: always inside the chunk, before it only when the
-// chunk is not the sequence's first (hist); otherwise they are zero.
+// [C][D] tile, channels ch .. ch + EPU - 1, in two steps so that the global
+// reads of q, k and v can all be in flight before any of the arithmetic:
+//   conv_halo   reads the W - 1 rows above r0 (the sequence's earlier tokens:
+//               inside the chunk, or before it only when the chunk is not the
+//               sequence's first, hist; else zero); hx[s - 1] = row r0 - s;
+//   conv_apply  turns the raw rows x (zero past the chunk's L tokens) into
+//               SiLU(z) rounded to T; rows past L stay zero. The taps come
+//               from LDS, sw = [kConvMaxWidth][D] by distance (tap on token
+//               t - s in row s, zero for s >= W) then the bias row, at channel ch.
 //   src   row pointer of token 0 at channel ch; token t at src + t * tok_stride
-//   w     taps of channel ch, [EPU][W] row-major; bias of channel ch or null
 // z is summed in FP32 from the bias, oldest tap first.
-template <typename T, int NU>
-__device__ __forceinline__ void conv_silu_rows(uint4 (&x)[NU], const T* __restrict__ src,
-                                               int64_t t0, int r0, int L, bool hist,
-                                               int64_t tok_stride, const float* __restrict__ w,
-                                               const float* __restrict__ bias, int W) {
-  constexpr int EPU = 16 / (int)sizeof(T);
-  constexpr int MW = kConvMaxWidth;
-  if (r0 >= L) return;
-  uint4 hx[MW - 1];  // hx[s - 1]: row r0 - s
+template <typename T>
+__device__ __forceinline__ void conv_halo(uint4 (&hx)[kConvMaxWidth - 1], const T* __restrict__ src,
+                                          int64_t t0, int r0, int L, bool hist, int64_t tok_stride,
+                                          int W) {
 #pragma unroll
-  for (int s = 1; s < MW; ++s) {
+  for (int s = 1; s < kConvMaxWidth; ++s) {
     hx[s - 1] = make_uint4(0, 0, 0, 0);
-    if (s < W && (r0 - s >= 0 || hist))
+    if (r0 < L && s < W && (r0 - s >= 0 || hist))
       hx[s - 1] = *reinterpret_cast<const uint4*>(src + (t0 + r0 - s) * tok_stride);
   }
-  float ws[EPU][MW];  // ws[e][s]: tap on token t - s
-  float bb[EPU];
+}
+
+// SiLU z / (1 + e^-z) with the hardware reciprocal (1 ulp); e^-z = +inf for
+// z below about -88 gives -0.
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
+
+template <typename T, int NU>
+__device__ __forceinline__ void conv_apply(uint4 (&x)[NU], const uint4 (&hx)[kConvMaxWidth - 1],
+                                           const float* sw, int D, int r0, int L) {
+  constexpr int EPU = 16 / (int)sizeof(T), MW = kConvMaxWidth;
+  if (r0 >= L) return;
+  // z[u][e] for the NU rows at once, tap by tap (oldest first), so each tap
+  // pair read from LDS is used at once. All kConvMaxWidth taps run: the staged
+  // taps beyond W are zero and the rows they meet are finite, so those terms
+  // add exactly zero.
+  float z[NU][EPU];
 #pragma unroll
-  for (int e = 0; e < EPU; ++e) {
-    bb[e] = bias ? bias[e] : 0.f;
+  for (int e4 = 0; e4 < EPU; e4 += 4) {
+    float b[4];
+    lds4(sw + MW * D + e4, b);
 #pragma unroll
-    for (int s = 0; s < MW; ++s) ws[e][s] = s < W ? w[e * W + (W - 1 - s)] : 0.f;
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[u][e4 + e] = b[e];
   }
 #pragma unroll
-  for (int u = NU - 1; u >= 0; --u) {  // descending: row u's raw value is read last by row u
+  for (int s = MW - 1; s >= 0; --s) {
+#pragma unroll
+    for (int e4 = 0; e4 < EPU; e4 += 4) {
+      float ws[4];
+      lds4(sw + s * D + e4, ws);
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xv = s <= u ? unit_elem<T>(x[s <= u ? u - s : 0], e4 + e)
+                                  : unit_elem<T>(hx[s > u ? s - u - 1 : 0], e4 + e);
+          z[u][e4 + e] = fmaf(ws[e], xv, z[u][e4 + e]);
+        }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
     if (r0 + u < L) {
       union {
         T t[EPU];
         uint4 v;
       } out;
 #pragma unroll
-      for (int e = 0; e < EPU; ++e) {
-        float z = bb[e];
-#pragma unroll
-        for (int s = MW - 1; s >= 0; --s) {
-          if (s < W) {
-            const float xv = s <= u ? unit_elem<T>(x[s <= u ? u - s : 0], e)
-                                    : unit_elem<T>(hx[s > u ? s - u - 1 : 0], e);
-            z = fmaf(ws[e][s], xv, z);
-          }
-        }
-        out.t[e] = from_f32<T>(z * sigmoid_f32(z));
-      }
+      for (int e = 0; e < EPU; ++e) out.t[e] = from_f32<T>(silu_f32(z[u][e]));
       x[u] = out.v;
     }
   }
@@ -312,7 +338,36 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   const int64_t t0 = geo.t0;
   const size_t ch = (size_t)blockIdx.x * HV + hv;
 
-  // ---- 1. global loads first (16-byte units), then LDS stores
+  // ---- 1. global loads first (16-byte units), then LDS stores. With the
+  // convolution its taps come first: their LDS staging then waits for them
+  // alone (the load counter drains in issue order).
+  constexpr int NCW = (kConvMaxWidth + 1) * (2 * K + V);  // k, q, v taps + biases
+  constexpr int NCWT = CONV ? (NCW + kThreads - 1) / kThreads : 1;
+  float cwr[NCWT];
+  if constexpr (CONV) {
+    // thread's staged values: taps of this workgroup's heads ordered by
+    // distance ([kConvMaxWidth][D], zero at distances >= W), then the bias row
+    constexpr int MW = kConvMaxWidth;
+    const int W = conv.width;
+#pragma unroll
+    for (int j = 0; j < NCWT; ++j) {
+      const int i = tid + j * kThreads;
+      cwr[j] = 0.f;
+      if (i < NCW) {
+        const int t = i < (MW + 1) * K ? 0 : i < 2 * (MW + 1) * K ? 1 : 2;
+        const int D = t < 2 ? K : V;
+        const int rem = i - t * (MW + 1) * K, s = rem / D;
+        const int c = (t < 2 ? h * K : hv * V) + rem % D;
+        const float* w = t == 0 ? conv.k_weight : t == 1 ? conv.q_weight : conv.v_weight;
+        const float* b = t == 0 ? conv.k_bias : t == 1 ? conv.q_bias : conv.v_bias;
+        if (s < MW) {
+          if (s < W) cwr[j] = w[(size_t)c * W + (W - 1 - s)];
+        } else if (b) {
+          cwr[j] = b[c];
+        }
+      }
+    }
+  }
   float4 gr[GU];
   uint4 kr[KU], qr[KU], vr[VU];
 #pragma unroll
@@ -338,15 +393,30 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   }
   if (tid < kC) sBeta[tid] = tid < L ? to_f32(beta[(t0 + tid) * HV + hv]) : 0.f;
   if constexpr (CONV) {
+    constexpr int MW = kConvMaxWidth;
     const bool hist = geo.c > 0;
     const int W = conv.width;
-    const int chk = h * K + EPU * (tid % TK), chv = hv * V + EPU * (tid % TV);
-    conv_silu_rows<T, KU>(kr, k + chk, t0, krow(tid, 0), L, hist, (int64_t)H * K,
-                          conv.k_weight + (size_t)chk * W, conv.k_bias ? conv.k_bias + chk : nullptr, W);
-    conv_silu_rows<T, KU>(qr, q + chk, t0, krow(tid, 0), L, hist, (int64_t)H * K,
-                          conv.q_weight + (size_t)chk * W, conv.q_bias ? conv.q_bias + chk : nullptr, W);
-    conv_silu_rows<T, VU>(vr, v + chv, t0, vrow(tid, 0), L, hist, (int64_t)HV * V,
-                          conv.v_weight + (size_t)chv * W, conv.v_bias ? conv.v_bias + chv : nullptr, W);
+    const int ck = EPU * (tid % TK), cv = EPU * (tid % TV);
+    const int rk = krow(tid, 0), rv = vrow(tid, 0);
+    uint4 hk[MW - 1], hq[MW - 1], hvv[MW - 1];
+    conv_halo<T>(hk, k + h * K + ck, t0, rk, L, hist, (int64_t)H * K, W);
+    conv_halo<T>(hq, q + h * K + ck, t0, rk, L, hist, (int64_t)H * K, W);
+    conv_halo<T>(hvv, v + hv * V + cv, t0, rv, L, hist, (int64_t)HV * V, W);
+    float* sCw = reinterpret_cast<float*>(smem + Lds::total);
+#pragma unroll
+    for (int j = 0; j < NCWT; ++j) {
+      const int i = tid + j * kThreads;
+      if (i < NCW) sCw[i] = cwr[j];
+    }
+    __syncthreads();
+    // one tensor at a time: interleaving the three raises register pressure
+    // past the budget of two workgroups per compute unit
+    conv_apply<T, KU>(kr, hk, sCw + ck, K, rk, L);
+    __builtin_amdgcn_sched_barrier(0);
+    conv_apply<T, KU>(qr, hq, sCw + (MW + 1) * K + ck, K, rk, L);
+    __builtin_amdgcn_sched_barrier(0);
+    conv_apply<T, VU>(vr, hvv, sCw + 2 * (MW + 1) * K + cv, V, rv, L);
+    __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (QN) {
     // the K / EPU threads holding a row of q and k are consecutive lanes
