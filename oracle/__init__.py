@@ -190,18 +190,24 @@ CONV_MAX_WIDTH = 4
 
 
 def short_conv_silu(x: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray],
-                    cu_seqlens=None) -> np.ndarray:
+                    cu_seqlens=None, state: Optional[np.ndarray] = None,
+                    return_state: bool = False):
     """Causal depthwise convolution along the tokens of each sequence, then SiLU.
 
     x: [B, T, D] (any trailing shape is flattened to D channels); weight
     [D, W]; bias [D] or None. Reading of the pages' ShortConvolution: a
-    PyTorch Conv1d cross-correlation per channel with W - 1 zeros of history in
-    front of every sequence, so weight[c, W - 1] multiplies the current token:
+    PyTorch Conv1d cross-correlation per channel, so weight[c, W - 1]
+    multiplies the current token:
         z[t, c] = bias[c] + sum_{j<W} weight[c, j] * x[t - (W - 1) + j, c]
-        y[t, c] = silu(z[t, c]),
-    with x taken as zero before the sequence's first token. Sequences are the
-    batch rows (dense) or [cu[n], cu[n+1]) of the packed rows (varlen); tokens
-    outside every sequence are NaN."""
+        y[t, c] = silu(z[t, c]).
+    Before a sequence's first token x is the sequence's carried history:
+    state[n, W - 1 + p, c] for the p-th position before it (p = -1 .. -(W-1);
+    state is [N, W - 1, D], oldest row first), or zero when state is None.
+    Sequences are the batch rows (dense) or [cu[n], cu[n+1]) of the packed rows
+    (varlen); tokens outside every sequence are NaN.
+    return_state: also return the history a following segment would carry,
+    [N, W - 1, D]: the last W - 1 inputs of each sequence, reaching back into
+    `state` (or zeros) when the sequence is shorter than W - 1."""
     x = _f64(x)
     B, T = x.shape[:2]
     D = int(np.prod(x.shape[2:]))
@@ -210,15 +216,20 @@ def short_conv_silu(x: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray
     b = np.zeros(D) if bias is None else _f64(bias).reshape(D)
     flat = x.reshape(B * T, D)
     out = np.full_like(flat, np.nan)
-    for bos, eos in seq_bounds(B, T, cu_seqlens):
+    bounds = seq_bounds(B, T, cu_seqlens)
+    st_out = np.zeros((len(bounds), W - 1, D))
+    for n, (bos, eos) in enumerate(bounds):
+        hist = np.zeros((W - 1, D)) if state is None else _f64(state)[n].reshape(W - 1, D)
+        seq = np.concatenate([hist, flat[bos:eos]], axis=0)  # position p at row W - 1 + p
         for t in range(bos, eos):
+            r = W - 1 + (t - bos)
             z = b.copy()
             for j in range(W):
-                src = t - (W - 1) + j
-                if src >= bos:
-                    z = z + w[:, j] * flat[src]
+                z = z + w[:, j] * seq[r - (W - 1) + j]
             out[t] = silu(z)
-    return out.reshape(x.shape)
+        st_out[n] = seq[len(seq) - (W - 1):] if W > 1 else st_out[n]
+    y = out.reshape(x.shape)
+    return (y, st_out) if return_state else y
 
 
 def preprocess(q: np.ndarray, k: np.ndarray, v: np.ndarray, conv=None, qk_l2norm: bool = False,

@@ -2,8 +2,9 @@
 
 The pages name the step (ShortConvolution / causal_conv1d_silu on q, k and v)
 without printing it; the pins fix the reading the oracle implements: a
-per-channel causal cross-correlation with W - 1 zeros of history in front of
-every sequence, weight[:, W - 1] on the current token, then SiLU.
+per-channel causal cross-correlation with W - 1 rows of history in front of
+every sequence (zeros, or a carried state whose hand-off splits a sequence
+exactly), weight[:, W - 1] on the current token, then SiLU.
 """
 import math
 
@@ -124,3 +125,41 @@ def test_preprocess_order_conv_then_l2norm(oracle):
     q2, _, v2 = oracle.preprocess(q, k, v, eye, qk_l2norm=False)
     np.testing.assert_allclose(q2, q * expit(q), rtol=1e-15)
     np.testing.assert_allclose(v2, v * expit(v), rtol=1e-15)
+
+
+@pytest.mark.parametrize("W", [1, 2, 4])
+@pytest.mark.parametrize("m", [0, 1, 2, 5, 17])
+def test_carried_state_splits_a_sequence_exactly(oracle, W, m):
+    """Convolving a sequence in two segments, the second starting from the
+    history the first returns, equals convolving it whole (outputs and the
+    final history), for splits before, inside and after the first W - 1 tokens."""
+    r = _rng(10 + W)
+    L, D = 17, 5
+    x = r.standard_normal((1, L, D))
+    w = r.standard_normal((D, W))
+    b = r.standard_normal(D)
+    y, st = oracle.short_conv_silu(x, w, b, return_state=True)
+    y1, st1 = oracle.short_conv_silu(x[:, :m], w, b, return_state=True)
+    y2, st2 = oracle.short_conv_silu(x[:, m:], w, b, state=st1, return_state=True)
+    np.testing.assert_allclose(np.concatenate([y1, y2], axis=1), y, rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(st2, st)
+    assert st.shape == (1, W - 1, D)
+
+
+def test_state_is_the_last_inputs_reaching_into_the_history(oracle):
+    r = _rng(20)
+    W, D = 4, 3
+    hist = r.standard_normal((3, W - 1, D))
+    x = r.standard_normal((1, 9, D))
+    cu = [0, 1, 1, 9]  # a 1-token sequence, an empty slot, an 8-token sequence
+    w = r.standard_normal((D, W))
+    _, st = oracle.short_conv_silu(x, w, None, cu, state=hist, return_state=True)
+    np.testing.assert_array_equal(st[0], np.concatenate([hist[0, 1:], x[0, 0:1]]))  # 2 old + 1 new
+    np.testing.assert_array_equal(st[1], hist[1])                                    # empty: unchanged
+    np.testing.assert_array_equal(st[2], x[0, 6:9])                                  # last 3 inputs
+    # an impulse in the history at position -1 reaches the first W - 1 outputs
+    h1 = np.zeros((1, W - 1, D))
+    h1[0, W - 2, 0] = 1.0
+    y = oracle.short_conv_silu(np.zeros((1, 5, D)), w, None, state=h1)
+    z = np.array([w[0, W - 2], w[0, W - 3], w[0, W - 4], 0.0, 0.0])
+    np.testing.assert_allclose(y[0, :, 0], z * expit(z), rtol=1e-15)
