@@ -36,7 +36,8 @@ EXPORTED = ("kda_status_string", "kda_gate_cumsum", "kda_gate_cumsum_biased",
             "kda_gate_bwd_workspace_bytes", "kda_gate_bwd", "kda_chunk_fwd_workspace_bytes",
             "kda_chunk_fwd", "kda_chunk_fwd_fused_gate", "kda_chunk_bwd_workspace_bytes",
             "kda_chunk_bwd", "kda_recurrent_fwd", "kda_recurrent_fwd_fused_gate",
-            "kda_chunk_fwd_ex", "kda_recurrent_fwd_ex", "kda_chunk_fwd_conv")
+            "kda_chunk_fwd_ex", "kda_recurrent_fwd_ex", "kda_chunk_fwd_conv", "kda_short_conv_fwd",
+            "kda_recurrent_fwd_conv_workspace_bytes", "kda_recurrent_fwd_conv")
 KDA_GATE_LOG2, KDA_GATE_NAT, KDA_GATE_RAW = 0, 1, 2
 
 
@@ -104,6 +105,14 @@ def _lib():
         lib.kda_chunk_fwd_conv.argtypes = [dims, ctypes.c_int, p, p, p, ctypes.POINTER(KdaShortConv), p,
                                            i32, p, i32, p, p, p, i32, i32, p, p, p, sz, p]
         lib.kda_chunk_fwd_conv.restype = ctypes.c_int
+        conv = ctypes.POINTER(KdaShortConv)
+        lib.kda_short_conv_fwd.argtypes = [dims, ctypes.c_int, p, p, p, conv, p, p, p, p, p, p, p]
+        lib.kda_short_conv_fwd.restype = ctypes.c_int
+        lib.kda_recurrent_fwd_conv_workspace_bytes.argtypes = [dims, ctypes.c_int]
+        lib.kda_recurrent_fwd_conv_workspace_bytes.restype = sz
+        lib.kda_recurrent_fwd_conv.argtypes = [dims, ctypes.c_int, p, p, p, conv, p, p, p, i32, p, i32,
+                                               p, p, p, i32, p, p, p, sz, p]
+        lib.kda_recurrent_fwd_conv.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -337,19 +346,58 @@ def chunk_kda_bwd(q, k, v, gate, beta, initial_state, do, dht=None, *, cu_seqlen
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=dh0)
 
 
+def conv_state_shape(q, v, cu_seqlens, width: int):
+    """Shape of a short-convolution history: [N, width - 1, 2*H*K + HV*V]."""
+    d = _dims(q, v, cu_seqlens)
+    return (d.N, width - 1, 2 * d.H * d.K + d.HV * d.V)
+
+
+def short_conv(q, k, v, short_conv, *, cu_seqlens=None, conv_state=None, conv_state_out=None,
+               outputs: bool = True, out=None):
+    """kda_short_conv_fwd: SiLU(causal conv) of raw q, k, v continuing each
+    sequence from its carried history `conv_state` ([N, W-1, 2HK + HV V] in the
+    input dtype, oldest row first; None = zeros). The new history goes to
+    `conv_state_out` (may be conv_state itself; None = not kept). outputs=False
+    computes the history only (prefill hand-off). `out` = (q_out, k_out, v_out)
+    to write into (may be the inputs). Returns ((q, k, v) or None, conv_state_out)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_seqlens, "cu_seqlens"), (conv_state, "conv_state"),
+                 (conv_state_out, "conv_state_out")):
+        _check(t, n)
+    d = _dims(q, v, cu_seqlens)
+    dt = _dtype_code(q)
+    sc = _short_conv(short_conv, d)
+    for st, n in ((conv_state, "conv_state"), (conv_state_out, "conv_state_out")):
+        if st is not None and (tuple(st.shape) != conv_state_shape(q, v, cu_seqlens, sc.width)
+                               or st.dtype != q.dtype):
+            raise ValueError(f"{n} must be {conv_state_shape(q, v, cu_seqlens, sc.width)} {q.dtype}")
+    res = None
+    if outputs:
+        res = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    rc = _lib().kda_short_conv_fwd(ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), ctypes.byref(sc),
+                                   _ptr(cu_seqlens), _ptr(conv_state), _ptr(conv_state_out),
+                                   *(_ptr(t) for t in (res or (None, None, None))), _stream())
+    if rc:
+        raise KdaError("kda_short_conv_fwd", rc)
+    return res, conv_state_out
+
+
 def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
                   output_final_state: bool = False, o: Optional[torch.Tensor] = None,
                   final_state: Optional[torch.Tensor] = None, use_gate_in_kernel: bool = False,
                   A_log: Optional[torch.Tensor] = None, gate_is_raw: bool = True,
-                  qk_l2norm: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  qk_l2norm: bool = False, short_conv=None, conv_state=None, conv_state_out=None,
+                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Step A7 (kda_recurrent_fwd). `gate` is the per-token log2 decay
     (gate_cumsum with chunk_size=1). With use_gate_in_kernel=True, `gate` is
     gate_cumsum's input instead (raw x with optional A_log, or the natural-log
     g if gate_is_raw=False), activated inside the scan kernel
     (kda_recurrent_fwd_fused_gate). qk_l2norm=True normalises q and k in the
-    kernel (kda_recurrent_fwd_ex). Inference only: inputs that require grad
-    are rejected (use chunk_kda for training). Pass final_state=initial_state
-    to update the states in place."""
+    kernel (kda_recurrent_fwd_ex). short_conv=((wq, bq), (wk, bk), (wv, bv))
+    treats q, k, v as raw projections and runs the short convolution + SiLU
+    first, continuing each sequence from `conv_state` and writing the new
+    history to `conv_state_out` (kda_recurrent_fwd_conv; see short_conv).
+    Inference only: inputs that require grad are rejected (use chunk_kda for
+    training). Pass final_state=initial_state to update the states in place."""
     if any(t is not None and t.requires_grad for t in (q, k, v, gate, beta, initial_state)):
         raise RuntimeError("recurrent_kda is inference-only; inputs require grad (use chunk_kda)")
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"),
@@ -365,8 +413,26 @@ def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
         final_state = torch.empty((d.N, d.HV, d.K, d.V), device=q.device, dtype=torch.float32)
     if not output_final_state:
         final_state = None
+    kind = (KDA_GATE_RAW if gate_is_raw else KDA_GATE_NAT) if use_gate_in_kernel else KDA_GATE_LOG2
+    if short_conv is not None:
+        sc = _short_conv(short_conv, d)
+        for st, n in ((conv_state, "conv_state"), (conv_state_out, "conv_state_out")):
+            _check(st, n)
+            if st is not None and (tuple(st.shape) != conv_state_shape(q, v, cu_seqlens, sc.width)
+                                   or st.dtype != q.dtype):
+                raise ValueError(f"{n} must be {conv_state_shape(q, v, cu_seqlens, sc.width)} {q.dtype}")
+        need = int(_lib().kda_recurrent_fwd_conv_workspace_bytes(ctypes.byref(d), dt))
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+        rc = _lib().kda_recurrent_fwd_conv(
+            ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), ctypes.byref(sc), _ptr(conv_state),
+            _ptr(conv_state_out), _ptr(gate), kind, _ptr(A_log), int(bool(qk_l2norm)), _ptr(beta),
+            _ptr(initial_state), _ptr(cu_seqlens), int(bool(output_final_state)), _ptr(o),
+            _ptr(final_state), _ptr(workspace), workspace.numel(), _stream())
+        if rc:
+            raise KdaError("kda_recurrent_fwd_conv", rc)
+        return o, final_state
     if qk_l2norm:
-        kind = (KDA_GATE_RAW if gate_is_raw else KDA_GATE_NAT) if use_gate_in_kernel else KDA_GATE_LOG2
         rc = _lib().kda_recurrent_fwd_ex(
             ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), kind, _ptr(A_log), 1,
             _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), int(bool(output_final_state)), _ptr(o),
@@ -390,5 +456,6 @@ def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     return o, final_state
 
 
-__all__ = ["gate_cumsum", "chunk_kda", "chunk_kda_bwd", "recurrent_kda", "chunk_workspace_bytes", "load",
+__all__ = ["gate_cumsum", "chunk_kda", "chunk_kda_bwd", "recurrent_kda", "short_conv", "conv_state_shape",
+           "chunk_workspace_bytes", "load",
            "KdaDims", "KdaShortConv", "KdaError", "LIB_PATH", "EXPORTED", "KDA_FP32", "KDA_BF16"]

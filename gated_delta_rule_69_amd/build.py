@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libkda.so")
 OBJDIR = os.path.join(os.path.dirname(HERE), "_build", "libkda")
-SOURCES = ["kda_api.hip", "kda_gate.hip", "kda_recurrent.hip", "kda_chunk.hip", "kda_chunk_bwd.hip"]
+SOURCES = ["kda_api.hip", "kda_gate.hip", "kda_recurrent.hip", "kda_conv.hip", "kda_chunk.hip",
+           "kda_chunk_bwd.hip"]
 ARCH = "gfx950"
 
 

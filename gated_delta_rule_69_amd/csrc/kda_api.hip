@@ -132,6 +132,26 @@ kda_status recurrent_impl(const kda_dims* d, kda_dtype dt, const void* q, const 
              : KDA_ERR_LAUNCH;
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Checks shared by the short-convolution entry points (no launch on failure).
+kda_status check_conv(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                      const void* v, const kda_short_conv* conv, const int32_t* cu) {
+  kda_status st = check_dims(d, cu);
+  if (st != KDA_OK) return st;
+  if (!valid_dtype(dt)) return KDA_ERR_DTYPE;
+  if (!conv || !conv->q_weight || !conv->k_weight || !conv->v_weight) return KDA_ERR_NULL;
+  if (conv->width < 1 || conv->width > kda::kConvMaxWidth) return KDA_ERR_UNSUPPORTED;
+  const size_t epu = 16 / esize(dt);
+  if (d->K % epu || d->V % epu) return KDA_ERR_UNSUPPORTED;  // 16-byte channel units
+  if ((size_t)d->B * d->T > 0 && (!q || !k || !v)) return KDA_ERR_NULL;
+  return KDA_OK;
+}
+
+size_t conv_state_bytes(const kda_dims* d, kda_dtype dt, int W) {
+  return (size_t)d->N * (W - 1) * (2 * (size_t)d->H * d->K + (size_t)d->HV * d->V) * esize(dt);
+}
+
 }  // namespace
 
 extern "C" {
@@ -350,6 +370,97 @@ kda_status kda_recurrent_fwd_fused_gate(const kda_dims* d, kda_dtype dt, const v
   if (!gate_in_is_raw && A_log) return KDA_ERR_SHAPE;
   return recurrent_impl(d, dt, q, k, v, gate_in, gate_in_is_raw ? kda::kGateRaw : kda::kGateLog,
                         A_log, 0, beta, h0, cu, write_final, o, ht, stream);
+}
+
+kda_status kda_short_conv_fwd(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                              const void* v, const kda_short_conv* conv, const int32_t* cu,
+                              const void* st_in, void* st_out, void* q_out, void* k_out,
+                              void* v_out, hipStream_t stream) {
+  kda_status st = check_conv(d, dt, q, k, v, conv, cu);
+  if (st != KDA_OK) return st;
+  const bool out = q_out || k_out || v_out;
+  if (out && (!q_out || !k_out || !v_out)) return KDA_ERR_NULL;
+  const Sizes s = sizes(d, dt);
+  const size_t sb = conv_state_bytes(d, dt, conv->width);
+  // outputs equal their own input or overlap nothing; the history may be updated in place
+  const void* ins[] = {q, k, v, st_in};
+  const size_t ins_n[] = {s.qk, s.qk, s.v, st_in ? sb : 0};
+  void* outs[] = {q_out, k_out, v_out, st_out};
+  const size_t outs_n[] = {s.qk, s.qk, s.v, st_out ? sb : 0};
+  for (int i = 0; i < 4; ++i) {
+    if (!outs[i]) continue;
+    for (int j = 0; j < 4; ++j) {
+      const bool own_input = i == j && outs[i] == ins[j];  // in place
+      if (!own_input && overlaps(outs[i], outs_n[i], ins[j], ins_n[j])) return KDA_ERR_ALIAS;
+    }
+    for (int j = i + 1; j < 4; ++j)
+      if (outs[j] && overlaps(outs[i], outs_n[i], outs[j], outs_n[j])) return KDA_ERR_ALIAS;
+  }
+  const size_t nqk = (size_t)d->H * d->K, nv = (size_t)d->HV * d->V, W = (size_t)conv->width;
+  const void* taps[] = {conv->q_weight, conv->k_weight, conv->v_weight,
+                        conv->q_bias, conv->k_bias, conv->v_bias};
+  const size_t taps_n[] = {nqk * W * 4, nqk * W * 4, nv * W * 4, nqk * 4, nqk * 4, nv * 4};
+  for (int i = 0; i < 6; ++i)
+    for (int j = 0; j < 4; ++j)
+      if (outs[j] && overlaps(taps[i], taps_n[i], outs[j], outs_n[j])) return KDA_ERR_ALIAS;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)st_in | (uintptr_t)st_out |
+        (uintptr_t)q_out | (uintptr_t)k_out | (uintptr_t)v_out) & 15))
+    return KDA_ERR_UNSUPPORTED;
+  if (d->N == 0) return KDA_OK;
+  return kda_host::launch_short_conv(*d, dt, q, k, v, *conv, cu, st_in, st_out, q_out, k_out, v_out,
+                                     stream) == hipSuccess
+             ? KDA_OK
+             : KDA_ERR_LAUNCH;
+}
+
+size_t kda_recurrent_fwd_conv_workspace_bytes(const kda_dims* d, kda_dtype dt) {
+  if (!d || !valid_dtype(dt) || d->B < 0 || d->T < 0 || d->H <= 0 || d->HV <= 0 || d->K <= 0 ||
+      d->V <= 0)
+    return 0;
+  const Sizes s = sizes(d, dt);
+  return 2 * align256(s.qk) + align256(s.v);
+}
+
+kda_status kda_recurrent_fwd_conv(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                                  const void* v, const kda_short_conv* conv, const void* st_in,
+                                  void* st_out, const float* gate, int32_t gate_kind,
+                                  const float* A_log, int32_t qk_l2norm, const void* beta,
+                                  const float* h0, const int32_t* cu, int32_t write_final, void* o,
+                                  float* ht, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  if (gate_kind < KDA_GATE_LOG2 || gate_kind > KDA_GATE_RAW) return KDA_ERR_SHAPE;
+  if (gate_kind != KDA_GATE_RAW && A_log) return KDA_ERR_SHAPE;
+  kda_status st = check_conv(d, dt, q, k, v, conv, cu);
+  if (st != KDA_OK) return st;
+  st = check_scan(d, dt, q, k, v, gate, beta, h0, cu, write_final, o, ht);
+  if (st != KDA_OK) return st;
+  if (d->K > 256 || d->V > 256) return KDA_ERR_UNSUPPORTED;
+  const Sizes s = sizes(d, dt);
+  const size_t need = kda_recurrent_fwd_conv_workspace_bytes(d, dt);
+  if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  if ((uintptr_t)workspace & 255) return KDA_ERR_UNSUPPORTED;
+  const size_t sb = conv_state_bytes(d, dt, conv->width);
+  const void* others[] = {q, k, v, gate, beta, h0, o, ht, st_in, st_out, A_log};
+  const size_t others_n[] = {s.qk, s.qk, s.v, s.gate, s.beta, s.state, s.v, s.state,
+                             st_in ? sb : 0, st_out ? sb : 0, A_log ? (size_t)d->HV * 4 : 0};
+  for (int i = 0; i < 11; ++i)
+    if (overlaps(workspace, need, others[i], others_n[i])) return KDA_ERR_ALIAS;
+  if (st_out && (overlaps(st_out, sb, o, s.v) || overlaps(st_out, sb, ht, s.state) ||
+                 overlaps(st_out, sb, q, s.qk) || overlaps(st_out, sb, k, s.qk) ||
+                 overlaps(st_out, sb, v, s.v)))
+    return KDA_ERR_ALIAS;
+  if (A_log && (overlaps(A_log, (size_t)d->HV * 4, o, s.v) ||
+                overlaps(A_log, (size_t)d->HV * 4, ht, s.state)))
+    return KDA_ERR_ALIAS;
+  if (d->N == 0) return KDA_OK;
+  char* p = reinterpret_cast<char*>(workspace);
+  void* qc = p;
+  void* kc = p + align256(s.qk);
+  void* vc = p + 2 * align256(s.qk);
+  st = kda_short_conv_fwd(d, dt, q, k, v, conv, cu, st_in, st_out, qc, kc, vc, stream);
+  if (st != KDA_OK) return st;
+  return recurrent_impl(d, dt, qc, kc, vc, gate, (int)gate_kind, A_log, qk_l2norm != 0, beta, h0,
+                        cu, write_final, o, ht, stream);
 }
 
 kda_status kda_recurrent_fwd_ex(const kda_dims* d, kda_dtype dt, const void* q, const void* k,

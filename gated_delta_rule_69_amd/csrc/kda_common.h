@@ -175,6 +175,10 @@ hipError_t launch_recurrent(const kda_dims& d, kda_dtype dt, const void* q, cons
                             const void* v, const float* gate, int gate_mode, const float* A_log,
                             int qk_norm, const void* beta, const float* h0, const int32_t* cu,
                             int write_final, void* o, float* ht, hipStream_t s);
+hipError_t launch_short_conv(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
+                             const void* v, const kda_short_conv& conv, const int32_t* cu,
+                             const void* st_in, void* st_out, void* qo, void* ko, void* vo,
+                             hipStream_t s);
 size_t chunk_workspace_bytes(const kda_dims& d, kda_dtype dt, int chunk);
 hipError_t launch_chunk_fwd(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
                             const void* v, const float* gate, int gate_mode, const float* A_log,

@@ -271,6 +271,55 @@ kda_status kda_chunk_fwd_conv(const kda_dims* dims, kda_dtype dtype, const void*
                               int32_t output_final_state, void* o, float* final_state,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * kda_short_conv_fwd -- the short convolution + SiLU on its own, with a carried
+ * per-sequence history (decode continues a sequence's filter; a prefill hands
+ * its history over):
+ *   q, k, v    raw projections [B, T, H, K], [B, T, H, K], [B, T, HV, V] in `dtype`.
+ *   conv       taps and biases (kda_short_conv), as kda_chunk_fwd_conv.
+ *   conv_state_in  [N, W - 1, 2*H*K + HV*V] in `dtype`, or NULL (zero history):
+ *              per sequence the W - 1 raw inputs before its first token, oldest
+ *              row first, channels in the order q (H*K), k (H*K), v (HV*V).
+ *   conv_state_out same layout, or NULL: receives the last W - 1 raw inputs of
+ *              each sequence, reaching back into conv_state_in (or zeros) for a
+ *              sequence shorter than W - 1; an empty slot gets conv_state_in
+ *              bitwise (or zeros). May equal conv_state_in (updated in place).
+ *   q_out, k_out, v_out  outputs SiLU(conv(x)) (layout of the inputs, rounded to
+ *              `dtype`), or all three NULL to compute the history only (reads
+ *              only the last W - 1 tokens of each sequence). Each may equal its
+ *              own input (in place); no other overlap (KDA_ERR_ALIAS).
+ * Rows outside every sequence are neither read nor written. Needs K and V
+ * multiples of 16 bytes' worth of elements and 16-byte aligned buffers
+ * (KDA_ERR_UNSUPPORTED). Each thread walks one sequence's tokens in order:
+ * meant for decode and short segments; long prefills use kda_chunk_fwd_conv.
+ */
+kda_status kda_short_conv_fwd(const kda_dims* dims, kda_dtype dtype, const void* q, const void* k,
+                              const void* v, const kda_short_conv* conv,
+                              const int32_t* cu_seqlens, const void* conv_state_in,
+                              void* conv_state_out, void* q_out, void* k_out, void* v_out,
+                              hipStream_t stream);
+
+/* Workspace bytes kda_recurrent_fwd_conv needs (the convolved q, k, v; 0 on
+ * invalid dims). */
+size_t kda_recurrent_fwd_conv_workspace_bytes(const kda_dims* dims, kda_dtype dtype);
+
+/*
+ * kda_recurrent_fwd_conv -- decode from raw projections: kda_short_conv_fwd
+ * (carried history conv_state_in -> conv_state_out, convolved q, k, v into the
+ * workspace) then kda_recurrent_fwd_ex on them (gate kind, A_log and q/k L2
+ * normalisation as there). Arguments as those two entry points; the workspace
+ * (256-byte aligned, kda_recurrent_fwd_conv_workspace_bytes) must not overlap
+ * any other buffer. All arguments are checked before the first launch.
+ */
+kda_status kda_recurrent_fwd_conv(const kda_dims* dims, kda_dtype dtype, const void* q,
+                                  const void* k, const void* v, const kda_short_conv* conv,
+                                  const void* conv_state_in, void* conv_state_out,
+                                  const float* gate, int32_t gate_kind, const float* A_log,
+                                  int32_t qk_l2norm, const void* beta, const float* initial_state,
+                                  const int32_t* cu_seqlens, int32_t output_final_state, void* o,
+                                  float* final_state, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
 /* Workspace bytes kda_chunk_bwd needs for these sizes (0 on unsupported input). */
 size_t kda_chunk_bwd_workspace_bytes(const kda_dims* dims, kda_dtype dtype, int32_t chunk_size);
 

@@ -211,3 +211,50 @@ def test_conv_entry_rejects_bad_arguments():
     assert lib.kda_chunk_fwd_conv(ctypes.byref(d), 1, FAKE[0], FAKE[1], FAKE[2], ctypes.byref(conv),
                                   FAKE[3], 0, FAKE[9], 0, FAKE[4], None, None, 64, 1, FAKE[5],
                                   FAKE[6], FAKE[7], 1 << 40, None) == 2  # A_log with a log2 gate
+
+
+def test_short_conv_and_conv_decode_reject_bad_arguments():
+    lib = kda.load()
+    d = _dims()
+
+    def taps(width=4, **kw):
+        f = dict(q_weight=FAKE[10].value, k_weight=FAKE[11].value, v_weight=FAKE[12].value,
+                 q_bias=None, k_bias=None, v_bias=None, width=width)
+        f.update(kw)
+        return kda.KdaShortConv(**f)
+
+    def sc(conv, outs=(FAKE[5], FAKE[6], FAKE[7]), st_in=None, st_out=None, dims=d, dt=1):
+        return lib.kda_short_conv_fwd(ctypes.byref(dims), dt, FAKE[0], FAKE[1], FAKE[2],
+                                      None if conv is None else ctypes.byref(conv), None, st_in,
+                                      st_out, *outs, None)
+
+    assert sc(None) == 1                                   # no taps
+    assert sc(taps(v_weight=None)) == 1
+    assert sc(taps(width=5)) == 4
+    assert sc(taps(), outs=(FAKE[5], None, FAKE[7])) == 1  # outputs: all three or none
+    assert sc(taps(), dims=_dims(K=60)) == 4               # 16-byte channel units
+    assert sc(taps(), dt=9) == 3
+    assert sc(taps(), outs=(FAKE[1], FAKE[6], FAKE[7])) == 5   # q_out over k
+    assert sc(taps(q_weight=FAKE[6].value)) == 5               # taps under an output
+    assert sc(taps(), outs=(ctypes.c_void_p(FAKE[5].value + 8), FAKE[6], FAKE[7])) == 4  # alignment
+    # history-only mode with an in-place history is accepted up to the launch;
+    # with N = 0 nothing is launched
+    assert sc(taps(), outs=(None, None, None), st_in=FAKE[8], st_out=FAKE[8],
+              dims=_dims(B=0, N=0)) == 0
+    assert lib.kda_recurrent_fwd_conv_workspace_bytes(None, 1) == 0
+    need = lib.kda_recurrent_fwd_conv_workspace_bytes(ctypes.byref(d), 1)
+    assert need == 3 * 64 * 64 * 2
+
+    def rec(conv, kind=2, A_log=None, ws=FAKE[13], ws_bytes=1 << 40):
+        return lib.kda_recurrent_fwd_conv(ctypes.byref(d), 1, FAKE[0], FAKE[1], FAKE[2],
+                                          None if conv is None else ctypes.byref(conv), None, None,
+                                          FAKE[3], kind, A_log, 1, FAKE[4], None, None, 1, FAKE[5],
+                                          FAKE[6], ws, ws_bytes, None)
+
+    assert rec(taps(), kind=4) == 2
+    assert rec(taps(), kind=0, A_log=FAKE[9]) == 2
+    assert rec(None) == 1
+    assert rec(taps(), ws=None) == 6
+    assert rec(taps(), ws_bytes=need - 1) == 6
+    assert rec(taps(), ws=FAKE[5]) == 5                    # workspace over o
+    assert rec(taps(), ws=ctypes.c_void_p(FAKE[13].value + 16)) == 4
