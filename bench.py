@@ -328,6 +328,23 @@ def main():
     dbytes = decode_bytes(ntok, wd.H, wd.HV, wd.K, wd.V)
     fused_dec_gbs = dbytes / (fused_us * 1e-6) / 1e9
 
+    # decode from raw projections: the short convolution (width 4, biases)
+    # continues each slot's history in place (kda_recurrent_fwd_conv), then
+    # the scan with the q/k L2 norm
+    cgen = torch.Generator(device=dev).manual_seed(851)
+    dtaps = tuple(((torch.rand(D, 4, device=dev, generator=cgen) - 0.5),
+                   (torch.rand(D, device=dev, generator=cgen) - 0.5))
+                  for D in (wd.H * wd.K, wd.H * wd.K, wd.HV * wd.V))
+    dhist = torch.zeros(kda.conv_state_shape(dq, dv, dcu, 4), device=dev, dtype=bf)
+    dws = torch.empty(1 << 24, device=dev, dtype=torch.uint8)
+
+    def dstep_conv():
+        kda.recurrent_kda(dq, dk, dv, dx, db, dh, cu_seqlens=dcu, output_final_state=True, o=do,
+                          final_state=dh, use_gate_in_kernel=True, qk_l2norm=True,
+                          short_conv=dtaps, conv_state=dhist, conv_state_out=dhist, workspace=dws)
+    conv_dec_us = timed_region(dstep_conv, a.decode_steps, 20)[1] * 1e3
+    del dtaps, dhist, dws
+
     # ---------------- other workloads (context lines; not part of `value`)
     def time_it(fn, reps, warm=3):
         for _ in range(warm):
@@ -492,7 +509,11 @@ def main():
                    "algorithmic_bytes": dbytes,
                    "two_call_us_per_step": round(dec2_us, 2),
                    "two_call_kda_gate_cumsum_us": round(g1_us, 2),
-                   "two_call_kda_recurrent_fwd_us": round(rec_us, 2)},
+                   "two_call_kda_recurrent_fwd_us": round(rec_us, 2),
+                   "raw_projections_conv_us": round(conv_dec_us, 2),
+                   "raw_projections_conv_entry": "kda_recurrent_fwd_conv (width-4 short "
+                                                 "convolution with the history updated in "
+                                                 "place, q/k L2 norm)"},
         "other_workloads": extra,
         "cpu_baseline": cpu,
     }

@@ -15,7 +15,7 @@ namespace {
 
 constexpr int kConvThreads = 256;
 
-// Element e of a 16-byte unit of T values, as float; and its inverse.
+// Element e of a 16-byte unit of T values, as float.
 template <typename T>
 __device__ __forceinline__ float elem(const uint4& u, int e) {
   return to_f32(reinterpret_cast<const T*>(&u)[e]);
@@ -58,17 +58,41 @@ short_conv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 #pragma unroll
   for (int s = 1; s < MW; ++s) {
     hx[s - 1] = make_uint4(0, 0, 0, 0);
-    if (s < W && st_in) hx[s - 1] = *reinterpret_cast<const uint4*>(st_in + st_base + (size_t)(W - 1 - s) * st_row);
+    if (s < W && st_in)
+      hx[s - 1] = *reinterpret_cast<const uint4*>(st_in + st_base + (size_t)(W - 1 - s) * st_row);
   }
 
   if (OUT) {
     // taps by distance (zero beyond W) and the bias of the unit's channels
     float ws[EPU][MW], bb[EPU];
+    const float* wc = w + (size_t)cc * W;  // the unit's EPU x W taps are contiguous
+    if (W == MW && ((uintptr_t)wc & 15) == 0) {
 #pragma unroll
-    for (int e = 0; e < EPU; ++e) {
-      bb[e] = b ? b[cc + e] : 0.f;
+      for (int e = 0; e < EPU; ++e) {
+        const float4 t = *reinterpret_cast<const float4*>(wc + e * MW);
+        ws[e][0] = t.w;
+        ws[e][1] = t.z;
+        ws[e][2] = t.y;
+        ws[e][3] = t.x;
+      }
+    } else {
 #pragma unroll
-      for (int s = 0; s < MW; ++s) ws[e][s] = s < W ? w[(size_t)(cc + e) * W + (W - 1 - s)] : 0.f;
+      for (int e = 0; e < EPU; ++e)
+#pragma unroll
+        for (int s = 0; s < MW; ++s) ws[e][s] = s < W ? wc[e * W + (W - 1 - s)] : 0.f;
+    }
+    if (b && ((uintptr_t)(b + cc) & 15) == 0) {
+#pragma unroll
+      for (int e = 0; e < EPU; e += 4) {
+        const float4 t = *reinterpret_cast<const float4*>(b + cc + e);
+        bb[e] = t.x;
+        bb[e + 1] = t.y;
+        bb[e + 2] = t.z;
+        bb[e + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) bb[e] = b ? b[cc + e] : 0.f;
     }
     for (int i = 0; i < len; ++i) {
       const int64_t t = bos + i;
@@ -105,7 +129,8 @@ short_conv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   if (st_out) {
 #pragma unroll
     for (int s = 1; s < MW; ++s)
-      if (s < W) *reinterpret_cast<uint4*>(st_out + st_base + (size_t)(W - 1 - s) * st_row) = hx[s - 1];
+      if (s < W)
+        *reinterpret_cast<uint4*>(st_out + st_base + (size_t)(W - 1 - s) * st_row) = hx[s - 1];
   }
 }
 
