@@ -122,3 +122,46 @@ def test_chunk_forward_graph_replay_with_new_boundaries():
     wl.x = d["x"].cpu().numpy()
     o_ref, h_ref = oracle.forward(wl)
     check_parity(wl, o_g, h_g, o_ref, h_ref, "graph replay")
+
+
+def test_conv_decode_graph_replay_advances_the_history():
+    """A captured decode step from raw projections (short convolution with the
+    history updated in place, then the scan with the state in place) replayed
+    three times with new tokens equals three eager steps bit for bit, history
+    and state included."""
+    wl = workloads.workload4()
+    wl, taps = workloads.with_raw_projections(wl, 905, 4, True)
+    d = device_inputs(wl)
+    tt = tuple((to_dev(w), to_dev(b)) for w, b in taps)
+    hist0 = torch.randn(kda.conv_state_shape(d["q"], d["v"], d["cu"], 4), device=DEV).to(d["q"].dtype)
+    h0 = d["h0"].clone()
+    ws = torch.empty(1 << 24, device=DEV, dtype=torch.uint8)
+    inp = {n: d[n].clone() for n in ("q", "k", "v", "x", "beta")}
+    hist, h, o = hist0.clone(), h0.clone(), torch.empty_like(d["v"])
+
+    def step(hist_, h_, o_, src):
+        kda.recurrent_kda(src["q"], src["k"], src["v"], src["x"], src["beta"], h_, cu_seqlens=d["cu"],
+                          output_final_state=True, final_state=h_, o=o_, use_gate_in_kernel=True,
+                          qk_l2norm=True, short_conv=tt, conv_state=hist_, conv_state_out=hist_,
+                          workspace=ws)
+
+    g = _capture(lambda: step(hist, h, o, inp))
+    # the capture's warm-up calls advanced the history and state: restart both
+    hist.copy_(hist0)
+    h.copy_(h0)
+    hist_e, h_e, o_e = hist0.clone(), h0.clone(), torch.empty_like(o)
+    gen = torch.Generator(device=DEV).manual_seed(906)
+    for rep in range(3):
+        for n in inp:
+            inp[n].copy_((torch.randn(inp[n].shape, device=DEV, generator=gen) *
+                          (1.0 if n != "beta" else 0.2)).to(inp[n].dtype))
+        if "beta" in inp:
+            inp["beta"].copy_(inp["beta"].abs())
+        g.replay()
+        torch.cuda.synchronize()
+        step(hist_e, h_e, o_e, inp)
+        torch.cuda.synchronize()
+        rows = int(wl.cu_seqlens[-1])
+        assert torch.equal(_bits(o[:, :rows]), _bits(o_e[:, :rows])), rep
+        assert torch.equal(_bits(hist), _bits(hist_e)), rep
+        assert torch.equal(_bits(h), _bits(h_e)), rep
