@@ -258,3 +258,25 @@ def test_short_conv_and_conv_decode_reject_bad_arguments():
     assert rec(taps(), ws_bytes=need - 1) == 6
     assert rec(taps(), ws=FAKE[5]) == 5                    # workspace over o
     assert rec(taps(), ws=ctypes.c_void_p(FAKE[13].value + 16)) == 4
+
+
+def test_prefill_and_step_ops_fake_shapes_on_meta_tensors():
+    import torch
+
+    import gated_delta_rule_69_amd.torch_ops  # noqa: F401
+
+    m = dict(device="meta")
+    q = torch.empty(1, 50, 2, 64, dtype=torch.bfloat16, **m)
+    v = torch.empty(1, 50, 4, 32, dtype=torch.bfloat16, **m)
+    x = torch.empty(1, 50, 4, 64, **m)
+    beta = torch.empty(1, 50, 4, dtype=torch.bfloat16, **m)
+    cu = torch.empty(4, dtype=torch.int32, **m)
+    wq, wv = torch.empty(128, 4, **m), torch.empty(128, 4, **m)
+    o, ht, hist = torch.ops.kda.chunk_kda_prefill(q, q, v, x, beta, None, None, cu, True,
+                                                  wq, wq, wv, None, None, None)
+    assert o.shape == v.shape and ht.shape == (3, 4, 64, 32) and hist.shape == (3, 3, 384)
+    assert hist.dtype == torch.bfloat16
+    st = torch.empty(3, 4, 64, 32, **m)
+    o = torch.ops.kda.recurrent_kda_step(q, q, v, x, beta, None, st, hist, cu, True,
+                                         wq, wq, wv, None, None, None)
+    assert o.shape == v.shape

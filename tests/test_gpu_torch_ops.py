@@ -91,3 +91,58 @@ def test_opcheck_registrations():
     n = int(wl.cu_seqlens[-1])
     assert normwise_max_err(to_np(o)[:, :n], o_ref[:, :n]) <= 2e-5
     assert normwise_max_err(to_np(ht), ht_ref) <= 2e-5
+
+
+def test_prefill_and_decode_step_ops():
+    """kda::chunk_kda_prefill and kda::recurrent_kda_step equal the direct
+    binding calls bit for bit (the step op mutating state and history), and
+    pass opcheck."""
+    import gated_delta_rule_69_amd as kda
+    import workloads as wls
+
+    wl = wls.tiny_case(1200, T=150, H=2, HV=4, K=64, V=64, dtype="bf16", cu_seqlens=[0, 70, 70, 148],
+                       A_log=0.3)
+    wl, taps = wls.with_raw_projections(wl, 1201, 4, True)
+    d = device_inputs(wl)
+    tt = [to_dev(a) for pair in taps for a in pair]  # wq, bq, wk, bk, wv, bv
+    wq, bq, wk, bk, wv, bv = tt
+    conv_args = (wq, wk, wv, bq, bk, bv)
+    o, ht, hist = torch.ops.kda.chunk_kda_prefill(d["q"], d["k"], d["v"], d["x"], d["beta"], d["A_log"],
+                                                  d["h0"], d["cu"], True, *conv_args)
+    o2, ht2 = kda.chunk_kda(d["q"], d["k"], d["v"], d["x"], d["beta"], d["h0"], cu_seqlens=d["cu"],
+                            output_final_state=True, use_gate_in_kernel=True, A_log=d["A_log"],
+                            qk_l2norm=True, short_conv=((wq, bq), (wk, bk), (wv, bv)))
+    hist2 = torch.zeros_like(hist)
+    kda.short_conv(d["q"], d["k"], d["v"], ((wq, bq), (wk, bk), (wv, bv)), cu_seqlens=d["cu"],
+                   conv_state_out=hist2, outputs=False)
+    torch.cuda.synchronize()
+    n = 148
+    assert torch.equal(o[:, :n].view(torch.int16), o2[:, :n].view(torch.int16))
+    assert torch.equal(ht.view(torch.int32), ht2.view(torch.int32))
+    assert torch.equal(hist.view(torch.int16), hist2.view(torch.int16))
+    # one decode token per slot continuing from the prefill
+    step = wls.tiny_case(1202, T=3, H=2, HV=4, K=64, V=64, dtype="bf16", cu_seqlens=[0, 1, 2, 3],
+                         A_log=0.3)
+    step, _ = wls.with_raw_projections(step, 1203, 4, True)
+    s = device_inputs(step)
+    st_a, st_b = ht.clone(), ht.clone()
+    hi_a, hi_b = hist.clone(), hist.clone()
+    oa = torch.ops.kda.recurrent_kda_step(s["q"], s["k"], s["v"], s["x"], s["beta"], s["A_log"], st_a,
+                                          hi_a, s["cu"], True, *conv_args)
+    ob, _ = kda.recurrent_kda(s["q"], s["k"], s["v"], s["x"], s["beta"], st_b, cu_seqlens=s["cu"],
+                              output_final_state=True, final_state=st_b, use_gate_in_kernel=True,
+                              A_log=s["A_log"], qk_l2norm=True,
+                              short_conv=((wq, bq), (wk, bk), (wv, bv)), conv_state=hi_b,
+                              conv_state_out=hi_b)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+    assert torch.equal(st_a.view(torch.int32), st_b.view(torch.int32))
+    assert torch.equal(hi_a.view(torch.int16), hi_b.view(torch.int16))
+    assert not torch.equal(hi_a.view(torch.int16), hist.view(torch.int16))  # it advanced
+    torch.library.opcheck(torch.ops.kda.chunk_kda_prefill.default,
+                          (d["q"], d["k"], d["v"], d["x"], d["beta"], d["A_log"], d["h0"], d["cu"],
+                           True, *conv_args), test_utils=("test_schema", "test_faketensor"))
+    torch.library.opcheck(torch.ops.kda.recurrent_kda_step.default,
+                          (s["q"], s["k"], s["v"], s["x"], s["beta"], s["A_log"], ht.clone(),
+                           hist.clone(), s["cu"], True, *conv_args),
+                          test_utils=("test_schema", "test_faketensor"))
