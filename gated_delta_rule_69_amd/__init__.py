@@ -320,6 +320,12 @@ def _short_conv(short_conv, d: KdaDims) -> KdaShortConv:
                         None if bv is None else bv.data_ptr(), W)
 
 
+def chunk_bwd_workspace_bytes(q: torch.Tensor, v: torch.Tensor, cu_seqlens=None,
+                              chunk_size: int = 64) -> int:
+    d = _dims(q, v, cu_seqlens)
+    return int(_lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(d), _dtype_code(q), int(chunk_size)))
+
+
 def chunk_kda_bwd(q, k, v, gate, beta, initial_state, do, dht=None, *, cu_seqlens=None,
                   chunk_size: int = 64, workspace: Optional[torch.Tensor] = None):
     """Steps B1..B3 (kda_chunk_bwd). Returns a dict with dq, dk (shape of q),

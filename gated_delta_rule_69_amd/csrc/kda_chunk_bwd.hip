@@ -1175,8 +1175,8 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
                        (T*)dk, dq_part, dk_part, (T*)dv, dg, (T*)dbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (d.HV != d.H) {
-    const int64_t n_tok = (int64_t)d.B * d.T;
+  const int64_t n_tok = (int64_t)d.B * d.T;
+  if (d.HV != d.H && n_tok > 0) {  // no tokens: nothing to reduce (and no empty grid)
     const int64_t total = n_tok * d.H * K;
     hipLaunchKernelGGL(gva_reduce_kernel<T>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        dq_part, dk_part, cu, d.N, n_tok, d.H, d.HV, K, (T*)dq, (T*)dk);
