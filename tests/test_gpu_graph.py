@@ -165,3 +165,44 @@ def test_conv_decode_graph_replay_advances_the_history():
         assert torch.equal(_bits(o[:, :rows]), _bits(o_e[:, :rows])), rep
         assert torch.equal(_bits(hist), _bits(hist_e)), rep
         assert torch.equal(_bits(h), _bits(h_e)), rep
+
+
+def test_chunk_backward_graph_replay_with_new_boundaries():
+    """The backward of a training step (gate recompute + kda_chunk_bwd, GVA,
+    empty slots) captured once and replayed with new upstream gradients, gate
+    inputs and sequence boundaries: every replay equals the eager call bit for
+    bit (fixed-order reductions, no atomics)."""
+    cu0 = [0, 0, 120, 250, 250, 400]
+    wl = workloads.tiny_case(920, T=450, H=2, HV=4, K=128, V=128, dtype="bf16", cu_seqlens=cu0,
+                             grads=True)
+    d = device_inputs(wl)
+    dO = to_dev(wl.dO, torch.bfloat16)
+    dht = to_dev(wl.dht)
+    ws = torch.empty(kda.chunk_bwd_workspace_bytes(d["q"], d["v"], d["cu"]), device=DEV,
+                     dtype=torch.uint8)
+    cu = d["cu"].clone()
+    res = {}
+
+    def step():
+        G = kda.gate_cumsum(d["x"], d["A_log"], cu, 64)
+        res.update(kda.chunk_kda_bwd(d["q"], d["k"], d["v"], G, d["beta"], d["h0"], dO, dht,
+                                     cu_seqlens=cu, workspace=ws))
+
+    g = _capture(step)
+    rng = np.random.default_rng(921)
+    for rep in range(3):
+        new_cu = _boundaries(rng, 5, 400 + 10 * rep, {(rep + 1) % 5})
+        cu.copy_(torch.from_numpy(new_cu).to(DEV))
+        d["x"].copy_(torch.randn_like(d["x"]))
+        dO.copy_(torch.randn_like(dO))
+        g.replay()
+        torch.cuda.synchronize()
+        got = {n: t.clone() for n, t in res.items()}
+        G = kda.gate_cumsum(d["x"], d["A_log"], cu, 64)
+        want = kda.chunk_kda_bwd(d["q"], d["k"], d["v"], G, d["beta"], d["h0"], dO, dht,
+                                 cu_seqlens=cu)
+        torch.cuda.synchronize()
+        n_tok = int(new_cu[-1])
+        for n in ("dq", "dk", "dv", "dg", "dbeta"):
+            assert torch.equal(_bits(got[n][:, :n_tok]), _bits(want[n][:, :n_tok])), (rep, n)
+        assert torch.equal(_bits(got["dh0"]), _bits(want["dh0"])), rep
