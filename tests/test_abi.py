@@ -96,6 +96,31 @@ def test_workspace_bytes():
     assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d), 1, 32) == 0
 
 
+def test_workspace_bindings_match_the_c_calls():
+    """The binding's workspace helpers only marshal shapes (meta tensors, no
+    device): they equal the C calls, grow with T, cover a varlen batch's extra
+    partial chunks, and the backward's workspace holds at least the forward's."""
+    import torch
+    lib = kda.load()
+    for T in (0, 1, 64, 4096):
+        q = torch.empty((4, T, 16, 128), dtype=torch.bfloat16, device="meta")
+        v = torch.empty((4, T, 16, 128), dtype=torch.bfloat16, device="meta")
+        d = _dims(B=4, T=T, N=4, H=16, HV=16, K=128, V=128)
+        f = kda.chunk_workspace_bytes(q, v)
+        b = kda.chunk_bwd_workspace_bytes(q, v)
+        assert f == lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d), 1, 64)
+        assert b == lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(d), 1, 64)
+        assert b >= f
+    small = kda.chunk_workspace_bytes(torch.empty((1, 64, 16, 128), device="meta", dtype=torch.bfloat16),
+                                      torch.empty((1, 64, 16, 128), device="meta", dtype=torch.bfloat16))
+    big = kda.chunk_workspace_bytes(torch.empty((1, 4096, 16, 128), device="meta", dtype=torch.bfloat16),
+                                    torch.empty((1, 4096, 16, 128), device="meta", dtype=torch.bfloat16))
+    assert big > small
+    cu = torch.empty((6,), dtype=torch.int32, device="meta")  # 5 sequences packed in one row
+    q1 = torch.empty((1, 4096, 16, 128), dtype=torch.bfloat16, device="meta")
+    assert kda.chunk_workspace_bytes(q1, q1, cu) > kda.chunk_workspace_bytes(q1, q1)
+
+
 def test_fused_gate_entries_reject_bad_arguments():
     lib = kda.load()
     d = _dims()
