@@ -376,22 +376,33 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     const int rr = row < L ? row : L - 1;  // pad rows repeat the last gate row
     gr[u] = *reinterpret_cast<const float4*>(gate + ((t0 + rr) * HV + hv) * K + 4 * c4);
   }
+  // Pad rows of a short last chunk load the last valid row, like the gate, and
+  // are zeroed where the values are first used: no load sits in a lane-
+  // dependent branch, whose join would make the compiler wait for every load
+  // issued so far before the remaining ones.
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
     const int row = krow(tid, u), cu_ = tid % TK;
-    kr[u] = qr[u] = make_uint4(0, 0, 0, 0);
-    if (row < L) {
-      kr[u] = *reinterpret_cast<const uint4*>(k + ((t0 + row) * H + h) * K + EPU * cu_);
-      qr[u] = *reinterpret_cast<const uint4*>(q + ((t0 + row) * H + h) * K + EPU * cu_);
-    }
+    const int rr = row < L ? row : L - 1;
+    kr[u] = *reinterpret_cast<const uint4*>(k + ((t0 + rr) * H + h) * K + EPU * cu_);
+    qr[u] = *reinterpret_cast<const uint4*>(q + ((t0 + rr) * H + h) * K + EPU * cu_);
   }
 #pragma unroll
   for (int u = 0; u < VU; ++u) {
     const int row = vrow(tid, u), cu_ = tid % TV;
-    vr[u] = make_uint4(0, 0, 0, 0);
-    if (row < L) vr[u] = *reinterpret_cast<const uint4*>(v + ((t0 + row) * HV + hv) * V + EPU * cu_);
+    const int rr = row < L ? row : L - 1;
+    vr[u] = *reinterpret_cast<const uint4*>(v + ((t0 + rr) * HV + hv) * V + EPU * cu_);
   }
-  if (tid < kC) sBeta[tid] = tid < L ? to_f32(beta[(t0 + tid) * HV + hv]) : 0.f;
+  const int brow = tid % kC < L ? tid % kC : L - 1;
+  const T braw = beta[(t0 + brow) * HV + hv];  // every thread loads; threads < kC store
+  auto zero_pad_rows = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+      if (krow(tid, u) >= L) kr[u] = qr[u] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < VU; ++u)
+      if (vrow(tid, u) >= L) vr[u] = make_uint4(0, 0, 0, 0);
+  };
   if constexpr (CONV) {
     constexpr int MW = kConvMaxWidth;
     const bool hist = geo.c > 0;
@@ -409,6 +420,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
       if (i < NCW) sCw[i] = cwr[j];
     }
     __syncthreads();
+    zero_pad_rows();
     // one tensor at a time: interleaving the three raises register pressure
     // past the budget of two workgroups per compute unit
     conv_apply<T, KU>(kr, hk, sCw + ck, K, rk, L);
@@ -418,6 +430,8 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     conv_apply<T, VU>(vr, hvv, sCw + 2 * (MW + 1) * K + cv, V, rv, L);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (!CONV) zero_pad_rows();
+  if (tid < kC) sBeta[tid] = tid < L ? to_f32(braw) : 0.f;
   if constexpr (QN) {
     // the K / EPU threads holding a row of q and k are consecutive lanes
     constexpr int TPR = K / EPU;
