@@ -44,7 +44,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_SOURCES = ("gated_delta_rule_69_amd/csrc/kda_common.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk_kernels.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk.hip")
-TRAFFIC_SHA16 = "e547badfcb127805"
+TRAFFIC_SHA16 = "15170fb2d1ebbe11"
 TRAFFIC_BYTES = 1020.9e6
 
 
