@@ -189,16 +189,28 @@ __device__ __forceinline__ uint4 unit_scaled(const uint4& u, float s) {
 //               t - s in row s, zero for s >= W) then the bias row, at channel ch.
 //   src   row pointer of token 0 at channel ch; token t at src + t * tok_stride
 // z is summed in FP32 from the bias, oldest tap first.
+// The loads are unconditional (a halo row that is not used loads a valid row
+// of the chunk instead) and conv_halo_mask zeroes the unused ones later: a
+// load under a lane-dependent branch makes the compiler wait for every load
+// issued before it at the branch join.
+__device__ __forceinline__ bool conv_halo_used(int s, int r0, int L, bool hist, int W) {
+  return r0 < L && s < W && (r0 - s >= 0 || hist);
+}
 template <typename T>
 __device__ __forceinline__ void conv_halo(uint4 (&hx)[kConvMaxWidth - 1], const T* __restrict__ src,
                                           int64_t t0, int r0, int L, bool hist, int64_t tok_stride,
                                           int W) {
 #pragma unroll
   for (int s = 1; s < kConvMaxWidth; ++s) {
-    hx[s - 1] = make_uint4(0, 0, 0, 0);
-    if (r0 < L && s < W && (r0 - s >= 0 || hist))
-      hx[s - 1] = *reinterpret_cast<const uint4*>(src + (t0 + r0 - s) * tok_stride);
+    const int rr = conv_halo_used(s, r0, L, hist, W) ? r0 - s : (r0 < L ? r0 : L - 1);
+    hx[s - 1] = *reinterpret_cast<const uint4*>(src + (t0 + rr) * tok_stride);
   }
+}
+__device__ __forceinline__ void conv_halo_mask(uint4 (&hx)[kConvMaxWidth - 1], int r0, int L,
+                                               bool hist, int W) {
+#pragma unroll
+  for (int s = 1; s < kConvMaxWidth; ++s)
+    if (!conv_halo_used(s, r0, L, hist, W)) hx[s - 1] = make_uint4(0, 0, 0, 0);
 }
 
 // SiLU z / (1 + e^-z) with the hardware reciprocal (1 ulp); e^-z = +inf for
@@ -421,6 +433,9 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     }
     __syncthreads();
     zero_pad_rows();
+    conv_halo_mask(hk, rk, L, hist, W);
+    conv_halo_mask(hq, rk, L, hist, W);
+    conv_halo_mask(hvv, rv, L, hist, W);
     // one tensor at a time: interleaving the three raises register pressure
     // past the budget of two workgroups per compute unit
     conv_apply<T, KU>(kr, hk, sCw + ck, K, rk, L);
