@@ -66,7 +66,7 @@ def _args():
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--skip-extra", action="store_true", help="skip the context workloads")
     p.add_argument("--profile", choices=["dense", "dense2", "dense_conv", "decode", "decode2", "long",
-                                         "gatebwd", "copy"],
+                                         "gatebwd", "varlen", "tiny", "copy"],
                    default=None,
                    help="run only one workload a few times (for rocprofv3), print no JSON")
     p.add_argument("--profile-reps", type=int, default=3)
@@ -136,6 +136,30 @@ def profile_only(a):
             G = kda.gate_cumsum(x, None, None, 64)
             kda.chunk_kda(*t[:3], G, t[3], h0, output_final_state=True)
             kda.chunk_kda_bwd(*t[:3], G, t[3], h0, dO, dht)
+    elif a.profile == "varlen":
+        # packed varlen + GVA: 32768 tokens in 16 sequences and 3 empty slots, HV = 32,
+        # nonzero initial states, gate in the kernel
+        w3 = workloads.workload3()
+        q, k, v, b = T_(w3.q, bf), T_(w3.k, bf), T_(w3.v, bf), T_(w3.beta, bf)
+        x, h0 = T_(w3.x), T_(w3.h0)
+        A = None if w3.A_log is None else T_(w3.A_log)
+        cu = torch.from_numpy(w3.cu_seqlens.astype(np.int32)).to(dev)
+        for _ in range(a.profile_reps):
+            kda.chunk_kda(q, k, v, x, b, h0, cu_seqlens=cu, output_final_state=True,
+                          use_gate_in_kernel=True, A_log=A)
+    elif a.profile == "tiny":
+        # the tiny FP32 varlen case (T = 73, HV = 2, K = V = 64): chunked and recurrent,
+        # gate in the kernel
+        w1 = workloads.workload1(dense=False)
+        q, k, v, b = T_(w1.q), T_(w1.k), T_(w1.v), T_(w1.beta)
+        x, h0 = T_(w1.x), T_(w1.h0)
+        A = None if w1.A_log is None else T_(w1.A_log)
+        cu = torch.from_numpy(w1.cu_seqlens.astype(np.int32)).to(dev)
+        for _ in range(a.profile_reps):
+            kda.chunk_kda(q, k, v, x, b, h0, cu_seqlens=cu, output_final_state=True,
+                          use_gate_in_kernel=True, A_log=A)
+            kda.recurrent_kda(q, k, v, x, b, h0, cu_seqlens=cu, output_final_state=True,
+                              use_gate_in_kernel=True, A_log=A)
     elif a.profile == "gatebwd":
         # gate backward on the long-context shape: B=1 T=65536 HV=32 K=128, A_log and dt_bias
         gen = torch.Generator(device=dev).manual_seed(5)
