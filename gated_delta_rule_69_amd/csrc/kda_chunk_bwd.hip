@@ -535,6 +535,10 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       const int f = tid + i * NT, row = f / (kC / 4), c4 = f % (kC / 4);
       tx[i] = *reinterpret_cast<const float4*>(wTm + row * kC + 4 * c4);
     }
+    // beta of the chunk's rows (row tid % C; pad rows load the last valid row):
+    // unconditional, in the same batch as the other loads
+    const int brow = tid % kC < L ? tid % kC : L - 1;
+    const T braw = beta[(t0 + brow) * HV + hv];
     load_blk(0, pf);
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
@@ -554,6 +558,9 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       const int f = tid + i * NT, row = f / (kC / 4), c4 = f % (kC / 4);
       *reinterpret_cast<float4*>(sT + row * TS + 4 * c4) = tx[i];
     }
+    // beta lives in the first pad column of the G2 rows (never written otherwise);
+    // zero past the chunk's last token
+    if (tid < kC) sG[tid * GS + K] = tid < L ? to_f32(braw) : 0.f;
     store_blk(pf);
     if (V / VB > 1) load_blk(1, pf);
   }
@@ -565,13 +572,10 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   float* const dkpb = dk_part ? dk_part + (t0 * HV + hv) * (int64_t)K : nullptr;
   T* const dqb = dq_out + (t0 * H + h) * (int64_t)K;
   T* const dkb = dk_out + (t0 * H + h) * (int64_t)K;
-  float bet[4];  // beta of the rows 16tt + 4g + e this lane's accumulators cover
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int i = 16 * tt + 4 * g + e;
-    bet[e] = i < L ? to_f32(beta[(t0 + i) * HV + hv]) : 0.f;
-  }
   __syncthreads();
+  float bet[4];  // beta of the rows 16tt + 4g + e this lane's accumulators cover (0 past L)
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bet[e] = sG[(16 * tt + 4 * g + e) * GS + K];
 
   // T^T fragments for rows j of token tile tt (T[i][j] down i), used three times
   F aTt[KS_C];
@@ -737,7 +741,7 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
 #pragma unroll
   for (int jj = 0; jj < JH; ++jj) {
     const int j = 16 * (JH * hh + jj) + l16;
-    const float bj = j < L ? to_f32(beta[(t0 + j) * HV + hv]) : 0.f;
+    const float bj = sG[j * GS + K];  // 0 past L
 #pragma unroll
     for (int e = 0; e < 4; ++e) dT1[jj][e] *= bj;
   }
@@ -778,7 +782,7 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       float km[4], gm[4];
       lds4(sK + m * KSTR + 4 * c4, km);
       lds4(sG + m * GS + 4 * c4, gm);
-      const float bm = m < L ? to_f32(beta[(t0 + m) * HV + hv]) : 0.f;
+      const float bm = sG[m * GS + K];  // 0 past L
 #pragma unroll
       for (int e = 0; e < 4; ++e) sBKg[m * KSTR + 4 * c4 + e] = from_f32<T>(bm * km[e] * ex2(gm[e]));
     }
