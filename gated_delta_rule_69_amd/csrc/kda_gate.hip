@@ -191,9 +191,12 @@ gate_bwd_kernel(const float* __restrict__ x, const float* __restrict__ A_log,
       ld(x, t, xv[b]);
       ld(dg, t, gv[b]);
     }
+    // every loaded token is used (the partial sums select, only the store is
+    // guarded): a token whose use sits behind a branch has its load sunk into
+    // that branch, where it is issued just before it is needed
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
-      if (t0 + b >= t_b) break;
+      const bool in = t0 + b < t_b;
       float r[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
@@ -201,9 +204,10 @@ gate_bwd_kernel(const float* __restrict__ x, const float* __restrict__ A_log,
         const float u = bias ? xv[b][e] + bv[e] : xv[b][e];
         const float g = -scale[e] * softplus_f32(u);
         r[e] = -scale[e] * sigmoid_f32(u) * gv[b][e];
-        adb[e] += r[e];
-        ada[e] += gv[b][e] * g;
+        adb[e] = in ? adb[e] + r[e] : adb[e];
+        ada[e] = in ? ada[e] + gv[b][e] * g : ada[e];
       }
+      if (!in) continue;
       float* p = dx + (t0 + b) * row + f0;
       if constexpr (VEC == 4) {
         *reinterpret_cast<float4*>(p) = make_float4(r[0], r[1], r[2], r[3]);
