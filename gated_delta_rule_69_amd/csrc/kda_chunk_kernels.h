@@ -1067,6 +1067,20 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   {
     constexpr int NP = V / 32;
     const int pw = wave % NP, I0 = (wave / NP) * NP;
+    // the wave's two value tiles of b V as B fragments (column gathers from
+    // LDS), built once and shared by its NP row tiles of T
+    F vb[2][KS_C];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int c = 16 * (2 * pw + h2) + l16;
+#pragma unroll
+      for (int p = 0; p < QC; ++p) {
+        float v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = to_f32(sV[(16 * p + 4 * g + e) * VSTR + c]);
+        put_quad<M>(vb[h2], p, v4);
+      }
+    }
 #pragma unroll
     for (int ii = 0; ii < NP; ++ii) {
       F ta[KS_C];
@@ -1079,18 +1093,9 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int vt = 2 * pw + h2;
-        const int c = 16 * vt + l16;
-        F vb[KS_C];
-#pragma unroll
-        for (int p = 0; p < QC; ++p) {
-          float v4[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = to_f32(sV[(16 * p + 4 * g + e) * VSTR + c]);
-          put_quad<M>(vb, p, v4);
-        }
         f32x4 acc = zero4();
 #pragma unroll
-        for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(ta[ks], vb[ks], acc);
+        for (int ks = 0; ks < KS_C; ++ks) acc = M::mma(ta[ks], vb[h2][ks], acc);
         T* dst = wsU + (((size_t)(I0 + ii) * (V / 16) + vt) * 64 + lane) * 4;
         if constexpr (sizeof(T) == 2) {
           bf16x4 x;
