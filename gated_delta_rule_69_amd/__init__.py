@@ -154,6 +154,100 @@ def _dims(q, v, cu_seqlens) -> KdaDims:
     return KdaDims(B, T, N, H, HV, K, V)
 
 
+_I32_MAX = 2**31 - 1
+
+
+def _expect(t: Optional[torch.Tensor], name: str, shape, dtype):
+    """Raise unless `t` (if given) has exactly this shape and dtype."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _cu_dims(cu_seqlens: Optional[torch.Tensor], B: int) -> int:
+    """Number of state entries N; checks cu_seqlens is a 1-D int32 tensor of
+    N + 1 >= 1 offsets with B == 1 (the C ABI reads it as int32 on the device,
+    so any other dtype would be misread rather than rejected there)."""
+    if cu_seqlens is None:
+        return B
+    if not isinstance(cu_seqlens, torch.Tensor):
+        raise TypeError("cu_seqlens must be a torch.Tensor")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError(f"cu_seqlens must be torch.int32, got {cu_seqlens.dtype}")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 >= 1 offsets")
+    if B != 1:
+        raise ValueError(f"varlen inputs are packed into one batch row (B == 1), got B = {B}")
+    return cu_seqlens.numel() - 1
+
+
+def _validate_scan(q, k, v, gate, beta, initial_state, cu_seqlens, *, o=None, final_state=None,
+                   A_log=None, do=None, dht=None):
+    """Full dtype and shape check of the scan arguments before any pointer is
+    handed to the C ABI, which cannot see buffer sizes: q, k [B, T, H, K] and
+    v [B, T, HV, V] and beta [B, T, HV] in one dtype (bfloat16 or float32),
+    gate [B, T, HV, K] float32, states [N, HV, K, V] float32, A_log [HV]
+    float32, o like v, do like v, dht like the states."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta"), (gate, "gate")):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{n} must be a torch.Tensor")
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [B, T, H, K] and v [B, T, HV, V]")
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    if tuple(v.shape[:2]) != (B, T):
+        raise ValueError(f"v must be [{B}, {T}, HV, V], got {tuple(v.shape)}")
+    if H < 1 or HV % H != 0:
+        raise ValueError(f"HV ({HV}) must be a positive multiple of H ({H})")
+    if max(B, T, H, HV, K, V) > _I32_MAX:
+        raise ValueError("every size must fit the C ABI's int32 fields")
+    dt = q.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"q must be bfloat16 or float32, got {dt}")
+    _expect(k, "k", (B, T, H, K), dt)
+    _expect(v, "v", (B, T, HV, V), dt)
+    _expect(beta, "beta", (B, T, HV), dt)
+    _expect(gate, "gate", (B, T, HV, K), torch.float32)
+    N = _cu_dims(cu_seqlens, B)
+    st = (N, HV, K, V)
+    _expect(initial_state, "initial_state", st, torch.float32)
+    _expect(final_state, "final_state", st, torch.float32)
+    _expect(o, "o", (B, T, HV, V), dt)
+    _expect(A_log, "A_log", (HV,), torch.float32)
+    _expect(do, "do", (B, T, HV, V), dt)
+    _expect(dht, "dht", st, torch.float32)
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (initial_state, "initial_state"),
+                 (cu_seqlens, "cu_seqlens"), (o, "o"), (final_state, "final_state"), (A_log, "A_log"),
+                 (do, "do"), (dht, "dht")):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{n} is on {t.device}, q on {dev}")
+
+
+def _validate_gate(x, A_log, cu_seqlens, out=None, dt_bias=None, name="gate_in"):
+    """x [B, T, HV, K] float32, A_log [HV], dt_bias [HV, K], out like x (all float32)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 4:
+        raise ValueError(f"{name} must be a [B, T, HV, K] tensor")
+    B, T, HV, K = x.shape
+    _expect(x, name, (B, T, HV, K), torch.float32)
+    _expect(A_log, "A_log", (HV,), torch.float32)
+    _expect(out, "out", (B, T, HV, K), torch.float32)
+    if dt_bias is not None and dt_bias.numel() == HV * K and dt_bias.dim() == 1:
+        _expect(dt_bias, "dt_bias", (HV * K,), torch.float32)
+    else:
+        _expect(dt_bias, "dt_bias", (HV, K), torch.float32)
+    _cu_dims(cu_seqlens, B)
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def gate_cumsum(gate_in: torch.Tensor, A_log: Optional[torch.Tensor] = None,
                 cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = 64,
                 is_raw: bool = True, out: Optional[torch.Tensor] = None,
@@ -161,6 +255,7 @@ def gate_cumsum(gate_in: torch.Tensor, A_log: Optional[torch.Tensor] = None,
     """Step A1 (kda_gate_cumsum): [B, T, HV, K] FP32 raw gate input x (or the
     natural-log g if is_raw=False) -> chunk-local inclusive cumsum in log2 units.
     With dt_bias ([HV, K] FP32, raw input only) it is kda_gate_cumsum_biased."""
+    _validate_gate(gate_in, A_log, cu_seqlens, out, dt_bias)
     for t, n in ((gate_in, "gate_in"), (A_log, "A_log"), (cu_seqlens, "cu_seqlens"), (out, "out"),
                  (dt_bias, "dt_bias")):
         _check(t, n)
@@ -199,6 +294,8 @@ def gate_bwd(x: torch.Tensor, dg: torch.Tensor, A_log: Optional[torch.Tensor] = 
     (dg = gradient of the per-token natural-log gate, e.g. chunk_kda_bwd's dg) ->
     (dx, dA_log or None, d_dt_bias or None); the parameter gradients are
     produced exactly for the parameters given."""
+    _validate_gate(x, A_log, cu_seqlens, dx, dt_bias, name="x")
+    _expect(dg, "dg", tuple(x.shape), torch.float32)
     for t, n in ((x, "x"), (dg, "dg"), (A_log, "A_log"), (dt_bias, "dt_bias"),
                  (cu_seqlens, "cu_seqlens"), (dx, "dx"), (workspace, "workspace")):
         _check(t, n)
@@ -212,7 +309,7 @@ def gate_bwd(x: torch.Tensor, dg: torch.Tensor, A_log: Optional[torch.Tensor] = 
     need = int(_lib().kda_gate_bwd_workspace_bytes(ctypes.byref(d)))
     if (dA is not None or db is not None) and workspace is None:
         workspace = torch.empty(max(need, 1), device=x.device, dtype=torch.uint8)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _nbytes(workspace)
     rc = _lib().kda_gate_bwd(ctypes.byref(d), _ptr(x), _ptr(A_log), _ptr(dt_bias), _ptr(dg),
                              _ptr(cu_seqlens), _ptr(dx), _ptr(dA), _ptr(db), _ptr(workspace),
                              ws_bytes, _stream())
@@ -242,8 +339,11 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     + SiLU to them in the kernel (kda_chunk_fwd_conv): FP32 taps [H*K, W] /
     [HV*V, W] (a [D, 1, W] Conv1d weight is accepted too), biases or None.
     Returns (o, final_state)."""
+    _validate_scan(q, k, v, gate, beta, initial_state, cu_seqlens, o=o, final_state=final_state,
+                   A_log=A_log)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"),
-                 (initial_state, "initial_state"), (cu_seqlens, "cu_seqlens"), (A_log, "A_log")):
+                 (initial_state, "initial_state"), (cu_seqlens, "cu_seqlens"), (A_log, "A_log"),
+                 (o, "o"), (final_state, "final_state"), (workspace, "workspace")):
         _check(t, n)
     if A_log is not None and not use_gate_in_kernel:
         raise ValueError("A_log needs use_gate_in_kernel=True (else pass it to gate_cumsum)")
@@ -256,7 +356,7 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     if not output_final_state:
         final_state = None
     need = int(_lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(d), dt, int(chunk_size)))
-    if workspace is None or workspace.numel() < need:
+    if workspace is None or _nbytes(workspace) < need:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
     kind = (KDA_GATE_RAW if gate_is_raw else KDA_GATE_NAT) if use_gate_in_kernel else KDA_GATE_LOG2
     if short_conv is not None:
@@ -265,7 +365,7 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
             ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), ctypes.byref(sc), _ptr(gate), kind,
             _ptr(A_log), int(bool(qk_l2norm)), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
             int(chunk_size), int(bool(output_final_state)), _ptr(o), _ptr(final_state),
-            _ptr(workspace), workspace.numel(), _stream())
+            _ptr(workspace), _nbytes(workspace), _stream())
         if rc:
             raise KdaError("kda_chunk_fwd_conv", rc)
         return o, final_state
@@ -274,7 +374,7 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
             ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), kind, _ptr(A_log), 1,
             _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size),
             int(bool(output_final_state)), _ptr(o), _ptr(final_state), _ptr(workspace),
-            workspace.numel(), _stream())
+            _nbytes(workspace), _stream())
         if rc:
             raise KdaError("kda_chunk_fwd_ex", rc)
         return o, final_state
@@ -283,14 +383,14 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
             ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), int(bool(gate_is_raw)),
             _ptr(A_log), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size),
             int(bool(output_final_state)), _ptr(o), _ptr(final_state), _ptr(workspace),
-            workspace.numel(), _stream())
+            _nbytes(workspace), _stream())
         if rc:
             raise KdaError("kda_chunk_fwd_fused_gate", rc)
         return o, final_state
     rc = _lib().kda_chunk_fwd(ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
                               _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size),
                               int(bool(output_final_state)), _ptr(o), _ptr(final_state),
-                              _ptr(workspace), workspace.numel(), _stream())
+                              _ptr(workspace), _nbytes(workspace), _stream())
     if rc:
         raise KdaError("kda_chunk_fwd", rc)
     return o, final_state
@@ -331,22 +431,27 @@ def chunk_kda_bwd(q, k, v, gate, beta, initial_state, do, dht=None, *, cu_seqlen
     """Steps B1..B3 (kda_chunk_bwd). Returns a dict with dq, dk (shape of q),
     dv (shape of v), dg (FP32, w.r.t. the per-token natural-log gate), dbeta
     and dh0 (FP32 [N, HV, K, V])."""
+    _validate_scan(q, k, v, gate, beta, initial_state, cu_seqlens, do=do, dht=dht)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (do, "do"),
-                 (initial_state, "initial_state"), (dht, "dht"), (cu_seqlens, "cu_seqlens")):
+                 (initial_state, "initial_state"), (dht, "dht"), (cu_seqlens, "cu_seqlens"),
+                 (workspace, "workspace")):
         _check(t, n)
     d = _dims(q, v, cu_seqlens)
     dt = _dtype_code(q)
-    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
-    dg = torch.zeros_like(gate)
-    dbeta = torch.zeros_like(beta)
+    # the kernels write every row inside a sequence: dense inputs need no fill;
+    # packed inputs get zeros in the capacity tail, which no kernel touches
+    new = torch.empty_like if cu_seqlens is None else torch.zeros_like
+    dq, dk, dv = new(q), new(k), new(v)
+    dg = new(gate)
+    dbeta = new(beta)
     dh0 = torch.empty((d.N, d.HV, d.K, d.V), device=q.device, dtype=torch.float32)
     need = int(_lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(d), dt, int(chunk_size)))
-    if workspace is None or workspace.numel() < need:
+    if workspace is None or _nbytes(workspace) < need:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
     rc = _lib().kda_chunk_bwd(ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
                               _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), _ptr(do),
                               _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta),
-                              _ptr(dh0), _ptr(workspace), workspace.numel(), _stream())
+                              _ptr(dh0), _ptr(workspace), _nbytes(workspace), _stream())
     if rc:
         raise KdaError("kda_chunk_bwd", rc)
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=dh0)
@@ -366,6 +471,14 @@ def short_conv(q, k, v, short_conv, *, cu_seqlens=None, conv_state=None, conv_st
     `conv_state_out` (may be conv_state itself; None = not kept). outputs=False
     computes the history only (prefill hand-off). `out` = (q_out, k_out, v_out)
     to write into (may be the inputs). Returns ((q, k, v) or None, conv_state_out)."""
+    if q.dim() != 4 or v.dim() != 4 or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q must be [B, T, H, K] and v [B, T, HV, V], bfloat16 or float32")
+    _expect(k, "k", tuple(q.shape), q.dtype)
+    _expect(v, "v", tuple(q.shape[:2]) + tuple(v.shape[2:]), q.dtype)
+    _cu_dims(cu_seqlens, q.shape[0])
+    if out is not None:
+        for t, ref, n in zip(out, (q, k, v), ("q_out", "k_out", "v_out")):
+            _expect(t, n, tuple(ref.shape), ref.dtype)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (cu_seqlens, "cu_seqlens"), (conv_state, "conv_state"),
                  (conv_state_out, "conv_state_out")):
         _check(t, n)
@@ -406,8 +519,11 @@ def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     training). Pass final_state=initial_state to update the states in place."""
     if any(t is not None and t.requires_grad for t in (q, k, v, gate, beta, initial_state)):
         raise RuntimeError("recurrent_kda is inference-only; inputs require grad (use chunk_kda)")
+    _validate_scan(q, k, v, gate, beta, initial_state, cu_seqlens, o=o, final_state=final_state,
+                   A_log=A_log)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"),
-                 (initial_state, "initial_state"), (cu_seqlens, "cu_seqlens"), (A_log, "A_log")):
+                 (initial_state, "initial_state"), (cu_seqlens, "cu_seqlens"), (A_log, "A_log"),
+                 (o, "o"), (final_state, "final_state"), (workspace, "workspace")):
         _check(t, n)
     if A_log is not None and not use_gate_in_kernel:
         raise ValueError("A_log needs use_gate_in_kernel=True (else pass it to gate_cumsum)")
@@ -428,13 +544,13 @@ def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
                                    or st.dtype != q.dtype):
                 raise ValueError(f"{n} must be {conv_state_shape(q, v, cu_seqlens, sc.width)} {q.dtype}")
         need = int(_lib().kda_recurrent_fwd_conv_workspace_bytes(ctypes.byref(d), dt))
-        if workspace is None or workspace.numel() < need:
+        if workspace is None or _nbytes(workspace) < need:
             workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
         rc = _lib().kda_recurrent_fwd_conv(
             ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), ctypes.byref(sc), _ptr(conv_state),
             _ptr(conv_state_out), _ptr(gate), kind, _ptr(A_log), int(bool(qk_l2norm)), _ptr(beta),
             _ptr(initial_state), _ptr(cu_seqlens), int(bool(output_final_state)), _ptr(o),
-            _ptr(final_state), _ptr(workspace), workspace.numel(), _stream())
+            _ptr(final_state), _ptr(workspace), _nbytes(workspace), _stream())
         if rc:
             raise KdaError("kda_recurrent_fwd_conv", rc)
         return o, final_state

@@ -445,10 +445,19 @@ kda_status kda_recurrent_fwd_conv(const kda_dims* d, kda_dtype dt, const void* q
                              st_in ? sb : 0, st_out ? sb : 0, A_log ? (size_t)d->HV * 4 : 0};
   for (int i = 0; i < 11; ++i)
     if (overlaps(workspace, need, others[i], others_n[i])) return KDA_ERR_ALIAS;
-  if (st_out && (overlaps(st_out, sb, o, s.v) || overlaps(st_out, sb, ht, s.state) ||
-                 overlaps(st_out, sb, q, s.qk) || overlaps(st_out, sb, k, s.qk) ||
-                 overlaps(st_out, sb, v, s.v)))
-    return KDA_ERR_ALIAS;
+  // the convolution writes the new history before the scan reads its inputs:
+  // the history may overlap nothing the scan reads or writes
+  if (st_out) {
+    const size_t nqk = (size_t)d->H * d->K, nv = (size_t)d->HV * d->V, W = (size_t)conv->width;
+    const void* scan_bufs[] = {o, ht, q, k, v, h0, gate, beta, A_log,
+                               conv->q_weight, conv->k_weight, conv->v_weight,
+                               conv->q_bias, conv->k_bias, conv->v_bias};
+    const size_t scan_n[] = {s.v, s.state, s.qk, s.qk, s.v, s.state, s.gate, s.beta,
+                             A_log ? (size_t)d->HV * 4 : 0, nqk * W * 4, nqk * W * 4, nv * W * 4,
+                             nqk * 4, nqk * 4, nv * 4};
+    for (int i = 0; i < 15; ++i)
+      if (overlaps(st_out, sb, scan_bufs[i], scan_n[i])) return KDA_ERR_ALIAS;
+  }
   if (A_log && (overlaps(A_log, (size_t)d->HV * 4, o, s.v) ||
                 overlaps(A_log, (size_t)d->HV * 4, ht, s.state)))
     return KDA_ERR_ALIAS;

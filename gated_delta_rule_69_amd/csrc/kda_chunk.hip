@@ -105,7 +105,7 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
   // W, Q~Gamma, Khat and P from L2, so blocks are as wide as possible while
   // the grid still has a workgroup for every compute unit.
   const int64_t chains = (int64_t)d.N * d.HV;
-  const int bv = scan_block_v(chains, V);
+  const int bv = scan_block_v(chains, V, kda_host::device_cus());
   // 4 waves per workgroup (8, with half the tiles per wave, measured slower:
   // more LDS traffic and wider barriers for the same chain latency)
   auto launch_scan = [&](auto bvc) {

@@ -1160,8 +1160,7 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
                        (const int*)ws_int, cu, (const T*)dO, dht, d.N, d.T, d.HV, dh0);
     return hipGetLastError();
   };
-  constexpr int64_t kCUs = 256;
-  e = chains * (V / 32) < kCUs ? launch_scans(std::integral_constant<int, 16>())
+  e = chains * (V / 32) < kda_host::device_cus() ? launch_scans(std::integral_constant<int, 16>())
                                 : launch_scans(std::integral_constant<int, 32>());
   if (e != hipSuccess) return e;
   // the instantiations the entry point accepts (bf16; FP32 with K = 64) stay within 158 KiB of

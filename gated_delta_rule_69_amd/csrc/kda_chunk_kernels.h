@@ -1477,10 +1477,9 @@ inline int64_t max_chunks(const kda_dims& d, bool varlen) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline int scan_block_v(int64_t chains, int V) {
-  constexpr int64_t kCUs = 256;
+inline int scan_block_v(int64_t chains, int V, int cus) {
   int bv = 64;
-  while (bv > 16 && chains * (V / bv) < kCUs) bv >>= 1;
+  while (bv > 16 && chains * (V / bv) < cus) bv >>= 1;
   return bv > V ? V : bv;
 }
 

@@ -80,10 +80,12 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 constexpr float kLn2 = 0.6931471805599453f;
 
 // softplus(x) = ln(1 + e^x) = max(x, 0) + ln(1 + z), z = e^{-|x|} in (0, 1],
-// on the transcendental unit. ln(1 + z) uses the classic correction
-// ln(u) * z / (u - 1) with u = 1 + z (u - 1 is exact), which keeps full
-// relative accuracy for small z; the quotient (a factor within an ulp of 1)
-// takes the hardware reciprocal. Above 20 the result is x itself.
+// on the transcendental unit. ln(1 + z) is computed as ln(u) * z / (u - 1)
+// with u = 1 + z (u - 1 is exact), the log1p method of D. Goldberg, "What
+// every computer scientist should know about floating-point arithmetic"
+// (ACM Computing Surveys, 1991), Theorem 4, which keeps full relative accuracy
+// for small z; the quotient (a factor within an ulp of 1) takes the hardware
+// reciprocal. Above 20 the result is x itself.
 // Branch-free (selects), so loads around it can stay batched. No FMA
 // contraction, so every kernel that inlines it rounds the same way.
 __device__ __forceinline__ float softplus_f32(float x) {
@@ -162,6 +164,15 @@ __device__ __forceinline__ void seq_range(const int32_t* cu, int n, int T, int64
 
 // Host-side launchers (defined in the .hip files, called by the C ABI).
 namespace kda_host {
+// Compute units of the calling thread's current device (256 on MI355X), for
+// launch shapes that must give every compute unit a workgroup.
+inline int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
 hipError_t launch_gate(const kda_dims& d, const float* in, int is_raw, const float* A_log,
                        const float* dt_bias, const int32_t* cu, int chunk, float* out,
                        hipStream_t s);

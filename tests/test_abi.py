@@ -284,6 +284,22 @@ def test_short_conv_and_conv_decode_reject_bad_arguments():
     assert rec(taps(), ws=FAKE[5]) == 5                    # workspace over o
     assert rec(taps(), ws=ctypes.c_void_p(FAKE[13].value + 16)) == 4
 
+    def rec_hist(st_out, h0=None, A_log=None):
+        return lib.kda_recurrent_fwd_conv(ctypes.byref(d), 1, FAKE[0], FAKE[1], FAKE[2],
+                                          ctypes.byref(taps()), None, st_out, FAKE[3], 2, A_log, 1,
+                                          FAKE[4], h0, None, 1, FAKE[5], FAKE[6], FAKE[13], 1 << 40,
+                                          None)
+
+    # the new history is written before the scan reads its inputs: it may overlap
+    # none of them (initial state, gate, beta, A_log, taps), nor o or the states
+    assert rec_hist(FAKE[9], h0=FAKE[9]) == 5      # history over the initial state
+    assert rec_hist(FAKE[3]) == 5                  # over the gate
+    assert rec_hist(FAKE[4]) == 5                  # over beta
+    assert rec_hist(FAKE[8], A_log=FAKE[8]) == 5   # over A_log
+    assert rec_hist(FAKE[10]) == 5                 # over the q taps
+    assert rec_hist(FAKE[12]) == 5                 # over the v taps
+    assert rec_hist(FAKE[5]) == 5                  # over o
+
 
 def test_prefill_and_step_ops_fake_shapes_on_meta_tensors():
     import torch
