@@ -53,8 +53,11 @@ struct Ws {
   static constexpr size_t QG = (size_t)kC * K;   // Q~*Gamma      [4][K/KSTEP][64][PER]
   static constexpr size_t KH = (size_t)K * kC;   // Khat^T        [K/16][C/KSTEP][64][PER]
   static constexpr size_t P = (size_t)kC * kC;   // P             [4][C/KSTEP][64][PER]
+  // bf16: P - bf16(P) (same fragment order), so the output's intra-chunk
+  // product P Delta sees P to about 16 mantissa bits; FP32 P is exact
+  static constexpr size_t PL = sizeof(T) == 2 ? (size_t)kC * kC : 0;
   static constexpr size_t U = (size_t)kC * V;    // U accum order [4][V/16][64][4]
-  static constexpr size_t elems = W + QG + KH + P + U;
+  static constexpr size_t elems = W + QG + KH + P + PL + U;
   static constexpr size_t bytes_T = elems * sizeof(T);
   static constexpr size_t bytes_GL = (size_t)K * sizeof(float);  // Gamma_last (FP32)
 };
@@ -280,6 +283,58 @@ __device__ __forceinline__ void put_quad(typename M::frag* fr, int p, const floa
 #pragma unroll
     for (int e = 0; e < 4; ++e) M::set(fr[4 * p + e], 0, v[e]);
   }
+}
+
+// A fragment carried as an unevaluated sum hi + lo of two bf16 values (about
+// 16 mantissa bits): hi = bf16(x), lo = bf16(x - hi), where x - hi is exact in
+// FP32. Products of such operands take three matrix-core steps (hi hi, hi lo,
+// lo hi; lo lo is below FP32 accumulation noise). For FP32 fragments the
+// value is exact already and lo does not exist.
+template <typename M>
+struct Frag2 {
+  typename M::frag hi;
+  typename M::frag lo;
+};
+template <>
+struct Frag2<MF<float>> {
+  typename MF<float>::frag hi;
+};
+template <typename M>
+__device__ __forceinline__ void put_quad2(Frag2<M>* fr, int p, const float v[4]) {
+  if constexpr (M::KSTEP == 32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16 h = (bf16)v[e];
+      fr[p >> 1].hi[4 * (p & 1) + e] = h;
+      fr[p >> 1].lo[4 * (p & 1) + e] = (bf16)(v[e] - (float)h);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) M::set(fr[4 * p + e].hi, 0, v[e]);
+  }
+}
+// c + a b with both operands split
+template <typename M>
+__device__ __forceinline__ f32x4 mma3(const Frag2<M>& a, const Frag2<M>& b, f32x4 c) {
+  c = M::mma(a.hi, b.hi, c);
+  if constexpr (M::KSTEP == 32) {
+    c = M::mma(a.hi, b.lo, c);
+    c = M::mma(a.lo, b.hi, c);
+  }
+  return c;
+}
+// c + a b with only b split (a exact in bf16), resp. only a split
+template <typename M>
+__device__ __forceinline__ f32x4 mma2(const typename M::frag& a, const Frag2<M>& b, f32x4 c) {
+  c = M::mma(a, b.hi, c);
+  if constexpr (M::KSTEP == 32) c = M::mma(a, b.lo, c);
+  return c;
+}
+template <typename M>
+__device__ __forceinline__ f32x4 mma2(const Frag2<M>& a, const typename M::frag& b, f32x4 c) {
+  c = M::mma(a.hi, b, c);
+  if constexpr (M::KSTEP == 32) c = M::mma(a.lo, b, c);
+  return c;
 }
 
 // Fragment of contraction step ks built from accumulator tiles of the
@@ -576,50 +631,94 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   // the recursive passes below.
   const bool mid = (lstar == 0) && !need_diag;
   const int r = 16 * I + (mid ? 8 : 0);
-  F lkf[KS_K], lqf[KS_K];  // column factors k_i 2^(G2_i - G2_r), q~_i 2^(G2_i - G2_r)
-#pragma unroll
-  for (int p = 0; p < QK; ++p) {
-    const int c0 = 16 * p + 4 * g;
-    float gi[4], g0[4], ki[4], qi[4], vk[4], vq[4];
-    lds4(sG + icol * GS + c0, gi);
-    lds4(sG + r * GS + c0, g0);
-    lds4(sK + icol * KSTR + c0, ki);
-    lds4(sQ + icol * KSTR + c0, qi);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = ex2(gi[e] - g0[e]);
-      vk[e] = ki[e] * x;
-      vq[e] = qi[e] * scale * x;
-    }
-    put_quad<M>(lkf, p, vk);
-    put_quad<M>(lqf, p, vq);
-  }
+  // The decay-scaled operands of A and P are not exact in bf16, and their
+  // rounding, amplified by the cancellation in the channel sums, would
+  // otherwise be the largest error of the bf16 forward: every one of them is
+  // split hi + lo (Frag2, three matrix-core steps per product). To keep the
+  // split operands within the register budget the channel sums run over
+  // halves of K (64 channels each), building one half's operands at a time.
+  constexpr int NHF = K >= 128 ? 2 : 1;  // channel halves
+  constexpr int QH = QK / NHF;           // quads per half
+  constexpr int FH = KS_K / NHF;         // fragments per half
   f32x4 accA[3], accP[3];            // tiles J < I
   f32x4 dA = zero4(), dP = zero4();  // tile J == I
   f32x4 pT[3], dPT = zero4();        // BWD: P tiles (rows i, cols j), J < I and J == I
 #pragma unroll
-  for (int J = 0; J < 3; ++J) {
-    accA[J] = accP[J] = pT[J] = zero4();
-    if (J < I) {
-      const int jrow = 16 * J + l16;
-      F rf[KS_K];  // row factors k_j 2^(G2_r - G2_j) (<= 1: j < 16I <= r)
+  for (int J = 0; J < 3; ++J) accA[J] = accP[J] = pT[J] = zero4();
+  f32x4 xa = zero4(), xp = zero4(), xt = zero4();  // diagonal tile, one-pass reference
 #pragma unroll
-      for (int p = 0; p < QK; ++p) {
-        const int c0 = 16 * p + 4 * g;
+  for (int hf = 0; hf < NHF; ++hf) {
+    // column factors k_i 2^(G2_i - G2_r), q~_i 2^(G2_i - G2_r) of this half
+    Frag2<M> lkf[FH], lqf[FH];
+#pragma unroll
+    for (int pp = 0; pp < QH; ++pp) {
+      const int c0 = 16 * (QH * hf + pp) + 4 * g;
+      float gi[4], g0[4], ki[4], qi[4], vk[4], vq[4];
+      lds4(sG + icol * GS + c0, gi);
+      lds4(sG + r * GS + c0, g0);
+      lds4(sK + icol * KSTR + c0, ki);
+      lds4(sQ + icol * KSTR + c0, qi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = ex2(gi[e] - g0[e]);
+        vk[e] = ki[e] * x;
+        vq[e] = qi[e] * scale * x;
+      }
+      put_quad2<M>(lkf, pp, vk);
+      put_quad2<M>(lqf, pp, vq);
+    }
+#pragma unroll
+    for (int J = 0; J < 3; ++J) {
+      if (J < I) {
+        const int jrow = 16 * J + l16;
+        Frag2<M> rf[FH];  // row factors k_j 2^(G2_r - G2_j) (<= 1: j < 16I <= r)
+#pragma unroll
+        for (int pp = 0; pp < QH; ++pp) {
+          const int c0 = 16 * (QH * hf + pp) + 4 * g;
+          float gj[4], g0[4], kj[4], vv[4];
+          lds4(sG + jrow * GS + c0, gj);
+          lds4(sG + r * GS + c0, g0);
+          lds4(sK + jrow * KSTR + c0, kj);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[e] = kj[e] * ex2(g0[e] - gj[e]);
+          put_quad2<M>(rf, pp, vv);
+        }
+#pragma unroll
+        for (int ks = 0; ks < FH; ++ks) {
+          accA[J] = mma3<M>(rf[ks], lkf[ks], accA[J]);
+          accP[J] = mma3<M>(rf[ks], lqf[ks], accP[J]);
+          if constexpr (BWD) pT[J] = mma3<M>(lqf[ks], rf[ks], pT[J]);
+        }
+      }
+    }
+    if (mid) {
+      Frag2<M> ra[FH];  // k_j 2^(G2_r - G2_j), within 2^-+kFastRange
+#pragma unroll
+      for (int pp = 0; pp < QH; ++pp) {
+        const int c0 = 16 * (QH * hf + pp) + 4 * g;
         float gj[4], g0[4], kj[4], vv[4];
         lds4(sG + jrow * GS + c0, gj);
         lds4(sG + r * GS + c0, g0);
         lds4(sK + jrow * KSTR + c0, kj);
 #pragma unroll
         for (int e = 0; e < 4; ++e) vv[e] = kj[e] * ex2(g0[e] - gj[e]);
-        put_quad<M>(rf, p, vv);
+        put_quad2<M>(ra, pp, vv);
       }
 #pragma unroll
-      for (int ks = 0; ks < KS_K; ++ks) {
-        accA[J] = M::mma(rf[ks], lkf[ks], accA[J]);
-        accP[J] = M::mma(rf[ks], lqf[ks], accP[J]);
-        if constexpr (BWD) pT[J] = M::mma(lqf[ks], rf[ks], pT[J]);
+      for (int ks = 0; ks < FH; ++ks) {
+        xa = mma3<M>(ra[ks], lkf[ks], xa);
+        xp = mma3<M>(ra[ks], lqf[ks], xp);
+        if constexpr (BWD) xt = mma3<M>(lqf[ks], ra[ks], xt);
       }
+    }
+  }
+  if (mid) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int jr = 4 * g + e;
+      dA[e] = (il > jr) ? xa[e] : 0.f;
+      dP[e] = (il >= jr) ? xp[e] : 0.f;
+      dPT[e] = (jr >= l16) ? xt[e] : 0.f;  // P tile: row i = 4g + e, column j = l16
     }
   }
   // Diagonal tile, recursive mid-point references. Pass `lev` (0..3) splits
@@ -632,68 +731,43 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   // at most kFastRange. The passes stop at the first level where that holds
   // for all segments (one pass for moderate gates); if even single tokens
   // exceed it, a last pass adds the diagonal i == j (decay factor 1).
-  if (mid) {
-    F ra[KS_K];  // k_j 2^(G2_r - G2_j), within 2^-+kFastRange
-#pragma unroll
-    for (int p = 0; p < QK; ++p) {
-      const int c0 = 16 * p + 4 * g;
-      float gj[4], g0[4], kj[4], vv[4];
-      lds4(sG + jrow * GS + c0, gj);
-      lds4(sG + r * GS + c0, g0);
-      lds4(sK + jrow * KSTR + c0, kj);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vv[e] = kj[e] * ex2(g0[e] - gj[e]);
-      put_quad<M>(ra, p, vv);
-    }
-    f32x4 xa = zero4(), xp = zero4(), xt = zero4();
-#pragma unroll
-    for (int ks = 0; ks < KS_K; ++ks) {
-      xa = M::mma(ra[ks], lkf[ks], xa);
-      xp = M::mma(ra[ks], lqf[ks], xp);
-      if constexpr (BWD) xt = M::mma(lqf[ks], ra[ks], xt);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int jr = 4 * g + e;
-      dA[e] = (il > jr) ? xa[e] : 0.f;
-      dP[e] = (il >= jr) ? xp[e] : 0.f;
-      dPT[e] = (jr >= l16) ? xt[e] : 0.f;  // P tile: row i = 4g + e, column j = l16
-    }
-  }
   for (int lev = 0; !mid && lev <= lstar; ++lev) {
     const int S = 16 >> lev;
     const bool final_pass = (lev == lstar) && !need_diag;
     const int mj = 16 * I + (jl / S) * S + S / 2;  // reference of row j
     const int mi = 16 * I + (il / S) * S + S / 2;  // reference of column i
-    F ra[KS_K], lk[KS_K], lq[KS_K];
+    f32x4 ya = zero4(), yp = zero4(), yt = zero4();
 #pragma unroll
-    for (int p = 0; p < QK; ++p) {
-      const int c0 = 16 * p + 4 * g;
-      float kj[4], ki[4], qi[4], gj[4], gmj[4], gi[4], gmi[4], va[4], vk[4], vq[4];
-      lds4(sK + jrow * KSTR + c0, kj);
-      lds4(sK + icol * KSTR + c0, ki);
-      lds4(sQ + icol * KSTR + c0, qi);
-      lds4(sG + jrow * GS + c0, gj);
-      lds4(sG + mj * GS + c0, gmj);
-      lds4(sG + icol * GS + c0, gi);
-      lds4(sG + mi * GS + c0, gmi);
+    for (int hf = 0; hf < NHF; ++hf) {
+      Frag2<M> ra[FH], lk[FH], lq[FH];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        va[e] = kj[e] * ex2(gmj[e] - gj[e]);
-        const float x = ex2(gi[e] - gmi[e]);
-        vk[e] = ki[e] * x;
-        vq[e] = qi[e] * scale * x;
+      for (int pp = 0; pp < QH; ++pp) {
+        const int c0 = 16 * (QH * hf + pp) + 4 * g;
+        float kj[4], ki[4], qi[4], gj[4], gmj[4], gi[4], gmi[4], va[4], vk[4], vq[4];
+        lds4(sK + jrow * KSTR + c0, kj);
+        lds4(sK + icol * KSTR + c0, ki);
+        lds4(sQ + icol * KSTR + c0, qi);
+        lds4(sG + jrow * GS + c0, gj);
+        lds4(sG + mj * GS + c0, gmj);
+        lds4(sG + icol * GS + c0, gi);
+        lds4(sG + mi * GS + c0, gmi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          va[e] = kj[e] * ex2(gmj[e] - gj[e]);
+          const float x = ex2(gi[e] - gmi[e]);
+          vk[e] = ki[e] * x;
+          vq[e] = qi[e] * scale * x;
+        }
+        put_quad2<M>(ra, pp, va);
+        put_quad2<M>(lk, pp, vk);
+        put_quad2<M>(lq, pp, vq);
       }
-      put_quad<M>(ra, p, va);
-      put_quad<M>(lk, p, vk);
-      put_quad<M>(lq, p, vq);
-    }
-    f32x4 xa = zero4(), xp = zero4(), xt = zero4();
 #pragma unroll
-    for (int ks = 0; ks < KS_K; ++ks) {
-      xa = M::mma(ra[ks], lk[ks], xa);
-      xp = M::mma(ra[ks], lq[ks], xp);
-      if constexpr (BWD) xt = M::mma(lq[ks], ra[ks], xt);
+      for (int ks = 0; ks < FH; ++ks) {
+        ya = mma3<M>(ra[ks], lk[ks], ya);
+        yp = mma3<M>(ra[ks], lq[ks], yp);
+        if constexpr (BWD) yt = mma3<M>(lq[ks], ra[ks], yt);
+      }
     }
     // pair (row a, column b) belongs to this pass: same segment, and either
     // the last pass or straddling the segment's middle
@@ -704,41 +778,45 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     for (int e = 0; e < 4; ++e) {
       const int jr = 4 * g + e;  // local row j of this accumulator element, column i = il
       if (take(jr, il)) {
-        if (il > jr) dA[e] += xa[e];
-        if (il >= jr) dP[e] += xp[e];
+        if (il > jr) dA[e] += ya[e];
+        if (il >= jr) dP[e] += yp[e];
       }
       if constexpr (BWD) {
         // transposed tile: row i = 4g + e, column j = l16
-        if (take(l16, jr) && jr >= l16) dPT[e] += xt[e];
+        if (take(l16, jr) && jr >= l16) dPT[e] += yt[e];
       }
     }
   }
   if (!mid && need_diag) {
-    // i == j: P_ii = q~_i . k_i (no decay)
-    F ra[KS_K], lq[KS_K];
+    // i == j: P_ii = q~_i . k_i (no decay; k is exact in its dtype, q~ is split)
+    f32x4 yp = zero4(), yt = zero4();
 #pragma unroll
-    for (int p = 0; p < QK; ++p) {
-      const int c0 = 16 * p + 4 * g;
-      float kj[4], qi[4], vq[4];
-      lds4(sK + jrow * KSTR + c0, kj);
-      lds4(sQ + icol * KSTR + c0, qi);
+    for (int hf = 0; hf < NHF; ++hf) {
+      F ra[FH];
+      Frag2<M> lq[FH];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vq[e] = qi[e] * scale;
-      put_quad<M>(ra, p, kj);
-      put_quad<M>(lq, p, vq);
-    }
-    f32x4 xp = zero4(), xt = zero4();
+      for (int pp = 0; pp < QH; ++pp) {
+        const int c0 = 16 * (QH * hf + pp) + 4 * g;
+        float kj[4], qi[4], vq[4];
+        lds4(sK + jrow * KSTR + c0, kj);
+        lds4(sQ + icol * KSTR + c0, qi);
 #pragma unroll
-    for (int ks = 0; ks < KS_K; ++ks) {
-      xp = M::mma(ra[ks], lq[ks], xp);
-      if constexpr (BWD) xt = M::mma(lq[ks], ra[ks], xt);
+        for (int e = 0; e < 4; ++e) vq[e] = qi[e] * scale;
+        put_quad<M>(ra, pp, kj);
+        put_quad2<M>(lq, pp, vq);
+      }
+#pragma unroll
+      for (int ks = 0; ks < FH; ++ks) {
+        yp = mma2<M>(ra[ks], lq[ks], yp);
+        if constexpr (BWD) yt = mma2<M>(lq[ks], ra[ks], yt);
+      }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int jr = 4 * g + e;
-      if (jr == il) dP[e] += xp[e];
+      if (jr == il) dP[e] += yp[e];
       if constexpr (BWD) {
-        if (jr == l16) dPT[e] += xt[e];
+        if (jr == l16) dPT[e] += yt[e];
       }
     }
   }
@@ -747,7 +825,8 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   T* wsQG = wsW + WsL::W;
   T* wsKH = wsQG + WsL::QG;
   T* wsP = wsKH + WsL::KH;
-  T* wsU = wsP + WsL::P;
+  T* wsPL = wsP + WsL::P;
+  T* wsU = wsPL + WsL::PL;
   float* wsGL = ws_GL + ch * K;
 
   // ---- 3. P fragments (rows i of tile I, contraction over j): accumulators of P^T
@@ -756,7 +835,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   if constexpr (!BWD) {
 #pragma unroll
     for (int ks = 0; ks < KS_C; ++ks) {
-      F f;
+      F f, fl;
 #pragma unroll
       for (int jj = 0; jj < M::PER; ++jj) {
         const int tile = acc_tile<M>(ks, jj), el = acc_elem<M>(ks, jj);
@@ -765,8 +844,10 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         for (int J = 0; J < 4; ++J)
           if (J == tile) x = (J < I) ? accP[J < 3 ? J : 0][el] : (J == I ? dP[el] : 0.f);
         M::set(f, jj, x);
+        if constexpr (WsL::PL > 0) M::set(fl, jj, x - M::get(f, jj));
       }
       reinterpret_cast<F*>(wsP)[((size_t)I * KS_C + ks) * 64 + lane] = f;
+      if constexpr (WsL::PL > 0) reinterpret_cast<F*>(wsPL)[((size_t)I * KS_C + ks) * 64 + lane] = fl;
     }
   }
   if constexpr (BWD) {
@@ -1046,28 +1127,24 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
       }
     }
   }
-  __syncthreads();  // G2 and k are dead: R1 <- b V (row-major)
+  __syncthreads();  // G2 and k are dead: R1 <- V (row-major)
   constexpr int VSTR = Lds::VSTR;
-  T* sV = reinterpret_cast<T*>(smem);  // R1: b v [C][VSTR]
+  T* sV = reinterpret_cast<T*>(smem);  // R1: v [C][VSTR]
 #pragma unroll
   for (int u = 0; u < VU; ++u) {
     const int m = vrow(tid, u), cu_ = tid % TV;
-    const float b = sBeta[m];
-    union {
-      T t[EPU];
-      uint4 u;
-    } tmp;
-#pragma unroll
-    for (int e = 0; e < EPU; ++e) tmp.t[e] = from_f32<T>(b * unit_elem<T>(vr[u], e));
-    *reinterpret_cast<uint4*>(sV + m * VSTR + EPU * cu_) = tmp.u;
+    *reinterpret_cast<uint4*>(sV + m * VSTR + EPU * cu_) = vr[u];
   }
   __syncthreads();
 
-  // ---- 9. U = T (b V), same wave split over value tiles; accumulator order
+  // ---- 9. U = (T diag(b)) V, same wave split over value tiles; accumulator
+  // order. b scales T's columns, so V enters the product exactly as loaded
+  // (rounding b v to bf16 instead costs about as much accuracy as rounding
+  // the output).
   {
     constexpr int NP = V / 32;
     const int pw = wave % NP, I0 = (wave / NP) * NP;
-    // the wave's two value tiles of b V as B fragments (column gathers from
+    // the wave's two value tiles of V as B fragments (column gathers from
     // LDS), built once and shared by its NP row tiles of T
     F vb[2][KS_C];
 #pragma unroll
@@ -1086,8 +1163,11 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
       F ta[KS_C];
 #pragma unroll
       for (int p = 0; p < QC; ++p) {
-        float t4[4];
+        float t4[4], b4[4];
         lds4(sA + (16 * (I0 + ii) + l16) * AS + 16 * p + 4 * g, t4);
+        lds4(sBeta + 16 * p + 4 * g, b4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t4[e] *= b4[e];
         put_quad<M>(ta, p, t4);
       }
 #pragma unroll
@@ -1193,8 +1273,9 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
   }
 
   // per-chunk operands of this wave, loaded one chunk ahead
+  constexpr int NPL = WsL::PL > 0 ? KS_C : 1;  // P low parts (bf16 only)
   struct Ops {
-    F w[KS_K], qg[KS_K], p[KS_C], kh[RTW][KS_C];
+    F w[KS_K], qg[KS_K], p[KS_C], pl[NPL], kh[RTW][KS_C];
     raw4 u[CPW];
     float4 gl[RTW];
   };
@@ -1205,7 +1286,8 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     const F* fQG = reinterpret_cast<const F*>(wsW + WsL::W);
     const F* fKH = reinterpret_cast<const F*>(wsW + WsL::W + WsL::QG);
     const F* fP = reinterpret_cast<const F*>(wsW + WsL::W + WsL::QG + WsL::KH);
-    const T* wsU = wsW + WsL::W + WsL::QG + WsL::KH + WsL::P;
+    const F* fPL = reinterpret_cast<const F*>(wsW + WsL::W + WsL::QG + WsL::KH + WsL::P);
+    const T* wsU = wsW + WsL::W + WsL::QG + WsL::KH + WsL::P + WsL::PL;
 #pragma unroll
     for (int ks = 0; ks < KS_K; ++ks) {
       op.w[ks] = fW[((size_t)tt * KS_K + ks) * 64 + lane];
@@ -1213,7 +1295,10 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     }
     if constexpr (!KEEP) {
 #pragma unroll
-      for (int ks = 0; ks < KS_C; ++ks) op.p[ks] = fP[((size_t)tt * KS_C + ks) * 64 + lane];
+      for (int ks = 0; ks < KS_C; ++ks) {
+        op.p[ks] = fP[((size_t)tt * KS_C + ks) * 64 + lane];
+        if constexpr (WsL::PL > 0) op.pl[ks] = fPL[((size_t)tt * KS_C + ks) * 64 + lane];
+      }
     }
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
@@ -1257,7 +1342,7 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
   // (intact until the step after next).
   constexpr bool CACHE = !KEEP && sizeof(T) == 2 && CTB <= 2;
   struct OutOps {
-    F qg[KS_K], p[KS_C];
+    F qg[KS_K], p[KS_C], pl[NPL];
     F sf[CACHE ? KS_K : 1][CACHE ? CPW : 1];  // S0 fragments (value tiles ct0..)
     F df[CACHE ? KS_C : 1][CACHE ? CPW : 1];  // Delta fragments (value tiles ct0..)
   };
@@ -1280,8 +1365,11 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     for (int ks = 0; ks < KS_C; ++ks)
 #pragma unroll
       for (int cc = 0; cc < CPW; ++cc) {
-        if constexpr (CACHE) OT[cc] = M::mma(op.df[ks][cc], op.p[ks], OT[cc]);
-        else OT[cc] = M::mma(sD[buf][ks][ct0 + cc][lane], op.p[ks], OT[cc]);
+        F dfr;
+        if constexpr (CACHE) dfr = op.df[ks][cc];
+        else dfr = sD[buf][ks][ct0 + cc][lane];
+        OT[cc] = M::mma(dfr, op.p[ks], OT[cc]);
+        if constexpr (WsL::PL > 0) OT[cc] = M::mma(dfr, op.pl[ks], OT[cc]);
       }
     const int i = 16 * tt + l16;
     if (i < L && o) {
@@ -1429,7 +1517,10 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
 #pragma unroll
       for (int ks = 0; ks < KS_K; ++ks) mine.qg[ks] = cur.qg[ks];
 #pragma unroll
-      for (int ks = 0; ks < KS_C; ++ks) mine.p[ks] = cur.p[ks];
+      for (int ks = 0; ks < KS_C; ++ks) {
+        mine.p[ks] = cur.p[ks];
+        if constexpr (WsL::PL > 0) mine.pl[ks] = cur.pl[ks];
+      }
     }
   };
 
