@@ -16,12 +16,18 @@ two-call path (kda_gate_cumsum(chunk 1) + kda_recurrent_fwd) beside it.
 
 Timing: HIP events on torch's current stream, which is the stream every libkda
 call in this process is enqueued on. Warmup W steps, then exactly K timed
-steps between two device synchronisations.
+steps between two device synchronisations (`value`, `ms_per_step`). Beside it,
+every workload is also timed cold the way the pages' benchmark table is
+(`do_bench`, warmup 100, rep 300, median with p20 / p80): each rep is bracketed
+by its own HIP events, with a 1 GiB write between reps so that no operand is
+left in the 256 MB Infinity Cache (`cold` fields).
 
 `roofline` reports the step's entry point (its two kernels, intra-chunk and
 scan) against MI355X's 8 TB/s HBM peak with algorithmic bytes (inputs read
-once, outputs written once). `cpu_baseline` times the FP64 oracle on the host cores over the
-same dense batch (median of 3 runs).
+once, outputs written once), and against the peaks measured on the same box
+(`measured_peaks`: a 1 GiB device copy for HBM, a large bf16 GEMM for the
+matrix cores). `cpu_baseline` times the FP64 oracle on the host cores over the
+same dense batch (median of 3 runs), plus one thread on a bounded sample.
 """
 from __future__ import annotations
 
@@ -70,6 +76,8 @@ def _args():
                    default=None,
                    help="run only one workload a few times (for rocprofv3), print no JSON")
     p.add_argument("--profile-reps", type=int, default=3)
+    p.add_argument("--cold-reps", type=int, default=300, help="reps of the cold-cache timing")
+    p.add_argument("--cold-warmup", type=int, default=100)
     return p.parse_args()
 
 
@@ -253,6 +261,49 @@ def main():
         wall = (time.perf_counter() - t0) * 1e3 / reps
         return wall, e0.elapsed_time(e1) / reps
 
+    # a write of 1 GiB between cold reps evicts every operand from the 256 MB
+    # Infinity Cache and the L2s (the pages' benchmark clears the cache the same way)
+    flush_buf = torch.empty(1 << 28, device=dev, dtype=torch.float32)
+
+    def cold(fn, reps=None, warm=None, scale=1.0):
+        """p20 / p50 / p80 of per-call HIP-event durations (ms), each call
+        preceded by the cache flush, after `warm` untimed calls."""
+        reps = reps or a.cold_reps
+        warm = a.cold_warmup if warm is None else warm
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            flush_buf.zero_()
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        t = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * scale
+        return {"p20": round(float(np.percentile(t, 20)), 4), "p50": round(float(np.median(t)), 4),
+                "p80": round(float(np.percentile(t, 80)), 4), "reps": reps, "warmup": warm}
+
+    # ---------------- measured peaks on this box
+    progress("measured peaks")
+    cpy_src = torch.empty(1 << 28, device=dev, dtype=torch.float32).fill_(1.0)
+    cpy_dst = torch.empty_like(cpy_src)
+    _, cpy_ms = timed_region(lambda: cpy_dst.copy_(cpy_src), 20, 3)
+    hbm_meas = 2 * cpy_src.numel() * 4 / (cpy_ms * 1e-3) / 1e9
+    del cpy_src, cpy_dst
+    gm = 8192
+    ga = torch.randn(gm, gm, device=dev, dtype=bf)
+    gbm = torch.randn(gm, gm, device=dev, dtype=bf)
+    gc = torch.empty(gm, gm, device=dev, dtype=bf)
+    _, gemm_ms = timed_region(lambda: torch.matmul(ga, gbm, out=gc), 20, 3)
+    mfma_meas = 2 * gm ** 3 / (gemm_ms * 1e-3) / 1e12
+    del ga, gbm, gc
+    measured = {"hbm_copy_GBps": round(hbm_meas, 1),
+                "hbm_copy_note": "1 GiB device-to-device copy (read + write bytes / time)",
+                "bf16_gemm_TFLOPs": round(mfma_meas, 1),
+                "bf16_gemm_note": f"torch.matmul (hipBLASLt) {gm}x{gm}x{gm} bf16, FP32 accumulation"}
+
     # ---------------- chunked forward workload
     progress("dense chunked forward")
     wl = workloads.workload2()
@@ -307,6 +358,8 @@ def main():
     _, cv_ms = timed_region(step_conv, a.steps, a.warmup)
     del qr, kr, taps
 
+    cold_dense = cold(step)
+    cold_dense2 = cold(lambda: (gate_call(), chunk_call()))
     cb = chunk_fwd_bytes(B, T, H, HV, K, V)
     gb = gate_bytes(B, T, HV, K)
     fused_gbs = cb / (f_ms * 1e-3) / 1e9
@@ -318,7 +371,11 @@ def main():
                 kernel="kda_chunk_fwd_fused_gate (chunk_intra_kernel + chunk_scan_kernel)",
                 algorithmic_bytes=cb, avg_ms=round(f_ms, 4),
                 mfma_tflops=round(flops / (f_ms * 1e-3) / 1e12, 2),
-                mfma_frac=round(flops / (f_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4))
+                mfma_frac=round(flops / (f_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                frac_of_measured_hbm=round(fused_gbs / hbm_meas, 4),
+                mfma_frac_of_measured=round(flops / (f_ms * 1e-3) / 1e12 / mfma_meas, 4),
+                cold_p50_ms=cold_dense["p50"],
+                cold_frac=round(cb / (cold_dense["p50"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
 
     # ---------------- recurrent decode workload
     progress("recurrent decode")
@@ -348,6 +405,7 @@ def main():
     dec2_us = timed_region(dstep2, a.decode_steps, 20)[0] * 1e3
     g1_us = timed_region(dgate, a.decode_steps, 20)[1] * 1e3
     rec_us = timed_region(drec, a.decode_steps, 20)[1] * 1e3
+    cold_dec = cold(dstep, scale=1e3)
     ntok = int(wd.cu_seqlens[-1])
     dbytes = decode_bytes(ntok, wd.H, wd.HV, wd.K, wd.V)
     fused_dec_gbs = dbytes / (fused_us * 1e-6) / 1e9
@@ -412,6 +470,8 @@ def main():
             "recurrent_us": round(time_it(tiny_rec, 200) * 1e3, 2),
             "two_call_chunk_us": round(time_it(tiny_chunk2, 200) * 1e3, 2),
             "two_call_recurrent_us": round(time_it(tiny_rec2, 200) * 1e3, 2),
+            "chunk_us_p20_p50_p80": cold(tiny_chunk, scale=1e3),
+            "recurrent_us_p20_p50_p80": cold(tiny_rec, scale=1e3),
             "note": "fused-gate call (and gate + scan calls) incl. output allocation by the "
                     "binding; launch-latency bound"}
         # packed varlen + GVA forward
@@ -429,7 +489,8 @@ def main():
                           A_log=t3["A"])
         ms3 = time_it(varlen_step, 20)
         extra["varlen_gva_32768tok_HV32"] = {"ms_per_step": round(ms3, 4),
-                                             "tokens_per_s": round(int(w3.cu_seqlens[-1]) / (ms3 * 1e-3), 1)}
+                                             "tokens_per_s": round(int(w3.cu_seqlens[-1]) / (ms3 * 1e-3), 1),
+                                             "cold_ms": cold(varlen_step)}
         del t3, G3, ws3
         # long-context training step: forward + backward, B=1 T=65536 H=HV=32
         progress("long-context forward + backward")
@@ -457,6 +518,8 @@ def main():
             kda.gate_bwd(t5["x"], r["dg"], t5["A"], dx=r["dg"], workspace=wsg)
         fwd_ms = time_it(fwd5, 5, warm=2)
         bwd_ms = time_it(bwd5, 3, warm=1)
+        cold_fwd5 = cold(fwd5, reps=min(a.cold_reps, 100), warm=10)
+        cold_bwd5 = cold(bwd5, reps=min(a.cold_reps, 30), warm=3)
         # gate backward alone, with a bias: x, dg in, dx out (FP32), dA_log and d_dt_bias
         gen = torch.Generator(device=dev).manual_seed(5)
         dg5 = torch.randn(t5["x"].shape, device=dev, generator=gen)
@@ -469,6 +532,7 @@ def main():
             "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
             "fwd_bwd_tokens_per_s": round(65536 / ((fwd_ms + bwd_ms) * 1e-3), 1),
             "note": "bwd = kda_gate_cumsum + kda_chunk_bwd + kda_gate_bwd (dx, dA_log)",
+            "fwd_cold_ms": cold_fwd5, "bwd_cold_ms": cold_bwd5,
             "gate_bwd_ms": round(gb_ms, 4), "gate_bwd_GBps": round(gb_bytes / (gb_ms * 1e-3) / 1e9, 1),
             "gate_bwd_hbm_frac": round(gb_bytes / (gb_ms * 1e-3) / 8e12, 4)}
         del t5, G5, o5, ws5f, wsg, dg5, db5, dx5
@@ -490,10 +554,35 @@ def main():
             oracle.recurrence(wl.q, wl.k, wl.v, g, wl.beta, None)
             walls.append(time.perf_counter() - c0)
         c_s = sorted(walls)[1]
+        # one thread on a bounded sample: batch row 0, value heads 0..3 (4 of the 64 chains)
+        oracle.set_threads(1)
+        sub = slice(0, 1), slice(None), slice(0, 4)
+        g1 = oracle.gate_activation(wl.x[sub], wl.A_log[:4])
+        c0 = time.perf_counter()
+        oracle.recurrence(wl.q[:, :, :4][:1], wl.k[:, :, :4][:1], wl.v[sub], g1, wl.beta[sub], None)
+        one_s = time.perf_counter() - c0
+        oracle.set_threads(threads)
+        one_tok_s = T * 4 / HV / one_s  # tokens/s of all HV heads at one thread
+        host_cores = os.cpu_count()
+        try:
+            host_cores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            pass
+        model = ""
+        try:
+            with open("/proc/cpuinfo") as fh:
+                model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
+        except OSError:
+            pass
         cpu = dict(value=round(B * T / c_s, 1), unit="tokens/s", cores=used, kind="oracle",
                    sample=f"FP64 oracle (gate activation + token recurrence) on the whole dense "
                           f"batch B={B} T={T} H=HV={HV} K=V={K}, median of 3 runs: {c_s:.2f} s "
-                          f"wall, about {sum(walls) * used:.0f} thread-seconds in total")
+                          f"wall, about {sum(walls) * used:.0f} thread-seconds in total",
+                   host_cores=host_cores, host_cpu=model,
+                   one_thread=dict(value=round(one_tok_s, 1), unit="tokens/s",
+                                   sample=f"batch row 0, value heads 0-3 (4 of {B * HV} chains, "
+                                          f"{T} tokens each) on 1 thread: {one_s:.2f} s; value "
+                                          f"scaled to all {HV} heads of a token"))
 
     out = {
         "metric": "chunk_kda fwd tokens/s (B4 T4096 H16 K=V=128 bf16) + recurrent decode us/step",
@@ -525,6 +614,12 @@ def main():
                              "ms": round(cv_ms, 4), "plain_ms": round(f_ms, 4),
                              "separate_pass_bytes": 2 * (2 * B * T * H * K + B * T * HV * V) * 2},
         "roofline": roof,
+        "measured_peaks": measured,
+        "cold": {"protocol": f"per-call HIP events, 1 GiB cache flush before each call, warmup "
+                             f"{a.cold_warmup}, {a.cold_reps} reps (long context: 100 / 30), "
+                             f"p20 / median / p80",
+                 "dense_fused_ms": cold_dense, "dense_two_call_ms": cold_dense2,
+                 "decode_us": cold_dec},
         "decode": {"workload": "recurrent_kda decode: 256 slots (26 empty), 1 token each, H=16 "
                                "HV=32 K=V=128 bf16, FP32 state in place, raw gate activated in "
                                "the scan kernel",
