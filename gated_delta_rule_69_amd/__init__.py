@@ -37,7 +37,10 @@ EXPORTED = ("kda_status_string", "kda_gate_cumsum", "kda_gate_cumsum_biased",
             "kda_chunk_fwd", "kda_chunk_fwd_fused_gate", "kda_chunk_bwd_workspace_bytes",
             "kda_chunk_bwd", "kda_recurrent_fwd", "kda_recurrent_fwd_fused_gate",
             "kda_chunk_fwd_ex", "kda_recurrent_fwd_ex", "kda_chunk_fwd_conv", "kda_short_conv_fwd",
-            "kda_recurrent_fwd_conv_workspace_bytes", "kda_recurrent_fwd_conv")
+            "kda_recurrent_fwd_conv_workspace_bytes", "kda_recurrent_fwd_conv",
+            "kda_recurrent_fwd_conv_noalloc")
+# bytes of the library's static device scratch behind kda_recurrent_fwd_conv_noalloc
+NOALLOC_SCRATCH_BYTES = 16 << 20
 KDA_GATE_LOG2, KDA_GATE_NAT, KDA_GATE_RAW = 0, 1, 2
 
 
@@ -113,6 +116,9 @@ def _lib():
         lib.kda_recurrent_fwd_conv.argtypes = [dims, ctypes.c_int, p, p, p, conv, p, p, p, i32, p, i32,
                                                p, p, p, i32, p, p, p, sz, p]
         lib.kda_recurrent_fwd_conv.restype = ctypes.c_int
+        lib.kda_recurrent_fwd_conv_noalloc.argtypes = [dims, ctypes.c_int, p, p, p, conv, p, p, p, i32,
+                                                       p, i32, p, p, p, i32, p, p, p]
+        lib.kda_recurrent_fwd_conv_noalloc.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -505,7 +511,8 @@ def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
                   final_state: Optional[torch.Tensor] = None, use_gate_in_kernel: bool = False,
                   A_log: Optional[torch.Tensor] = None, gate_is_raw: bool = True,
                   qk_l2norm: bool = False, short_conv=None, conv_state=None, conv_state_out=None,
-                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  workspace: Optional[torch.Tensor] = None,
+                  no_alloc: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Step A7 (kda_recurrent_fwd). `gate` is the per-token log2 decay
     (gate_cumsum with chunk_size=1). With use_gate_in_kernel=True, `gate` is
     gate_cumsum's input instead (raw x with optional A_log, or the natural-log
@@ -514,8 +521,10 @@ def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     kernel (kda_recurrent_fwd_ex). short_conv=((wq, bq), (wk, bk), (wv, bv))
     treats q, k, v as raw projections and runs the short convolution + SiLU
     first, continuing each sequence from `conv_state` and writing the new
-    history to `conv_state_out` (kda_recurrent_fwd_conv; see short_conv).
-    Inference only: inputs that require grad are rejected (use chunk_kda for
+    history to `conv_state_out` (kda_recurrent_fwd_conv; see short_conv);
+    with no_alloc=True that step runs kda_recurrent_fwd_conv_noalloc instead,
+    which takes no workspace (the library's own static scratch; pass `o` and
+    `final_state` too so that nothing is allocated at all). Inference only: inputs that require grad are rejected (use chunk_kda for
     training). Pass final_state=initial_state to update the states in place."""
     if any(t is not None and t.requires_grad for t in (q, k, v, gate, beta, initial_state)):
         raise RuntimeError("recurrent_kda is inference-only; inputs require grad (use chunk_kda)")
@@ -527,6 +536,8 @@ def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
         _check(t, n)
     if A_log is not None and not use_gate_in_kernel:
         raise ValueError("A_log needs use_gate_in_kernel=True (else pass it to gate_cumsum)")
+    if no_alloc and short_conv is None:
+        raise ValueError("no_alloc applies to decode from raw projections (short_conv)")
     d = _dims(q, v, cu_seqlens)
     dt = _dtype_code(q)
     if o is None:
@@ -543,6 +554,15 @@ def recurrent_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
             if st is not None and (tuple(st.shape) != conv_state_shape(q, v, cu_seqlens, sc.width)
                                    or st.dtype != q.dtype):
                 raise ValueError(f"{n} must be {conv_state_shape(q, v, cu_seqlens, sc.width)} {q.dtype}")
+        if no_alloc:
+            rc = _lib().kda_recurrent_fwd_conv_noalloc(
+                ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), ctypes.byref(sc), _ptr(conv_state),
+                _ptr(conv_state_out), _ptr(gate), kind, _ptr(A_log), int(bool(qk_l2norm)), _ptr(beta),
+                _ptr(initial_state), _ptr(cu_seqlens), int(bool(output_final_state)), _ptr(o),
+                _ptr(final_state), _stream())
+            if rc:
+                raise KdaError("kda_recurrent_fwd_conv_noalloc", rc)
+            return o, final_state
         need = int(_lib().kda_recurrent_fwd_conv_workspace_bytes(ctypes.byref(d), dt))
         if workspace is None or _nbytes(workspace) < need:
             workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)

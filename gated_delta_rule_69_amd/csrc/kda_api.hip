@@ -1,7 +1,17 @@
 // C ABI of libkda: argument validation, then kernel launches on the caller's stream.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kda_common.h"
+
+// Scratch of kda_recurrent_fwd_conv_noalloc: device memory the library owns, so
+// that callers that cannot allocate (graph capture, serving loops) need not
+// pass a workspace. Every GPU the library runs on holds its own copy until the
+// process ends. In host code `scratch` names a host-side stand-in, never a
+// device address: its address on a device comes from hipGetSymbolAddress,
+// taken once per device with that device current (scratch_on_current_device).
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -470,6 +480,53 @@ kda_status kda_recurrent_fwd_conv(const kda_dims* d, kda_dtype dt, const void* q
   if (st != KDA_OK) return st;
   return recurrent_impl(d, dt, qc, kc, vc, gate, (int)gate_kind, A_log, qk_l2norm != 0, beta, h0,
                         cu, write_final, o, ht, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device address of `scratch` on the calling thread's current device, looked
+// up on the first call for that device and kept.
+kda_status scratch_on_current_device(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KDA_ERR_LAUNCH;
+  if (dev >= kMaxDevices) return KDA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDA_ERR_LAUNCH;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_recurrent_fwd_conv_noalloc(const kda_dims* d, kda_dtype dt, const void* q,
+                                          const void* k, const void* v, const kda_short_conv* conv,
+                                          const void* conv_state_in, void* conv_state_out,
+                                          const float* gate, int32_t gate_kind, const float* A_log,
+                                          int32_t qk_l2norm, const void* beta, const float* h0,
+                                          const int32_t* cu, int32_t write_final, void* o,
+                                          float* ht, hipStream_t stream) {
+  if (!d) return KDA_ERR_NULL;
+  const size_t need = kda_recurrent_fwd_conv_workspace_bytes(d, dt);
+  if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const kda_status st = scratch_on_current_device(&ws);
+  if (st != KDA_OK) return st;
+  // every byte of the scratch the call uses is written before it is read
+  // (the convolved q, k, v), so nothing needs clearing between calls
+  return kda_recurrent_fwd_conv(d, dt, q, k, v, conv, conv_state_in, conv_state_out, gate,
+                                gate_kind, A_log, qk_l2norm, beta, h0, cu, write_final, o, ht, ws,
+                                (size_t)KDA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 kda_status kda_recurrent_fwd_ex(const kda_dims* d, kda_dtype dt, const void* q, const void* k,

@@ -40,6 +40,8 @@
  *   - The caller owns every buffer. The library allocates nothing, keeps no
  *     global state and never synchronises: each call only enqueues work on
  *     `stream`, and results are valid once that stream has been synchronised.
+ *     The one exception is kda_recurrent_fwd_conv_noalloc, which uses a static
+ *     device scratch of the library's own instead of a caller's workspace.
  *   - Host-checkable errors return before anything is enqueued. A failed
  *     kernel launch returns KDA_ERR_LAUNCH.
  */
@@ -319,6 +321,37 @@ kda_status kda_recurrent_fwd_conv(const kda_dims* dims, kda_dtype dtype, const v
                                   const int32_t* cu_seqlens, int32_t output_final_state, void* o,
                                   float* final_state, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
+
+/* Size of the library's own device scratch used by
+ * kda_recurrent_fwd_conv_noalloc (16 MiB per GPU, held until the process ends). */
+#define KDA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * kda_recurrent_fwd_conv_noalloc -- kda_recurrent_fwd_conv without a workspace
+ * argument, for callers that cannot allocate device memory (HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). Same arguments,
+ * results (bit-identical) and errors as kda_recurrent_fwd_conv, minus
+ * workspace / workspace_bytes: the convolved q, k, v live in a static device
+ * scratch of KDA_NOALLOC_SCRATCH_BYTES that the library owns (one per GPU).
+ *   Limit: kda_recurrent_fwd_conv_workspace_bytes(dims, dtype) must be at most
+ *          KDA_NOALLOC_SCRATCH_BYTES (else KDA_ERR_WORKSPACE, nothing enqueued);
+ *          e.g. 2 * T * H * K + T * HV * V bf16 elements = 4 MiB for 256 decode
+ *          tokens at H = 16, HV = 32, K = V = 128.
+ *   Allocates nothing: no hipMalloc / hipFree. The first call on a device
+ *          looks up that device's scratch address (hipGetSymbolAddress).
+ *   Concurrency: every call on a GPU shares that GPU's scratch; calls that
+ *          overlap on one GPU (different streams, or host threads without
+ *          ordering) race and must be serialised by the caller. The scratch
+ *          keeps the last call's contents; each call writes all it reads.
+ */
+kda_status kda_recurrent_fwd_conv_noalloc(const kda_dims* dims, kda_dtype dtype, const void* q,
+                                          const void* k, const void* v, const kda_short_conv* conv,
+                                          const void* conv_state_in, void* conv_state_out,
+                                          const float* gate, int32_t gate_kind, const float* A_log,
+                                          int32_t qk_l2norm, const void* beta,
+                                          const float* initial_state, const int32_t* cu_seqlens,
+                                          int32_t output_final_state, void* o, float* final_state,
+                                          hipStream_t stream);
 
 /* Workspace bytes kda_chunk_bwd needs for these sizes (0 on unsupported input). */
 size_t kda_chunk_bwd_workspace_bytes(const kda_dims* dims, kda_dtype dtype, int32_t chunk_size);

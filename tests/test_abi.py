@@ -301,6 +301,22 @@ def test_short_conv_and_conv_decode_reject_bad_arguments():
     assert rec_hist(FAKE[5]) == 5                  # over o
 
 
+def test_noalloc_conv_decode_checks_its_scratch_limit():
+    """The allocation-free decode rejects a problem whose convolved q, k, v
+    exceed the library's static scratch before touching any device."""
+    lib = kda.load()
+    assert lib.kda_recurrent_fwd_conv_noalloc(None, 1, *[None] * 4, None, None, None, 2, None, 1,
+                                              None, None, None, 1, None, None, None) == 1
+    big = _dims(T=4096, N=1, H=16, HV=32, K=128, V=128)
+    assert lib.kda_recurrent_fwd_conv_workspace_bytes(ctypes.byref(big), 1) > kda.NOALLOC_SCRATCH_BYTES
+    taps = kda.KdaShortConv(q_weight=FAKE[10].value, k_weight=FAKE[11].value, v_weight=FAKE[12].value,
+                            q_bias=None, k_bias=None, v_bias=None, width=4)
+    rc = lib.kda_recurrent_fwd_conv_noalloc(ctypes.byref(big), 1, FAKE[0], FAKE[1], FAKE[2],
+                                            ctypes.byref(taps), None, None, FAKE[3], 2, None, 1,
+                                            FAKE[4], None, FAKE[8], 1, FAKE[5], FAKE[6], None)
+    assert rc == 6  # KDA_ERR_WORKSPACE
+
+
 def test_prefill_and_step_ops_fake_shapes_on_meta_tensors():
     import torch
 
