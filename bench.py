@@ -72,7 +72,7 @@ def _args():
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--skip-extra", action="store_true", help="skip the context workloads")
     p.add_argument("--profile", choices=["dense", "dense2", "dense_conv", "decode", "decode2", "long",
-                                         "gatebwd", "varlen", "tiny", "copy"],
+                                         "gatebwd", "varlen", "tiny", "prefill", "copy"],
                    default=None,
                    help="run only one workload a few times (for rocprofv3), print no JSON")
     p.add_argument("--profile-reps", type=int, default=3)
@@ -168,6 +168,13 @@ def profile_only(a):
                           use_gate_in_kernel=True, A_log=A)
             kda.recurrent_kda(q, k, v, x, b, h0, cu_seqlens=cu, output_final_state=True,
                               use_gate_in_kernel=True, A_log=A)
+    elif a.profile == "prefill":
+        # recurrent prefill of one sequence: B=1 T=4096 H=HV=16 K=V=128 bf16, gate in the kernel
+        wp = workloads.tiny_case(20261299, B=1, T=4096, H=16, HV=16, K=128, V=128, dtype="bf16")
+        q, k, v, b = T_(wp.q, bf), T_(wp.k, bf), T_(wp.v, bf), T_(wp.beta, bf)
+        x, h0 = T_(wp.x), T_(wp.h0)
+        for _ in range(a.profile_reps):
+            kda.recurrent_kda(q, k, v, x, b, h0, output_final_state=True, use_gate_in_kernel=True)
     elif a.profile == "gatebwd":
         # gate backward on the long-context shape: B=1 T=65536 HV=32 K=128, A_log and dt_bias
         gen = torch.Generator(device=dev).manual_seed(5)
@@ -474,6 +481,24 @@ def main():
             "recurrent_us_p20_p50_p80": cold(tiny_rec, scale=1e3),
             "note": "fused-gate call (and gate + scan calls) incl. output allocation by the "
                     "binding; launch-latency bound"}
+        # recurrent prefill of one long sequence: B=1, T=4096, H=HV=16, K=V=128 bf16, gate in the
+        # kernel (few chains: the per-token chain length decides)
+        wp = workloads.tiny_case(20261299, B=1, T=4096, H=16, HV=16, K=128, V=128, dtype="bf16")
+        tp = dict(q=T_(wp.q, bf), k=T_(wp.k, bf), v=T_(wp.v, bf), b=T_(wp.beta, bf), x=T_(wp.x),
+                  h0=T_(wp.h0))
+        op = torch.empty_like(tp["v"])
+        hp = torch.empty_like(tp["h0"])
+
+        def prefill_rec():
+            kda.recurrent_kda(tp["q"], tp["k"], tp["v"], tp["x"], tp["b"], tp["h0"],
+                              output_final_state=True, o=op, final_state=hp, use_gate_in_kernel=True)
+        pre_ms = time_it(prefill_rec, 10)
+        extra["recurrent_prefill_T4096_H16_K128"] = {
+            "ms": round(pre_ms, 4), "us_per_token": round(pre_ms * 1e3 / 4096, 3),
+            "cold_ms": cold(prefill_rec, reps=50, warm=5),
+            "note": "recurrent_kda (kda_recurrent_fwd_fused_gate) over one 4096-token sequence, "
+                    "16 value heads, bf16"}
+        del tp, op, hp
         # packed varlen + GVA forward
         progress("varlen + GVA forward")
         w3 = workloads.workload3()

@@ -14,6 +14,8 @@
 // is read once and written once; for decode (one token per sequence) the
 // kernel is HBM-bound on those two passes. The reductions over K (u, w and
 // k . q~) go through LDS.
+#include <type_traits>
+
 #include "kda_common.h"
 
 namespace kda {
@@ -213,22 +215,70 @@ recurrent_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
 // aligned operands (the common case, and the decode hot path).
 //
 // Each 64-lane wave owns all K rows of a CW-column block of one (sequence,
-// value head) state: lane = rl * CL + cl holds rows [16 rl, 16 rl + 16) of the
-// 4 columns starting at 4 cl. The reductions over K are 16-term partial sums
-// followed by a butterfly over the RL row lanes (lane xor CL, 2 CL, ..., 32), so
-// every lane ends with u, w and k . q~ of its columns and computes delta
-// redundantly: no LDS and no barrier. Waves are independent. The decays of a
-// row group are split over its CL lanes (NPL rows each, activation included
-// for a fused gate) and gathered with lane shuffles. The next token's inputs
-// are loaded while the current one is processed (two register sets).
-template <int K>
+// value head) state; a lane holds RPL rows of 4 consecutive columns. The
+// reductions over K are RPL-term partial sums followed by a sum over the RL
+// lanes holding the other rows of the same columns, so every lane ends with
+// u, w and k . q~ of its columns and computes delta redundantly: no LDS and no
+// barrier. Waves are independent. The next token's inputs are loaded while
+// the current one is processed (two register sets). Two layouts:
+//   MANY (many chains, e.g. decode): RPL = 16, lane = rl * CL + cl; the row
+//     sums are a butterfly of lane shuffles (xor CL, 2 CL, ..., 32), and the
+//     16 decays of a row group are split over its CL lanes (NPL each,
+//     activation included for a fused gate) and gathered with shuffles.
+//     Fewest redundant k / q loads for a bandwidth-bound pass.
+//   FEW (fewer waves than SIMDs): RPL = 2 (4 for K = 256), RL = K / RPL
+//     consecutive row lanes, lane = cl * RL + rl, 8 / 4 / 4 columns per wave
+//     for K = 64 / 128 / 256; the row sums are lane_group_sum, and every lane
+//     activates its own RPL decays. A token costs a lane 8 (16) state updates
+//     instead of 64, and each chain spreads over 8 to 16 times as many waves:
+//     a shorter sequential chain per token (measured: 2 rows per lane beat 4 by
+//     10% on one 4096-token sequence and on the tiny FP32 case).
+template <int K, bool FEW>
 struct WaveGeo {
-  static constexpr int RPL = 16;       // state rows per lane
-  static constexpr int RL = K / RPL;   // row lanes
-  static constexpr int CL = 64 / RL;   // column lanes (4 columns each)
-  static constexpr int CW = 4 * CL;    // columns per wave
-  static constexpr int NPL = RPL / CL; // decays computed per lane
+  static constexpr int RPL = FEW ? (K >= 256 ? 4 : 2) : 16;  // state rows per lane
+  static constexpr int RL = K / RPL;             // row lanes
+  static constexpr int CL = 64 / RL;             // column lanes (4 columns each)
+  static constexpr int CW = 4 * CL;              // columns per wave
+  static constexpr int NPL = RPL / CL;           // decays activated per lane (MANY)
+  static_assert(RL * CL == 64 && (FEW || (NPL >= 1 && RPL % CL == 0)), "wave geometry");
 };
+
+// Sum of x over aligned groups of RL consecutive lanes (RL = 16, 32 or 64),
+// left in every lane of the group: four rotations inside each 16-lane row (DPP
+// row_ror 1, 2, 4, 8), then for RL >= 32 the row-pair swap and for RL = 64 the
+// half-wave swap (v_permlane16_swap / v_permlane32_swap, which exchange rows
+// between two registers holding copies of x: their sum is x plus the value of
+// the lane 16, resp. 32, lanes away). All VALU: no LDS round trip per step, as
+// a shuffle through ds_bpermute would take. The swaps are written out because
+// the compiler's two-result form of them loses the second result; the s_nop
+// pairs give the two wait states a VALU result needs before a permlane reads
+// it, and the same after.
+template <int M>
+__device__ __forceinline__ float add_row_ror(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                 0, __builtin_bit_cast(int, x), 0x120 + M, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float add_swap16(float x) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float add_swap32(float x) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+template <int RL>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  static_assert(RL == 16 || RL == 32 || RL == 64, "row lanes");
+  x = add_row_ror<1>(x);
+  x = add_row_ror<2>(x);
+  x = add_row_ror<4>(x);
+  x = add_row_ror<8>(x);
+  if constexpr (RL >= 32) x = add_swap16(x);
+  if constexpr (RL == 64) x = add_swap32(x);
+  return x;
+}
 
 template <int NPL>
 struct GVec;  // the NPL gate values of one lane
@@ -238,52 +288,48 @@ template <>
 struct GVec<2> { float2 v; };
 template <>
 struct GVec<4> { float4 v; };
+template <>
+struct GVec<8> { float4 v[2]; };
+template <>
+struct GVec<16> { float4 v[4]; };
 
-template <typename T, int NPL>
-struct WTok;  // one token's inputs for one lane (16 rows of k and q, NPL gates, 4 of v)
-template <int NPL>
-struct WTok<bf16, NPL> {
-  uint4 k[2], q[2];
-  GVec<NPL> g;
-  uint2 v;
-  bf16 b;
-};
-template <int NPL>
-struct WTok<float, NPL> {
-  float4 k[4], q[4];
-  GVec<NPL> g;
-  float4 v;
-  float b;
+// RPL consecutive elements of T as one or more vector loads of exactly BYTES
+// bytes in all (4, 8 or a multiple of 16)
+template <int BYTES>
+struct RowVec {
+  static_assert(BYTES == 4 || BYTES == 8 || BYTES % 16 == 0, "row vector size");
+  static constexpr int N = BYTES >= 16 ? BYTES / 16 : 1;
+  typedef typename std::conditional<BYTES >= 16, uint4,
+                                    typename std::conditional<BYTES == 8, uint2, uint32_t>::type>::type U;
+  U u[N];
 };
 
-template <int NPL>
-__device__ __forceinline__ void unpack16(const WTok<bf16, NPL>& x, float* kf, float* qf) {
-  const bf16* kk = reinterpret_cast<const bf16*>(x.k);
-  const bf16* qq = reinterpret_cast<const bf16*>(x.q);
+template <typename T, int NPL, int RPL>
+struct WTok {  // one token's inputs for one lane (RPL rows of k and q, NPL gates, 4 of v)
+  RowVec<RPL * (int)sizeof(T)> k, q;
+  GVec<NPL> g;
+  typename std::conditional<sizeof(T) == 2, uint2, float4>::type v;
+  T b;
+};
+
+template <typename T, int NPL, int RPL>
+__device__ __forceinline__ void unpack_rows(const WTok<T, NPL, RPL>& x, float* kf, float* qf) {
+  const T* kk = reinterpret_cast<const T*>(x.k.u);
+  const T* qq = reinterpret_cast<const T*>(x.q.u);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    kf[i] = (float)kk[i];
-    qf[i] = (float)qq[i];
+  for (int i = 0; i < RPL; ++i) {
+    kf[i] = to_f32(kk[i]);
+    qf[i] = to_f32(qq[i]);
   }
 }
-template <int NPL>
-__device__ __forceinline__ void unpack16(const WTok<float, NPL>& x, float* kf, float* qf) {
-  const float* kk = reinterpret_cast<const float*>(x.k);
-  const float* qq = reinterpret_cast<const float*>(x.q);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    kf[i] = kk[i];
-    qf[i] = qq[i];
-  }
-}
-template <int NPL>
-__device__ __forceinline__ void unpack_v(const WTok<bf16, NPL>& x, float* vf) {
+template <int NPL, int RPL>
+__device__ __forceinline__ void unpack_v(const WTok<bf16, NPL, RPL>& x, float* vf) {
   const bf16* vv = reinterpret_cast<const bf16*>(&x.v);
 #pragma unroll
   for (int e = 0; e < 4; ++e) vf[e] = (float)vv[e];
 }
-template <int NPL>
-__device__ __forceinline__ void unpack_v(const WTok<float, NPL>& x, float* vf) {
+template <int NPL, int RPL>
+__device__ __forceinline__ void unpack_v(const WTok<float, NPL, RPL>& x, float* vf) {
   vf[0] = x.v.x; vf[1] = x.v.y; vf[2] = x.v.z; vf[3] = x.v.w;
 }
 __device__ __forceinline__ void store_o4(bf16* p, const float* r) {
@@ -294,7 +340,7 @@ __device__ __forceinline__ void store_o4(float* p, const float* r) {
   *reinterpret_cast<float4*>(p) = make_float4(r[0], r[1], r[2], r[3]);
 }
 
-template <typename T, int K>
+template <typename T, int K, bool FEW>
 __global__ void __launch_bounds__(kRecThreads)
 recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                       const float* __restrict__ gate, int gate_mode,
@@ -302,9 +348,10 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
                       const float* h0, const int32_t* __restrict__ cu, int Tlen, int H, int HV,
                       int V, int n_cb, int64_t n_tasks, float scale, int write_final,
                       T* __restrict__ o, float* ht) {
-  using G = WaveGeo<K>;
+  using G = WaveGeo<K, FEW>;
   constexpr int RPL = G::RPL, CL = G::CL, CW = G::CW, NPL = G::NPL;
-  using Tok = WTok<T, NPL>;
+  constexpr int GPL = FEW ? RPL : NPL;  // gate values loaded (and activated) per lane
+  using Tok = WTok<T, GPL, RPL>;
   const int64_t task = (int64_t)blockIdx.x * (kRecThreads / 64) + (threadIdx.x >> 6);
   if (task >= n_tasks) return;  // whole wave
   const int lane = threadIdx.x & 63;
@@ -312,7 +359,7 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
   const int64_t nh = task / n_cb;
   const int n = (int)(nh / HV), hv = (int)(nh % HV);
   const int h = hv / (HV / H);
-  const int rl = lane / CL, cl = lane % CL;
+  const int rl = FEW ? lane % G::RL : lane / CL, cl = FEW ? lane / G::RL : lane % CL;
   const int r0 = rl * RPL;
   const int col = cb * CW + cl * 4;
   const bool col_ok = col < V;
@@ -355,31 +402,31 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
   const float gscale = gate_head_scale(gate_mode, A_log, hv);
   const int colc = col_ok ? col : 0;  // lanes past V read column 0 and discard it
   auto load_tok = [&](int64_t t, Tok& x) {
-    const T* kp = k + (t * H + h) * K + r0;
-    const T* qp = q + (t * H + h) * K + r0;
-    constexpr int NV = 16 * sizeof(T) / 16;
+    typedef typename decltype(x.k)::U U;
+    const U* kp = reinterpret_cast<const U*>(k + (t * H + h) * K + r0);
+    const U* qp = reinterpret_cast<const U*>(q + (t * H + h) * K + r0);
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      reinterpret_cast<uint4*>(x.k)[j] = reinterpret_cast<const uint4*>(kp)[j];
-      reinterpret_cast<uint4*>(x.q)[j] = reinterpret_cast<const uint4*>(qp)[j];
+    for (int j = 0; j < decltype(x.k)::N; ++j) {
+      x.k.u[j] = kp[j];
+      x.q.u[j] = qp[j];
     }
-    x.g = *reinterpret_cast<const GVec<NPL>*>(gate + (t * HV + hv) * K + r0 + cl * NPL);
+    x.g = *reinterpret_cast<const GVec<GPL>*>(gate + (t * HV + hv) * K + r0 + (FEW ? 0 : cl * NPL));
     x.v = *reinterpret_cast<const decltype(x.v)*>(v + (t * HV + hv) * V + colc);
     x.b = beta[t * HV + hv];
   };
   auto step = [&](const Tok& x, int64_t t) {
     float kf[RPL], qf[RPL], vf[4];
-    unpack16(x, kf, qf);
+    unpack_rows(x, kf, qf);
     unpack_v(x, vf);
     // this lane's NPL decays (rows r0 + cl * NPL + m), then the row group's 16
     const float* gf = reinterpret_cast<const float*>(&x.g);
-    float dloc[NPL];
+    float dloc[GPL];
 #pragma unroll
-    for (int m = 0; m < NPL; ++m) dloc[m] = exp2f(gate_log2_token(gf[m], gate_mode, gscale));
+    for (int m = 0; m < GPL; ++m) dloc[m] = exp2f(gate_log2_token(gf[m], gate_mode, gscale));
     float u[4] = {0.f, 0.f, 0.f, 0.f}, w[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      const float d = __shfl(dloc[i % NPL], rl * CL + i / NPL);
+      const float d = FEW ? dloc[FEW ? i : 0] : __shfl(dloc[i % GPL], rl * CL + i / NPL);
       kk += kf[i] * kf[i];
       qq += qf[i] * qf[i];
       qf[i] *= scale;
@@ -391,17 +438,30 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
         w[e] += s[i][e] * qf[i];
       }
     }
-#pragma unroll
-    for (int m = CL; m < 64; m <<= 1) {
+    if constexpr (FEW) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        u[e] += __shfl_xor(u[e], m);
-        w[e] += __shfl_xor(w[e], m);
+        u[e] = lane_group_sum<G::RL>(u[e]);
+        w[e] = lane_group_sum<G::RL>(w[e]);
       }
-      kq += __shfl_xor(kq, m);
+      kq = lane_group_sum<G::RL>(kq);
       if (qk_norm) {
-        kk += __shfl_xor(kk, m);
-        qq += __shfl_xor(qq, m);
+        kk = lane_group_sum<G::RL>(kk);
+        qq = lane_group_sum<G::RL>(qq);
+      }
+    } else {
+#pragma unroll
+      for (int m = CL; m < 64; m <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u[e] += __shfl_xor(u[e], m);
+          w[e] += __shfl_xor(w[e], m);
+        }
+        kq += __shfl_xor(kq, m);
+        if (qk_norm) {
+          kk += __shfl_xor(kk, m);
+          qq += __shfl_xor(qq, m);
+        }
       }
     }
     // optional q/k normalisation, applied to the reduced terms (u and the update
@@ -433,14 +493,31 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     }
   };
 
-  Tok A, B;
-  load_tok(bos, A);
-  for (int it = 0; it < len; it += 2) {
-    load_tok(bos + min(it + 1, len - 1), B);
-    step(A, bos + it);
-    if (it + 1 >= len) break;
-    load_tok(bos + min(it + 2, len - 1), A);
-    step(B, bos + it + 1);
+  if constexpr (FEW) {
+    // a ring of RING token input sets: a token's inputs are requested RING - 1
+    // steps before its step (the short per-token chain of this form would
+    // otherwise wait on each load); loads past the end re-read the last token
+    constexpr int RING = 4;
+    Tok ring[RING];
+#pragma unroll
+    for (int j = 0; j < RING; ++j) load_tok(bos + min(j, len - 1), ring[j]);
+    for (int it = 0; it < len; it += RING) {
+#pragma unroll
+      for (int j = 0; j < RING; ++j) {
+        if (it + j < len) step(ring[j], bos + it + j);
+        load_tok(bos + min(it + j + RING, len - 1), ring[j]);
+      }
+    }
+  } else {
+    Tok A, B;
+    load_tok(bos, A);
+    for (int it = 0; it < len; it += 2) {
+      load_tok(bos + min(it + 1, len - 1), B);
+      step(A, bos + it);
+      if (it + 1 >= len) break;
+      load_tok(bos + min(it + 2, len - 1), A);
+      step(B, bos + it + 1);
+    }
   }
 
   if (write_final && col_ok) {
@@ -451,20 +528,33 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
   }
 }
 
+template <typename T, int K, bool FEW>
+static hipError_t launch_rec_wave_form(const kda_dims& d, const void* q, const void* k, const void* v,
+                                      const float* gate, int gm, const float* A_log, int qn,
+                                      const void* beta, const float* h0, const int32_t* cu,
+                                      int write_final, void* o, float* ht, hipStream_t s) {
+  const int n_cb = (d.V + WaveGeo<K, FEW>::CW - 1) / WaveGeo<K, FEW>::CW;
+  const int64_t n_tasks = (int64_t)d.N * d.HV * n_cb;
+  const int wpb = kRecThreads / 64;
+  dim3 grid((unsigned)((n_tasks + wpb - 1) / wpb));
+  hipLaunchKernelGGL((recurrent_wave_kernel<T, K, FEW>), grid, dim3(kRecThreads), 0, s, (const T*)q,
+                     (const T*)k, (const T*)v, gate, gm, A_log, qn, (const T*)beta, h0, cu, d.T, d.H,
+                     d.HV, d.V, n_cb, n_tasks, 1.0f / sqrtf((float)d.K), write_final, (T*)o, ht);
+  return hipGetLastError();
+}
+
+// Layout: MANY when its (sequence, value head, column block) waves already give
+// every SIMD of the device one wave, else FEW (more waves, shorter per-token
+// chain).
 template <typename T, int K>
 static hipError_t launch_rec_wave(const kda_dims& d, const void* q, const void* k, const void* v,
                                   const float* gate, int gm, const float* A_log, int qn, const void* beta,
                                   const float* h0, const int32_t* cu, int write_final, void* o,
                                   float* ht, hipStream_t s) {
-  const int n_cb = (d.V + WaveGeo<K>::CW - 1) / WaveGeo<K>::CW;
-  const int64_t n_tasks = (int64_t)d.N * d.HV * n_cb;
-  const int wpb = kRecThreads / 64;
-  dim3 grid((unsigned)((n_tasks + wpb - 1) / wpb));
-  hipLaunchKernelGGL((recurrent_wave_kernel<T, K>), grid, dim3(kRecThreads), 0, s, (const T*)q,
-                     (const T*)k, (const T*)v, gate, gm, A_log, qn, (const T*)beta, h0, cu, d.T, d.H,
-                     d.HV, d.V,
-                     n_cb, n_tasks, 1.0f / sqrtf((float)d.K), write_final, (T*)o, ht);
-  return hipGetLastError();
+  const int64_t many = (int64_t)d.N * d.HV * ((d.V + WaveGeo<K, false>::CW - 1) / WaveGeo<K, false>::CW);
+  if (many >= 4 * (int64_t)kda_host::device_cus())
+    return launch_rec_wave_form<T, K, false>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, s);
+  return launch_rec_wave_form<T, K, true>(d, q, k, v, gate, gm, A_log, qn, beta, h0, cu, write_final, o, ht, s);
 }
 
 template <typename T, int VEC, int ROWS>

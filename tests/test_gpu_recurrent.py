@@ -38,6 +38,26 @@ def test_bf16_gva_varlen():
     check_parity(wl, o, ht, o_ref, ht_ref, "gva")
 
 
+@pytest.mark.parametrize("dtype,B,T,H,HV,K,V", [
+    ("bf16", 8, 37, 4, 32, 128, 128),   # 1024 waves at 16 rows per lane: the many-chain form
+    ("fp32", 16, 12, 16, 64, 64, 64),   # 1024 waves, one column block each
+    ("bf16", 2, 150, 1, 4, 256, 64),    # few chains, K = 256: 64 row lanes (both lane swaps)
+    ("fp32", 1, 90, 1, 3, 128, 64),     # few chains, K = 128: 64 row lanes of 2 rows
+    ("bf16", 3, 70, 1, 2, 64, 128),     # few chains, K = 64: 32 row lanes (one lane swap)
+])
+def test_row_split_forms_multi_token(dtype, B, T, H, HV, K, V):
+    """The per-wave kernel takes 16 state rows per lane when there are enough
+    (sequence, value head) waves to fill the device and 2 (K = 256: 4) rows per
+    lane otherwise (many times the waves, a shorter per-token chain, the row
+    sums over 32 or 64 lanes); both forms over multi-token sequences against
+    the oracle."""
+    wl = workloads.tiny_case(270 + K + B, B=B, T=T, H=H, HV=HV, K=K, V=V, dtype=dtype)
+    d = device_inputs(wl)
+    o, ht = run_gpu(wl, d, "recurrent")
+    o_ref, ht_ref = oracle.forward(wl)
+    check_parity(wl, o, ht, o_ref, ht_ref, f"rows split {dtype} B{B} HV{HV} K{K}")
+
+
 def test_decode_in_place_and_empty_slots_bitwise():
     """Decode workload: 256 slots (26 empty), state updated in place."""
     wl = workloads.workload4()
