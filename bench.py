@@ -140,10 +140,14 @@ def profile_only(a):
         t = [T_(w5.q, bf), T_(w5.k, bf), T_(w5.v, bf), T_(w5.beta, bf)]
         x, h0, dO, dht = T_(w5.x), T_(w5.h0), T_(w5.dO, bf), T_(w5.dht)
         del w5
+        wsb = torch.empty(kda.chunk_bwd_workspace_bytes(t[0], t[2]), device=dev, dtype=torch.uint8)
         for _ in range(a.profile_reps):
             G = kda.gate_cumsum(x, None, None, 64)
             kda.chunk_kda(*t[:3], G, t[3], h0, output_final_state=True)
             kda.chunk_kda_bwd(*t[:3], G, t[3], h0, dO, dht)
+            # training step with saved states
+            kda.chunk_kda(*t[:3], G, t[3], h0, output_final_state=True, save_for_backward=wsb)
+            kda.chunk_kda_bwd(*t[:3], G, t[3], h0, dO, dht, saved=True, workspace=wsb)
     elif a.profile == "varlen":
         # packed varlen + GVA: 32768 tokens in 16 sequences and 3 empty slots, HV = 32,
         # nonzero initial states, gate in the kernel
@@ -545,6 +549,24 @@ def main():
         bwd_ms = time_it(bwd5, 3, warm=1)
         cold_fwd5 = cold(fwd5, reps=min(a.cold_reps, 100), warm=10)
         cold_bwd5 = cold(bwd5, reps=min(a.cold_reps, 30), warm=3)
+        # training step with the states saved by the forward: gate cumsum, kda_chunk_fwd_train
+        # (outputs + chunk start states and Deltas in the backward's workspace), then
+        # kda_chunk_bwd_saved (no second recurrence) and the gate backward
+        wsb = torch.empty(kda.chunk_bwd_workspace_bytes(t5["q"], t5["v"]), device=dev,
+                          dtype=torch.uint8)
+
+        def fwd5_train():
+            kda.gate_cumsum(t5["x"], t5["A"], None, 64, out=G5)
+            kda.chunk_kda(t5["q"], t5["k"], t5["v"], G5, t5["b"], t5["h0"], output_final_state=True,
+                          o=o5, save_for_backward=wsb)
+
+        def bwd5_saved():
+            r = kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], G5, t5["b"], t5["h0"], t5["dO"],
+                                  t5["dht"], saved=True, workspace=wsb)
+            kda.gate_bwd(t5["x"], r["dg"], t5["A"], dx=r["dg"], workspace=wsg)
+        tr_fwd_ms = time_it(fwd5_train, 5, warm=2)
+        tr_bwd_ms = time_it(bwd5_saved, 3, warm=1)
+        del wsb
         # gate backward alone, with a bias: x, dg in, dx out (FP32), dA_log and d_dt_bias
         gen = torch.Generator(device=dev).manual_seed(5)
         dg5 = torch.randn(t5["x"].shape, device=dev, generator=gen)
@@ -556,7 +578,12 @@ def main():
         extra["long_context_T65536_H32_train"] = {
             "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
             "fwd_bwd_tokens_per_s": round(65536 / ((fwd_ms + bwd_ms) * 1e-3), 1),
-            "note": "bwd = kda_gate_cumsum + kda_chunk_bwd + kda_gate_bwd (dx, dA_log)",
+            "note": "fwd = kda_chunk_fwd_fused_gate; bwd = kda_gate_cumsum + kda_chunk_bwd + "
+                    "kda_gate_bwd (dx, dA_log), recomputing the forward recurrence",
+            "train_saved_fwd_ms": round(tr_fwd_ms, 3), "train_saved_bwd_ms": round(tr_bwd_ms, 3),
+            "train_saved_tokens_per_s": round(65536 / ((tr_fwd_ms + tr_bwd_ms) * 1e-3), 1),
+            "train_saved_note": "fwd = kda_gate_cumsum + kda_chunk_fwd_train (states saved); "
+                                "bwd = kda_chunk_bwd_saved + kda_gate_bwd",
             "fwd_cold_ms": cold_fwd5, "bwd_cold_ms": cold_bwd5,
             "gate_bwd_ms": round(gb_ms, 4), "gate_bwd_GBps": round(gb_bytes / (gb_ms * 1e-3) / 1e9, 1),
             "gate_bwd_hbm_frac": round(gb_bytes / (gb_ms * 1e-3) / 8e12, 4)}

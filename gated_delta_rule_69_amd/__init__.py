@@ -38,7 +38,7 @@ EXPORTED = ("kda_status_string", "kda_gate_cumsum", "kda_gate_cumsum_biased",
             "kda_chunk_bwd", "kda_recurrent_fwd", "kda_recurrent_fwd_fused_gate",
             "kda_chunk_fwd_ex", "kda_recurrent_fwd_ex", "kda_chunk_fwd_conv", "kda_short_conv_fwd",
             "kda_recurrent_fwd_conv_workspace_bytes", "kda_recurrent_fwd_conv",
-            "kda_recurrent_fwd_conv_noalloc")
+            "kda_recurrent_fwd_conv_noalloc", "kda_chunk_fwd_train", "kda_chunk_bwd_saved")
 # bytes of the library's static device scratch behind kda_recurrent_fwd_conv_noalloc
 NOALLOC_SCRATCH_BYTES = 16 << 20
 KDA_GATE_LOG2, KDA_GATE_NAT, KDA_GATE_RAW = 0, 1, 2
@@ -94,6 +94,10 @@ def _lib():
         lib.kda_chunk_bwd_workspace_bytes.restype = sz
         lib.kda_chunk_bwd.argtypes = [dims, ctypes.c_int] + [p] * 7 + [i32] + [p] * 8 + [p, sz, p]
         lib.kda_chunk_bwd.restype = ctypes.c_int
+        lib.kda_chunk_bwd_saved.argtypes = lib.kda_chunk_bwd.argtypes
+        lib.kda_chunk_bwd_saved.restype = ctypes.c_int
+        lib.kda_chunk_fwd_train.argtypes = lib.kda_chunk_fwd.argtypes
+        lib.kda_chunk_fwd_train.restype = ctypes.c_int
         lib.kda_recurrent_fwd.argtypes = [dims, ctypes.c_int, p, p, p, p, p, p, p, i32, p, p, p]
         lib.kda_recurrent_fwd.restype = ctypes.c_int
         lib.kda_recurrent_fwd_fused_gate.argtypes = [dims, ctypes.c_int, p, p, p, p, i32, p, p, p, p,
@@ -334,7 +338,8 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
               o: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, use_gate_in_kernel: bool = False,
               A_log: Optional[torch.Tensor] = None, gate_is_raw: bool = True,
-              qk_l2norm: bool = False, short_conv=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              qk_l2norm: bool = False, short_conv=None,
+              save_for_backward: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Steps A2..A6 (kda_chunk_fwd). `gate` is the chunk-local cumulative log2
     gate (gate_cumsum with the same chunk_size). With use_gate_in_kernel=True,
     `gate` is gate_cumsum's input instead (raw x with optional A_log, or the
@@ -344,6 +349,10 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     treats q, k, v as raw projections and applies the short causal convolution
     + SiLU to them in the kernel (kda_chunk_fwd_conv): FP32 taps [H*K, W] /
     [HV*V, W] (a [D, 1, W] Conv1d weight is accepted too), biases or None.
+    save_for_backward: a device buffer of at least chunk_bwd_workspace_bytes()
+    bytes (plain log2 gate only): the forward runs as kda_chunk_fwd_train and
+    leaves the chunk start states and Deltas there for chunk_kda_bwd(...,
+    saved=True, workspace=that buffer), which then skips the recurrence.
     Returns (o, final_state)."""
     _validate_scan(q, k, v, gate, beta, initial_state, cu_seqlens, o=o, final_state=final_state,
                    A_log=A_log)
@@ -362,9 +371,22 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     if not output_final_state:
         final_state = None
     need = int(_lib().kda_chunk_fwd_workspace_bytes(ctypes.byref(d), dt, int(chunk_size)))
-    if workspace is None or _nbytes(workspace) < need:
+    if save_for_backward is None and (workspace is None or _nbytes(workspace) < need):
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
     kind = (KDA_GATE_RAW if gate_is_raw else KDA_GATE_NAT) if use_gate_in_kernel else KDA_GATE_LOG2
+    if save_for_backward is not None:
+        if use_gate_in_kernel or qk_l2norm or short_conv is not None:
+            raise ValueError("save_for_backward takes the chunk-local log2 gate (gate_cumsum), "
+                             "without in-kernel gate, normalisation or convolution")
+        _check(save_for_backward, "save_for_backward")
+        rc = _lib().kda_chunk_fwd_train(
+            ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+            _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), int(bool(output_final_state)),
+            _ptr(o), _ptr(final_state), _ptr(save_for_backward), _nbytes(save_for_backward),
+            _stream())
+        if rc:
+            raise KdaError("kda_chunk_fwd_train", rc)
+        return o, final_state
     if short_conv is not None:
         sc = _short_conv(short_conv, d)
         rc = _lib().kda_chunk_fwd_conv(
@@ -433,10 +455,13 @@ def chunk_bwd_workspace_bytes(q: torch.Tensor, v: torch.Tensor, cu_seqlens=None,
 
 
 def chunk_kda_bwd(q, k, v, gate, beta, initial_state, do, dht=None, *, cu_seqlens=None,
-                  chunk_size: int = 64, workspace: Optional[torch.Tensor] = None):
+                  chunk_size: int = 64, workspace: Optional[torch.Tensor] = None,
+                  saved: bool = False):
     """Steps B1..B3 (kda_chunk_bwd). Returns a dict with dq, dk (shape of q),
     dv (shape of v), dg (FP32, w.r.t. the per-token natural-log gate), dbeta
-    and dh0 (FP32 [N, HV, K, V])."""
+    and dh0 (FP32 [N, HV, K, V]). saved=True (kda_chunk_bwd_saved): `workspace`
+    is the buffer a chunk_kda(..., save_for_backward=workspace) call on the
+    same inputs filled, and the recurrence is not run again."""
     _validate_scan(q, k, v, gate, beta, initial_state, cu_seqlens, do=do, dht=dht)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (do, "do"),
                  (initial_state, "initial_state"), (dht, "dht"), (cu_seqlens, "cu_seqlens"),
@@ -452,14 +477,18 @@ def chunk_kda_bwd(q, k, v, gate, beta, initial_state, do, dht=None, *, cu_seqlen
     dbeta = new(beta)
     dh0 = torch.empty((d.N, d.HV, d.K, d.V), device=q.device, dtype=torch.float32)
     need = int(_lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(d), dt, int(chunk_size)))
-    if workspace is None or _nbytes(workspace) < need:
+    if saved:
+        if workspace is None:
+            raise ValueError("saved=True needs the workspace the training forward filled")
+    elif workspace is None or _nbytes(workspace) < need:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
-    rc = _lib().kda_chunk_bwd(ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
-                              _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), _ptr(do),
-                              _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta),
-                              _ptr(dh0), _ptr(workspace), _nbytes(workspace), _stream())
+    fn = _lib().kda_chunk_bwd_saved if saved else _lib().kda_chunk_bwd
+    rc = fn(ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+            _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), _ptr(do),
+            _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta),
+            _ptr(dh0), _ptr(workspace), _nbytes(workspace), _stream())
     if rc:
-        raise KdaError("kda_chunk_bwd", rc)
+        raise KdaError("kda_chunk_bwd_saved" if saved else "kda_chunk_bwd", rc)
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=dh0)
 
 

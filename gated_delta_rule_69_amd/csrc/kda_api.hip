@@ -82,11 +82,13 @@ kda_status chunk_fwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const 
                           int qk_norm, const kda_short_conv* conv, const void* beta,
                           const float* h0, const int32_t* cu, int32_t chunk_size,
                           int32_t write_final, void* o, float* ht, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
+                          size_t workspace_bytes, hipStream_t stream, int save = 0) {
   kda_status st = check_scan(d, dt, q, k, v, gate, beta, h0, cu, write_final, o, ht);
   if (st != KDA_OK) return st;
   if (chunk_size != 64) return KDA_ERR_UNSUPPORTED;
   if (!((d->K == 64 || d->K == 128) && (d->V == 64 || d->V == 128))) return KDA_ERR_UNSUPPORTED;
+  // a training forward fills the backward's workspace: only sizes the backward supports
+  if (save && dt == KDA_FP32 && d->K != 64) return KDA_ERR_UNSUPPORTED;
   const Sizes s = sizes(d, dt);
   if (A_log && (overlaps(A_log, (size_t)d->HV * 4, o, s.v) ||
                 overlaps(A_log, (size_t)d->HV * 4, ht, s.state)))
@@ -97,7 +99,8 @@ kda_status chunk_fwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const 
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)gate | (uintptr_t)o) & 15) ||
       ((uintptr_t)workspace & 255))
     return KDA_ERR_UNSUPPORTED;
-  const size_t need = kda_host::chunk_workspace_bytes(*d, dt, chunk_size);
+  const size_t need = save ? kda_host::chunk_bwd_workspace_bytes(*d, dt, chunk_size)
+                           : kda_host::chunk_workspace_bytes(*d, dt, chunk_size);
   if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
   if (overlaps(workspace, need, o, s.v) || overlaps(workspace, need, ht, s.state) ||
       overlaps(workspace, need, h0, s.state) || overlaps(workspace, need, q, s.qk) ||
@@ -117,7 +120,7 @@ kda_status chunk_fwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const 
   }
   return kda_host::launch_chunk_fwd(*d, dt, q, k, v, gate, gate_mode, A_log, qk_norm ? 1 : 0,
                                     conv, beta, h0, cu,
-                                    write_final ? 1 : 0, o, ht, workspace, workspace_bytes,
+                                    write_final ? 1 : 0, o, ht, workspace, workspace_bytes, save,
                                     stream) == hipSuccess
              ? KDA_OK
              : KDA_ERR_LAUNCH;
@@ -321,11 +324,16 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_dims* d, kda_dtype dt, int32_t ch
   return kda_host::chunk_bwd_workspace_bytes(*d, dt, chunk_size);
 }
 
-kda_status kda_chunk_bwd(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
-                         const void* v, const float* gate, const void* beta, const float* h0,
-                         const int32_t* cu, int32_t chunk_size, const void* do_,
-                         const float* dht, void* dq, void* dk, void* dv, float* dg, void* dbeta,
-                         float* dh0, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+kda_status chunk_bwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                          const void* v, const float* gate, const void* beta, const float* h0,
+                          const int32_t* cu, int32_t chunk_size, const void* do_,
+                          const float* dht, void* dq, void* dk, void* dv, float* dg, void* dbeta,
+                          float* dh0, void* workspace, size_t workspace_bytes, int saved,
+                          hipStream_t stream) {
   kda_status st = check_dims(d, cu);
   if (st != KDA_OK) return st;
   if (!valid_dtype(dt)) return KDA_ERR_DTYPE;
@@ -358,9 +366,42 @@ kda_status kda_chunk_bwd(const kda_dims* d, kda_dtype dt, const void* q, const v
   for (int j = 0; j < 8; ++j)
     if (overlaps(workspace, need, ins[j], ins_n[j])) return KDA_ERR_ALIAS;
   return kda_host::launch_chunk_bwd(*d, dt, q, k, v, gate, beta, h0, cu, do_, dht, dq, dk, dv, dg,
-                                    dbeta, dh0, workspace, stream) == hipSuccess
+                                    dbeta, dh0, workspace, saved, stream) == hipSuccess
              ? KDA_OK
              : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_bwd(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                         const void* v, const float* gate, const void* beta, const float* h0,
+                         const int32_t* cu, int32_t chunk_size, const void* do_,
+                         const float* dht, void* dq, void* dk, void* dv, float* dg, void* dbeta,
+                         float* dh0, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return chunk_bwd_impl(d, dt, q, k, v, gate, beta, h0, cu, chunk_size, do_, dht, dq, dk, dv, dg,
+                        dbeta, dh0, workspace, workspace_bytes, 0, stream);
+}
+
+kda_status kda_chunk_fwd_train(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                               const void* v, const float* gate, const void* beta,
+                               const float* h0, const int32_t* cu, int32_t chunk_size,
+                               int32_t write_final, void* o, float* ht, void* bwd_workspace,
+                               size_t bwd_workspace_bytes, hipStream_t stream) {
+  return chunk_fwd_impl(d, dt, q, k, v, gate, kda::kGateLog2, nullptr, 0, nullptr, beta, h0, cu,
+                        chunk_size, write_final, o, ht, bwd_workspace, bwd_workspace_bytes, stream,
+                        1);
+}
+
+kda_status kda_chunk_bwd_saved(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                               const void* v, const float* gate, const void* beta,
+                               const float* h0, const int32_t* cu, int32_t chunk_size,
+                               const void* do_, const float* dht, void* dq, void* dk, void* dv,
+                               float* dg, void* dbeta, float* dh0, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  return chunk_bwd_impl(d, dt, q, k, v, gate, beta, h0, cu, chunk_size, do_, dht, dq, dk, dv, dg,
+                        dbeta, dh0, workspace, workspace_bytes, 1, stream);
 }
 
 kda_status kda_recurrent_fwd(const kda_dims* d, kda_dtype dt, const void* q, const void* k,

@@ -68,7 +68,7 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
                        const float* gate, int gate_mode, const float* A_log, int qn,
                        const kda_short_conv* conv, const void* beta, const float* h0,
                        const int32_t* cu, int write_final, void* o, float* ht, void* ws,
-                       hipStream_t s) {
+                       int save, hipStream_t s) {
   const bool varlen = cu != nullptr;
   const int64_t mc = max_chunks(d, varlen);
   char* p = reinterpret_cast<char*>(ws);
@@ -77,6 +77,10 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
   T* ws_T = reinterpret_cast<T*>(p);
   p += align256((size_t)mc * d.HV * Ws<T, K, V>::bytes_T);
   float* ws_GL = reinterpret_cast<float*>(p);
+  p += align256((size_t)mc * d.HV * Ws<T, K, V>::bytes_GL);
+  // save != 0: `ws` is the backward pass's workspace, whose first regions have
+  // the forward's layout and whose per-chunk area follows them
+  T* ws_save = save ? reinterpret_cast<T*>(p) : nullptr;
   if (varlen) {
     hipError_t e = launch_chunk_table(cu, d.N, ws_int, (int)mc, s);
     if (e != hipSuccess) return e;
@@ -108,12 +112,20 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
   const int bv = scan_block_v(chains, V, kda_host::device_cus());
   // 4 waves per workgroup (8, with half the tiles per wave, measured slower:
   // more LDS traffic and wider barriers for the same chain latency)
+  // ws_save: the backward pass's per-chunk area (kda_chunk_fwd_train), which
+  // receives every chunk's start state and Delta as the scan forms them
   auto launch_scan = [&](auto bvc) {
     constexpr int BVC = decltype(bvc)::value;
-    hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, false, 4>), dim3((unsigned)chains, V / BVC),
-                       dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL,
-                       (const int*)ws_int, cu, h0, d.N, d.T, d.HV, write_final, (T*)o, ht,
-                       (T*)nullptr);
+    if (ws_save)
+      hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, false, 4, true>),
+                         dim3((unsigned)chains, V / BVC), dim3(kThreads), 0, s, (const T*)ws_T,
+                         (const float*)ws_GL, (const int*)ws_int, cu, h0, d.N, d.T, d.HV,
+                         write_final, (T*)o, ht, ws_save);
+    else
+      hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, false, 4>), dim3((unsigned)chains, V / BVC),
+                         dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL,
+                         (const int*)ws_int, cu, h0, d.N, d.T, d.HV, write_final, (T*)o, ht,
+                         (T*)nullptr);
   };
   // FP32 with K = 128 stays at 32 columns: the 64-column tile set does not
   // fit the register file
@@ -153,7 +165,7 @@ static hipError_t run_kv(const kda_dims& d, const void* q, const void* k, const 
                          const float* gate, int gm, const float* A_log, int qn,
                          const kda_short_conv* conv, const void* beta, const float* h0,
                          const int32_t* cu, int write_final, void* o, float* ht, void* ws,
-                         hipStream_t s) {
+                         int save, hipStream_t s) {
   using Lds = kda::IntraLds<T, K, V>;
   static_assert(sizeof(T) == 4 && K == 128 ? true : 2 * Lds::total_conv <= 158 * 1024,
                 "two workgroups per compute unit, also with the convolution taps");
@@ -167,7 +179,7 @@ static hipError_t run_kv(const kda_dims& d, const void* q, const void* k, const 
     if (e != hipSuccess) return e;
   }
   return kda::chunk_fwd_t<T, K, V>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final,
-                                   o, ht, ws, s);
+                                   o, ht, ws, save, s);
 }
 
 template <typename T>
@@ -175,11 +187,11 @@ static hipError_t run_t(const kda_dims& d, const void* q, const void* k, const v
                         const float* gate, int gm, const float* A_log, int qn,
                         const kda_short_conv* conv, const void* beta,
                         const float* h0, const int32_t* cu, int write_final, void* o, float* ht,
-                        void* ws, hipStream_t s) {
-  if (d.K == 64 && d.V == 64) return run_kv<T, 64, 64>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, s);
-  if (d.K == 64 && d.V == 128) return run_kv<T, 64, 128>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, s);
-  if (d.K == 128 && d.V == 64) return run_kv<T, 128, 64>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, s);
-  if (d.K == 128 && d.V == 128) return run_kv<T, 128, 128>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, s);
+                        void* ws, int save, hipStream_t s) {
+  if (d.K == 64 && d.V == 64) return run_kv<T, 64, 64>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, save, s);
+  if (d.K == 64 && d.V == 128) return run_kv<T, 64, 128>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, save, s);
+  if (d.K == 128 && d.V == 64) return run_kv<T, 128, 64>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, save, s);
+  if (d.K == 128 && d.V == 128) return run_kv<T, 128, 128>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, save, s);
   return hipErrorInvalidValue;
 }
 
@@ -187,9 +199,9 @@ hipError_t launch_chunk_fwd(const kda_dims& d, kda_dtype dt, const void* q, cons
                             const void* v, const float* gate, int gm, const float* A_log,
                             int qn, const kda_short_conv* conv, const void* beta,
                             const float* h0, const int32_t* cu, int write_final, void* o,
-                            float* ht, void* ws, size_t /*ws_bytes*/, hipStream_t s) {
-  if (dt == KDA_BF16) return run_t<kda::bf16>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, s);
-  return run_t<float>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, s);
+                            float* ht, void* ws, size_t /*ws_bytes*/, int save, hipStream_t s) {
+  if (dt == KDA_BF16) return run_t<kda::bf16>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, save, s);
+  return run_t<float>(d, q, k, v, gate, gm, A_log, qn, conv, beta, h0, cu, write_final, o, ht, ws, save, s);
 }
 
 }  // namespace kda_host

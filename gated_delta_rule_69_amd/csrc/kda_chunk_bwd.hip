@@ -1105,7 +1105,7 @@ template <typename T, int K, int V>
 hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const void* v,
                        const float* gate, const void* beta, const float* h0, const int32_t* cu,
                        const void* dO, const float* dht, void* dq, void* dk, void* dv, float* dg,
-                       void* dbeta, float* dh0, void* ws, hipStream_t s) {
+                       void* dbeta, float* dh0, void* ws, int saved, hipStream_t s) {
   const bool varlen = cu != nullptr;
   const int64_t mc = max_chunks(d, varlen);
   char* p = reinterpret_cast<char*>(ws);
@@ -1149,12 +1149,15 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
   // blocks would leave compute units without a workgroup
   auto launch_scans = [&](auto bvc) -> hipError_t {
     constexpr int BVC = decltype(bvc)::value;
-    // forward recurrence keeping S0 and Delta (no outputs)
-    hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, true, 4>), dim3((unsigned)chains, V / BVC),
-                       dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL, (const int*)ws_int,
-                       cu, h0, d.N, d.T, d.HV, 0, (T*)nullptr, (float*)nullptr, ws_B);
-    hipError_t e2 = hipGetLastError();
-    if (e2 != hipSuccess) return e2;
+    // forward recurrence keeping S0 and Delta (no outputs), unless a training
+    // forward (kda_chunk_fwd_train) already stored them in this workspace
+    if (!saved) {
+      hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, true, 4>), dim3((unsigned)chains, V / BVC),
+                         dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL, (const int*)ws_int,
+                         cu, h0, d.N, d.T, d.HV, 0, (T*)nullptr, (float*)nullptr, ws_B);
+      hipError_t e2 = hipGetLastError();
+      if (e2 != hipSuccess) return e2;
+    }
     hipLaunchKernelGGL((chunk_rev_scan_kernel<T, K, V, BVC>), dim3((unsigned)chains, V / BVC),
                        dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL, ws_B,
                        (const int*)ws_int, cu, (const T*)dO, dht, d.N, d.T, d.HV, dh0);
@@ -1211,11 +1214,11 @@ template <typename T>
 static hipError_t bwd_t(const kda_dims& d, const void* q, const void* k, const void* v,
                         const float* gate, const void* beta, const float* h0, const int32_t* cu,
                         const void* dO, const float* dht, void* dq, void* dk, void* dv, float* dg,
-                        void* dbeta, float* dh0, void* ws, hipStream_t s) {
+                        void* dbeta, float* dh0, void* ws, int saved, hipStream_t s) {
 #define KDA_BWD_CASE(KK, VV)                                                                    \
   if (d.K == KK && d.V == VV)                                                                   \
     return kda::chunk_bwd_t<T, KK, VV>(d, q, k, v, gate, beta, h0, cu, dO, dht, dq, dk, dv, dg, \
-                                       dbeta, dh0, ws, s);
+                                       dbeta, dh0, ws, saved, s);
   KDA_BWD_CASE(64, 64)
   KDA_BWD_CASE(64, 128)
   KDA_BWD_CASE(128, 64)
@@ -1228,10 +1231,10 @@ hipError_t launch_chunk_bwd(const kda_dims& d, kda_dtype dt, const void* q, cons
                             const void* v, const float* gate, const void* beta, const float* h0,
                             const int32_t* cu, const void* dO, const float* dht, void* dq,
                             void* dk, void* dv, float* dg, void* dbeta, float* dh0, void* ws,
-                            hipStream_t s) {
+                            int saved, hipStream_t s) {
   if (dt == KDA_BF16)
-    return bwd_t<kda::bf16>(d, q, k, v, gate, beta, h0, cu, dO, dht, dq, dk, dv, dg, dbeta, dh0, ws, s);
-  return bwd_t<float>(d, q, k, v, gate, beta, h0, cu, dO, dht, dq, dk, dv, dg, dbeta, dh0, ws, s);
+    return bwd_t<kda::bf16>(d, q, k, v, gate, beta, h0, cu, dO, dht, dq, dk, dv, dg, dbeta, dh0, ws, saved, s);
+  return bwd_t<float>(d, q, k, v, gate, beta, h0, cu, dO, dht, dq, dk, dv, dg, dbeta, dh0, ws, saved, s);
 }
 
 }  // namespace kda_host

@@ -1212,13 +1212,15 @@ struct Raw4<float> {
 
 // KEEP: store every chunk's start state S0 and Delta into ws_B for the
 // backward pass instead of forming outputs (Q~ Gamma and P are not read);
-// the forward instantiation has none of it.
+// the forward instantiation has none of it. SAVE: the forward (outputs formed)
+// that also stores S0 and Delta, bit for bit what KEEP stores, so that a
+// backward pass that follows need not run the recurrence again.
 // NW waves per workgroup (4 or 8). Work of one chunk: the Delta and output
 // tiles (token tile x value tile) are split over the waves, NW / 4 waves per
 // token tile; the state tiles (channel tile x value tile) by channel tile.
 // With 8 waves every SIMD holds two waves of the chain, which hides part of
 // the LDS, matrix-core and barrier latency of the sequential recurrence.
-template <typename T, int K, int V, int BV, bool KEEP, int NW>
+template <typename T, int K, int V, int BV, bool KEEP, int NW, bool SAVE = false>
 __global__ void __launch_bounds__(NW * 64)
 chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
                   const int* __restrict__ ws_int, const int32_t* __restrict__ cu,
@@ -1228,6 +1230,8 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
   using F = typename M::frag;
   using WsL = Ws<T, K, V>;
   using R4 = Raw4<T>;
+  static_assert(!(KEEP && SAVE), "SAVE is a forward mode");
+  constexpr bool STORE = KEEP || SAVE;  // S0 and Delta of every chunk into ws_B
   typedef typename R4::type raw4;
   constexpr int KS_K = K / M::KSTEP;
   constexpr int KS_C = kC / M::KSTEP;
@@ -1396,7 +1400,7 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     const int64_t t0 = bos + (int64_t)cidx * kC;
     const int L = min(kC, len - cidx * kC);
 
-    if constexpr (KEEP) {  // backward support: keep the chunk's start state
+    if constexpr (STORE) {  // backward support: keep the chunk's start state
       T* st = ws_B + ((size_t)cj * HV + hv) * WsB<T, K, V>::elems + WsB<T, K, V>::oS0;
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt)
@@ -1452,7 +1456,7 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
 #pragma unroll
         for (int e = 0; e < 4; ++e) D[cc][e] = R4::get(cur.u[cc], e) - ws_[cc][e];
     }
-    if constexpr (KEEP) {  // backward support: keep Delta
+    if constexpr (STORE) {  // backward support: keep Delta
       T* dl = ws_B + ((size_t)cj * HV + hv) * WsB<T, K, V>::elems + WsB<T, K, V>::oDL;
 #pragma unroll
       for (int cc = 0; cc < CPW; ++cc)

@@ -381,6 +381,47 @@ kda_status kda_chunk_bwd(const kda_dims* dims, kda_dtype dtype, const void* q, c
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd_train -- kda_chunk_fwd for training: the same outputs (o and
+ * final_state bit-identical to kda_chunk_fwd), and on the way every chunk's
+ * start state and Delta = U - W S0 (what the backward's recurrence would form
+ * again, steps B1 and B2 of the chunked pipeline's backward, fwd_h / bwd_dhu in
+ * the squashed commit bodies of "[Fix] Use unit KDA gate scale when A_log is
+ * omitted") are stored in the backward pass's workspace, so that
+ * kda_chunk_bwd_saved can skip that recurrence.
+ *   Arguments as kda_chunk_fwd, except the workspace:
+ *   bwd_workspace  at least kda_chunk_bwd_workspace_bytes() for the same
+ *          dims, dtype and chunk_size, 256-byte aligned; to be handed,
+ *          unmodified, to kda_chunk_bwd_saved with the same inputs (q, k, v,
+ *          gate, beta, initial_state, cu_seqlens). The caller owns it.
+ *   Supported sizes as kda_chunk_bwd (FP32 needs K == 64). Errors as
+ *   kda_chunk_fwd (KDA_ERR_WORKSPACE if the workspace is smaller than the
+ *   backward's).
+ */
+kda_status kda_chunk_fwd_train(const kda_dims* dims, kda_dtype dtype, const void* q, const void* k,
+                               const void* v, const float* gate, const void* beta,
+                               const float* initial_state, const int32_t* cu_seqlens,
+                               int32_t chunk_size, int32_t output_final_state, void* o,
+                               float* final_state, void* bwd_workspace, size_t bwd_workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * kda_chunk_bwd_saved -- kda_chunk_bwd after kda_chunk_fwd_train: takes the
+ * chunk start states and Deltas that the training forward stored in
+ * `workspace` instead of running the forward recurrence again; all other
+ * steps as kda_chunk_bwd, and every gradient bit-identical to it.
+ *   Arguments, sizes and errors as kda_chunk_bwd. Precondition (not
+ *   checkable on the host): `workspace` holds the output of
+ *   kda_chunk_fwd_train on the same dims, dtype, chunk_size and inputs, and has
+ *   not been written since; otherwise the results are undefined.
+ */
+kda_status kda_chunk_bwd_saved(const kda_dims* dims, kda_dtype dtype, const void* q, const void* k,
+                               const void* v, const float* gate, const void* beta,
+                               const float* initial_state, const int32_t* cu_seqlens,
+                               int32_t chunk_size, const void* do_, const float* dht, void* dq,
+                               void* dk, void* dv, float* dg, void* dbeta, float* dh0,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * kda_recurrent_fwd -- step A7: the token-sequential scan (recurrent_kda).
  *   gate   [B, T, HV, K] FP32 per-token log2 decay (kda_gate_cumsum with
  *          chunk_size == 1).

@@ -317,6 +317,33 @@ def test_noalloc_conv_decode_checks_its_scratch_limit():
     assert rc == 6  # KDA_ERR_WORKSPACE
 
 
+def test_training_forward_and_saved_backward_reject_bad_arguments():
+    lib = kda.load()
+    d = _dims(K=128, V=128)
+    need_b = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(d), 1, 64)
+    need_f = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d), 1, 64)
+    assert need_b > need_f > 0
+
+    def fwd(dims, dt=1, ws_bytes=1 << 40, ws=FAKE[7]):
+        return lib.kda_chunk_fwd_train(ctypes.byref(dims), dt, FAKE[0], FAKE[1], FAKE[2], FAKE[3],
+                                       FAKE[4], None, None, 64, 1, FAKE[5], FAKE[6], ws, ws_bytes, None)
+
+    assert fwd(d, ws_bytes=need_f) == 6          # the backward's workspace is larger
+    assert fwd(d, ws=None) == 6
+    assert fwd(_dims(K=128, V=64), dt=0) == 4     # FP32 backward needs K = 64
+    assert fwd(_dims(H=2, HV=3)) == 2
+    assert fwd(d, ws=FAKE[5]) == 5                # workspace over o
+
+    def bwd(dims, ws=FAKE[9], ws_bytes=1 << 40):
+        return lib.kda_chunk_bwd_saved(ctypes.byref(dims), 1, FAKE[0], FAKE[1], FAKE[2], FAKE[3],
+                                       FAKE[4], None, None, 64, FAKE[5], None, FAKE[6], FAKE[7],
+                                       FAKE[8], FAKE[10], FAKE[11], FAKE[12], ws, ws_bytes, None)
+
+    assert bwd(d, ws=None) == 6
+    assert bwd(d, ws_bytes=need_b - 1) == 6
+    assert bwd(_dims(K=96)) == 4
+
+
 def test_prefill_and_step_ops_fake_shapes_on_meta_tensors():
     import torch
 

@@ -117,3 +117,45 @@ def test_bwd_no_dht_no_h0():
     ref = oracle.recurrence_bwd(wl.q, wl.k, wl.v, g, wl.beta, wl.dO, None, None, None)
     for n in NAMES:
         assert rel_rms(to_np(got[n]), ref[n]) < 1e-2, n
+
+
+@pytest.mark.parametrize("dtype,K,V,B,H,HV,cu", [
+    ("bf16", 128, 128, 4, 16, 16, None),          # 64 chains: 32-column scans
+    ("bf16", 128, 128, 1, 2, 4, [0, 0, 70, 200, 200, 265]),  # varlen + GVA, empty slots
+    ("fp32", 64, 128, 2, 1, 2, None),
+    ("bf16", 64, 64, 1, 1, 1, [0, 130]),          # one chain: 16-column scans
+])
+def test_training_forward_then_saved_backward_bitwise(dtype, K, V, B, H, HV, cu):
+    """kda_chunk_fwd_train stores every chunk's start state and Delta in the
+    backward's workspace; kda_chunk_bwd_saved then skips the recurrence. Both
+    must give bit for bit what kda_chunk_fwd and kda_chunk_bwd give."""
+    T = 200 if cu is None else cu[-1] + 7
+    wl = workloads.tiny_case(470 + K + V + HV, B=B, T=T, H=H, HV=HV, K=K, V=V, dtype=dtype,
+                             cu_seqlens=cu, grads=True, A_log=1.0)
+    d = device_inputs(wl)
+    dt = tdtype(wl)
+    dO = to_dev(np.nan_to_num(wl.dO), dt)
+    dht = to_dev(wl.dht)
+    G = kda.gate_cumsum(d["x"], d["A_log"], d["cu"], 64)
+    o1, h1 = kda.chunk_kda(d["q"], d["k"], d["v"], G, d["beta"], d["h0"], cu_seqlens=d["cu"],
+                           output_final_state=True)
+    r1 = kda.chunk_kda_bwd(d["q"], d["k"], d["v"], G, d["beta"], d["h0"], dO, dht, cu_seqlens=d["cu"])
+    ws = torch.full((kda.chunk_bwd_workspace_bytes(d["q"], d["v"], d["cu"]),), 0xFF, device=DEV,
+                    dtype=torch.uint8)  # NaN bytes: everything read must have been written
+    o2, h2 = kda.chunk_kda(d["q"], d["k"], d["v"], G, d["beta"], d["h0"], cu_seqlens=d["cu"],
+                           output_final_state=True, save_for_backward=ws)
+    r2 = kda.chunk_kda_bwd(d["q"], d["k"], d["v"], G, d["beta"], d["h0"], dO, dht,
+                           cu_seqlens=d["cu"], saved=True, workspace=ws)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    n = wl.T if cu is None else cu[-1]
+    assert torch.equal(bits(o1[:, :n]), bits(o2[:, :n]))
+    assert torch.equal(bits(h1), bits(h2))
+    mask = torch.from_numpy(in_contract_rows(wl)).to(DEV)
+    for name in NAMES:
+        a, b = r1[name], r2[name]
+        if name != "dh0":
+            a, b = a[mask], b[mask]
+        assert torch.equal(bits(a), bits(b)), name
+    ref = _ref(wl)
+    _check(wl, {n_: to_np(t) for n_, t in r2.items()}, ref)
