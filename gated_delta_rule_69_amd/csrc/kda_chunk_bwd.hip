@@ -201,9 +201,8 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
       const int tileK = RTW * wave + rt;
 #pragma unroll
       for (int ct = 0; ct < CTB; ++ct) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          dsl[(size_t)(16 * tileK + 4 * g + e) * V + col_base + 16 * ct + l16] = from_f32<T>(S[rt][ct][e]);
+        store4<T>(dsl + il4(16 * tileK + 4 * g, col_base + 16 * ct + l16, V), S[rt][ct][0],
+                  S[rt][ct][1], S[rt][ct][2], S[rt][ct][3]);
         if constexpr (M::KSTEP == 32) {
           bf16x4 x;
 #pragma unroll
@@ -230,9 +229,8 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
     T* ddl = wb + WB::oDDL;
 #pragma unroll
     for (int ct = 0; ct < CTB; ++ct) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        ddl[(size_t)(16 * wave + 4 * g + e) * V + col_base + 16 * ct + l16] = from_f32<T>(D[ct][e]);
+      store4<T>(ddl + il4(16 * wave + 4 * g, col_base + 16 * ct + l16, V), D[ct][0], D[ct][1],
+                D[ct][2], D[ct][3]);
       if constexpr (M::KSTEP == 32) {
         bf16x4 x;
 #pragma unroll
@@ -457,8 +455,17 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   T* bdS = bS0 + K * BS;
   constexpr int UPR = VB / EPU;  // 16-byte units per block row
   constexpr int NUC = (kC * UPR + NT - 1) / NT, NUK = (K * UPR + NT - 1) / NT;
+  // S0, Delta, dS1, dDelta are stored with rows interleaved by four (il4): a
+  // 16-byte unit holds CPU columns x 4 rows, unit i of row group rg covering
+  // columns CPU i .. CPU i + CPU - 1 of the block; the same number of units per
+  // block as the row-major inputs
+  constexpr int CPU = EPU / 4;   // columns per interleaved unit
+  constexpr int UPG = VB / CPU;  // interleaved units per row group
   struct Blk {
     uint4 a[NUC], b[NUC], c[NUC], d[NUC], s0[NUK], ds[NUK];
+  };
+  auto il_unit = [&](size_t off, int u, int c0) {
+    return *reinterpret_cast<const uint4*>(wb + off + il4(4 * (u / UPG), c0 + CPU * (u % UPG), V));
   };
   auto load_blk = [&](int vb, Blk& x) {
     const int c0 = vb * VB;
@@ -467,22 +474,38 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       const int u = tid + i * NT;
       const int row = u / UPR < kC ? u / UPR : 0, cu_ = u % UPR;
       const int rr = row < L ? row : 0;
+      const int ui = u < kC * UPR ? u : 0;
       x.a[i] = *reinterpret_cast<const uint4*>(dO + ((t0 + rr) * HV + hv) * V + c0 + EPU * cu_);
       x.d[i] = *reinterpret_cast<const uint4*>(v + ((t0 + rr) * HV + hv) * V + c0 + EPU * cu_);
-      x.b[i] = *reinterpret_cast<const uint4*>(wb + WB::oDL + (size_t)row * V + c0 + EPU * cu_);
-      x.c[i] = *reinterpret_cast<const uint4*>(wb + WB::oDDL + (size_t)row * V + c0 + EPU * cu_);
+      x.b[i] = il_unit(WB::oDL, ui, c0);
+      x.c[i] = il_unit(WB::oDDL, ui, c0);
     }
 #pragma unroll
     for (int i = 0; i < NUK; ++i) {
       const int u = tid + i * NT;
-      const int row = u / UPR < K ? u / UPR : 0, cu_ = u % UPR;
-      x.s0[i] = *reinterpret_cast<const uint4*>(wb + WB::oS0 + (size_t)row * V + c0 + EPU * cu_);
-      x.ds[i] = *reinterpret_cast<const uint4*>(wb + WB::oDS + (size_t)row * V + c0 + EPU * cu_);
+      const int ui = u < K * UPR ? u : 0;
+      x.s0[i] = il_unit(WB::oS0, ui, c0);
+      x.ds[i] = il_unit(WB::oDS, ui, c0);
     }
   };
   auto put16 = [](T* dst, const uint4& x) {  // block rows are 8-byte aligned
     reinterpret_cast<uint2*>(dst)[0] = make_uint2(x.x, x.y);
     reinterpret_cast<uint2*>(dst)[1] = make_uint2(x.z, x.w);
+  };
+  // an interleaved unit into the row-major [R][BS] block: row 4 rg + j takes
+  // element j of each of the unit's CPU columns (4-byte LDS writes)
+  auto put_il = [&](T* base, int u, const uint4& x) {
+    const int r0 = 4 * (u / UPG), c = CPU * (u % UPG);
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w[4] = {(x.x & 0xFFFFu) | (x.z << 16), (x.x >> 16) | (x.z & 0xFFFF0000u),
+                             (x.y & 0xFFFFu) | (x.w << 16), (x.y >> 16) | (x.w & 0xFFFF0000u)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(base + (r0 + j) * BS + c) = w[j];
+    } else {
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(base + (r0 + j) * BS + c) = w[j];
+    }
   };
   auto store_blk = [&](const Blk& x) {
 #pragma unroll
@@ -493,8 +516,8 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
         uint4 av = x.a[i], dv_ = x.d[i];
         if (row >= L) av = dv_ = make_uint4(0, 0, 0, 0);
         put16(bdO + row * BS + EPU * cu_, av);
-        put16(bDl + row * BS + EPU * cu_, x.b[i]);
-        put16(bdDl + row * BS + EPU * cu_, x.c[i]);
+        put_il(bDl, u, x.b[i]);
+        put_il(bdDl, u, x.c[i]);
         put16(bV + row * BS + EPU * cu_, dv_);
       }
     }
@@ -502,9 +525,8 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     for (int i = 0; i < NUK; ++i) {
       const int u = tid + i * NT;
       if (u < K * UPR) {
-        const int row = u / UPR, cu_ = u % UPR;
-        put16(bS0 + row * BS + EPU * cu_, x.s0[i]);
-        put16(bdS + row * BS + EPU * cu_, x.ds[i]);
+        put_il(bS0, u, x.s0[i]);
+        put_il(bdS, u, x.ds[i]);
       }
     }
   };

@@ -70,10 +70,12 @@ struct WsB {
   static constexpr size_t KHn = (size_t)kC * K;   // Khat fragments    [4][K/KSTEP][64][PER]
   static constexpr size_t QGT = (size_t)K * kC;   // (Q~ Gamma)^T frags [K/16][C/KSTEP][64][PER]
   static constexpr size_t WT = (size_t)K * kC;    // W^T fragments     [K/16][C/KSTEP][64][PER]
-  static constexpr size_t S0 = (size_t)K * V;     // chunk start state, row-major [K][V]
-  static constexpr size_t DL = (size_t)kC * V;    // Delta, row-major [C][V]
-  static constexpr size_t DS = (size_t)K * V;     // dS at the chunk end, row-major [K][V]
-  static constexpr size_t DDL = (size_t)kC * V;   // dDelta, row-major [C][V]
+  // the next four are R x V matrices with their rows interleaved by four
+  // (il4: element (r, c) at ((r / 4) V + c) 4 + r % 4), as the scans hold them
+  static constexpr size_t S0 = (size_t)K * V;     // chunk start state [K][V]
+  static constexpr size_t DL = (size_t)kC * V;    // Delta [C][V]
+  static constexpr size_t DS = (size_t)K * V;     // dS at the chunk end [K][V]
+  static constexpr size_t DDL = (size_t)kC * V;   // dDelta [C][V]
   static constexpr size_t elems = PT + KHn + QGT + WT + S0 + DL + DS + DDL;
   // FP32
   static constexpr size_t TM = (size_t)kC * kC;   // T = (I + A)^-1, row-major [C][C]
@@ -83,6 +85,26 @@ struct WsB {
   static constexpr size_t oPT = 0, oKHn = PT, oQGT = oKHn + KHn, oWT = oQGT + QGT,
                           oS0 = oWT + WT, oDL = oS0 + S0, oDS = oDL + DL, oDDL = oDS + DS;
 };
+
+// Offset of element (r, c) of an R x V matrix with rows interleaved by four:
+// the four rows 4g .. 4g + 3 of one column that an accumulator lane holds are
+// four consecutive elements, written with one 8-byte (bf16) or 16-byte (FP32)
+// store instead of four 2- or 4-byte ones.
+__device__ __forceinline__ size_t il4(int r, int c, int V) {
+  return ((size_t)(r >> 2) * V + c) * 4 + (r & 3);
+}
+// Store 4 FP32 values as consecutive elements of T (16-byte aligned for FP32,
+// 8-byte for bf16).
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float v0, const float v1, const float v2,
+                                       const float v3) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 x = {(bf16)v0, (bf16)v1, (bf16)v2, (bf16)v3};
+    *reinterpret_cast<bf16x4*>(p) = x;
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(v0, v1, v2, v3);
+  }
+}
 
 struct ChunkGeo {
   int ok;        // 0: no such chunk (grid over-provisioned)
@@ -1406,9 +1428,8 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
       for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int ct = 0; ct < CTB; ++ct)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            st[(size_t)(16 * (RTW * wave + rt) + 4 * g + e) * V + col_base + 16 * ct + l16] = from_f32<T>(S[rt][ct][e]);
+          store4<T>(st + il4(16 * (RTW * wave + rt) + 4 * g, col_base + 16 * ct + l16, V),
+                    S[rt][ct][0], S[rt][ct][1], S[rt][ct][2], S[rt][ct][3]);
     }
     // (1) publish S as B fragments: k-step ks is owned by the wave holding its channels
 #pragma unroll
@@ -1460,9 +1481,8 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
       T* dl = ws_B + ((size_t)cj * HV + hv) * WsB<T, K, V>::elems + WsB<T, K, V>::oDL;
 #pragma unroll
       for (int cc = 0; cc < CPW; ++cc)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          dl[(size_t)(16 * tt + 4 * g + e) * V + col_base + 16 * (ct0 + cc) + l16] = from_f32<T>(D[cc][e]);
+        store4<T>(dl + il4(16 * tt + 4 * g, col_base + 16 * (ct0 + cc) + l16, V), D[cc][0], D[cc][1],
+                  D[cc][2], D[cc][3]);
     }
     // publish Delta as B fragments (contraction over tokens)
 #pragma unroll
