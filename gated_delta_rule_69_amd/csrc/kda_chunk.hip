@@ -90,7 +90,7 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
     const kda_short_conv taps = conv ? *conv : kda_short_conv{};
     auto launch_intra = [&](auto qnc, auto cvc) {
       constexpr bool QN = decltype(qnc)::value, CV = decltype(cvc)::value;
-      hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, false, QN, CV>), dim3((unsigned)mc, (unsigned)d.HV),
+      hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, false, QN, CV>), dim3((unsigned)(mc * d.HV)),
                          dim3(kThreads), lds, s, (const T*)q, (const T*)k, (const T*)v, gate,
                          gate_mode, A_log, (const T*)beta, cu, ws_int, d.N, d.T, d.H, d.HV,
                          1.0f / sqrtf((float)K), ws_T, ws_GL, (T*)nullptr, (float*)nullptr, taps);

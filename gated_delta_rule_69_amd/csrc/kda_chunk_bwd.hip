@@ -431,16 +431,19 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   float* sDgam = sColP + 4 * K;                               // [K]
   float* sRow = sDgam + K;                                    // [3 parts][2 halves][C] dbeta parts
 
-  const ChunkGeo geo = chunk_geo(blockIdx.x, cu, ws_int, N, T_);
+  // 1-D grid, value head fastest and rotated by the chunk index (the order of
+  // the backward's intra-chunk recompute): 2% faster than chunk fastest here
+  const int chunk = (int)(blockIdx.x / (unsigned)HV);
+  const int hv = (int)((blockIdx.x % (unsigned)HV + (unsigned)chunk) % (unsigned)HV);
+  const ChunkGeo geo = chunk_geo(chunk, cu, ws_int, N, T_);
   if (!geo.ok) return;
-  const int hv = blockIdx.y;
   const int h = hv / (HV / H);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int tt = w & 3, hh = w >> 2;
   const int cb = NCH * hh;  // first channel tile of the wave
   const int L = geo.L;
   const int64_t t0 = geo.t0;
-  const size_t ch = (size_t)blockIdx.x * HV + hv;
+  const size_t ch = (size_t)chunk * HV + hv;
   const T* wb = ws_B + ch * WB::elems;
   const float* wTm = ws_Bf + ch * WB::elems_f;
   const float* wAb = wTm + WB::TM;
@@ -1159,7 +1162,7 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)IntraLds<T, K, V>::total);
     if (e != hipSuccess) return e;
     const size_t lds_intra = IntraLds<T, K, V>::total;
-    hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, true, false, false>), dim3((unsigned)mc, (unsigned)d.HV),
+    hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, true, false, false>), dim3((unsigned)(mc * d.HV)),
                        dim3(kThreads), lds_intra, s, (const T*)q, (const T*)k,
                        (const T*)v, gate, (int)kGateLog2, (const float*)nullptr, (const T*)beta,
                        cu, ws_int, d.N, d.T, d.H, d.HV, scale,
@@ -1196,7 +1199,7 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)BwdLds<T, K, V>::total);
     if (e != hipSuccess) return e;
     const size_t lds_local = BwdLds<T, K, V>::total;
-    hipLaunchKernelGGL((chunk_bwd_local_kernel<T, K, V>), dim3((unsigned)mc, (unsigned)d.HV),
+    hipLaunchKernelGGL((chunk_bwd_local_kernel<T, K, V>), dim3((unsigned)(mc * d.HV)),
                        dim3(kBwdThreads), lds_local, s, (const T*)q, (const T*)k,
                        (const T*)v, gate, (const T*)beta, (const T*)dO, cu, (const int*)ws_int,
                        (const T*)ws_B, (const float*)ws_Bf, d.N, d.T, d.H, d.HV, scale, (T*)dq,
