@@ -215,30 +215,35 @@ recurrent_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
 // aligned operands (the common case, and the decode hot path).
 //
 // Each 64-lane wave owns all K rows of a CW-column block of one (sequence,
-// value head) state; a lane holds RPL rows of 4 consecutive columns. The
+// value head) state; a lane holds RPL rows of CPL consecutive columns. The
 // reductions over K are RPL-term partial sums followed by a sum over the RL
 // lanes holding the other rows of the same columns, so every lane ends with
 // u, w and k . q~ of its columns and computes delta redundantly: no LDS and no
-// barrier. Waves are independent. The next token's inputs are loaded while
-// the current one is processed (two register sets). Two layouts:
-//   MANY (many chains, e.g. decode): RPL = 16, lane = rl * CL + cl; the row
-//     sums are a butterfly of lane shuffles (xor CL, 2 CL, ..., 32), and the
-//     16 decays of a row group are split over its CL lanes (NPL each,
-//     activation included for a fused gate) and gathered with shuffles.
-//     Fewest redundant k / q loads for a bandwidth-bound pass.
-//   FEW (fewer waves than SIMDs): RPL = 2 (4 for K = 256), RL = K / RPL
-//     consecutive row lanes, lane = cl * RL + rl, 8 / 4 / 4 columns per wave
+// barrier. Waves are independent. Two layouts:
+//   MANY (many chains, e.g. decode): RPL = 16, CPL = 4, lane = rl * CL + cl;
+//     the row sums are a butterfly of lane shuffles (xor CL, 2 CL, ..., 32),
+//     and the 16 decays of a row group are split over its CL lanes (NPL each,
+//     activation included for a fused gate) and gathered with shuffles. The
+//     next token's inputs are loaded while the current one is processed (two
+//     register sets). Fewest redundant k / q loads for a bandwidth-bound pass.
+//   FEW (fewer waves than SIMDs): RPL = 2 (4 for K = 256), CPL = 1, RL = K / RPL
+//     consecutive row lanes, lane = cl * RL + rl, 2 / 1 / 1 columns per wave
 //     for K = 64 / 128 / 256; the row sums are lane_group_sum, and every lane
-//     activates its own RPL decays. A token costs a lane 8 (16) state updates
-//     instead of 64, and each chain spreads over 8 to 16 times as many waves:
-//     a shorter sequential chain per token (measured: 2 rows per lane beat 4 by
-//     10% on one 4096-token sequence and on the tiny FP32 case).
+//     activates its own RPL decays. A token costs a lane 2 (4) state updates
+//     and three row sums (u, w, k . q~) instead of 64 updates, and a chain
+//     spreads over 32 to 128 times as many waves: the shortest sequential chain
+//     per token. Measured against 4 columns per lane: 50 -> 36 us on the tiny
+//     FP32 case, 3.49 -> 2.49 ms on one 4096-token bf16 sequence with 16 heads
+//     (2 columns: 42 us, 2.68 ms); 2 rows per lane beat 4 by 10% at 4 columns.
+constexpr int kFewCols = 1;  // state columns per lane in the FEW form
+
 template <int K, bool FEW>
 struct WaveGeo {
   static constexpr int RPL = FEW ? (K >= 256 ? 4 : 2) : 16;  // state rows per lane
+  static constexpr int CPL = FEW ? kFewCols : 4;  // state columns per lane
   static constexpr int RL = K / RPL;             // row lanes
-  static constexpr int CL = 64 / RL;             // column lanes (4 columns each)
-  static constexpr int CW = 4 * CL;              // columns per wave
+  static constexpr int CL = 64 / RL;             // column lanes (CPL columns each)
+  static constexpr int CW = CPL * CL;            // columns per wave
   static constexpr int NPL = RPL / CL;           // decays activated per lane (MANY)
   static_assert(RL * CL == 64 && (FEW || (NPL >= 1 && RPL % CL == 0)), "wave geometry");
 };
@@ -297,23 +302,51 @@ struct GVec<16> { float4 v[4]; };
 // bytes in all (4, 8 or a multiple of 16)
 template <int BYTES>
 struct RowVec {
-  static_assert(BYTES == 4 || BYTES == 8 || BYTES % 16 == 0, "row vector size");
+  static_assert(BYTES == 2 || BYTES == 4 || BYTES == 8 || BYTES % 16 == 0, "row vector size");
   static constexpr int N = BYTES >= 16 ? BYTES / 16 : 1;
-  typedef typename std::conditional<BYTES >= 16, uint4,
-                                    typename std::conditional<BYTES == 8, uint2, uint32_t>::type>::type U;
+  typedef typename std::conditional<
+      BYTES >= 16, uint4,
+      typename std::conditional<BYTES == 8, uint2,
+                                typename std::conditional<BYTES == 4, uint32_t, uint16_t>::type>::type>::type U;
   U u[N];
 };
 
-template <typename T, int NPL, int RPL>
-struct WTok {  // one token's inputs for one lane (RPL rows of k and q, NPL gates, 4 of v)
+// CPL consecutive FP32 state elements as one vector (one 4-, 8- or 16-byte access)
+template <int CPL>
+struct StVec;
+template <>
+struct StVec<1> { typedef float type; typedef uint32_t bits; };
+template <>
+struct StVec<2> { typedef float __attribute__((ext_vector_type(2))) type; typedef uint32_t __attribute__((ext_vector_type(2))) bits; };
+template <>
+struct StVec<4> { typedef f32x4 type; typedef u32x4 bits; };
+template <int CPL>
+__device__ __forceinline__ float st_get(const typename StVec<CPL>::type& x, int e) {
+  if constexpr (CPL == 1) return x;
+  else return x[e];
+}
+template <int CPL>
+__device__ __forceinline__ typename StVec<CPL>::type st_make(const float* r) {
+  typename StVec<CPL>::type x;
+  if constexpr (CPL == 1) {
+    x = r[0];
+  } else {
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) x[e] = r[e];
+  }
+  return x;
+}
+
+template <typename T, int NPL, int RPL, int CPL>
+struct WTok {  // one token's inputs for one lane (RPL rows of k and q, NPL gates, CPL of v)
   RowVec<RPL * (int)sizeof(T)> k, q;
   GVec<NPL> g;
-  typename std::conditional<sizeof(T) == 2, uint2, float4>::type v;
+  RowVec<CPL * (int)sizeof(T)> v;
   T b;
 };
 
-template <typename T, int NPL, int RPL>
-__device__ __forceinline__ void unpack_rows(const WTok<T, NPL, RPL>& x, float* kf, float* qf) {
+template <typename T, int NPL, int RPL, int CPL>
+__device__ __forceinline__ void unpack_rows(const WTok<T, NPL, RPL, CPL>& x, float* kf, float* qf) {
   const T* kk = reinterpret_cast<const T*>(x.k.u);
   const T* qq = reinterpret_cast<const T*>(x.q.u);
 #pragma unroll
@@ -322,22 +355,29 @@ __device__ __forceinline__ void unpack_rows(const WTok<T, NPL, RPL>& x, float* k
     qf[i] = to_f32(qq[i]);
   }
 }
-template <int NPL, int RPL>
-__device__ __forceinline__ void unpack_v(const WTok<bf16, NPL, RPL>& x, float* vf) {
-  const bf16* vv = reinterpret_cast<const bf16*>(&x.v);
+template <typename T, int NPL, int RPL, int CPL>
+__device__ __forceinline__ void unpack_v(const WTok<T, NPL, RPL, CPL>& x, float* vf) {
+  const T* vv = reinterpret_cast<const T*>(x.v.u);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) vf[e] = (float)vv[e];
+  for (int e = 0; e < CPL; ++e) vf[e] = to_f32(vv[e]);
 }
-template <int NPL, int RPL>
-__device__ __forceinline__ void unpack_v(const WTok<float, NPL, RPL>& x, float* vf) {
-  vf[0] = x.v.x; vf[1] = x.v.y; vf[2] = x.v.z; vf[3] = x.v.w;
+// CPL output values as one store
+template <int CPL>
+__device__ __forceinline__ void store_o(bf16* p, const float* r) {
+  if constexpr (CPL == 4) {
+    bf16x4 t = {(bf16)r[0], (bf16)r[1], (bf16)r[2], (bf16)r[3]};
+    *reinterpret_cast<bf16x4*>(p) = t;
+  } else if constexpr (CPL == 2) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 t = {(bf16)r[0], (bf16)r[1]};
+    *reinterpret_cast<bf16x2*>(p) = t;
+  } else {
+    *p = (bf16)r[0];
+  }
 }
-__device__ __forceinline__ void store_o4(bf16* p, const float* r) {
-  bf16x4 t = {(bf16)r[0], (bf16)r[1], (bf16)r[2], (bf16)r[3]};
-  *reinterpret_cast<bf16x4*>(p) = t;
-}
-__device__ __forceinline__ void store_o4(float* p, const float* r) {
-  *reinterpret_cast<float4*>(p) = make_float4(r[0], r[1], r[2], r[3]);
+template <int CPL>
+__device__ __forceinline__ void store_o(float* p, const float* r) {
+  *reinterpret_cast<typename StVec<CPL>::type*>(p) = st_make<CPL>(r);
 }
 
 template <typename T, int K, bool FEW>
@@ -349,9 +389,11 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
                       int V, int n_cb, int64_t n_tasks, float scale, int write_final,
                       T* __restrict__ o, float* ht) {
   using G = WaveGeo<K, FEW>;
-  constexpr int RPL = G::RPL, CL = G::CL, CW = G::CW, NPL = G::NPL;
+  constexpr int RPL = G::RPL, CL = G::CL, CW = G::CW, NPL = G::NPL, CPL = G::CPL;
   constexpr int GPL = FEW ? RPL : NPL;  // gate values loaded (and activated) per lane
-  using Tok = WTok<T, GPL, RPL>;
+  using Tok = WTok<T, GPL, RPL, CPL>;
+  using SV = typename StVec<CPL>::type;
+  using SB = typename StVec<CPL>::bits;
   const int64_t task = (int64_t)blockIdx.x * (kRecThreads / 64) + (threadIdx.x >> 6);
   if (task >= n_tasks) return;  // whole wave
   const int lane = threadIdx.x & 63;
@@ -361,7 +403,7 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
   const int h = hv / (HV / H);
   const int rl = FEW ? lane % G::RL : lane / CL, cl = FEW ? lane / G::RL : lane % CL;
   const int r0 = rl * RPL;
-  const int col = cb * CW + cl * 4;
+  const int col = cb * CW + cl * CPL;
   const bool col_ok = col < V;
 
   int64_t bos;
@@ -372,31 +414,34 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
   if (len == 0) {
     // empty slot: bitwise passthrough of the state (or +0.0 without one)
     if (!write_final || (h0 == ht && h0 != nullptr) || !col_ok) return;
-    u32x4 bits[RPL];
+    SB bits[RPL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i)
       bits[i] = h0 ? __builtin_nontemporal_load(
-                         reinterpret_cast<const u32x4*>(h0 + st_base + (size_t)i * V))
-                   : u32x4{0u, 0u, 0u, 0u};
+                         reinterpret_cast<const SB*>(h0 + st_base + (size_t)i * V))
+                   : SB(0u);
 #pragma unroll
     for (int i = 0; i < RPL; ++i)
-      __builtin_nontemporal_store(bits[i], reinterpret_cast<u32x4*>(ht + st_base + (size_t)i * V));
+      __builtin_nontemporal_store(bits[i], reinterpret_cast<SB*>(ht + st_base + (size_t)i * V));
     return;
   }
 
   // The state streams through once: non-temporal loads and stores keep it
   // from evicting the small per-token inputs from the caches.
-  float s[RPL][4];
+  float s[RPL][CPL];
   if (h0 && col_ok) {
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      const f32x4 x =
-          __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(h0 + st_base + (size_t)i * V));
-      s[i][0] = x[0]; s[i][1] = x[1]; s[i][2] = x[2]; s[i][3] = x[3];
+      const SV x =
+          __builtin_nontemporal_load(reinterpret_cast<const SV*>(h0 + st_base + (size_t)i * V));
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) s[i][e] = st_get<CPL>(x, e);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) s[i][0] = s[i][1] = s[i][2] = s[i][3] = 0.f;
+    for (int i = 0; i < RPL; ++i)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) s[i][e] = 0.f;
   }
 
   const float gscale = gate_head_scale(gate_mode, A_log, hv);
@@ -411,11 +456,11 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
       x.q.u[j] = qp[j];
     }
     x.g = *reinterpret_cast<const GVec<GPL>*>(gate + (t * HV + hv) * K + r0 + (FEW ? 0 : cl * NPL));
-    x.v = *reinterpret_cast<const decltype(x.v)*>(v + (t * HV + hv) * V + colc);
+    x.v.u[0] = *reinterpret_cast<const typename decltype(x.v)::U*>(v + (t * HV + hv) * V + colc);
     x.b = beta[t * HV + hv];
   };
   auto step = [&](const Tok& x, int64_t t) {
-    float kf[RPL], qf[RPL], vf[4];
+    float kf[RPL], qf[RPL], vf[CPL];
     unpack_rows(x, kf, qf);
     unpack_v(x, vf);
     // this lane's NPL decays (rows r0 + cl * NPL + m), then the row group's 16
@@ -423,7 +468,9 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     float dloc[GPL];
 #pragma unroll
     for (int m = 0; m < GPL; ++m) dloc[m] = exp2f(gate_log2_token(gf[m], gate_mode, gscale));
-    float u[4] = {0.f, 0.f, 0.f, 0.f}, w[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f, kk = 0.f, qq = 0.f;
+    float u[CPL], w[CPL], kq = 0.f, kk = 0.f, qq = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) u[e] = w[e] = 0.f;
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
       const float d = FEW ? dloc[FEW ? i : 0] : __shfl(dloc[i % GPL], rl * CL + i / NPL);
@@ -432,7 +479,7 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
       qf[i] *= scale;
       kq += kf[i] * qf[i];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < CPL; ++e) {
         s[i][e] *= d;
         u[e] += s[i][e] * kf[i];
         w[e] += s[i][e] * qf[i];
@@ -440,7 +487,7 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     }
     if constexpr (FEW) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < CPL; ++e) {
         u[e] = lane_group_sum<G::RL>(u[e]);
         w[e] = lane_group_sum<G::RL>(w[e]);
       }
@@ -453,7 +500,7 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
 #pragma unroll
       for (int m = CL; m < 64; m <<= 1) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < CPL; ++e) {
           u[e] += __shfl_xor(u[e], m);
           w[e] += __shfl_xor(w[e], m);
         }
@@ -471,25 +518,25 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
       rk = l2norm_inv(kk);
       const float rq = l2norm_inv(qq);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < CPL; ++e) {
         u[e] *= rk;
         w[e] *= rq;
       }
       kq *= rk * rq;
     }
     const float b = to_f32(x.b);
-    float dl[4], r[4];
+    float dl[CPL], r[CPL];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < CPL; ++e) {
       dl[e] = b * (vf[e] - u[e]);
       r[e] = w[e] + dl[e] * kq;
       dl[e] *= rk;
     }
-    if (rl == 0 && col_ok) store_o4(o + (t * HV + hv) * V + col, r);
+    if (rl == 0 && col_ok) store_o<CPL>(o + (t * HV + hv) * V + col, r);
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[i][e] += kf[i] * dl[e];
+      for (int e = 0; e < CPL; ++e) s[i][e] += kf[i] * dl[e];
     }
   };
 
@@ -523,8 +570,8 @@ recurrent_wave_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
   if (write_final && col_ok) {
 #pragma unroll
     for (int i = 0; i < RPL; ++i)
-      __builtin_nontemporal_store(f32x4{s[i][0], s[i][1], s[i][2], s[i][3]},
-                                  reinterpret_cast<f32x4*>(ht + st_base + (size_t)i * V));
+      __builtin_nontemporal_store(st_make<CPL>(s[i]),
+                                  reinterpret_cast<SV*>(ht + st_base + (size_t)i * V));
   }
 }
 
