@@ -1166,7 +1166,7 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
                        dim3(kThreads), lds_intra, s, (const T*)q, (const T*)k,
                        (const T*)v, gate, (int)kGateLog2, (const float*)nullptr, (const T*)beta,
                        cu, ws_int, d.N, d.T, d.H, d.HV, scale,
-                       ws_T, ws_GL, ws_B, ws_Bf, kda_short_conv{});
+                       ws_T, ws_GL, ws_B, ws_Bf, kda_short_conv{}, 1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t chains = (int64_t)d.N * d.HV;

@@ -389,7 +389,8 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                    const float* __restrict__ A_log, const T* __restrict__ beta,
                    const int32_t* __restrict__ cu, const int* __restrict__ ws_int, int N, int T_,
                    int H, int HV, float scale, T* __restrict__ ws_T, float* __restrict__ ws_GL,
-                   T* __restrict__ ws_B, float* __restrict__ ws_Bf, kda_short_conv conv) {
+                   T* __restrict__ ws_B, float* __restrict__ ws_Bf, kda_short_conv conv,
+                   int head_fast) {
   using M = MF<T>;
   using F = typename M::frag;
   using Lds = IntraLds<T, K, V>;
@@ -418,19 +419,17 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   float* sBeta = reinterpret_cast<float*>(smem + Lds::R1 + Lds::R2 + Lds::R3);
   float* sTot = reinterpret_cast<float*>(smem + Lds::R1 + Lds::R2 + Lds::R3 + Lds::RB);
 
-  // 1-D grid over (chunk, value head). The backward's recompute takes the value
-  // head fastest: the workgroups in flight together read whole token rows of q,
-  // k, v and the gate (all heads of a few chunks) instead of one head's
-  // 256-byte pieces of many chunks, with the head rotated by the chunk index
+  // 1-D grid over (chunk, value head). head_fast != 0 takes the value head
+  // fastest: the workgroups in flight together read whole token rows of q, k,
+  // v and the gate (all heads of a few chunks) instead of one head's 256-byte
+  // pieces of many chunks, with the head rotated by the chunk index
   // (workgroups are dealt to the XCDs in turn; without the rotation every chunk
-  // of head hv would land on XCD hv % 8). Measured on the long-context shape:
-  // 8% faster. The forward keeps the chunk fastest: on heads of very different
-  // decay strength (more reference passes on the strong ones) the head-fastest
-  // order measured 2% slower.
+  // of head hv would land on XCD hv % 8).
   const unsigned nch = gridDim.x / (unsigned)HV;
-  const int chunk = BWD ? (int)(blockIdx.x / (unsigned)HV) : (int)(blockIdx.x % nch);
-  const int hv = BWD ? (int)((blockIdx.x % (unsigned)HV + (unsigned)chunk) % (unsigned)HV)
-                     : (int)(blockIdx.x / nch);
+  const bool hf = BWD || head_fast;
+  const int chunk = hf ? (int)(blockIdx.x / (unsigned)HV) : (int)(blockIdx.x % nch);
+  const int hv = hf ? (int)((blockIdx.x % (unsigned)HV + (unsigned)chunk) % (unsigned)HV)
+                    : (int)(blockIdx.x / nch);
   const ChunkGeo geo = chunk_geo(chunk, cu, ws_int, N, T_);
   if (!geo.ok) return;
   const int h = hv / (HV / H);

@@ -239,7 +239,7 @@ constexpr int kFewCols = 1;  // state columns per lane in the FEW form
 
 template <int K, bool FEW>
 struct WaveGeo {
-  static constexpr int RPL = FEW ? (K >= 256 ? 4 : 2) : 16;  // state rows per lane
+  static constexpr int RPL = FEW ? K / 64 : 16;  // state rows per lane
   static constexpr int CPL = FEW ? kFewCols : 4;  // state columns per lane
   static constexpr int RL = K / RPL;             // row lanes
   static constexpr int CL = 64 / RL;             // column lanes (CPL columns each)
