@@ -322,7 +322,12 @@ struct BwdLds {
   // dT^T then dAbar, Xm, dAbar^T
   static constexpr size_t p2a = (size_t)K * CS * sizeof(T) + 2 * (size_t)kC * KSTR * sizeof(T);
   static constexpr size_t p2b = 3 * (size_t)kC * CS * sizeof(T);
-  static constexpr size_t szX = cmax(p1, pP + cmax(p2a, p2b));
+  // decay products (one-reference mode, bf16): kd, ke, qd fragments (hi and
+  // lo) of one channel tile per half, behind the three phase-2 slots; FP32
+  // builds them per wave (no room left in LDS)
+  static constexpr bool share_ops = sizeof(T) == 2;
+  static constexpr size_t pOp = share_ops ? 2 * 3 * 2 * (size_t)kC * 16 * sizeof(T) : 0;
+  static constexpr size_t szX = cmax(p1, pP + cmax(p2a, p2b + pOp));
   // small arrays: per-token-tile column sums [4][K], dgamma [K], row sums [C] x 3 parts x 2 halves
   static constexpr size_t szSmall = (4 * (size_t)K + K + 6 * (size_t)kC) * 4;
   static constexpr size_t oG = 0, oK = oG + szG, oT = oK + szK, oQ = oT + szT, oX = oQ + szQ,
@@ -944,6 +949,12 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     // operand rows that enter the products: Z pattern j <= jmax, Z' pattern i >= imin
     const int jmax = fastC ? kC - 1 : (tfast ? 16 * tt + 15 : 16 * tt - 1);
     const int imin = fastC ? 0 : (tfast ? 16 * tt : 16 * tt + 16);
+    // shared operand fragments of the one-reference mode, behind dP, dP^T and
+    // the three phase-2 slots: [half][operand kd, ke, qd][hi, lo][k-step][lane]
+    char* const sOp = X + Lds::pP + Lds::p2b;
+    auto op_slot = [&](int op, int hl, int ks) {
+      return sOp + ((((size_t)hh * 3 + op) * 2 + hl) * KS_C + ks) * 64 * sizeof(F) + lane * sizeof(F);
+    };
     F aP[KS_C], aPT[KS_C], aAb[KS_C], aAbT[KS_C];
     frag_rows<M, T, QC>(aP, sdP, 16 * tt + l16, CS, g);
     frag_rows<M, T, QC>(aPT, sdPT, 16 * tt + l16, CS, g);
@@ -955,29 +966,75 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       const float gz = sG[rz * GS + c], gzt = sG[rzt * GS + c];
       F kdh[KS_C], kdl[KS_C], keh[KS_C], kel[KS_C], qdh[KS_C], qdl[KS_C];
       float ed_t[4], eu_t[4], q_t[4], k_t[4], g_t[4];  // rows 16tt + 4g + e
-#pragma unroll
-      for (int p = 0; p < QC; ++p) {
+      if (Lds::share_ops && fastC) {
+        // One reference for the whole chunk: the operands of a channel tile are
+        // the same for the four waves of a half, so wave tt builds token quad tt
+        // (its own rows) and the quads meet in LDS.
         float kd[4], ke[4], qd[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int j = 16 * p + 4 * g + e;
+          const int j = 16 * tt + 4 * g + e;
           const float gj = sG[j * GS + c];
           const float kj = to_f32(sK[j * KSTR + c]), qj = to_f32(sQ[j * KSTR + c]);
           const float ed = ex2(gz - gj), eu = ex2(gj - gzt);
-          kd[e] = j <= jmax ? kj * ed : 0.f;
-          ke[e] = j >= imin ? kj * eu : 0.f;
-          qd[e] = j >= imin ? qj * scale * eu : 0.f;
-          if (p == tt) {
-            ed_t[e] = ed;
-            eu_t[e] = eu;
-            q_t[e] = qj;
-            k_t[e] = kj;
-            g_t[e] = gj;
-          }
+          kd[e] = kj * ed;
+          ke[e] = kj * eu;
+          qd[e] = qj * scale * eu;
+          ed_t[e] = ed;
+          eu_t[e] = eu;
+          q_t[e] = qj;
+          k_t[e] = kj;
+          g_t[e] = gj;
         }
-        put_quad_split<M>(kdh, kdl, p, kd);
-        put_quad_split<M>(keh, kel, p, ke);
-        put_quad_split<M>(qdh, qdl, p, qd);
+        __syncthreads();  // the previous channel tile's operands are read
+        const float* src[3] = {kd, ke, qd};
+#pragma unroll
+        for (int op = 0; op < 3; ++op) {
+          bf16x4 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hi[e] = (bf16)src[op][e];
+            lo[e] = (bf16)(src[op][e] - (float)hi[e]);
+          }
+          // quad tt is slots 4 (tt & 1) .. + 3 of fragment tt / 2
+          *reinterpret_cast<bf16x4*>(op_slot(op, 0, tt >> 1) + 8 * (tt & 1)) = hi;
+          *reinterpret_cast<bf16x4*>(op_slot(op, 1, tt >> 1) + 8 * (tt & 1)) = lo;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) {
+          kdh[ks] = *reinterpret_cast<const F*>(op_slot(0, 0, ks));
+          keh[ks] = *reinterpret_cast<const F*>(op_slot(1, 0, ks));
+          qdh[ks] = *reinterpret_cast<const F*>(op_slot(2, 0, ks));
+          kdl[ks] = *reinterpret_cast<const F*>(op_slot(0, 1, ks));
+          kel[ks] = *reinterpret_cast<const F*>(op_slot(1, 1, ks));
+          qdl[ks] = *reinterpret_cast<const F*>(op_slot(2, 1, ks));
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < QC; ++p) {
+          float kd[4], ke[4], qd[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 16 * p + 4 * g + e;
+            const float gj = sG[j * GS + c];
+            const float kj = to_f32(sK[j * KSTR + c]), qj = to_f32(sQ[j * KSTR + c]);
+            const float ed = ex2(gz - gj), eu = ex2(gj - gzt);
+            kd[e] = j <= jmax ? kj * ed : 0.f;
+            ke[e] = j >= imin ? kj * eu : 0.f;
+            qd[e] = j >= imin ? qj * scale * eu : 0.f;
+            if (p == tt) {
+              ed_t[e] = ed;
+              eu_t[e] = eu;
+              q_t[e] = qj;
+              k_t[e] = kj;
+              g_t[e] = gj;
+            }
+          }
+          put_quad_split<M>(kdh, kdl, p, kd);
+          put_quad_split<M>(keh, kel, p, ke);
+          put_quad_split<M>(qdh, qdl, p, qd);
+        }
       }
       f32x4 y1 = zero4(), x1 = zero4(), y2 = zero4(), x2 = zero4();
 #pragma unroll
