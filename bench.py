@@ -50,8 +50,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_SOURCES = ("gated_delta_rule_69_amd/csrc/kda_common.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk_kernels.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk.hip")
-TRAFFIC_SHA16 = "337d32f33fe50fce"
-TRAFFIC_BYTES = 1020.9e6
+TRAFFIC_SHA16 = "26f3522294292751"
+TRAFFIC_BYTES = 1087.9e6
 
 
 def measured_traffic():
