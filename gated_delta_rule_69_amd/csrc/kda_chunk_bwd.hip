@@ -793,6 +793,13 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
 
   // ---- phase 2: dT, T^T dW, dA
   {
+    // Abar entries of this lane's dA elements, requested now and used at the
+    // end of the phase (a load at the use would stall the wave on its latency)
+    float abv[JH][4];
+#pragma unroll
+    for (int jj = 0; jj < JH; ++jj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) abv[jj][e] = wAb[(16 * tt + 4 * g + e) * kC + 16 * (JH * hh + jj) + l16];
     T* sdWT = XP;                                 // [K][CS]
     T* sBKg = sdWT + K * CS;                      // [C][KSTR] b * k * Gamma
     T* sdW = sBKg + kC * KSTR;                    // [C][KSTR] row-major dW
@@ -899,7 +906,7 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
         for (int e = 0; e < 4; ++e) {
           const int a = 16 * tt + 4 * g + e, c = 16 * J + l16;
           const float da = (c < a) ? -acc[e] : 0.f;
-          dba[e] += wAb[a * kC + c] * da;
+          dba[e] += abv[jj][e] * da;
           const T x = from_f32<T>(bet[e] * da);
           sdAb[a * CS + c] = x;
           sdAbT[c * CS + a] = x;
