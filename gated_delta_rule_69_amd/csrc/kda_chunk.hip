@@ -79,8 +79,13 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
   float* ws_GL = reinterpret_cast<float*>(p);
   p += align256((size_t)mc * d.HV * Ws<T, K, V>::bytes_GL);
   // save != 0: `ws` is the backward pass's workspace, whose first regions have
-  // the forward's layout and whose per-chunk area follows them
+  // the forward's layout and whose per-chunk areas (T-typed, then FP32) follow
   T* ws_save = save ? reinterpret_cast<T*>(p) : nullptr;
+  float* ws_save_f =
+      save ? reinterpret_cast<float*>(p + align256((size_t)mc * d.HV * WsB<T, K, V>::elems * sizeof(T)))
+           : nullptr;
+  // the training forward takes the precomputed gate and no pre-processing
+  if (save && (gate_mode != kGateLog2 || qn || conv)) return hipErrorInvalidValue;
   if (varlen) {
     hipError_t e = launch_chunk_table(cu, d.N, ws_int, (int)mc, s);
     if (e != hipSuccess) return e;
@@ -102,7 +107,15 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
                          1.0f / sqrtf((float)K), ws_T, ws_GL, (T*)nullptr, (float*)nullptr, taps,
                          head_fast);
     };
-    if (conv) {
+    if (save) {
+      // training forward: the intra kernel also forms the backward's entries
+      // (so the backward after it runs no intra-chunk recompute)
+      hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, true, false, false, true>),
+                         dim3((unsigned)(mc * d.HV)), dim3(kThreads), lds, s, (const T*)q,
+                         (const T*)k, (const T*)v, gate, gate_mode, A_log, (const T*)beta, cu,
+                         ws_int, d.N, d.T, d.H, d.HV, 1.0f / sqrtf((float)K), ws_T, ws_GL, ws_save,
+                         ws_save_f, taps, 1);
+    } else if (conv) {
       if (qn) launch_intra(std::true_type(), std::true_type());
       else launch_intra(std::false_type(), std::true_type());
     } else {
@@ -179,9 +192,10 @@ static hipError_t run_kv(const kda_dims& d, const void* q, const void* k, const 
   const void* fns[] = {reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, false, false>),
                        reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, true, false>),
                        reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, false, true>),
-                       reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, true, true>)};
-  for (int i = 0; i < 4; ++i) {
-    const int lds = (int)(i < 2 ? Lds::total : Lds::total_conv);
+                       reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, false, true, true>),
+                       reinterpret_cast<const void*>(&kda::chunk_intra_kernel<T, K, V, true, false, false, true>)};
+  for (int i = 0; i < 5; ++i) {
+    const int lds = (int)(i == 2 || i == 3 ? Lds::total_conv : Lds::total);
     hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
   }

@@ -1222,24 +1222,18 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
   }
   const float scale = 1.0f / sqrtf((float)K);
   if (mc > 0) {
-    // after a training forward (saved) the forward pass's entries of the
-    // workspace are in place: the recompute forms only the backward's
-    auto launch_intra = [&](auto skc) -> hipError_t {
-      constexpr bool SK = decltype(skc)::value;
-      hipError_t r = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&chunk_intra_kernel<T, K, V, true, false, false, SK>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, (int)IntraLds<T, K, V>::total);
-      if (r != hipSuccess) return r;
+    // after a training forward (saved) every intra-chunk entry is in place
+    if (!saved) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_intra_kernel<T, K, V, true, false, false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)IntraLds<T, K, V>::total);
+      if (e != hipSuccess) return e;
       const size_t lds_intra = IntraLds<T, K, V>::total;
-      hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, true, false, false, SK>), dim3((unsigned)(mc * d.HV)),
+      hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, true, false, false>), dim3((unsigned)(mc * d.HV)),
                          dim3(kThreads), lds_intra, s, (const T*)q, (const T*)k,
                          (const T*)v, gate, (int)kGateLog2, (const float*)nullptr, (const T*)beta,
                          cu, ws_int, d.N, d.T, d.H, d.HV, scale,
                          ws_T, ws_GL, ws_B, ws_Bf, kda_short_conv{}, 1);
-      return hipSuccess;
-    };
-    e = saved ? launch_intra(std::true_type()) : launch_intra(std::false_type());
-    if (e != hipSuccess) return e;
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t chains = (int64_t)d.N * d.HV;

@@ -382,10 +382,10 @@ constexpr float kFastRange = 112.f;
 // are raw projections; the short convolution + SiLU (taps in `conv`) runs on
 // them first, and each thread then holds consecutive rows so that a row's
 // window above it is its own rows plus W - 1 rows read again from L2.
-// SKIPT (with BWD): a training forward already wrote the forward pass's
-// entries of this workspace (W, Khat^T, U, the gate row), which the backward
-// after it does not read again: only the backward's entries are formed.
-template <typename T, int K, int V, bool BWD, bool QN, bool CONV, bool SKIPT = false>
+// TRAIN (with BWD): the training forward -- the forward pass's entries (P and
+// Q~ Gamma as well) and the backward's, so that the backward after it needs
+// no intra-chunk recompute.
+template <typename T, int K, int V, bool BWD, bool QN, bool CONV, bool TRAIN = false>
 __global__ void __launch_bounds__(kThreads, 2)
 chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                    const float* __restrict__ gate, int gate_mode,
@@ -494,8 +494,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   for (int u = 0; u < VU; ++u) {
     const int row = vrow(tid, u), cu_ = tid % TV;
     const int rr = row < L ? row : L - 1;
-    if constexpr (SKIPT) vr[u] = make_uint4(0, 0, 0, 0);  // U is not formed
-    else vr[u] = *reinterpret_cast<const uint4*>(v + ((t0 + rr) * HV + hv) * V + EPU * cu_);
+    vr[u] = *reinterpret_cast<const uint4*>(v + ((t0 + rr) * HV + hv) * V + EPU * cu_);
   }
   const int brow = tid % kC < L ? tid % kC : L - 1;
   const T braw = beta[(t0 + brow) * HV + hv];  // every thread loads; threads < kC store
@@ -869,7 +868,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   // ---- 3. P fragments (rows i of tile I, contraction over j): accumulators of P^T
   // (P and Q~ Gamma in ws_T feed only the forward output; the backward's
   // recurrence forms no output and reads neither)
-  if constexpr (!BWD) {
+  if constexpr (!BWD || TRAIN) {
 #pragma unroll
     for (int ks = 0; ks < KS_C; ++ks) {
       F f, fl;
@@ -948,7 +947,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     }
   }
   // ---- 4. Q~ * Gamma fragments (rows i of tile I, contraction over channels)
-  if constexpr (!BWD) {
+  if constexpr (!BWD || TRAIN) {
     F f[KS_K];
 #pragma unroll
     for (int p = 0; p < QK; ++p) {
@@ -965,7 +964,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   }
   // ---- 5. Khat^T fragments (rows = channels, contraction over tokens j)
 #pragma unroll
-  for (int rt0 = 0; rt0 < (SKIPT ? 0 : K / 16); rt0 += 4) {
+  for (int rt0 = 0; rt0 < K / 16; rt0 += 4) {
     const int rt = rt0 + wave;
     const int c = 16 * rt + l16;
     const float gl = sG[(L - 1) * GS + c];
@@ -983,7 +982,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 #pragma unroll
     for (int ks = 0; ks < KS_C; ++ks) reinterpret_cast<F*>(wsKH)[((size_t)rt * KS_C + ks) * 64 + lane] = f[ks];
   }
-  if (!SKIPT && tid < K) wsGL[tid] = ex2(sG[(L - 1) * GS + tid]);
+  if (tid < K) wsGL[tid] = ex2(sG[(L - 1) * GS + tid]);
   __syncthreads();  // q is dead: R3 <- A
 
   // ---- 6. A = b_i (A^T accumulators)^T into LDS (zero above the diagonal tiles)
@@ -1146,7 +1145,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     }
     // channel tiles 2pw, 2pw+1 are contraction steps {pw} (bf16) or {8pw..8pw+7} (FP32)
 #pragma unroll
-    for (int ii = 0; ii < (SKIPT ? 0 : NP); ++ii) {
+    for (int ii = 0; ii < NP; ++ii) {
       if constexpr (M::KSTEP == 32) {
         F f;
 #pragma unroll
@@ -1164,7 +1163,6 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
       }
     }
   }
-  if constexpr (SKIPT) return;  // U is not formed
   __syncthreads();  // G2 and k are dead: R1 <- V (row-major)
   constexpr int VSTR = Lds::VSTR;
   T* sV = reinterpret_cast<T*>(smem);  // R1: v [C][VSTR]
