@@ -382,12 +382,14 @@ kda_status kda_chunk_bwd(const kda_dims* dims, kda_dtype dtype, const void* q, c
 
 /*
  * kda_chunk_fwd_train -- kda_chunk_fwd for training: the same outputs (o and
- * final_state bit-identical to kda_chunk_fwd), and on the way every chunk's
- * start state and Delta = U - W S0 (what the backward's recurrence would form
- * again, steps B1 and B2 of the chunked pipeline's backward, fwd_h / bwd_dhu in
- * the squashed commit bodies of "[Fix] Use unit KDA gate scale when A_log is
- * omitted") are stored in the backward pass's workspace, so that
- * kda_chunk_bwd_saved can skip that recurrence.
+ * final_state bit-identical to kda_chunk_fwd), and on the way the backward
+ * pass's workspace is filled with what the backward would otherwise form
+ * again: every chunk's start state and Delta = U - W S0 (the backward's
+ * forward recurrence, steps B1 and B2 of the chunked pipeline's backward,
+ * fwd_h / bwd_dhu in the squashed commit bodies of "[Fix] Use unit KDA gate
+ * scale when A_log is omitted") and the intra-chunk matrices the backward
+ * reads (its recompute of the intra-chunk terms), so that kda_chunk_bwd_saved
+ * skips both.
  *   Arguments as kda_chunk_fwd, except the workspace:
  *   bwd_workspace  at least kda_chunk_bwd_workspace_bytes() for the same
  *          dims, dtype and chunk_size, 256-byte aligned; to be handed,
@@ -406,9 +408,10 @@ kda_status kda_chunk_fwd_train(const kda_dims* dims, kda_dtype dtype, const void
 
 /*
  * kda_chunk_bwd_saved -- kda_chunk_bwd after kda_chunk_fwd_train: takes the
- * chunk start states and Deltas that the training forward stored in
- * `workspace` instead of running the forward recurrence again; all other
- * steps as kda_chunk_bwd, and every gradient bit-identical to it.
+ * chunk start states, Deltas and intra-chunk matrices that the training
+ * forward stored in `workspace` instead of forming them again (no forward
+ * recurrence, no intra-chunk recompute); the remaining steps as kda_chunk_bwd,
+ * and every gradient bit-identical to it.
  *   Arguments, sizes and errors as kda_chunk_bwd. Precondition (not
  *   checkable on the host): `workspace` holds the output of
  *   kda_chunk_fwd_train on the same dims, dtype, chunk_size and inputs, and has
