@@ -1319,7 +1319,9 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     raw4 u[CPW];
     float4 gl[RTW];
   };
-  auto load_ops = [&](int cj, Ops& op) {
+  // part < 0: every operand; else one of four batches (W; Q~Gamma; P; Khat^T,
+  // gate row, U), issued at four points of the previous chunk's step
+  auto load_ops = [&](int cj, Ops& op, int part = -1) __attribute__((always_inline)) {
     const size_t ch = (size_t)cj * HV + hv;
     const T* wsW = ws_T + ch * WsL::elems;
     const F* fW = reinterpret_cast<const F*>(wsW);
@@ -1328,29 +1330,36 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     const F* fP = reinterpret_cast<const F*>(wsW + WsL::W + WsL::QG + WsL::KH);
     const F* fPL = reinterpret_cast<const F*>(wsW + WsL::W + WsL::QG + WsL::KH + WsL::P);
     const T* wsU = wsW + WsL::W + WsL::QG + WsL::KH + WsL::P + WsL::PL;
+    if (part < 0 || part == 0) {
 #pragma unroll
-    for (int ks = 0; ks < KS_K; ++ks) {
-      op.w[ks] = fW[((size_t)tt * KS_K + ks) * 64 + lane];
-      if constexpr (!KEEP) op.qg[ks] = fQG[((size_t)tt * KS_K + ks) * 64 + lane];
+      for (int ks = 0; ks < KS_K; ++ks) op.w[ks] = fW[((size_t)tt * KS_K + ks) * 64 + lane];
     }
     if constexpr (!KEEP) {
+      if (part < 0 || part == 1) {
 #pragma unroll
-      for (int ks = 0; ks < KS_C; ++ks) {
-        op.p[ks] = fP[((size_t)tt * KS_C + ks) * 64 + lane];
-        if constexpr (WsL::PL > 0) op.pl[ks] = fPL[((size_t)tt * KS_C + ks) * 64 + lane];
+        for (int ks = 0; ks < KS_K; ++ks) op.qg[ks] = fQG[((size_t)tt * KS_K + ks) * 64 + lane];
+      }
+      if (part < 0 || part == 2) {
+#pragma unroll
+        for (int ks = 0; ks < KS_C; ++ks) {
+          op.p[ks] = fP[((size_t)tt * KS_C + ks) * 64 + lane];
+          if constexpr (WsL::PL > 0) op.pl[ks] = fPL[((size_t)tt * KS_C + ks) * 64 + lane];
+        }
       }
     }
+    if (part < 0 || part == 3) {
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
+      for (int rt = 0; rt < RTW; ++rt) {
 #pragma unroll
-      for (int ks = 0; ks < KS_C; ++ks)
-        op.kh[rt][ks] = fKH[((size_t)(RTW * wave + rt) * KS_C + ks) * 64 + lane];
-      op.gl[rt] = *reinterpret_cast<const float4*>(ws_GL + ch * K + 16 * (RTW * wave + rt) + 4 * g);
-    }
+        for (int ks = 0; ks < KS_C; ++ks)
+          op.kh[rt][ks] = fKH[((size_t)(RTW * wave + rt) * KS_C + ks) * 64 + lane];
+        op.gl[rt] = *reinterpret_cast<const float4*>(ws_GL + ch * K + 16 * (RTW * wave + rt) + 4 * g);
+      }
 #pragma unroll
-    for (int cc = 0; cc < CPW; ++cc) {
-      const int vt = (col_base >> 4) + ct0 + cc;
-      op.u[cc] = *reinterpret_cast<const raw4*>(wsU + (((size_t)tt * (V / 16) + vt) * 64 + lane) * 4);
+      for (int cc = 0; cc < CPW; ++cc) {
+        const int vt = (col_base >> 4) + ct0 + cc;
+        op.u[cc] = *reinterpret_cast<const raw4*>(wsU + (((size_t)tt * (V / 16) + vt) * 64 + lane) * 4);
+      }
     }
   };
 
@@ -1430,11 +1439,21 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
   // one chunk of the recurrence with operands `cur`, LDS buffer `buf`; the
   // previous chunk's output (registers `prv`) is formed after the first
   // barrier, and this chunk's output registers are collected in `mine`
+  // The next chunk's operands (chunk cn into `nxt`): with an output and 32 or
+  // more value columns, requested in four batches spread over the step (a wave
+  // stalls when it issues more loads than the compute unit's memory path has
+  // room for, and a stall between phases leaves the phases running:
+  // 138 -> 131 us dense, 651 -> 578 us varlen); the short steps of narrower
+  // blocks and of the backward's recurrence need every operand a whole step
+  // ahead and take them at once.
+  constexpr bool SPLIT = !KEEP && BV >= 32;
   auto step = [&](const Ops& cur, const int cj, const int buf, OutOps& mine,
-                  const OutOps& prv) __attribute__((always_inline)) {
+                  const OutOps& prv, const int cn, Ops& nxt) __attribute__((always_inline)) {
     const int cidx = cj - cbeg;
     const int64_t t0 = bos + (int64_t)cidx * kC;
     const int L = min(kC, len - cidx * kC);
+    load_ops(cn, nxt, SPLIT ? 0 : -1);
+    __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (STORE) {  // backward support: keep the chunk's start state
       T* st = ws_B + ((size_t)cj * HV + hv) * WsB<T, K, V>::elems + WsB<T, K, V>::oS0;
@@ -1470,7 +1489,16 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     }
     __syncthreads();
 
+    if constexpr (SPLIT) {
+      load_ops(cn, nxt, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (cj > cbeg) output(prv, cj - 1, buf ^ 1);
+    if constexpr (SPLIT) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_ops(cn, nxt, 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // (2) Delta = U - W S for token tile tt, value tiles ct0..ct0+CPW-1
     f32x4 D[CPW];
     {
@@ -1518,6 +1546,10 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
       }
     }
     __syncthreads();
+    if constexpr (SPLIT) {
+      load_ops(cn, nxt, 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     F dall[KS_C][CTB];
 #pragma unroll
     for (int ks = 0; ks < KS_C; ++ks) {
@@ -1570,14 +1602,12 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
   OutOps oA, oB;
   load_ops(cbeg, opA);
   for (int cj = cbeg;; cj += 2) {
-    load_ops(min(cj + 1, cend - 1), opB);
-    step(opA, cj, 0, oA, oB);
+    step(opA, cj, 0, oA, oB, min(cj + 1, cend - 1), opB);
     if (cj + 1 >= cend) {
       output(oA, cj, 0);
       break;
     }
-    load_ops(min(cj + 2, cend - 1), opA);
-    step(opB, cj + 1, 1, oB, oA);
+    step(opB, cj + 1, 1, oB, oA, min(cj + 2, cend - 1), opA);
     if (cj + 2 >= cend) {
       output(oB, cj + 1, 1);
       break;
