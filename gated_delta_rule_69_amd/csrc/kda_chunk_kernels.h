@@ -490,21 +490,30 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     kr[u] = *reinterpret_cast<const uint4*>(k + ((t0 + rr) * H + h) * K + EPU * cu_);
     qr[u] = *reinterpret_cast<const uint4*>(q + ((t0 + rr) * H + h) * K + EPU * cu_);
   }
+  // v is first used by U, the last phase: without the convolution its loads
+  // are issued after the A/P tiles, so the workgroup's first load batch (the
+  // one every phase waits for) is a fifth smaller
+  auto load_v = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int u = 0; u < VU; ++u) {
-    const int row = vrow(tid, u), cu_ = tid % TV;
-    const int rr = row < L ? row : L - 1;
-    vr[u] = *reinterpret_cast<const uint4*>(v + ((t0 + rr) * HV + hv) * V + EPU * cu_);
-  }
+    for (int u = 0; u < VU; ++u) {
+      const int row = vrow(tid, u), cu_ = tid % TV;
+      const int rr = row < L ? row : L - 1;
+      vr[u] = *reinterpret_cast<const uint4*>(v + ((t0 + rr) * HV + hv) * V + EPU * cu_);
+    }
+  };
+  if constexpr (CONV) load_v();
   const int brow = tid % kC < L ? tid % kC : L - 1;
   const T braw = beta[(t0 + brow) * HV + hv];  // every thread loads; threads < kC store
+  auto zero_v_pad = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < VU; ++u)
+      if (vrow(tid, u) >= L) vr[u] = make_uint4(0, 0, 0, 0);
+  };
   auto zero_pad_rows = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < KU; ++u)
       if (krow(tid, u) >= L) kr[u] = qr[u] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < VU; ++u)
-      if (vrow(tid, u) >= L) vr[u] = make_uint4(0, 0, 0, 0);
+    if constexpr (CONV) zero_v_pad();
   };
   if constexpr (CONV) {
     constexpr int MW = kConvMaxWidth;
@@ -857,6 +866,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     }
   }
 
+  if constexpr (!CONV) load_v();
   T* wsW = ws_T + ch * WsL::elems;
   T* wsQG = wsW + WsL::W;
   T* wsKH = wsQG + WsL::QG;
@@ -1166,6 +1176,7 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   __syncthreads();  // G2 and k are dead: R1 <- V (row-major)
   constexpr int VSTR = Lds::VSTR;
   T* sV = reinterpret_cast<T*>(smem);  // R1: v [C][VSTR]
+  if constexpr (!CONV) zero_v_pad();
 #pragma unroll
   for (int u = 0; u < VU; ++u) {
     const int m = vrow(tid, u), cu_ = tid % TV;
