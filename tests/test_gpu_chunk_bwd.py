@@ -126,9 +126,12 @@ def test_bwd_no_dht_no_h0():
     ("bf16", 64, 64, 1, 1, 1, [0, 130]),          # one chain: 16-column scans
 ])
 def test_training_forward_then_saved_backward_bitwise(dtype, K, V, B, H, HV, cu):
-    """kda_chunk_fwd_train stores every chunk's start state and Delta in the
-    backward's workspace; kda_chunk_bwd_saved then skips the recurrence. Both
-    must give bit for bit what kda_chunk_fwd and kda_chunk_bwd give."""
+    """kda_chunk_fwd_train stores every chunk's start state and Delta and the
+    backward's intra-chunk matrices in the backward's workspace;
+    kda_chunk_bwd_saved then skips the recurrence and the intra-chunk
+    recompute. Both must give bit for bit what kda_chunk_fwd and kda_chunk_bwd
+    give (a workspace filled with NaN bytes first: everything the saved
+    backward reads must have been written by the training forward)."""
     T = 200 if cu is None else cu[-1] + 7
     wl = workloads.tiny_case(470 + K + V + HV, B=B, T=T, H=H, HV=HV, K=K, V=V, dtype=dtype,
                              cu_seqlens=cu, grads=True, A_log=1.0)
