@@ -98,11 +98,16 @@ __device__ __forceinline__ size_t il4(int r, int c, int V) {
 template <typename T>
 __device__ __forceinline__ void store4(T* p, const float v0, const float v1, const float v2,
                                        const float v3) {
+  // non-temporal: these are read back by a later kernel, long after the
+  // caches could hold them, and would otherwise evict the operands the other
+  // workgroups of the chain are about to read (saving, keeping and reverse
+  // scans 3% faster)
   if constexpr (sizeof(T) == 2) {
     bf16x4 x = {(bf16)v0, (bf16)v1, (bf16)v2, (bf16)v3};
-    *reinterpret_cast<bf16x4*>(p) = x;
+    typedef unsigned int u32x2_ __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x2_, x), reinterpret_cast<u32x2_*>(p));
   } else {
-    *reinterpret_cast<float4*>(p) = make_float4(v0, v1, v2, v3);
+    __builtin_nontemporal_store(f32x4{v0, v1, v2, v3}, reinterpret_cast<f32x4*>(p));
   }
 }
 
