@@ -473,7 +473,7 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     uint4 a[NUC], b[NUC], c[NUC], d[NUC], s0[NUK], ds[NUK];
   };
   auto il_unit = [&](size_t off, int u, int c0) {
-    return *reinterpret_cast<const uint4*>(wb + off + il4(4 * (u / UPG), c0 + CPU * (u % UPG), V));
+    return ldg_nt(reinterpret_cast<const uint4*>(wb + off + il4(4 * (u / UPG), c0 + CPU * (u % UPG), V)));
   };
   auto load_blk = [&](int vb, Blk& x) {
     const int c0 = vb * VB;
@@ -563,7 +563,7 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
 #pragma unroll
     for (int i = 0; i < NTm; ++i) {
       const int f = tid + i * NT, row = f / (kC / 4), c4 = f % (kC / 4);
-      tx[i] = *reinterpret_cast<const float4*>(wTm + row * kC + 4 * c4);
+      tx[i] = ldg_nt(reinterpret_cast<const float4*>(wTm + row * kC + 4 * c4));
     }
     // beta of the chunk's rows (row tid % C; pad rows load the last valid row):
     // unconditional, in the same batch as the other loads

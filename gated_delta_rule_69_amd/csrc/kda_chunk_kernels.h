@@ -132,6 +132,18 @@ __device__ __forceinline__ void st_nt(V_* p, const V_& v) {
   }
 }
 
+// Non-temporal 16-byte load, for data a kernel reads exactly once (the
+// backward local kernel's saved states and matrices: 1.9% faster there).
+__device__ __forceinline__ uint4 ldg_nt(const uint4* p) {
+  typedef unsigned u4_ __attribute__((ext_vector_type(4)));
+  const u4_ r = __builtin_nontemporal_load(reinterpret_cast<const u4_*>(p));
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+__device__ __forceinline__ float4 ldg_nt(const float4* p) {
+  const f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(r[0], r[1], r[2], r[3]);
+}
+
 struct ChunkGeo {
   int ok;        // 0: no such chunk (grid over-provisioned)
   int n;         // sequence
