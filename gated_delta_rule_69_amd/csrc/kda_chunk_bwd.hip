@@ -483,8 +483,8 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
       const int row = u / UPR < kC ? u / UPR : 0, cu_ = u % UPR;
       const int rr = row < L ? row : 0;
       const int ui = u < kC * UPR ? u : 0;
-      x.a[i] = *reinterpret_cast<const uint4*>(dO + ((t0 + rr) * HV + hv) * V + c0 + EPU * cu_);
-      x.d[i] = *reinterpret_cast<const uint4*>(v + ((t0 + rr) * HV + hv) * V + c0 + EPU * cu_);
+      x.a[i] = ldg_nt(reinterpret_cast<const uint4*>(dO + ((t0 + rr) * HV + hv) * V + c0 + EPU * cu_));
+      x.d[i] = ldg_nt(reinterpret_cast<const uint4*>(v + ((t0 + rr) * HV + hv) * V + c0 + EPU * cu_));
       x.b[i] = il_unit(WB::oDL, ui, c0);
       x.c[i] = il_unit(WB::oDDL, ui, c0);
     }
@@ -551,14 +551,14 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     for (int i = 0; i < NG; ++i) {
       const int f = tid + i * NT, row = f / (K / 4), c4 = f % (K / 4);
       const int rr = row < L ? row : L - 1;
-      gx[i] = *reinterpret_cast<const float4*>(gate + ((t0 + rr) * HV + hv) * K + 4 * c4);
+      gx[i] = ldg_nt(reinterpret_cast<const float4*>(gate + ((t0 + rr) * HV + hv) * K + 4 * c4));
     }
 #pragma unroll
     for (int i = 0; i < NKQ; ++i) {
       const int f = tid + i * NT, row = f / (K / EPU), cu_ = f % (K / EPU);
       const int rr = row < L ? row : 0;
-      kx[i] = *reinterpret_cast<const uint4*>(k + ((t0 + rr) * H + h) * K + EPU * cu_);
-      qx[i] = *reinterpret_cast<const uint4*>(q + ((t0 + rr) * H + h) * K + EPU * cu_);
+      kx[i] = ldg_nt(reinterpret_cast<const uint4*>(k + ((t0 + rr) * H + h) * K + EPU * cu_));
+      qx[i] = ldg_nt(reinterpret_cast<const uint4*>(q + ((t0 + rr) * H + h) * K + EPU * cu_));
     }
 #pragma unroll
     for (int i = 0; i < NTm; ++i) {

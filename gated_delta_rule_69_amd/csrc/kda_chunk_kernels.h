@@ -133,7 +133,8 @@ __device__ __forceinline__ void st_nt(V_* p, const V_& v) {
 }
 
 // Non-temporal 16-byte load, for data a kernel reads exactly once (the
-// backward local kernel's saved states and matrices: 1.9% faster there).
+// backward local kernel's saved states and matrices, its q, k, gate, dO and v
+// rows: 3613 -> 3486 us).
 __device__ __forceinline__ uint4 ldg_nt(const uint4* p) {
   typedef unsigned u4_ __attribute__((ext_vector_type(4)));
   const u4_ r = __builtin_nontemporal_load(reinterpret_cast<const u4_*>(p));
