@@ -50,8 +50,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_SOURCES = ("gated_delta_rule_69_amd/csrc/kda_common.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk_kernels.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk.hip")
-TRAFFIC_SHA16 = "86cedee695e1b0b2"
-TRAFFIC_BYTES = 1088.7e6
+TRAFFIC_SHA16 = "23bb1d0c05a65900"
+TRAFFIC_BYTES = 1085.7e6
 
 
 def measured_traffic():
