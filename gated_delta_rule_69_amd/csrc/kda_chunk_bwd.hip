@@ -194,15 +194,23 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
         for (int rt = 0; rt < RTW; ++rt) Sin[rt][ct] = M::mma(op.qgt[rt][ks], bdo[ct][ks], Sin[rt][ct]);
       }
 
-    // keep dS1 of this chunk for the local kernel; publish it as B fragments
+    // keep dS1 of this chunk for the local kernel; publish it as B fragments.
+    // With up to 32 columns the stores of dS1 and dDelta wait until after the
+    // second barrier (a copy of dS1 in registers), behind the step's loads
+    // rather than in front of them
+    constexpr bool LATE = BV <= 32;
     T* dsl = wb + WB::oDS;
+    f32x4 s1c[LATE ? RTW : 1][LATE ? CTB : 1];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
       const int tileK = RTW * wave + rt;
 #pragma unroll
       for (int ct = 0; ct < CTB; ++ct) {
-        store4<T>(dsl + il4(16 * tileK + 4 * g, col_base + 16 * ct + l16, V), S[rt][ct][0],
-                  S[rt][ct][1], S[rt][ct][2], S[rt][ct][3]);
+        if constexpr (LATE)
+          s1c[rt][ct] = S[rt][ct];
+        else
+          store4<T>(dsl + il4(16 * tileK + 4 * g, col_base + 16 * ct + l16, V), S[rt][ct][0],
+                    S[rt][ct][1], S[rt][ct][2], S[rt][ct][3]);
         if constexpr (M::KSTEP == 32) {
           bf16x4 x;
 #pragma unroll
@@ -229,8 +237,9 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
     T* ddl = wb + WB::oDDL;
 #pragma unroll
     for (int ct = 0; ct < CTB; ++ct) {
-      store4<T>(ddl + il4(16 * wave + 4 * g, col_base + 16 * ct + l16, V), D[ct][0], D[ct][1],
-                D[ct][2], D[ct][3]);
+      if constexpr (!LATE)
+        store4<T>(ddl + il4(16 * wave + 4 * g, col_base + 16 * ct + l16, V), D[ct][0], D[ct][1],
+                  D[ct][2], D[ct][3]);
       if constexpr (M::KSTEP == 32) {
         bf16x4 x;
 #pragma unroll
@@ -248,6 +257,18 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
     // the dO block of the next chunk in the reverse order
     stage_dob(max(cj - 1, cbeg), op.dob, sdO[buf ^ 1]);
     __syncthreads();
+    if constexpr (LATE) {
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CTB; ++ct)
+          store4<T>(dsl + il4(16 * (RTW * wave + rt) + 4 * g, col_base + 16 * ct + l16, V),
+                    s1c[rt][ct][0], s1c[rt][ct][1], s1c[rt][ct][2], s1c[rt][ct][3]);
+#pragma unroll
+      for (int ct = 0; ct < CTB; ++ct)
+        store4<T>(ddl + il4(16 * wave + 4 * g, col_base + 16 * ct + l16, V), D[ct][0], D[ct][1],
+                  D[ct][2], D[ct][3]);
+    }
 
     // dS0 = Diag(gamma) dS1 + (Q~Gamma)^T dO - W^T dDelta
 #pragma unroll

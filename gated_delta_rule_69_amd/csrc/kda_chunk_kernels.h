@@ -1505,7 +1505,18 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     load_ops(cn, nxt, SPLIT ? 0 : -1);
     __builtin_amdgcn_sched_barrier(0);
 
-    if constexpr (STORE) {  // backward support: keep the chunk's start state
+    // backward support: keep the chunk's start state and Delta. With up to 32
+    // columns the stores wait until after the second barrier (copies in
+    // registers), so that they queue behind the step's loads, not in front of them
+    constexpr bool LATE = STORE && BV <= 32;
+    f32x4 s0c[LATE ? RTW : 1][LATE ? CTB : 1];
+    f32x4 dc[LATE ? CPW : 1];
+    if constexpr (LATE) {
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CTB; ++ct) s0c[rt][ct] = S[rt][ct];
+    } else if constexpr (STORE) {
       T* st = ws_B + ((size_t)cj * HV + hv) * WsB<T, K, V>::elems + WsB<T, K, V>::oS0;
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt)
@@ -1569,7 +1580,10 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
 #pragma unroll
         for (int e = 0; e < 4; ++e) D[cc][e] = R4::get(cur.u[cc], e) - ws_[cc][e];
     }
-    if constexpr (STORE) {  // backward support: keep Delta
+    if constexpr (LATE) {
+#pragma unroll
+      for (int cc = 0; cc < CPW; ++cc) dc[cc] = D[cc];
+    } else if constexpr (STORE) {  // backward support: keep Delta
       T* dl = ws_B + ((size_t)cj * HV + hv) * WsB<T, K, V>::elems + WsB<T, K, V>::oDL;
 #pragma unroll
       for (int cc = 0; cc < CPW; ++cc)
@@ -1620,6 +1634,20 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
       }
     }
 
+    if constexpr (LATE) {
+      T* st = ws_B + ((size_t)cj * HV + hv) * WsB<T, K, V>::elems + WsB<T, K, V>::oS0;
+      T* dl = ws_B + ((size_t)cj * HV + hv) * WsB<T, K, V>::elems + WsB<T, K, V>::oDL;
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CTB; ++ct)
+          store4<T>(st + il4(16 * (RTW * wave + rt) + 4 * g, col_base + 16 * ct + l16, V),
+                    s0c[rt][ct][0], s0c[rt][ct][1], s0c[rt][ct][2], s0c[rt][ct][3]);
+#pragma unroll
+      for (int cc = 0; cc < CPW; ++cc)
+        store4<T>(dl + il4(16 * tt + 4 * g, col_base + 16 * (ct0 + cc) + l16, V), dc[cc][0], dc[cc][1],
+                  dc[cc][2], dc[cc][3]);
+    }
     // (3) S = Diag(Gamma_last) S + Khat^T Delta for the wave's channel tiles
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
