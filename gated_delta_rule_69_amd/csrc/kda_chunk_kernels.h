@@ -1445,12 +1445,7 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     F sf[CACHE ? KS_K : 1][CACHE ? CPW : 1];  // S0 fragments (value tiles ct0..)
     F df[CACHE ? KS_C : 1][CACHE ? CPW : 1];  // Delta fragments (value tiles ct0..)
   };
-  auto output = [&](const OutOps& op, const int cj, const int buf) __attribute__((always_inline)) {
-    if constexpr (KEEP) return;  // the backward's recurrence forms no output
-    const int cidx = cj - cbeg;
-    const int64_t t0 = bos + (int64_t)cidx * kC;
-    const int L = min(kC, len - cidx * kC);
-    f32x4 OT[CPW];
+  auto output_mma = [&](const OutOps& op, const int buf, f32x4* OT) __attribute__((always_inline)) {
 #pragma unroll
     for (int cc = 0; cc < CPW; ++cc) OT[cc] = zero4();
 #pragma unroll
@@ -1470,6 +1465,11 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
         OT[cc] = M::mma(dfr, op.p[ks], OT[cc]);
         if constexpr (WsL::PL > 0) OT[cc] = M::mma(dfr, op.pl[ks], OT[cc]);
       }
+  };
+  auto store_out = [&](const f32x4* OT, const int cj) __attribute__((always_inline)) {
+    const int cidx = cj - cbeg;
+    const int64_t t0 = bos + (int64_t)cidx * kC;
+    const int L = min(kC, len - cidx * kC);
     const int i = 16 * tt + l16;
     if (i < L && o) {
       T* orow = o + ((t0 + i) * HV + hv) * V + col_base + 16 * ct0 + 4 * g;
@@ -1485,6 +1485,12 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
         }
       }
     }
+  };
+  auto output = [&](const OutOps& op, const int cj, const int buf) __attribute__((always_inline)) {
+    if constexpr (KEEP) return;  // the backward's recurrence forms no output
+    f32x4 OT[CPW];
+    output_mma(op, buf, OT);
+    store_out(OT, cj);
   };
   // one chunk of the recurrence with operands `cur`, LDS buffer `buf`; the
   // previous chunk's output (registers `prv`) is formed after the first
@@ -1554,7 +1560,16 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
       load_ops(cn, nxt, 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (cj > cbeg) output(prv, cj - 1, buf ^ 1);
+    // 32-column blocks: the deferred output's stores wait until after the
+    // second barrier, behind the step's loads (dense scan 120 -> 112 us; with 16
+    // and 64 columns measured slower and not used)
+    constexpr bool LATE_OUT = !KEEP && BV == 32;
+    f32x4 OTd[CPW];
+    if constexpr (LATE_OUT) {
+      if (cj > cbeg) output_mma(prv, buf ^ 1, OTd);
+    } else {
+      if (cj > cbeg) output(prv, cj - 1, buf ^ 1);
+    }
     if constexpr (SPLIT) {
       __builtin_amdgcn_sched_barrier(0);
       load_ops(cn, nxt, 2);
@@ -1613,6 +1628,9 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
     if constexpr (SPLIT) {
       load_ops(cn, nxt, 3);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (LATE_OUT) {
+      if (cj > cbeg) store_out(OTd, cj - 1);
     }
     F dall[KS_C][CTB];
 #pragma unroll
