@@ -50,7 +50,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_SOURCES = ("gated_delta_rule_69_amd/csrc/kda_common.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk_kernels.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk.hip")
-TRAFFIC_SHA16 = "23bb1d0c05a65900"
+TRAFFIC_SHA16 = "058641c2e87fe6ab"
 TRAFFIC_BYTES = 1085.7e6
 
 
