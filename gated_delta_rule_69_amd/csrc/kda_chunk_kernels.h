@@ -510,11 +510,19 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
       }
     }
   }
+  // Gate rows. When a thread's GU units make up one whole cumsum block
+  // (GU == kGateBlock, K = 128), thread (block rb, channel group cg) loads
+  // rows 8 rb .. 8 rb + 7 of channels 4 cg .. 4 cg + 3, and the in-block part
+  // of a fused gate's cumsum runs in its registers; otherwise unit u is row
+  // (tid + u * threads) / (K / 4) and the cumsum reads the rows back from LDS.
+  constexpr bool GREG = GU == kGateBlock;
+  auto grow = [&](int u) { return GREG ? kGateBlock * (tid / (K / 4)) + u : (tid + u * kThreads) / (K / 4); };
+  auto gc4 = [&](int u) { return GREG ? tid % (K / 4) : (tid + u * kThreads) % (K / 4); };
   float4 gr[GU];
   uint4 kr[KU], qr[KU], vr[VU];
 #pragma unroll
   for (int u = 0; u < GU; ++u) {
-    const int f = tid + u * kThreads, row = f / (K / 4), c4 = f % (K / 4);
+    const int row = grow(u), c4 = gc4(u);
     const int rr = row < L ? row : L - 1;  // pad rows repeat the last gate row
     gr[u] = *reinterpret_cast<const float4*>(gate + ((t0 + rr) * HV + hv) * K + 4 * c4);
   }
@@ -618,10 +626,26 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
       gr[u].w = gate_nat(gr[u].w, gate_mode, sc);
     }
   }
+  // fused gate with register blocks: in-block inclusive sums in registers
+  // (pad rows keep the last token's value), block totals to LDS
+  const bool greg_sum = GREG && gate_mode != kGateLog2;
+  if (greg_sum) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < GU; ++u) {
-    const int f = tid + u * kThreads, row = f / (K / 4), c4 = f % (K / 4);
-    *reinterpret_cast<float4*>(sG + row * GS + 4 * c4) = gr[u];
+    for (int u = 0; u < GU; ++u) {
+      float ge[4] = {gr[u].x, gr[u].y, gr[u].z, gr[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (grow(u) < L) acc[e] = acc[e] + ge[e];
+        ge[e] = acc[e];
+      }
+      gr[u] = make_float4(ge[0], ge[1], ge[2], ge[3]);
+    }
+    *reinterpret_cast<float4*>(sTot + (tid / (K / 4)) * K + 4 * gc4(0)) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < GU; ++u)
+      *reinterpret_cast<float4*>(sG + grow(u) * GS + 4 * gc4(u)) = gr[u];
   }
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
@@ -630,7 +654,24 @@ chunk_intra_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     *reinterpret_cast<uint4*>(sQ + row * KSTR + EPU * cu_) = qr[u];
   }
   __syncthreads();
-  if (gate_mode != kGateLog2) {
+  if (greg_sum) {
+    // block offsets C_b (totals of the earlier blocks, in order), then
+    // G2 = (C_b + in-block sum) * log2(e): the gate kernel's order
+    const int rb = tid / (K / 4), cg = gc4(0);
+    float c[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < rb; ++b) {
+      float t4[4];
+      lds4(sTot + b * K + 4 * cg, t4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = c[e] + t4[e];
+    }
+#pragma unroll
+    for (int u = 0; u < GU; ++u)
+      *reinterpret_cast<float4*>(sG + grow(u) * GS + 4 * cg) =
+          make_float4((c[0] + gr[u].x) * kLog2e, (c[1] + gr[u].y) * kLog2e, (c[2] + gr[u].z) * kLog2e,
+                      (c[3] + gr[u].w) * kLog2e);
+    __syncthreads();
+  } else if (gate_mode != kGateLog2) {
     // chunk-local inclusive cumsum times log2(e) in the blocked order of
     // kGateBlock (the gate kernel's order, so G2 is bit-identical to its
     // output). Thread (cg, rb) owns channels 4cg..4cg+3 of token block rb.
