@@ -71,7 +71,7 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--skip-extra", action="store_true", help="skip the context workloads")
-    p.add_argument("--profile", choices=["dense", "dense2", "dense_conv", "decode", "decode2", "long",
+    p.add_argument("--profile", choices=["dense", "dense2", "dense_conv", "decode", "decode2", "long", "long_fused",
                                          "gatebwd", "varlen", "tiny", "prefill", "copy"],
                    default=None,
                    help="run only one workload a few times (for rocprofv3), print no JSON")
@@ -148,6 +148,19 @@ def profile_only(a):
             # training step with saved states
             kda.chunk_kda(*t[:3], G, t[3], h0, output_final_state=True, save_for_backward=wsb)
             kda.chunk_kda_bwd(*t[:3], G, t[3], h0, dO, dht, saved=True, workspace=wsb)
+    elif a.profile == "long_fused":
+        # the same shapes with the gate step inside the backward's kernels: the
+        # recomputing backward, then the training pair, from the raw gate
+        w5 = workloads.workload5()
+        t = [T_(w5.q, bf), T_(w5.k, bf), T_(w5.v, bf), T_(w5.beta, bf)]
+        x, A, h0, dO, dht = T_(w5.x), T_(w5.A_log), T_(w5.h0), T_(w5.dO, bf), T_(w5.dht)
+        del w5
+        wsb = torch.empty(kda.chunk_bwd_workspace_bytes(t[0], t[2]), device=dev, dtype=torch.uint8)
+        fused = dict(use_gate_in_kernel=True, A_log=A)
+        for _ in range(a.profile_reps):
+            kda.chunk_kda_bwd(*t[:3], x, t[3], h0, dO, dht, **fused)
+            kda.chunk_kda(*t[:3], x, t[3], h0, output_final_state=True, save_for_backward=wsb, **fused)
+            kda.chunk_kda_bwd(*t[:3], x, t[3], h0, dO, dht, saved=True, workspace=wsb, **fused)
     elif a.profile == "varlen":
         # packed varlen + GVA: 32768 tokens in 16 sequences and 3 empty slots, HV = 32,
         # nonzero initial states, gate in the kernel
@@ -566,6 +579,26 @@ def main():
             kda.gate_bwd(t5["x"], r["dg"], t5["A"], dx=r["dg"], workspace=wsg)
         tr_fwd_ms = time_it(fwd5_train, 5, warm=2)
         tr_bwd_ms = time_it(bwd5_saved, 3, warm=1)
+        # the same two backward forms and the training pair with the gate step inside the
+        # kernels (kda_chunk_bwd_ex, kda_chunk_fwd_train_ex): no chunk-local log2 gate anywhere
+        fused = dict(use_gate_in_kernel=True, A_log=t5["A"])
+
+        def bwd5_fused():
+            r = kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], t5["x"], t5["b"], t5["h0"], t5["dO"],
+                                  t5["dht"], **fused)
+            kda.gate_bwd(t5["x"], r["dg"], t5["A"], dx=r["dg"], workspace=wsg)
+
+        def fwd5_train_fused():
+            kda.chunk_kda(t5["q"], t5["k"], t5["v"], t5["x"], t5["b"], t5["h0"], output_final_state=True,
+                          o=o5, save_for_backward=wsb, **fused)
+
+        def bwd5_saved_fused():
+            r = kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], t5["x"], t5["b"], t5["h0"], t5["dO"],
+                                  t5["dht"], saved=True, workspace=wsb, **fused)
+            kda.gate_bwd(t5["x"], r["dg"], t5["A"], dx=r["dg"], workspace=wsg)
+        bwdf_ms = time_it(bwd5_fused, 3, warm=1)
+        trf_fwd_ms = time_it(fwd5_train_fused, 5, warm=2)
+        trf_bwd_ms = time_it(bwd5_saved_fused, 3, warm=1)
         del wsb
         # gate backward alone, with a bias: x, dg in, dx out (FP32), dA_log and d_dt_bias
         gen = torch.Generator(device=dev).manual_seed(5)
@@ -584,6 +617,14 @@ def main():
             "train_saved_tokens_per_s": round(65536 / ((tr_fwd_ms + tr_bwd_ms) * 1e-3), 1),
             "train_saved_note": "fwd = kda_gate_cumsum + kda_chunk_fwd_train (states saved); "
                                 "bwd = kda_chunk_bwd_saved + kda_gate_bwd",
+            "fused_gate": {
+                "bwd_ms": round(bwdf_ms, 3),
+                "train_saved_fwd_ms": round(trf_fwd_ms, 3), "train_saved_bwd_ms": round(trf_bwd_ms, 3),
+                "train_saved_tokens_per_s": round(65536 / ((trf_fwd_ms + trf_bwd_ms) * 1e-3), 1),
+                "note": "gate step inside the kernels, from the raw gate x: bwd = kda_chunk_bwd_ex "
+                        "(recomputing) + kda_gate_bwd; training pair = kda_chunk_fwd_train_ex, then "
+                        "kda_chunk_bwd_ex (saved) + kda_gate_bwd; results bit-identical to the "
+                        "kda_gate_cumsum forms"},
             "fwd_cold_ms": cold_fwd5, "bwd_cold_ms": cold_bwd5,
             "gate_bwd_ms": round(gb_ms, 4), "gate_bwd_GBps": round(gb_bytes / (gb_ms * 1e-3) / 1e9, 1),
             "gate_bwd_hbm_frac": round(gb_bytes / (gb_ms * 1e-3) / 8e12, 4)}

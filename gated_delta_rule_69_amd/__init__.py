@@ -38,7 +38,8 @@ EXPORTED = ("kda_status_string", "kda_gate_cumsum", "kda_gate_cumsum_biased",
             "kda_chunk_bwd", "kda_recurrent_fwd", "kda_recurrent_fwd_fused_gate",
             "kda_chunk_fwd_ex", "kda_recurrent_fwd_ex", "kda_chunk_fwd_conv", "kda_short_conv_fwd",
             "kda_recurrent_fwd_conv_workspace_bytes", "kda_recurrent_fwd_conv",
-            "kda_recurrent_fwd_conv_noalloc", "kda_chunk_fwd_train", "kda_chunk_bwd_saved")
+            "kda_recurrent_fwd_conv_noalloc", "kda_chunk_fwd_train", "kda_chunk_bwd_saved",
+            "kda_chunk_fwd_train_ex", "kda_chunk_bwd_ex")
 # bytes of the library's static device scratch behind kda_recurrent_fwd_conv_noalloc
 NOALLOC_SCRATCH_BYTES = 16 << 20
 KDA_GATE_LOG2, KDA_GATE_NAT, KDA_GATE_RAW = 0, 1, 2
@@ -98,6 +99,12 @@ def _lib():
         lib.kda_chunk_bwd_saved.restype = ctypes.c_int
         lib.kda_chunk_fwd_train.argtypes = lib.kda_chunk_fwd.argtypes
         lib.kda_chunk_fwd_train.restype = ctypes.c_int
+        lib.kda_chunk_fwd_train_ex.argtypes = [dims, ctypes.c_int, p, p, p, p, i32, p, p, p, p, i32,
+                                               i32, p, p, p, sz, p]
+        lib.kda_chunk_fwd_train_ex.restype = ctypes.c_int
+        lib.kda_chunk_bwd_ex.argtypes = ([dims, ctypes.c_int] + [p] * 4 + [i32, p] + [p] * 3 + [i32]
+                                         + [p] * 8 + [i32, p, sz, p])
+        lib.kda_chunk_bwd_ex.restype = ctypes.c_int
         lib.kda_recurrent_fwd.argtypes = [dims, ctypes.c_int, p, p, p, p, p, p, p, i32, p, p, p]
         lib.kda_recurrent_fwd.restype = ctypes.c_int
         lib.kda_recurrent_fwd_fused_gate.argtypes = [dims, ctypes.c_int, p, p, p, p, i32, p, p, p, p,
@@ -350,9 +357,10 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
     + SiLU to them in the kernel (kda_chunk_fwd_conv): FP32 taps [H*K, W] /
     [HV*V, W] (a [D, 1, W] Conv1d weight is accepted too), biases or None.
     save_for_backward: a device buffer of at least chunk_bwd_workspace_bytes()
-    bytes (plain log2 gate only): the forward runs as kda_chunk_fwd_train and
-    leaves the chunk start states and Deltas there for chunk_kda_bwd(...,
-    saved=True, workspace=that buffer), which then skips the recurrence.
+    bytes: the forward runs as kda_chunk_fwd_train (kda_chunk_fwd_train_ex
+    with use_gate_in_kernel=True) and leaves the chunk start states and Deltas
+    there for chunk_kda_bwd(..., saved=True, workspace=that buffer, and the
+    same gate arguments), which then skips the recurrence.
     Returns (o, final_state)."""
     _validate_scan(q, k, v, gate, beta, initial_state, cu_seqlens, o=o, final_state=final_state,
                    A_log=A_log)
@@ -375,10 +383,18 @@ def chunk_kda(q, k, v, gate, beta, initial_state=None, *, cu_seqlens=None,
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
     kind = (KDA_GATE_RAW if gate_is_raw else KDA_GATE_NAT) if use_gate_in_kernel else KDA_GATE_LOG2
     if save_for_backward is not None:
-        if use_gate_in_kernel or qk_l2norm or short_conv is not None:
-            raise ValueError("save_for_backward takes the chunk-local log2 gate (gate_cumsum), "
-                             "without in-kernel gate, normalisation or convolution")
+        if qk_l2norm or short_conv is not None:
+            raise ValueError("save_for_backward runs without in-kernel normalisation or convolution")
         _check(save_for_backward, "save_for_backward")
+        if use_gate_in_kernel:
+            rc = _lib().kda_chunk_fwd_train_ex(
+                ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), kind, _ptr(A_log),
+                _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size),
+                int(bool(output_final_state)), _ptr(o), _ptr(final_state), _ptr(save_for_backward),
+                _nbytes(save_for_backward), _stream())
+            if rc:
+                raise KdaError("kda_chunk_fwd_train_ex", rc)
+            return o, final_state
         rc = _lib().kda_chunk_fwd_train(
             ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
             _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), int(bool(output_final_state)),
@@ -456,17 +472,23 @@ def chunk_bwd_workspace_bytes(q: torch.Tensor, v: torch.Tensor, cu_seqlens=None,
 
 def chunk_kda_bwd(q, k, v, gate, beta, initial_state, do, dht=None, *, cu_seqlens=None,
                   chunk_size: int = 64, workspace: Optional[torch.Tensor] = None,
-                  saved: bool = False):
+                  saved: bool = False, use_gate_in_kernel: bool = False,
+                  A_log: Optional[torch.Tensor] = None, gate_is_raw: bool = True):
     """Steps B1..B3 (kda_chunk_bwd). Returns a dict with dq, dk (shape of q),
     dv (shape of v), dg (FP32, w.r.t. the per-token natural-log gate), dbeta
     and dh0 (FP32 [N, HV, K, V]). saved=True (kda_chunk_bwd_saved): `workspace`
     is the buffer a chunk_kda(..., save_for_backward=workspace) call on the
-    same inputs filled, and the recurrence is not run again."""
-    _validate_scan(q, k, v, gate, beta, initial_state, cu_seqlens, do=do, dht=dht)
+    same inputs filled, and the recurrence is not run again. With
+    use_gate_in_kernel=True (kda_chunk_bwd_ex), `gate` is gate_cumsum's input
+    (raw x with optional A_log, or the natural-log g if gate_is_raw=False), as
+    in chunk_kda, and the gate step runs inside the backward's kernels."""
+    _validate_scan(q, k, v, gate, beta, initial_state, cu_seqlens, do=do, dht=dht, A_log=A_log)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (beta, "beta"), (do, "do"),
                  (initial_state, "initial_state"), (dht, "dht"), (cu_seqlens, "cu_seqlens"),
-                 (workspace, "workspace")):
+                 (workspace, "workspace"), (A_log, "A_log")):
         _check(t, n)
+    if A_log is not None and not (use_gate_in_kernel and gate_is_raw):
+        raise ValueError("A_log needs use_gate_in_kernel=True with a raw gate")
     d = _dims(q, v, cu_seqlens)
     dt = _dtype_code(q)
     # the kernels write every row inside a sequence: dense inputs need no fill;
@@ -482,6 +504,16 @@ def chunk_kda_bwd(q, k, v, gate, beta, initial_state, do, dht=None, *, cu_seqlen
             raise ValueError("saved=True needs the workspace the training forward filled")
     elif workspace is None or _nbytes(workspace) < need:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    if use_gate_in_kernel:
+        kind = KDA_GATE_RAW if gate_is_raw else KDA_GATE_NAT
+        rc = _lib().kda_chunk_bwd_ex(
+            ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), kind, _ptr(A_log),
+            _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), _ptr(do),
+            _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0),
+            int(bool(saved)), _ptr(workspace), _nbytes(workspace), _stream())
+        if rc:
+            raise KdaError("kda_chunk_bwd_ex", rc)
+        return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=dh0)
     fn = _lib().kda_chunk_bwd_saved if saved else _lib().kda_chunk_bwd
     rc = fn(ctypes.byref(d), dt, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
             _ptr(initial_state), _ptr(cu_seqlens), int(chunk_size), _ptr(do),

@@ -329,7 +329,8 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_dims* d, kda_dtype dt, int32_t ch
 namespace {
 
 kda_status chunk_bwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
-                          const void* v, const float* gate, const void* beta, const float* h0,
+                          const void* v, const float* gate, int gate_kind, const float* A_log,
+                          const void* beta, const float* h0,
                           const int32_t* cu, int32_t chunk_size, const void* do_,
                           const float* dht, void* dq, void* dk, void* dv, float* dg, void* dbeta,
                           float* dh0, void* workspace, size_t workspace_bytes, int saved,
@@ -337,6 +338,8 @@ kda_status chunk_bwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const 
   kda_status st = check_dims(d, cu);
   if (st != KDA_OK) return st;
   if (!valid_dtype(dt)) return KDA_ERR_DTYPE;
+  if (gate_kind < KDA_GATE_LOG2 || gate_kind > KDA_GATE_RAW) return KDA_ERR_SHAPE;
+  if (gate_kind != KDA_GATE_RAW && A_log) return KDA_ERR_SHAPE;
   const bool has_tokens = (size_t)d->B * d->T > 0;
   if (has_tokens && (!q || !k || !v || !gate || !beta || !do_ || !dq || !dk || !dv || !dg || !dbeta))
     return KDA_ERR_NULL;
@@ -345,12 +348,14 @@ kda_status chunk_bwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const 
   if (!((d->K == 64 || d->K == 128) && (d->V == 64 || d->V == 128))) return KDA_ERR_UNSUPPORTED;
   if (dt == KDA_FP32 && d->K != 64) return KDA_ERR_UNSUPPORTED;  // FP32 staging exceeds LDS
   const Sizes s = sizes(d, dt);
-  const void* ins[] = {q, k, v, gate, beta, h0, do_, dht};
-  const size_t ins_n[] = {s.qk, s.qk, s.v, s.gate, s.beta, s.state, s.v, s.state};
+  const void* ins[] = {q, k, v, gate, beta, h0, do_, dht, A_log};
+  const size_t ins_n[] = {s.qk, s.qk, s.v, s.gate, s.beta, s.state, s.v, s.state,
+                          A_log ? (size_t)d->HV * sizeof(float) : 0};
+  constexpr int NIN = 9;
   const void* outs[] = {dq, dk, dv, dg, dbeta, dh0};
   const size_t outs_n[] = {s.qk, s.qk, s.v, s.gate, s.beta, s.state};
   for (int i = 0; i < 6; ++i) {
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < NIN; ++j)
       if (overlaps(outs[i], outs_n[i], ins[j], ins_n[j])) return KDA_ERR_ALIAS;
     for (int j = i + 1; j < 6; ++j)
       if (overlaps(outs[i], outs_n[i], outs[j], outs_n[j])) return KDA_ERR_ALIAS;
@@ -363,10 +368,11 @@ kda_status chunk_bwd_impl(const kda_dims* d, kda_dtype dt, const void* q, const 
   if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
   for (int i = 0; i < 6; ++i)
     if (overlaps(workspace, need, outs[i], outs_n[i])) return KDA_ERR_ALIAS;
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < NIN; ++j)
     if (overlaps(workspace, need, ins[j], ins_n[j])) return KDA_ERR_ALIAS;
-  return kda_host::launch_chunk_bwd(*d, dt, q, k, v, gate, beta, h0, cu, do_, dht, dq, dk, dv, dg,
-                                    dbeta, dh0, workspace, saved, stream) == hipSuccess
+  return kda_host::launch_chunk_bwd(*d, dt, q, k, v, gate, gate_kind, A_log, beta, h0, cu, do_,
+                                    dht, dq, dk, dv, dg, dbeta, dh0, workspace, saved,
+                                    stream) == hipSuccess
              ? KDA_OK
              : KDA_ERR_LAUNCH;
 }
@@ -380,8 +386,8 @@ kda_status kda_chunk_bwd(const kda_dims* d, kda_dtype dt, const void* q, const v
                          const int32_t* cu, int32_t chunk_size, const void* do_,
                          const float* dht, void* dq, void* dk, void* dv, float* dg, void* dbeta,
                          float* dh0, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return chunk_bwd_impl(d, dt, q, k, v, gate, beta, h0, cu, chunk_size, do_, dht, dq, dk, dv, dg,
-                        dbeta, dh0, workspace, workspace_bytes, 0, stream);
+  return chunk_bwd_impl(d, dt, q, k, v, gate, KDA_GATE_LOG2, nullptr, beta, h0, cu, chunk_size, do_,
+                        dht, dq, dk, dv, dg, dbeta, dh0, workspace, workspace_bytes, 0, stream);
 }
 
 kda_status kda_chunk_fwd_train(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
@@ -400,8 +406,33 @@ kda_status kda_chunk_bwd_saved(const kda_dims* d, kda_dtype dt, const void* q, c
                                const void* do_, const float* dht, void* dq, void* dk, void* dv,
                                float* dg, void* dbeta, float* dh0, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
-  return chunk_bwd_impl(d, dt, q, k, v, gate, beta, h0, cu, chunk_size, do_, dht, dq, dk, dv, dg,
-                        dbeta, dh0, workspace, workspace_bytes, 1, stream);
+  return chunk_bwd_impl(d, dt, q, k, v, gate, KDA_GATE_LOG2, nullptr, beta, h0, cu, chunk_size, do_,
+                        dht, dq, dk, dv, dg, dbeta, dh0, workspace, workspace_bytes, 1, stream);
+}
+
+kda_status kda_chunk_fwd_train_ex(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                                  const void* v, const float* gate, int32_t gate_kind,
+                                  const float* A_log, const void* beta, const float* h0,
+                                  const int32_t* cu, int32_t chunk_size, int32_t write_final,
+                                  void* o, float* ht, void* bwd_workspace,
+                                  size_t bwd_workspace_bytes, hipStream_t stream) {
+  if (gate_kind < KDA_GATE_LOG2 || gate_kind > KDA_GATE_RAW) return KDA_ERR_SHAPE;
+  if (gate_kind != KDA_GATE_RAW && A_log) return KDA_ERR_SHAPE;
+  return chunk_fwd_impl(d, dt, q, k, v, gate, (int)gate_kind, A_log, 0, nullptr, beta, h0, cu,
+                        chunk_size, write_final, o, ht, bwd_workspace, bwd_workspace_bytes, stream,
+                        1);
+}
+
+kda_status kda_chunk_bwd_ex(const kda_dims* d, kda_dtype dt, const void* q, const void* k,
+                            const void* v, const float* gate, int32_t gate_kind, const float* A_log,
+                            const void* beta, const float* h0, const int32_t* cu,
+                            int32_t chunk_size, const void* do_, const float* dht, void* dq,
+                            void* dk, void* dv, float* dg, void* dbeta, float* dh0,
+                            int32_t saved, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return chunk_bwd_impl(d, dt, q, k, v, gate, (int)gate_kind, A_log, beta, h0, cu, chunk_size, do_,
+                        dht, dq, dk, dv, dg, dbeta, dh0, workspace, workspace_bytes, saved ? 1 : 0,
+                        stream);
 }
 
 kda_status kda_recurrent_fwd(const kda_dims* d, kda_dtype dt, const void* q, const void* k,

@@ -84,8 +84,8 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
   float* ws_save_f =
       save ? reinterpret_cast<float*>(p + align256((size_t)mc * d.HV * WsB<T, K, V>::elems * sizeof(T)))
            : nullptr;
-  // the training forward takes the precomputed gate and no pre-processing
-  if (save && (gate_mode != kGateLog2 || qn || conv)) return hipErrorInvalidValue;
+  // the training forward takes no pre-processing (its backward has none)
+  if (save && (qn || conv)) return hipErrorInvalidValue;
   if (varlen) {
     hipError_t e = launch_chunk_table(cu, d.N, ws_int, (int)mc, s);
     if (e != hipSuccess) return e;

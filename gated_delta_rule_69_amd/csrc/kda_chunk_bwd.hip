@@ -423,7 +423,8 @@ constexpr int kBwdThreads = 512;
 template <typename T, int K, int V>
 __global__ void __launch_bounds__(kBwdThreads, 1)
 chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                       const float* __restrict__ gate, const T* __restrict__ beta,
+                       const float* __restrict__ gate, int gate_mode, const float* __restrict__ A_log,
+                       const T* __restrict__ beta,
                        const T* __restrict__ dO, const int32_t* __restrict__ cu,
                        const int* __restrict__ ws_int, const T* __restrict__ ws_B,
                        const float* __restrict__ ws_Bf, int N, int T_, int H, int HV, float scale,
@@ -562,17 +563,25 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
   Blk pf;
 
   // ---- stage G2, k, q, T and the first phase-1 block (all loads of a thread
-  // issued before its stores); zero the small arrays
+  // issued before its stores); zero the small arrays.
+  // Gate rows: thread (group gg, channel group gcg) holds rows NG gg .. NG gg +
+  // NG - 1 of channels 4 gcg .. 4 gcg + 3, i.e. segment gg % GSEG of cumsum
+  // block gg / GSEG; the lanes of one block's segments sit NCG apart in a wave.
+  constexpr int NG = kC * K / 4 / NT, NCG = K / 4, GSEG = kGateBlock / NG;
+  static_assert(NG * GSEG == kGateBlock && (NT / NCG) * NG == kC && GSEG * NCG <= 64, "gate rows");
+  const int gg = tid / NCG, gcg = tid % NCG;
+  const bool gfused = gate_mode != kGateLog2;
+  float4 gx[NG];
   {
-    constexpr int NG = kC * K / 4 / NT, NKQ = kC * K / EPU / NT, NTm = kC * kC / 4 / NT;
+    constexpr int NKQ = kC * K / EPU / NT, NTm = kC * kC / 4 / NT;
     static_assert(NG * NT == kC * K / 4 && NKQ * NT == kC * K / EPU && NTm * NT == kC * kC / 4, "stage");
-    float4 gx[NG], tx[NTm];
+    float4 tx[NTm];
     uint4 kx[NKQ], qx[NKQ];
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
-      const int f = tid + i * NT, row = f / (K / 4), c4 = f % (K / 4);
+      const int row = NG * gg + i;
       const int rr = row < L ? row : L - 1;
-      gx[i] = ldg_nt(reinterpret_cast<const float4*>(gate + ((t0 + rr) * HV + hv) * K + 4 * c4));
+      gx[i] = ldg_nt(reinterpret_cast<const float4*>(gate + ((t0 + rr) * HV + hv) * K + 4 * gcg));
     }
 #pragma unroll
     for (int i = 0; i < NKQ; ++i) {
@@ -591,10 +600,49 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     const int brow = tid % kC < L ? tid % kC : L - 1;
     const T braw = beta[(t0 + brow) * HV + hv];
     load_blk(0, pf);
+    if (gfused) {
+      // fused gate step: the per-token natural-log gate, then the in-block part
+      // of the chunk-local cumsum in the kernel's blocked order (segments of a
+      // block take turns, each continuing from the previous one's last sum;
+      // pad rows keep the last token's value); block totals to the small arrays
+      const float sc = gate_head_scale(gate_mode, A_log, hv);
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int f = tid + i * NT, row = f / (K / 4), c4 = f % (K / 4);
-      *reinterpret_cast<float4*>(sG + row * GS + 4 * c4) = gx[i];
+      for (int i = 0; i < NG; ++i) {
+        gx[i].x = gate_nat(gx[i].x, gate_mode, sc);
+        gx[i].y = gate_nat(gx[i].y, gate_mode, sc);
+        gx[i].z = gate_nat(gx[i].z, gate_mode, sc);
+        gx[i].w = gate_nat(gx[i].w, gate_mode, sc);
+      }
+      const int seg = gg % GSEG;
+      float st[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < GSEG; ++r) {
+        if (seg == r) {
+#pragma unroll
+          for (int i = 0; i < NG; ++i) {
+            float ge[4] = {gx[i].x, gx[i].y, gx[i].z, gx[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (NG * gg + i < L) st[e] = st[e] + ge[e];
+              ge[e] = st[e];
+            }
+            gx[i] = make_float4(ge[0], ge[1], ge[2], ge[3]);
+          }
+        }
+        if (r + 1 < GSEG) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float nx = __shfl_up(st[e], NCG);
+            if (seg == r + 1) st[e] = nx;
+          }
+        }
+      }
+      if (seg == GSEG - 1)
+        *reinterpret_cast<float4*>(sColP + (gg / GSEG) * K + 4 * gcg) = make_float4(st[0], st[1], st[2], st[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+        *reinterpret_cast<float4*>(sG + (NG * gg + i) * GS + 4 * gcg) = gx[i];
     }
 #pragma unroll
     for (int i = 0; i < NKQ; ++i) {
@@ -614,6 +662,26 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     if (tid < kC) sG[tid * GS + K] = tid < L ? to_f32(braw) : 0.f;
     store_blk(pf);
     if (V / VB > 1) load_blk(1, pf);
+  }
+  if (gfused) {
+    // G2 = (C_b + in-block sum) * log2(e), C_b the totals of the earlier
+    // blocks in order: the gate kernel's order, so G2 is bit-identical to its
+    // output. The totals sat in the small arrays, cleared after this.
+    static_assert(kC / kGateBlock * K <= 4 * K + K + 6 * kC, "block totals");
+    __syncthreads();
+    float c[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < gg / GSEG; ++b) {
+      float t4[4];
+      lds4(sColP + b * K + 4 * gcg, t4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = c[e] + t4[e];
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+      *reinterpret_cast<float4*>(sG + (NG * gg + i) * GS + 4 * gcg) =
+          make_float4((c[0] + gx[i].x) * kLog2e, (c[1] + gx[i].y) * kLog2e, (c[2] + gx[i].z) * kLog2e,
+                      (c[3] + gx[i].w) * kLog2e);
+    __syncthreads();
   }
   for (int f = tid; f < 4 * K + K + 6 * kC; f += NT) sColP[f] = 0.f;
   // outputs of this chunk: uniform base pointers, 32-bit element offsets per lane
@@ -1213,7 +1281,8 @@ size_t bwd_ws_bytes_t(const kda_dims& d, bool varlen) {
 
 template <typename T, int K, int V>
 hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const void* v,
-                       const float* gate, const void* beta, const float* h0, const int32_t* cu,
+                       const float* gate, int gate_mode, const float* A_log, const void* beta,
+                       const float* h0, const int32_t* cu,
                        const void* dO, const float* dht, void* dq, void* dk, void* dv, float* dg,
                        void* dbeta, float* dh0, void* ws, int saved, hipStream_t s) {
   const bool varlen = cu != nullptr;
@@ -1251,7 +1320,7 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
       const size_t lds_intra = IntraLds<T, K, V>::total;
       hipLaunchKernelGGL((chunk_intra_kernel<T, K, V, true, false, false>), dim3((unsigned)(mc * d.HV)),
                          dim3(kThreads), lds_intra, s, (const T*)q, (const T*)k,
-                         (const T*)v, gate, (int)kGateLog2, (const float*)nullptr, (const T*)beta,
+                         (const T*)v, gate, gate_mode, A_log, (const T*)beta,
                          cu, ws_int, d.N, d.T, d.H, d.HV, scale,
                          ws_T, ws_GL, ws_B, ws_Bf, kda_short_conv{}, 1);
     }
@@ -1289,7 +1358,8 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
     const size_t lds_local = BwdLds<T, K, V>::total;
     hipLaunchKernelGGL((chunk_bwd_local_kernel<T, K, V>), dim3((unsigned)(mc * d.HV)),
                        dim3(kBwdThreads), lds_local, s, (const T*)q, (const T*)k,
-                       (const T*)v, gate, (const T*)beta, (const T*)dO, cu, (const int*)ws_int,
+                       (const T*)v, gate, gate_mode, A_log, (const T*)beta, (const T*)dO, cu,
+                       (const int*)ws_int,
                        (const T*)ws_B, (const float*)ws_Bf, d.N, d.T, d.H, d.HV, scale, (T*)dq,
                        (T*)dk, dq_part, dk_part, (T*)dv, dg, (T*)dbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1325,13 +1395,14 @@ size_t chunk_bwd_workspace_bytes(const kda_dims& d, kda_dtype dt, int chunk) {
 
 template <typename T>
 static hipError_t bwd_t(const kda_dims& d, const void* q, const void* k, const void* v,
-                        const float* gate, const void* beta, const float* h0, const int32_t* cu,
+                        const float* gate, int gate_mode, const float* A_log, const void* beta,
+                        const float* h0, const int32_t* cu,
                         const void* dO, const float* dht, void* dq, void* dk, void* dv, float* dg,
                         void* dbeta, float* dh0, void* ws, int saved, hipStream_t s) {
 #define KDA_BWD_CASE(KK, VV)                                                                    \
   if (d.K == KK && d.V == VV)                                                                   \
-    return kda::chunk_bwd_t<T, KK, VV>(d, q, k, v, gate, beta, h0, cu, dO, dht, dq, dk, dv, dg, \
-                                       dbeta, dh0, ws, saved, s);
+    return kda::chunk_bwd_t<T, KK, VV>(d, q, k, v, gate, gate_mode, A_log, beta, h0, cu, dO, dht, \
+                                       dq, dk, dv, dg, dbeta, dh0, ws, saved, s);
   KDA_BWD_CASE(64, 64)
   KDA_BWD_CASE(64, 128)
   KDA_BWD_CASE(128, 64)
@@ -1341,13 +1412,16 @@ static hipError_t bwd_t(const kda_dims& d, const void* q, const void* k, const v
 }
 
 hipError_t launch_chunk_bwd(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
-                            const void* v, const float* gate, const void* beta, const float* h0,
+                            const void* v, const float* gate, int gate_mode, const float* A_log,
+                            const void* beta, const float* h0,
                             const int32_t* cu, const void* dO, const float* dht, void* dq,
                             void* dk, void* dv, float* dg, void* dbeta, float* dh0, void* ws,
                             int saved, hipStream_t s) {
   if (dt == KDA_BF16)
-    return bwd_t<kda::bf16>(d, q, k, v, gate, beta, h0, cu, dO, dht, dq, dk, dv, dg, dbeta, dh0, ws, saved, s);
-  return bwd_t<float>(d, q, k, v, gate, beta, h0, cu, dO, dht, dq, dk, dv, dg, dbeta, dh0, ws, saved, s);
+    return bwd_t<kda::bf16>(d, q, k, v, gate, gate_mode, A_log, beta, h0, cu, dO, dht, dq, dk, dv,
+                            dg, dbeta, dh0, ws, saved, s);
+  return bwd_t<float>(d, q, k, v, gate, gate_mode, A_log, beta, h0, cu, dO, dht, dq, dk, dv, dg,
+                      dbeta, dh0, ws, saved, s);
 }
 
 }  // namespace kda_host

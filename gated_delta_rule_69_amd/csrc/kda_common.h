@@ -198,7 +198,8 @@ hipError_t launch_chunk_fwd(const kda_dims& d, kda_dtype dt, const void* q, cons
                             float* ht, void* ws, size_t ws_bytes, int save, hipStream_t s);
 size_t chunk_bwd_workspace_bytes(const kda_dims& d, kda_dtype dt, int chunk);
 hipError_t launch_chunk_bwd(const kda_dims& d, kda_dtype dt, const void* q, const void* k,
-                            const void* v, const float* gate, const void* beta, const float* h0,
+                            const void* v, const float* gate, int gate_mode, const float* A_log,
+                            const void* beta, const float* h0,
                             const int32_t* cu, const void* dO, const float* dht, void* dq,
                             void* dk, void* dv, float* dg, void* dbeta, float* dh0, void* ws,
                             int saved, hipStream_t s);

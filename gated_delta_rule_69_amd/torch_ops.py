@@ -3,10 +3,12 @@ only; every step runs in libkda's kernels).
 
   torch.ops.kda.chunk_kda_train(q, k, v, x, beta, A_log, dt_bias,
                                 initial_state, cu_seqlens) -> (o, final_state)
-      The chunked forward from the raw gate input x (kda_gate_cumsum_biased,
-      then kda_chunk_fwd), differentiable in q, k, v, x, beta, A_log, dt_bias
-      and initial_state: the backward recomputes the chunk-local log2 gate
-      and runs kda_chunk_bwd, then kda_gate_bwd on its dg.
+      The chunked forward from the raw gate input x, differentiable in q, k,
+      v, x, beta, A_log, dt_bias and initial_state. Without dt_bias the gate
+      step runs inside the kernels (kda_chunk_fwd_fused_gate forward,
+      kda_chunk_bwd_ex backward); with it, kda_gate_cumsum_biased forms the
+      chunk-local log2 gate for kda_chunk_fwd and kda_chunk_bwd. Then
+      kda_gate_bwd on the backward's dg.
   torch.ops.kda.recurrent_kda(q, k, v, x, beta, A_log, initial_state,
                               cu_seqlens) -> (o, final_state)
       Token-sequential forward with the gate activated in the scan kernel
@@ -49,6 +51,10 @@ def chunk_kda_train(q: Tensor, k: Tensor, v: Tensor, x: Tensor, beta: Tensor,
                     A_log: Optional[Tensor], dt_bias: Optional[Tensor],
                     initial_state: Optional[Tensor],
                     cu_seqlens: Optional[Tensor]) -> Tuple[Tensor, Tensor]:
+    if dt_bias is None:  # gate step inside the chunk kernel (bit-identical to the two calls)
+        return chunk_kda(q, k, v, x, beta, initial_state, cu_seqlens=cu_seqlens,
+                         output_final_state=True, chunk_size=_CHUNK, use_gate_in_kernel=True,
+                         A_log=A_log)
     G = gate_cumsum(x, A_log, cu_seqlens, _CHUNK, dt_bias=dt_bias)
     o, ht = chunk_kda(q, k, v, G, beta, initial_state, cu_seqlens=cu_seqlens,
                       output_final_state=True, chunk_size=_CHUNK)
@@ -68,9 +74,13 @@ def _chunk_setup(ctx, inputs, output):
 
 def _chunk_backward(ctx, do, dht):
     q, k, v, x, beta, A_log, dt_bias, h0, cu = ctx.saved_tensors
-    G = gate_cumsum(x, A_log, cu, _CHUNK, dt_bias=dt_bias)
-    r = chunk_kda_bwd(q, k, v, G, beta, h0, do.contiguous(), dht.contiguous(), cu_seqlens=cu,
-                      chunk_size=_CHUNK)
+    if dt_bias is None:  # gate step inside the backward's kernels (kda_chunk_bwd_ex)
+        r = chunk_kda_bwd(q, k, v, x, beta, h0, do.contiguous(), dht.contiguous(), cu_seqlens=cu,
+                          chunk_size=_CHUNK, use_gate_in_kernel=True, A_log=A_log)
+    else:
+        G = gate_cumsum(x, A_log, cu, _CHUNK, dt_bias=dt_bias)
+        r = chunk_kda_bwd(q, k, v, G, beta, h0, do.contiguous(), dht.contiguous(), cu_seqlens=cu,
+                          chunk_size=_CHUNK)
     dx, dA, db = gate_bwd(x, r["dg"], A_log, dt_bias, cu, dx=r["dg"])
     return (r["dq"], r["dk"], r["dv"], dx, r["dbeta"], dA, db,
             r["dh0"] if h0 is not None else None, None)

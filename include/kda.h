@@ -425,6 +425,43 @@ kda_status kda_chunk_bwd_saved(const kda_dims* dims, kda_dtype dtype, const void
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd_train_ex, kda_chunk_bwd_ex -- the training forward and the
+ * backward with the gate kind as an argument, as kda_chunk_fwd_ex takes it:
+ * with KDA_GATE_RAW (g = -exp(A_log[hv]) softplus(x), A_log NULL = unit
+ * scale) or KDA_GATE_NAT the gate step (the fused-gate chunk KDA path,
+ * `use_gate_in_kernel`, of "[Fix] Use unit KDA gate scale when A_log is
+ * omitted", Summary) runs inside the kernels that read the gate, so a
+ * training step never materialises the chunk-local log2 gate. The kernels use
+ * the gate kernel's float operations and summation order: every result is
+ * bit-identical to kda_gate_cumsum(chunk_size) followed by the KDA_GATE_LOG2
+ * call.
+ *   kda_chunk_fwd_train_ex  as kda_chunk_fwd_train, gate in `gate_kind`.
+ *   kda_chunk_bwd_ex        as kda_chunk_bwd (saved == 0) or
+ *          kda_chunk_bwd_saved (saved != 0: `workspace` filled by
+ *          kda_chunk_fwd_train(_ex) on the same inputs and gate kind). dg is
+ *          the gradient w.r.t. the per-token natural-log gate g in every kind
+ *          (kda_gate_bwd takes it back to the raw input).
+ *   gate_kind outside kda_gate_kind, or A_log with a kind other than
+ *   KDA_GATE_RAW: KDA_ERR_SHAPE; A_log [HV] FP32 overlapping an output or
+ *   the workspace: KDA_ERR_ALIAS. Everything else as the KDA_GATE_LOG2 entry
+ *   points (with KDA_GATE_LOG2 they are those calls).
+ */
+kda_status kda_chunk_fwd_train_ex(const kda_dims* dims, kda_dtype dtype, const void* q,
+                                  const void* k, const void* v, const float* gate,
+                                  int32_t gate_kind, const float* A_log, const void* beta,
+                                  const float* initial_state, const int32_t* cu_seqlens,
+                                  int32_t chunk_size, int32_t output_final_state, void* o,
+                                  float* final_state, void* bwd_workspace,
+                                  size_t bwd_workspace_bytes, hipStream_t stream);
+kda_status kda_chunk_bwd_ex(const kda_dims* dims, kda_dtype dtype, const void* q, const void* k,
+                            const void* v, const float* gate, int32_t gate_kind,
+                            const float* A_log, const void* beta, const float* initial_state,
+                            const int32_t* cu_seqlens, int32_t chunk_size, const void* do_,
+                            const float* dht, void* dq, void* dk, void* dv, float* dg,
+                            void* dbeta, float* dh0, int32_t saved, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
  * kda_recurrent_fwd -- step A7: the token-sequential scan (recurrent_kda).
  *   gate   [B, T, HV, K] FP32 per-token log2 decay (kda_gate_cumsum with
  *          chunk_size == 1).

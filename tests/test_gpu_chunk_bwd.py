@@ -162,3 +162,57 @@ def test_training_forward_then_saved_backward_bitwise(dtype, K, V, B, H, HV, cu)
         assert torch.equal(bits(a), bits(b)), name
     ref = _ref(wl)
     _check(wl, {n_: to_np(t) for n_, t in r2.items()}, ref)
+
+
+@pytest.mark.parametrize("dtype,K,V,B,H,HV,cu,kind", [
+    ("bf16", 128, 128, 4, 16, 16, None, "raw"),         # 32-column scans, A_log
+    ("bf16", 128, 128, 1, 2, 4, [0, 0, 70, 200, 200, 265], "raw"),  # varlen + GVA, empty slots
+    ("fp32", 64, 128, 2, 1, 2, None, "raw_unit"),        # raw gate without A_log (unit scale)
+    ("bf16", 64, 64, 1, 1, 1, [0, 130], "nat"),          # natural-log gate input
+])
+def test_fused_gate_training_pair_and_backward_bitwise(dtype, K, V, B, H, HV, cu, kind):
+    """kda_chunk_fwd_train_ex and kda_chunk_bwd_ex with the gate step inside
+    the kernels (raw x with or without A_log, or the natural-log g) give bit
+    for bit what kda_gate_cumsum followed by the log2-gate calls gives: the
+    recomputing backward, the training forward's o and final state, and the
+    saved backward (its workspace filled with NaN bytes first)."""
+    T = 200 if cu is None else cu[-1] + 7
+    wl = workloads.tiny_case(530 + K + V + HV, B=B, T=T, H=H, HV=HV, K=K, V=V, dtype=dtype,
+                             cu_seqlens=cu, grads=True, A_log=1.0)
+    d = device_inputs(wl)
+    dt = tdtype(wl)
+    dO = to_dev(np.nan_to_num(wl.dO), dt)
+    dht = to_dev(wl.dht)
+    if kind == "nat":  # the per-token natural-log gate as the kernels' input
+        gin, A, raw = to_dev(oracle.gate_activation(wl.x, wl.A_log)), None, False
+    else:
+        gin, A, raw = d["x"], (d["A_log"] if kind == "raw" else None), True
+    G = kda.gate_cumsum(gin, A, d["cu"], 64, is_raw=raw)
+    o1, h1 = kda.chunk_kda(d["q"], d["k"], d["v"], G, d["beta"], d["h0"], cu_seqlens=d["cu"],
+                           output_final_state=True)
+    r1 = kda.chunk_kda_bwd(d["q"], d["k"], d["v"], G, d["beta"], d["h0"], dO, dht, cu_seqlens=d["cu"])
+    fused = dict(use_gate_in_kernel=True, A_log=A, gate_is_raw=raw)
+    r2 = kda.chunk_kda_bwd(d["q"], d["k"], d["v"], gin, d["beta"], d["h0"], dO, dht,
+                           cu_seqlens=d["cu"], **fused)
+    ws = torch.full((kda.chunk_bwd_workspace_bytes(d["q"], d["v"], d["cu"]),), 0xFF, device=DEV,
+                    dtype=torch.uint8)
+    o3, h3 = kda.chunk_kda(d["q"], d["k"], d["v"], gin, d["beta"], d["h0"], cu_seqlens=d["cu"],
+                           output_final_state=True, save_for_backward=ws, **fused)
+    r3 = kda.chunk_kda_bwd(d["q"], d["k"], d["v"], gin, d["beta"], d["h0"], dO, dht,
+                           cu_seqlens=d["cu"], saved=True, workspace=ws, **fused)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    n = wl.T if cu is None else cu[-1]
+    assert torch.equal(bits(o1[:, :n]), bits(o3[:, :n]))
+    assert torch.equal(bits(h1), bits(h3))
+    mask = torch.from_numpy(in_contract_rows(wl)).to(DEV)
+    for r in (r2, r3):
+        for name in NAMES:
+            a, b = r1[name], r[name]
+            if name != "dh0":
+                a, b = a[mask], b[mask]
+            assert torch.equal(bits(a), bits(b)), name
+    if kind != "nat":
+        if kind == "raw_unit":
+            wl.A_log = np.zeros_like(wl.A_log)
+        _check(wl, {n_: to_np(t) for n_, t in r3.items()}, _ref(wl))

@@ -77,6 +77,42 @@ def test_chunk_kda_train_forward_equals_entry_points_bitwise():
     assert torch.equal(ht.view(torch.int32), ht2.view(torch.int32))
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_chunk_kda_train_without_bias_runs_fused_gate_bitwise(dtype):
+    """Without dt_bias the op runs the gate step inside the kernels (fused-gate
+    forward, kda_chunk_bwd_ex backward); with a zero dt_bias it forms the log2
+    gate with kda_gate_cumsum_biased first (x + 0 = x). Outputs and every
+    gradient agree bit for bit."""
+    wl, _ = _case(dtype)
+    d = device_inputs(wl)
+    zero_b = torch.zeros((wl.HV, wl.K), device=DEV, dtype=torch.float32)
+    n = int(wl.cu_seqlens[-1])
+    W_o = np.nan_to_num(wl.dO.astype(np.float64))
+    W_o[:, n:] = 0.0
+    res = []
+    for bias in (None, zero_b):
+        leaves = dict(q=d["q"].clone(), k=d["k"].clone(), v=d["v"].clone(), x=d["x"].clone(),
+                      beta=d["beta"].clone(), A_log=d["A_log"].clone(), h0=d["h0"].clone())
+        for t in leaves.values():
+            t.requires_grad_(True)
+        o, ht = torch.ops.kda.chunk_kda_train(leaves["q"], leaves["k"], leaves["v"], leaves["x"],
+                                              leaves["beta"], leaves["A_log"], bias, leaves["h0"],
+                                              d["cu"])
+        loss = (o[:, :n].float() * to_dev(W_o[:, :n])).sum() + (ht * to_dev(wl.dht)).sum()
+        grads = torch.autograd.grad(loss, list(leaves.values()))
+        res.append((o.detach(), ht.detach(), grads))
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    (o1, h1, g1), (o2, h2, g2) = res
+    assert torch.equal(bits(o1[:, :n]), bits(o2[:, :n]))
+    assert torch.equal(bits(h1), bits(h2))
+    mask = torch.from_numpy(in_contract_rows(wl)).to(DEV)
+    for name, a, c in zip(("q", "k", "v", "x", "beta", "A_log", "h0"), g1, g2):
+        if name not in ("A_log", "h0"):
+            a, c = a[mask], c[mask]
+        assert torch.equal(bits(a), bits(c)), name
+
+
 def test_opcheck_registrations():
     wl, b = _case("fp32")
     d = device_inputs(wl)
