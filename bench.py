@@ -50,7 +50,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_SOURCES = ("gated_delta_rule_69_amd/csrc/kda_common.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk_kernels.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk.hip")
-TRAFFIC_SHA16 = "37614ac4195cdc3d"
+TRAFFIC_SHA16 = "cd2c9c266519aced"
 TRAFFIC_BYTES = 1085.5e6
 
 
