@@ -364,3 +364,28 @@ def test_prefill_and_step_ops_fake_shapes_on_meta_tensors():
     o = torch.ops.kda.recurrent_kda_step(q, q, v, x, beta, None, st, hist, cu, True,
                                          wq, wq, wv, None, None, None)
     assert o.shape == v.shape
+
+
+def test_gate_kind_entry_points_reject_bad_arguments():
+    """kda_chunk_bwd_ex / kda_chunk_fwd_train_ex: a gate kind outside
+    kda_gate_kind or an A_log with a kind other than KDA_GATE_RAW is
+    KDA_ERR_SHAPE; an A_log overlapping an output is KDA_ERR_ALIAS."""
+    lib = kda.load()
+    d = _dims()
+
+    def bwd(kind, A_log, dq=None):
+        return lib.kda_chunk_bwd_ex(ctypes.byref(d), 1, FAKE[0], FAKE[1], FAKE[2], FAKE[3], kind, A_log,
+                                    FAKE[4], None, None, 64, FAKE[5], None,
+                                    dq if dq is not None else FAKE[6], FAKE[7], FAKE[8], FAKE[9],
+                                    FAKE[10], FAKE[11], 0, FAKE[12], 1 << 40, None)
+
+    def train(kind, A_log):
+        return lib.kda_chunk_fwd_train_ex(ctypes.byref(d), 1, FAKE[0], FAKE[1], FAKE[2], FAKE[3], kind,
+                                          A_log, FAKE[4], None, None, 64, 1, FAKE[5], FAKE[6],
+                                          FAKE[7], 1 << 40, None)
+
+    assert bwd(3, None) == 2 and bwd(-1, None) == 2
+    assert bwd(kda.KDA_GATE_LOG2, FAKE[13]) == 2 and bwd(kda.KDA_GATE_NAT, FAKE[13]) == 2
+    assert bwd(kda.KDA_GATE_RAW, FAKE[13], dq=FAKE[13]) == 5  # A_log inside dq
+    assert train(3, None) == 2
+    assert train(kda.KDA_GATE_NAT, FAKE[13]) == 2
