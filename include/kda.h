@@ -111,6 +111,11 @@ const char* kda_status_string(kda_status s);
 
 /*
  * kda_gate_cumsum -- step A1: gate activation and chunk-local cumsum.
+ * Pages: "[Fix] Use unit KDA gate scale when A_log is omitted", Summary and
+ * Breaking changes (decay scale exp(A_log), an omitted A_log is the unit
+ * scale); "kda in torchtitan (training)", quoted attention-gym description
+ * (the gate as a per-token log2 decay, chunk-local cumulative for the chunked
+ * op, produced by the gate cumsum with chunk_size 1 or the chunk size).
  *   gate_in  [B, T, HV, K] FP32. If gate_in_is_raw != 0 it holds the raw
  *            activation input x and the per-token natural-log decay is
  *            g = -exp(A_log[hv]) * softplus(x), softplus(x) = ln(1 + e^x)
@@ -186,6 +191,11 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_dims* dims, kda_dtype dtype, int3
 
 /*
  * kda_chunk_fwd -- steps A2..A6: the chunked scan (chunk_kda forward).
+ * Pages: "[Fix] Use unit KDA gate scale when A_log is omitted", squashed
+ * commit bodies (the chunked pipeline kkt, solve_tril, recompute_w_u, fwd_h,
+ * fwd_o of the sibling gated delta rule op, here with a per-channel gate);
+ * "kda in torchtitan (training)", quoted attention-gym description (the
+ * chunk_kda argument contract and packed-sequence layout).
  *   gate   [B, T, HV, K] FP32 chunk-local cumulative log2 gate, i.e. the
  *          output of kda_gate_cumsum with the same chunk_size and cu_seqlens.
  *   initial_state [N, HV, K, V] FP32 or NULL (zeros).
@@ -358,6 +368,12 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_dims* dims, kda_dtype dtype, int3
 
 /*
  * kda_chunk_bwd -- steps B1..B3: gradients of kda_chunk_fwd.
+ * Pages: "[KDA] Add Paddle training compatibility", Summary (dense and
+ * variable-length chunk_kda forward/backward with gate, beta, state and GVA
+ * gradients); "[Fix] Use unit KDA gate scale when A_log is omitted",
+ * squashed commit bodies (the sibling op's backward kernels: bwd_dhu for the
+ * reverse state-gradient recurrence, chunk_bwd_dqkwg and chunk_bwd_dv_local
+ * for the local gradients, prepare_wy_repr_bwd for the UT transform's).
  *   Forward arguments as kda_chunk_fwd (gate = chunk-local log2 cumsum).
  *   do_    [B, T, HV, V] in `dtype`: gradient of o.
  *   dht    [N, HV, K, V] FP32 gradient of the final state, or NULL (zero).
@@ -463,6 +479,9 @@ kda_status kda_chunk_bwd_ex(const kda_dims* dims, kda_dtype dtype, const void* q
 
 /*
  * kda_recurrent_fwd -- step A7: the token-sequential scan (recurrent_kda).
+ * Page: "kda in torchtitan (training)", quoted attention-gym description of
+ * recurrent_kda (signature and packed contract of chunk_kda, per-token log2
+ * gate, 1/sqrt(K) query scale, FP32 state and compute).
  *   gate   [B, T, HV, K] FP32 per-token log2 decay (kda_gate_cumsum with
  *          chunk_size == 1).
  *   Other arguments as kda_chunk_fwd. Computes in FP32 for any input dtype.
