@@ -33,14 +33,21 @@ chunk_table_kernel(const int32_t* __restrict__ cu, int N, int* __restrict__ ws_i
     }
     const int incl = s_scan[threadIdx.x];
     const int excl = incl - cnt;
-    if (n < N) {
-      seq_off[n] = carry + excl;
-      for (int c = 0; c < cnt; ++c) {
-        const int j = carry + excl + c;
-        if (j < max_chunks) chunk_seq[j] = n;
+    if (n < N) seq_off[n] = carry + excl;
+    // chunks of this group of sequences, all threads together: chunk carry + j
+    // belongs to the first sequence whose inclusive count exceeds j (binary
+    // search over the counts in LDS)
+    const int group = s_scan[1023];
+    for (int j = threadIdx.x; j < group; j += 1024) {
+      int lo = 0, hi = 1023;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_scan[mid] > j) hi = mid;
+        else lo = mid + 1;
       }
+      if (carry + j < max_chunks) chunk_seq[carry + j] = base + lo;
     }
-    carry += s_scan[1023];
+    carry += group;
     __syncthreads();
   }
   if (threadIdx.x == 0) {
