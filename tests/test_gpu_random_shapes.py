@@ -1,4 +1,4 @@
-"""Randomized shapes: 150 seeded small cases over dtype (bf16, FP32), K and V
+"""Randomized shapes. Chunked path: 150 seeded small cases over dtype (bf16, FP32), K and V
 in {64, 128}, grouped value heads, dense batches and packed varlen batches
 (empty, single-token, chunk-boundary and ragged sequences, a capacity tail),
 gate strength, the log2-gate and fused-gate entry points, and the
@@ -8,7 +8,8 @@ the FP64 oracle: forward output and final state, and all six gradients.
 Tolerances: bf16 5e-3 rel-RMS (outputs), 1e-2 (states, gradients); FP32 2e-5
 normwise, widened to ln2 * ulp(max |G2|) where the chunk-local log2 gate is
 large (the FP32 representation bound of the two-call contract), and 4x that
-for gradients. The cases are drawn from a fixed seed."""
+for gradients. Token-sequential path: 200 cases with any K, V up to 256.
+The cases are drawn from fixed seeds."""
 import numpy as np
 import pytest
 import torch
@@ -105,4 +106,53 @@ def test_random_shapes_forward_and_backward():
         print("   " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()), flush=True)
         if over:
             failures.append((label, over))
+    assert not failures, failures
+
+
+def test_random_shapes_recurrent():
+    """200 seeded cases of the token-sequential path: any K, V up to 256 (not
+    only powers of two), grouped value heads, dense and packed batches with
+    empty and short sequences, both gate entry points."""
+    rng = np.random.default_rng(21)
+    failures = []
+    for case in range(200):
+        dtype = "bf16" if rng.random() < 0.5 else "fp32"
+        K = int(rng.integers(1, 257)) if rng.random() < 0.5 else int(rng.choice([16, 32, 64, 128, 256]))
+        V = int(rng.integers(1, 257)) if rng.random() < 0.5 else int(rng.choice([16, 32, 64, 128, 256]))
+        H = int(rng.choice([1, 2]))
+        HV = H * int(rng.choice([1, 2, 4]))
+        if rng.random() < 0.6:
+            N = int(rng.integers(1, 7))
+            lens = [int(rng.choice([0, 1, 2, 5]) if rng.random() < 0.6 else rng.integers(0, 90))
+                    for _ in range(N)]
+            cu = [0] + [int(c) for c in np.cumsum(lens)]
+            B, T = 1, max(cu[-1] + int(rng.integers(0, 5)), 1)
+        else:
+            cu = None
+            B, T = int(rng.integers(1, 4)), int(rng.choice([1, 2, 7, 40]))
+        A = float(rng.choice([0.0, 1.0, 2.7]))
+        fused = bool(rng.random() < 0.5)
+        s = int(rng.integers(1, 1 << 30))
+        label = f"case {case}: {dtype} K{K} V{V} H{H} HV{HV} B{B} T{T} cu={cu} A_log={A} fused={fused}"
+        print(label, flush=True)
+        wl = workloads.tiny_case(s, B=B, T=T, H=H, HV=HV, K=K, V=V, dtype=dtype, cu_seqlens=cu, A_log=A)
+        d = device_inputs(wl)
+        if fused:
+            o, ht = kda.recurrent_kda(d["q"], d["k"], d["v"], d["x"], d["beta"], d["h0"],
+                                      cu_seqlens=d["cu"], output_final_state=True,
+                                      use_gate_in_kernel=True, A_log=d["A_log"])
+        else:
+            G1 = kda.gate_cumsum(d["x"], d["A_log"], d["cu"], 1)
+            o, ht = kda.recurrent_kda(d["q"], d["k"], d["v"], G1, d["beta"], d["h0"],
+                                      cu_seqlens=d["cu"], output_final_state=True)
+        torch.cuda.synchronize()
+        o_ref, ht_ref = oracle.forward(wl)
+        mask = in_contract_rows(wl)
+        err = normwise_max_err if dtype == "fp32" else rel_rms
+        eo = err(to_np(o)[mask], o_ref[mask]) if mask.any() else 0.0
+        eh = err(to_np(ht), ht_ref)
+        ok = eo <= (2e-5 if dtype == "fp32" else 5e-3) and eh <= (2e-5 if dtype == "fp32" else 1e-2)
+        print(f"   o {eo:.1e} state {eh:.1e}", flush=True)
+        if not ok:
+            failures.append((label, eo, eh))
     assert not failures, failures
