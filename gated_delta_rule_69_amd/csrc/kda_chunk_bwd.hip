@@ -420,7 +420,10 @@ __device__ __forceinline__ void pin(f32x4& x) { asm volatile("" : "+v"(x)); }
 // the C x C products), so every SIMD holds two waves of the workgroup.
 constexpr int kBwdThreads = 512;
 
-template <typename T, int K, int V>
+// GF: the gate arrives raw or natural-log (gate_mode) and its step runs in the
+// prologue; otherwise it is the chunk-local log2 cumsum. Two instantiations, so
+// that the log2-gate kernel carries nothing of the gate step.
+template <typename T, int K, int V, bool GF = false>
 __global__ void __launch_bounds__(kBwdThreads, 1)
 chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                        const float* __restrict__ gate, int gate_mode, const float* __restrict__ A_log,
@@ -564,13 +567,16 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
 
   // ---- stage G2, k, q, T and the first phase-1 block (all loads of a thread
   // issued before its stores); zero the small arrays.
-  // Gate rows: thread (group gg, channel group gcg) holds rows NG gg .. NG gg +
-  // NG - 1 of channels 4 gcg .. 4 gcg + 3, i.e. segment gg % GSEG of cumsum
-  // block gg / GSEG; the lanes of one block's segments sit NCG apart in a wave.
+  // Gate rows. With the gate step (GF), thread (group gg, channel group gcg)
+  // holds rows NG gg .. NG gg + NG - 1 of channels 4 gcg .. 4 gcg + 3, i.e.
+  // segment gg % GSEG of cumsum block gg / GSEG (the lanes of one block's
+  // segments sit NCG apart in a wave); otherwise unit i of a thread is row
+  // (tid + i NT) / NCG.
   constexpr int NG = kC * K / 4 / NT, NCG = K / 4, GSEG = kGateBlock / NG;
   static_assert(NG * GSEG == kGateBlock && (NT / NCG) * NG == kC && GSEG * NCG <= 64, "gate rows");
   const int gg = tid / NCG, gcg = tid % NCG;
-  const bool gfused = gate_mode != kGateLog2;
+  auto grow = [&](int i) { return GF ? NG * gg + i : (tid + i * NT) / NCG; };
+  auto gcol = [&](int i) { return GF ? gcg : (tid + i * NT) % NCG; };
   float4 gx[NG];
   {
     constexpr int NKQ = kC * K / EPU / NT, NTm = kC * kC / 4 / NT;
@@ -579,9 +585,9 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     uint4 kx[NKQ], qx[NKQ];
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
-      const int row = NG * gg + i;
+      const int row = grow(i);
       const int rr = row < L ? row : L - 1;
-      gx[i] = ldg_nt(reinterpret_cast<const float4*>(gate + ((t0 + rr) * HV + hv) * K + 4 * gcg));
+      gx[i] = ldg_nt(reinterpret_cast<const float4*>(gate + ((t0 + rr) * HV + hv) * K + 4 * gcol(i)));
     }
 #pragma unroll
     for (int i = 0; i < NKQ; ++i) {
@@ -600,7 +606,7 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     const int brow = tid % kC < L ? tid % kC : L - 1;
     const T braw = beta[(t0 + brow) * HV + hv];
     load_blk(0, pf);
-    if (gfused) {
+    if constexpr (GF) {
       // fused gate step: the per-token natural-log gate, then the in-block part
       // of the chunk-local cumsum in the kernel's blocked order (segments of a
       // block take turns, each continuing from the previous one's last sum;
@@ -642,7 +648,7 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     } else {
 #pragma unroll
       for (int i = 0; i < NG; ++i)
-        *reinterpret_cast<float4*>(sG + (NG * gg + i) * GS + 4 * gcg) = gx[i];
+        *reinterpret_cast<float4*>(sG + grow(i) * GS + 4 * gcol(i)) = gx[i];
     }
 #pragma unroll
     for (int i = 0; i < NKQ; ++i) {
@@ -663,7 +669,7 @@ chunk_bwd_local_kernel(const T* __restrict__ q, const T* __restrict__ k, const T
     store_blk(pf);
     if (V / VB > 1) load_blk(1, pf);
   }
-  if (gfused) {
+  if constexpr (GF) {
     // G2 = (C_b + in-block sum) * log2(e), C_b the totals of the earlier
     // blocks in order: the gate kernel's order, so G2 is bit-identical to its
     // output. The totals sat in the small arrays, cleared after this.
@@ -1352,17 +1358,23 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
   // LDS (a workgroup asking for the full 160 KiB of the CU does not launch)
   static_assert(!(sizeof(T) == 2 || K == 64) || BwdLds<T, K, V>::total <= 158 * 1024, "LDS budget");
   if (mc > 0) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_bwd_local_kernel<T, K, V>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)BwdLds<T, K, V>::total);
+    auto launch_local = [&](auto gfc) -> hipError_t {
+      constexpr bool GF = decltype(gfc)::value;
+      hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_bwd_local_kernel<T, K, V, GF>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          (int)BwdLds<T, K, V>::total);
+      if (e2 != hipSuccess) return e2;
+      const size_t lds_local = BwdLds<T, K, V>::total;
+      hipLaunchKernelGGL((chunk_bwd_local_kernel<T, K, V, GF>), dim3((unsigned)(mc * d.HV)),
+                         dim3(kBwdThreads), lds_local, s, (const T*)q, (const T*)k,
+                         (const T*)v, gate, gate_mode, A_log, (const T*)beta, (const T*)dO, cu,
+                         (const int*)ws_int,
+                         (const T*)ws_B, (const float*)ws_Bf, d.N, d.T, d.H, d.HV, scale, (T*)dq,
+                         (T*)dk, dq_part, dk_part, (T*)dv, dg, (T*)dbeta);
+      return hipGetLastError();
+    };
+    e = gate_mode != kGateLog2 ? launch_local(std::true_type()) : launch_local(std::false_type());
     if (e != hipSuccess) return e;
-    const size_t lds_local = BwdLds<T, K, V>::total;
-    hipLaunchKernelGGL((chunk_bwd_local_kernel<T, K, V>), dim3((unsigned)(mc * d.HV)),
-                       dim3(kBwdThreads), lds_local, s, (const T*)q, (const T*)k,
-                       (const T*)v, gate, gate_mode, A_log, (const T*)beta, (const T*)dO, cu,
-                       (const int*)ws_int,
-                       (const T*)ws_B, (const float*)ws_Bf, d.N, d.T, d.H, d.HV, scale, (T*)dq,
-                       (T*)dk, dq_part, dk_part, (T*)dv, dg, (T*)dbeta);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t n_tok = (int64_t)d.B * d.T;
   if (d.HV != d.H && n_tok > 0) {  // no tokens: nothing to reduce (and no empty grid)
