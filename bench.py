@@ -555,53 +555,56 @@ def main():
 
         wsg = torch.empty(max(1, kda.gate_bwd_workspace_bytes(t5["x"])), device=dev, dtype=torch.uint8)
 
+        # the backward recomputing the forward's recurrence, from the raw gate: the gate step
+        # runs inside its kernels (kda_chunk_bwd_ex); the gate backward turns its dg into dx
+        # and dA_log (in place over dg)
+        fused = dict(use_gate_in_kernel=True, A_log=t5["A"])
+
         def bwd5():
-            # the backward takes the chunk-local log2 gate (kda_gate_cumsum) as input; the gate
-            # backward turns its dg into dx and dA_log (in place over dg)
-            kda.gate_cumsum(t5["x"], t5["A"], None, 64, out=G5)
-            r = kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], G5, t5["b"], t5["h0"], t5["dO"], t5["dht"])
+            r = kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], t5["x"], t5["b"], t5["h0"], t5["dO"],
+                                  t5["dht"], **fused)
             kda.gate_bwd(t5["x"], r["dg"], t5["A"], dx=r["dg"], workspace=wsg)
         fwd_ms = time_it(fwd5, 5, warm=2)
         bwd_ms = time_it(bwd5, 3, warm=1)
         cold_fwd5 = cold(fwd5, reps=min(a.cold_reps, 100), warm=10)
         cold_bwd5 = cold(bwd5, reps=min(a.cold_reps, 30), warm=3)
-        # training step with the states saved by the forward: gate cumsum, kda_chunk_fwd_train
-        # (outputs + chunk start states and Deltas in the backward's workspace), then
-        # kda_chunk_bwd_saved (no second recurrence) and the gate backward
+        # training pair: kda_chunk_fwd_train_ex (outputs + chunk start states and Deltas in the
+        # backward's workspace), then kda_chunk_bwd_ex on them (no second recurrence) and the
+        # gate backward
         wsb = torch.empty(kda.chunk_bwd_workspace_bytes(t5["q"], t5["v"]), device=dev,
                           dtype=torch.uint8)
 
         def fwd5_train():
+            kda.chunk_kda(t5["q"], t5["k"], t5["v"], t5["x"], t5["b"], t5["h0"], output_final_state=True,
+                          o=o5, save_for_backward=wsb, **fused)
+
+        def bwd5_saved():
+            r = kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], t5["x"], t5["b"], t5["h0"], t5["dO"],
+                                  t5["dht"], saved=True, workspace=wsb, **fused)
+            kda.gate_bwd(t5["x"], r["dg"], t5["A"], dx=r["dg"], workspace=wsg)
+        tr_fwd_ms = time_it(fwd5_train, 5, warm=2)
+        tr_bwd_ms = time_it(bwd5_saved, 3, warm=1)
+        # the same two backward forms with the gate step as its own kernel: kda_gate_cumsum
+        # writes the chunk-local log2 gate, which kda_chunk_bwd / kda_chunk_fwd_train take
+        # (results bit-identical to the forms above)
+
+        def bwd5_2c():
+            kda.gate_cumsum(t5["x"], t5["A"], None, 64, out=G5)
+            r = kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], G5, t5["b"], t5["h0"], t5["dO"], t5["dht"])
+            kda.gate_bwd(t5["x"], r["dg"], t5["A"], dx=r["dg"], workspace=wsg)
+
+        def fwd5_train_2c():
             kda.gate_cumsum(t5["x"], t5["A"], None, 64, out=G5)
             kda.chunk_kda(t5["q"], t5["k"], t5["v"], G5, t5["b"], t5["h0"], output_final_state=True,
                           o=o5, save_for_backward=wsb)
 
-        def bwd5_saved():
+        def bwd5_saved_2c():
             r = kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], G5, t5["b"], t5["h0"], t5["dO"],
                                   t5["dht"], saved=True, workspace=wsb)
             kda.gate_bwd(t5["x"], r["dg"], t5["A"], dx=r["dg"], workspace=wsg)
-        tr_fwd_ms = time_it(fwd5_train, 5, warm=2)
-        tr_bwd_ms = time_it(bwd5_saved, 3, warm=1)
-        # the same two backward forms and the training pair with the gate step inside the
-        # kernels (kda_chunk_bwd_ex, kda_chunk_fwd_train_ex): no chunk-local log2 gate anywhere
-        fused = dict(use_gate_in_kernel=True, A_log=t5["A"])
-
-        def bwd5_fused():
-            r = kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], t5["x"], t5["b"], t5["h0"], t5["dO"],
-                                  t5["dht"], **fused)
-            kda.gate_bwd(t5["x"], r["dg"], t5["A"], dx=r["dg"], workspace=wsg)
-
-        def fwd5_train_fused():
-            kda.chunk_kda(t5["q"], t5["k"], t5["v"], t5["x"], t5["b"], t5["h0"], output_final_state=True,
-                          o=o5, save_for_backward=wsb, **fused)
-
-        def bwd5_saved_fused():
-            r = kda.chunk_kda_bwd(t5["q"], t5["k"], t5["v"], t5["x"], t5["b"], t5["h0"], t5["dO"],
-                                  t5["dht"], saved=True, workspace=wsb, **fused)
-            kda.gate_bwd(t5["x"], r["dg"], t5["A"], dx=r["dg"], workspace=wsg)
-        bwdf_ms = time_it(bwd5_fused, 3, warm=1)
-        trf_fwd_ms = time_it(fwd5_train_fused, 5, warm=2)
-        trf_bwd_ms = time_it(bwd5_saved_fused, 3, warm=1)
+        bwd2_ms = time_it(bwd5_2c, 3, warm=1)
+        tr2_fwd_ms = time_it(fwd5_train_2c, 5, warm=2)
+        tr2_bwd_ms = time_it(bwd5_saved_2c, 3, warm=1)
         del wsb
         # gate backward alone, with a bias: x, dg in, dx out (FP32), dA_log and d_dt_bias
         gen = torch.Generator(device=dev).manual_seed(5)
@@ -614,20 +617,21 @@ def main():
         extra["long_context_T65536_H32_train"] = {
             "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
             "fwd_bwd_tokens_per_s": round(65536 / ((fwd_ms + bwd_ms) * 1e-3), 1),
-            "note": "fwd = kda_chunk_fwd_fused_gate; bwd = kda_gate_cumsum + kda_chunk_bwd + "
-                    "kda_gate_bwd (dx, dA_log), recomputing the forward recurrence",
+            "note": "from the raw gate x (unit scale), the gate step inside the kernels: fwd = "
+                    "kda_chunk_fwd_fused_gate; bwd = kda_chunk_bwd_ex (recomputing the forward's "
+                    "recurrence) + kda_gate_bwd (dx, dA_log)",
             "train_saved_fwd_ms": round(tr_fwd_ms, 3), "train_saved_bwd_ms": round(tr_bwd_ms, 3),
             "train_saved_tokens_per_s": round(65536 / ((tr_fwd_ms + tr_bwd_ms) * 1e-3), 1),
-            "train_saved_note": "fwd = kda_gate_cumsum + kda_chunk_fwd_train (states saved); "
-                                "bwd = kda_chunk_bwd_saved + kda_gate_bwd",
-            "fused_gate": {
-                "bwd_ms": round(bwdf_ms, 3),
-                "train_saved_fwd_ms": round(trf_fwd_ms, 3), "train_saved_bwd_ms": round(trf_bwd_ms, 3),
-                "train_saved_tokens_per_s": round(65536 / ((trf_fwd_ms + trf_bwd_ms) * 1e-3), 1),
-                "note": "gate step inside the kernels, from the raw gate x: bwd = kda_chunk_bwd_ex "
-                        "(recomputing) + kda_gate_bwd; training pair = kda_chunk_fwd_train_ex, then "
-                        "kda_chunk_bwd_ex (saved) + kda_gate_bwd; results bit-identical to the "
-                        "kda_gate_cumsum forms"},
+            "train_saved_note": "fwd = kda_chunk_fwd_train_ex (states saved); bwd = kda_chunk_bwd_ex "
+                                "(saved) + kda_gate_bwd",
+            "two_call_gate": {
+                "bwd_ms": round(bwd2_ms, 3),
+                "train_saved_fwd_ms": round(tr2_fwd_ms, 3), "train_saved_bwd_ms": round(tr2_bwd_ms, 3),
+                "train_saved_tokens_per_s": round(65536 / ((tr2_fwd_ms + tr2_bwd_ms) * 1e-3), 1),
+                "note": "the gate step as its own kernel (kda_gate_cumsum, chunk-local log2 gate): "
+                        "bwd = kda_gate_cumsum + kda_chunk_bwd + kda_gate_bwd; training pair = "
+                        "kda_gate_cumsum + kda_chunk_fwd_train, then kda_chunk_bwd_saved + "
+                        "kda_gate_bwd; results bit-identical to the forms above"},
             "fwd_cold_ms": cold_fwd5, "bwd_cold_ms": cold_bwd5,
             "gate_bwd_ms": round(gb_ms, 4), "gate_bwd_GBps": round(gb_bytes / (gb_ms * 1e-3) / 1e9, 1),
             "gate_bwd_hbm_frac": round(gb_bytes / (gb_ms * 1e-3) / 8e12, 4)}
