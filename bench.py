@@ -251,8 +251,8 @@ def main():
         profile_only(a)
         return
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the KDA scan has no "
-              "multi-GPU path in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}): the library runs each "
+              "call on one GPU and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
