@@ -80,25 +80,24 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 constexpr float kLn2 = 0.6931471805599453f;
 
 // softplus(x) = ln(1 + e^x) = max(x, 0) + ln(1 + z), z = e^{-|x|} in (0, 1],
-// on the transcendental unit. ln(1 + z) is computed as ln(u) * z / (u - 1)
-// with u = 1 + z (u - 1 is exact), the log1p method of D. Goldberg, "What
-// every computer scientist should know about floating-point arithmetic"
-// (ACM Computing Surveys, 1991), Theorem 4, which keeps full relative accuracy
-// for small z; the quotient (a factor within an ulp of 1) takes the hardware
-// reciprocal. Above 20 the result is x itself.
-// Branch-free (selects), so loads around it can stay batched. No FMA
-// contraction, so every kernel that inlines it rounds the same way.
+// on the transcendental unit. With u = 1 + z rounded, c = z - (u - 1) is the
+// exact rounding error of that sum (Dekker's Fast2Sum, since 1 >= z), so
+// 1 + z = u + c exactly and ln(1 + z) = ln(u) + ln(1 + c / u); as |c| <= 2^-24,
+// the second term is c to within |c| (u - 1) / u, a relative 2^-24 of the
+// result. This keeps full relative accuracy for small z (where u rounds to 1,
+// the result is z itself) with one logarithm and no division. Above 20 the
+// result is x itself (z is below half an ulp of x). Branch-free, so loads
+// around it can stay batched. No FMA contraction, so every kernel that inlines
+// it rounds the same way.
 __device__ __forceinline__ float softplus_f32(float x) {
 #pragma clang fp contract(off)
   const float z = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
   const float u = 1.f + z;
-  const float corr = __builtin_amdgcn_logf(u) * kLn2 * (z * __builtin_amdgcn_rcpf(u - 1.f));
-  const float l = (u == 1.f) ? z : corr;
-  const float r = fmaxf(x, 0.f) + l;
-  return x > 20.f ? x : r;
+  const float l = __builtin_amdgcn_logf(u) * kLn2 + (z - (u - 1.f));
+  return fmaxf(x, 0.f) + l;
 }
 
-// d softplus_f32 / dx = 1 / (1 + e^-x), exactly 1 above softplus_f32's threshold
+// d softplus_f32 / dx = 1 / (1 + e^-x), exactly 1 above 20 (where softplus_f32 is x)
 __device__ __forceinline__ float sigmoid_f32(float x) {
 #pragma clang fp contract(off)
   const float z = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
