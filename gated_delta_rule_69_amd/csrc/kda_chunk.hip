@@ -145,11 +145,11 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
     constexpr int BVC = decltype(bvc)::value;
     if (ws_save)
       hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, false, 4, true>),
-                         dim3((unsigned)chains, V / BVC), dim3(kThreads), 0, s, (const T*)ws_T,
+                         dim3(scan_grid(chains, V, BVC)), dim3(kThreads), 0, s, (const T*)ws_T,
                          (const float*)ws_GL, (const int*)ws_int, cu, h0, d.N, d.T, d.HV,
                          write_final, (T*)o, ht, ws_save);
     else
-      hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, false, 4>), dim3((unsigned)chains, V / BVC),
+      hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, false, 4>), dim3(scan_grid(chains, V, BVC)),
                          dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL,
                          (const int*)ws_int, cu, h0, d.N, d.T, d.HV, write_final, (T*)o, ht,
                          (T*)nullptr);

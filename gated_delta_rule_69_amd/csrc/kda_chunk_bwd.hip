@@ -57,7 +57,12 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
   __shared__ F sD[2][KS_C][CTB][64];  // dDelta as B fragments (contraction over tokens)
   __shared__ __align__(16) T sdO[2][kC * DS];  // dO block of the chunk, row-major, staged a chunk ahead
 
-  const int n = blockIdx.x / HV, hv = blockIdx.x % HV, vb = blockIdx.y;
+  // 1-D grid, the forward scan's mapping (scan_grid)
+  constexpr int NVB = V / BV;
+  const int grp = (int)blockIdx.x / (8 * NVB), rem = (int)blockIdx.x % (8 * NVB);
+  const int cl = grp * 8 + rem % 8;
+  if (cl >= N * HV) return;
+  const int n = cl / HV, hv = cl % HV, vb = rem / 8;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   int64_t bos;
   int len;
@@ -1340,13 +1345,13 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
     // forward recurrence keeping S0 and Delta (no outputs), unless a training
     // forward (kda_chunk_fwd_train) already stored them in this workspace
     if (!saved) {
-      hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, true, 4>), dim3((unsigned)chains, V / BVC),
+      hipLaunchKernelGGL((chunk_scan_kernel<T, K, V, BVC, true, 4>), dim3(scan_grid(chains, V, BVC)),
                          dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL, (const int*)ws_int,
                          cu, h0, d.N, d.T, d.HV, 0, (T*)nullptr, (float*)nullptr, ws_B);
       hipError_t e2 = hipGetLastError();
       if (e2 != hipSuccess) return e2;
     }
-    hipLaunchKernelGGL((chunk_rev_scan_kernel<T, K, V, BVC>), dim3((unsigned)chains, V / BVC),
+    hipLaunchKernelGGL((chunk_rev_scan_kernel<T, K, V, BVC>), dim3(scan_grid(chains, V, BVC)),
                        dim3(kThreads), 0, s, (const T*)ws_T, (const float*)ws_GL, ws_B,
                        (const int*)ws_int, cu, (const T*)dO, dht, d.N, d.T, d.HV, dh0);
     return hipGetLastError();

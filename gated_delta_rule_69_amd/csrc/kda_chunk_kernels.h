@@ -1373,7 +1373,15 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
   __shared__ F sS[2][KS_K][CTB][64];  // S as B fragments (contraction over channels), 2 buffers
   __shared__ F sD[2][KS_C][CTB][64];  // Delta as B fragments (contraction over tokens), 2 buffers
 
-  const int n = blockIdx.x / HV, hv = blockIdx.x % HV, vb = blockIdx.y;
+  // 1-D grid (scan_grid): groups of 8 chains x all V blocks, block vb of chain
+  // c being workgroup (c / 8) * 8 * NVB + vb * 8 + c % 8, so that every block
+  // of a chain lands on the same XCD (workgroups are dealt to the 8 XCDs in
+  // turn) and all of them are dispatched together
+  constexpr int NVB = V / BV;
+  const int grp = (int)blockIdx.x / (8 * NVB), rem = (int)blockIdx.x % (8 * NVB);
+  const int cl = grp * 8 + rem % 8;
+  if (cl >= N * HV) return;
+  const int n = cl / HV, hv = cl % HV, vb = rem / 8;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   // token tile and first value tile of this wave's Delta / output tiles
   const int tt = wave % NTT, ct0 = WPT == 1 ? 0 : (wave / NTT) * CPW;
@@ -1772,6 +1780,13 @@ inline int64_t max_chunks(const kda_dims& d, bool varlen) {
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workgroups of a scan over `chains` chains in V blocks of bv columns (the
+// 1-D grid of chunk_scan_kernel and chunk_rev_scan_kernel: groups of 8 chains
+// times V / bv blocks).
+inline unsigned scan_grid(int64_t chains, int V, int bv) {
+  return (unsigned)(((chains + 7) / 8) * 8 * (V / bv));
+}
 
 inline int scan_block_v(int64_t chains, int V, int cus) {
   int bv = 64;
