@@ -53,7 +53,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_SOURCES = ("gated_delta_rule_69_amd/csrc/kda_common.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk_kernels.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk.hip")
-TRAFFIC_SHA16 = "3f8ebba4054850e6"
+TRAFFIC_SHA16 = "956bd367f6f2253b"
 TRAFFIC_BYTES = 1085.6e6
 
 
