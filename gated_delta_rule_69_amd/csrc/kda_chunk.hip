@@ -7,14 +7,16 @@ namespace kda {
 
 // ------------------------------------------------------------------ chunk table
 // ws_int layout: [0] total chunks, [1 .. N+1] first chunk of each sequence
-// (seq_off, N+1 entries), then chunk_seq[max_chunks].
+// (seq_off, N+1 entries), [N+2 .. 2N+2) the order in which the scans take the
+// sequences (scan_seq), then chunk_seq[max_chunks].
 __global__ void __launch_bounds__(1024)
 chunk_table_kernel(const int32_t* __restrict__ cu, int N, int* __restrict__ ws_int,
                    int max_chunks) {
   __shared__ int s_scan[1024];
   int* total = ws_int;
   int* seq_off = ws_int + 1;
-  int* chunk_seq = ws_int + 2 + N;
+  int* scan_seq = ws_int + 2 + N;
+  int* chunk_seq = ws_int + 2 + 2 * N;
   int carry = 0;
   for (int base = 0; base < N; base += 1024) {
     const int n = base + threadIdx.x;
@@ -54,6 +56,26 @@ chunk_table_kernel(const int32_t* __restrict__ cu, int N, int* __restrict__ ws_i
     seq_off[N] = carry;
     total[0] = carry;
   }
+  // scan order: longest sequence first (ties in index order), so that the
+  // longest chains, which bound a scan's time, start when the launch does
+  // rather than behind workgroups of shorter ones; above 1024 sequences the
+  // index order (each sequence is then a small share of the batch)
+  if (N <= 1024) {
+    const int n = threadIdx.x;
+    const int len = n < N ? cu[n + 1] - cu[n] : 0;
+    s_scan[n] = len;
+    __syncthreads();
+    if (n < N) {
+      int r = 0;
+      for (int j = 0; j < N; ++j) {
+        const int lj = s_scan[j];
+        r += (lj > len || (lj == len && j < n)) ? 1 : 0;
+      }
+      scan_seq[r] = n;
+    }
+  } else {
+    for (int n = threadIdx.x; n < N; n += 1024) scan_seq[n] = n;
+  }
 }
 
 hipError_t launch_chunk_table(const int32_t* cu, int N, int* ws_int, int max_chunks, hipStream_t s) {
@@ -64,7 +86,7 @@ hipError_t launch_chunk_table(const int32_t* cu, int N, int* ws_int, int max_chu
 template <typename T, int K, int V>
 size_t ws_bytes_t(const kda_dims& d, bool varlen) {
   const int64_t mc = max_chunks(d, varlen);
-  size_t b = align256(sizeof(int) * (size_t)(2 + d.N + mc));
+  size_t b = align256(sizeof(int) * (size_t)(2 + 2 * (size_t)d.N + mc));
   b += align256((size_t)mc * d.HV * Ws<T, K, V>::bytes_T);
   b += align256((size_t)mc * d.HV * Ws<T, K, V>::bytes_GL);
   return b;
@@ -80,7 +102,7 @@ hipError_t chunk_fwd_t(const kda_dims& d, const void* q, const void* k, const vo
   const int64_t mc = max_chunks(d, varlen);
   char* p = reinterpret_cast<char*>(ws);
   int* ws_int = reinterpret_cast<int*>(p);
-  p += align256(sizeof(int) * (size_t)(2 + d.N + mc));
+  p += align256(sizeof(int) * (size_t)(2 + 2 * (size_t)d.N + mc));
   T* ws_T = reinterpret_cast<T*>(p);
   p += align256((size_t)mc * d.HV * Ws<T, K, V>::bytes_T);
   float* ws_GL = reinterpret_cast<float*>(p);

@@ -62,7 +62,8 @@ chunk_rev_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_G
   const int grp = (int)blockIdx.x / (8 * NVB), rem = (int)blockIdx.x % (8 * NVB);
   const int cl = grp * 8 + rem % 8;
   if (cl >= N * HV) return;
-  const int n = cl / HV, hv = cl % HV, vb = rem / 8;
+  // packed batches: sequences in the chunk table's scan order (longest first)
+  const int n = cu ? ws_int[2 + N + cl / HV] : cl / HV, hv = cl % HV, vb = rem / 8;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   int64_t bos;
   int len;
@@ -1281,7 +1282,7 @@ __global__ void gva_reduce_kernel(const float* __restrict__ dq_part, const float
 template <typename T, int K, int V>
 size_t bwd_ws_bytes_t(const kda_dims& d, bool varlen) {
   const int64_t mc = max_chunks(d, varlen);
-  size_t b = align256(sizeof(int) * (size_t)(2 + d.N + mc));
+  size_t b = align256(sizeof(int) * (size_t)(2 + 2 * (size_t)d.N + mc));
   b += align256((size_t)mc * d.HV * Ws<T, K, V>::bytes_T);
   b += align256((size_t)mc * d.HV * Ws<T, K, V>::bytes_GL);
   b += align256((size_t)mc * d.HV * WsB<T, K, V>::elems * sizeof(T));
@@ -1300,7 +1301,7 @@ hipError_t chunk_bwd_t(const kda_dims& d, const void* q, const void* k, const vo
   const int64_t mc = max_chunks(d, varlen);
   char* p = reinterpret_cast<char*>(ws);
   int* ws_int = reinterpret_cast<int*>(p);
-  p += align256(sizeof(int) * (size_t)(2 + d.N + mc));
+  p += align256(sizeof(int) * (size_t)(2 + 2 * (size_t)d.N + mc));
   T* ws_T = reinterpret_cast<T*>(p);
   p += align256((size_t)mc * d.HV * Ws<T, K, V>::bytes_T);
   float* ws_GL = reinterpret_cast<float*>(p);

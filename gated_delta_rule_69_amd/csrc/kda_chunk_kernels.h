@@ -167,7 +167,7 @@ __device__ __forceinline__ ChunkGeo chunk_geo(int j, const int32_t* cu, const in
     r.c = c;
   } else {
     if (j >= ws_int[0]) return r;
-    const int n = ws_int[2 + N + j];
+    const int n = ws_int[2 + 2 * N + j];
     const int c = j - ws_int[1 + n];
     const int bos = cu[n], len = cu[n + 1] - bos;
     r.ok = 1;
@@ -1381,7 +1381,8 @@ chunk_scan_kernel(const T* __restrict__ ws_T, const float* __restrict__ ws_GL,
   const int grp = (int)blockIdx.x / (8 * NVB), rem = (int)blockIdx.x % (8 * NVB);
   const int cl = grp * 8 + rem % 8;
   if (cl >= N * HV) return;
-  const int n = cl / HV, hv = cl % HV, vb = rem / 8;
+  // packed batches: sequences in the chunk table's scan order (longest first)
+  const int n = cu ? ws_int[2 + N + cl / HV] : cl / HV, hv = cl % HV, vb = rem / 8;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   // token tile and first value tile of this wave's Delta / output tiles
   const int tt = wave % NTT, ct0 = WPT == 1 ? 0 : (wave / NTT) * CPW;
