@@ -53,8 +53,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_SOURCES = ("gated_delta_rule_69_amd/csrc/kda_common.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk_kernels.h",
                    "gated_delta_rule_69_amd/csrc/kda_chunk.hip")
-TRAFFIC_SHA16 = "26435ae3d251c5dc"
-TRAFFIC_BYTES = 1085.4e6
+TRAFFIC_SHA16 = "8aba7f40c156fcf1"
+TRAFFIC_BYTES = 1085.6e6
 
 
 def measured_traffic():
